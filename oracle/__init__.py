@@ -1,0 +1,186 @@
+"""CPU oracle for the BitLinear forward pass -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The product package
+(``ternary_weight_quantized_bitlinear_amd``) never imports it; the two share no
+code.  The arithmetic lives in ``bitlinear_oracle.c`` (plain single-threaded C,
+built with ``-ffp-contract=off``); this module only marshals numpy arrays.
+
+Functions and the passages they follow (page titles abbreviated as in the C
+source header):
+
+* :func:`gamma` -- mean |W| ([b158] "The Mathematical Formulation of
+  BitLinear", eq. 1), exact sum, rounded once to fp32, clamp(min=eps).
+* :func:`quantize_weights` -- Clip(Round(W/gamma), -1, 1) and the 2-bit
+  packing ([b158] eq. 1; [2b4t] "1. The BitLinear Operator").
+* :func:`quantize_acts` -- per-token / per-tensor absmax int8 ([b158] eq. 2;
+  [2b4t] "1. The BitLinear Operator") and int4 ([a48] "1. Hybrid W1.58 / A4
+  Quantization Function").
+* :func:`forward`, :func:`forward_at` -- integer contraction, rescale
+  ([b158] eq. 3; [a48] dataflow figure), bias, ReLU^2 ([2b4t] "2. Squared
+  ReLU Activation").
+
+bf16 arrays are passed as ``numpy.uint16`` holding the bf16 bit patterns.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "bitlinear_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+F32, BF16 = 0, 1
+PER_TOKEN, PER_TENSOR = 0, 1
+EPI_NONE, EPI_RELU2 = 0, 1
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with gcc (plain C, no fast-math, no contraction)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC",
+               "-shared", "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        # ORACLE_LIB points the pin suite at a deliberately broken build (mutation tests)
+        lib = ctypes.CDLL(os.environ.get("ORACLE_LIB") or build())
+        P = ctypes.c_void_p
+        I64 = ctypes.c_int64
+        I = ctypes.c_int
+        F = ctypes.c_float
+        lib.oracle_gamma.argtypes = [P, I, I64, I64, F, P]
+        lib.oracle_quantize_weights.argtypes = [P, I, I64, I64, F, P, P, P]
+        lib.oracle_quantize_acts.argtypes = [P, I, I64, I64, I, I, F, P, P]
+        lib.oracle_forward.argtypes = [P, I, P, I, P, P, P, I64, I64, I64, I, P, I, P]
+        lib.oracle_forward_at.argtypes = [P, I, P, I, P, P, P, I64, I64, I64, I, I64, P, P, P, I,
+                                          P]
+        lib.oracle_to_bf16.argtypes = [P, P, I64]
+        for name in ("oracle_gamma", "oracle_quantize_weights", "oracle_quantize_acts",
+                     "oracle_forward", "oracle_forward_at"):
+            getattr(lib, name).restype = I
+        lib.oracle_to_bf16.restype = None
+        _lib = lib
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _check(st, what):
+    if st != 0:
+        raise OracleError("%s failed with status %d" % (what, st))
+
+
+def _dtype_code(a: np.ndarray) -> int:
+    if a.dtype == np.float32:
+        return F32
+    if a.dtype == np.uint16:
+        return BF16
+    raise TypeError("oracle inputs are float32 or uint16 (bf16 bits), got %s" % a.dtype)
+
+
+def gamma(W: np.ndarray, eps: float = 1e-5) -> np.float32:
+    W = np.ascontiguousarray(W)
+    N, K = W.shape
+    out = np.zeros(1, np.float32)
+    _check(_load().oracle_gamma(_ptr(W), _dtype_code(W), N, K, eps, _ptr(out)), "oracle_gamma")
+    return out[0]
+
+
+def quantize_weights(W: np.ndarray, eps: float = 1e-5):
+    """Returns (packed uint8 [N, K/4], gamma float32, codes int8 [N, K])."""
+    W = np.ascontiguousarray(W)
+    N, K = W.shape
+    packed = np.zeros((N, K // 4), np.uint8)
+    g = np.zeros(1, np.float32)
+    codes = np.zeros((N, K), np.int8)
+    _check(_load().oracle_quantize_weights(_ptr(W), _dtype_code(W), N, K, eps, _ptr(packed),
+                                           _ptr(g), _ptr(codes)), "oracle_quantize_weights")
+    return packed, g[0], codes
+
+
+def quantize_acts(X: np.ndarray, bits: int = 8, gran: int = PER_TOKEN, eps: float = 1e-5):
+    """Returns (Xq, act_scale).  Xq is int8 [M, K] for bits=8, uint8 [M, K/2] for bits=4."""
+    X = np.ascontiguousarray(X)
+    M, K = X.shape
+    if bits == 8:
+        Xq = np.zeros((M, K), np.int8)
+    else:
+        Xq = np.zeros((M, K // 2), np.uint8)
+    scale = np.zeros(M if gran == PER_TOKEN else 1, np.float32)
+    _check(_load().oracle_quantize_acts(_ptr(X), _dtype_code(X), M, K, bits, gran, eps, _ptr(Xq),
+                                        _ptr(scale)), "oracle_quantize_acts")
+    return Xq, scale
+
+
+def _fwd_common(Xq, bits, act_scale, packed, gamma_, bias):
+    Xq = np.ascontiguousarray(Xq)
+    act_scale = np.ascontiguousarray(act_scale, dtype=np.float32)
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    g = np.array([gamma_], np.float32)
+    b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
+    M = Xq.shape[0]
+    K = Xq.shape[1] * (1 if bits == 8 else 2)
+    N = packed.shape[0]
+    return Xq, act_scale, packed, g, b, M, N, K
+
+
+def forward(Xq, bits, act_scale, gran, packed, gamma_, bias=None, epi=EPI_NONE,
+            y_dtype=F32):
+    """Returns (Y [M, N] float32 or uint16 bf16 bits, acc int32 [M, N])."""
+    Xq, act_scale, packed, g, b, M, N, K = _fwd_common(Xq, bits, act_scale, packed, gamma_, bias)
+    Y = np.zeros((M, N), np.float32 if y_dtype == F32 else np.uint16)
+    acc = np.zeros((M, N), np.int32)
+    _check(_load().oracle_forward(_ptr(Xq), bits, _ptr(act_scale), gran, _ptr(packed), _ptr(g),
+                                  _ptr(b), M, N, K, epi, _ptr(Y), y_dtype, _ptr(acc)),
+           "oracle_forward")
+    return Y, acc
+
+
+def forward_at(Xq, bits, act_scale, gran, packed, gamma_, ms, ns, bias=None, epi=EPI_NONE,
+               y_dtype=F32):
+    """The outputs at positions (ms[i], ns[i]): returns (y [count], acc int32 [count])."""
+    Xq, act_scale, packed, g, b, M, N, K = _fwd_common(Xq, bits, act_scale, packed, gamma_, bias)
+    ms = np.ascontiguousarray(ms, dtype=np.int64)
+    ns = np.ascontiguousarray(ns, dtype=np.int64)
+    count = ms.shape[0]
+    Y = np.zeros(count, np.float32 if y_dtype == F32 else np.uint16)
+    acc = np.zeros(count, np.int32)
+    _check(_load().oracle_forward_at(_ptr(Xq), bits, _ptr(act_scale), gran, _ptr(packed),
+                                     _ptr(g), _ptr(b), M, N, K, epi, count, _ptr(ms), _ptr(ns),
+                                     _ptr(Y), y_dtype, _ptr(acc)), "oracle_forward_at")
+    return Y, acc
+
+
+def to_bf16(y: np.ndarray) -> np.ndarray:
+    y = np.ascontiguousarray(y, dtype=np.float32)
+    out = np.zeros(y.shape, np.uint16)
+    _load().oracle_to_bf16(_ptr(y), _ptr(out), y.size)
+    return out
+
+
+def bitlinear(X, packed, gamma_, bits=8, gran=PER_TOKEN, bias=None, epi=EPI_NONE, y_dtype=F32,
+              eps=1e-5):
+    """The whole layer on pre-packed weights: quantize_acts then forward."""
+    Xq, s = quantize_acts(X, bits, gran, eps)
+    Y, acc = forward(Xq, bits, s, gran, packed, gamma_, bias, epi, y_dtype)
+    return Y, acc, Xq, s

@@ -1,0 +1,375 @@
+/*
+ * BitLinear forward-pass ORACLE  --  TEST INFRASTRUCTURE ONLY.
+ *
+ * Plain, slow, single-threaded CPU code that computes what the BitNet b1.58
+ * BitLinear layer computes, written so that a reader can check every step
+ * against the source pages by eye.  Only tests/, __graft_entry__.smoke() and
+ * the cpu_baseline leg of bench.py may load it.  The product library
+ * (ternary_weight_quantized_bitlinear_amd) never links, loads or calls it,
+ * and the two share no code: no headers, no helpers, no tables.
+ *
+ * Build: gcc -O2 -std=c11 -ffp-contract=off -fPIC -shared (no -ffast-math, no
+ * SIMD intrinsics, no threads).  -ffp-contract=off keeps every a*b+c as two
+ * separately rounded fp32 operations, as the pages' PyTorch listings do.
+ *
+ * Sources (cited by title and section):
+ *   [b158]  "BitNet b1.58: The 1-Bit Ternary LLM Architecture Guide"
+ *           (aifetchly-blog.pages.dev), section "The Mathematical Formulation
+ *           of BitLinear" (equations 1-3) and "Implementation: Building a
+ *           Working BitLinear Layer in PyTorch" (Step 1 and Step 2 listings).
+ *   [2b4t]  "BitNet 2B4T Guide: Scaling Native 1.58-Bit LLMs"
+ *           (aifetchly-blog.pages.dev), section "BitNet b1.58 2B4T
+ *           Architecture: BitLinear, Squared ReLU, and SubLN" (pipeline
+ *           figure, "1. The BitLinear Operator", "2. Squared ReLU Activation")
+ *           and the "End-to-End PyTorch Implementation" listing.
+ *   [a48]   "BitNet a4.8 Guide: 4-Bit Activation 1-Bit LLMs"
+ *           (aifetchly-blog.pages.dev), section "The Solution" ("1. Hybrid
+ *           W1.58 / A4 Quantization Function", "3. Native Hardware INT4
+ *           Tensor Core Mapping" with its dataflow figure) and the
+ *           "Implementation" section (layer-pipeline figure, Step 2-4 listings).
+ *
+ * Readings taken where the pages are silent or disagree (each one is listed,
+ * with its reason, in the design notes of the repository):
+ *   - eps is applied as clamp(min=eps) on gamma and on the activation absmax
+ *     (the [a48] and [2b4t] listings), eps = 1e-5 by default.
+ *   - gamma is the exact mean of |W| rounded once to fp32, ties to even.
+ *   - int8: Q_b = 127, s = 127 / a (fp32 divide), q = clamp(round(x*s), -128, 127)
+ *     ([2b4t] "1. The BitLinear Operator"); int4: s = a / 7,
+ *     q = clamp(round(x / s), -8, 7) ([a48] "1. Hybrid W1.58 / A4 ...").
+ *   - round() is round-half-to-even (torch.round in every listing).
+ *   - dequant factor: int8 f = gamma / s ([b158] eq. 3), int4 f = s * gamma
+ *     ([a48] dataflow figure); y = (float)acc * f, then + bias, then ReLU^2.
+ *   - 2-bit layout: field value c+1 in {0,1,2}, 4 codes per byte, code k of a
+ *     row in bits 2*(k%4) of byte k/4, rows of K/4 bytes, W is [N=out][K=in].
+ *   - int4 layout: two's-complement nibbles, element 2i in the low nibble of
+ *     byte i, rows of K/2 bytes.
+ */
+#include <stdint.h>
+#include <string.h>
+#include <math.h>
+
+/* dtype codes of the oracle's own C interface */
+#define OR_F32  0
+#define OR_BF16 1
+
+/* status codes of the oracle's own C interface */
+#define OR_OK     0
+#define OR_EINVAL 1
+#define OR_ERANGE 2
+
+static float f32_from_bits(uint32_t u) { float f; memcpy(&f, &u, 4); return f; }
+static uint32_t bits_from_f32(float f) { uint32_t u; memcpy(&u, &f, 4); return u; }
+
+/* bf16 is the top half of an fp32 word: widening is exact. */
+static float widen_bf16(uint16_t h) { return f32_from_bits((uint32_t)h << 16); }
+
+/* fp32 -> bf16, round to nearest, ties to even; NaN stays NaN. */
+static uint16_t narrow_bf16(float f)
+{
+    uint32_t u = bits_from_f32(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u)
+        return (uint16_t)((u >> 16) | 0x0040u);
+    uint32_t lsb = (u >> 16) & 1u;
+    u += 0x7FFFu + lsb;
+    return (uint16_t)(u >> 16);
+}
+
+static float load_elem(const void *p, int dtype, int64_t i)
+{
+    if (dtype == OR_BF16)
+        return widen_bf16(((const uint16_t *)p)[i]);
+    return ((const float *)p)[i];
+}
+
+/* ------------------------------------------------------------------------ */
+/* gamma = mean |W|, exactly, rounded once to fp32                           */
+/* ------------------------------------------------------------------------ */
+/*
+ * [b158] eq. 1 and [2b4t] "1. The BitLinear Operator" define gamma (beta on
+ * [2b4t]) as (1/nm) * sum |W_ij|.  Every finite fp32 value is an integer
+ * multiple of 2^-149, so the sum is accumulated exactly as a multi-word
+ * integer in units of 2^-149, divided by n*m with a remainder, and rounded to
+ * the nearest fp32 (ties to even).
+ */
+#define NLIMB 10 /* 320 bits: |w| < 2^277 units, times n*m < 2^32 */
+
+static void big_add_shifted(uint32_t *acc, uint32_t mant, int shift)
+{
+    int li = shift / 32, off = shift % 32;
+    uint64_t v = (uint64_t)mant << off;
+    uint64_t carry = 0;
+    for (int i = li; i < NLIMB; ++i) {
+        uint64_t add = 0;
+        if (i == li) add = v & 0xFFFFFFFFu;
+        else if (i == li + 1) add = v >> 32;
+        uint64_t t = (uint64_t)acc[i] + add + carry;
+        acc[i] = (uint32_t)t;
+        carry = t >> 32;
+        if (i > li + 1 && carry == 0) break;
+    }
+}
+
+static int big_bit(const uint32_t *a, int i) { return (int)((a[i / 32] >> (i % 32)) & 1u); }
+
+static int big_msb(const uint32_t *a)
+{
+    for (int i = NLIMB * 32 - 1; i >= 0; --i)
+        if (big_bit(a, i)) return i;
+    return -1;
+}
+
+/* Round-to-nearest-even fp32 value of (sum of units * 2^-149) / count. */
+static float exact_mean_units(const uint32_t *sum, uint64_t count)
+{
+    uint32_t q[NLIMB];
+    uint64_t r = 0;
+    for (int i = NLIMB - 1; i >= 0; --i) {
+        uint64_t cur = (r << 32) | sum[i];
+        q[i] = (uint32_t)(cur / count);
+        r = cur % count;
+    }
+    int p = big_msb(q);
+    /* fp32 keeps 24 significant bits; below 2^23 units the quantum is one unit */
+    int shift = p > 23 ? p - 23 : 0;
+    uint64_t mant = 0;
+    for (int i = 23; i >= 0; --i) {
+        int b = shift + i;
+        mant = (mant << 1) | (uint64_t)(b < NLIMB * 32 ? big_bit(q, b) : 0);
+    }
+    int round_up;
+    if (shift > 0) {
+        int half = big_bit(q, shift - 1);
+        int sticky = (r != 0);
+        for (int i = 0; i < shift - 1 && !sticky; ++i) sticky = big_bit(q, i);
+        round_up = half && (sticky || (mant & 1u));
+    } else {
+        /* the discarded part is r / count */
+        uint64_t twice = 2 * r;
+        round_up = twice > count || (twice == count && (mant & 1u));
+    }
+    mant += (uint64_t)round_up;
+    return (float)ldexp((double)mant, shift - 149);
+}
+
+int oracle_gamma(const void *W, int w_dtype, int64_t N, int64_t K, float eps, float *gamma_out)
+{
+    if (!W || !gamma_out || N <= 0 || K <= 0) return OR_EINVAL;
+    uint64_t count = (uint64_t)N * (uint64_t)K;
+    if (count >= (1ull << 32)) return OR_ERANGE;
+    uint32_t sum[NLIMB];
+    memset(sum, 0, sizeof sum);
+    for (uint64_t i = 0; i < count; ++i) {
+        uint32_t b = bits_from_f32(load_elem(W, w_dtype, (int64_t)i)) & 0x7FFFFFFFu;
+        uint32_t e = b >> 23;
+        if (e == 255) return OR_ERANGE; /* inputs must be finite */
+        uint32_t m = (b & 0x7FFFFFu) | (e ? 0x800000u : 0u);
+        int shift = (e ? (int)e : 1) - 1; /* value = m * 2^(max(e,1)-150) */
+        big_add_shifted(sum, m, shift);
+    }
+    float g = exact_mean_units(sum, count);
+    /* clamp(min=eps), as the [a48] and [2b4t] listings do */
+    *gamma_out = g < eps ? eps : g;
+    return OR_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* weight quantization: codes in {-1,0,+1} and the 2-bit packing             */
+/* ------------------------------------------------------------------------ */
+/*
+ * [b158] eq. 1, [2b4t] "1. The BitLinear Operator", [a48] "1. Hybrid W1.58 /
+ * A4 ...": W~ = Clip(Round(W / gamma), -1, 1).  The division is one fp32
+ * division, rounding is half-to-even.  Rounding and clipping to integer
+ * bounds commute, so the order in which the pages write them does not matter.
+ */
+int oracle_quantize_weights(const void *W, int w_dtype, int64_t N, int64_t K, float eps,
+                            uint8_t *packed, float *gamma_out, int8_t *codes_out)
+{
+    if (!W || !packed || !gamma_out || N <= 0 || K <= 0 || K % 4 != 0) return OR_EINVAL;
+    float gamma;
+    int st = oracle_gamma(W, w_dtype, N, K, eps, &gamma);
+    if (st != OR_OK) return st;
+    *gamma_out = gamma;
+    int64_t row_bytes = K / 4;
+    memset(packed, 0, (size_t)(N * row_bytes));
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t k = 0; k < K; ++k) {
+            float w = load_elem(W, w_dtype, n * K + k);
+            float v = rintf(w / gamma);
+            if (v < -1.0f) v = -1.0f;
+            if (v > 1.0f) v = 1.0f;
+            int c = (int)v;
+            if (codes_out) codes_out[n * K + k] = (int8_t)c;
+            packed[n * row_bytes + k / 4] |= (uint8_t)((c + 1) << (2 * (k % 4)));
+        }
+    }
+    return OR_OK;
+}
+
+/* the code at (n, k) of a packed matrix, read back from the 2-bit field */
+static int weight_code(const uint8_t *packed, int64_t K, int64_t n, int64_t k)
+{
+    int field = (packed[n * (K / 4) + k / 4] >> (2 * (k % 4))) & 3;
+    return field - 1;
+}
+
+/* ------------------------------------------------------------------------ */
+/* activation quantization                                                   */
+/* ------------------------------------------------------------------------ */
+/*
+ * int8 ([b158] eq. 2, [2b4t] "1. The BitLinear Operator"):
+ *     a = max |x| over the token (gran 0) or over the whole tensor (gran 1),
+ *     s = 127 / max(a, eps), q = Clip(Round(x * s), -128, 127).
+ * int4 ([a48] "1. Hybrid W1.58 / A4 Quantization Function", Step 3 listing):
+ *     s = max(a, eps) / 7, q = Clip(Round(x / s), -8, 7), two per byte.
+ * act_scale receives s: one value per token, or one for the tensor.
+ */
+int oracle_quantize_acts(const void *X, int x_dtype, int64_t M, int64_t K, int bits, int gran,
+                         float eps, void *Xq, float *act_scale)
+{
+    if (!X || !Xq || !act_scale || M <= 0 || K <= 0) return OR_EINVAL;
+    if (bits != 8 && bits != 4) return OR_EINVAL;
+    if (gran != 0 && gran != 1) return OR_EINVAL;
+    if (bits == 4 && K % 2 != 0) return OR_EINVAL;
+
+    float tensor_max = 0.0f;
+    if (gran == 1) {
+        for (int64_t i = 0; i < M * K; ++i) {
+            float a = fabsf(load_elem(X, x_dtype, i));
+            if (!(a <= 3.4028235e38f)) return OR_ERANGE; /* inputs must be finite */
+            if (a > tensor_max) tensor_max = a;
+        }
+    }
+    for (int64_t m = 0; m < M; ++m) {
+        float amax = tensor_max;
+        if (gran == 0) {
+            amax = 0.0f;
+            for (int64_t k = 0; k < K; ++k) {
+                float a = fabsf(load_elem(X, x_dtype, m * K + k));
+                if (!(a <= 3.4028235e38f)) return OR_ERANGE;
+                if (a > amax) amax = a;
+            }
+        }
+        float a = amax < eps ? eps : amax;
+        if (bits == 8) {
+            float s = 127.0f / a;
+            if (gran == 0 || m == 0) act_scale[gran == 0 ? m : 0] = s;
+            for (int64_t k = 0; k < K; ++k) {
+                float v = rintf(load_elem(X, x_dtype, m * K + k) * s);
+                if (v < -128.0f) v = -128.0f;
+                if (v > 127.0f) v = 127.0f;
+                ((int8_t *)Xq)[m * K + k] = (int8_t)v;
+            }
+        } else {
+            float s = a / 7.0f;
+            if (gran == 0 || m == 0) act_scale[gran == 0 ? m : 0] = s;
+            uint8_t *row = (uint8_t *)Xq + m * (K / 2);
+            memset(row, 0, (size_t)(K / 2));
+            for (int64_t k = 0; k < K; ++k) {
+                float v = rintf(load_elem(X, x_dtype, m * K + k) / s);
+                if (v < -8.0f) v = -8.0f;
+                if (v > 7.0f) v = 7.0f;
+                int q = (int)v;
+                row[k / 2] |= (uint8_t)((q & 0xF) << (4 * (k % 2)));
+            }
+        }
+    }
+    return OR_OK;
+}
+
+/* the activation code at (m, k), read back from int8 or from the nibbles */
+static int act_code(const void *Xq, int bits, int64_t K, int64_t m, int64_t k)
+{
+    if (bits == 8) return ((const int8_t *)Xq)[m * K + k];
+    int nib = (((const uint8_t *)Xq)[m * (K / 2) + k / 2] >> (4 * (k % 2))) & 0xF;
+    return nib >= 8 ? nib - 16 : nib;
+}
+
+/* ------------------------------------------------------------------------ */
+/* forward: integer contraction, rescale, bias, ReLU^2                       */
+/* ------------------------------------------------------------------------ */
+/*
+ * [b158] eq. 3: Y = (X~ W~^T) * (gamma / scale_X), the product accumulated in
+ * integers ([a48] "3. Native Hardware INT4 Tensor Core Mapping": int32
+ * accumulators).  int4 uses Output = acc * (s_x * beta) ([a48] dataflow
+ * figure).  Optional bias after the rescale ([b158] Step 2 listing).
+ * ReLU^2(x) = max(0, x)^2 ([2b4t] "2. Squared ReLU Activation").
+ */
+static int one_output(const void *Xq, int bits, const float *act_scale, int gran,
+                      const uint8_t *packed, float gamma, const float *bias,
+                      int64_t N, int64_t K, int epi, int64_t m, int64_t n,
+                      int32_t *acc_out, float *y_out)
+{
+    (void)N;
+    int64_t acc = 0;
+    for (int64_t k = 0; k < K; ++k)
+        acc += (int64_t)act_code(Xq, bits, K, m, k) * (int64_t)weight_code(packed, K, n, k);
+    if (acc > INT32_MAX || acc < INT32_MIN) return OR_ERANGE;
+    float s = act_scale[gran == 0 ? m : 0];
+    float f = bits == 8 ? gamma / s : s * gamma;
+    float y = (float)acc * f;
+    if (bias) y = y + bias[n];
+    if (epi == 1) {
+        float r = y > 0.0f ? y : 0.0f;
+        y = r * r;
+    }
+    *acc_out = (int32_t)acc;
+    *y_out = y;
+    return OR_OK;
+}
+
+static void store_y(void *Y, int y_dtype, int64_t idx, float y)
+{
+    if (y_dtype == OR_BF16) ((uint16_t *)Y)[idx] = narrow_bf16(y);
+    else ((float *)Y)[idx] = y;
+}
+
+int oracle_forward(const void *Xq, int bits, const float *act_scale, int gran,
+                   const uint8_t *packed, const float *gamma, const float *bias,
+                   int64_t M, int64_t N, int64_t K, int epi, void *Y, int y_dtype,
+                   int32_t *acc_out)
+{
+    if (!Xq || !act_scale || !packed || !gamma || M <= 0 || N <= 0 || K <= 0 || K % 4 != 0)
+        return OR_EINVAL;
+    if ((bits != 8 && bits != 4) || (gran != 0 && gran != 1) || (epi != 0 && epi != 1))
+        return OR_EINVAL;
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            int32_t acc;
+            float y;
+            int st = one_output(Xq, bits, act_scale, gran, packed, *gamma, bias, N, K, epi, m, n,
+                                &acc, &y);
+            if (st != OR_OK) return st;
+            if (acc_out) acc_out[m * N + n] = acc;
+            if (Y) store_y(Y, y_dtype, m * N + n, y);
+        }
+    }
+    return OR_OK;
+}
+
+/* The same outputs at a list of (m, n) positions, for checks at full size. */
+int oracle_forward_at(const void *Xq, int bits, const float *act_scale, int gran,
+                      const uint8_t *packed, const float *gamma, const float *bias,
+                      int64_t M, int64_t N, int64_t K, int epi, int64_t count,
+                      const int64_t *ms, const int64_t *ns, void *Y, int y_dtype,
+                      int32_t *acc_out)
+{
+    if (!Xq || !act_scale || !packed || !gamma || !ms || !ns || count < 0 || K % 4 != 0)
+        return OR_EINVAL;
+    for (int64_t i = 0; i < count; ++i) {
+        if (ms[i] < 0 || ms[i] >= M || ns[i] < 0 || ns[i] >= N) return OR_EINVAL;
+        int32_t acc;
+        float y;
+        int st = one_output(Xq, bits, act_scale, gran, packed, *gamma, bias, N, K, epi, ms[i],
+                            ns[i], &acc, &y);
+        if (st != OR_OK) return st;
+        if (acc_out) acc_out[i] = acc;
+        if (Y) store_y(Y, y_dtype, i, y);
+    }
+    return OR_OK;
+}
+
+/* fp32 -> bf16 as the oracle rounds outputs (exposed for tests of the oracle) */
+void oracle_to_bf16(const float *src, uint16_t *dst, int64_t count)
+{
+    for (int64_t i = 0; i < count; ++i) dst[i] = narrow_bf16(src[i]);
+}

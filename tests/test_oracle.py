@@ -1,0 +1,539 @@
+"""Pins of the CPU oracle against what the pages and mathematics fix.
+
+No GPU.  Each test checks the oracle against something other than itself:
+hand-worked examples (tests/golden), exact rational arithmetic (tests/exact.py),
+a library matmul, closed forms, invariants and textbook statistics.
+"""
+from __future__ import annotations
+
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from exact import f32_bits, f32_from_bits, frac_of_f32, round_half_even, round_to_f32
+
+EPS = np.float32(1e-5)
+
+
+def _bits(h):
+    return int(h, 16)
+
+
+def _unpack_2bit(packed: np.ndarray, K: int) -> np.ndarray:
+    """Documented layout: field (c+1) of code k in bits 2*(k%4) of byte k/4."""
+    fields = np.stack([(packed >> (2 * j)) & 3 for j in range(4)], axis=-1)
+    return fields.reshape(packed.shape[0], K).astype(np.int64) - 1
+
+
+def _unpack_nibbles(xq: np.ndarray, K: int) -> np.ndarray:
+    lo = (xq & 0xF).astype(np.int64)
+    hi = (xq >> 4).astype(np.int64)
+    v = np.stack([lo, hi], axis=-1).reshape(xq.shape[0], K)
+    return np.where(v >= 8, v - 16, v)
+
+
+# ---------------------------------------------------------------- worked examples
+
+def test_worked_weights(golden):
+    g = golden["weights"]
+    W = np.array(g["W"], np.float32)
+    packed, gamma, codes = oracle.quantize_weights(W)
+    assert f32_bits(gamma) == _bits(g["gamma_bits"])
+    assert codes.tolist() == g["codes"]
+    assert packed.tolist() == g["packed"]
+
+
+@pytest.mark.parametrize("name", ["B", "C", "D", "E"])
+def test_worked_acts_and_forward(golden, name):
+    ex = [e for e in golden["acts"] if e["name"] == name][0]
+    W = np.array(golden["weights"]["W"], np.float32)
+    packed, gamma, _ = oracle.quantize_weights(W)
+    x = np.array([ex["x"]], np.float32)
+    bits = ex["bits"]
+    xq, s = oracle.quantize_acts(x, bits=bits)
+    assert f32_bits(s[0]) == _bits(ex["scale_bits"])
+    if bits == 8:
+        assert xq[0].tolist() == ex["q"]
+    else:
+        assert xq[0].tolist() == ex["packed_bytes"]
+        assert _unpack_nibbles(xq, 4)[0].tolist() == ex["q"]
+    y, acc = oracle.forward(xq, bits, s, oracle.PER_TOKEN, packed, gamma)
+    y2, acc2 = oracle.forward(xq, bits, s, oracle.PER_TOKEN, packed, gamma, epi=oracle.EPI_RELU2)
+    assert acc[0].tolist() == ex["acc"] and acc2[0].tolist() == ex["acc"]
+    if "y" in ex:
+        assert y[0].tolist() == ex["y"]
+        assert y2[0].tolist() == ex["y_relu2"]
+    else:
+        assert [f32_bits(v) for v in y[0]] == [_bits(h) for h in ex["y_bits"]]
+        assert [f32_bits(v) for v in y2[0]] == [_bits(h) for h in ex["y_relu2_bits"]]
+
+
+def test_worked_per_tensor(golden):
+    ex = golden["per_tensor"]
+    W = np.array(golden["weights"]["W"], np.float32)
+    packed, gamma, _ = oracle.quantize_weights(W)
+    X = np.array(ex["X"], np.float32)
+    xq, s = oracle.quantize_acts(X, bits=8, gran=oracle.PER_TENSOR)
+    assert s.shape == (1,) and f32_bits(s[0]) == _bits(ex["scale_bits"])
+    assert xq.tolist() == ex["q"]
+    y, acc = oracle.forward(xq, 8, s, oracle.PER_TENSOR, packed, gamma)
+    assert acc.tolist() == ex["acc"] and y.tolist() == ex["y"]
+
+
+def test_worked_zeros(golden):
+    z = golden["zeros"]
+    W = np.zeros((3, 8), np.float32)
+    packed, gamma, codes = oracle.quantize_weights(W)
+    assert f32_bits(gamma) == _bits(z["gamma_bits"])
+    assert (codes == 0).all() and (packed == z["packed_byte"]).all()
+    X = np.zeros((2, 8), np.float32)
+    for bits, key in ((8, "int8_scale_bits"), (4, "int4_scale_bits")):
+        xq, s = oracle.quantize_acts(X, bits=bits)
+        assert all(f32_bits(v) == _bits(z[key]) for v in s)
+        assert (xq == 0).all()
+        Xr = np.random.default_rng(5).standard_normal((2, 8)).astype(np.float32)
+        xq2, s2 = oracle.quantize_acts(Xr, bits=bits)
+        for epi in (oracle.EPI_NONE, oracle.EPI_RELU2):
+            y, acc = oracle.forward(xq2, bits, s2, 0, packed, gamma, epi=epi)
+            assert (acc == 0).all() and (y == 0).all()
+
+
+# ---------------------------------------------------------------- gamma = exact mean
+
+def _exact_mean_f32(W: np.ndarray) -> np.float32:
+    total = sum((abs(frac_of_f32(v)) for v in W.ravel()), Fraction(0))
+    return round_to_f32(total / W.size)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_gamma_is_correctly_rounded_mean(seed):
+    rng = np.random.default_rng(seed)
+    n, k = 7, 12
+    kind = seed % 3
+    if kind == 0:
+        W = (0.02 * rng.standard_normal((n, k))).astype(np.float32)
+    elif kind == 1:  # wide exponent range
+        W = (rng.standard_normal((n, k)) * 2.0 ** rng.integers(-60, 60, (n, k))).astype(np.float32)
+    else:  # subnormals and tiny normals mixed with ordinary values
+        W = (rng.standard_normal((n, k)) * 2.0 ** rng.integers(-149, -120, (n, k))).astype(
+            np.float32)
+        W[0, :3] = [1.0, -3.0, 0.25]
+    g = oracle.gamma(W)
+    ref = max(_exact_mean_f32(W), EPS)
+    assert f32_bits(g) == f32_bits(ref)
+
+
+def test_gamma_ties_to_even():
+    # mean = (1 + 2^-24) exactly: the midpoint between 1 and 1 + 2^-23 -> ties to 1.0
+    W = np.array([[1.0, 1.0 + 2.0 ** -23]], np.float32)
+    assert f32_bits(oracle.gamma(W)) == f32_bits(np.float32(1.0))
+    # mean = 1 + 3*2^-24: midpoint between 1+2^-23 and 1+2^-22 -> ties to 1+2^-22 (even)
+    W = np.array([[1.0 + 2.0 ** -23, 1.0 + 2.0 ** -22]], np.float32)
+    assert f32_bits(oracle.gamma(W)) == f32_bits(np.float32(1.0 + 2.0 ** -22))
+
+
+def test_gamma_large_sum_exact():
+    # 2^20 copies of a value whose fp32 running sum would drift: exact mean is the value
+    v = np.float32(0.015958)
+    W = np.full((1024, 1024), v, np.float32)
+    assert f32_bits(oracle.gamma(W)) == f32_bits(v)
+    # mixed magnitudes: exact mean known in closed form
+    W = np.zeros((1024, 1024), np.float32)
+    W[:, 0] = 3.0
+    W[:, 1] = 2.0 ** -30
+    exact = (Fraction(3) * 1024 + Fraction(1, 2 ** 30) * 1024) / (1024 * 1024)
+    assert f32_bits(oracle.gamma(W)) == f32_bits(round_to_f32(exact))
+
+
+def test_gamma_eps_clamp():
+    W = np.full((2, 4), 1e-7, np.float32)
+    assert f32_bits(oracle.gamma(W)) == f32_bits(EPS)
+    assert f32_bits(oracle.gamma(W, eps=1e-8)) == f32_bits(np.float32(1e-7))
+
+
+def test_gamma_bf16_input():
+    W = (0.02 * np.random.default_rng(3).standard_normal((16, 32))).astype(np.float32)
+    Wb = workloads.to_bf16_bits(W)
+    Wf = workloads.bf16_bits_to_f32(Wb)
+    assert f32_bits(oracle.gamma(Wb)) == f32_bits(oracle.gamma(Wf))
+    pb, gb, cb = oracle.quantize_weights(Wb)
+    pf, gf, cf = oracle.quantize_weights(Wf)
+    assert (pb == pf).all() and (cb == cf).all()
+
+
+# ---------------------------------------------------------------- weight codes
+
+def test_weight_codes_threshold_rule():
+    """c != 0 exactly when |w| > gamma * (1/2 + 2^-25) (the exact condition for the fp32
+    quotient w/gamma to exceed 1/2, which rounds half to even to 0)."""
+    rng = np.random.default_rng(11)
+    W = (0.02 * rng.standard_normal((8, 64))).astype(np.float32)
+    g = oracle.gamma(W)
+    # plant boundary values: exactly gamma/2, and its fp32 neighbours
+    for _ in range(8):  # replant until gamma no longer moves
+        half = np.float32(g) * np.float32(0.5)
+        nb = [half, np.nextafter(half, np.float32(1)), np.nextafter(half, np.float32(0)),
+              np.nextafter(np.nextafter(half, np.float32(1)), np.float32(1))]
+        W[0, :4] = nb
+        W[1, :4] = [-v for v in nb]
+        g_new = oracle.gamma(W)
+        if g_new == g:
+            break
+        g = g_new
+    assert g == oracle.gamma(W) and W[0, 0] == np.float32(g) * np.float32(0.5)
+    _, g2, codes = oracle.quantize_weights(W)
+    assert f32_bits(g2) == f32_bits(g)
+    th = frac_of_f32(g) * (Fraction(1, 2) + Fraction(1, 2 ** 25))
+    for (i, j), w in np.ndenumerate(W):
+        fw = frac_of_f32(w)
+        expect = 0 if abs(fw) <= th else (1 if fw > 0 else -1)
+        assert codes[i, j] == expect, (i, j, w)
+    # only gamma/2 itself (an exact tie at 0.5) rounds to 0: one ulp above is already past
+    # gamma*(1/2 + 2^-25) because ulp(gamma/2) >= gamma*2^-24
+    assert codes[0, :4].tolist() == [0, 1, 0, 1] and codes[1, :4].tolist() == [0, -1, 0, -1]
+
+
+def test_weight_codes_rounding_and_clip():
+    """gamma = 32/16 = 2 exactly, so W/gamma hits exact ties: half-to-even, then clip."""
+    W = np.array([[1.0, 3.0, 5.0, -1.0, -3.0, -5.0, 0.75, -0.75],
+                  [2.0, 2.0, 2.0, 2.0, 2.0, 2.0, 0.25, 0.25]], np.float32)
+    packed, g, codes = oracle.quantize_weights(W)
+    assert f32_bits(g) == f32_bits(np.float32(2.0))
+    # W/gamma = [0.5, 1.5, 2.5, -0.5, -1.5, -2.5, 0.375, -0.375] / [1 x6, 0.125 x2]
+    assert codes.tolist() == [[0, 1, 1, 0, -1, -1, 0, 0], [1, 1, 1, 1, 1, 1, 0, 0]]
+
+
+def test_packing_layout_and_field_range():
+    W, _ = workloads.parity_layer()
+    packed, gamma, codes = oracle.quantize_weights(W)
+    N, K = W.shape
+    assert packed.shape == (N, K // 4) and packed.nbytes == N * K * 2 // 8
+    fields = np.stack([(packed >> (2 * j)) & 3 for j in range(4)])
+    assert (fields != 3).all()
+    assert (_unpack_2bit(packed, K) == codes).all()
+    assert set(np.unique(codes).tolist()) <= {-1, 0, 1}
+
+
+def test_uniform_ternary_roundtrip():
+    rng = np.random.default_rng(2)
+    W = workloads.ternary_weights(rng, 64, 128)
+    packed, gamma, codes = oracle.quantize_weights(W)
+    nnz = int(np.count_nonzero(W))
+    assert f32_bits(gamma) == f32_bits(round_to_f32(Fraction(nnz, W.size)))
+    assert (codes == W.astype(np.int8)).all()
+
+
+def test_weight_statistics_gaussian():
+    """W ~ N(0, s): gamma -> s*sqrt(2/pi); P(c=0) = 2*Phi(sqrt(2/pi)/2) - 1 (textbook)."""
+    rng = np.random.default_rng(0)
+    s = 0.02
+    W = (s * rng.standard_normal((1024, 1024))).astype(np.float32)
+    packed, gamma, codes = oracle.quantize_weights(W)
+    assert abs(float(gamma) / (s * math.sqrt(2 / math.pi)) - 1) < 3e-3
+    p0 = math.erf(math.sqrt(2 / math.pi) / 2 / math.sqrt(2))
+    frac0 = float(np.mean(codes == 0))
+    assert abs(frac0 - p0) < 3e-3
+    assert abs(float(np.mean(codes == 1)) - (1 - p0) / 2) < 3e-3
+
+
+def test_weight_scaling_and_sign_invariance():
+    W, _ = workloads.parity_layer()
+    p, g, c = oracle.quantize_weights(W)
+    pn, gn, cn = oracle.quantize_weights(-W)
+    assert f32_bits(gn) == f32_bits(g) and (cn == -c).all()
+    for j in (-3, 5):
+        ps, gs, cs = oracle.quantize_weights((W * np.float32(2.0 ** j)).astype(np.float32))
+        assert (cs == c).all() and (ps == p).all()
+        assert f32_bits(gs) == f32_bits(np.float32(g * np.float32(2.0 ** j)))
+
+
+# ---------------------------------------------------------------- activation codes
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_int8_codes_exact(dtype):
+    _, X = workloads.parity_layer()
+    if dtype == "bf16":
+        Xin = workloads.to_bf16_bits(X)
+        X = workloads.bf16_bits_to_f32(Xin)
+    else:
+        Xin = X
+    xq, s = oracle.quantize_acts(Xin, bits=8)
+    for m in range(X.shape[0]):
+        a = max(np.abs(X[m]).max(), EPS)
+        s_ref = round_to_f32(Fraction(127) / frac_of_f32(a))
+        assert f32_bits(s[m]) == f32_bits(s_ref)
+        assert np.abs(xq[m]).max() == 127
+        for k in range(X.shape[1]):
+            prod = round_to_f32(frac_of_f32(X[m, k]) * frac_of_f32(s_ref))
+            q = max(-128, min(127, round_half_even(frac_of_f32(prod))))
+            assert xq[m, k] == q
+        # real-arithmetic bound: |q - x*127/a| <= 1/2 + 2^-17 (two fp32 roundings at <= 127)
+        err = np.abs(xq[m].astype(np.float64) - X[m].astype(np.float64) * 127.0 / float(a))
+        assert err.max() <= 0.5 + 2.0 ** -17
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_int4_codes_exact(dtype):
+    _, X = workloads.parity_layer(m=4)
+    if dtype == "bf16":
+        Xin = workloads.to_bf16_bits(X)
+        X = workloads.bf16_bits_to_f32(Xin)
+    else:
+        Xin = X
+    xq, s = oracle.quantize_acts(Xin, bits=4)
+    q_all = _unpack_nibbles(xq, X.shape[1])
+    assert xq.nbytes == X.shape[0] * X.shape[1] // 2
+    for m in range(X.shape[0]):
+        a = max(np.abs(X[m]).max(), EPS)
+        s_ref = round_to_f32(frac_of_f32(a) / 7)
+        assert f32_bits(s[m]) == f32_bits(s_ref)
+        assert np.abs(q_all[m]).max() == 7 and q_all[m].min() >= -7
+        for k in range(X.shape[1]):
+            quo = round_to_f32(frac_of_f32(X[m, k]) / frac_of_f32(s_ref))
+            assert q_all[m, k] == max(-8, min(7, round_half_even(frac_of_f32(quo))))
+
+
+def test_int8_multiply_form_on_rare_values():
+    """int8 codes come from the fp32 product x * (127/a) (the multiply form printed in
+    the b1.58 eq. 2 and the 2B4T operator), not from x / (a/127): the two differ on rare
+    inputs.  Find such inputs in a large sample and check them with exact rationals."""
+    rng = np.random.default_rng(123)
+    rows_ = []
+    for a in rng.uniform(0.5, 40.0, 32).astype(np.float32):
+        cand = [a]
+        for j in range(0, 127):
+            c = np.float32((j + 0.5) * float(a) / 127.0)
+            for d in range(-3, 4):
+                v = c
+                for _ in range(abs(d)):
+                    v = np.nextafter(v, np.float32(np.sign(d) * np.inf))
+                cand.append(v)
+        rows_.append(np.array(cand, np.float32))
+    X = np.stack(rows_)
+    xq, s = oracle.quantize_acts(X, bits=8)
+    a = np.maximum(np.abs(X).max(axis=1, keepdims=True), EPS)
+    mul = np.rint(X * (np.float32(127) / a))
+    div = np.rint(X / (a / np.float32(127)))
+    rows, cols = np.nonzero(mul != div)
+    assert len(rows) > 0  # the sample does contain inputs that tell the forms apart
+    for m, k in zip(rows, cols):
+        prod = round_to_f32(frac_of_f32(X[m, k]) * frac_of_f32(s[m]))
+        assert xq[m, k] == round_half_even(frac_of_f32(prod))
+
+
+def test_int8_ties_and_saturation():
+    # a = 127 gives s = 1, so x*s = x: exact half-integers exercise the tie rule
+    x = np.array([[127.0, -127.0, 0.5, 1.5, 2.5, -0.5, -1.5, -2.5, 126.5, -126.5, 3.5, 4.5]],
+                 np.float32)
+    xq, s = oracle.quantize_acts(x, bits=8)
+    assert f32_bits(s[0]) == f32_bits(np.float32(1.0))
+    assert xq[0].tolist() == [127, -127, 0, 2, 2, 0, -2, -2, 126, -126, 4, 4]
+
+
+def test_per_tensor_equals_per_token_with_common_max():
+    rng = np.random.default_rng(9)
+    X = rng.standard_normal((5, 32)).astype(np.float32)
+    X[:, 0] = 10.0  # every row has the same absmax -> identical scales
+    for bits in (8, 4):
+        a, sa = oracle.quantize_acts(X, bits=bits, gran=oracle.PER_TOKEN)
+        b, sb = oracle.quantize_acts(X, bits=bits, gran=oracle.PER_TENSOR)
+        assert (a == b).all() and sb.shape == (1,) and (sa == sb[0]).all()
+
+
+def test_act_symmetry_and_power_of_two_scaling():
+    _, X = workloads.parity_layer()
+    for bits in (8, 4):
+        q, s = oracle.quantize_acts(X, bits=bits)
+        qn, sn = oracle.quantize_acts(-X, bits=bits)
+        K = X.shape[1]
+        dq = (lambda t: t.astype(np.int64)) if bits == 8 else (lambda t: _unpack_nibbles(t, K))
+        assert (dq(qn) == -dq(q)).all() and (sn == s).all()
+        for j in (-4, 3):
+            qs, ss = oracle.quantize_acts((X * np.float32(2.0 ** j)).astype(np.float32), bits=bits)
+            assert (qs == q).all()
+            expect = s * np.float32(2.0 ** -j) if bits == 8 else s * np.float32(2.0 ** j)
+            assert (ss == expect.astype(np.float32)).all()
+
+
+# ---------------------------------------------------------------- contraction & output
+
+@pytest.mark.parametrize("bits", [8, 4])
+@pytest.mark.parametrize("shape", [(1, 16, 8), (3, 20, 5), (8, 256, 512), (5, 64, 33)])
+def test_contraction_matches_library_matmul(bits, shape):
+    M, K, N = shape
+    W, X = workloads.random_case(17, M, K, N, n_outliers=2)
+    packed, gamma, codes = oracle.quantize_weights(W)
+    xq, s = oracle.quantize_acts(X, bits=bits)
+    q = xq.astype(np.int64) if bits == 8 else _unpack_nibbles(xq, K)
+    ref = np.matmul(q, codes.astype(np.int64).T)
+    y, acc = oracle.forward(xq, bits, s, oracle.PER_TOKEN, packed, gamma)
+    assert (acc == ref).all()
+
+
+def test_contraction_brute_force_tiny():
+    """Every 4-wide ternary row against every activation row in a small grid."""
+    import itertools
+    rows = np.array(list(itertools.product([-1.0, 0.0, 1.0], repeat=4)), np.float32)  # 81 x 4
+    W = rows
+    packed, gamma, codes = oracle.quantize_weights(W)
+    assert (codes == W.astype(np.int8)).all()
+    X = np.array([[3.0, -1.0, 0.5, 2.0], [-7.0, 7.0, 1.0, -2.0]], np.float32)
+    xq, s = oracle.quantize_acts(X, bits=8)
+    y, acc = oracle.forward(xq, 8, s, 0, packed, gamma)
+    for m in range(2):
+        for n in range(81):
+            tot = 0
+            for k in range(4):
+                tot += int(xq[m, k]) * int(W[n, k])
+            assert acc[m, n] == tot
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+def test_output_rescale_exact_rational(bits):
+    W, X = workloads.parity_layer()
+    bias = np.random.default_rng(4).standard_normal(W.shape[0]).astype(np.float32)
+    packed, gamma, codes = oracle.quantize_weights(W)
+    xq, s = oracle.quantize_acts(X, bits=bits)
+    for b in (None, bias):
+        for epi in (0, 1):
+            y, acc = oracle.forward(xq, bits, s, 0, packed, gamma, bias=b, epi=epi)
+            for m in range(0, X.shape[0], 3):
+                fg, fs = frac_of_f32(gamma), frac_of_f32(s[m])
+                f = round_to_f32(fg / fs if bits == 8 else fs * fg)
+                for n in range(0, W.shape[0], 37):
+                    v = round_to_f32(Fraction(int(acc[m, n])) * frac_of_f32(f))
+                    if b is not None:
+                        v = round_to_f32(frac_of_f32(v) + frac_of_f32(b[n]))
+                    if epi:
+                        r = max(frac_of_f32(v), Fraction(0))
+                        v = round_to_f32(r * r)
+                    assert f32_bits(y[m, n]) == f32_bits(v), (m, n)
+
+
+def test_output_matches_listing_formulation_float64():
+    """The listings' F.linear(x_q, w_q) * (gamma / scale): float64 within 1e-6 relative."""
+    W, X = workloads.parity_layer()
+    packed, gamma, codes = oracle.quantize_weights(W)
+    xq, s = oracle.quantize_acts(X, bits=8)
+    y, acc = oracle.forward(xq, 8, s, 0, packed, gamma)
+    ref = torch.nn.functional.linear(torch.from_numpy(xq.astype(np.float64)),
+                                     torch.from_numpy(codes.astype(np.float64)))
+    ref = ref * (float(gamma) / torch.from_numpy(s.astype(np.float64))[:, None])
+    ref = ref.numpy()
+    assert np.all(np.abs(y - ref) <= 1e-6 * np.abs(ref) + 1e-30)
+    # and the layer approximates the float64 product X W^T (quantization error, loose)
+    full = X.astype(np.float64) @ (codes.astype(np.float64) * float(gamma)).T
+    rel = np.linalg.norm(y - full) / np.linalg.norm(full)
+    assert rel < 0.05
+
+
+def test_closed_form_basis_vector():
+    """X = a*e_k: q = 127*e_k, acc[:, n] = 127*c[n, k], y = a*gamma*c[n, k] (within fp32)."""
+    W, _ = workloads.parity_layer()
+    packed, gamma, codes = oracle.quantize_weights(W)
+    K = W.shape[1]
+    a = np.float32(3.75)
+    for k in (0, 17, K - 1):
+        X = np.zeros((1, K), np.float32)
+        X[0, k] = a
+        xq, s = oracle.quantize_acts(X, bits=8)
+        assert xq[0, k] == 127 and np.count_nonzero(xq) == 1
+        y, acc = oracle.forward(xq, 8, s, 0, packed, gamma)
+        assert (acc[0] == 127 * codes[:, k]).all()
+        np.testing.assert_allclose(y[0], float(a) * float(gamma) * codes[:, k], rtol=4e-7)
+
+
+def test_closed_form_constant_weights():
+    K, N = 32, 8
+    W = np.full((N, K), 0.3, np.float32)
+    packed, gamma, codes = oracle.quantize_weights(W)
+    assert f32_bits(gamma) == f32_bits(np.float32(0.3)) and (codes == 1).all()
+    X = np.random.default_rng(1).standard_normal((3, K)).astype(np.float32)
+    xq, s = oracle.quantize_acts(X, bits=8)
+    y, acc = oracle.forward(xq, 8, s, 0, packed, gamma)
+    assert (acc == xq.astype(np.int64).sum(axis=1, keepdims=True)).all()
+
+
+def test_output_symmetries_and_permutation():
+    W, X = workloads.parity_layer()
+    p, g, c = oracle.quantize_weights(W)
+    pn, gn, cn = oracle.quantize_weights(-W)
+    xq, s = oracle.quantize_acts(X, bits=8)
+    y, acc = oracle.forward(xq, 8, s, 0, p, g)
+    yn, accn = oracle.forward(xq, 8, s, 0, pn, gn)
+    assert (accn == -acc).all() and (yn == -y).all()
+    # scaling an activation row by 2^j scales y by exactly 2^j
+    Xs = X.copy()
+    Xs[2] *= np.float32(8.0)
+    xqs, ss = oracle.quantize_acts(Xs, bits=8)
+    ys, _ = oracle.forward(xqs, 8, ss, 0, p, g)
+    assert (ys[2] == y[2] * np.float32(8.0)).all()
+    # permuting the K axis of X and W alike leaves acc unchanged
+    perm = np.random.default_rng(8).permutation(W.shape[1])
+    pp, gp, cp = oracle.quantize_weights(np.ascontiguousarray(W[:, perm]))
+    xqp, sp = oracle.quantize_acts(np.ascontiguousarray(X[:, perm]), bits=8)
+    yp, accp = oracle.forward(xqp, 8, sp, 0, pp, gp)
+    assert (accp == acc).all() and (yp == y).all()
+
+
+def test_relu2_closed_form():
+    W = np.array([[1.0, 0.0, 0.0, 0.0], [-1.0, 0.0, 0.0, 0.0]], np.float32)
+    packed, gamma, codes = oracle.quantize_weights(W)  # gamma = 1/4 -> codes [[1,0,0,0],[-1,..]]
+    assert codes.tolist() == [[1, 0, 0, 0], [-1, 0, 0, 0]]
+    X = np.array([[2.0, 0.0, 0.0, 0.0]], np.float32)
+    xq, s = oracle.quantize_acts(X, bits=8)
+    y, acc = oracle.forward(xq, 8, s, 0, packed, gamma, epi=oracle.EPI_RELU2)
+    # acc = [127, -127]; f = fl(0.25 / fl(127/2)); y0 = fl(127*f) = 0.5 (exact here)
+    assert acc[0].tolist() == [127, -127]
+    y_lin, _ = oracle.forward(xq, 8, s, 0, packed, gamma)
+    assert y_lin[0, 1] < 0 and y[0, 1] == 0.0
+    assert y[0, 0] == np.float32(y_lin[0, 0]) * np.float32(y_lin[0, 0])
+
+
+def test_forward_at_matches_full():
+    W, X = workloads.parity_layer()
+    packed, gamma, _ = oracle.quantize_weights(W)
+    for bits in (8, 4):
+        xq, s = oracle.quantize_acts(X, bits=bits)
+        y, acc = oracle.forward(xq, bits, s, 0, packed, gamma, epi=1, y_dtype=oracle.BF16)
+        rng = np.random.default_rng(0)
+        ms = rng.integers(0, X.shape[0], 50)
+        ns = rng.integers(0, W.shape[0], 50)
+        ys, accs = oracle.forward_at(xq, bits, s, 0, packed, gamma, ms, ns, epi=1,
+                                     y_dtype=oracle.BF16)
+        assert (accs == acc[ms, ns]).all() and (ys == y[ms, ns]).all()
+
+
+def test_bf16_output_rounding_matches_torch():
+    rng = np.random.default_rng(21)
+    v = (rng.standard_normal(4096) * 10.0 ** rng.integers(-5, 5, 4096)).astype(np.float32)
+    # exact ties between two bf16 values, both parities
+    ties = np.array([0x3F808000, 0x3F818000, 0xBF808000, 0x40490000 | 0x8000], np.uint32)
+    v = np.concatenate([v, ties.view(np.float32), np.array([0.0, -0.0, 65504.0], np.float32)])
+    ours = oracle.to_bf16(v)
+    ref = torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert (ours == ref).all()
+
+
+def test_memory_reduction_figures():
+    """The a4.8 Step 4 harness sizes: in=1024, out=2048, batch 2, seq 128 -> weights
+    fp16 4096 KB -> 512 KB (87.5% cut), activations fp16 512 KB -> 128 KB (75% cut)."""
+    rng = np.random.default_rng(0)
+    W = workloads.ternary_weights(rng, 2048, 1024)
+    packed, _, _ = oracle.quantize_weights(W)
+    assert packed.nbytes == 512 * 1024 and 1 - packed.nbytes / (2048 * 1024 * 2) == 0.875
+    X = rng.standard_normal((2 * 128, 1024)).astype(np.float32)
+    xq, _ = oracle.quantize_acts(X, bits=4)
+    assert xq.nbytes == 128 * 1024 and 1 - xq.nbytes / (256 * 1024 * 2) == 0.75
+
+
+def test_oracle_rejects_bad_input():
+    with pytest.raises(oracle.OracleError):
+        oracle.quantize_weights(np.array([[np.inf, 1.0, 0.0, 0.0]], np.float32))
+    with pytest.raises(oracle.OracleError):
+        oracle.quantize_acts(np.array([[np.nan, 1.0]], np.float32))

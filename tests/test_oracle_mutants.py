@@ -1,0 +1,58 @@
+"""The pins catch plausible mistakes: each mutant below plants one mistake in a copy
+of the oracle's C source (on the CPU), and the pin suite must fail on it."""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+import tempfile
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "bitlinear_oracle.c")
+
+# (name, text in the source, replacement, occurrence index or None for all)
+MUTANTS = [
+    ("round_half_away", "rintf(", "roundf(", None),
+    ("no_weight_clip", "if (v > 1.0f) v = 1.0f;", "", None),
+    ("int8_no_eps_clamp", "float s = 127.0f / a;", "float s = 127.0f / (amax + 1e-7f);", None),
+    ("int8_divide_not_multiply", "load_elem(X, x_dtype, m * K + k) * s", "load_elem(X, x_dtype, m * K + k) / (1.0f / s)", None),
+    ("int4_scale_over_8", "float s = a / 7.0f;", "float s = a / 8.0f;", None),
+    ("dequant_swapped", "bits == 8 ? gamma / s : s * gamma", "bits == 8 ? s * gamma : gamma / s", None),
+    ("gamma_ties_away", "round_up = half && (sticky || (mant & 1u));", "round_up = half;", None),
+    ("gamma_truncated", "mant += (uint64_t)round_up;", "", None),
+    ("relu2_unrectified", "y = r * r;", "y = y * y;", None),
+    ("bias_before_rescale", "if (bias) y = y + bias[n];", "if (bias) y = y + bias[n] * f;", None),
+    ("pack_msb_first", "(uint8_t)((c + 1) << (2 * (k % 4)))", "(uint8_t)((c + 1) << (2 * (3 - k % 4)))", None),
+    ("nibble_high_first", "(uint8_t)((q & 0xF) << (4 * (k % 2)))", "(uint8_t)((q & 0xF) << (4 * (1 - k % 2)))", None),
+    ("field_offset", "return field - 1;", "return field - 2 + (field == 0);", None),
+    ("bf16_truncate", "u += 0x7FFFu + lsb;", "(void)lsb;", None),
+    ("per_tensor_uses_row_max", "float amax = tensor_max;", "float amax = 0.0f; if (gran == 1) { for (int64_t k = 0; k < K; ++k) { float t = fabsf(load_elem(X, x_dtype, m * K + k)); if (t > amax) amax = t; } }", None),
+]
+
+
+def _build_mutant(src_text: str, out_dir: str, name: str) -> str:
+    c_path = os.path.join(out_dir, name + ".c")
+    so_path = os.path.join(out_dir, name + ".so")
+    with open(c_path, "w") as f:
+        f.write(src_text)
+    subprocess.run(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fPIC", "-shared", "-w",
+                    "-o", so_path, c_path, "-lm"], check=True)
+    return so_path
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name,old,new,occ", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_mutant(name, old, new, occ):
+    src = open(SRC).read()
+    assert old in src, "mutation site vanished: " + old
+    mutated = src.replace(old, new)
+    assert mutated != src
+    with tempfile.TemporaryDirectory() as d:
+        so = _build_mutant(mutated, d, name)
+        env = dict(os.environ, ORACLE_LIB=so)
+        r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                            os.path.join(ROOT, "tests", "test_oracle.py")],
+                           cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    assert r.returncode != 0, "pin suite did not catch mutant %s:\n%s" % (name, r.stdout[-2000:])
