@@ -1,0 +1,179 @@
+/*
+ * bitlinear.h -- C ABI of the MI355X (gfx950) BitLinear forward-pass library.
+ *
+ * The library implements the BitNet b1.58 BitLinear layer in hand-written HIP:
+ * absmean ternary weight quantization into 2-bit codes, absmax int8 / int4
+ * activation quantization, the ternary x integer contraction with int32
+ * accumulation, and the rescale epilogue with optional bias and ReLU^2.
+ *
+ * Sources (cited by page title and section):
+ *   [b158] "BitNet b1.58: The 1-Bit Ternary LLM Architecture Guide",
+ *          "The Mathematical Formulation of BitLinear", equations 1-3, and the
+ *          "Implementation" listings (WeightQuantizerSTE, ActivationQuantizerSTE,
+ *          BitLinear.forward).
+ *   [2b4t] "BitNet 2B4T Guide: Scaling Native 1.58-Bit LLMs", "1. The BitLinear
+ *          Operator", "2. Squared ReLU Activation", "End-to-End PyTorch
+ *          Implementation" listing.
+ *   [a48]  "BitNet a4.8 Guide: 4-Bit Activation 1-Bit LLMs", "1. Hybrid W1.58 / A4
+ *          Quantization Function", "3. Native Hardware INT4 Tensor Core Mapping"
+ *          and its "Hardware Execution Dataflow" figure.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Pointers named as device pointers must point to device memory of the
+ *    current HIP device; the caller allocates and owns every buffer, the library
+ *    never allocates or frees memory.  Buffers must not overlap.
+ *  - Every call enqueues its kernels on `stream` (a hipStream_t passed as void*,
+ *    NULL = the null stream) and returns without synchronizing.  Results are
+ *    valid once the stream has reached that point.
+ *  - Shapes and enums are checked on the host before any HIP call; a rejected
+ *    call enqueues nothing.  A HIP launch failure (including "no device")
+ *    returns BL_EDEVICE; the HIP error text is in bitlinear_last_error().
+ *  - Calls never abort and never throw.  The library keeps no state except a
+ *    thread-local error string, so calls from different threads on different
+ *    streams do not interfere as long as their workspaces differ.
+ *  - Inputs must be finite.  With a non-finite input the outputs are unspecified
+ *    (no fault: every kernel still stays within its buffers).
+ *  - K must be a positive multiple of 16; M, N positive; N*K < 2^32.
+ *  - Device pointers must be 16-byte aligned (act_scale, gamma and bias: 4-byte).
+ *
+ * Data layouts (all row-major)
+ * ----------------------------
+ *  - W (latent weights): [N][K], N = out_features, K = in_features, fp32 or bf16
+ *    ([b158] Step 2 listing: weight is (out_features, in_features)).
+ *  - W_packed: [N][K/4] bytes.  The code c in {-1,0,+1} of W[n][k] is stored as
+ *    the 2-bit field c+1 in bits 2*(k%4)..2*(k%4)+1 of byte n*(K/4) + k/4.  The
+ *    field value 3 is never written.
+ *  - Xq, int8: [M][K] int8 codes.  Xq, int4: [M][K/2] bytes; element 2i of a row
+ *    is the low nibble of byte i, element 2i+1 the high nibble, two's complement.
+ *  - act_scale: [M] fp32 (per token) or [1] (per tensor).
+ *  - Y: [M][N], fp32, bf16 (round to nearest even from the fp32 result), or the
+ *    raw int32 accumulators (BL_I32, epilogue skipped).
+ */
+#ifndef BITLINEAR_H
+#define BITLINEAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    BL_OK = 0,
+    BL_EINVAL = 1,       /* null pointer, bad enum, eps <= 0 or not finite */
+    BL_ESHAPE = 2,       /* M, N, K out of range (K % 16 != 0, N*K >= 2^32, ...) */
+    BL_EALIGN = 3,       /* pointer not aligned as required */
+    BL_EUNSUPPORTED = 4, /* valid request this build does not implement */
+    BL_EDEVICE = 5,      /* HIP error; see bitlinear_last_error() */
+    BL_EWORKSPACE = 6    /* workspace missing or smaller than bitlinear_workspace_size() */
+} bl_status;
+
+typedef enum { BL_F32 = 0, BL_BF16 = 1, BL_I32 = 2 } bl_dtype;
+typedef enum { BL_PER_TOKEN = 0, BL_PER_TENSOR = 1 } bl_gran;
+typedef enum { BL_EPI_NONE = 0, BL_EPI_RELU2 = 1 } bl_epi;
+typedef enum {
+    BL_OP_QUANTIZE_WEIGHTS = 0,
+    BL_OP_QUANTIZE_ACTS = 1,
+    BL_OP_FORWARD = 2,
+    BL_OP_FORWARD_FUSED = 3
+} bl_op;
+
+/*
+ * Absmean ternary weight quantization and 2-bit packing.
+ * [b158] eq. 1; [2b4t] "1. The BitLinear Operator"; [a48] "1. Hybrid W1.58 / A4".
+ *
+ *   gamma = max(mean |W|, eps)      mean taken exactly, rounded once to fp32
+ *                                   (nearest, ties to even); eps as clamp(min=eps)
+ *   c     = Clip(Round(W / gamma), -1, 1)   fp32 quotient, round half to even
+ *
+ * W        device, [N][K] fp32 (w_dtype BL_F32) or bf16 (BL_BF16)
+ * eps      > 0, finite (the pages' listings use 1e-5)
+ * W_packed device, N*K/4 bytes, written in the layout above
+ * gamma    device, 1 fp32, written
+ * workspace device, >= bitlinear_workspace_size(BL_OP_QUANTIZE_WEIGHTS, ...) bytes
+ *           (exact per-exponent sums of |W|); contents on entry are ignored.
+ */
+bl_status bitlinear_quantize_weights(const void *W, bl_dtype w_dtype, int64_t N, int64_t K,
+                                     float eps, uint8_t *W_packed, float *gamma, void *workspace,
+                                     size_t workspace_bytes, void *stream);
+
+/*
+ * Absmax activation quantization, per token or per tensor.
+ *   int8 ([b158] eq. 2 with Q_b = 127; [2b4t] "1. The BitLinear Operator"):
+ *       a = max(max|x|, eps), s = 127 / a, q = Clip(Round(x * s), -128, 127)
+ *   int4 ([a48] "1. Hybrid W1.58 / A4 Quantization Function"):
+ *       a = max(max|x|, eps), s = a / 7,  q = Clip(Round(x / s), -8, 7)
+ * Every operation is one fp32 operation; Round is half to even.  max|x| runs over
+ * the token's K values (BL_PER_TOKEN) or over all M*K values (BL_PER_TENSOR).
+ *
+ * X         device, [M][K] fp32 or bf16
+ * bits      8 or 4
+ * Xq        device, M*K bytes (int8) or M*K/2 bytes (int4), layout above
+ * act_scale device, M fp32 (per token) or 1 fp32 (per tensor): receives s
+ * workspace device, >= bitlinear_workspace_size(BL_OP_QUANTIZE_ACTS, ...) bytes
+ *           (0 for per token: may be NULL; a few bytes for per tensor).
+ */
+bl_status bitlinear_quantize_acts(const void *X, bl_dtype x_dtype, int64_t M, int64_t K, int bits,
+                                  bl_gran gran, float eps, void *Xq, float *act_scale,
+                                  void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Forward on quantized activations: integer contraction, rescale, bias, ReLU^2.
+ *   acc[m][n] = sum_k q[m][k] * c[n][k]          int32 ([a48] "3. Native Hardware
+ *                                                INT4 Tensor Core Mapping")
+ *   f[m] = gamma / s[m]   (int8, [b158] eq. 3)   or   s[m] * gamma   (int4, [a48]
+ *          dataflow figure);  s[m] = act_scale[0] for per-tensor scales
+ *   y = (float)acc * f; if bias: y = y + bias[n]; if BL_EPI_RELU2: y = max(y, 0)^2
+ *          ([2b4t] "2. Squared ReLU Activation"); every step one fp32 operation.
+ *
+ * Xq, act_scale  device, as produced by bitlinear_quantize_acts with the same bits/gran
+ * W_packed, gamma device, as produced by bitlinear_quantize_weights
+ * bias      device [N] fp32, or NULL
+ * Y         device [M][N] in y_dtype (BL_F32, BL_BF16, or BL_I32 = raw acc; with
+ *           BL_I32 epi must be BL_EPI_NONE and bias NULL)
+ * workspace device, >= bitlinear_workspace_size(BL_OP_FORWARD, ...) bytes (may be 0).
+ */
+bl_status bitlinear_forward(const void *Xq, int bits, const float *act_scale, bl_gran gran,
+                            const uint8_t *W_packed, const float *gamma, const float *bias,
+                            int64_t M, int64_t N, int64_t K, bl_epi epi, void *Y,
+                            bl_dtype y_dtype, void *workspace, size_t workspace_bytes,
+                            void *stream);
+
+/*
+ * The whole layer on unquantized activations: bitlinear_quantize_acts followed by
+ * bitlinear_forward, with identical results, in as few launches as the shape
+ * allows (one launch for decode-sized M: the activation quantization runs in the
+ * prologue of the contraction kernel).  This is also the requantization between
+ * two BitLinear layers: the next layer takes this layer's Y as its X.
+ *
+ * X   device [M][K] fp32 or bf16; other arguments as in the two calls above.
+ * workspace device, >= bitlinear_workspace_size(BL_OP_FORWARD_FUSED, ...) bytes.
+ */
+bl_status bitlinear_forward_fused(const void *X, bl_dtype x_dtype, int bits, bl_gran gran,
+                                  float eps, const uint8_t *W_packed, const float *gamma,
+                                  const float *bias, int64_t M, int64_t N, int64_t K, bl_epi epi,
+                                  void *Y, bl_dtype y_dtype, void *workspace,
+                                  size_t workspace_bytes, void *stream);
+
+/* Workspace bytes a call needs for these sizes (0 if none).  bits and gran are
+ * ignored where they do not matter.  Never fails; returns 0 for invalid sizes. */
+size_t bitlinear_workspace_size(bl_op op, int64_t M, int64_t N, int64_t K, int bits,
+                                bl_gran gran);
+
+/* Static text for a status code. */
+const char *bitlinear_status_string(bl_status s);
+
+/* Detail of the last failing call on this thread ("" if none).  Valid until the
+ * next call on this thread. */
+const char *bitlinear_last_error(void);
+
+/* ABI version: major * 10000 + minor * 100 + patch. */
+int bitlinear_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BITLINEAR_H */

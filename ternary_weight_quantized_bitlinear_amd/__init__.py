@@ -1,0 +1,209 @@
+"""Python binding of the MI355X BitLinear library (libbitlinear.so, C ABI in
+include/bitlinear.h).
+
+Argument marshalling only: every step of the BitLinear forward pass runs in the
+library's HIP kernels.  torch supplies device memory and the current stream.
+There is no CPU fallback: if the library has not been built, importing works
+but every call raises :class:`BitLinearError`.
+
+The functions mirror the C entry points:
+
+* :func:`quantize_weights`  -> ``bitlinear_quantize_weights``
+* :func:`quantize_acts`     -> ``bitlinear_quantize_acts``
+* :func:`forward`           -> ``bitlinear_forward``
+* :func:`forward_fused`     -> ``bitlinear_forward_fused``
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libbitlinear.so")
+HEADER = os.path.join(os.path.dirname(PKG_DIR), "include", "bitlinear.h")
+
+# enums of include/bitlinear.h
+BL_OK, BL_EINVAL, BL_ESHAPE, BL_EALIGN, BL_EUNSUPPORTED, BL_EDEVICE, BL_EWORKSPACE = range(7)
+BL_F32, BL_BF16, BL_I32 = 0, 1, 2
+BL_PER_TOKEN, BL_PER_TENSOR = 0, 1
+BL_EPI_NONE, BL_EPI_RELU2 = 0, 1
+BL_OP_QUANTIZE_WEIGHTS, BL_OP_QUANTIZE_ACTS, BL_OP_FORWARD, BL_OP_FORWARD_FUSED = range(4)
+
+
+class BitLinearError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__("bitlinear status %d: %s" % (status, message))
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded C library (raises BitLinearError if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise BitLinearError(BL_EDEVICE, "libbitlinear.so is not built (%s); run "
+                                 "__graft_entry__.build()" % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        P, I, I64, F, SZ = (ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float,
+                            ctypes.c_size_t)
+        L.bitlinear_quantize_weights.argtypes = [P, I, I64, I64, F, P, P, P, SZ, P]
+        L.bitlinear_quantize_acts.argtypes = [P, I, I64, I64, I, I, F, P, P, P, SZ, P]
+        L.bitlinear_forward.argtypes = [P, I, P, I, P, P, P, I64, I64, I64, I, P, I, P, SZ, P]
+        L.bitlinear_forward_fused.argtypes = [P, I, I, I, F, P, P, P, I64, I64, I64, I, P, I, P,
+                                              SZ, P]
+        L.bitlinear_workspace_size.argtypes = [I, I64, I64, I64, I, I]
+        L.bitlinear_workspace_size.restype = SZ
+        L.bitlinear_status_string.argtypes = [I]
+        L.bitlinear_status_string.restype = ctypes.c_char_p
+        L.bitlinear_last_error.argtypes = []
+        L.bitlinear_last_error.restype = ctypes.c_char_p
+        L.bitlinear_version.restype = I
+        for n in ("bitlinear_quantize_weights", "bitlinear_quantize_acts", "bitlinear_forward",
+                  "bitlinear_forward_fused"):
+            getattr(L, n).restype = I
+        _lib = L
+    return _lib
+
+
+def header_functions() -> list:
+    """Names of the functions include/bitlinear.h declares."""
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(bitlinear_[a-z_]+)\s*\(", text)))
+
+
+def _check(status: int):
+    if status != BL_OK:
+        L = lib()
+        raise BitLinearError(status, "%s: %s" % (L.bitlinear_status_string(status).decode(),
+                                                 L.bitlinear_last_error().decode()))
+
+
+# ------------------------------------------------------------------ torch helpers
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return BL_F32
+    if t.dtype == torch.bfloat16:
+        return BL_BF16
+    if t.dtype == torch.int32:
+        return BL_I32
+    raise TypeError("unsupported dtype %s" % t.dtype)
+
+
+def _gran_code(gran) -> int:
+    if gran in ("token", BL_PER_TOKEN):
+        return BL_PER_TOKEN
+    if gran in ("tensor", BL_PER_TENSOR):
+        return BL_PER_TENSOR
+    raise ValueError("gran must be 'token' or 'tensor'")
+
+
+def _epi_code(epilogue) -> int:
+    if epilogue in (None, "none", BL_EPI_NONE):
+        return BL_EPI_NONE
+    if epilogue in ("relu2", BL_EPI_RELU2):
+        return BL_EPI_RELU2
+    raise ValueError("epilogue must be None or 'relu2'")
+
+
+def _stream(device, stream):
+    if stream is not None:
+        return ctypes.c_void_p(stream if isinstance(stream, int) else stream.cuda_stream)
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _workspace(nbytes, device, workspace):
+    torch = _torch()
+    if nbytes == 0:
+        return None, 0
+    if workspace is not None:
+        return workspace, workspace.numel() * workspace.element_size()
+    return torch.empty(nbytes, dtype=torch.uint8, device=device), nbytes
+
+
+def workspace_size(op: int, M: int, N: int, K: int, bits: int = 8, gran="token") -> int:
+    return lib().bitlinear_workspace_size(op, M, N, K, bits, _gran_code(gran))
+
+
+# ------------------------------------------------------------------ entry points
+
+def quantize_weights(W, eps: float = 1e-5, workspace=None, stream=None, out=None):
+    """W [N, K] fp32/bf16 (device) -> (packed uint8 [N, K/4], gamma fp32 [1])."""
+    torch = _torch()
+    N, K = W.shape
+    packed = out[0] if out else torch.empty((N, K // 4), dtype=torch.uint8, device=W.device)
+    gamma = out[1] if out else torch.empty(1, dtype=torch.float32, device=W.device)
+    ws, wsb = _workspace(workspace_size(BL_OP_QUANTIZE_WEIGHTS, 1, N, K), W.device, workspace)
+    _check(lib().bitlinear_quantize_weights(_ptr(W), _dtype_code(W), N, K, eps, _ptr(packed),
+                                            _ptr(gamma), _ptr(ws), wsb,
+                                            _stream(W.device, stream)))
+    return packed, gamma
+
+
+def quantize_acts(X, bits: int = 8, gran="token", eps: float = 1e-5, workspace=None,
+                  stream=None, out=None):
+    """X [M, K] fp32/bf16 -> (Xq int8 [M, K] or uint8 [M, K/2], act_scale fp32 [M] or [1])."""
+    torch = _torch()
+    M, K = X.shape
+    g = _gran_code(gran)
+    if out:
+        Xq, scale = out
+    else:
+        Xq = torch.empty((M, K) if bits == 8 else (M, K // 2),
+                         dtype=torch.int8 if bits == 8 else torch.uint8, device=X.device)
+        scale = torch.empty(M if g == BL_PER_TOKEN else 1, dtype=torch.float32, device=X.device)
+    ws, wsb = _workspace(workspace_size(BL_OP_QUANTIZE_ACTS, M, 1, K, bits, g), X.device,
+                         workspace)
+    _check(lib().bitlinear_quantize_acts(_ptr(X), _dtype_code(X), M, K, bits, g, eps, _ptr(Xq),
+                                         _ptr(scale), _ptr(ws), wsb, _stream(X.device, stream)))
+    return Xq, scale
+
+
+def forward(Xq, act_scale, packed, gamma, bits: int = 8, gran="token", bias=None,
+            epilogue=None, out_dtype=None, workspace=None, stream=None, out=None):
+    """Quantized activations -> Y [M, N] (fp32, bf16 or int32 accumulators)."""
+    torch = _torch()
+    M = Xq.shape[0]
+    K = Xq.shape[1] * (1 if bits == 8 else 2)
+    N = packed.shape[0]
+    g = _gran_code(gran)
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype or torch.float32, device=Xq.device)
+    ws, wsb = _workspace(workspace_size(BL_OP_FORWARD, M, N, K, bits, g), Xq.device, workspace)
+    _check(lib().bitlinear_forward(_ptr(Xq), bits, _ptr(act_scale), g, _ptr(packed), _ptr(gamma),
+                                   _ptr(bias), M, N, K, _epi_code(epilogue), _ptr(out),
+                                   _dtype_code(out), _ptr(ws), wsb, _stream(Xq.device, stream)))
+    return out
+
+
+def forward_fused(X, packed, gamma, bits: int = 8, gran="token", eps: float = 1e-5, bias=None,
+                  epilogue=None, out_dtype=None, workspace=None, stream=None, out=None):
+    """Unquantized activations X [M, K] fp32/bf16 -> Y [M, N]: quantize_acts + forward."""
+    torch = _torch()
+    M, K = X.shape
+    N = packed.shape[0]
+    g = _gran_code(gran)
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype or torch.float32, device=X.device)
+    ws, wsb = _workspace(workspace_size(BL_OP_FORWARD_FUSED, M, N, K, bits, g), X.device,
+                         workspace)
+    _check(lib().bitlinear_forward_fused(_ptr(X), _dtype_code(X), bits, g, eps, _ptr(packed),
+                                         _ptr(gamma), _ptr(bias), M, N, K, _epi_code(epilogue),
+                                         _ptr(out), _dtype_code(out), _ptr(ws), wsb,
+                                         _stream(X.device, stream)))
+    return out

@@ -1,0 +1,254 @@
+// The C ABI of the BitLinear library (declared in include/bitlinear.h).
+//
+// Every entry point validates its arguments on the host first; a rejected call
+// enqueues nothing and makes no HIP call.  Valid calls dispatch to the kernel
+// launchers of the other translation units and translate HIP failures into
+// BL_EDEVICE with the HIP error text kept per thread.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/bitlinear.h"
+#include "common.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+bl_status fail(bl_status st, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+bl_status fail(bl_status st, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+bl_status ok() {
+    g_last_error.clear();
+    return BL_OK;
+}
+
+bl_status device(hipError_t e, const char *what) {
+    if (e == hipSuccess) return ok();
+    return fail(BL_EDEVICE, "%s: %s (%s)", what, hipGetErrorString(e), hipGetErrorName(e));
+}
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Shapes: positive, K a multiple of 16, N*K < 2^32, grids within HIP limits.
+bl_status check_shape(int64_t M, int64_t N, int64_t K, const char *fn) {
+    if (M <= 0 || N <= 0 || K <= 0)
+        return fail(BL_ESHAPE, "%s: M, N, K must be positive (M=%lld N=%lld K=%lld)", fn,
+                    (long long)M, (long long)N, (long long)K);
+    if (K % 16 != 0) return fail(BL_ESHAPE, "%s: K=%lld is not a multiple of 16", fn, (long long)K);
+    if (N > (1ll << 31) || K > (1ll << 31) || N * K >= (1ll << 32))
+        return fail(BL_ESHAPE, "%s: N*K=%lld must be below 2^32", fn, (long long)(N * K));
+    if (M > 65535ll * 128 || M * K >= (1ll << 40))
+        return fail(BL_ESHAPE, "%s: M=%lld too large", fn, (long long)M);
+    return BL_OK;
+}
+
+bl_status check_eps(float eps, const char *fn) {
+    if (!(eps > 0.0f) || !std::isfinite(eps))
+        return fail(BL_EINVAL, "%s: eps must be positive and finite", fn);
+    return BL_OK;
+}
+
+bool is_xdtype(bl_dtype d) { return d == BL_F32 || d == BL_BF16; }
+
+size_t ws_fused(int64_t M, int64_t K, int bits, bl_gran gran) {
+    if (bl::gemv_supports(M, K)) return bl::ws_gemv((int)gran);
+    // quantized activations, scales and the per-tensor absmax, each 256-byte aligned
+    const size_t xq = (size_t)(bits == 8 ? M * K : M * K / 2);
+    const size_t sc = (size_t)M * sizeof(float);
+    auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
+    return up(xq) + up(sc) + up(bl::ws_quantize_acts((int)gran)) + up(bl::ws_gemm(M, 0, K));
+}
+
+#define CHECK(x)                                                                                   \
+    do {                                                                                           \
+        bl_status st_ = (x);                                                                       \
+        if (st_ != BL_OK) return st_;                                                              \
+    } while (0)
+
+}  // namespace
+
+extern "C" {
+
+int bitlinear_version(void) { return 10000; }
+
+const char *bitlinear_status_string(bl_status s) {
+    switch (s) {
+    case BL_OK: return "ok";
+    case BL_EINVAL: return "invalid argument";
+    case BL_ESHAPE: return "unsupported shape";
+    case BL_EALIGN: return "misaligned pointer";
+    case BL_EUNSUPPORTED: return "unsupported request";
+    case BL_EDEVICE: return "HIP device error";
+    case BL_EWORKSPACE: return "workspace missing or too small";
+    }
+    return "unknown status";
+}
+
+const char *bitlinear_last_error(void) { return g_last_error.c_str(); }
+
+size_t bitlinear_workspace_size(bl_op op, int64_t M, int64_t N, int64_t K, int bits,
+                                bl_gran gran) {
+    if (N <= 0 || K <= 0 || (op != BL_OP_QUANTIZE_WEIGHTS && M <= 0)) return 0;
+    switch (op) {
+    case BL_OP_QUANTIZE_WEIGHTS: return bl::ws_quantize_weights();
+    case BL_OP_QUANTIZE_ACTS: return bl::ws_quantize_acts((int)gran);
+    case BL_OP_FORWARD:
+        return bl::gemv_supports(M, K) ? bl::ws_gemv((int)gran) : bl::ws_gemm(M, N, K);
+    case BL_OP_FORWARD_FUSED:
+        return (bits == 8 || bits == 4) ? ws_fused(M, K, bits, gran) : 0;
+    }
+    return 0;
+}
+
+bl_status bitlinear_quantize_weights(const void *W, bl_dtype w_dtype, int64_t N, int64_t K,
+                                     float eps, uint8_t *W_packed, float *gamma, void *workspace,
+                                     size_t workspace_bytes, void *stream) {
+    static const char fn[] = "bitlinear_quantize_weights";
+    if (!W || !W_packed || !gamma) return fail(BL_EINVAL, "%s: null pointer", fn);
+    if (!is_xdtype(w_dtype)) return fail(BL_EINVAL, "%s: w_dtype must be BL_F32 or BL_BF16", fn);
+    CHECK(check_shape(1, N, K, fn));
+    CHECK(check_eps(eps, fn));
+    if (!aligned(W, 16) || !aligned(W_packed, 16) || !aligned(gamma, 4))
+        return fail(BL_EALIGN, "%s: W and W_packed need 16-byte, gamma 4-byte alignment", fn);
+    const size_t need = bl::ws_quantize_weights();
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 16))
+        return fail(BL_EWORKSPACE, "%s: need %zu bytes of 16-byte aligned workspace", fn, need);
+    (void)hipGetLastError();
+    return device(bl::launch_quantize_weights(W, w_dtype == BL_BF16, N, K, eps, W_packed, gamma,
+                                              workspace, (hipStream_t)stream),
+                  fn);
+}
+
+bl_status bitlinear_quantize_acts(const void *X, bl_dtype x_dtype, int64_t M, int64_t K, int bits,
+                                  bl_gran gran, float eps, void *Xq, float *act_scale,
+                                  void *workspace, size_t workspace_bytes, void *stream) {
+    static const char fn[] = "bitlinear_quantize_acts";
+    if (!X || !Xq || !act_scale) return fail(BL_EINVAL, "%s: null pointer", fn);
+    if (!is_xdtype(x_dtype)) return fail(BL_EINVAL, "%s: x_dtype must be BL_F32 or BL_BF16", fn);
+    if (bits != 8 && bits != 4) return fail(BL_EINVAL, "%s: bits must be 8 or 4", fn);
+    if (gran != BL_PER_TOKEN && gran != BL_PER_TENSOR) return fail(BL_EINVAL, "%s: bad gran", fn);
+    CHECK(check_shape(M, 1, K, fn));
+    CHECK(check_eps(eps, fn));
+    if (!aligned(X, 16) || !aligned(Xq, 16) || !aligned(act_scale, 4))
+        return fail(BL_EALIGN, "%s: X and Xq need 16-byte, act_scale 4-byte alignment", fn);
+    const size_t need = bl::ws_quantize_acts((int)gran);
+    if (need && (!workspace || workspace_bytes < need || !aligned(workspace, 16)))
+        return fail(BL_EWORKSPACE, "%s: need %zu bytes of 16-byte aligned workspace", fn, need);
+    (void)hipGetLastError();
+    return device(bl::launch_quantize_acts(X, x_dtype == BL_BF16, M, K, bits, (int)gran, eps, Xq,
+                                           act_scale, workspace, (hipStream_t)stream),
+                  fn);
+}
+
+static bl_status check_forward_common(const char *fn, int bits, bl_gran gran,
+                                      const uint8_t *W_packed, const float *gamma,
+                                      const float *bias, int64_t M, int64_t N, int64_t K,
+                                      bl_epi epi, void *Y, bl_dtype y_dtype) {
+    if (!W_packed || !gamma || !Y) return fail(BL_EINVAL, "%s: null pointer", fn);
+    if (bits != 8 && bits != 4) return fail(BL_EINVAL, "%s: bits must be 8 or 4", fn);
+    if (gran != BL_PER_TOKEN && gran != BL_PER_TENSOR) return fail(BL_EINVAL, "%s: bad gran", fn);
+    if (epi != BL_EPI_NONE && epi != BL_EPI_RELU2) return fail(BL_EINVAL, "%s: bad epi", fn);
+    if (y_dtype != BL_F32 && y_dtype != BL_BF16 && y_dtype != BL_I32)
+        return fail(BL_EINVAL, "%s: bad y_dtype", fn);
+    if (y_dtype == BL_I32 && (epi != BL_EPI_NONE || bias))
+        return fail(BL_EINVAL, "%s: BL_I32 output takes no epilogue and no bias", fn);
+    CHECK(check_shape(M, N, K, fn));
+    if (!aligned(W_packed, 16) || !aligned(Y, 16) || !aligned(gamma, 4) ||
+        (bias && !aligned(bias, 4)))
+        return fail(BL_EALIGN, "%s: W_packed and Y need 16-byte, gamma/bias 4-byte alignment",
+                    fn);
+    return BL_OK;
+}
+
+static bl::FwdArgs make_args(const void *x, int x_bf16, int bits, const float *act_scale,
+                             bl_gran gran, float eps, const uint8_t *W_packed, const float *gamma,
+                             const float *bias, int64_t M, int64_t N, int64_t K, bl_epi epi,
+                             void *Y, bl_dtype y_dtype) {
+    bl::FwdArgs a;
+    a.xq = x;
+    a.x_raw_bf16 = x_bf16;
+    a.bits = bits;
+    a.act_scale = act_scale;
+    a.gran = (int)gran;
+    a.eps = eps;
+    a.w = W_packed;
+    a.gamma = gamma;
+    a.bias = bias;
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    a.epi = (int)epi;
+    a.y = Y;
+    a.y_dtype = (int)y_dtype;
+    return a;
+}
+
+bl_status bitlinear_forward(const void *Xq, int bits, const float *act_scale, bl_gran gran,
+                            const uint8_t *W_packed, const float *gamma, const float *bias,
+                            int64_t M, int64_t N, int64_t K, bl_epi epi, void *Y,
+                            bl_dtype y_dtype, void *workspace, size_t workspace_bytes,
+                            void *stream) {
+    static const char fn[] = "bitlinear_forward";
+    if (!Xq || !act_scale) return fail(BL_EINVAL, "%s: null pointer", fn);
+    CHECK(check_forward_common(fn, bits, gran, W_packed, gamma, bias, M, N, K, epi, Y, y_dtype));
+    if (!aligned(Xq, 16) || !aligned(act_scale, 4))
+        return fail(BL_EALIGN, "%s: Xq needs 16-byte, act_scale 4-byte alignment", fn);
+    const size_t need = bitlinear_workspace_size(BL_OP_FORWARD, M, N, K, bits, gran);
+    if (need && (!workspace || workspace_bytes < need || !aligned(workspace, 16)))
+        return fail(BL_EWORKSPACE, "%s: need %zu bytes of 16-byte aligned workspace", fn, need);
+    const bl::FwdArgs a = make_args(Xq, 0, bits, act_scale, gran, 0.0f, W_packed, gamma, bias, M,
+                                    N, K, epi, Y, y_dtype);
+    (void)hipGetLastError();
+    hipError_t e = bl::gemv_supports(M, K) ? bl::launch_gemv(a, false, workspace, (hipStream_t)stream)
+                                           : bl::launch_gemm(a, workspace, (hipStream_t)stream);
+    return device(e, fn);
+}
+
+bl_status bitlinear_forward_fused(const void *X, bl_dtype x_dtype, int bits, bl_gran gran,
+                                  float eps, const uint8_t *W_packed, const float *gamma,
+                                  const float *bias, int64_t M, int64_t N, int64_t K, bl_epi epi,
+                                  void *Y, bl_dtype y_dtype, void *workspace,
+                                  size_t workspace_bytes, void *stream) {
+    static const char fn[] = "bitlinear_forward_fused";
+    if (!X) return fail(BL_EINVAL, "%s: null pointer", fn);
+    if (!is_xdtype(x_dtype)) return fail(BL_EINVAL, "%s: x_dtype must be BL_F32 or BL_BF16", fn);
+    CHECK(check_forward_common(fn, bits, gran, W_packed, gamma, bias, M, N, K, epi, Y, y_dtype));
+    CHECK(check_eps(eps, fn));
+    if (!aligned(X, 16)) return fail(BL_EALIGN, "%s: X needs 16-byte alignment", fn);
+    const size_t need = ws_fused(M, K, bits, gran);
+    if (need && (!workspace || workspace_bytes < need || !aligned(workspace, 256)))
+        return fail(BL_EWORKSPACE, "%s: need %zu bytes of 256-byte aligned workspace", fn, need);
+    hipStream_t s = (hipStream_t)stream;
+    (void)hipGetLastError();
+    if (bl::gemv_supports(M, K)) {
+        const bl::FwdArgs a = make_args(X, x_dtype == BL_BF16, bits, nullptr, gran, eps, W_packed,
+                                        gamma, bias, M, N, K, epi, Y, y_dtype);
+        return device(bl::launch_gemv(a, true, workspace, s), fn);
+    }
+    // quantize into the workspace, then the GEMM on the codes
+    auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
+    uint8_t *base = static_cast<uint8_t *>(workspace);
+    void *xq = base;
+    float *scale = reinterpret_cast<float *>(base + up((size_t)(bits == 8 ? M * K : M * K / 2)));
+    void *aq_ws = reinterpret_cast<uint8_t *>(scale) + up((size_t)M * sizeof(float));
+    void *gemm_ws = static_cast<uint8_t *>(aq_ws) + up(bl::ws_quantize_acts((int)gran));
+    hipError_t e = bl::launch_quantize_acts(X, x_dtype == BL_BF16, M, K, bits, (int)gran, eps, xq,
+                                            scale, aq_ws, s);
+    if (e != hipSuccess) return device(e, fn);
+    const bl::FwdArgs a = make_args(xq, 0, bits, scale, gran, eps, W_packed, gamma, bias, M, N, K,
+                                    epi, Y, y_dtype);
+    return device(bl::launch_gemm(a, gemm_ws, s), fn);
+}
+
+}  // extern "C"

@@ -1,0 +1,150 @@
+// Absmax activation quantization, int8 or int4, per token or per tensor.
+//
+// int8: "BitNet b1.58: The 1-Bit Ternary LLM Architecture Guide", "The
+// Mathematical Formulation of BitLinear", eq. 2 (Q_b = 127), with the [-128, 127]
+// clip of "BitNet 2B4T Guide", "1. The BitLinear Operator":
+//     s = 127 / max(a, eps),  q = Clip(Round(x * s), -128, 127)
+// int4: "BitNet a4.8 Guide", "1. Hybrid W1.58 / A4 Quantization Function":
+//     s = max(a, eps) / 7,    q = Clip(Round(x / s), -8, 7), two nibbles per byte
+// a is max |x| over the token (per token) or over the tensor (per tensor).  Each
+// step is one correctly rounded fp32 operation and Round is half to even
+// (v_rndne_f32), so the codes are exactly those of the definition.
+//
+// Per token: one 256-thread block per row; pass 1 reduces the row's absmax (wave
+// shuffles, then LDS across the 4 waves), pass 2 re-reads the row (an L2 hit) and
+// writes the codes.  Per tensor: a grid-wide absmax into the workspace (|x| is
+// non-negative, so its fp32 bits order like unsigned integers and atomicMax on the
+// bits is the float max), then the same pass 2 with that shared absmax.
+#include "common.hpp"
+
+namespace bl {
+namespace {
+
+constexpr int kAqThreads = 256;
+
+__device__ __forceinline__ float block_max(float v, float *red) {
+    v = wave_max(v);
+    const int wid = threadIdx.x / kWave;
+    if ((threadIdx.x & (kWave - 1)) == 0) red[wid] = v;
+    __syncthreads();
+    float r = red[0];
+#pragma unroll
+    for (int i = 1; i < kAqThreads / kWave; ++i) r = fmaxf(r, red[i]);
+    return r;
+}
+
+
+template <bool kBf16, int kBits, bool kTensor>
+__global__ void __launch_bounds__(kAqThreads)
+aq_rows(const void *__restrict__ x, int64_t K, float eps, const uint32_t *__restrict__ tensor_amax,
+        void *__restrict__ xq, float *__restrict__ scale) {
+    __shared__ float red[kAqThreads / kWave];
+    const int64_t m = blockIdx.x;
+    const void *row = kBf16 ? (const void *)(static_cast<const uint16_t *>(x) + m * K)
+                            : (const void *)(static_cast<const float *>(x) + m * K);
+    const int64_t n8 = K / 8;
+    float amax;
+    if (kTensor) {
+        amax = __uint_as_float(*tensor_amax);
+    } else {
+        float mx = 0.0f;
+        for (int64_t u = threadIdx.x; u < n8; u += kAqThreads) {
+            float v[8];
+            load8<kBf16>(row, u * 8, v);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) mx = fmaxf(mx, fabsf(v[j]));
+        }
+        amax = block_max(mx, red);
+    }
+    const float a = fmaxf(amax, eps);
+    const float s = kBits == 8 ? 127.0f / a : a / 7.0f;
+    if (threadIdx.x == 0 && (!kTensor || m == 0)) scale[kTensor ? 0 : m] = s;
+    for (int64_t u = threadIdx.x; u < n8; u += kAqThreads) {
+        float v[8];
+        load8<kBf16>(row, u * 8, v);
+        if (kBits == 8) {
+            uint2 o;
+            o.x = q8(v[0], s) | (q8(v[1], s) << 8) | (q8(v[2], s) << 16) | (q8(v[3], s) << 24);
+            o.y = q8(v[4], s) | (q8(v[5], s) << 8) | (q8(v[6], s) << 16) | (q8(v[7], s) << 24);
+            reinterpret_cast<uint2 *>(static_cast<int8_t *>(xq) + m * K)[u] = o;
+        } else {
+            uint32_t o = 0;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) o |= q4(v[j], s) << (4 * j);
+            reinterpret_cast<uint32_t *>(static_cast<uint8_t *>(xq) + m * (K / 2))[u] = o;
+        }
+    }
+}
+
+template <bool kBf16>
+__global__ void __launch_bounds__(kAqThreads)
+aq_tensor_amax(const void *__restrict__ x, int64_t n8, uint32_t *__restrict__ amax_bits) {
+    __shared__ float red[kAqThreads / kWave];
+    float mx = 0.0f;
+    const int64_t stride = (int64_t)gridDim.x * kAqThreads;
+    for (int64_t u = (int64_t)blockIdx.x * kAqThreads + threadIdx.x; u < n8; u += stride) {
+        float v[8];
+        load8<kBf16>(x, u * 8, v);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) mx = fmaxf(mx, fabsf(v[j]));
+    }
+    mx = block_max(mx, red);
+    if (threadIdx.x == 0) atomicMax(amax_bits, __float_as_uint(mx));
+}
+
+__global__ void zero_u32(uint32_t *p, int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = 0u;
+}
+
+template <bool kBf16, int kBits, bool kTensor>
+void launch_rows(const void *x, int64_t M, int64_t K, float eps, const uint32_t *amax, void *xq,
+                 float *scale, hipStream_t s) {
+    hipLaunchKernelGGL((aq_rows<kBf16, kBits, kTensor>), dim3((unsigned)M), dim3(kAqThreads), 0,
+                       s, x, K, eps, amax, xq, scale);
+}
+
+}  // namespace
+
+hipError_t launch_zero_u32(uint32_t *p, int64_t n, hipStream_t s) {
+    int g = (int)((n + 255) / 256);
+    if (g > 4096) g = 4096;
+    if (g < 1) g = 1;
+    hipLaunchKernelGGL(zero_u32, dim3(g), dim3(256), 0, s, p, n);
+    return hipGetLastError();
+}
+
+size_t ws_quantize_acts(int gran) { return gran == 1 ? 256 : 0; }
+
+hipError_t launch_quantize_acts(const void *x, int x_bf16, int64_t M, int64_t K, int bits,
+                                int gran, float eps, void *xq, float *scale, void *ws,
+                                hipStream_t s) {
+    uint32_t *amax = static_cast<uint32_t *>(ws);
+    if (gran == 1) {
+        launch_zero_u32(amax, 1, s);
+        const int64_t n8 = M * K / 8;
+        int g = (int)((n8 + kAqThreads * 4 - 1) / (kAqThreads * 4));
+        if (g > 2048) g = 2048;
+        if (g < 1) g = 1;
+        if (x_bf16)
+            hipLaunchKernelGGL(aq_tensor_amax<true>, dim3(g), dim3(kAqThreads), 0, s, x, n8, amax);
+        else
+            hipLaunchKernelGGL(aq_tensor_amax<false>, dim3(g), dim3(kAqThreads), 0, s, x, n8, amax);
+    }
+    const bool t = gran == 1;
+    if (x_bf16) {
+        if (bits == 8) t ? launch_rows<true, 8, true>(x, M, K, eps, amax, xq, scale, s)
+                         : launch_rows<true, 8, false>(x, M, K, eps, amax, xq, scale, s);
+        else t ? launch_rows<true, 4, true>(x, M, K, eps, amax, xq, scale, s)
+               : launch_rows<true, 4, false>(x, M, K, eps, amax, xq, scale, s);
+    } else {
+        if (bits == 8) t ? launch_rows<false, 8, true>(x, M, K, eps, amax, xq, scale, s)
+                         : launch_rows<false, 8, false>(x, M, K, eps, amax, xq, scale, s);
+        else t ? launch_rows<false, 4, true>(x, M, K, eps, amax, xq, scale, s)
+               : launch_rows<false, 4, false>(x, M, K, eps, amax, xq, scale, s);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace bl

@@ -1,0 +1,147 @@
+// Shared device helpers and internal launcher declarations of the BitLinear
+// library (gfx950, wave64).  Nothing here is part of the public C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+namespace bl {
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- bf16
+// bf16 is the upper half of an fp32 word: widening is a shift.
+__device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xFFFF0000u); }
+
+// fp32 -> bf16, round to nearest, ties to even; NaN stays a (quiet) NaN.
+__device__ __forceinline__ uint32_t to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+// ---------------------------------------------------------------- wave reductions
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+    return v;
+}
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+
+// ---------------------------------------------------------------- 2-bit ternary fields
+// A packed dword holds the fields (c+1) of 16 consecutive k, field k in bits 2k.
+// Shifting by 2i and masking every byte leaves, in byte j, the field of k = 4j + i:
+// the four results hold the 16 fields in the order (4j + i) for dword i, byte j.
+// Activation bytes are laid out in the same order ("k-interleaved") wherever they
+// meet these fields, so every product pairs the right (x, c).
+__device__ __forceinline__ uint32_t fields(uint32_t w, int i) {
+    return (w >> (2 * i)) & 0x03030303u;
+}
+// fields {0,1,2} -> signed codes {-1,0,+1} as bytes (0xFF, 0x00, 0x01), one v_perm:
+// each selector byte (0..2) picks a byte of the table 0x000100FF.
+__device__ __forceinline__ uint32_t codes_from_fields(uint32_t f) {
+    return __builtin_amdgcn_perm(0u, 0x000100FFu, f);
+}
+
+// 4x4 byte transpose of 16 natural-order activation bytes (a[d] byte j = x[4d + j])
+// into the k-interleaved order (r[i] byte j = x[4j + i]).
+__device__ __forceinline__ void interleave16(const uint32_t a[4], uint32_t r[4]) {
+    // stage 1: pairs of dwords -> (a0.b0 a1.b0 a0.b2 a1.b2), (a0.b1 a1.b1 a0.b3 a1.b3)
+    uint32_t t0 = __builtin_amdgcn_perm(a[1], a[0], 0x06020400u);
+    uint32_t t1 = __builtin_amdgcn_perm(a[1], a[0], 0x07030501u);
+    uint32_t t2 = __builtin_amdgcn_perm(a[3], a[2], 0x06020400u);
+    uint32_t t3 = __builtin_amdgcn_perm(a[3], a[2], 0x07030501u);
+    // stage 2: t0 = (a0.b0 a1.b0 a0.b2 a1.b2), t2 = (a2.b0 a3.b0 a2.b2 a3.b2)
+    r[0] = __builtin_amdgcn_perm(t2, t0, 0x05040100u);  // a0.b0 a1.b0 a2.b0 a3.b0
+    r[2] = __builtin_amdgcn_perm(t2, t0, 0x07060302u);  // a0.b2 a1.b2 a2.b2 a3.b2
+    r[1] = __builtin_amdgcn_perm(t3, t1, 0x05040100u);  // a0.b1 a1.b1 a2.b1 a3.b1
+    r[3] = __builtin_amdgcn_perm(t3, t1, 0x07060302u);  // a0.b3 a1.b3 a2.b3 a3.b3
+}
+
+// int4 nibbles (element 2i low) -> int8 bytes, 8 elements per input dword.
+__device__ __forceinline__ void nibbles_to_i8(uint32_t v, uint32_t out[2]) {
+    // sign-extend each nibble: (n ^ 8) - 8 per byte, done on spread nibbles
+    uint32_t lo = v & 0x0F0F0F0Fu;         // elements 0,2,4,6 in bytes 0..3
+    uint32_t hi = (v >> 4) & 0x0F0F0F0Fu;  // elements 1,3,5,7
+    // bytes are in [0,15]; map n -> n - 16*(n>=8) per byte without borrows:
+    lo = ((lo ^ 0x08080808u) + 0x78787878u) ^ 0x80808080u;
+    hi = ((hi ^ 0x08080808u) + 0x78787878u) ^ 0x80808080u;
+    // interleave back to natural order: out[0] = e0 e1 e2 e3, out[1] = e4 e5 e6 e7
+    out[0] = __builtin_amdgcn_perm(hi, lo, 0x05010400u);
+    out[1] = __builtin_amdgcn_perm(hi, lo, 0x07030602u);
+}
+
+// ---------------------------------------------------------------- activation codes
+// 8 consecutive elements of a row as fp32 (one 16-byte bf16 load or two fp32 loads)
+template <bool kBf16>
+__device__ __forceinline__ void load8(const void *x, int64_t elem, float v[8]) {
+    if (kBf16) {
+        uint4 q = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(x) + elem);
+        v[0] = bf16_lo(q.x); v[1] = bf16_hi(q.x); v[2] = bf16_lo(q.y); v[3] = bf16_hi(q.y);
+        v[4] = bf16_lo(q.z); v[5] = bf16_hi(q.z); v[6] = bf16_lo(q.w); v[7] = bf16_hi(q.w);
+    } else {
+        const float4 *p = reinterpret_cast<const float4 *>(static_cast<const float *>(x) + elem);
+        float4 a = p[0], b = p[1];
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    }
+}
+
+__device__ __forceinline__ uint32_t q8(float x, float s) {
+    float v = __builtin_rintf(x * s);
+    v = fminf(fmaxf(v, -128.0f), 127.0f);
+    return (uint32_t)((int)v) & 0xFFu;
+}
+__device__ __forceinline__ uint32_t q4(float x, float s) {
+    float v = __builtin_rintf(x / s);
+    v = fminf(fmaxf(v, -8.0f), 7.0f);
+    return (uint32_t)((int)v) & 0xFu;
+}
+
+}  // namespace bl
+
+// ---------------------------------------------------------------- launchers
+// Implemented in the kernel translation units; called by the C ABI layer after
+// all arguments have been validated.  They return the HIP launch status.
+namespace bl {
+
+struct FwdArgs {
+    const void *xq;        // quantized activations (forward) or raw X (fused)
+    int x_raw_bf16;        // fused: 1 = X is bf16, 0 = fp32
+    int bits;              // 8 or 4
+    const float *act_scale;
+    int gran;              // 0 per token, 1 per tensor
+    float eps;             // fused only
+    const uint8_t *w;
+    const float *gamma;
+    const float *bias;
+    int64_t M, N, K;
+    int epi;               // 0 none, 1 relu2
+    void *y;
+    int y_dtype;           // 0 f32, 1 bf16, 2 i32
+};
+
+hipError_t launch_zero_u32(uint32_t *p, int64_t n, hipStream_t s);
+hipError_t launch_quantize_weights(const void *w, int w_bf16, int64_t N, int64_t K, float eps,
+                                   uint8_t *packed, float *gamma, void *ws, hipStream_t s);
+size_t ws_quantize_weights();
+hipError_t launch_quantize_acts(const void *x, int x_bf16, int64_t M, int64_t K, int bits,
+                                int gran, float eps, void *xq, float *scale, void *ws,
+                                hipStream_t s);
+size_t ws_quantize_acts(int gran);
+// decode-sized M: one launch, optional fused activation quantization prologue
+bool gemv_supports(int64_t M, int64_t K);
+hipError_t launch_gemv(const FwdArgs &a, bool fused, void *ws, hipStream_t s);
+size_t ws_gemv(int gran);
+// prefill-sized M: int8 MFMA GEMM on quantized activations
+hipError_t launch_gemm(const FwdArgs &a, void *ws, hipStream_t s);
+size_t ws_gemm(int64_t M, int64_t N, int64_t K);
+
+}  // namespace bl

@@ -1,0 +1,147 @@
+"""The C-ABI library on the host: it loads, exports every function the header
+declares, and rejects bad arguments before any HIP call.  No GPU needed."""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import pytest
+
+import ternary_weight_quantized_bitlinear_amd as bl
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(bl.LIB_PATH):
+        from ternary_weight_quantized_bitlinear_amd import build
+        build.build()
+    return bl.lib()
+
+
+def test_exports_every_header_function(L):
+    names = bl.header_functions()
+    assert set(names) == {
+        "bitlinear_quantize_weights", "bitlinear_quantize_acts", "bitlinear_forward",
+        "bitlinear_forward_fused", "bitlinear_workspace_size", "bitlinear_status_string",
+        "bitlinear_last_error", "bitlinear_version"}
+    for n in names:
+        assert hasattr(L, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", bl.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    assert set(names) <= exported
+
+
+def test_library_is_gfx950_code():
+    # the library's own offload bundle names its target
+    data = open(bl.LIB_PATH, "rb").read()
+    assert b"amdgcn-amd-amdhsa--gfx950" in data
+
+
+def test_status_strings_and_version(L):
+    for s in range(7):
+        assert L.bitlinear_status_string(s).decode()
+    assert L.bitlinear_version() >= 10000
+
+
+def test_workspace_sizes(L):
+    assert L.bitlinear_workspace_size(bl.BL_OP_QUANTIZE_WEIGHTS, 1, 512, 256, 8, 0) >= 256 * 8
+    assert L.bitlinear_workspace_size(bl.BL_OP_QUANTIZE_ACTS, 8, 1, 256, 8, 0) == 0
+    assert L.bitlinear_workspace_size(bl.BL_OP_QUANTIZE_ACTS, 8, 1, 256, 8, 1) >= 4
+    # decode-sized fused forward needs no workspace; prefill-sized holds the codes
+    assert L.bitlinear_workspace_size(bl.BL_OP_FORWARD_FUSED, 1, 6912, 2560, 8, 0) == 0
+    assert L.bitlinear_workspace_size(bl.BL_OP_FORWARD_FUSED, 2048, 6912, 2560, 8, 0) >= 2048 * 2560
+    assert L.bitlinear_workspace_size(bl.BL_OP_FORWARD_FUSED, 2048, 6912, 2560, 4, 0) >= 2048 * 1280
+    assert L.bitlinear_workspace_size(bl.BL_OP_FORWARD, -1, 6912, 2560, 8, 0) == 0
+
+
+# Fake device addresses: validation must reject the call before touching them.
+A = 0x10000
+P = ctypes.c_void_p
+
+
+def _fwd(L, **kw):
+    a = dict(Xq=P(A), bits=8, scale=P(A), gran=0, W=P(A), gamma=P(A), bias=None, M=8, N=512,
+             K=256, epi=0, Y=P(A), ydt=0, ws=None, wsb=0, stream=None)
+    a.update(kw)
+    return L.bitlinear_forward(a["Xq"], a["bits"], a["scale"], a["gran"], a["W"], a["gamma"],
+                               a["bias"], a["M"], a["N"], a["K"], a["epi"], a["Y"], a["ydt"],
+                               a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Xq=None), bl.BL_EINVAL),
+    (dict(W=None), bl.BL_EINVAL),
+    (dict(Y=None), bl.BL_EINVAL),
+    (dict(bits=2), bl.BL_EINVAL),
+    (dict(gran=7), bl.BL_EINVAL),
+    (dict(epi=3), bl.BL_EINVAL),
+    (dict(ydt=9), bl.BL_EINVAL),
+    (dict(ydt=2, epi=1), bl.BL_EINVAL),
+    (dict(ydt=2, bias=P(A)), bl.BL_EINVAL),
+    (dict(K=100), bl.BL_ESHAPE),
+    (dict(K=0), bl.BL_ESHAPE),
+    (dict(M=0), bl.BL_ESHAPE),
+    (dict(N=-4), bl.BL_ESHAPE),
+    (dict(N=1 << 20, K=1 << 12), bl.BL_ESHAPE),
+    (dict(W=P(A + 4)), bl.BL_EALIGN),
+    (dict(Xq=P(A + 8)), bl.BL_EALIGN),
+    (dict(Y=P(A + 2)), bl.BL_EALIGN),
+    (dict(gamma=P(A + 2)), bl.BL_EALIGN),
+])
+def test_forward_rejects(L, kw, status):
+    assert _fwd(L, **kw) == status
+    assert L.bitlinear_last_error().decode().startswith("bitlinear_forward")
+
+
+def test_quantize_weights_rejects(L):
+    f = L.bitlinear_quantize_weights
+    assert f(P(A), 0, 512, 256, 1e-5, P(A), P(A), None, 0, None) == bl.BL_EWORKSPACE
+    assert f(P(A), 0, 512, 256, 1e-5, P(A), P(A), P(A), 8, None) == bl.BL_EWORKSPACE
+    assert f(P(A), 0, 512, 256, 0.0, P(A), P(A), P(A), 1 << 20, None) == bl.BL_EINVAL
+    assert f(P(A), 0, 512, 256, float("nan"), P(A), P(A), P(A), 1 << 20, None) == bl.BL_EINVAL
+    assert f(P(A), 2, 512, 256, 1e-5, P(A), P(A), P(A), 1 << 20, None) == bl.BL_EINVAL
+    assert f(P(A), 0, 512, 250, 1e-5, P(A), P(A), P(A), 1 << 20, None) == bl.BL_ESHAPE
+    assert f(None, 0, 512, 256, 1e-5, P(A), P(A), P(A), 1 << 20, None) == bl.BL_EINVAL
+
+
+def test_quantize_acts_rejects(L):
+    f = L.bitlinear_quantize_acts
+    assert f(P(A), 0, 8, 256, 3, 0, 1e-5, P(A), P(A), None, 0, None) == bl.BL_EINVAL
+    assert f(P(A), 0, 8, 256, 8, 5, 1e-5, P(A), P(A), None, 0, None) == bl.BL_EINVAL
+    assert f(P(A), 0, 8, 256, 8, 1, 1e-5, P(A), P(A), None, 0, None) == bl.BL_EWORKSPACE
+    assert f(P(A), 0, 8, 24, 8, 0, 1e-5, P(A), P(A), None, 0, None) == bl.BL_ESHAPE
+    assert f(P(A), 0, 8, 256, 8, 0, -1.0, P(A), P(A), None, 0, None) == bl.BL_EINVAL
+
+
+def test_forward_fused_rejects(L):
+    f = L.bitlinear_forward_fused
+    # prefill-sized fused call needs a workspace for the codes
+    assert f(P(A), 1, 8, 0, 1e-5, P(A), P(A), None, 2048, 6912, 2560, 0, P(A), 1, None, 0,
+             None) == bl.BL_EWORKSPACE
+    assert f(P(A), 2, 8, 0, 1e-5, P(A), P(A), None, 1, 6912, 2560, 0, P(A), 1, None, 0,
+             None) == bl.BL_EINVAL
+
+
+def _gpu_visible() -> bool:
+    try:
+        import torch
+        return torch.cuda.device_count() > 0
+    except Exception:
+        return False
+
+
+def test_valid_call_without_device_reports_edevice(L):
+    if _gpu_visible():
+        pytest.skip("a GPU is visible: this test needs a host with no device")
+    st = _fwd(L)
+    assert st == bl.BL_EDEVICE
+    assert L.bitlinear_last_error().decode()
+
+
+def test_binding_raises_loudly_without_library(monkeypatch):
+    monkeypatch.setattr(bl, "_lib", None)
+    monkeypatch.setattr(bl, "LIB_PATH", "/nonexistent/libbitlinear.so")
+    with pytest.raises(bl.BitLinearError):
+        bl.lib()

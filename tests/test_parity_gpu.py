@@ -1,0 +1,285 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle, element by
+element, on the same seeded inputs.
+
+Bar: packed weights, gamma, activation codes, scales and int32 accumulators
+bit-identical; outputs within 1e-5 relative in fp32 / one ulp in bf16 and, since
+both sides fix the same fp32 operation order, bit-identical too.
+Small shapes are compared in full; the full-size shapes (2B decode/prefill, 70B
+layer) on sampled outputs the oracle computes one by one.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+import ternary_weight_quantized_bitlinear_amd as bl
+from gpu_util import (assert_same_bytes, assert_y_matches, bits32, sample_positions, say,
+                      to_dev, to_host)
+
+pytestmark = pytest.mark.gpu
+
+YD = {"f32": (torch.float32, oracle.F32), "bf16": (torch.bfloat16, oracle.BF16),
+      "i32": (torch.int32, None)}
+
+
+def _weights_case(kind, n, k, seed=0):
+    rng = np.random.default_rng([seed, n, k])
+    if kind == "gauss":
+        return (np.float32(0.02) * rng.standard_normal((n, k), dtype=np.float32)).astype(np.float32)
+    if kind == "ternary":
+        return workloads.ternary_weights(rng, n, k)
+    if kind == "zeros":
+        return np.zeros((n, k), np.float32)
+    if kind == "tiny":  # mean far below eps -> gamma = eps, codes mostly 0
+        return (1e-9 * rng.standard_normal((n, k))).astype(np.float32)
+    if kind == "halfgrid":  # many exact ties at gamma/2 multiples
+        return (rng.integers(-4, 5, (n, k)) * 0.25).astype(np.float32)
+    raise ValueError(kind)
+
+
+# ---------------------------------------------------------------- weights
+
+@pytest.mark.parametrize("kind,n,k,dtype", [
+    ("gauss", 512, 256, "f32"),
+    ("gauss", 512, 256, "bf16"),
+    ("gauss", 1, 16, "f32"),
+    ("gauss", 3, 48, "f32"),
+    ("gauss", 37, 80, "bf16"),
+    ("zeros", 16, 64, "f32"),
+    ("tiny", 33, 32, "f32"),
+    ("halfgrid", 64, 128, "f32"),
+    ("ternary", 6912, 2560, "f32"),
+    ("ternary", 2560, 6912, "f32"),
+    ("gauss", 7680, 2560, "bf16"),
+    ("gauss", 2560, 6912, "f32"),
+])
+def test_quantize_weights_parity(kind, n, k, dtype):
+    W = _weights_case(kind, n, k)
+    Win = workloads.to_bf16_bits(W) if dtype == "bf16" else W
+    say("quantize_weights", kind, n, k, dtype)
+    packed, gamma = bl.quantize_weights(to_dev(Win))
+    torch.cuda.synchronize()
+    p_ref, g_ref, _ = oracle.quantize_weights(Win)
+    assert bits32(to_host(gamma))[0] == bits32(np.array([g_ref]))[0], "gamma differs"
+    assert_same_bytes(to_host(packed), p_ref, "packed weights")
+
+
+def test_quantize_weights_70b_layer():
+    codes, _ = workloads.layer_70b(m=1)
+    W = codes.astype(np.float32)
+    say("quantize_weights 70B layer", W.shape)
+    packed, gamma = bl.quantize_weights(to_dev(W))
+    torch.cuda.synchronize()
+    p_ref, g_ref, _ = oracle.quantize_weights(W)
+    assert bits32(to_host(gamma))[0] == bits32(np.array([g_ref]))[0]
+    assert_same_bytes(to_host(packed), p_ref, "packed weights 28672x8192")
+
+
+# ---------------------------------------------------------------- activations
+
+def _acts_case(m, k, seed=0, outliers=4, factor=20.0, zero_row=False):
+    X = workloads.outlier_acts(np.random.default_rng([seed, m, k]), m, k, outliers if k > 64 else 0,
+                               factor)
+    if zero_row and m > 1:
+        X[1] = 0.0
+    return X
+
+
+@pytest.mark.parametrize("m,k", [(8, 256), (1, 2560), (1, 6912), (3, 16), (5, 48), (7, 8192),
+                                 (2048, 2560), (2048, 6912)])
+@pytest.mark.parametrize("bits", [8, 4])
+@pytest.mark.parametrize("gran", ["token", "tensor"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_quantize_acts_parity(m, k, bits, gran, dtype):
+    X = _acts_case(m, k, zero_row=True)
+    Xin = workloads.to_bf16_bits(X) if dtype == "bf16" else X
+    say("quantize_acts", m, k, bits, gran, dtype)
+    xq, s = bl.quantize_acts(to_dev(Xin), bits=bits, gran=gran)
+    torch.cuda.synchronize()
+    g = oracle.PER_TOKEN if gran == "token" else oracle.PER_TENSOR
+    xq_ref, s_ref = oracle.quantize_acts(Xin, bits=bits, gran=g)
+    assert_same_bytes(bits32(to_host(s)), bits32(s_ref), "act_scale")
+    assert_same_bytes(to_host(xq), xq_ref, "activation codes")
+
+
+def test_quantize_acts_70b_layer_outliers():
+    _, X = workloads.layer_70b()
+    for bits in (8, 4):
+        say("quantize_acts 70B layer", X.shape, bits)
+        xq, s = bl.quantize_acts(to_dev(X), bits=bits)
+        torch.cuda.synchronize()
+        xq_ref, s_ref = oracle.quantize_acts(X, bits=bits)
+        assert_same_bytes(bits32(to_host(s)), bits32(s_ref), "act_scale")
+        assert_same_bytes(to_host(xq), xq_ref, "activation codes")
+
+
+# ---------------------------------------------------------------- forward
+
+def _layer(m, k, n, seed, kind="gauss"):
+    W = _weights_case(kind, n, k, seed)
+    X = _acts_case(m, k, seed=seed)
+    return W, X
+
+
+def _run_forward(W, X, bits, gran, epi, ydt, bias, fused, x_dtype="f32"):
+    g = oracle.PER_TOKEN if gran == "token" else oracle.PER_TENSOR
+    Xin = workloads.to_bf16_bits(X) if x_dtype == "bf16" else X
+    Wd = to_dev(W)
+    packed, gamma = bl.quantize_weights(Wd)
+    bias_d = to_dev(bias) if bias is not None else None
+    tdt, _ = YD[ydt]
+    if fused:
+        y = bl.forward_fused(to_dev(Xin), packed, gamma, bits=bits, gran=gran, bias=bias_d,
+                             epilogue=epi, out_dtype=tdt)
+    else:
+        xq, s = bl.quantize_acts(to_dev(Xin), bits=bits, gran=gran)
+        y = bl.forward(xq, s, packed, gamma, bits=bits, gran=gran, bias=bias_d, epilogue=epi,
+                       out_dtype=tdt)
+    torch.cuda.synchronize()
+    p_ref, g_ref, _ = oracle.quantize_weights(W)
+    xq_ref, s_ref = oracle.quantize_acts(Xin, bits=bits, gran=g)
+    return to_host(y), (p_ref, g_ref, xq_ref, s_ref, g)
+
+
+def _check_forward(M, K, N, bits, gran, epi, ydt, with_bias, fused, x_dtype="f32", seed=0,
+                   kind="gauss", sampled=None):
+    W, X = _layer(M, K, N, seed, kind)
+    bias = (np.random.default_rng(seed).standard_normal(N).astype(np.float32)
+            if with_bias else None)
+    say("forward", dict(M=M, K=K, N=N, bits=bits, gran=gran, epi=epi, y=ydt, bias=with_bias,
+                        fused=fused, x=x_dtype))
+    y, (p_ref, g_ref, xq_ref, s_ref, g) = _run_forward(W, X, bits, gran, epi, ydt, bias, fused,
+                                                       x_dtype)
+    e = oracle.EPI_RELU2 if epi == "relu2" else oracle.EPI_NONE
+    _, odt = YD[ydt]
+    if sampled is None:
+        sampled = M * N * K > 3e8
+    if not sampled:
+        y_ref, acc_ref = oracle.forward(xq_ref, bits, s_ref, g, p_ref, g_ref, bias=bias, epi=e,
+                                        y_dtype=odt if odt is not None else oracle.F32)
+        ref = acc_ref if ydt == "i32" else y_ref
+        assert_y_matches(y, ref, ydt, "Y")
+    else:
+        ms, ns = sample_positions(M, N, 4096, seed)
+        y_ref, acc_ref = oracle.forward_at(xq_ref, bits, s_ref, g, p_ref, g_ref, ms, ns,
+                                           bias=bias, epi=e,
+                                           y_dtype=odt if odt is not None else oracle.F32)
+        ref = acc_ref if ydt == "i32" else y_ref
+        assert_y_matches(y[ms, ns], ref, ydt, "Y (sampled)")
+
+
+# decode path (GEMV, M <= 8, K % 64 == 0)
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8])
+@pytest.mark.parametrize("K,N", [(256, 512), (64, 17), (2560, 300), (6912, 129)])
+@pytest.mark.parametrize("bits", [8, 4])
+def test_forward_decode_shapes(M, K, N, bits):
+    _check_forward(M, K, N, bits, "token", None, "i32", False, False)
+    _check_forward(M, K, N, bits, "token", "relu2", "f32", True, False)
+
+
+@pytest.mark.parametrize("gran", ["token", "tensor"])
+@pytest.mark.parametrize("epi", [None, "relu2"])
+@pytest.mark.parametrize("ydt", ["f32", "bf16"])
+@pytest.mark.parametrize("fused", [False, True])
+def test_forward_decode_variants(gran, epi, ydt, fused):
+    for bits in (8, 4):
+        _check_forward(4, 256, 512, bits, gran, epi, ydt, False, fused)
+        _check_forward(1, 2560, 6912, bits, gran, epi, ydt, False, fused, x_dtype="bf16",
+                       kind="ternary")
+
+
+# prefill path (MFMA GEMM)
+@pytest.mark.parametrize("M,K,N", [(9, 256, 512), (130, 48, 37), (200, 336, 300),
+                                   (128, 128, 128), (257, 2560, 129), (64, 6912, 200)])
+@pytest.mark.parametrize("bits", [8, 4])
+def test_forward_prefill_shapes(M, K, N, bits):
+    _check_forward(M, K, N, bits, "token", None, "i32", False, False)
+    _check_forward(M, K, N, bits, "tensor", "relu2", "f32", True, False)
+
+
+@pytest.mark.parametrize("gran", ["token", "tensor"])
+@pytest.mark.parametrize("epi", [None, "relu2"])
+@pytest.mark.parametrize("ydt", ["f32", "bf16", "i32"])
+def test_forward_prefill_variants(gran, epi, ydt):
+    if ydt == "i32" and epi:
+        pytest.skip("raw accumulators take no epilogue")
+    for bits in (8, 4):
+        _check_forward(300, 512, 260, bits, gran, epi, ydt, ydt != "i32", bits == 4)
+
+
+# full-size 2B shapes, sampled
+@pytest.mark.parametrize("shape,epi", [(workloads.SHAPE_UP, "relu2"), (workloads.SHAPE_DOWN, None)])
+@pytest.mark.parametrize("bits", [8, 4])
+def test_forward_prefill_2b_shapes(shape, epi, bits):
+    K, N = shape
+    _check_forward(2048, K, N, bits, "token", epi, "bf16", False, True, x_dtype="bf16",
+                   kind="ternary", sampled=True)
+    _check_forward(2048, K, N, bits, "token", None, "i32", False, False, x_dtype="bf16",
+                   kind="ternary", sampled=True)
+
+
+@pytest.mark.parametrize("shape,epi", [(workloads.SHAPE_UP, "relu2"), (workloads.SHAPE_DOWN, None)])
+def test_forward_decode_2b_shapes_full(shape, epi):
+    K, N = shape
+    for bits in (8, 4):
+        _check_forward(1, K, N, bits, "token", epi, "bf16", False, True, x_dtype="bf16",
+                       kind="ternary", sampled=False)
+        _check_forward(1, K, N, bits, "token", None, "i32", False, True, x_dtype="bf16",
+                       kind="ternary", sampled=False)
+
+
+def test_forward_70b_layer_sampled():
+    codes, X = workloads.layer_70b()
+    W = codes.astype(np.float32)
+    del codes
+    Wd = to_dev(W)
+    packed, gamma = bl.quantize_weights(Wd)
+    del Wd
+    p_ref, g_ref, _ = oracle.quantize_weights(W)
+    del W
+    Xd = to_dev(X)
+    M, K = X.shape
+    N = packed.shape[0]
+    ms, ns = sample_positions(M, N, 4096, 4)
+    for bits in (8, 4):
+        say("forward 70B layer", bits)
+        y = bl.forward_fused(Xd, packed, gamma, bits=bits, out_dtype=torch.bfloat16)
+        acc_w = bl.quantize_acts(Xd, bits=bits)
+        acc = bl.forward(acc_w[0], acc_w[1], packed, gamma, bits=bits, out_dtype=torch.int32)
+        torch.cuda.synchronize()
+        xq_ref, s_ref = oracle.quantize_acts(X, bits=bits)
+        y_ref, acc_ref = oracle.forward_at(xq_ref, bits, s_ref, 0, p_ref, g_ref, ms, ns,
+                                           y_dtype=oracle.BF16)
+        yh = to_host(y)
+        assert_y_matches(yh[ms, ns], y_ref, "bf16", "Y 70B layer")
+        assert_same_bytes(to_host(acc)[ms, ns], acc_ref, "acc 70B layer")
+        del y, acc
+
+
+def test_forward_edge_zero_weights_and_rows():
+    M, K, N = 5, 128, 64
+    W = np.zeros((N, K), np.float32)
+    X = _acts_case(M, K)
+    X[2] = 0.0
+    for fused in (False, True):
+        y, _ = _run_forward(W, X, 8, "token", "relu2", "f32", None, fused)
+        assert (y == 0).all()
+    W = _weights_case("gauss", N, K)
+    y, _ = _run_forward(W, X, 8, "token", None, "f32", None, False)
+    assert (y[2] == 0).all()
+
+
+def test_forward_deterministic():
+    W, X = _layer(2048, 2560, 600, 3, "ternary")
+    Xd, Wd = to_dev(X), to_dev(W)
+    packed, gamma = bl.quantize_weights(Wd)
+    outs = []
+    for _ in range(2):
+        xq, s = bl.quantize_acts(Xd)
+        outs.append(to_host(bl.forward(xq, s, packed, gamma, out_dtype=torch.int32)))
+    assert_same_bytes(outs[0], outs[1], "repeat run")
+    p2, g2 = bl.quantize_weights(Wd)
+    assert_same_bytes(to_host(p2), to_host(packed), "repeat pack")
