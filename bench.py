@@ -1,0 +1,330 @@
+"""Benchmark of the MI355X BitLinear forward pass.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--legs decode,prefill,pack]
+
+Headline (one JSON line on stdout): decode-GEMV HBM throughput on the BitNet 2B
+FFN shapes at M=1 token.  One step = the FFN of one block at decode time:
+    x (bf16 [1, 2560])  --up 2560->6912, ReLU^2-->  h (bf16 [1, 6912])
+                        --down 6912->2560-->         y (bf16 [1, 2560])
+Each projection is one bitlinear_forward_fused launch: per-token absmax int8
+quantization of its input (for down: the requantization of up's output), the
+ternary GEMV with int32 accumulation and the rescale epilogue.  Packed weights
+are pre-quantized (bitlinear_quantize_weights, timed separately as the "pack"
+leg): the pages treat weights as static.
+
+Inputs are resident in HBM before timing.  Weights rotate through 64 distinct
+copies per shape (566 MB, more than twice the 256 MB Infinity Cache), so the
+weight stream really comes from HBM.  The K timed steps are captured in one HIP
+graph (host launch overhead would otherwise dominate a ~2 us GEMV) and timed
+with HIP events on the stream the kernels run on.
+
+value      = algorithmic bytes per step / time per step (GB/s, 1e9 B/s)
+roofline   = the GEMV kernel against MI355X HBM (8 TB/s)
+prefill    = the prefill GEMM leg: M=2048 tokens, int TOPS against int8 MFMA peak
+cpu_baseline = the CPU oracle on the same decode step, single-threaded
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, GB/s
+INT8_PEAK_TOPS = 5000.0         # MI355X dense int8 MFMA, TOPS (5.0 POP/s)
+MALL_BYTES = 256 << 20          # Infinity Cache
+METRIC = "BitLinear decode GEMV HBM GB/s + prefill GEMM int TOPS, % of MI355X roofline"
+
+
+def gemv_bytes(K: int, N: int) -> int:
+    """Algorithmic bytes of one decode GEMV: packed W + bf16 x + bf16 y + gamma."""
+    return N * K // 4 + 2 * K + 2 * N + 4
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def graph_time_ms(torch, fn, replays: int, warm: int = 2):
+    """Capture fn() in a HIP graph; return (ms per replay, graph) over `replays` replays."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()  # eager warm-up outside capture (allocations, lazy init)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    for _ in range(warm):
+        g.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(replays):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / replays, g
+
+
+def make_weight_copies(torch, bl, W0, copies, seed):
+    """Copy 0: the seeded host weights; the others: distinct uniform-ternary tensors drawn
+    on the device; all packed by bitlinear_quantize_weights."""
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    N, K = W0.shape
+    out = []
+    for c in range(copies):
+        if c == 0:
+            W = torch.from_numpy(W0).to(dev)
+        else:
+            W = torch.randint(-1, 2, (N, K), device=dev, generator=gen, dtype=torch.int8).float()
+        out.append(bl.quantize_weights(W))
+        del W
+    torch.cuda.synchronize()
+    return out
+
+
+def leg_decode(torch, bl, steps, warmup, copies):
+    import workloads
+    dev = torch.device("cuda:0")
+    (K1, N1), (K2, N2) = workloads.SHAPE_UP, workloads.SHAPE_DOWN
+    W_up, x = workloads.decode_gemv(seed=1, shape=workloads.SHAPE_UP)
+    W_dn, _ = workloads.decode_gemv(seed=1, shape=workloads.SHAPE_DOWN)
+    up = make_weight_copies(torch, bl, W_up, copies, 11)
+    dn = make_weight_copies(torch, bl, W_dn, copies, 12)
+    xd = torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+    h = torch.empty((1, N1), dtype=torch.bfloat16, device=dev)
+    y = torch.empty((1, N2), dtype=torch.bfloat16, device=dev)
+
+    def step(i):
+        pu, gu = up[i % copies]
+        pd, gd = dn[i % copies]
+        bl.forward_fused(xd, pu, gu, epilogue="relu2", out=h)
+        bl.forward_fused(h, pd, gd, out=y)
+
+    def run_k():
+        for i in range(steps):
+            step(i)
+
+    # warm-up steps (untimed), then exactly `steps` steps in one graph
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ms_total, _ = graph_time_ms(torch, run_k, replays=1, warm=1)
+    ms_step = ms_total / steps
+    step_bytes = gemv_bytes(K1, N1) + gemv_bytes(K2, N2)
+    gbs = step_bytes / (ms_step * 1e-3) / 1e9
+    per_launch_us = ms_step * 1e3 / 2
+    return {
+        "ms_per_step": ms_step, "gbs": gbs, "step_bytes": step_bytes,
+        "per_launch_us": per_launch_us, "launches_per_step": 2,
+        "bytes_per_launch": step_bytes / 2, "weight_copies": copies,
+        "rotation_bytes": copies * (N1 * K1 // 4 + N2 * K2 // 4),
+        "x": x, "W_up": W_up, "W_dn": W_dn,
+    }
+
+
+def leg_decode_single(torch, bl, copies=64, reps=200):
+    """Each GEMV alone (up, then down), rotating copies, graph-captured: per-launch time."""
+    import workloads
+    dev = torch.device("cuda:0")
+    res = {}
+    for name, shape, epi in (("up", workloads.SHAPE_UP, "relu2"),
+                             ("down", workloads.SHAPE_DOWN, None)):
+        K, N = shape
+        W, x = workloads.decode_gemv(seed=1, shape=shape)
+        ws = make_weight_copies(torch, bl, W, copies, 21)
+        xd = torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+        y = torch.empty((1, N), dtype=torch.bfloat16, device=dev)
+
+        def run():
+            for i in range(reps):
+                p, g = ws[i % copies]
+                bl.forward_fused(xd, p, g, epilogue=epi, out=y)
+
+        ms, _ = graph_time_ms(torch, run, replays=1)
+        us = ms * 1e3 / reps
+        res[name] = {"us_per_launch": us, "gbs": gemv_bytes(K, N) / (us * 1e-6) / 1e9}
+        del ws
+    return res
+
+
+def leg_prefill(torch, bl, reps=20):
+    """C3: M=2048 tokens; bf16 X -> int8 per token -> MFMA GEMM -> bf16 Y (ReLU^2 on up)."""
+    import workloads
+    dev = torch.device("cuda:0")
+    res = {}
+    tot_ops, tot_gemm_ms, tot_step_ms = 0.0, 0.0, 0.0
+    for name, shape, epi in (("up", workloads.SHAPE_UP, "relu2"),
+                             ("down", workloads.SHAPE_DOWN, None)):
+        K, N = shape
+        W, X = workloads.prefill_gemm(seed=2, shape=shape)
+        packed, gamma = bl.quantize_weights(torch.from_numpy(W).to(dev))
+        Xd = torch.from_numpy(X.view(np.int16)).to(dev).view(torch.bfloat16)
+        M = X.shape[0]
+        xq, s = bl.quantize_acts(Xd)
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+
+        def gemm():
+            for _ in range(reps):
+                bl.forward(xq, s, packed, gamma, epilogue=epi, out=y)
+
+        def stepf():
+            for _ in range(reps):
+                bl.quantize_acts(Xd, out=(xq, s))
+                bl.forward(xq, s, packed, gamma, epilogue=epi, out=y)
+
+        ms_gemm, _ = graph_time_ms(torch, gemm, replays=1)
+        ms_step, _ = graph_time_ms(torch, stepf, replays=1)
+        ms_gemm /= reps
+        ms_step /= reps
+        ops = 2.0 * M * N * K
+        res[name] = {"M": M, "K": K, "N": N, "gemm_us": ms_gemm * 1e3,
+                     "gemm_tops": ops / (ms_gemm * 1e-3) / 1e12,
+                     "step_us": ms_step * 1e3, "step_tops": ops / (ms_step * 1e-3) / 1e12}
+        tot_ops += ops
+        tot_gemm_ms += ms_gemm
+        tot_step_ms += ms_step
+    tops = tot_ops / (tot_gemm_ms * 1e-3) / 1e12
+    res["gemm_tops"] = tops
+    res["gemm_frac"] = tops / INT8_PEAK_TOPS
+    res["step_tops"] = tot_ops / (tot_step_ms * 1e-3) / 1e12
+    return res
+
+
+def leg_pack(torch, bl, reps=10):
+    """a1: weight quantization + packing of the 2B up projection, fp32 W in HBM."""
+    import workloads
+    dev = torch.device("cuda:0")
+    W, _ = workloads.decode_gemv(seed=1, shape=workloads.SHAPE_UP)
+    Wd = torch.from_numpy(W).to(dev)
+    packed, gamma = bl.quantize_weights(Wd)
+    ws = torch.empty(bl.workspace_size(bl.BL_OP_QUANTIZE_WEIGHTS, 1, *W.shape), dtype=torch.uint8,
+                     device=dev)
+
+    def run():
+        for _ in range(reps):
+            bl.quantize_weights(Wd, workspace=ws, out=(packed, gamma))
+
+    ms, _ = graph_time_ms(torch, run, replays=1)
+    ms /= reps
+    N, K = W.shape
+    alg = 2 * 4 * N * K + N * K // 4  # two passes over fp32 W, packed write
+    return {"N": N, "K": K, "us": ms * 1e3, "gbs": alg / (ms * 1e-3) / 1e9,
+            "alg_bytes": alg}
+
+
+def cpu_baseline(x, W_up, W_dn, budget_s=12.0):
+    """The oracle (single-threaded C, as it stands) on the same decode FFN step."""
+    import oracle
+    import workloads
+    p_up, g_up, _ = oracle.quantize_weights(W_up)
+    p_dn, g_dn, _ = oracle.quantize_weights(W_dn)
+    (K1, N1), (K2, N2) = workloads.SHAPE_UP, workloads.SHAPE_DOWN
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        h, _, _, _ = oracle.bitlinear(x, p_up, g_up, epi=oracle.EPI_RELU2, y_dtype=oracle.BF16)
+        oracle.bitlinear(h, p_dn, g_dn, y_dtype=oracle.BF16)
+        n += 1
+        el = time.perf_counter() - t0
+        if el > budget_s or n >= 200:
+            break
+    step_bytes = gemv_bytes(K1, N1) + gemv_bytes(K2, N2)
+    return {"value": step_bytes * n / el / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": "%d decode FFN steps (up 2560->6912 + ReLU^2, down 6912->2560, M=1, "
+                      "int8 per token, bf16 out) in %.1f s on one core of %s" % (
+                          n, el, cpu_model()),
+            "ms_per_step": el * 1e3 / n}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--copies", type=int, default=64)
+    ap.add_argument("--legs", default="decode,single,prefill,pack,cpu")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import ternary_weight_quantized_bitlinear_amd as bl
+    if not os.path.exists(bl.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    legs = set(args.legs.split(","))
+
+    dec = leg_decode(torch, bl, args.steps, args.warmup, args.copies)
+    out = {
+        "metric": METRIC,
+        "value": round(dec["gbs"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": dec["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8 x ternary -> int32 acc, fp32 rescale, bf16 io",
+        "data": "synthetic: seeded uniform-ternary weights, N(0,1) bf16 activations",
+        "config": {"workload": "BitNet-2B FFN decode step, M=1: up 2560->6912 (+ReLU^2) then "
+                               "down 6912->2560, fused int8 per-token quantization, bf16 out",
+                   "tokens": 1, "hidden": 2560, "ffn": 6912,
+                   "weight_copies_rotated": dec["weight_copies"],
+                   "rotation_bytes": dec["rotation_bytes"]},
+        "roofline": {"bound": "hbm", "kernel": "gemv_kernel (fused decode GEMV)",
+                     "achieved": round(dec["bytes_per_launch"] / (dec["per_launch_us"] * 1e-6)
+                                       / 1e9, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(dec["bytes_per_launch"] / (dec["per_launch_us"] * 1e-6) / 1e9
+                                   / HBM_PEAK_GBS, 4),
+                     "traffic": None,
+                     "bytes_per_launch": dec["bytes_per_launch"],
+                     "us_per_launch": dec["per_launch_us"]},
+    }
+    if "single" in legs:
+        out["decode_single"] = leg_decode_single(torch, bl)
+    if "prefill" in legs:
+        pf = leg_prefill(torch, bl)
+        out["prefill"] = {"metric": "prefill GEMM int TOPS (2*M*N*K / GEMM time)",
+                          "workload": "M=2048 tokens, 2560->6912 (+ReLU^2) and 6912->2560, "
+                                      "int8 per token, bf16 out",
+                          "value": round(pf["gemm_tops"], 2), "unit": "TOPS",
+                          "roofline": {"bound": "mfma", "peak": INT8_PEAK_TOPS, "unit": "TOPS",
+                                       "frac": round(pf["gemm_frac"], 4)},
+                          "with_act_quant_tops": round(pf["step_tops"], 2),
+                          "shapes": {k: v for k, v in pf.items() if isinstance(v, dict)}}
+    if "pack" in legs:
+        out["pack"] = leg_pack(torch, bl)
+    if "cpu" in legs:
+        out["cpu_baseline"] = cpu_baseline(dec["x"], dec["W_up"], dec["W_dn"])
+    out["device"] = torch.cuda.get_device_name(0)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

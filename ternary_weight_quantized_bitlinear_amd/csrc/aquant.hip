@@ -23,7 +23,7 @@ namespace {
 constexpr int kAqThreads = 256;
 
 __device__ __forceinline__ float block_max(float v, float *red) {
-    v = wave_max(v);
+    v = wave_max_abs(v);
     const int wid = threadIdx.x / kWave;
     if ((threadIdx.x & (kWave - 1)) == 0) red[wid] = v;
     __syncthreads();

@@ -24,15 +24,42 @@ __device__ __forceinline__ uint32_t to_bf16_bits(float f) {
 }
 
 // ---------------------------------------------------------------- wave reductions
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-    return v;
+// Whole-wave reductions on DPP lane moves (VALU latency, no LDS round trips): swaps
+// within quads, mirrors within half-rows and rows of 16, then the two row broadcasts
+// carry the partial results across the four rows; lane 63 ends with the total, which
+// readlane broadcasts.  Masked-off rows read the identity value.
+constexpr int kDppQuadXor1 = 0xB1;     // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;     // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;  // row_half_mirror
+constexpr int kDppMirror = 0x140;      // row_mirror
+constexpr int kDppBcast15 = 0x142;     // row_bcast:15
+constexpr int kDppBcast31 = 0x143;     // row_bcast:31
+
+template <int kCtrl, int kRowMask = 0xF>
+__device__ __forceinline__ int dpp_mov(int identity, int v) {
+    return __builtin_amdgcn_update_dpp(identity, v, kCtrl, kRowMask, 0xF, false);
 }
+
 __device__ __forceinline__ int wave_sum(int v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-    return v;
+    v += dpp_mov<kDppQuadXor1>(0, v);
+    v += dpp_mov<kDppQuadXor2>(0, v);
+    v += dpp_mov<kDppHalfMirror>(0, v);
+    v += dpp_mov<kDppMirror>(0, v);
+    v += dpp_mov<kDppBcast15, 0xA>(0, v);
+    v += dpp_mov<kDppBcast31, 0xC>(0, v);
+    return __builtin_amdgcn_readlane(v, 63);
+}
+
+// max of non-negative floats (absolute values): their bits order like integers
+__device__ __forceinline__ float wave_max_abs(float f) {
+    int v = (int)__float_as_uint(f);
+    v = max(v, dpp_mov<kDppQuadXor1>(0, v));
+    v = max(v, dpp_mov<kDppQuadXor2>(0, v));
+    v = max(v, dpp_mov<kDppHalfMirror>(0, v));
+    v = max(v, dpp_mov<kDppMirror>(0, v));
+    v = max(v, dpp_mov<kDppBcast15, 0xA>(0, v));
+    v = max(v, dpp_mov<kDppBcast31, 0xC>(0, v));
+    return __uint_as_float((uint32_t)__builtin_amdgcn_readlane(v, 63));
 }
 
 // ---------------------------------------------------------------- 2-bit ternary fields

@@ -1,47 +1,60 @@
-// Decode-sized BitLinear forward (M <= 8 tokens): the HBM-bound ternary GEMV.
+// Decode-sized BitLinear forward (M <= 16 tokens): the HBM-bound ternary GEMV.
 //
 // "BitNet b1.58: The 1-Bit Ternary LLM Architecture Guide", "3. Multiplier-Free
 // Forward Pass & Dequantization": Y = (X~ W~^T) * (gamma / scale_X); "BitNet 2B4T
-// Guide", "1. The BitLinear Operator": every product is an add, a subtract or a skip.
+// Guide", "1. The BitLinear Operator": each product is an add, a subtract or a skip.
 //
-// One launch does the whole layer for a handful of tokens:
-//  prologue  every block brings the activations of all M tokens into LDS as int8,
-//            k-interleaved (see fields() in common.hpp).  The fused variant reads the
-//            raw bf16/fp32 rows and quantizes them itself (absmax, s, codes -- the
-//            same arithmetic as the activation quantizer); the plain variant reads
-//            int8 or int4 codes.  The packed-weight loads of the block's first rows
-//            are issued *before* the prologue, so their HBM latency overlaps it.
-//  main loop each row of W (K/4 bytes) is read by kLPR lanes in 16-byte units (64
-//            weights); a unit's 4 dwords expand, with a shift and a mask each, to the
-//            2-bit fields (c+1) in {0,1,2}, and v_dot4 multiplies four fields by four
-//            activation codes at a time.  With fields in place of codes,
-//            sum (c+1) x - sum x = sum c x, so the token's code sum is subtracted once.
-//  epilogue  the kLPR partial sums are reduced with lane shuffles; one lane per row
-//            applies f = gamma/s (int8) or s*gamma (int4), bias and ReLU^2, and
-//            stores fp32, bf16 or the raw int32 accumulator.
-// The weight stream (the only HBM-heavy traffic) is read exactly once, in 16-byte
-// loads of which kLPR consecutive lanes cover kLPR*16 contiguous bytes of a row.
+// The weight stream is the whole cost (2 bits per weight, read once); everything
+// else is arranged so that it hides under the stream's HBM latency.
+//
+// Work split.  A block owns 16 output rows (one MFMA column tile) over the full K;
+// its waves split K: wave w takes the 256-wide k tiles w, w + nw, w + 2nw, ...
+// A tile is 16 rows x 256 k = 1 KB of packed weights, one 16-byte load per lane:
+// lane l reads chunk c = l/16 (64 k) of row l%16.
+//
+// Contraction on the matrix cores.  v_mfma_i32_16x16x64_i8 takes a 16(token) x 64(k)
+// activation fragment and a 64(k) x 16(row) weight fragment.  Dword j of a lane's
+// chunk (16 codes) expands with a shift and a mask per output dword into the 2-bit
+// fields (c+1) in {0,1,2} -- the weight fragment of MFMA j; the activation fragment
+// is the same 16 k of the lane's token, read from LDS where the codes were stored
+// k-interleaved to match the fields' order.  Which 64 k form one MFMA does not
+// matter to an integer sum, so the chunk-wise assignment is exact.  Fields instead
+// of codes add sum_k x[m][k] to every output; the prologue computes that sum per
+// token and the epilogue subtracts it.  Tokens m >= M feed zero fragments: for
+// M = 1 the matrix core wastes 15/16 of its rate, which costs nothing here because
+// its rate is ~100x what the weight stream needs.
+//
+// Prologue.  Each block brings the M activation rows into LDS as int8: the fused
+// variant reads raw bf16/fp32 rows, reduces each token's absmax across the block,
+// and quantizes (s = 127/a or a/7, exactly as the activation quantizer does); the
+// plain variant reads int8 or int4 codes.  The activation loads are issued first and
+// every weight load of the wave right after, so the weights are in flight while
+// the prologue runs (vector-memory counters retire in order: the prologue's waits
+// then never wait on the weights).
+//
+// Epilogue.  The waves' 16x16 partial tiles are summed through LDS; the first wave
+// applies f = gamma/s (int8) or s*gamma (int4), bias, ReLU^2, and stores.
 #include "common.hpp"
 
 namespace bl {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWavesPerBlock = kThreads / kWave;
-constexpr int kBatch = 4;  // 16-byte units each lane keeps in flight
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+constexpr int kMaxM = 16;
 
 enum Mode { kInt8 = 0, kInt4 = 1, kRawBf16 = 2, kRawF32 = 3 };
 
 struct GemvParams {
-    const void *x;          // int8/int4 codes, or raw bf16/fp32 rows (fused)
-    const float *act_scale; // plain variant: s per token or per tensor
+    const void *x;           // int8/int4 codes, or raw bf16/fp32 rows (fused)
+    const float *act_scale;  // plain variant: s per token or per tensor
     int gran;
     int bits;
     float eps;
     const uint8_t *w;
     const float *gamma;
     const float *bias;
-    int64_t M, N, K;
+    int M, N, K;
     int epi;
     void *y;
     int y_dtype;
@@ -51,252 +64,335 @@ __device__ __forceinline__ int dot4(uint32_t a, uint32_t b, int c) {
     return __builtin_amdgcn_sdot4((int)a, (int)b, c, false);
 }
 
-template <int kM, int kLPR, int kMode>
-__global__ void __launch_bounds__(kThreads) gemv_kernel(GemvParams p) {
-    extern __shared__ uint32_t smem[];
-    // LDS: x codes [kM][K] bytes (k-interleaved per 16), then per-token scalars
-    uint32_t *xl = smem;
-    const int64_t K = p.K;
-    const int ngroups = (int)(K / 16);
-    __shared__ float s_f[kM];
-    __shared__ int s_sum[kM];
-    __shared__ float s_red[kWavesPerBlock][kM];
-    __shared__ int s_ired[kWavesPerBlock][kM];
 
-    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-    constexpr int kRowsPerWave = kWave / kLPR;
-    const int64_t n = (int64_t)blockIdx.x * (kWavesPerBlock * kRowsPerWave) +
-                      wave * kRowsPerWave + lane / kLPR;
-    const int part = lane % kLPR;
-    const bool row_ok = n < p.N;
-    const int nunits = (int)(K / 64);
-    const uint4 *wrow = reinterpret_cast<const uint4 *>(p.w + (row_ok ? n : 0) * (K / 4));
+template <int kMode> struct RawWords { static constexpr int n = kMode == kRawF32 ? 4 : kMode == kRawBf16 ? 2 : 1; };
 
-    // ---- issue the first batch of weight loads before anything else
-    uint4 wb[kBatch];
+// one 16-element group's raw 16-byte words (address clamped into the row; a group
+// past the end is never used)
+template <int kMode>
+__device__ __forceinline__ void load_group(const uint8_t *xbase, int row_bytes, int gbytes,
+                                           int ngroups, int m, int g,
+                                           uint4 (&r)[RawWords<kMode>::n]) {
+    const int gc = g < ngroups ? g : 0;
+    const uint8_t *src = xbase + (size_t)m * row_bytes + (size_t)gc * gbytes;
+    if (kMode == kInt4) {
+        const uint2 q = *reinterpret_cast<const uint2 *>(src);
+        r[0] = make_uint4(q.x, q.y, 0u, 0u);
+    } else {
 #pragma unroll
-    for (int j = 0; j < kBatch; ++j) {
-        const int u = part + j * kLPR;
-        wb[j] = (row_ok && u < nunits) ? wrow[u] : make_uint4(0u, 0u, 0u, 0u);
+        for (int j = 0; j < RawWords<kMode>::n; ++j) r[j] = reinterpret_cast<const uint4 *>(src)[j];
     }
+}
 
-    // ---- prologue: activation codes into LDS, per-token code sums and factors
-    const float gamma = *p.gamma;
-    int my_sum[kM];
+template <int kMode>
+__device__ __forceinline__ void widen16(const uint4 (&r)[RawWords<kMode>::n], float (&v)[16]) {
+    constexpr int n = RawWords<kMode>::n;
+    if (kMode == kRawBf16) {
+        const uint32_t w[8] = {r[0].x, r[0].y, r[0].z, r[0].w, r[n - 1].x, r[n - 1].y, r[n - 1].z, r[n - 1].w};
 #pragma unroll
-    for (int m = 0; m < kM; ++m) my_sum[m] = 0;
-
-    if (kMode == kRawBf16 || kMode == kRawF32) {
-        constexpr bool kBf = kMode == kRawBf16;
-        float mx[kM];
-#pragma unroll
-        for (int m = 0; m < kM; ++m) {
-            mx[m] = 0.0f;
-            if (m < p.M) {
-                const void *row = kBf ? (const void *)(static_cast<const uint16_t *>(p.x) + m * K)
-                                      : (const void *)(static_cast<const float *>(p.x) + m * K);
-                for (int u = tid; u < ngroups * 2; u += kThreads) {
-                    float v[8];
-                    load8<kBf>(row, (int64_t)u * 8, v);
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) mx[m] = fmaxf(mx[m], fabsf(v[j]));
-                }
-            }
-            mx[m] = wave_max(mx[m]);
-            if (lane == 0) s_red[wave][m] = mx[m];
-        }
-        __syncthreads();
-        float s_tok[kM];
-        float tmax = 0.0f;
-#pragma unroll
-        for (int m = 0; m < kM; ++m) {
-            float a = s_red[0][m];
-#pragma unroll
-            for (int w = 1; w < kWavesPerBlock; ++w) a = fmaxf(a, s_red[w][m]);
-            mx[m] = a;
-            if (m < p.M) tmax = fmaxf(tmax, a);
-        }
-#pragma unroll
-        for (int m = 0; m < kM; ++m) {
-            const float a = fmaxf(p.gran == 1 ? tmax : mx[m], p.eps);
-            s_tok[m] = p.bits == 8 ? 127.0f / a : a / 7.0f;
-        }
-#pragma unroll
-        for (int m = 0; m < kM; ++m) {
-            const void *row = kBf ? (const void *)(static_cast<const uint16_t *>(p.x) + m * K)
-                                  : (const void *)(static_cast<const float *>(p.x) + m * K);
-            for (int g = tid; g < ngroups; g += kThreads) {
-                uint32_t nat[4] = {0u, 0u, 0u, 0u};
-                if (m < p.M) {
-                    float v[16];
-                    load8<kBf>(row, (int64_t)g * 16, v);
-                    load8<kBf>(row, (int64_t)g * 16 + 8, v + 8);
-#pragma unroll
-                    for (int d = 0; d < 4; ++d) {
-                        uint32_t w = 0;
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            uint32_t q;
-                            if (p.bits == 8) q = q8(v[4 * d + j], s_tok[m]);
-                            else q = (uint32_t)(((int)(q4(v[4 * d + j], s_tok[m]) << 28)) >> 28) & 0xFFu;
-                            w |= q << (8 * j);
-                        }
-                        nat[d] = w;
-                        my_sum[m] = dot4(w, 0x01010101u, my_sum[m]);
-                    }
-                }
-                uint32_t il[4];
-                interleave16(nat, il);
-                *reinterpret_cast<uint4 *>(xl + (size_t)m * (K / 4) + 4 * g) =
-                    make_uint4(il[0], il[1], il[2], il[3]);
-            }
-            if (tid == 0 && m < kM) s_f[m] = p.bits == 8 ? gamma / s_tok[m] : s_tok[m] * gamma;
+        for (int j = 0; j < 8; ++j) {
+            v[2 * j] = bf16_lo(w[j]);
+            v[2 * j + 1] = bf16_hi(w[j]);
         }
     } else {
 #pragma unroll
-        for (int m = 0; m < kM; ++m) {
-            for (int g = tid; g < ngroups; g += kThreads) {
-                uint32_t nat[4] = {0u, 0u, 0u, 0u};
-                if (m < p.M) {
-                    if (kMode == kInt8) {
-                        uint4 q = reinterpret_cast<const uint4 *>(
-                            static_cast<const int8_t *>(p.x) + m * K)[g];
-                        nat[0] = q.x; nat[1] = q.y; nat[2] = q.z; nat[3] = q.w;
-                    } else {
-                        uint2 q = reinterpret_cast<const uint2 *>(
-                            static_cast<const uint8_t *>(p.x) + m * (K / 2))[g];
-                        nibbles_to_i8(q.x, nat);
-                        nibbles_to_i8(q.y, nat + 2);
-                    }
-#pragma unroll
-                    for (int d = 0; d < 4; ++d) my_sum[m] = dot4(nat[d], 0x01010101u, my_sum[m]);
-                }
-                uint32_t il[4];
-                interleave16(nat, il);
-                *reinterpret_cast<uint4 *>(xl + (size_t)m * (K / 4) + 4 * g) =
-                    make_uint4(il[0], il[1], il[2], il[3]);
-            }
-            if (tid == 0 && m < p.M) {
-                const float s = p.act_scale[p.gran == 1 ? 0 : m];
-                s_f[m] = p.bits == 8 ? gamma / s : s * gamma;
-            }
-        }
-    }
-    // per-token code sums (for the field offset)
-#pragma unroll
-    for (int m = 0; m < kM; ++m) {
-        int v = wave_sum(my_sum[m]);
-        if (lane == 0) s_ired[wave][m] = v;
-    }
-    __syncthreads();
-    if (tid < kM) {
-        int t = 0;
-#pragma unroll
-        for (int w = 0; w < kWavesPerBlock; ++w) t += s_ired[w][tid];
-        s_sum[tid] = t;
-    }
-    __syncthreads();
-
-    // ---- main loop over this lane's 16-byte units of its row
-    int acc[kM];
-#pragma unroll
-    for (int m = 0; m < kM; ++m) acc[m] = 0;
-    for (int u0 = part; u0 < nunits; u0 += kBatch * kLPR) {
-        uint4 cur[kBatch];
-#pragma unroll
-        for (int j = 0; j < kBatch; ++j) cur[j] = wb[j];
-        const int un = u0 + kBatch * kLPR;
-        if (un < nunits) {
-#pragma unroll
-            for (int j = 0; j < kBatch; ++j) {
-                const int u = un + j * kLPR;
-                wb[j] = (row_ok && u < nunits) ? wrow[u] : make_uint4(0u, 0u, 0u, 0u);
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < kBatch; ++j) {
-            const int u = u0 + j * kLPR;
-            if (u < nunits) {
-                const uint32_t wd[4] = {cur[j].x, cur[j].y, cur[j].z, cur[j].w};
-#pragma unroll
-                for (int d = 0; d < 4; ++d) {
-                    const int g = 4 * u + d;
-                    const uint32_t f0 = fields(wd[d], 0), f1 = fields(wd[d], 1);
-                    const uint32_t f2 = fields(wd[d], 2), f3 = fields(wd[d], 3);
-#pragma unroll
-                    for (int m = 0; m < kM; ++m) {
-                        const uint4 xv = *reinterpret_cast<const uint4 *>(
-                            xl + (size_t)m * (K / 4) + 4 * g);
-                        acc[m] = dot4(f0, xv.x, acc[m]);
-                        acc[m] = dot4(f1, xv.y, acc[m]);
-                        acc[m] = dot4(f2, xv.z, acc[m]);
-                        acc[m] = dot4(f3, xv.w, acc[m]);
-                    }
-                }
-            }
-        }
-    }
-
-    // ---- reduce across the kLPR lanes of the row, epilogue by the row's first lane
-#pragma unroll
-    for (int m = 0; m < kM; ++m) {
-#pragma unroll
-        for (int o = kLPR / 2; o > 0; o >>= 1) acc[m] += __shfl_xor(acc[m], o, kWave);
-    }
-    if (part == 0 && row_ok) {
-#pragma unroll
-        for (int m = 0; m < kM; ++m) {
-            if (m < p.M) {
-                const int a = acc[m] - s_sum[m];
-                const int64_t idx = (int64_t)m * p.N + n;
-                if (p.y_dtype == 2) {
-                    static_cast<int32_t *>(p.y)[idx] = a;
-                } else {
-                    float y = __fmul_rn((float)a, s_f[m]);
-                    if (p.bias) y = __fadd_rn(y, p.bias[n]);
-                    if (p.epi == 1) {
-                        const float r = y > 0.0f ? y : 0.0f;
-                        y = __fmul_rn(r, r);
-                    }
-                    if (p.y_dtype == 1) static_cast<uint16_t *>(p.y)[idx] = (uint16_t)to_bf16_bits(y);
-                    else static_cast<float *>(p.y)[idx] = y;
-                }
-            }
+        for (int j = 0; j < n; ++j) {
+            v[4 * j + 0] = __uint_as_float(r[j].x);
+            v[4 * j + 1] = __uint_as_float(r[j].y);
+            v[4 * j + 2] = __uint_as_float(r[j].z);
+            v[4 * j + 3] = __uint_as_float(r[j].w);
         }
     }
 }
 
-template <int kM, int kLPR>
-hipError_t launch_mode(const GemvParams &p, int mode, hipStream_t s) {
-    const int rows_per_block = kWavesPerBlock * (kWave / kLPR);
-    const dim3 grid((unsigned)((p.N + rows_per_block - 1) / rows_per_block));
-    const size_t lds = (size_t)kM * p.K;
-    switch (mode) {
-    case kInt8: hipLaunchKernelGGL((gemv_kernel<kM, kLPR, kInt8>), grid, dim3(kThreads), lds, s, p); break;
-    case kInt4: hipLaunchKernelGGL((gemv_kernel<kM, kLPR, kInt4>), grid, dim3(kThreads), lds, s, p); break;
-    case kRawBf16: hipLaunchKernelGGL((gemv_kernel<kM, kLPR, kRawBf16>), grid, dim3(kThreads), lds, s, p); break;
-    default: hipLaunchKernelGGL((gemv_kernel<kM, kLPR, kRawF32>), grid, dim3(kThreads), lds, s, p); break;
+template <int kMode>
+__device__ __forceinline__ float group_absmax(const uint4 (&r)[RawWords<kMode>::n]) {
+    float v[16];
+    widen16<kMode>(r, v);
+    float mx = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) mx = fmaxf(mx, fabsf(v[j]));
+    return mx;
+}
+
+__device__ __forceinline__ void store_interleaved(uint8_t *xrow, int g, const uint32_t (&nat)[4]) {
+    uint32_t il[4];
+    interleave16(nat, il);
+    *reinterpret_cast<uint4 *>(xrow + 16 * g) = make_uint4(il[0], il[1], il[2], il[3]);
+}
+
+// raw activations -> int8 codes of one group, stored k-interleaved
+template <int kMode, int kBits>
+__device__ __forceinline__ void quantize_store(const uint4 (&r)[RawWords<kMode>::n], float sc,
+                                               uint8_t *xrow, int g) {
+    float v[16];
+    widen16<kMode>(r, v);
+    uint32_t nat[4];
+    if (kBits == 8) {
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+            nat[d] = q8(v[4 * d], sc) | (q8(v[4 * d + 1], sc) << 8) | (q8(v[4 * d + 2], sc) << 16) |
+                     (q8(v[4 * d + 3], sc) << 24);
+    } else {
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            uint32_t wd = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                wd |= ((uint32_t)(((int)(q4(v[4 * d + j], sc) << 28)) >> 28) & 0xFFu) << (8 * j);
+            nat[d] = wd;
+        }
     }
+    store_interleaved(xrow, g, nat);
+}
+
+// int8 / int4 codes of one group, stored k-interleaved
+template <int kMode>
+__device__ __forceinline__ void codes_store(const uint4 (&r)[RawWords<kMode>::n], uint8_t *xrow, int g) {
+    uint32_t nat[4];
+    if (kMode == kInt8) {
+        nat[0] = r[0].x; nat[1] = r[0].y; nat[2] = r[0].z; nat[3] = r[0].w;
+    } else {
+        nibbles_to_i8(r[0].x, nat);
+        nibbles_to_i8(r[0].y, nat + 2);
+    }
+    store_interleaved(xrow, g, nat);
+}
+
+template <int kMode, int kBits, int kWaves, int kMaxTilesPerWave>
+__global__ void __launch_bounds__(kWaves * 64) gemv_kernel(GemvParams p) {
+    constexpr int kThreads = kWaves * 64;
+    extern __shared__ __attribute__((aligned(16))) uint8_t xl[];  // [M][K] int8, k-interleaved
+    __shared__ float s_f[kMaxM];        // dequant factor per token
+    __shared__ float s_sc[kMaxM];       // activation scale per token
+    __shared__ uint32_t s_amax[kMaxM];  // absmax bits per token (non-negative: uint order)
+    __shared__ v4i s_acc[kWaves][64];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
+    const int M = p.M, K = p.K;
+    const int ngroups = K >> 4;
+    const int n0 = blockIdx.x * 16;
+    const int r16 = lane & 15, chunk = lane >> 4;
+    const int nrow = n0 + r16;
+    const bool row_ok = nrow < p.N;
+    const int ntiles = (K + 255) >> 8;
+
+    // ---- activation loads first.  A thread owns the 16-element groups g = tid + i *
+    // kThreads of every token; the raw 16-byte words of its first kXG groups of token 0
+    // are loaded into registers *before* any weight load is issued and are consumed
+    // only after (any earlier use would make the compiler wait for them, and
+    // vector-memory loads retire in order, which would hold back the weights).
+    constexpr bool kRaw = kMode == kRawBf16 || kMode == kRawF32;
+    constexpr bool kBf = kMode == kRawBf16;
+    constexpr int kXG = 2;  // groups per thread kept in registers
+    // 16-byte words per group: fp32 4, bf16 2, int8 1, int4 1 (half used)
+    constexpr int kWpg = RawWords<kMode>::n;
+    const int row_bytes = kMode == kRawF32 ? 4 * K : kMode == kRawBf16 ? 2 * K
+                        : kMode == kInt8 ? K : K / 2;
+    const int gbytes = row_bytes / ngroups;  // bytes per group: 64, 32, 16 or 8
+    const uint8_t *xbase = static_cast<const uint8_t *>(p.x);
+    uint4 xg0[kWpg], xg1[kWpg];
+    load_group<kMode>(xbase, row_bytes, gbytes, ngroups, 0, tid, xg0);
+    load_group<kMode>(xbase, row_bytes, gbytes, ngroups, 0, tid + kThreads, xg1);
+
+    // ---- then every weight load of this wave's tiles.  Addresses are clamped into
+    // the row (row 0 for rows past N, the row's last 64 k for a partial last tile):
+    // those values meet zero activations or are never stored.
+    uint4 wreg[kMaxTilesPerWave];
+    const uint8_t *wrow = p.w + (size_t)(row_ok ? nrow : 0) * (K >> 2);
+    auto load_w = [&](int t) __attribute__((always_inline)) {
+        const int kb = min(t * 256 + chunk * 64, K - 64);
+        return *reinterpret_cast<const uint4 *>(wrow + (kb >> 2));
+    };
+    // unconditional (a tile index past the end repeats the last tile: a cache hit whose
+    // value is never used), so the wait-count bookkeeping knows every load was issued
+#pragma unroll
+    for (int i = 0; i < kMaxTilesPerWave; ++i) wreg[i] = load_w(min(wave + i * kWaves, ntiles - 1));
+
+    // ---- prologue: per-token absmax (raw activations), scale, int8 codes into LDS
+    // (k-interleaved).  Token 0's first two groups come from registers; any other
+    // (token, group) is re-read from memory.
+    if (tid < kMaxM) s_amax[tid] = 0u;
+    const float gamma = *p.gamma;
+    const int gpt = (ngroups + kThreads - 1) / kThreads;  // groups per thread per token
+    const bool ok0 = tid < ngroups, ok1 = tid + kThreads < ngroups;
+    if (kRaw) {
+        __syncthreads();  // s_amax cleared
+        #pragma unroll 1
+
+        for (int m = 0; m < M; ++m) {
+            float mx = 0.0f;
+            if (m == 0) {
+                if (ok0) mx = fmaxf(mx, group_absmax<kMode>(xg0));
+                if (ok1) mx = fmaxf(mx, group_absmax<kMode>(xg1));
+            }
+            #pragma unroll 1
+
+            for (int i = m == 0 ? 2 : 0; i < gpt; ++i) {
+                const int g = tid + i * kThreads;
+                if (g >= ngroups) break;
+                uint4 r[kWpg];
+                load_group<kMode>(xbase, row_bytes, gbytes, ngroups, m, g, r);
+                mx = fmaxf(mx, group_absmax<kMode>(r));
+            }
+            mx = wave_max_abs(mx);
+            if (lane == 0) atomicMax(&s_amax[m], __float_as_uint(mx));
+        }
+        __syncthreads();
+        #pragma unroll 1
+
+        for (int m = 0; m < M; ++m) {
+            // every thread derives the scale itself (no extra barrier)
+            float a = __uint_as_float(s_amax[m]);
+            if (p.gran == 1)
+                #pragma unroll 1
+
+                for (int mm = 0; mm < M; ++mm) a = fmaxf(a, __uint_as_float(s_amax[mm]));
+            a = fmaxf(a, p.eps);
+            const float sc = kBits == 8 ? 127.0f / a : a / 7.0f;
+            if (tid == 0) s_f[m] = kBits == 8 ? gamma / sc : sc * gamma;
+            uint8_t *xrow_m = xl + (size_t)m * K;
+            if (m == 0) {
+                if (ok0) quantize_store<kMode, kBits>(xg0, sc, xrow_m, tid);
+                if (ok1) quantize_store<kMode, kBits>(xg1, sc, xrow_m, tid + kThreads);
+            }
+            #pragma unroll 1
+
+            for (int i = m == 0 ? 2 : 0; i < gpt; ++i) {
+                const int g = tid + i * kThreads;
+                if (g >= ngroups) break;
+                uint4 r[kWpg];
+                load_group<kMode>(xbase, row_bytes, gbytes, ngroups, m, g, r);
+                quantize_store<kMode, kBits>(r, sc, xrow_m, g);
+            }
+        }
+    } else {
+        #pragma unroll 1
+
+        for (int m = 0; m < M; ++m) {
+            uint8_t *xrow_m = xl + (size_t)m * K;
+            if (m == 0) {
+                if (ok0) codes_store<kMode>(xg0, xrow_m, tid);
+                if (ok1) codes_store<kMode>(xg1, xrow_m, tid + kThreads);
+            }
+            #pragma unroll 1
+
+            for (int i = m == 0 ? 2 : 0; i < gpt; ++i) {
+                const int g = tid + i * kThreads;
+                if (g >= ngroups) break;
+                uint4 r[kWpg];
+                load_group<kMode>(xbase, row_bytes, gbytes, ngroups, m, g, r);
+                codes_store<kMode>(r, xrow_m, g);
+            }
+        }
+        if (tid < M) {
+            const float sc = p.act_scale[p.gran == 1 ? 0 : tid];
+            s_f[tid] = kBits == 8 ? gamma / sc : sc * gamma;
+        }
+    }
+    __syncthreads();
+
+    // ---- main loop: 4 MFMAs per 16x256 tile.  All activation fragments of the batch
+    // are read from LDS first (one wait instead of one per MFMA); a lane whose token
+    // does not exist, or whose k is past K, feeds zeros.
+    // accs collects sum_k x[m][k] with an all-ones weight fragment: the fields (c+1)
+    // put that sum into every output, and acc - accs removes it.
+    v4i acc = v4i{0, 0, 0, 0}, acc1 = v4i{0, 0, 0, 0}, accs = v4i{0, 0, 0, 0};
+    const v4i ones = v4i{0x01010101, 0x01010101, 0x01010101, 0x01010101};
+    const bool tok_ok = r16 < M;  // this lane's activation row (token) exists
+    const uint8_t *xrow = xl + (size_t)(tok_ok ? r16 : 0) * K;
+    auto run_batch = [&](int t0) __attribute__((always_inline)) {
+        v4i af[kMaxTilesPerWave][4];
+#pragma unroll
+        for (int i = 0; i < kMaxTilesPerWave; ++i) {
+            const int t = t0 + i * kWaves;
+            const int kb = min(t * 256 + chunk * 64, K - 64);
+            const bool ok = tok_ok && t * 256 + chunk * 64 < K;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint4 q = *reinterpret_cast<const uint4 *>(xrow + kb + 16 * j);
+                af[i][j] = ok ? v4i{(int)q.x, (int)q.y, (int)q.z, (int)q.w} : v4i{0, 0, 0, 0};
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < kMaxTilesPerWave; ++i) {
+            if (t0 + i * kWaves >= ntiles) break;  // uniform
+            const uint32_t wd[4] = {wreg[i].x, wreg[i].y, wreg[i].z, wreg[i].w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const v4i b = v4i{(int)fields(wd[j], 0), (int)fields(wd[j], 1),
+                                  (int)fields(wd[j], 2), (int)fields(wd[j], 3)};
+                if (j & 1) acc1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[i][j], b, acc1, 0, 0, 0);
+                else acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[i][j], b, acc, 0, 0, 0);
+                accs = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[i][j], ones, accs, 0, 0, 0);
+            }
+        }
+    };
+    #pragma unroll 1
+
+    for (int t0 = wave; t0 < ntiles; t0 += kMaxTilesPerWave * kWaves) {
+        if (t0 != wave) {
+#pragma unroll
+            for (int i = 0; i < kMaxTilesPerWave; ++i) wreg[i] = load_w(min(t0 + i * kWaves, ntiles - 1));
+        }
+        run_batch(t0);
+    }
+    acc += acc1;
+    acc -= accs;
+    // ---- sum the waves' partial tiles; epilogue by wave 0
+    if (kWaves > 1) {
+        s_acc[wave][lane] = acc;
+        __syncthreads();
+        if (wave != 0) return;
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) acc += s_acc[w][lane];
+    }
+    // lane holds C[m = 4*chunk + r][n = n0 + r16]
+    if (!row_ok) return;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int m = 4 * chunk + r;
+        if (m >= M) continue;
+        const int a = acc[r];
+        const size_t idx = (size_t)m * p.N + nrow;
+        if (p.y_dtype == 2) {
+            static_cast<int32_t *>(p.y)[idx] = a;
+        } else {
+            float y = __fmul_rn((float)a, s_f[m]);
+            if (p.bias) y = __fadd_rn(y, p.bias[nrow]);
+            if (p.epi == 1) {
+                const float rr = y > 0.0f ? y : 0.0f;
+                y = __fmul_rn(rr, rr);
+            }
+            if (p.y_dtype == 1) static_cast<uint16_t *>(p.y)[idx] = (uint16_t)to_bf16_bits(y);
+            else static_cast<float *>(p.y)[idx] = y;
+        }
+    }
+}
+
+constexpr int64_t kMaxLds = 64 * 1024;
+
+// the int8 codes [M][K]
+size_t lds_bytes(int64_t M, int64_t K, int) { return (size_t)(M * K); }
+
+template <int kWaves, int kT>
+hipError_t launch_cfg(const GemvParams &p, int mode, hipStream_t s) {
+    const dim3 grid((unsigned)((p.N + 15) / 16)), block(kWaves * 64);
+    const size_t lds = lds_bytes(p.M, p.K, mode);
+    if (mode == kInt8) hipLaunchKernelGGL((gemv_kernel<kInt8, 8, kWaves, kT>), grid, block, lds, s, p);
+    else if (mode == kInt4) hipLaunchKernelGGL((gemv_kernel<kInt4, 4, kWaves, kT>), grid, block, lds, s, p);
+    else if (mode == kRawBf16 && p.bits == 8) hipLaunchKernelGGL((gemv_kernel<kRawBf16, 8, kWaves, kT>), grid, block, lds, s, p);
+    else if (mode == kRawBf16) hipLaunchKernelGGL((gemv_kernel<kRawBf16, 4, kWaves, kT>), grid, block, lds, s, p);
+    else if (p.bits == 8) hipLaunchKernelGGL((gemv_kernel<kRawF32, 8, kWaves, kT>), grid, block, lds, s, p);
+    else hipLaunchKernelGGL((gemv_kernel<kRawF32, 4, kWaves, kT>), grid, block, lds, s, p);
     return hipGetLastError();
 }
-
-template <int kM>
-hipError_t launch_m(const GemvParams &p, int mode, hipStream_t s) {
-    // lanes per row: enough lanes that each holds at most ~4 units of its row
-    const int64_t nunits = p.K / 64;
-    if (nunits <= 4 * 8) return launch_mode<kM, 8>(p, mode, s);
-    if (nunits <= 4 * 16) return launch_mode<kM, 16>(p, mode, s);
-    return launch_mode<kM, 32>(p, mode, s);
-}
-
-constexpr int64_t kMaxLds = 60 * 1024;
-
-int padded_m(int64_t M) { return M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8; }
 
 }  // namespace
 
 bool gemv_supports(int64_t M, int64_t K) {
-    return M >= 1 && M <= 8 && K % 64 == 0 && (int64_t)padded_m(M) * K <= kMaxLds;
+    return M >= 1 && M <= kMaxM && K % 64 == 0 && M * K <= kMaxLds;
 }
 
 size_t ws_gemv(int) { return 0; }
@@ -311,19 +407,21 @@ hipError_t launch_gemv(const FwdArgs &a, bool fused, void *, hipStream_t s) {
     p.w = a.w;
     p.gamma = a.gamma;
     p.bias = a.bias;
-    p.M = a.M;
-    p.N = a.N;
-    p.K = a.K;
+    p.M = (int)a.M;
+    p.N = (int)a.N;
+    p.K = (int)a.K;
     p.epi = a.epi;
     p.y = a.y;
     p.y_dtype = a.y_dtype;
     const int mode = fused ? (a.x_raw_bf16 ? kRawBf16 : kRawF32) : (a.bits == 8 ? kInt8 : kInt4);
-    switch (padded_m(a.M)) {
-    case 1: return launch_m<1>(p, mode, s);
-    case 2: return launch_m<2>(p, mode, s);
-    case 4: return launch_m<4>(p, mode, s);
-    default: return launch_m<8>(p, mode, s);
-    }
+    // 4 waves split K; each lane issues all of its weight loads at once when the tiles
+    // per wave fit the batch (K <= 8192), otherwise in batches of 8
+    const int ntiles = (int)((a.K + 255) / 256);
+    const int per_wave = (ntiles + 3) / 4;
+    if (per_wave <= 1) return launch_cfg<4, 1>(p, mode, s);
+    if (per_wave <= 2) return launch_cfg<4, 2>(p, mode, s);
+    if (per_wave <= 4) return launch_cfg<4, 4>(p, mode, s);
+    return launch_cfg<4, 8>(p, mode, s);
 }
 
 }  // namespace bl

@@ -172,7 +172,7 @@ def _check_forward(M, K, N, bits, gran, epi, ydt, with_bias, fused, x_dtype="f32
 
 
 # decode path (GEMV, M <= 8, K % 64 == 0)
-@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8])
+@pytest.mark.parametrize("M", [1, 2, 3, 5, 8, 11, 16])
 @pytest.mark.parametrize("K,N", [(256, 512), (64, 17), (2560, 300), (6912, 129)])
 @pytest.mark.parametrize("bits", [8, 4])
 def test_forward_decode_shapes(M, K, N, bits):
