@@ -22,7 +22,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libbitlinear.so")
-SOURCES = ["api.hip", "wquant.hip", "aquant.hip", "gemv.hip", "gemm.hip"]
+SOURCES = ["api.hip", "wquant.hip", "aquant.hip", "gemv.hip", "gemm.hip", "gemm_big.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -30,7 +30,7 @@ FLAGS = [
     "-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt",
     "-fno-gpu-flush-denormals-to-zero",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-Wall", "-Wno-unused-function",
+    "-Wall", "-Wno-unused-function", "-Wno-inline-asm",
     "-I", os.path.join(ROOT, "include"),
 ]
 

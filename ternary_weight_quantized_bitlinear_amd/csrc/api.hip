@@ -194,6 +194,13 @@ static bl::FwdArgs make_args(const void *x, int x_bf16, int bits, const float *a
     return a;
 }
 
+// forward on quantized activations: decode GEMV, large-tile GEMM or general GEMM
+static hipError_t launch_forward(const bl::FwdArgs &a, void *ws, hipStream_t s) {
+    if (bl::gemv_supports(a.M, a.K)) return bl::launch_gemv(a, false, ws, s);
+    if (bl::gemm_big_supports(a.M, a.N, a.K, a.bits)) return bl::launch_gemm_big(a, s);
+    return bl::launch_gemm(a, ws, s);
+}
+
 bl_status bitlinear_forward(const void *Xq, int bits, const float *act_scale, bl_gran gran,
                             const uint8_t *W_packed, const float *gamma, const float *bias,
                             int64_t M, int64_t N, int64_t K, bl_epi epi, void *Y,
@@ -210,9 +217,7 @@ bl_status bitlinear_forward(const void *Xq, int bits, const float *act_scale, bl
     const bl::FwdArgs a = make_args(Xq, 0, bits, act_scale, gran, 0.0f, W_packed, gamma, bias, M,
                                     N, K, epi, Y, y_dtype);
     (void)hipGetLastError();
-    hipError_t e = bl::gemv_supports(M, K) ? bl::launch_gemv(a, false, workspace, (hipStream_t)stream)
-                                           : bl::launch_gemm(a, workspace, (hipStream_t)stream);
-    return device(e, fn);
+    return device(launch_forward(a, workspace, (hipStream_t)stream), fn);
 }
 
 bl_status bitlinear_forward_fused(const void *X, bl_dtype x_dtype, int bits, bl_gran gran,
@@ -248,7 +253,7 @@ bl_status bitlinear_forward_fused(const void *X, bl_dtype x_dtype, int bits, bl_
     if (e != hipSuccess) return device(e, fn);
     const bl::FwdArgs a = make_args(xq, 0, bits, scale, gran, eps, W_packed, gamma, bias, M, N, K,
                                     epi, Y, y_dtype);
-    return device(bl::launch_gemm(a, gemm_ws, s), fn);
+    return device(launch_forward(a, gemm_ws, s), fn);
 }
 
 }  // extern "C"

@@ -169,6 +169,9 @@ hipError_t launch_gemv(const FwdArgs &a, bool fused, void *ws, hipStream_t s);
 size_t ws_gemv(int gran);
 // prefill-sized M: int8 MFMA GEMM on quantized activations
 hipError_t launch_gemm(const FwdArgs &a, void *ws, hipStream_t s);
+// prefill-sized M with whole 64-wide k steps: 256x256 tiles, LDS ring, 32x32x32 MFMA
+bool gemm_big_supports(int64_t M, int64_t N, int64_t K, int bits);
+hipError_t launch_gemm_big(const FwdArgs &a, hipStream_t s);
 size_t ws_gemm(int64_t M, int64_t N, int64_t K);
 
 }  // namespace bl
