@@ -26,6 +26,7 @@ cpu_baseline = the CPU oracle on the same decode step, single-threaded
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import platform
@@ -41,11 +42,41 @@ HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, GB/s
 INT8_PEAK_TOPS = 5000.0         # MI355X dense int8 MFMA, TOPS (5.0 POP/s)
 MALL_BYTES = 256 << 20          # Infinity Cache
 METRIC = "BitLinear decode GEMV HBM GB/s + prefill GEMM int TOPS, % of MI355X roofline"
+CSRC = os.path.join(ROOT, "ternary_weight_quantized_bitlinear_amd", "csrc")
+# HBM traffic of the decode GEMV, from two rocprofv3 --pmc runs of the "traffic" leg
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "gemv_decode_2b_traffic.txt")
+GEMV_SOURCES = ("gemv.hip", "common.hpp")
 
 
 def gemv_bytes(K: int, N: int) -> int:
     """Algorithmic bytes of one decode GEMV: packed W + bf16 x + bf16 y + gamma."""
     return N * K // 4 + 2 * K + 2 * N + 4
+
+
+def gemv_source_digest() -> str:
+    """Digest of the sources the decode GEMV kernel is built from."""
+    h = hashlib.sha256()
+    for name in GEMV_SOURCES:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per decode GEMV launch from the committed counter summary, or None when
+    there is none or the kernel sources changed after the counters were taken."""
+    try:
+        with open(TRAFFIC_PROFILE) as f:
+            kv = dict(line.split(":", 1) for line in f if ":" in line and not line.startswith(" "))
+    except OSError:
+        return None
+    kv = {k.strip(): v.strip() for k, v in kv.items()}
+    if kv.get("kernel_source_digest") != gemv_source_digest():
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def cpu_model() -> str:
@@ -211,6 +242,37 @@ def leg_prefill(torch, bl, reps=20):
     return res
 
 
+def leg_traffic(torch, bl, reps=16, copies=64):
+    """Eager launches for the counter runs (rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE):
+    the two decode GEMVs over rotating weight copies, and a plain int32 streaming kernel of
+    known size (256 MiB read, 256 MiB written) that calibrates what the counters report."""
+    import workloads
+    dev = torch.device("cuda:0")
+    for name, shape, epi in (("up", workloads.SHAPE_UP, "relu2"),
+                             ("down", workloads.SHAPE_DOWN, None)):
+        K, N = shape
+        W, x = workloads.decode_gemv(seed=1, shape=shape)
+        ws = make_weight_copies(torch, bl, W, copies, 31)
+        xd = torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+        y = torch.empty((1, N), dtype=torch.bfloat16, device=dev)
+        for i in range(reps):
+            p, g = ws[(7 * i) % copies]
+            bl.forward_fused(xd, p, g, epilogue=epi, out=y)
+        torch.cuda.synchronize()
+        print("traffic leg: %d launches of the %s GEMV (K=%d, N=%d), %d B algorithmic each"
+              % (reps, name, K, N, gemv_bytes(K, N)), flush=True)
+        del ws
+    n = 64 << 20
+    src = torch.arange(n, dtype=torch.int32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(4):
+        torch.bitwise_not(src, out=dst)
+    torch.cuda.synchronize()
+    print("traffic leg: 4 launches of bitwise_not over %d B int32 (reads %d B, writes %d B)"
+          % (4 * n, 4 * n, 4 * n), flush=True)
+    print("traffic leg: gemv source digest %s" % gemv_source_digest(), flush=True)
+
+
 def leg_pack(torch, bl, reps=10):
     """a1: weight quantization + packing of the 2B up projection, fp32 W in HBM."""
     import workloads
@@ -276,6 +338,18 @@ def main():
         import __graft_entry__
         __graft_entry__.build()
     legs = set(args.legs.split(","))
+    if "traffic" in legs:
+        leg_traffic(torch, bl)
+    if "decode" not in legs:
+        # counter runs: only the named legs, no headline line
+        side = {}
+        if "prefill" in legs:
+            side["prefill"] = leg_prefill(torch, bl)
+        if "pack" in legs:
+            side["pack"] = leg_pack(torch, bl)
+        if side:
+            print(json.dumps(side))
+        return
 
     dec = leg_decode(torch, bl, args.steps, args.warmup, args.copies)
     out = {
@@ -302,7 +376,7 @@ def main():
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(dec["bytes_per_launch"] / (dec["per_launch_us"] * 1e-6) / 1e9
                                    / HBM_PEAK_GBS, 4),
-                     "traffic": None,
+                     "traffic": measured_traffic(),
                      "bytes_per_launch": dec["bytes_per_launch"],
                      "us_per_launch": dec["per_launch_us"]},
     }
