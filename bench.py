@@ -1,27 +1,29 @@
 """Benchmark of the MI355X BitLinear forward pass.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--legs decode,prefill,pack]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--legs decode,chain,single,prefill,pack,cpu]
 
-Headline (one JSON line on stdout): decode-GEMV HBM throughput on the BitNet 2B
-FFN shapes at M=1 token.  One step = the FFN of one block at decode time:
-    x (bf16 [1, 2560])  --up 2560->6912, ReLU^2-->  h (bf16 [1, 6912])
-                        --down 6912->2560-->         y (bf16 [1, 2560])
-Each projection is one bitlinear_forward_fused launch: per-token absmax int8
-quantization of its input (for down: the requantization of up's output), the
-ternary GEMV with int32 accumulation and the rescale epilogue.  Packed weights
-are pre-quantized (bitlinear_quantize_weights, timed separately as the "pack"
-leg): the pages treat weights as static.
+Headline (one JSON line on stdout): decode-GEMV HBM throughput on the BitNet 2B FFN
+shapes at M=1 token, streamed.  One step = the FFN of 64 independent 2B-shaped layers
+(64 distinct weight sets, 566 MB, more than twice the 256 MB Infinity Cache, so the
+weight stream really comes from HBM), each at decode time:
+    x_b (bf16 [1, 2560])  --up 2560->6912, ReLU^2-->  h_b (bf16 [1, 6912])
+                          --down 6912->2560-->         y_b (bf16 [1, 2560])
+as two launches of bitlinear_forward_fused_batched (all 64 up projections, then all 64
+down projections).  Each fuses per-token absmax int8 quantization of its input (for
+down: the requantization of up's output), the ternary GEMV with int32 accumulation and
+the rescale epilogue.  Packed weights are pre-quantized (bitlinear_quantize_weights,
+timed separately as the "pack" leg): the pages treat weights as static.
 
-Inputs are resident in HBM before timing.  Weights rotate through 64 distinct
-copies per shape (566 MB, more than twice the 256 MB Infinity Cache), so the
-weight stream really comes from HBM.  The K timed steps are captured in one HIP
-graph (host launch overhead would otherwise dominate a ~2 us GEMV) and timed
-with HIP events on the stream the kernels run on.
+Inputs are resident in HBM before timing.  The K timed steps are captured in one HIP
+graph and timed with HIP events on the stream the kernels run on.
 
-value      = algorithmic bytes per step / time per step (GB/s, 1e9 B/s)
-roofline   = the GEMV kernel against MI355X HBM (8 TB/s)
-prefill    = the prefill GEMM leg: M=2048 tokens, int TOPS against int8 MFMA peak
-cpu_baseline = the CPU oracle on the same decode step, single-threaded
+value        = algorithmic bytes per step / time per step (GB/s, 1e9 B/s)
+roofline     = the batched GEMV kernel against MI355X HBM (8 TB/s); traffic from the
+               committed FETCH_SIZE/WRITE_SIZE counter summary while it matches the
+               kernel sources
+decode_chain = one layer's FFN step alone (two dependent 4.4 MB launches: latency-bound)
+prefill      = the prefill GEMM leg: M=2048 tokens, int TOPS against int8 MFMA peak
+cpu_baseline = the CPU oracle on one layer's decode FFN step, single-threaded
 """
 from __future__ import annotations
 
@@ -174,6 +176,64 @@ def leg_decode(torch, bl, steps, warmup, copies):
     }
 
 
+def make_weight_batch(torch, bl, W0, batch, seed):
+    """[batch, N, K/4] packed weights + gamma [batch]: problem 0 from the seeded host
+    weights, the others distinct uniform-ternary tensors drawn on the device."""
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    N, K = W0.shape
+    packed = torch.empty((batch, N, K // 4), dtype=torch.uint8, device=dev)
+    gamma = torch.empty((batch,), dtype=torch.float32, device=dev)
+    for b in range(batch):
+        if b == 0:
+            W = torch.from_numpy(W0).to(dev)
+        else:
+            W = torch.randint(-1, 2, (N, K), device=dev, generator=gen, dtype=torch.int8).float()
+        bl.quantize_weights(W, out=(packed[b], gamma[b:b + 1]))
+        del W
+    torch.cuda.synchronize()
+    return packed, gamma
+
+
+def leg_decode_stream(torch, bl, steps, warmup, batch):
+    """Headline: the FFN decode step of `batch` independent 2B-shaped layers, M=1 each.
+    Per step two launches of bitlinear_forward_fused_batched: up (x_b -> h_b, ReLU^2) over
+    all layers, then down (h_b requantized -> y_b).  The K timed steps are one HIP graph."""
+    import workloads
+    dev = torch.device("cuda:0")
+    (K1, N1), (K2, N2) = workloads.SHAPE_UP, workloads.SHAPE_DOWN
+    W_up, x = workloads.decode_gemv(seed=1, shape=workloads.SHAPE_UP)
+    W_dn, _ = workloads.decode_gemv(seed=1, shape=workloads.SHAPE_DOWN)
+    pu, gu = make_weight_batch(torch, bl, W_up, batch, 41)
+    pd, gd = make_weight_batch(torch, bl, W_dn, batch, 42)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(43)
+    X = torch.randn((batch, 1, K1), device=dev, generator=gen).to(torch.bfloat16)
+    X[0, 0] = torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)[0]
+    h = torch.empty((batch, 1, N1), dtype=torch.bfloat16, device=dev)
+    y = torch.empty((batch, 1, N2), dtype=torch.bfloat16, device=dev)
+
+    def step():
+        bl.forward_fused_batched(X, pu, gu, epilogue="relu2", out=h)
+        bl.forward_fused_batched(h, pd, gd, out=y)
+
+    def run_k():
+        for _ in range(steps):
+            step()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ms_total, _ = graph_time_ms(torch, run_k, replays=1, warm=1)
+    ms_step = ms_total / steps
+    step_bytes = batch * (gemv_bytes(K1, N1) + gemv_bytes(K2, N2))
+    return {"ms_per_step": ms_step, "gbs": step_bytes / (ms_step * 1e-3) / 1e9,
+            "step_bytes": step_bytes, "per_launch_us": ms_step * 1e3 / 2,
+            "bytes_per_launch": step_bytes / 2, "batch": batch, "x": x, "W_up": W_up,
+            "W_dn": W_dn}
+
+
 def leg_decode_single(torch, bl, copies=64, reps=200):
     """Each GEMV alone (up, then down), rotating copies, graph-captured: per-launch time."""
     import workloads
@@ -242,26 +302,27 @@ def leg_prefill(torch, bl, reps=20):
     return res
 
 
-def leg_traffic(torch, bl, reps=16, copies=64):
+def leg_traffic(torch, bl, reps=4, batch=64):
     """Eager launches for the counter runs (rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE):
-    the two decode GEMVs over rotating weight copies, and a plain int32 streaming kernel of
-    known size (256 MiB read, 256 MiB written) that calibrates what the counters report."""
+    the two streamed decode launches of the headline (batched fused GEMV over `batch`
+    layers), and a plain int32 streaming kernel of known size (256 MiB read, 256 MiB
+    written) that calibrates what the counters report."""
     import workloads
     dev = torch.device("cuda:0")
     for name, shape, epi in (("up", workloads.SHAPE_UP, "relu2"),
                              ("down", workloads.SHAPE_DOWN, None)):
         K, N = shape
         W, x = workloads.decode_gemv(seed=1, shape=shape)
-        ws = make_weight_copies(torch, bl, W, copies, 31)
-        xd = torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
-        y = torch.empty((1, N), dtype=torch.bfloat16, device=dev)
-        for i in range(reps):
-            p, g = ws[(7 * i) % copies]
-            bl.forward_fused(xd, p, g, epilogue=epi, out=y)
+        packed, gamma = make_weight_batch(torch, bl, W, batch, 31)
+        X = torch.randn((batch, 1, K), device=dev).to(torch.bfloat16)
+        y = torch.empty((batch, 1, N), dtype=torch.bfloat16, device=dev)
+        for _ in range(reps):
+            bl.forward_fused_batched(X, packed, gamma, epilogue=epi, out=y)
         torch.cuda.synchronize()
-        print("traffic leg: %d launches of the %s GEMV (K=%d, N=%d), %d B algorithmic each"
-              % (reps, name, K, N, gemv_bytes(K, N)), flush=True)
-        del ws
+        print("traffic leg: %d launches of the batched %s GEMV (%d layers, K=%d, N=%d), "
+              "%d B algorithmic each" % (reps, name, batch, K, N, batch * gemv_bytes(K, N)),
+              flush=True)
+        del packed
     n = 64 << 20
     src = torch.arange(n, dtype=torch.int32, device=dev)
     dst = torch.empty_like(src)
@@ -324,8 +385,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--copies", type=int, default=64)
-    ap.add_argument("--legs", default="decode,single,prefill,pack,cpu")
+    ap.add_argument("--batch", type=int, default=64, help="layers per streamed launch")
+    ap.add_argument("--copies", type=int, default=64, help="weight copies of the chain leg")
+    ap.add_argument("--chain-steps", type=int, default=2000)
+    ap.add_argument("--legs", default="decode,chain,single,prefill,pack,cpu")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -351,35 +414,43 @@ def main():
             print(json.dumps(side))
         return
 
-    dec = leg_decode(torch, bl, args.steps, args.warmup, args.copies)
+    st = leg_decode_stream(torch, bl, args.steps, args.warmup, args.batch)
+    alg = st["bytes_per_launch"] / (st["per_launch_us"] * 1e-6) / 1e9
     out = {
         "metric": METRIC,
-        "value": round(dec["gbs"], 2),
+        "value": round(st["gbs"], 2),
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": dec["ms_per_step"],
+        "ms_per_step": st["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "int8 x ternary -> int32 acc, fp32 rescale, bf16 io",
         "data": "synthetic: seeded uniform-ternary weights, N(0,1) bf16 activations",
-        "config": {"workload": "BitNet-2B FFN decode step, M=1: up 2560->6912 (+ReLU^2) then "
-                               "down 6912->2560, fused int8 per-token quantization, bf16 out",
-                   "tokens": 1, "hidden": 2560, "ffn": 6912,
-                   "weight_copies_rotated": dec["weight_copies"],
-                   "rotation_bytes": dec["rotation_bytes"]},
-        "roofline": {"bound": "hbm", "kernel": "gemv_kernel (fused decode GEMV)",
-                     "achieved": round(dec["bytes_per_launch"] / (dec["per_launch_us"] * 1e-6)
-                                       / 1e9, 2),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(dec["bytes_per_launch"] / (dec["per_launch_us"] * 1e-6) / 1e9
-                                   / HBM_PEAK_GBS, 4),
+        "config": {"workload": "BitNet-2B FFN decode GEMVs, M=1, streamed: %d independent layers "
+                               "per launch; step = up 2560->6912 (+ReLU^2) then down 6912->2560 "
+                               "on every layer, fused int8 per-token quantization, bf16 out"
+                               % st["batch"],
+                   "tokens_per_layer": 1, "hidden": 2560, "ffn": 6912,
+                   "layers_per_launch": st["batch"], "weight_bytes_per_step": st["step_bytes"]},
+        "roofline": {"bound": "hbm", "kernel": "gemv_kernel (fused decode GEMV, batched)",
+                     "achieved": round(alg, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(alg / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(),
-                     "bytes_per_launch": dec["bytes_per_launch"],
-                     "us_per_launch": dec["per_launch_us"]},
+                     "bytes_per_launch": st["bytes_per_launch"],
+                     "us_per_launch": st["per_launch_us"]},
     }
+    if "chain" in legs:
+        dec = leg_decode(torch, bl, args.chain_steps, args.warmup, args.copies)
+        out["decode_chain"] = {
+            "workload": "one 2B FFN decode step, M=1, single layer: up (+ReLU^2) then down, two "
+                        "dependent launches; %d weight copies rotated (%d B)" % (
+                            dec["weight_copies"], dec["rotation_bytes"]),
+            "us_per_step": dec["ms_per_step"] * 1e3, "gbs": round(dec["gbs"], 2),
+            "frac": round(dec["gbs"] / HBM_PEAK_GBS, 4),
+            "us_per_launch": dec["per_launch_us"]}
     if "single" in legs:
         out["decode_single"] = leg_decode_single(torch, bl)
     if "prefill" in legs:
@@ -395,7 +466,7 @@ def main():
     if "pack" in legs:
         out["pack"] = leg_pack(torch, bl)
     if "cpu" in legs:
-        out["cpu_baseline"] = cpu_baseline(dec["x"], dec["W_up"], dec["W_dn"])
+        out["cpu_baseline"] = cpu_baseline(st["x"], st["W_up"], st["W_dn"])
     out["device"] = torch.cuda.get_device_name(0)
     print(json.dumps(out))
 

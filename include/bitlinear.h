@@ -157,6 +157,28 @@ bl_status bitlinear_forward_fused(const void *X, bl_dtype x_dtype, int bits, bl_
                                   void *Y, bl_dtype y_dtype, void *workspace,
                                   size_t workspace_bytes, void *stream);
 
+/*
+ * bitlinear_forward_fused over `batch` independent layers of one shape, in one
+ * launch where the shape allows (decode-sized M): problem b computes exactly what
+ * bitlinear_forward_fused computes on
+ *   X + b*M*K elements, W_packed + b*N*K/4 bytes, gamma[b], bias + b*N (if bias),
+ *   Y + b*M*N elements,
+ * i.e. X is [batch][M][K], W_packed [batch][N][K/4], gamma [batch], bias
+ * [batch][N] or NULL, Y [batch][M][N], all contiguous.  Same equations and
+ * citations as bitlinear_forward_fused: each problem's scales come from its own
+ * X ([b158] eq. 2), its own gamma ([b158] eq. 1) and its own rescale ([b158] eq. 3).
+ * Every problem's base pointers must meet bitlinear_forward_fused's alignment.
+ * 1 <= batch <= 65535.  workspace: >= bitlinear_workspace_size(BL_OP_FORWARD_FUSED,
+ * M, N, K, bits, gran) bytes (shapes that need more than one launch run the
+ * problems one after another on `stream`, reusing it).
+ */
+bl_status bitlinear_forward_fused_batched(const void *X, bl_dtype x_dtype, int bits,
+                                          bl_gran gran, float eps, const uint8_t *W_packed,
+                                          const float *gamma, const float *bias, int64_t batch,
+                                          int64_t M, int64_t N, int64_t K, bl_epi epi, void *Y,
+                                          bl_dtype y_dtype, void *workspace,
+                                          size_t workspace_bytes, void *stream);
+
 /* Workspace bytes a call needs for these sizes (0 if none).  bits and gran are
  * ignored where they do not matter.  Never fails; returns 0 for invalid sizes. */
 size_t bitlinear_workspace_size(bl_op op, int64_t M, int64_t N, int64_t K, int bits,

@@ -12,6 +12,7 @@ The functions mirror the C entry points:
 * :func:`quantize_acts`     -> ``bitlinear_quantize_acts``
 * :func:`forward`           -> ``bitlinear_forward``
 * :func:`forward_fused`     -> ``bitlinear_forward_fused``
+* :func:`forward_fused_batched` -> ``bitlinear_forward_fused_batched``
 """
 from __future__ import annotations
 
@@ -55,6 +56,8 @@ def lib() -> ctypes.CDLL:
         L.bitlinear_forward.argtypes = [P, I, P, I, P, P, P, I64, I64, I64, I, P, I, P, SZ, P]
         L.bitlinear_forward_fused.argtypes = [P, I, I, I, F, P, P, P, I64, I64, I64, I, P, I, P,
                                               SZ, P]
+        L.bitlinear_forward_fused_batched.argtypes = [P, I, I, I, F, P, P, P, I64, I64, I64, I64,
+                                                      I, P, I, P, SZ, P]
         L.bitlinear_workspace_size.argtypes = [I, I64, I64, I64, I, I]
         L.bitlinear_workspace_size.restype = SZ
         L.bitlinear_status_string.argtypes = [I]
@@ -63,7 +66,7 @@ def lib() -> ctypes.CDLL:
         L.bitlinear_last_error.restype = ctypes.c_char_p
         L.bitlinear_version.restype = I
         for n in ("bitlinear_quantize_weights", "bitlinear_quantize_acts", "bitlinear_forward",
-                  "bitlinear_forward_fused"):
+                  "bitlinear_forward_fused", "bitlinear_forward_fused_batched"):
             getattr(L, n).restype = I
         _lib = L
     return _lib
@@ -206,4 +209,24 @@ def forward_fused(X, packed, gamma, bits: int = 8, gran="token", eps: float = 1e
                                          _ptr(gamma), _ptr(bias), M, N, K, _epi_code(epilogue),
                                          _ptr(out), _dtype_code(out), _ptr(ws), wsb,
                                          _stream(X.device, stream)))
+    return out
+
+
+def forward_fused_batched(X, packed, gamma, bits: int = 8, gran="token", eps: float = 1e-5,
+                          bias=None, epilogue=None, out_dtype=None, workspace=None, stream=None,
+                          out=None):
+    """`batch` independent layers of one shape: X [B, M, K], packed [B, N, K/4], gamma [B],
+    bias [B, N] or None -> Y [B, M, N]; problem b is forward_fused(X[b], packed[b], ...)."""
+    torch = _torch()
+    B, M, K = X.shape
+    N = packed.shape[1]
+    g = _gran_code(gran)
+    if out is None:
+        out = torch.empty((B, M, N), dtype=out_dtype or torch.float32, device=X.device)
+    ws, wsb = _workspace(workspace_size(BL_OP_FORWARD_FUSED, M, N, K, bits, g), X.device,
+                         workspace)
+    _check(lib().bitlinear_forward_fused_batched(
+        _ptr(X), _dtype_code(X), bits, g, eps, _ptr(packed), _ptr(gamma), _ptr(bias), B, M, N, K,
+        _epi_code(epilogue), _ptr(out), _dtype_code(out), _ptr(ws), wsb,
+        _stream(X.device, stream)))
     return out

@@ -256,4 +256,47 @@ bl_status bitlinear_forward_fused(const void *X, bl_dtype x_dtype, int bits, bl_
     return device(launch_forward(a, gemm_ws, s), fn);
 }
 
+bl_status bitlinear_forward_fused_batched(const void *X, bl_dtype x_dtype, int bits,
+                                          bl_gran gran, float eps, const uint8_t *W_packed,
+                                          const float *gamma, const float *bias, int64_t batch,
+                                          int64_t M, int64_t N, int64_t K, bl_epi epi, void *Y,
+                                          bl_dtype y_dtype, void *workspace,
+                                          size_t workspace_bytes, void *stream) {
+    static const char fn[] = "bitlinear_forward_fused_batched";
+    if (!X) return fail(BL_EINVAL, "%s: null pointer", fn);
+    if (!is_xdtype(x_dtype)) return fail(BL_EINVAL, "%s: x_dtype must be BL_F32 or BL_BF16", fn);
+    if (batch < 1 || batch > 65535)
+        return fail(BL_ESHAPE, "%s: batch=%lld must be in [1, 65535]", fn, (long long)batch);
+    CHECK(check_forward_common(fn, bits, gran, W_packed, gamma, bias, M, N, K, epi, Y, y_dtype));
+    CHECK(check_eps(eps, fn));
+    if (!aligned(X, 16)) return fail(BL_EALIGN, "%s: X needs 16-byte alignment", fn);
+    // byte strides between problems; every problem's pointers keep the single-call alignment
+    const int64_t xs = M * K * (x_dtype == BL_BF16 ? 2 : 4);
+    const int64_t ws_ = N * (K / 4);
+    const int64_t ys = M * N * (y_dtype == BL_BF16 ? 2 : 4);
+    if (batch > 1 && (xs % 16 != 0 || ws_ % 16 != 0 || ys % 16 != 0))
+        return fail(BL_EALIGN, "%s: per-problem strides (X %lld, W %lld, Y %lld bytes) must be "
+                    "multiples of 16", fn, (long long)xs, (long long)ws_, (long long)ys);
+    if (batch * ws_ >= (1ll << 40) || batch * xs >= (1ll << 40) || batch * ys >= (1ll << 40))
+        return fail(BL_ESHAPE, "%s: batch too large for these sizes", fn);
+    const size_t need = ws_fused(M, K, bits, gran);
+    if (need && (!workspace || workspace_bytes < need || !aligned(workspace, 256)))
+        return fail(BL_EWORKSPACE, "%s: need %zu bytes of 256-byte aligned workspace", fn, need);
+    (void)hipGetLastError();
+    if (bl::gemv_supports(M, K)) {
+        bl::FwdArgs a = make_args(X, x_dtype == BL_BF16, bits, nullptr, gran, eps, W_packed, gamma,
+                                  bias, M, N, K, epi, Y, y_dtype);
+        a.batch = batch;
+        return device(bl::launch_gemv(a, true, workspace, (hipStream_t)stream), fn);
+    }
+    for (int64_t b = 0; b < batch; ++b) {
+        const bl_status st = bitlinear_forward_fused(
+            static_cast<const uint8_t *>(X) + b * xs, x_dtype, bits, gran, eps, W_packed + b * ws_,
+            gamma + b, bias ? bias + b * N : nullptr, M, N, K, epi,
+            static_cast<uint8_t *>(Y) + b * ys, y_dtype, workspace, workspace_bytes, stream);
+        if (st != BL_OK) return st;
+    }
+    return ok();
+}
+
 }  // extern "C"

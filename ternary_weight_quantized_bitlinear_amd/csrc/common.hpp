@@ -153,6 +153,7 @@ struct FwdArgs {
     int epi;               // 0 none, 1 relu2
     void *y;
     int y_dtype;           // 0 f32, 1 bf16, 2 i32
+    int64_t batch = 1;     // independent problems laid out back to back (GEMV path)
 };
 
 hipError_t launch_zero_u32(uint32_t *p, int64_t n, hipStream_t s);

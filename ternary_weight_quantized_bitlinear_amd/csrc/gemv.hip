@@ -34,6 +34,9 @@
 //
 // Epilogue.  The waves' 16x16 partial tiles are summed through LDS; the first wave
 // applies f = gamma/s (int8) or s*gamma (int4), bias, ReLU^2, and stores.
+#include <algorithm>
+#include <atomic>
+
 #include "common.hpp"
 
 namespace bl {
@@ -58,6 +61,8 @@ struct GemvParams {
     int epi;
     void *y;
     int y_dtype;
+    // problem blockIdx.y starts this many bytes further on (0 for a single problem)
+    int64_t x_bstride, w_bstride, y_bstride;
 };
 
 __device__ __forceinline__ int dot4(uint32_t a, uint32_t b, int c) {
@@ -162,6 +167,15 @@ __device__ __forceinline__ void codes_store(const uint4 (&r)[RawWords<kMode>::n]
 template <int kMode, int kBits, int kWaves, int kMaxTilesPerWave>
 __global__ void __launch_bounds__(kWaves * 64) gemv_kernel(GemvParams p) {
     constexpr int kThreads = kWaves * 64;
+    if (gridDim.y > 1) {  // batched: move to problem blockIdx.y (uniform)
+        const int64_t b = blockIdx.y;
+        p.x = static_cast<const uint8_t *>(p.x) + b * p.x_bstride;
+        p.w += b * p.w_bstride;
+        p.gamma += b;
+        if (p.bias) p.bias += b * p.N;
+        if (p.act_scale) p.act_scale += b * (p.gran == 1 ? 1 : p.M);
+        p.y = static_cast<uint8_t *>(p.y) + b * p.y_bstride;
+    }
     extern __shared__ __attribute__((aligned(16))) uint8_t xl[];  // [M][K] int8, k-interleaved
     __shared__ float s_f[kMaxM];        // dequant factor per token
     __shared__ float s_sc[kMaxM];       // activation scale per token
@@ -371,14 +385,291 @@ __global__ void __launch_bounds__(kWaves * 64) gemv_kernel(GemvParams p) {
     }
 }
 
+// ---------------------------------------------------------------- streaming variant
+// For many row tiles per launch (a batch of layers, or a very wide layer): the weight
+// stream has to stay in flight for the whole launch, and the issue cost per weight
+// byte has to stay well below what the stream allows (about 1 KB per SIMD every
+// ~300 cycles at full HBM rate), so the work is reorganised.
+//  - A block owns a contiguous range of 64-row groups of one problem (blockIdx.y).
+//    It brings that problem's activations into LDS once (quantizing them, for the
+//    fused modes), plus sum_k q[m][k] per token (the offset-binary correction) and
+//    the bias of its rows.  LDS rows are zero-padded to a multiple of 256 k and
+//    absent tokens read a zero row, so the main loop needs no masks or clamps.
+//  - Wave w owns row tile 4g + w (16 rows) of each group g over the full K: no
+//    cross-wave reduction and no barrier after the prologue.
+//  - A wave's weight loads form one flat sequence over (group, 256-wide k tile):
+//    lane (r16 = l%16, c = l/16) reads bytes [64t + 16c, +16) of row r16 of the tile
+//    with a buffer load at a fixed per-lane offset plus a uniform (group, tile)
+//    offset; rows past N (and loads past the wave's last tile, sent 2 GB out) fall
+//    outside the buffer's range and return zeros without touching memory.  A ring of kDepth registers keeps kDepth tiles in flight per lane.
+//  - Per tile: weight dword d (16 codes, byte q holds k = 16d + 4q + i in bits 2i)
+//    yields field i of all four dwords with one AND (fields scaled by 4^i, i < 3,
+//    still valid int8) or a shift and an AND (i = 3); MFMA i pairs them with the
+//    activations k = 16d + 4q + i, stored in that order in LDS by the prologue, and
+//    accumulates into acc[i].  The row-tile epilogue takes acc0 + acc1/4 + acc2/16 +
+//    acc3 - sum_k q (all exact integers), rescales and stores.
+template <int kMode, int kBits, int kDepth>
+__global__ void __launch_bounds__(256) gemv_stream_kernel(GemvParams p, int groups_per_block) {
+    constexpr int kThreads = 256;
+    // dynamic LDS: [M + 1][Kpad] int8 codes (row M all zero), then the block's bias rows
+    extern __shared__ __attribute__((aligned(16))) uint8_t xl[];
+    __shared__ float s_f[kMaxM];
+    __shared__ uint32_t s_amax[kMaxM];
+    __shared__ int s_sum[kMaxM];
+
+    {   // problem blockIdx.y (uniform)
+        const int64_t b = blockIdx.y;
+        p.x = static_cast<const uint8_t *>(p.x) + b * p.x_bstride;
+        p.w += b * p.w_bstride;
+        p.gamma += b;
+        if (p.bias) p.bias += b * p.N;
+        if (p.act_scale) p.act_scale += b * (p.gran == 1 ? 1 : p.M);
+        p.y = static_cast<uint8_t *>(p.y) + b * p.y_bstride;
+    }
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int M = p.M, K = p.K, N = p.N;
+    const int ngroups = K >> 4;                  // 16-element activation groups
+    const int ntiles = (K + 255) >> 8;           // 256-wide k tiles per row tile
+    const int Kpad = ntiles << 8;
+    const int G = (N + 63) >> 6;                 // 64-row groups
+    const int g0 = blockIdx.x * groups_per_block;
+    const int g1 = min(g0 + groups_per_block, G);
+    if (g0 >= G) return;  // whole block, before any barrier
+    const int items = g1 - g0;
+    const int r16 = lane & 15, chunk = lane >> 4;
+    const int F = items * ntiles;                // this wave's tiles
+
+    // ---- activation loads first (they retire before the weights)
+    constexpr bool kRaw = kMode == kRawBf16 || kMode == kRawF32;
+    constexpr int kWpg = RawWords<kMode>::n;
+    const int row_bytes = kMode == kRawF32 ? 4 * K : kMode == kRawBf16 ? 2 * K
+                        : kMode == kInt8 ? K : K / 2;
+    const int gbytes = row_bytes / ngroups;
+    const uint8_t *xbase = static_cast<const uint8_t *>(p.x);
+    uint4 xg0[kWpg], xg1[kWpg];
+    load_group<kMode>(xbase, row_bytes, gbytes, ngroups, 0, tid, xg0);
+    load_group<kMode>(xbase, row_bytes, gbytes, ngroups, 0, tid + kThreads, xg1);
+
+    // ---- weight ring
+    const uint32_t kw = (uint32_t)K >> 2;  // packed bytes per row
+    const __amdgpu_buffer_rsrc_t wsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t *>(p.w), (short)0, (int)((uint32_t)N * kw), 0x00020000);
+    const uint32_t voff = (uint32_t)r16 * kw + (uint32_t)chunk * 16u;
+    constexpr uint32_t kPast = 0x80000000u;  // beyond any buffer: loads return zeros
+    uint32_t lso = ((uint32_t)g0 * 64u + (uint32_t)wave * 16u) * kw;  // next load's row-tile base
+    int lt = 0, lg = 0;                                                // next load's (tile, item)
+    auto next_load = [&]() __attribute__((always_inline)) {
+        // the whole offset goes in the VGPR operand, whose range check is what makes
+        // rows past N and loads past the wave's last tile return zeros
+        const uint32_t so = lg < items ? lso + 64u * (uint32_t)lt : kPast;
+        const v4i v = __builtin_amdgcn_raw_buffer_load_b128(wsrc, voff + so, 0, 0);
+        if (++lt == ntiles) { lt = 0; ++lg; lso += 64u * kw; }
+        return v;
+    };
+    v4i ring[kDepth];
+#pragma unroll
+    for (int d = 0; d < kDepth; ++d) ring[d] = next_load();
+
+    // ---- prologue: per-token absmax, scale, codes into LDS, code sums, bias rows
+    if (tid < kMaxM) { s_amax[tid] = 0u; s_sum[tid] = 0; }
+    float *s_bias = reinterpret_cast<float *>(xl + (size_t)(M + 1) * Kpad);
+    if (p.bias) {
+#pragma unroll 1
+        for (int i = tid; i < items * 64; i += kThreads)
+            s_bias[i] = p.bias[min(g0 * 64 + i, N - 1)];
+    }
+    {   // zero padding of every row, and the zero row M
+        const int padw = (Kpad - K) >> 4;  // 16-byte words per row
+#pragma unroll 1
+        for (int i = tid; i < M * padw; i += kThreads)
+            *reinterpret_cast<uint4 *>(xl + (size_t)(i / padw) * Kpad + K + 16 * (i % padw)) =
+                make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll 1
+        for (int i = tid; i < (Kpad >> 4); i += kThreads)
+            *reinterpret_cast<uint4 *>(xl + (size_t)M * Kpad + 16 * i) = make_uint4(0u, 0u, 0u, 0u);
+    }
+    const float gamma = *p.gamma;
+    const int gpt = (ngroups + kThreads - 1) / kThreads;
+    const bool ok0 = tid < ngroups, ok1 = tid + kThreads < ngroups;
+    __syncthreads();
+    if (kRaw) {
+#pragma unroll 1
+        for (int m = 0; m < M; ++m) {
+            float mx = 0.0f;
+            if (m == 0) {
+                if (ok0) mx = fmaxf(mx, group_absmax<kMode>(xg0));
+                if (ok1) mx = fmaxf(mx, group_absmax<kMode>(xg1));
+            }
+#pragma unroll 1
+            for (int i = m == 0 ? 2 : 0; i < gpt; ++i) {
+                const int g = tid + i * kThreads;
+                if (g >= ngroups) break;
+                uint4 r[kWpg];
+                load_group<kMode>(xbase, row_bytes, gbytes, ngroups, m, g, r);
+                mx = fmaxf(mx, group_absmax<kMode>(r));
+            }
+            mx = wave_max_abs(mx);
+            if (lane == 0) atomicMax(&s_amax[m], __float_as_uint(mx));
+        }
+        __syncthreads();
+    }
+#pragma unroll 1
+    for (int m = 0; m < M; ++m) {
+        float sc = 0.0f;
+        if (kRaw) {
+            float a = __uint_as_float(s_amax[m]);
+            if (p.gran == 1)
+#pragma unroll 1
+                for (int mm = 0; mm < M; ++mm) a = fmaxf(a, __uint_as_float(s_amax[mm]));
+            a = fmaxf(a, p.eps);
+            sc = kBits == 8 ? 127.0f / a : a / 7.0f;
+        } else {
+            sc = p.act_scale[p.gran == 1 ? 0 : m];
+        }
+        if (tid == 0) s_f[m] = kBits == 8 ? gamma / sc : sc * gamma;
+        uint8_t *xrow_m = xl + (size_t)m * Kpad;
+        int csum = 0;
+#pragma unroll 1
+        for (int i = 0; i < gpt; ++i) {
+            const int g = tid + i * kThreads;
+            if (g >= ngroups) break;
+            uint4 r[kWpg];
+            if (m == 0 && i < 2) {
+#pragma unroll
+                for (int j = 0; j < kWpg; ++j) r[j] = i == 0 ? xg0[j] : xg1[j];
+            } else {
+                load_group<kMode>(xbase, row_bytes, gbytes, ngroups, m, g, r);
+            }
+            uint32_t nat[4];  // the group's 16 codes in natural order
+            if (kRaw) {
+                float v[16];
+                widen16<kMode>(r, v);
+                if (kBits == 8) {
+#pragma unroll
+                    for (int d = 0; d < 4; ++d)
+                        nat[d] = q8(v[4 * d], sc) | (q8(v[4 * d + 1], sc) << 8) |
+                                 (q8(v[4 * d + 2], sc) << 16) | (q8(v[4 * d + 3], sc) << 24);
+                } else {
+#pragma unroll
+                    for (int d = 0; d < 4; ++d) {
+                        uint32_t wd = 0;
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            wd |= ((uint32_t)(((int)(q4(v[4 * d + j], sc) << 28)) >> 28) & 0xFFu) << (8 * j);
+                        nat[d] = wd;
+                    }
+                }
+            } else if (kMode == kInt8) {
+                nat[0] = r[0].x; nat[1] = r[0].y; nat[2] = r[0].z; nat[3] = r[0].w;
+            } else {
+                nibbles_to_i8(r[0].x, nat);
+                nibbles_to_i8(r[0].y, nat + 2);
+            }
+#pragma unroll
+            for (int d = 0; d < 4; ++d) csum = __builtin_amdgcn_sdot4((int)nat[d], 0x01010101, csum, false);
+            // group g is dword d = g % 4 of its 64-k chunk; its codes k = 16d + 4q + i go
+            // to byte 4d + q of the chunk's segment i (segment = 16 bytes)
+            uint32_t il[4];
+            interleave16(nat, il);
+            uint8_t *seg = xrow_m + 64 * (g >> 2) + 4 * (g & 3);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) *reinterpret_cast<uint32_t *>(seg + 16 * i) = il[i];
+        }
+        csum = wave_sum(csum);
+        if (lane == 0) atomicAdd(&s_sum[m], csum);
+    }
+    __syncthreads();
+
+    // ---- stream
+    const uint8_t *xrow = xl + (size_t)(r16 < M ? r16 : M) * Kpad + chunk * 64;
+    float f4[4];
+    int sum4[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int m = 4 * chunk + r;
+        f4[r] = s_f[m < M ? m : 0];
+        sum4[r] = s_sum[m < M ? m : 0];
+    }
+    // the accumulators run on across row tiles (int32 wrap-around); a row tile's sums
+    // are the differences from their values at the previous row tile's end, exact
+    // because every row tile's true sum fits in int32
+    v4i acc0 = v4i{0, 0, 0, 0}, acc1 = v4i{0, 0, 0, 0}, acc2 = v4i{0, 0, 0, 0},
+        acc3 = v4i{0, 0, 0, 0};
+    v4i pre0 = acc0, pre1 = acc0, pre2 = acc0, pre3 = acc0;
+    int ug = 0, ut = 0;  // tile being consumed (uniform)
+#pragma unroll 1
+    for (int fb = 0; fb < F; fb += kDepth) {
+#pragma unroll
+        for (int d = 0; d < kDepth; ++d) {
+            const v4i wv = ring[d];
+            ring[d] = next_load();
+            if (fb + d >= F) continue;  // uniform: past this wave's last tile
+            const uint8_t *xa = xrow + ut * 256;
+            const uint4 q0 = *reinterpret_cast<const uint4 *>(xa);
+            const uint4 q1 = *reinterpret_cast<const uint4 *>(xa + 16);
+            const uint4 q2 = *reinterpret_cast<const uint4 *>(xa + 32);
+            const uint4 q3 = *reinterpret_cast<const uint4 *>(xa + 48);
+            const v4i b0 = wv & 0x03030303;
+            const v4i b1 = wv & 0x0C0C0C0C;
+            const v4i b2 = wv & 0x30303030;
+            const v4i b3 = (v4i)((__attribute__((ext_vector_type(4))) unsigned)wv >> 6u) & 0x03030303;
+            acc0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(v4i{(int)q0.x, (int)q0.y, (int)q0.z, (int)q0.w}, b0, acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(v4i{(int)q1.x, (int)q1.y, (int)q1.z, (int)q1.w}, b1, acc1, 0, 0, 0);
+            acc2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(v4i{(int)q2.x, (int)q2.y, (int)q2.z, (int)q2.w}, b2, acc2, 0, 0, 0);
+            acc3 = __builtin_amdgcn_mfma_i32_16x16x64_i8(v4i{(int)q3.x, (int)q3.y, (int)q3.z, (int)q3.w}, b3, acc3, 0, 0, 0);
+            if (++ut == ntiles) {  // row tile done: epilogue (uniform branch)
+                const int nrow = (g0 + ug) * 64 + wave * 16 + r16;
+                const v4i d0 = acc0 - pre0, d1 = acc1 - pre1, d2 = acc2 - pre2, d3 = acc3 - pre3;
+                pre0 = acc0;
+                pre1 = acc1;
+                pre2 = acc2;
+                pre3 = acc3;
+                if (nrow < N) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int m = 4 * chunk + r;
+                        if (m >= M) continue;
+                        const int a = d0[r] + d3[r] + (d1[r] >> 2) + (d2[r] >> 4) - sum4[r];
+                        const size_t idx = (size_t)m * N + nrow;
+                        if (p.y_dtype == 2) {
+                            static_cast<int32_t *>(p.y)[idx] = a;
+                        } else {
+                            float y = __fmul_rn((float)a, f4[r]);
+                            if (p.bias) y = __fadd_rn(y, s_bias[nrow - g0 * 64]);
+                            if (p.epi == 1) {
+                                const float rr = y > 0.0f ? y : 0.0f;
+                                y = __fmul_rn(rr, rr);
+                            }
+                            if (p.y_dtype == 1) static_cast<uint16_t *>(p.y)[idx] = (uint16_t)to_bf16_bits(y);
+                            else static_cast<float *>(p.y)[idx] = y;
+                        }
+                    }
+                }
+                ut = 0;
+                ++ug;
+            }
+        }
+    }
+}
+
 constexpr int64_t kMaxLds = 64 * 1024;
+// streaming kernel: 16-byte weight loads in flight per lane, and blocks per CU
+#ifndef BL_STREAM_DEPTH
+#define BL_STREAM_DEPTH 8
+#endif
+#ifndef BL_STREAM_BLOCKS_PER_CU
+#define BL_STREAM_BLOCKS_PER_CU 2
+#endif
+constexpr int kStreamDepth = BL_STREAM_DEPTH;
+constexpr int kStreamBlocksPerCu = BL_STREAM_BLOCKS_PER_CU;
 
 // the int8 codes [M][K]
 size_t lds_bytes(int64_t M, int64_t K, int) { return (size_t)(M * K); }
 
 template <int kWaves, int kT>
-hipError_t launch_cfg(const GemvParams &p, int mode, hipStream_t s) {
-    const dim3 grid((unsigned)((p.N + 15) / 16)), block(kWaves * 64);
+hipError_t launch_cfg(const GemvParams &p, int mode, int64_t batch, hipStream_t s) {
+    const dim3 grid((unsigned)((p.N + 15) / 16), (unsigned)batch), block(kWaves * 64);
     const size_t lds = lds_bytes(p.M, p.K, mode);
     if (mode == kInt8) hipLaunchKernelGGL((gemv_kernel<kInt8, 8, kWaves, kT>), grid, block, lds, s, p);
     else if (mode == kInt4) hipLaunchKernelGGL((gemv_kernel<kInt4, 4, kWaves, kT>), grid, block, lds, s, p);
@@ -387,6 +678,40 @@ hipError_t launch_cfg(const GemvParams &p, int mode, hipStream_t s) {
     else if (p.bits == 8) hipLaunchKernelGGL((gemv_kernel<kRawF32, 8, kWaves, kT>), grid, block, lds, s, p);
     else hipLaunchKernelGGL((gemv_kernel<kRawF32, 4, kWaves, kT>), grid, block, lds, s, p);
     return hipGetLastError();
+}
+
+// [M + 1][K rounded up to 256] codes, then the bias of gpb groups of 64 rows
+size_t stream_lds_bytes(int64_t M, int64_t K, bool bias, int64_t gpb) {
+    return (size_t)((M + 1) * ((K + 255) / 256 * 256)) + (bias ? (size_t)gpb * 64 * sizeof(float) : 0);
+}
+
+template <int kDepth>
+hipError_t launch_stream(const GemvParams &p, int mode, dim3 grid, int gpb, hipStream_t s) {
+    const dim3 block(256);
+    const size_t lds = stream_lds_bytes(p.M, p.K, p.bias != nullptr, gpb);
+    if (mode == kInt8) hipLaunchKernelGGL((gemv_stream_kernel<kInt8, 8, kDepth>), grid, block, lds, s, p, gpb);
+    else if (mode == kInt4) hipLaunchKernelGGL((gemv_stream_kernel<kInt4, 4, kDepth>), grid, block, lds, s, p, gpb);
+    else if (mode == kRawBf16 && p.bits == 8) hipLaunchKernelGGL((gemv_stream_kernel<kRawBf16, 8, kDepth>), grid, block, lds, s, p, gpb);
+    else if (mode == kRawBf16) hipLaunchKernelGGL((gemv_stream_kernel<kRawBf16, 4, kDepth>), grid, block, lds, s, p, gpb);
+    else if (p.bits == 8) hipLaunchKernelGGL((gemv_stream_kernel<kRawF32, 8, kDepth>), grid, block, lds, s, p, gpb);
+    else hipLaunchKernelGGL((gemv_stream_kernel<kRawF32, 4, kDepth>), grid, block, lds, s, p, gpb);
+    return hipGetLastError();
+}
+
+// compute units of the current device (cached per device)
+int device_cus() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+    if (dev < 64) {
+        const int c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+        n = 256;
+    if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+    return n;
 }
 
 }  // namespace
@@ -413,15 +738,34 @@ hipError_t launch_gemv(const FwdArgs &a, bool fused, void *, hipStream_t s) {
     p.epi = a.epi;
     p.y = a.y;
     p.y_dtype = a.y_dtype;
+    const int64_t xrow = fused ? (a.x_raw_bf16 ? 2 * a.K : 4 * a.K) : (a.bits == 8 ? a.K : a.K / 2);
+    p.x_bstride = a.M * xrow;
+    p.w_bstride = a.N * (a.K / 4);
+    p.y_bstride = a.M * a.N * (a.y_dtype == 1 ? 2 : 4);
     const int mode = fused ? (a.x_raw_bf16 ? kRawBf16 : kRawF32) : (a.bits == 8 ? kInt8 : kInt4);
+    // many 64-row groups per launch: the streaming kernel, two blocks per CU, each block
+    // a contiguous run of one problem's groups
+    const int64_t G = (a.N + 63) / 64;
+    const int64_t target = kStreamBlocksPerCu * (int64_t)device_cus();
+    if (a.batch * G >= 4 * target) {
+        const int64_t bpp = std::max<int64_t>(1, std::min<int64_t>(G, target / a.batch));
+        int64_t gpb = (G + bpp - 1) / bpp;
+        // the block's bias rows share LDS with the codes (at most 64 KB in all)
+        const int64_t codes = (int64_t)stream_lds_bytes(a.M, a.K, false, 0);
+        if (a.bias) gpb = std::min<int64_t>(gpb, (kMaxLds - codes) / 256);
+        if (codes <= kMaxLds && gpb >= 1) {
+            const dim3 grid((unsigned)((G + gpb - 1) / gpb), (unsigned)a.batch);
+            return launch_stream<kStreamDepth>(p, mode, grid, (int)gpb, s);
+        }
+    }
     // 4 waves split K; each lane issues all of its weight loads at once when the tiles
     // per wave fit the batch (K <= 8192), otherwise in batches of 8
     const int ntiles = (int)((a.K + 255) / 256);
     const int per_wave = (ntiles + 3) / 4;
-    if (per_wave <= 1) return launch_cfg<4, 1>(p, mode, s);
-    if (per_wave <= 2) return launch_cfg<4, 2>(p, mode, s);
-    if (per_wave <= 4) return launch_cfg<4, 4>(p, mode, s);
-    return launch_cfg<4, 8>(p, mode, s);
+    if (per_wave <= 1) return launch_cfg<4, 1>(p, mode, a.batch, s);
+    if (per_wave <= 2) return launch_cfg<4, 2>(p, mode, a.batch, s);
+    if (per_wave <= 4) return launch_cfg<4, 4>(p, mode, a.batch, s);
+    return launch_cfg<4, 8>(p, mode, a.batch, s);
 }
 
 }  // namespace bl

@@ -23,7 +23,7 @@ def test_exports_every_header_function(L):
     names = bl.header_functions()
     assert set(names) == {
         "bitlinear_quantize_weights", "bitlinear_quantize_acts", "bitlinear_forward",
-        "bitlinear_forward_fused", "bitlinear_workspace_size", "bitlinear_status_string",
+        "bitlinear_forward_fused", "bitlinear_forward_fused_batched", "bitlinear_workspace_size", "bitlinear_status_string",
         "bitlinear_last_error", "bitlinear_version"}
     for n in names:
         assert hasattr(L, n), n
@@ -122,6 +122,32 @@ def test_forward_fused_rejects(L):
              None) == bl.BL_EWORKSPACE
     assert f(P(A), 2, 8, 0, 1e-5, P(A), P(A), None, 1, 6912, 2560, 0, P(A), 1, None, 0,
              None) == bl.BL_EINVAL
+
+
+def test_forward_fused_batched_rejects(L):
+    f = L.bitlinear_forward_fused_batched
+
+    def call(**kw):
+        a = dict(X=P(A), xdt=1, bits=8, gran=0, eps=1e-5, W=P(A), gamma=P(A), bias=None, B=4,
+                 M=1, N=6912, K=2560, epi=0, Y=P(A), ydt=1, ws=None, wsb=0)
+        a.update(kw)
+        return f(a["X"], a["xdt"], a["bits"], a["gran"], a["eps"], a["W"], a["gamma"], a["bias"],
+                 a["B"], a["M"], a["N"], a["K"], a["epi"], a["Y"], a["ydt"], a["ws"], a["wsb"],
+                 None)
+
+    assert call(B=0) == bl.BL_ESHAPE
+    assert call(B=65536) == bl.BL_ESHAPE
+    assert call(X=None) == bl.BL_EINVAL
+    assert call(xdt=2) == bl.BL_EINVAL
+    assert call(K=100) == bl.BL_ESHAPE
+    assert call(eps=0.0) == bl.BL_EINVAL
+    # problem 1 would start 4 bytes into a 16-byte line (N*K/4 = 4 bytes of weights)
+    assert call(N=1, K=16) == bl.BL_EALIGN
+    # a bf16 output row of 3 elements puts problem 1's Y off 16-byte alignment
+    assert call(N=3, K=64) == bl.BL_EALIGN
+    # prefill-sized problems run one by one and need the fused workspace
+    assert call(M=2048) == bl.BL_EWORKSPACE
+    assert L.bitlinear_last_error().decode().startswith("bitlinear_forward_fused_batched")
 
 
 def _gpu_visible() -> bool:

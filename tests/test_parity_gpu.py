@@ -283,3 +283,54 @@ def test_forward_deterministic():
     assert_same_bytes(outs[0], outs[1], "repeat run")
     p2, g2 = bl.quantize_weights(Wd)
     assert_same_bytes(to_host(p2), to_host(packed), "repeat pack")
+
+
+# batched fused forward: independent problems of one shape in one call
+@pytest.mark.parametrize("B,M,K,N,bits,gran,epi,ydt,xdt,with_bias", [
+    (3, 1, 256, 512, 8, "token", "relu2", "f32", "f32", True),
+    (5, 5, 2560, 304, 4, "tensor", None, "bf16", "bf16", False),
+    (2, 16, 640, 48, 8, "token", None, "i32", "bf16", False),
+    (4, 1, 2560, 6912, 8, "token", "relu2", "bf16", "bf16", False),
+    (4, 1, 6912, 2560, 8, "token", None, "bf16", "bf16", False),
+    (2, 40, 256, 128, 8, "token", "relu2", "f32", "f32", True),  # one launch per problem
+    # >= 2048 groups of 64 rows per launch: the streaming kernel
+    (40, 1, 320, 4000, 8, "token", "relu2", "bf16", "bf16", False),  # ragged rows, partial k tile
+    (36, 5, 256, 4096, 4, "tensor", None, "f32", "f32", True),
+    (33, 16, 192, 4100, 8, "token", "relu2", "f32", "bf16", True),
+    (64, 2, 64, 2048, 8, "token", None, "i32", "f32", False),
+])
+def test_forward_fused_batched(B, M, K, N, bits, gran, epi, ydt, xdt, with_bias):
+    say("forward_fused_batched", dict(B=B, M=M, K=K, N=N, bits=bits, gran=gran, epi=epi, y=ydt,
+                                      x=xdt, bias=with_bias))
+    g = oracle.PER_TOKEN if gran == "token" else oracle.PER_TENSOR
+    e = oracle.EPI_RELU2 if epi == "relu2" else oracle.EPI_NONE
+    tdt, odt = YD[ydt]
+    kind = "ternary" if N * K > 1 << 20 else "gauss"
+    cases = [_layer(M, K, N, seed=10 + b, kind=kind) for b in range(B)]
+    Xin = np.stack([workloads.to_bf16_bits(X) if xdt == "bf16" else X for _, X in cases])
+    bias = (np.random.default_rng(B).standard_normal((B, N)).astype(np.float32)
+            if with_bias else None)
+    packed = torch.empty((B, N, K // 4), dtype=torch.uint8, device="cuda")
+    gamma = torch.empty((B,), dtype=torch.float32, device="cuda")
+    for b, (W, _) in enumerate(cases):
+        bl.quantize_weights(to_dev(W), out=(packed[b], gamma[b:b + 1]))
+    y = bl.forward_fused_batched(to_dev(Xin), packed, gamma, bits=bits, gran=gran,
+                                 bias=to_dev(bias) if with_bias else None, epilogue=epi,
+                                 out_dtype=tdt)
+    torch.cuda.synchronize()
+    yh = to_host(y)
+    for b, (W, _) in enumerate(cases):
+        p_ref, g_ref, _ = oracle.quantize_weights(W)
+        xq_ref, s_ref = oracle.quantize_acts(Xin[b], bits=bits, gran=g)
+        y_ref, acc_ref = oracle.forward(xq_ref, bits, s_ref, g, p_ref, g_ref,
+                                        bias=bias[b] if with_bias else None, epi=e,
+                                        y_dtype=odt if odt is not None else oracle.F32)
+        assert_y_matches(yh[b], acc_ref if ydt == "i32" else y_ref, ydt, "Y problem %d" % b)
+
+
+# one very wide layer (2048 groups of 64 rows): the streaming kernel on a single problem
+@pytest.mark.parametrize("bits", [8, 4])
+@pytest.mark.parametrize("fused", [False, True])
+def test_forward_wide_stream(bits, fused):
+    _check_forward(3, 64, 131072, bits, "token", "relu2", "f32", True, fused, sampled=False)
+    _check_forward(1, 128, 131072 + 40, bits, "tensor", None, "i32", False, fused, sampled=False)
