@@ -408,8 +408,9 @@ __global__ void __launch_bounds__(kWaves * 64) gemv_kernel(GemvParams p) {
 //    activations k = 16d + 4q + i, stored in that order in LDS by the prologue, and
 //    accumulates into acc[i].  The row-tile epilogue takes acc0 + acc1/4 + acc2/16 +
 //    acc3 - sum_k q (all exact integers), rescales and stores.
-template <int kMode, int kBits, int kDepth>
-__global__ void __launch_bounds__(256) gemv_stream_kernel(GemvParams p, int groups_per_block) {
+template <int kMode, int kBits, int kDepth, int kR>
+__global__ void __launch_bounds__(256) gemv_stream_kernel(GemvParams p, int groups_per_block,
+                                                          int xcd_order) {
     constexpr int kThreads = 256;
     // dynamic LDS: [M + 1][Kpad] int8 codes (row M all zero), then the block's bias rows
     extern __shared__ __attribute__((aligned(16))) uint8_t xl[];
@@ -417,8 +418,20 @@ __global__ void __launch_bounds__(256) gemv_stream_kernel(GemvParams p, int grou
     __shared__ uint32_t s_amax[kMaxM];
     __shared__ int s_sum[kMaxM];
 
-    {   // problem blockIdx.y (uniform)
-        const int64_t b = blockIdx.y;
+    // Workgroups go to the 8 XCDs round-robin by linear id.  With xcd_order set (the
+    // grid holds a multiple of 8 blocks) block (bx, by) is taken from the linear ids
+    // of one XCD in turn, so a problem's blocks share an XCD and its L2 fetches the
+    // problem's activations once.
+    int bx = blockIdx.x, by = blockIdx.y;
+    if (xcd_order) {
+        const int T = gridDim.x * gridDim.y;
+        const int L = blockIdx.x + gridDim.x * blockIdx.y;
+        const int q = (L & 7) * (T >> 3) + (L >> 3);
+        by = q / gridDim.x;
+        bx = q - by * gridDim.x;
+    }
+    {   // problem by (uniform)
+        const int64_t b = by;
         p.x = static_cast<const uint8_t *>(p.x) + b * p.x_bstride;
         p.w += b * p.w_bstride;
         p.gamma += b;
@@ -432,8 +445,9 @@ __global__ void __launch_bounds__(256) gemv_stream_kernel(GemvParams p, int grou
     const int ngroups = K >> 4;                  // 16-element activation groups
     const int ntiles = (K + 255) >> 8;           // 256-wide k tiles per row tile
     const int Kpad = ntiles << 8;
-    const int G = (N + 63) >> 6;                 // 64-row groups
-    const int g0 = blockIdx.x * groups_per_block;
+    constexpr int GS = 64 * kR;                  // rows per group: 4 waves x kR x 16
+    const int G = (N + GS - 1) / GS;
+    const int g0 = bx * groups_per_block;
     const int g1 = min(g0 + groups_per_block, G);
     if (g0 >= G) return;  // whole block, before any barrier
     const int items = g1 - g0;
@@ -457,27 +471,39 @@ __global__ void __launch_bounds__(256) gemv_stream_kernel(GemvParams p, int grou
         const_cast<uint8_t *>(p.w), (short)0, (int)((uint32_t)N * kw), 0x00020000);
     const uint32_t voff = (uint32_t)r16 * kw + (uint32_t)chunk * 16u;
     constexpr uint32_t kPast = 0x80000000u;  // beyond any buffer: loads return zeros
-    uint32_t lso = ((uint32_t)g0 * 64u + (uint32_t)wave * 16u) * kw;  // next load's row-tile base
-    int lt = 0, lg = 0;                                                // next load's (tile, item)
+    // next load's first row tile: wave w owns rows [g GS + 16 kR w, +16 kR) of group g
+    uint32_t lso = ((uint32_t)g0 * GS + (uint32_t)wave * 16u * kR) * kw;
+    int lt = 0, lg = 0;  // next load's (tile, item)
+    struct Tile { v4i w[kR]; };
     auto next_load = [&]() __attribute__((always_inline)) {
         // the whole offset goes in the VGPR operand, whose range check is what makes
         // rows past N and loads past the wave's last tile return zeros
-        const uint32_t so = lg < items ? lso + 64u * (uint32_t)lt : kPast;
-        const v4i v = __builtin_amdgcn_raw_buffer_load_b128(wsrc, voff + so, 0, 0);
-        if (++lt == ntiles) { lt = 0; ++lg; lso += 64u * kw; }
-        return v;
+        const uint32_t so = lso + 64u * (uint32_t)lt;
+        const bool live = lg < items;
+        Tile t;
+#pragma unroll
+        for (int j = 0; j < kR; ++j)
+            t.w[j] = __builtin_amdgcn_raw_buffer_load_b128(
+                wsrc, voff + (live ? so + 16u * kw * j : kPast), 0, 0);
+        if (++lt == ntiles) { lt = 0; ++lg; lso += (uint32_t)GS * kw; }
+        return t;
     };
-    v4i ring[kDepth];
+    Tile ring[kDepth];
 #pragma unroll
     for (int d = 0; d < kDepth; ++d) ring[d] = next_load();
 
     // ---- prologue: per-token absmax, scale, codes into LDS, code sums, bias rows
     if (tid < kMaxM) { s_amax[tid] = 0u; s_sum[tid] = 0; }
     float *s_bias = reinterpret_cast<float *>(xl + (size_t)(M + 1) * Kpad);
+    // outputs of the block's rows, [M][items * GS] in the output type, written to Y
+    // row-contiguously at the end (the row tiles' own stores would be 32-byte pieces)
+    const int ysz = p.y_dtype == 1 ? 2 : 4;
+    const int brow = items * GS;  // rows of this block (some may be past N)
+    uint8_t *s_y = reinterpret_cast<uint8_t *>(s_bias) + (p.bias ? (size_t)brow * sizeof(float) : 0);
     if (p.bias) {
 #pragma unroll 1
-        for (int i = tid; i < items * 64; i += kThreads)
-            s_bias[i] = p.bias[min(g0 * 64 + i, N - 1)];
+        for (int i = tid; i < items * GS; i += kThreads)
+            s_bias[i] = p.bias[min(g0 * GS + i, N - 1)];
     }
     {   // zero padding of every row, and the zero row M
         const int padw = (Kpad - K) >> 4;  // 16-byte words per row
@@ -594,61 +620,90 @@ __global__ void __launch_bounds__(256) gemv_stream_kernel(GemvParams p, int grou
     // the accumulators run on across row tiles (int32 wrap-around); a row tile's sums
     // are the differences from their values at the previous row tile's end, exact
     // because every row tile's true sum fits in int32
-    v4i acc0 = v4i{0, 0, 0, 0}, acc1 = v4i{0, 0, 0, 0}, acc2 = v4i{0, 0, 0, 0},
-        acc3 = v4i{0, 0, 0, 0};
-    v4i pre0 = acc0, pre1 = acc0, pre2 = acc0, pre3 = acc0;
+    v4i acc[kR][4], pre[kR][4];
+#pragma unroll
+    for (int j = 0; j < kR; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[j][i] = pre[j][i] = v4i{0, 0, 0, 0};
     int ug = 0, ut = 0;  // tile being consumed (uniform)
 #pragma unroll 1
     for (int fb = 0; fb < F; fb += kDepth) {
 #pragma unroll
         for (int d = 0; d < kDepth; ++d) {
-            const v4i wv = ring[d];
+            const Tile wt = ring[d];
             ring[d] = next_load();
             if (fb + d >= F) continue;  // uniform: past this wave's last tile
             const uint8_t *xa = xrow + ut * 256;
-            const uint4 q0 = *reinterpret_cast<const uint4 *>(xa);
-            const uint4 q1 = *reinterpret_cast<const uint4 *>(xa + 16);
-            const uint4 q2 = *reinterpret_cast<const uint4 *>(xa + 32);
-            const uint4 q3 = *reinterpret_cast<const uint4 *>(xa + 48);
-            const v4i b0 = wv & 0x03030303;
-            const v4i b1 = wv & 0x0C0C0C0C;
-            const v4i b2 = wv & 0x30303030;
-            const v4i b3 = (v4i)((__attribute__((ext_vector_type(4))) unsigned)wv >> 6u) & 0x03030303;
-            acc0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(v4i{(int)q0.x, (int)q0.y, (int)q0.z, (int)q0.w}, b0, acc0, 0, 0, 0);
-            acc1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(v4i{(int)q1.x, (int)q1.y, (int)q1.z, (int)q1.w}, b1, acc1, 0, 0, 0);
-            acc2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(v4i{(int)q2.x, (int)q2.y, (int)q2.z, (int)q2.w}, b2, acc2, 0, 0, 0);
-            acc3 = __builtin_amdgcn_mfma_i32_16x16x64_i8(v4i{(int)q3.x, (int)q3.y, (int)q3.z, (int)q3.w}, b3, acc3, 0, 0, 0);
-            if (++ut == ntiles) {  // row tile done: epilogue (uniform branch)
-                const int nrow = (g0 + ug) * 64 + wave * 16 + r16;
-                const v4i d0 = acc0 - pre0, d1 = acc1 - pre1, d2 = acc2 - pre2, d3 = acc3 - pre3;
-                pre0 = acc0;
-                pre1 = acc1;
-                pre2 = acc2;
-                pre3 = acc3;
-                if (nrow < N) {
+            v4i a[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint4 q = *reinterpret_cast<const uint4 *>(xa + 16 * i);
+                a[i] = v4i{(int)q.x, (int)q.y, (int)q.z, (int)q.w};
+            }
+#pragma unroll
+            for (int j = 0; j < kR; ++j) {
+                const v4i wv = wt.w[j];
+                const v4i b0 = wv & 0x03030303;
+                const v4i b1 = wv & 0x0C0C0C0C;
+                const v4i b2 = wv & 0x30303030;
+                const v4i b3 = (v4i)((__attribute__((ext_vector_type(4))) unsigned)wv >> 6u) & 0x03030303;
+                acc[j][0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[0], b0, acc[j][0], 0, 0, 0);
+                acc[j][1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[1], b1, acc[j][1], 0, 0, 0);
+                acc[j][2] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[2], b2, acc[j][2], 0, 0, 0);
+                acc[j][3] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[3], b3, acc[j][3], 0, 0, 0);
+            }
+            if (++ut == ntiles) {  // row tiles done: epilogue (uniform branch)
+#pragma unroll
+                for (int j = 0; j < kR; ++j) {
+                    const int nrow = (g0 + ug) * GS + (wave * kR + j) * 16 + r16;
+                    v4i dd[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        dd[i] = acc[j][i] - pre[j][i];
+                        pre[j][i] = acc[j][i];
+                    }
+                    if (nrow >= N) continue;
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int m = 4 * chunk + r;
                         if (m >= M) continue;
-                        const int a = d0[r] + d3[r] + (d1[r] >> 2) + (d2[r] >> 4) - sum4[r];
-                        const size_t idx = (size_t)m * N + nrow;
+                        const int av = dd[0][r] + dd[3][r] + (dd[1][r] >> 2) + (dd[2][r] >> 4) - sum4[r];
+                        const int sidx = m * brow + (nrow - g0 * GS);
                         if (p.y_dtype == 2) {
-                            static_cast<int32_t *>(p.y)[idx] = a;
+                            reinterpret_cast<int32_t *>(s_y)[sidx] = av;
                         } else {
-                            float y = __fmul_rn((float)a, f4[r]);
-                            if (p.bias) y = __fadd_rn(y, s_bias[nrow - g0 * 64]);
+                            float y = __fmul_rn((float)av, f4[r]);
+                            if (p.bias) y = __fadd_rn(y, s_bias[nrow - g0 * GS]);
                             if (p.epi == 1) {
                                 const float rr = y > 0.0f ? y : 0.0f;
                                 y = __fmul_rn(rr, rr);
                             }
-                            if (p.y_dtype == 1) static_cast<uint16_t *>(p.y)[idx] = (uint16_t)to_bf16_bits(y);
-                            else static_cast<float *>(p.y)[idx] = y;
+                            if (p.y_dtype == 1) reinterpret_cast<uint16_t *>(s_y)[sidx] = (uint16_t)to_bf16_bits(y);
+                            else reinterpret_cast<float *>(s_y)[sidx] = y;
                         }
                     }
                 }
                 ut = 0;
                 ++ug;
             }
+        }
+    }
+    // ---- write the block's outputs: token m's rows [g0 GS, min(g1 GS, N)) are contiguous
+    __syncthreads();
+    const int r0 = g0 * GS;
+    const int nr = min(brow, N - r0);
+#pragma unroll 1
+    for (int m = 0; m < M; ++m) {
+        if (ysz == 2) {
+            const uint16_t *src = reinterpret_cast<const uint16_t *>(s_y) + (size_t)m * brow;
+            uint16_t *dst = static_cast<uint16_t *>(p.y) + (size_t)m * N + r0;
+#pragma unroll 1
+            for (int i = tid; i < nr; i += kThreads) dst[i] = src[i];
+        } else {
+            const uint32_t *src = reinterpret_cast<const uint32_t *>(s_y) + (size_t)m * brow;
+            uint32_t *dst = static_cast<uint32_t *>(p.y) + (size_t)m * N + r0;
+#pragma unroll 1
+            for (int i = tid; i < nr; i += kThreads) dst[i] = src[i];
         }
     }
 }
@@ -661,8 +716,17 @@ constexpr int64_t kMaxLds = 64 * 1024;
 #ifndef BL_STREAM_BLOCKS_PER_CU
 #define BL_STREAM_BLOCKS_PER_CU 2
 #endif
+#ifndef BL_STREAM_ROWS
+#define BL_STREAM_ROWS 1
+#endif
+#ifndef BL_STREAM_XCD
+#define BL_STREAM_XCD 1
+#endif
 constexpr int kStreamDepth = BL_STREAM_DEPTH;
 constexpr int kStreamBlocksPerCu = BL_STREAM_BLOCKS_PER_CU;
+constexpr int kStreamRows = BL_STREAM_ROWS;      // 16-row tiles per wave item
+constexpr int kStreamXcdOrder = BL_STREAM_XCD;  // problem-per-XCD block order
+constexpr int64_t kStreamLds = 63 * 1024;         // dynamic LDS (static use is < 1 KB)
 
 // the int8 codes [M][K]
 size_t lds_bytes(int64_t M, int64_t K, int) { return (size_t)(M * K); }
@@ -680,21 +744,24 @@ hipError_t launch_cfg(const GemvParams &p, int mode, int64_t batch, hipStream_t 
     return hipGetLastError();
 }
 
-// [M + 1][K rounded up to 256] codes, then the bias of gpb groups of 64 rows
-size_t stream_lds_bytes(int64_t M, int64_t K, bool bias, int64_t gpb) {
-    return (size_t)((M + 1) * ((K + 255) / 256 * 256)) + (bias ? (size_t)gpb * 64 * sizeof(float) : 0);
+// [M + 1][K rounded up to 256] codes, then per row of gpb groups of 64 kR rows: the
+// bias (4 bytes, if any) and M staged outputs of ysz bytes
+size_t stream_lds_bytes(int64_t M, int64_t K, bool bias, int ysz, int64_t gpb) {
+    return (size_t)((M + 1) * ((K + 255) / 256 * 256)) +
+           (size_t)gpb * 64 * kStreamRows * ((bias ? 4 : 0) + M * ysz);
 }
 
 template <int kDepth>
 hipError_t launch_stream(const GemvParams &p, int mode, dim3 grid, int gpb, hipStream_t s) {
     const dim3 block(256);
-    const size_t lds = stream_lds_bytes(p.M, p.K, p.bias != nullptr, gpb);
-    if (mode == kInt8) hipLaunchKernelGGL((gemv_stream_kernel<kInt8, 8, kDepth>), grid, block, lds, s, p, gpb);
-    else if (mode == kInt4) hipLaunchKernelGGL((gemv_stream_kernel<kInt4, 4, kDepth>), grid, block, lds, s, p, gpb);
-    else if (mode == kRawBf16 && p.bits == 8) hipLaunchKernelGGL((gemv_stream_kernel<kRawBf16, 8, kDepth>), grid, block, lds, s, p, gpb);
-    else if (mode == kRawBf16) hipLaunchKernelGGL((gemv_stream_kernel<kRawBf16, 4, kDepth>), grid, block, lds, s, p, gpb);
-    else if (p.bits == 8) hipLaunchKernelGGL((gemv_stream_kernel<kRawF32, 8, kDepth>), grid, block, lds, s, p, gpb);
-    else hipLaunchKernelGGL((gemv_stream_kernel<kRawF32, 4, kDepth>), grid, block, lds, s, p, gpb);
+    const int xo = kStreamXcdOrder && (grid.x * grid.y) % 8 == 0;
+    const size_t lds = stream_lds_bytes(p.M, p.K, p.bias != nullptr, p.y_dtype == 1 ? 2 : 4, gpb);
+    if (mode == kInt8) hipLaunchKernelGGL((gemv_stream_kernel<kInt8, 8, kDepth, kStreamRows>), grid, block, lds, s, p, gpb, xo);
+    else if (mode == kInt4) hipLaunchKernelGGL((gemv_stream_kernel<kInt4, 4, kDepth, kStreamRows>), grid, block, lds, s, p, gpb, xo);
+    else if (mode == kRawBf16 && p.bits == 8) hipLaunchKernelGGL((gemv_stream_kernel<kRawBf16, 8, kDepth, kStreamRows>), grid, block, lds, s, p, gpb, xo);
+    else if (mode == kRawBf16) hipLaunchKernelGGL((gemv_stream_kernel<kRawBf16, 4, kDepth, kStreamRows>), grid, block, lds, s, p, gpb, xo);
+    else if (p.bits == 8) hipLaunchKernelGGL((gemv_stream_kernel<kRawF32, 8, kDepth, kStreamRows>), grid, block, lds, s, p, gpb, xo);
+    else hipLaunchKernelGGL((gemv_stream_kernel<kRawF32, 4, kDepth, kStreamRows>), grid, block, lds, s, p, gpb, xo);
     return hipGetLastError();
 }
 
@@ -745,15 +812,17 @@ hipError_t launch_gemv(const FwdArgs &a, bool fused, void *, hipStream_t s) {
     const int mode = fused ? (a.x_raw_bf16 ? kRawBf16 : kRawF32) : (a.bits == 8 ? kInt8 : kInt4);
     // many 64-row groups per launch: the streaming kernel, two blocks per CU, each block
     // a contiguous run of one problem's groups
-    const int64_t G = (a.N + 63) / 64;
     const int64_t target = kStreamBlocksPerCu * (int64_t)device_cus();
-    if (a.batch * G >= 4 * target) {
+    if (a.batch * ((a.N + 63) / 64) >= 4 * target) {
+        const int64_t G = (a.N + 64 * kStreamRows - 1) / (64 * kStreamRows);
         const int64_t bpp = std::max<int64_t>(1, std::min<int64_t>(G, target / a.batch));
         int64_t gpb = (G + bpp - 1) / bpp;
-        // the block's bias rows share LDS with the codes (at most 64 KB in all)
-        const int64_t codes = (int64_t)stream_lds_bytes(a.M, a.K, false, 0);
-        if (a.bias) gpb = std::min<int64_t>(gpb, (kMaxLds - codes) / 256);
-        if (codes <= kMaxLds && gpb >= 1) {
+        // the block's bias rows and staged outputs share LDS with the codes (64 KB in all)
+        const int ysz = a.y_dtype == 1 ? 2 : 4;
+        const int64_t codes = (int64_t)stream_lds_bytes(a.M, a.K, false, ysz, 0);
+        const int64_t per_group = (int64_t)stream_lds_bytes(a.M, a.K, a.bias != nullptr, ysz, 1) - codes;
+        gpb = std::min<int64_t>(gpb, (kStreamLds - codes) / per_group);
+        if (codes <= kStreamLds && gpb >= 1) {
             const dim3 grid((unsigned)((G + gpb - 1) / gpb), (unsigned)a.batch);
             return launch_stream<kStreamDepth>(p, mode, grid, (int)gpb, s);
         }
