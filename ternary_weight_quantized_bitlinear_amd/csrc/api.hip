@@ -61,13 +61,26 @@ bl_status check_eps(float eps, const char *fn) {
 
 bool is_xdtype(bl_dtype d) { return d == BL_F32 || d == BL_BF16; }
 
-size_t ws_fused(int64_t M, int64_t K, int bits, bl_gran gran) {
+size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+// prepared activations (int8 [M][K]) and their per-token code sums
+size_t ws_prepared(int64_t M, int64_t K) { return up256((size_t)(M * K)) + up256((size_t)M * 4); }
+
+size_t ws_forward(int64_t M, int64_t N, int64_t K, int bits, bl_gran gran) {
     if (bl::gemv_supports(M, K)) return bl::ws_gemv((int)gran);
-    // quantized activations, scales and the per-tensor absmax, each 256-byte aligned
+    if (bl::gemm_big_supports(M, N, K, bits)) return ws_prepared(M, K);
+    return bl::ws_gemm(M, N, K);
+}
+
+size_t ws_fused(int64_t M, int64_t N, int64_t K, int bits, bl_gran gran) {
+    if (bl::gemv_supports(M, K)) return bl::ws_gemv((int)gran);
+    // quantized activations (prepared for the large-tile GEMM), scales, the per-tensor
+    // absmax and the GEMM's own workspace, each 256-byte aligned
+    const size_t sc = up256((size_t)M * sizeof(float));
+    const size_t aq = up256(bl::ws_quantize_acts((int)gran));
+    if (bl::gemm_big_supports(M, N, K, bits)) return ws_prepared(M, K) + sc + aq;
     const size_t xq = (size_t)(bits == 8 ? M * K : M * K / 2);
-    const size_t sc = (size_t)M * sizeof(float);
-    auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
-    return up(xq) + up(sc) + up(bl::ws_quantize_acts((int)gran)) + up(bl::ws_gemm(M, 0, K));
+    return up256(xq) + sc + aq + up256(bl::ws_gemm(M, N, K));
 }
 
 #define CHECK(x)                                                                                   \
@@ -104,9 +117,9 @@ size_t bitlinear_workspace_size(bl_op op, int64_t M, int64_t N, int64_t K, int b
     case BL_OP_QUANTIZE_WEIGHTS: return bl::ws_quantize_weights();
     case BL_OP_QUANTIZE_ACTS: return bl::ws_quantize_acts((int)gran);
     case BL_OP_FORWARD:
-        return bl::gemv_supports(M, K) ? bl::ws_gemv((int)gran) : bl::ws_gemm(M, N, K);
+        return (bits == 8 || bits == 4) ? ws_forward(M, N, K, bits, gran) : 0;
     case BL_OP_FORWARD_FUSED:
-        return (bits == 8 || bits == 4) ? ws_fused(M, K, bits, gran) : 0;
+        return (bits == 8 || bits == 4) ? ws_fused(M, N, K, bits, gran) : 0;
     }
     return 0;
 }
@@ -194,10 +207,20 @@ static bl::FwdArgs make_args(const void *x, int x_bf16, int bits, const float *a
     return a;
 }
 
-// forward on quantized activations: decode GEMV, large-tile GEMM or general GEMM
+// forward on quantized activations: decode GEMV, large-tile GEMM (after preparing the
+// activations into the workspace) or general GEMM
 static hipError_t launch_forward(const bl::FwdArgs &a, void *ws, hipStream_t s) {
     if (bl::gemv_supports(a.M, a.K)) return bl::launch_gemv(a, false, ws, s);
-    if (bl::gemm_big_supports(a.M, a.N, a.K, a.bits)) return bl::launch_gemm_big(a, s);
+    if (bl::gemm_big_supports(a.M, a.N, a.K, a.bits)) {
+        uint8_t *xp = static_cast<uint8_t *>(ws);
+        int32_t *rs = reinterpret_cast<int32_t *>(xp + up256((size_t)(a.M * a.K)));
+        const hipError_t e = bl::launch_prepare_acts(a.xq, a.bits, a.M, a.K, xp, rs, s);
+        if (e != hipSuccess) return e;
+        bl::FwdArgs b = a;
+        b.xq = xp;
+        b.rowsum = rs;
+        return bl::launch_gemm_big(b, s);
+    }
     return bl::launch_gemm(a, ws, s);
 }
 
@@ -212,8 +235,8 @@ bl_status bitlinear_forward(const void *Xq, int bits, const float *act_scale, bl
     if (!aligned(Xq, 16) || !aligned(act_scale, 4))
         return fail(BL_EALIGN, "%s: Xq needs 16-byte, act_scale 4-byte alignment", fn);
     const size_t need = bitlinear_workspace_size(BL_OP_FORWARD, M, N, K, bits, gran);
-    if (need && (!workspace || workspace_bytes < need || !aligned(workspace, 16)))
-        return fail(BL_EWORKSPACE, "%s: need %zu bytes of 16-byte aligned workspace", fn, need);
+    if (need && (!workspace || workspace_bytes < need || !aligned(workspace, 256)))
+        return fail(BL_EWORKSPACE, "%s: need %zu bytes of 256-byte aligned workspace", fn, need);
     const bl::FwdArgs a = make_args(Xq, 0, bits, act_scale, gran, 0.0f, W_packed, gamma, bias, M,
                                     N, K, epi, Y, y_dtype);
     (void)hipGetLastError();
@@ -231,7 +254,7 @@ bl_status bitlinear_forward_fused(const void *X, bl_dtype x_dtype, int bits, bl_
     CHECK(check_forward_common(fn, bits, gran, W_packed, gamma, bias, M, N, K, epi, Y, y_dtype));
     CHECK(check_eps(eps, fn));
     if (!aligned(X, 16)) return fail(BL_EALIGN, "%s: X needs 16-byte alignment", fn);
-    const size_t need = ws_fused(M, K, bits, gran);
+    const size_t need = ws_fused(M, N, K, bits, gran);
     if (need && (!workspace || workspace_bytes < need || !aligned(workspace, 256)))
         return fail(BL_EWORKSPACE, "%s: need %zu bytes of 256-byte aligned workspace", fn, need);
     hipStream_t s = (hipStream_t)stream;
@@ -241,9 +264,23 @@ bl_status bitlinear_forward_fused(const void *X, bl_dtype x_dtype, int bits, bl_
                                         gamma, bias, M, N, K, epi, Y, y_dtype);
         return device(bl::launch_gemv(a, true, workspace, s), fn);
     }
+    uint8_t *base = static_cast<uint8_t *>(workspace);
+    if (bl::gemm_big_supports(M, N, K, bits)) {
+        // quantize straight into the large-tile GEMM's prepared form, then the GEMM
+        uint8_t *xp = base;
+        int32_t *rs = reinterpret_cast<int32_t *>(base + up256((size_t)(M * K)));
+        float *scale = reinterpret_cast<float *>(base + ws_prepared(M, K));
+        void *aq_ws = reinterpret_cast<uint8_t *>(scale) + up256((size_t)M * sizeof(float));
+        hipError_t e = bl::launch_quantize_acts_prepared(X, x_dtype == BL_BF16, M, K, bits,
+                                                         (int)gran, eps, xp, scale, rs, aq_ws, s);
+        if (e != hipSuccess) return device(e, fn);
+        bl::FwdArgs a = make_args(xp, 0, bits, scale, gran, eps, W_packed, gamma, bias, M, N, K,
+                                  epi, Y, y_dtype);
+        a.rowsum = rs;
+        return device(bl::launch_gemm_big(a, s), fn);
+    }
     // quantize into the workspace, then the GEMM on the codes
     auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
-    uint8_t *base = static_cast<uint8_t *>(workspace);
     void *xq = base;
     float *scale = reinterpret_cast<float *>(base + up((size_t)(bits == 8 ? M * K : M * K / 2)));
     void *aq_ws = reinterpret_cast<uint8_t *>(scale) + up((size_t)M * sizeof(float));
@@ -279,7 +316,7 @@ bl_status bitlinear_forward_fused_batched(const void *X, bl_dtype x_dtype, int b
                     "multiples of 16", fn, (long long)xs, (long long)ws_, (long long)ys);
     if (batch * ws_ >= (1ll << 40) || batch * xs >= (1ll << 40) || batch * ys >= (1ll << 40))
         return fail(BL_ESHAPE, "%s: batch too large for these sizes", fn);
-    const size_t need = ws_fused(M, K, bits, gran);
+    const size_t need = ws_fused(M, N, K, bits, gran);
     if (need && (!workspace || workspace_bytes < need || !aligned(workspace, 256)))
         return fail(BL_EWORKSPACE, "%s: need %zu bytes of 256-byte aligned workspace", fn, need);
     (void)hipGetLastError();

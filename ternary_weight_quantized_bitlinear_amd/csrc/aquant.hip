@@ -76,6 +76,105 @@ aq_rows(const void *__restrict__ x, int64_t K, float eps, const uint32_t *__rest
     }
 }
 
+__device__ __forceinline__ int block_sum(int v, int *red) {
+    v = wave_sum(v);
+    const int wid = threadIdx.x / kWave;
+    if ((threadIdx.x & (kWave - 1)) == 0) red[wid] = v;
+    __syncthreads();
+    int r = red[0];
+#pragma unroll
+    for (int i = 1; i < kAqThreads / kWave; ++i) r += red[i];
+    return r;
+}
+
+// Prepared activations, the operand layout of the large-tile GEMM: int8 codes (int4
+// codes widened) with every 16-element group stored 4x4-transposed (byte j of dword i
+// = element 4j + i, the order in which the GEMM extracts 2-bit weight fields), and
+// sum_k q[m][k] per token (the correction for offset-binary weight fields).  The
+// codes are the quantizer's own, only reordered.
+__device__ __forceinline__ void store_prepared(uint8_t *dst, const uint32_t nat[4], int &csum) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d) csum = __builtin_amdgcn_sdot4((int)nat[d], 0x01010101, csum, false);
+    uint32_t il[4];
+    interleave16(nat, il);
+    *reinterpret_cast<uint4 *>(dst) = make_uint4(il[0], il[1], il[2], il[3]);
+}
+
+template <bool kBf16, int kBits, bool kTensor>
+__global__ void __launch_bounds__(kAqThreads)
+aq_rows_prep(const void *__restrict__ x, int64_t K, float eps,
+             const uint32_t *__restrict__ tensor_amax, uint8_t *__restrict__ xp,
+             float *__restrict__ scale, int32_t *__restrict__ rowsum) {
+    __shared__ float red[kAqThreads / kWave];
+    __shared__ int redi[kAqThreads / kWave];
+    const int64_t m = blockIdx.x;
+    const void *row = kBf16 ? (const void *)(static_cast<const uint16_t *>(x) + m * K)
+                            : (const void *)(static_cast<const float *>(x) + m * K);
+    const int64_t n16 = K / 16;
+    float amax;
+    if (kTensor) {
+        amax = __uint_as_float(*tensor_amax);
+    } else {
+        float mx = 0.0f;
+        for (int64_t u = threadIdx.x; u < n16; u += kAqThreads) {
+            float v[16];
+            load8<kBf16>(row, u * 16, v);
+            load8<kBf16>(row, u * 16 + 8, v + 8);
+#pragma unroll
+            for (int j = 0; j < 16; ++j) mx = fmaxf(mx, fabsf(v[j]));
+        }
+        amax = block_max(mx, red);
+    }
+    const float a = fmaxf(amax, eps);
+    const float s = kBits == 8 ? 127.0f / a : a / 7.0f;
+    if (threadIdx.x == 0 && (!kTensor || m == 0)) scale[kTensor ? 0 : m] = s;
+    int csum = 0;
+    for (int64_t u = threadIdx.x; u < n16; u += kAqThreads) {
+        float v[16];
+        load8<kBf16>(row, u * 16, v);
+        load8<kBf16>(row, u * 16 + 8, v + 8);
+        uint32_t nat[4];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            uint32_t o = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t c = kBits == 8 ? q8(v[4 * d + j], s)
+                                              : ((uint32_t)(((int)(q4(v[4 * d + j], s) << 28)) >> 28) & 0xFFu);
+                o |= c << (8 * j);
+            }
+            nat[d] = o;
+        }
+        store_prepared(xp + m * K + 16 * u, nat, csum);
+    }
+    csum = block_sum(csum, redi);
+    if (threadIdx.x == 0) rowsum[m] = csum;
+}
+
+// quantized activations (int8 [M][K] or int4 nibbles [M][K/2]) -> prepared form
+template <int kBits>
+__global__ void __launch_bounds__(kAqThreads)
+aq_prepare(const uint8_t *__restrict__ xq, int64_t K, uint8_t *__restrict__ xp,
+           int32_t *__restrict__ rowsum) {
+    __shared__ int redi[kAqThreads / kWave];
+    const int64_t m = blockIdx.x;
+    int csum = 0;
+    for (int64_t u = threadIdx.x; u < K / 16; u += kAqThreads) {
+        uint32_t nat[4];
+        if (kBits == 8) {
+            const uint4 q = *reinterpret_cast<const uint4 *>(xq + m * K + 16 * u);
+            nat[0] = q.x; nat[1] = q.y; nat[2] = q.z; nat[3] = q.w;
+        } else {
+            const uint2 q = *reinterpret_cast<const uint2 *>(xq + m * (K / 2) + 8 * u);
+            nibbles_to_i8(q.x, nat);
+            nibbles_to_i8(q.y, nat + 2);
+        }
+        store_prepared(xp + m * K + 16 * u, nat, csum);
+    }
+    csum = block_sum(csum, redi);
+    if (threadIdx.x == 0) rowsum[m] = csum;
+}
+
 template <bool kBf16>
 __global__ void __launch_bounds__(kAqThreads)
 aq_tensor_amax(const void *__restrict__ x, int64_t n8, uint32_t *__restrict__ amax_bits) {
@@ -105,6 +204,16 @@ void launch_rows(const void *x, int64_t M, int64_t K, float eps, const uint32_t 
                        s, x, K, eps, amax, xq, scale);
 }
 
+template <bool kBf16, int kBits, bool kTensor>
+void launch_rows_prep(const void *x, int64_t M, int64_t K, float eps, const uint32_t *amax,
+                      uint8_t *xp, float *scale, int32_t *rowsum, hipStream_t s) {
+    hipLaunchKernelGGL((aq_rows_prep<kBf16, kBits, kTensor>), dim3((unsigned)M), dim3(kAqThreads),
+                       0, s, x, K, eps, amax, xp, scale, rowsum);
+}
+
+hipError_t launch_tensor_amax(const void *x, int x_bf16, int64_t M, int64_t K, uint32_t *amax,
+                              hipStream_t s);
+
 }  // namespace
 
 hipError_t launch_zero_u32(uint32_t *p, int64_t n, hipStream_t s) {
@@ -117,21 +226,58 @@ hipError_t launch_zero_u32(uint32_t *p, int64_t n, hipStream_t s) {
 
 size_t ws_quantize_acts(int gran) { return gran == 1 ? 256 : 0; }
 
+namespace {
+// grid-wide absmax of X into *amax (as float bits), for per-tensor scales
+hipError_t launch_tensor_amax(const void *x, int x_bf16, int64_t M, int64_t K, uint32_t *amax,
+                              hipStream_t s) {
+    launch_zero_u32(amax, 1, s);
+    const int64_t n8 = M * K / 8;
+    int g = (int)((n8 + kAqThreads * 4 - 1) / (kAqThreads * 4));
+    if (g > 2048) g = 2048;
+    if (g < 1) g = 1;
+    if (x_bf16)
+        hipLaunchKernelGGL(aq_tensor_amax<true>, dim3(g), dim3(kAqThreads), 0, s, x, n8, amax);
+    else
+        hipLaunchKernelGGL(aq_tensor_amax<false>, dim3(g), dim3(kAqThreads), 0, s, x, n8, amax);
+    return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_quantize_acts_prepared(const void *x, int x_bf16, int64_t M, int64_t K,
+                                         int bits, int gran, float eps, uint8_t *xp,
+                                         float *scale, int32_t *rowsum, void *ws,
+                                         hipStream_t s) {
+    uint32_t *amax = static_cast<uint32_t *>(ws);
+    if (gran == 1) launch_tensor_amax(x, x_bf16, M, K, amax, s);
+    const bool t = gran == 1;
+#define BL_PREP(BF, B, T) launch_rows_prep<BF, B, T>(x, M, K, eps, amax, xp, scale, rowsum, s)
+    if (x_bf16) {
+        if (bits == 8) t ? BL_PREP(true, 8, true) : BL_PREP(true, 8, false);
+        else t ? BL_PREP(true, 4, true) : BL_PREP(true, 4, false);
+    } else {
+        if (bits == 8) t ? BL_PREP(false, 8, true) : BL_PREP(false, 8, false);
+        else t ? BL_PREP(false, 4, true) : BL_PREP(false, 4, false);
+    }
+#undef BL_PREP
+    return hipGetLastError();
+}
+
+hipError_t launch_prepare_acts(const void *xq, int bits, int64_t M, int64_t K, uint8_t *xp,
+                               int32_t *rowsum, hipStream_t s) {
+    if (bits == 8)
+        hipLaunchKernelGGL(aq_prepare<8>, dim3((unsigned)M), dim3(kAqThreads), 0, s,
+                           static_cast<const uint8_t *>(xq), K, xp, rowsum);
+    else
+        hipLaunchKernelGGL(aq_prepare<4>, dim3((unsigned)M), dim3(kAqThreads), 0, s,
+                           static_cast<const uint8_t *>(xq), K, xp, rowsum);
+    return hipGetLastError();
+}
+
 hipError_t launch_quantize_acts(const void *x, int x_bf16, int64_t M, int64_t K, int bits,
                                 int gran, float eps, void *xq, float *scale, void *ws,
                                 hipStream_t s) {
     uint32_t *amax = static_cast<uint32_t *>(ws);
-    if (gran == 1) {
-        launch_zero_u32(amax, 1, s);
-        const int64_t n8 = M * K / 8;
-        int g = (int)((n8 + kAqThreads * 4 - 1) / (kAqThreads * 4));
-        if (g > 2048) g = 2048;
-        if (g < 1) g = 1;
-        if (x_bf16)
-            hipLaunchKernelGGL(aq_tensor_amax<true>, dim3(g), dim3(kAqThreads), 0, s, x, n8, amax);
-        else
-            hipLaunchKernelGGL(aq_tensor_amax<false>, dim3(g), dim3(kAqThreads), 0, s, x, n8, amax);
-    }
+    if (gran == 1) launch_tensor_amax(x, x_bf16, M, K, amax, s);
     const bool t = gran == 1;
     if (x_bf16) {
         if (bits == 8) t ? launch_rows<true, 8, true>(x, M, K, eps, amax, xq, scale, s)

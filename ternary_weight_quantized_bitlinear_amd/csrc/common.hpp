@@ -154,6 +154,7 @@ struct FwdArgs {
     void *y;
     int y_dtype;           // 0 f32, 1 bf16, 2 i32
     int64_t batch = 1;     // independent problems laid out back to back (GEMV path)
+    const int32_t *rowsum = nullptr;  // prepared activations: sum_k q[m][k] per token
 };
 
 hipError_t launch_zero_u32(uint32_t *p, int64_t n, hipStream_t s);
@@ -164,6 +165,13 @@ hipError_t launch_quantize_acts(const void *x, int x_bf16, int64_t M, int64_t K,
                                 int gran, float eps, void *xq, float *scale, void *ws,
                                 hipStream_t s);
 size_t ws_quantize_acts(int gran);
+// prepared activations for the large-tile GEMM (int8, 16-element groups 4x4-transposed,
+// int4 widened) and sum_k q per token: straight from X, or from quantized codes
+hipError_t launch_quantize_acts_prepared(const void *x, int x_bf16, int64_t M, int64_t K,
+                                         int bits, int gran, float eps, uint8_t *xp,
+                                         float *scale, int32_t *rowsum, void *ws, hipStream_t s);
+hipError_t launch_prepare_acts(const void *xq, int bits, int64_t M, int64_t K, uint8_t *xp,
+                               int32_t *rowsum, hipStream_t s);
 // decode-sized M: one launch, optional fused activation quantization prologue
 bool gemv_supports(int64_t M, int64_t K);
 hipError_t launch_gemv(const FwdArgs &a, bool fused, void *ws, hipStream_t s);

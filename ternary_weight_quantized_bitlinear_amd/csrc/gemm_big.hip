@@ -19,11 +19,16 @@
 // & 1)) so that fragment reads of 8 or 16 consecutive rows hit distinct banks; the
 // swizzle is applied by choosing which global chunk each lane loads.
 //
-// Fragments.  Activation fragment (32 tokens x 32 k): lane l reads 16 bytes of row
-// l%32, k group l/32, and transposes them 4x4 (v_perm) into the k-interleaved order
-// of the weight fragment.  Weight fragment (32 k x 32 rows): lane l reads the dword
-// (16 codes) of row l%32, k group l/32, and expands it to signed bytes with a shift,
-// a mask and a v_perm table lookup per output dword.
+// Operands.  The activations arrive prepared: int8 codes (int4 codes widened) whose
+// 16-element groups are stored 4x4-transposed, plus sum_k q[m][k] per token.  A
+// weight dword (16 codes, code k in bits 2(k%4) of byte k/4) splits with a shift and
+// a mask per output dword into the raw fields c+1 in {0,1,2}, dword i holding codes
+// i, 4+i, 8+i, 12+i -- exactly the order of a prepared 16-byte activation group.  So
+// the activation fragment (32 tokens x 32 k: lane l reads the 16 bytes of row l%32,
+// k group l/32) is used as read, the weight fragment (32 k x 32 rows: the dword of
+// row l%32, k group l/32) costs 7 VALU, and each MFMA accumulates sum x (c + 1); the
+// epilogue subtracts sum_k x per token.  That keeps the VALU work per MFMA below
+// what the matrix core's 32-cycle issue hides.
 //
 // Requires K % 64 == 0 (whole k steps; every operand byte a real one).  Rows past M
 // or N read clamped addresses and are never stored.
@@ -48,9 +53,11 @@ constexpr int kBStage = BN * BK / 4;   // 4 KB
 constexpr int kStageBytes = kAStage + kBStage;
 
 struct BigParams {
-    const uint8_t *xq;  // int8 [M][K] or int4 nibbles [M][K/2]
+    const uint8_t *xq;        // prepared int8 activations [M][K]
+    const int32_t *rowsum;    // sum_k q[m][k]
     const float *act_scale;
     int gran;
+    int bits;                 // of the codes: selects gamma/s (8) or s*gamma (4)
     const uint8_t *w;
     const float *gamma;
     const float *bias;
@@ -78,10 +85,11 @@ __device__ __forceinline__ void lds_dma16(const void *src, void *lds_dst) {
                  : "memory", "m0");
 }
 
-template <int kBits, int kYD, bool kRelu2, bool kBias>
+template <int kYD, bool kRelu2, bool kBias>
 __global__ void __launch_bounds__(kThreads, 1) gemm_big_kernel(BigParams p) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     float *s_f = reinterpret_cast<float *>(smem + kStages * kStageBytes);
+    int *s_sum = reinterpret_cast<int *>(s_f + BM);
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -93,16 +101,19 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_big_kernel(BigParams p) {
     const int K = p.K;
     const int nk = K / BK;
 
-    // per-row dequant factors of this block's 256 tokens
+    // per-row dequant factors and code sums of this block's 256 tokens
     {
         const int m = m0 + tid;
         float f = 0.0f;
+        int cs = 0;
         if (m < p.M) {
             const float s = p.act_scale[p.gran == 1 ? 0 : m];
             const float g = *p.gamma;
-            f = kBits == 8 ? g / s : s * g;
+            f = p.bits == 8 ? g / s : s * g;
+            cs = p.rowsum[m];
         }
         s_f[tid] = f;
+        s_sum[tid] = cs;
     }
 
     // ---- direct-to-LDS loads of one k step into ring slot `slot`
@@ -139,88 +150,150 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_big_kernel(BigParams p) {
 #pragma unroll
     for (int s = 0; s < kStages - 1; ++s) issue_stage(s, s);
 
+    // ---- fragments of (k step, 32-wide sub-step s) from its ring slot
     const int r32 = lane & 31, kg = lane >> 5;
+    auto read_a = [&](int kt, int s, v4i (&af)[4]) __attribute__((always_inline)) {
+        const uint8_t *sa = smem + (kt % kStages) * kStageBytes;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = 128 * wm + 32 * i + r32;
+            const int c = 2 * s + kg;
+            const uint4 q = *reinterpret_cast<const uint4 *>(sa + row * BK + 16 * (c ^ a_swz(row)));
+            af[i] = v4i{(int)q.x, (int)q.y, (int)q.z, (int)q.w};
+        }
+    };
+    auto read_b = [&](int kt, int s, uint32_t (&bw)[4]) __attribute__((always_inline)) {
+        const uint8_t *sb = smem + (kt % kStages) * kStageBytes + kAStage;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int row = 128 * wn + 32 * j + r32;
+            bw[j] = *reinterpret_cast<const uint32_t *>(sb + row * 16 + 4 * (2 * s + kg));
+        }
+    };
+    auto expand_b = [&](const uint32_t (&bw)[4], v4i (&bf)[4]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            bf[j] = v4i{(int)fields(bw[j], 0), (int)fields(bw[j], 1), (int)fields(bw[j], 2),
+                        (int)fields(bw[j], 3)};
+    };
+    // MFMA (i, j) for i in [i0, i0 + ni)
+    auto mfmas = [&](const v4i (&af)[4], const v4i (&bf)[4], int i0, int ni) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = i0; i < i0 + ni; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bf[j], af[i], acc[i][j], 0, 0, 0);
+    };
+
+    // Software pipeline (one wave per SIMD, so the wave itself must keep its matrix
+    // core fed): the fragment reads and weight-field extraction of the next sub-step
+    // are interleaved with the current sub-step's MFMAs; the wait for the next k step's
+    // stage, the barrier and the next DMA issue sit halfway through the second
+    // sub-step, with 8 MFMAs queued.  The barrier there also certifies that every wave
+    // finished step kt - 1, whose slot the new DMA refills.
+    __builtin_amdgcn_s_waitcnt((((kStages - 2) * 5) & 0xF) | ((((kStages - 2) * 5) >> 4) << 14) |
+                               (0x7 << 4) | (0xF << 8));
+    __syncthreads();
+    v4i a0[4], b0[4], a1[4], b1[4];
+    uint32_t bw[4];
+    read_a(0, 0, a0);
+    read_b(0, 0, bw);
+    expand_b(bw, b0);
+#pragma unroll 1
     for (int kt = 0; kt < nk; ++kt) {
-        // this wave's loads of step kt have landed (kStages-2 younger steps may still
-        // be in flight, 5 loads each); the barrier extends that to every wave's loads
-        // and to every wave having finished step kt-1, whose slot is refilled below
-        __builtin_amdgcn_s_waitcnt((((kStages - 2) * 5) & 0xF) | ((((kStages - 2) * 5) >> 4) << 14) |
+        // phase 1: sub-step 0 MFMAs; reads and field extraction of sub-step 1
+        read_a(kt, 1, a1);
+        read_b(kt, 1, bw);
+        mfmas(a0, b0, 0, 4);
+        expand_b(bw, b1);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+        }
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // phase 2: half of sub-step 1, then the next stage's wait, barrier and DMA
+        mfmas(a1, b1, 0, 2);
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt((((kStages - 3) * 5) & 0xF) | ((((kStages - 3) * 5) >> 4) << 14) |
                                    (0x7 << 4) | (0xF << 8));
         __syncthreads();
         issue_stage(kt + kStages - 1, (kt + kStages - 1) % kStages);
-
-        const uint8_t *sa = smem + (kt % kStages) * kStageBytes;
-        const uint8_t *sb = sa + kAStage;
+        __builtin_amdgcn_sched_barrier(0);
+        // phase 3: rest of sub-step 1; reads of the next step's sub-step 0
+        read_a(kt + 1, 0, a0);
+        read_b(kt + 1, 0, bw);
+        mfmas(a1, b1, 2, 2);
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {  // two 32-wide k sub-steps
-            v4i af[4], bfr[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = 128 * wm + 32 * i + r32;
-                const int c = 2 * s + kg;
-                const uint4 q = *reinterpret_cast<const uint4 *>(sa + row * BK + 16 * (c ^ a_swz(row)));
-                const uint32_t nat[4] = {q.x, q.y, q.z, q.w};
-                uint32_t il[4];
-                interleave16(nat, il);
-                af[i] = v4i{(int)il[0], (int)il[1], (int)il[2], (int)il[3]};
-            }
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int row = 128 * wn + 32 * j + r32;
-                const uint32_t wd = *reinterpret_cast<const uint32_t *>(sb + row * 16 + 4 * (2 * s + kg));
-                bfr[j] = v4i{(int)codes_from_fields(fields(wd, 0)), (int)codes_from_fields(fields(wd, 1)),
-                             (int)codes_from_fields(fields(wd, 2)), (int)codes_from_fields(fields(wd, 3))};
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        for (int t = 0; t < 8; ++t) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
         }
+        __builtin_amdgcn_sched_barrier(0);
+        expand_b(bw, b0);
     }
 
-    // ---- epilogue straight from the accumulators: lane l holds acc[i][j][r] =
-    // C[32i + 8(r/4) + 4(l/32) + r%4][32j + l%32]; for each (tile, r) the 32 lanes of
-    // a half-wave store 32 consecutive columns of one row.  Output type, ReLU^2 and
-    // bias are compile-time, so the store sequence has no branches but the bounds.
+    // ---- epilogue straight from the accumulators.  The MFMAs compute the transposed
+    // tile (weights as the first operand), so lane l holds acc[i][j][r] =
+    // Y[32i + l%32][32j + 8(r/4) + 4(l/32) + r%4]: four consecutive outputs of one
+    // token row per r/4, stored together (8 bytes of bf16, 16 of fp32/int32) when N
+    // keeps them aligned.  The token's dequant factor and code sum are per lane.
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the ring's last (dummy) loads
-    float bv[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int n = n0 + 128 * wn + 32 * j + r32;
-        bv[j] = (kBias && n < p.N) ? p.bias[n] : 0.0f;
-    }
+    const bool vec = (p.N & 3) == 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        // the 16 row factors of this tile row, read once (one LDS wait), unconditionally
-        float f[16];
-        int mrow[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int ml = 128 * wm + 32 * i + 8 * (r >> 2) + 4 * kg + (r & 3);
-            f[r] = s_f[ml];
-            mrow[r] = m0 + ml;
-        }
+        const int ml = 128 * wm + 32 * i + r32;
+        const int m = m0 + ml;
+        const float f = s_f[ml];
+        const int cs = s_sum[ml];
+        const bool m_ok = m < p.M;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const v16i c = acc[i][j];
-            const int n = n0 + 128 * wn + 32 * j + r32;
-            const bool n_ok = n < p.N;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const size_t idx = (size_t)mrow[r] * p.N + n;
-                if (kYD == 2) {
-                    if (n_ok && mrow[r] < p.M) static_cast<int32_t *>(p.y)[idx] = c[r];
-                } else {
-                    float y = __fmul_rn((float)c[r], f[r]);
-                    if (kBias) y = __fadd_rn(y, bv[j]);
+            for (int q = 0; q < 4; ++q) {
+                const int n = n0 + 128 * wn + 32 * j + 8 * q + 4 * kg;
+                const size_t idx = (size_t)m * p.N + n;
+                float y[4];
+                int av[4];
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    av[t] = c[4 * q + t] - cs;
+                    float v = __fmul_rn((float)av[t], f);
+                    if (kBias) v = __fadd_rn(v, n + t < p.N ? p.bias[n + t] : 0.0f);
                     if (kRelu2) {
-                        const float rr = y > 0.0f ? y : 0.0f;
-                        y = __fmul_rn(rr, rr);
+                        const float rr = v > 0.0f ? v : 0.0f;
+                        v = __fmul_rn(rr, rr);
                     }
-                    if (n_ok && mrow[r] < p.M) {
-                        if (kYD == 1) static_cast<uint16_t *>(p.y)[idx] = (uint16_t)to_bf16_bits(y);
-                        else static_cast<float *>(p.y)[idx] = y;
+                    y[t] = v;
+                }
+                if (!m_ok) continue;
+                if (vec && n + 3 < p.N) {
+                    if (kYD == 2) {
+                        *reinterpret_cast<int4 *>(static_cast<int32_t *>(p.y) + idx) =
+                            make_int4(av[0], av[1], av[2], av[3]);
+                    } else if (kYD == 1) {
+                        typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+                        const bf2 lo = {(__bf16)y[0], (__bf16)y[1]};
+                        const bf2 hi = {(__bf16)y[2], (__bf16)y[3]};
+                        *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(p.y) + idx) =
+                            make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+                    } else {
+                        *reinterpret_cast<float4 *>(static_cast<float *>(p.y) + idx) =
+                            make_float4(y[0], y[1], y[2], y[3]);
+                    }
+                } else {
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        if (n + t >= p.N) continue;
+                        if (kYD == 2) static_cast<int32_t *>(p.y)[idx + t] = av[t];
+                        else if (kYD == 1) static_cast<uint16_t *>(p.y)[idx + t] = (uint16_t)to_bf16_bits(y[t]);
+                        else static_cast<float *>(p.y)[idx + t] = y[t];
                     }
                 }
             }
@@ -232,10 +305,10 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_big_kernel(BigParams p) {
 }  // namespace
 
 bool gemm_big_supports(int64_t M, int64_t N, int64_t K, int bits) {
-    return bits == 8 && K % BK == 0 && M >= 128 && N >= 128;
+    return (bits == 8 || bits == 4) && K % BK == 0 && M >= 128 && N >= 128;
 }
 
-size_t gemm_big_lds() { return (size_t)kStages * kStageBytes + BM * sizeof(float); }
+size_t gemm_big_lds() { return (size_t)kStages * kStageBytes + BM * (sizeof(float) + sizeof(int)); }
 
 // more than 64 KB of dynamic LDS must be allowed once per device and kernel
 hipError_t allow_lds(const void *fn, size_t lds) {
@@ -254,8 +327,10 @@ hipError_t allow_lds(const void *fn, size_t lds) {
 hipError_t launch_gemm_big(const FwdArgs &a, hipStream_t s) {
     BigParams p;
     p.xq = static_cast<const uint8_t *>(a.xq);
+    p.rowsum = a.rowsum;
     p.act_scale = a.act_scale;
     p.gran = a.gran;
+    p.bits = a.bits;
     p.w = a.w;
     p.gamma = a.gamma;
     p.bias = a.bias;
@@ -273,9 +348,9 @@ hipError_t launch_gemm_big(const FwdArgs &a, hipStream_t s) {
     switch (key) {
 #define BL_CASE(YD, R, B)                                                                        \
     case YD * 4 + (R ? 2 : 0) + (B ? 1 : 0): {                                                    \
-        hipError_t e = allow_lds((const void *)gemm_big_kernel<8, YD, R, B>, lds);                \
+        hipError_t e = allow_lds((const void *)gemm_big_kernel<YD, R, B>, lds);                   \
         if (e != hipSuccess) return e;                                                            \
-        hipLaunchKernelGGL((gemm_big_kernel<8, YD, R, B>), grid, block, lds, s, p);               \
+        hipLaunchKernelGGL((gemm_big_kernel<YD, R, B>), grid, block, lds, s, p);                  \
         break;                                                                                    \
     }
         BL_CASE(0, false, false) BL_CASE(0, false, true) BL_CASE(0, true, false) BL_CASE(0, true, true)
