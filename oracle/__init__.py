@@ -73,6 +73,7 @@ def _load():
         lib.oracle_forward_at.argtypes = [P, I, P, I, P, P, P, I64, I64, I64, I, I64, P, P, P, I,
                                           P]
         lib.oracle_to_bf16.argtypes = [P, P, I64]
+        lib.oracle_rmsnorm.argtypes = [P, P, I64, I64, F, P, P]
         for name in ("oracle_gamma", "oracle_quantize_weights", "oracle_quantize_acts",
                      "oracle_forward", "oracle_forward_at"):
             getattr(lib, name).restype = I
@@ -184,3 +185,16 @@ def bitlinear(X, packed, gamma_, bits=8, gran=PER_TOKEN, bias=None, epi=EPI_NONE
     Xq, s = quantize_acts(X, bits, gran, eps)
     Y, acc = forward(Xq, bits, s, gran, packed, gamma_, bias, epi, y_dtype)
     return Y, acc, Xq, s
+
+
+def rmsnorm(X: np.ndarray, delta=None, eps: float = 1e-6):
+    """Residual add and RMS norm of bf16 rows (uint16 bit patterns [M, K]):
+    returns (x', h) with x' = bf16(x + delta) (or x) and h = bf16(x' / rms(x'))."""
+    X = np.ascontiguousarray(X, dtype=np.uint16)
+    M, K = X.shape
+    d = None if delta is None else np.ascontiguousarray(delta, dtype=np.uint16)
+    x_out = np.empty_like(X)
+    h_out = np.empty_like(X)
+    _check(_load().oracle_rmsnorm(_ptr(X), None if d is None else _ptr(d), M, K, eps,
+                                  _ptr(x_out), _ptr(h_out)), "rmsnorm")
+    return x_out, h_out

@@ -373,3 +373,40 @@ void oracle_to_bf16(const float *src, uint16_t *dst, int64_t count)
 {
     for (int64_t i = 0; i < count; ++i) dst[i] = narrow_bf16(src[i]);
 }
+
+/* ------------------------------------------------------------------------ */
+/* glue between the BitLinear layers of a block: residual add, RMS norm      */
+/* ------------------------------------------------------------------------ */
+/*
+ * "BitNet 2B4T Guide", "3. Sub-Layer Normalization (SubLN)" and the block of the
+ * "End-to-End PyTorch Implementation" listing: each sub-layer adds its output to
+ * the residual stream, and the next sub-layer normalizes the stream by its root
+ * mean square before its BitLinear quantizes it.  Reading taken (the pages give no
+ * epsilon, no precision and no learned weight at initialisation): weight 1,
+ *     x' = bf16(fl32(x + delta))                 (delta absent: x' = x)
+ *     r  = 1 / sqrt(sum_k x'^2 / K + eps)         in fp64, sum in k order
+ *     h  = bf16(fl32(x' * r))                     product in fp64
+ * Arrays are bf16 bit patterns, row-major [M][K]; delta may be NULL.
+ */
+int oracle_rmsnorm(const uint16_t *X, const uint16_t *delta, int64_t M, int64_t K, float eps,
+                   uint16_t *x_out, uint16_t *h_out)
+{
+    if (!X || !x_out || !h_out || M <= 0 || K <= 0 || !(eps > 0.0f))
+        return OR_EINVAL;
+    for (int64_t m = 0; m < M; ++m) {
+        double ss = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            float v = widen_bf16(X[m * K + k]);
+            if (delta)
+                v = widen_bf16(narrow_bf16(v + widen_bf16(delta[m * K + k])));
+            x_out[m * K + k] = narrow_bf16(v);
+            ss += (double)v * (double)v;
+        }
+        const double r = 1.0 / sqrt(ss / (double)K + (double)eps);
+        for (int64_t k = 0; k < K; ++k) {
+            const double v = (double)widen_bf16(x_out[m * K + k]);
+            h_out[m * K + k] = narrow_bf16((float)(v * r));
+        }
+    }
+    return OR_OK;
+}

@@ -537,3 +537,84 @@ def test_oracle_rejects_bad_input():
         oracle.quantize_weights(np.array([[np.inf, 1.0, 0.0, 0.0]], np.float32))
     with pytest.raises(oracle.OracleError):
         oracle.quantize_acts(np.array([[np.nan, 1.0]], np.float32))
+
+
+# ---------------------------------------------------------------- RMS norm glue
+# Pins of the residual + RMS-norm glue between BitLinear layers ("BitNet 2B4T
+# Guide", "3. Sub-Layer Normalization (SubLN)"): closed forms and invariants.
+
+def _bf(vals):
+    return workloads.to_bf16_bits(np.asarray(vals, dtype=np.float32))
+
+
+def _f(bits):
+    return workloads.bf16_bits_to_f32(bits)
+
+
+def test_rmsnorm_constant_row_is_unit():
+    # x = c everywhere: rms = |c|, h = c / sqrt(c^2 + eps) -> 1.0 once rounded to bf16
+    X = _bf(np.full((3, 64), [[2.0], [-0.5], [8.0]], dtype=np.float32))
+    _, h = oracle.rmsnorm(X)
+    assert np.array_equal(_f(h), np.sign(_f(X)))
+
+
+def test_rmsnorm_single_spike_is_sqrt_k():
+    # one nonzero a in K = 16: rms = |a| / 4, h = sign(a) * 4 exactly (eps is negligible)
+    x = np.zeros((2, 16), np.float32)
+    x[0, 5] = 3.0
+    x[1, 11] = -0.375
+    _, h = oracle.rmsnorm(_bf(x))
+    hf = _f(h)
+    assert hf[0, 5] == 4.0 and hf[1, 11] == -4.0
+    assert np.count_nonzero(hf) == 2
+
+
+def test_rmsnorm_power_of_two_scaling_invariant():
+    rng = np.random.default_rng(5)
+    X = _bf(rng.standard_normal((4, 256)).astype(np.float32))
+    _, h0 = oracle.rmsnorm(X, eps=1e-30)
+    for j in (-3, 2, 5):
+        Xs = _bf(_f(X) * np.float32(2.0 ** j))
+        _, hj = oracle.rmsnorm(Xs, eps=1e-30)
+        assert np.array_equal(hj, h0), j
+
+
+def test_rmsnorm_sign_symmetry():
+    rng = np.random.default_rng(6)
+    X = _bf(rng.standard_normal((3, 128)).astype(np.float32))
+    _, h = oracle.rmsnorm(X)
+    _, hn = oracle.rmsnorm(_bf(-_f(X)))
+    assert np.array_equal(_f(hn), -_f(h))
+
+
+def test_rmsnorm_output_has_unit_mean_square():
+    rng = np.random.default_rng(7)
+    X = _bf((3.0 * rng.standard_normal((8, 2560))).astype(np.float32))
+    _, h = oracle.rmsnorm(X)
+    ms = (_f(h).astype(np.float64) ** 2).mean(axis=1)
+    # each h is within half a bf16 ulp (2^-9 relative) of x / rms
+    assert np.all(np.abs(ms - 1.0) < 2 * 2.0 ** -8)
+
+
+def test_rmsnorm_residual_add_rounds_to_bf16():
+    # sums chosen so the exact sum is known: 1 + 2^-8 rounds to 1 (tie to even),
+    # 1 + 3*2^-8 to 1 + 2^-6 (tie to even), 3 + 0.5 = 3.5 exactly
+    x = _bf([[1.0, 1.0, 3.0, -2.0]])
+    d = _bf([[2.0 ** -8, 3 * 2.0 ** -8, 0.5, 2.0]])
+    x_out, _ = oracle.rmsnorm(x, d)
+    assert list(_f(x_out)[0]) == [1.0, 1.0 + 2.0 ** -6, 3.5, 0.0]
+    # delta = None is delta = 0
+    X = _bf(np.random.default_rng(8).standard_normal((2, 32)).astype(np.float32))
+    a = oracle.rmsnorm(X)
+    b = oracle.rmsnorm(X, np.zeros_like(X))
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_rmsnorm_eps_dominates_zero_row():
+    # x = 0: h = 0 (no division by zero); tiny x: eps bounds the gain at 1/sqrt(eps)
+    X = np.zeros((1, 32), np.uint16)
+    _, h = oracle.rmsnorm(X)
+    assert not h.any()
+    x = _bf(np.full((1, 32), 2.0 ** -20, np.float32))
+    _, h = oracle.rmsnorm(x, eps=1e-6)
+    assert np.all(_f(h) < 2.0 ** -20 * 1000.0 * 1.01)

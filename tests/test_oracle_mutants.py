@@ -28,6 +28,9 @@ MUTANTS = [
     ("nibble_high_first", "(uint8_t)((q & 0xF) << (4 * (k % 2)))", "(uint8_t)((q & 0xF) << (4 * (1 - k % 2)))", None),
     ("field_offset", "return field - 1;", "return field - 2 + (field == 0);", None),
     ("bf16_truncate", "u += 0x7FFFu + lsb;", "(void)lsb;", None),
+    ("rmsnorm_mean_not_sum", "ss / (double)K + (double)eps", "ss + (double)eps", None),
+    ("rmsnorm_no_sqrt", "1.0 / sqrt(ss / (double)K + (double)eps)", "1.0 / (ss / (double)K + (double)eps)", None),
+    ("rmsnorm_residual_dropped", "v = widen_bf16(narrow_bf16(v + widen_bf16(delta[m * K + k])));", "(void)delta;", None),
     ("per_tensor_uses_row_max", "float amax = tensor_max;", "float amax = 0.0f; if (gran == 1) { for (int64_t k = 0; k < K; ++k) { float t = fabsf(load_elem(X, x_dtype, m * K + k)); if (t > amax) amax = t; } }", None),
 ]
 
