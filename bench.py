@@ -334,6 +334,120 @@ def leg_traffic(torch, bl, reps=4, batch=64):
     print("traffic leg: gemv source digest %s" % gemv_source_digest(), flush=True)
 
 
+def leg_70b(torch, bl, reps=5, err_rows=16):
+    """70B-class FFN layer, int8 vs int4 activations (the a4.8 comparison): M=4096 tokens,
+    K=8192, N=28672, 41 outlier channels x30, bf16 Y.  Per path: the GEMM on quantized
+    activations (bitlinear_forward) and the fused quantize + GEMM (bitlinear_forward_fused),
+    and the quantization error: ||Y - Y_ref||_F / ||Y_ref||_F over `err_rows` sampled tokens,
+    Y_ref = X (gamma c)^T in float64 on the host."""
+    import workloads
+    dev = torch.device("cuda:0")
+    codes, X = workloads.layer_70b()
+    M, K = X.shape
+    N = codes.shape[0]
+    Wd = torch.from_numpy(codes).to(dev).float()
+    packed, gamma = bl.quantize_weights(Wd)
+    del Wd
+    Xd = torch.from_numpy(X.view(np.int16)).to(dev).view(torch.bfloat16)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    rows = np.random.default_rng(7).choice(M, err_rows, replace=False)
+    xr = workloads.bf16_bits_to_f32(X[rows]).astype(np.float64)
+    g = float(gamma.cpu()[0])
+    y_ref = (xr @ codes.T.astype(np.float64)) * g
+    ref_norm = np.linalg.norm(y_ref)
+    ops = 2.0 * M * N * K
+    out = {"M": M, "K": K, "N": N, "int_ops": ops}
+    for bits in (8, 4):
+        xq, sc = bl.quantize_acts(Xd, bits=bits)
+        ws = torch.empty(bl.workspace_size(bl.BL_OP_FORWARD, M, N, K, bits), dtype=torch.uint8,
+                         device=dev)
+        wsf = torch.empty(bl.workspace_size(bl.BL_OP_FORWARD_FUSED, M, N, K, bits), dtype=torch.uint8,
+                          device=dev)
+
+        def gemm():
+            for _ in range(reps):
+                bl.forward(xq, sc, packed, gamma, bits=bits, out=y, workspace=ws)
+
+        def fused():
+            for _ in range(reps):
+                bl.forward_fused(Xd, packed, gamma, bits=bits, out=y, workspace=wsf)
+
+        ms_g, _ = graph_time_ms(torch, gemm, replays=1)
+        ms_f, _ = graph_time_ms(torch, fused, replays=1)
+        ms_g /= reps
+        ms_f /= reps
+        yr = torch.from_numpy(rows).to(dev)
+        yh = y.index_select(0, yr).float().cpu().numpy().astype(np.float64)
+        out["int%d" % bits] = {
+            "gemm_us": ms_g * 1e3, "gemm_tops": ops / (ms_g * 1e-3) / 1e12,
+            "fused_us": ms_f * 1e3, "fused_tops": ops / (ms_f * 1e-3) / 1e12,
+            "act_bytes": M * K if bits == 8 else M * K // 2,
+            "rel_fro_err": float(np.linalg.norm(yh - y_ref) / ref_norm)}
+        del xq, ws, wsf
+    out["err_sample"] = "%d token rows x all %d outputs vs float64 X (gamma c)^T" % (err_rows, N)
+    return out
+
+
+def leg_stack(torch, bl, steps=10, layers=30, batch=16):
+    """The 2B-shaped decode stack: 30 blocks of QKV 2560->7680, O 2560->2560, up
+    2560->6912 (+ReLU^2), down 6912->2560, batch 16 tokens, seed-fixed weights.  Per
+    block: RMS norm -> QKV (Q,K rows; V rows, whose output feeds O) -> O -> residual + RMS
+    norm -> up -> down -> residual; every BitLinear quantizes its bf16 input in its own
+    prologue.  One step = all 30 blocks for the 16 tokens, the K steps in one graph."""
+    import workloads
+    dev = torch.device("cuda:0")
+    H = workloads.HIDDEN
+    W = []
+    wbytes = 0
+    for layer in range(layers):
+        codes = workloads.stack_layer_codes(3, layer)
+        lw = {}
+        for name, c in codes.items():
+            Wd = torch.from_numpy(c).to(dev).float()
+            lw[name] = bl.quantize_weights(Wd)
+            wbytes += c.size // 4
+            del Wd
+        W.append(lw)
+    torch.cuda.synchronize()
+    x0 = torch.from_numpy(workloads.stack_input(seed=3, m=batch).view(np.int16)).to(dev).view(
+        torch.bfloat16)
+    x = x0.clone()
+    h = torch.empty_like(x)
+    qk = torch.empty((batch, 2 * H), dtype=torch.bfloat16, device=dev)
+    v = torch.empty((batch, H), dtype=torch.bfloat16, device=dev)
+    o = torch.empty((batch, H), dtype=torch.bfloat16, device=dev)
+    u = torch.empty((batch, workloads.FFN), dtype=torch.bfloat16, device=dev)
+    d = torch.empty((batch, H), dtype=torch.bfloat16, device=dev)
+
+    def step():
+        x.copy_(x0)
+        delta = None
+        for lw in W:
+            pq, gq = lw["qkv"]
+            bl.rmsnorm(x, delta, out=h)
+            bl.forward_fused(h, pq[:2 * H], gq, out=qk)
+            bl.forward_fused(h, pq[2 * H:], gq, out=v)
+            bl.forward_fused(v, *lw["o"], out=o)
+            bl.rmsnorm(x, o, out=h)
+            bl.forward_fused(h, *lw["up"], epilogue="relu2", out=u)
+            bl.forward_fused(u, *lw["down"], out=d)
+            delta = d
+        bl.rmsnorm(x, delta, out=h)  # the last residual
+
+    def run():
+        for _ in range(steps):
+            step()
+
+    step()
+    torch.cuda.synchronize()
+    finite = bool(torch.isfinite(x.float()).all())
+    ms, _ = graph_time_ms(torch, run, replays=1)
+    ms /= steps
+    return {"layers": layers, "batch": batch, "ms_per_step": ms, "tokens_per_s": batch / (ms * 1e-3),
+            "weight_bytes_per_step": wbytes, "weight_gbs": wbytes / (ms * 1e-3) / 1e9,
+            "library_calls_per_step": layers * 7 + 1, "output_finite": finite}
+
+
 def leg_pack(torch, bl, reps=10):
     """a1: weight quantization + packing of the 2B up projection, fp32 W in HBM."""
     import workloads
@@ -388,7 +502,7 @@ def main():
     ap.add_argument("--batch", type=int, default=64, help="layers per streamed launch")
     ap.add_argument("--copies", type=int, default=64, help="weight copies of the chain leg")
     ap.add_argument("--chain-steps", type=int, default=2000)
-    ap.add_argument("--legs", default="decode,chain,single,prefill,pack,cpu")
+    ap.add_argument("--legs", default="decode,chain,single,prefill,stack,c5,pack,cpu")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -410,6 +524,10 @@ def main():
             side["prefill"] = leg_prefill(torch, bl)
         if "pack" in legs:
             side["pack"] = leg_pack(torch, bl)
+        if "c5" in legs:
+            side["layer_70b"] = leg_70b(torch, bl)
+        if "stack" in legs:
+            side["stack_2b"] = leg_stack(torch, bl)
         if side:
             print(json.dumps(side))
         return
@@ -465,6 +583,17 @@ def main():
                           "shapes": {k: v for k, v in pf.items() if isinstance(v, dict)}}
     if "pack" in legs:
         out["pack"] = leg_pack(torch, bl)
+    if "stack" in legs:
+        out["stack_2b"] = {"workload": "30-layer BitNet-2B-shaped decode stack, batch 16: QKV, O, "
+                                       "up (+ReLU^2), down per layer with RMS norm, residual and "
+                                       "requantization between them",
+                           **leg_stack(torch, bl)}
+    if "c5" in legs:
+        c5 = leg_70b(torch, bl)
+        out["layer_70b"] = {"workload": "70B-class FFN layer, M=4096 tokens, K=8192, N=28672, "
+                                        "0.5% outlier channels x30, bf16 out: int8 vs int4 "
+                                        "activations",
+                            "unit": "TOPS", "peak_int8": INT8_PEAK_TOPS, **c5}
     if "cpu" in legs:
         out["cpu_baseline"] = cpu_baseline(st["x"], st["W_up"], st["W_dn"])
     out["device"] = torch.cuda.get_device_name(0)

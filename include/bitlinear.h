@@ -179,6 +179,26 @@ bl_status bitlinear_forward_fused_batched(const void *X, bl_dtype x_dtype, int b
                                           bl_dtype y_dtype, void *workspace,
                                           size_t workspace_bytes, void *stream);
 
+/*
+ * Glue between the BitLinear layers of a transformer block, outside the BitLinear
+ * steps themselves: residual add and RMS normalisation of bf16 rows ("BitNet 2B4T
+ * Guide", "3. Sub-Layer Normalization (SubLN)", and the block of its "End-to-End
+ * PyTorch Implementation" listing).  With weight 1, per row m:
+ *   x'[m][k] = bf16(fl32(x[m][k] + delta[m][k]))   (delta NULL: x' = x)
+ *   r        = 1 / sqrt(sum_k x'[m][k]^2 / K + eps)  in fp64
+ *   h[m][k]  = bf16(fl32(x'[m][k] * r))              product in fp64
+ * The next layer's bitlinear_forward_fused quantizes h.
+ *
+ * X      device bf16 [M][K], read and (if delta) overwritten with x'
+ * delta  device bf16 [M][K], or NULL
+ * H      device bf16 [M][K] output (must not overlap X or delta)
+ * K % 8 == 0, 16-byte aligned pointers, eps > 0.  The fp64 sum of squares is
+ * reduced in a fixed tree order: results are deterministic; against a sequential
+ * sum they can differ in the last bit of r, so h can (rarely) differ by one bf16 ulp.
+ */
+bl_status bitlinear_rmsnorm(void *X, const void *delta, void *H, int64_t M, int64_t K,
+                            float eps, void *stream);
+
 /* Workspace bytes a call needs for these sizes (0 if none).  bits and gran are
  * ignored where they do not matter.  Never fails; returns 0 for invalid sizes. */
 size_t bitlinear_workspace_size(bl_op op, int64_t M, int64_t N, int64_t K, int bits,

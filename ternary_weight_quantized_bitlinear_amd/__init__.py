@@ -13,6 +13,7 @@ The functions mirror the C entry points:
 * :func:`forward`           -> ``bitlinear_forward``
 * :func:`forward_fused`     -> ``bitlinear_forward_fused``
 * :func:`forward_fused_batched` -> ``bitlinear_forward_fused_batched``
+* :func:`rmsnorm`           -> ``bitlinear_rmsnorm`` (glue between layers)
 """
 from __future__ import annotations
 
@@ -58,6 +59,7 @@ def lib() -> ctypes.CDLL:
                                               SZ, P]
         L.bitlinear_forward_fused_batched.argtypes = [P, I, I, I, F, P, P, P, I64, I64, I64, I64,
                                                       I, P, I, P, SZ, P]
+        L.bitlinear_rmsnorm.argtypes = [P, P, P, I64, I64, F, P]
         L.bitlinear_workspace_size.argtypes = [I, I64, I64, I64, I, I]
         L.bitlinear_workspace_size.restype = SZ
         L.bitlinear_status_string.argtypes = [I]
@@ -66,7 +68,8 @@ def lib() -> ctypes.CDLL:
         L.bitlinear_last_error.restype = ctypes.c_char_p
         L.bitlinear_version.restype = I
         for n in ("bitlinear_quantize_weights", "bitlinear_quantize_acts", "bitlinear_forward",
-                  "bitlinear_forward_fused", "bitlinear_forward_fused_batched"):
+                  "bitlinear_forward_fused", "bitlinear_forward_fused_batched",
+                  "bitlinear_rmsnorm"):
             getattr(L, n).restype = I
         _lib = L
     return _lib
@@ -229,4 +232,16 @@ def forward_fused_batched(X, packed, gamma, bits: int = 8, gran="token", eps: fl
         _ptr(X), _dtype_code(X), bits, g, eps, _ptr(packed), _ptr(gamma), _ptr(bias), B, M, N, K,
         _epi_code(epilogue), _ptr(out), _dtype_code(out), _ptr(ws), wsb,
         _stream(X.device, stream)))
+    return out
+
+
+def rmsnorm(X, delta=None, eps: float = 1e-6, out=None, stream=None):
+    """Residual add and RMS norm of bf16 rows: X [M, K] bf16 (overwritten with X + delta
+    when delta is given) -> H [M, K] bf16 = X / rms(X)."""
+    torch = _torch()
+    M, K = X.shape
+    if out is None:
+        out = torch.empty_like(X)
+    _check(lib().bitlinear_rmsnorm(_ptr(X), _ptr(delta), _ptr(out), M, K, eps,
+                                   _stream(X.device, stream)))
     return out

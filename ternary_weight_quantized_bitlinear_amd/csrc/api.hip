@@ -72,15 +72,23 @@ size_t ws_forward(int64_t M, int64_t N, int64_t K, int bits, bl_gran gran) {
     return bl::ws_gemm(M, N, K);
 }
 
+// Decode-sized M: up to this many tokens the activation quantization runs in the GEMV's
+// own prologue (one launch); above it, every GEMV block would redo the quantization of
+// all M rows, so it runs once in its own launch instead.
+constexpr int64_t kFusedPrologueMaxM = 4;
+
+bool fused_in_prologue(int64_t M, int64_t K) { return bl::gemv_supports(M, K) && M <= kFusedPrologueMaxM; }
+
 size_t ws_fused(int64_t M, int64_t N, int64_t K, int bits, bl_gran gran) {
-    if (bl::gemv_supports(M, K)) return bl::ws_gemv((int)gran);
+    if (fused_in_prologue(M, K)) return bl::ws_gemv((int)gran);
     // quantized activations (prepared for the large-tile GEMM), scales, the per-tensor
     // absmax and the GEMM's own workspace, each 256-byte aligned
     const size_t sc = up256((size_t)M * sizeof(float));
     const size_t aq = up256(bl::ws_quantize_acts((int)gran));
-    if (bl::gemm_big_supports(M, N, K, bits)) return ws_prepared(M, K) + sc + aq;
+    if (!bl::gemv_supports(M, K) && bl::gemm_big_supports(M, N, K, bits))
+        return ws_prepared(M, K) + sc + aq;
     const size_t xq = (size_t)(bits == 8 ? M * K : M * K / 2);
-    return up256(xq) + sc + aq + up256(bl::ws_gemm(M, N, K));
+    return up256(xq) + sc + aq + up256(bl::gemv_supports(M, K) ? 0 : bl::ws_gemm(M, N, K));
 }
 
 #define CHECK(x)                                                                                   \
@@ -259,13 +267,13 @@ bl_status bitlinear_forward_fused(const void *X, bl_dtype x_dtype, int bits, bl_
         return fail(BL_EWORKSPACE, "%s: need %zu bytes of 256-byte aligned workspace", fn, need);
     hipStream_t s = (hipStream_t)stream;
     (void)hipGetLastError();
-    if (bl::gemv_supports(M, K)) {
+    if (fused_in_prologue(M, K)) {
         const bl::FwdArgs a = make_args(X, x_dtype == BL_BF16, bits, nullptr, gran, eps, W_packed,
                                         gamma, bias, M, N, K, epi, Y, y_dtype);
         return device(bl::launch_gemv(a, true, workspace, s), fn);
     }
     uint8_t *base = static_cast<uint8_t *>(workspace);
-    if (bl::gemm_big_supports(M, N, K, bits)) {
+    if (!bl::gemv_supports(M, K) && bl::gemm_big_supports(M, N, K, bits)) {
         // quantize straight into the large-tile GEMM's prepared form, then the GEMM
         uint8_t *xp = base;
         int32_t *rs = reinterpret_cast<int32_t *>(base + up256((size_t)(M * K)));
@@ -334,6 +342,28 @@ bl_status bitlinear_forward_fused_batched(const void *X, bl_dtype x_dtype, int b
         if (st != BL_OK) return st;
     }
     return ok();
+}
+
+bl_status bitlinear_rmsnorm(void *X, const void *delta, void *H, int64_t M, int64_t K,
+                            float eps, void *stream) {
+    static const char fn[] = "bitlinear_rmsnorm";
+    if (!X || !H) return fail(BL_EINVAL, "%s: null pointer", fn);
+    if (M <= 0 || K <= 0 || K % 8 != 0)
+        return fail(BL_ESHAPE, "%s: M, K must be positive and K a multiple of 8 (M=%lld K=%lld)",
+                    fn, (long long)M, (long long)K);
+    if (M > (1ll << 31) || M * K >= (1ll << 40))
+        return fail(BL_ESHAPE, "%s: M=%lld too large", fn, (long long)M);
+    CHECK(check_eps(eps, fn));
+    if (!aligned(X, 16) || !aligned(H, 16) || (delta && !aligned(delta, 16)))
+        return fail(BL_EALIGN, "%s: X, delta and H need 16-byte alignment", fn);
+    const uintptr_t bytes = (uintptr_t)(M * K * 2);
+    auto overlap = [&](const void *a, const void *b) {
+        return (uintptr_t)a < (uintptr_t)b + bytes && (uintptr_t)b < (uintptr_t)a + bytes;
+    };
+    if (overlap(H, X) || (delta && overlap(H, delta)))
+        return fail(BL_EINVAL, "%s: H must not overlap X or delta", fn);
+    (void)hipGetLastError();
+    return device(bl::launch_rmsnorm(X, delta, H, M, K, eps, (hipStream_t)stream), fn);
 }
 
 }  // extern "C"

@@ -170,6 +170,11 @@ size_t ws_quantize_acts(int gran);
 hipError_t launch_quantize_acts_prepared(const void *x, int x_bf16, int64_t M, int64_t K,
                                          int bits, int gran, float eps, uint8_t *xp,
                                          float *scale, int32_t *rowsum, void *ws, hipStream_t s);
+// residual add and RMS norm of bf16 rows (glue between BitLinear layers)
+hipError_t launch_rmsnorm(void *x, const void *delta, void *h, int64_t M, int64_t K, float eps,
+                          hipStream_t s);
+// more than 64 KB of dynamic LDS must be allowed once per device and kernel
+hipError_t allow_lds(const void *fn, size_t lds);
 hipError_t launch_prepare_acts(const void *xq, int bits, int64_t M, int64_t K, uint8_t *xp,
                                int32_t *rowsum, hipStream_t s);
 // decode-sized M: one launch, optional fused activation quantization prologue

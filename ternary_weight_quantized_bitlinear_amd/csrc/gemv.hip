@@ -708,7 +708,9 @@ __global__ void __launch_bounds__(256) gemv_stream_kernel(GemvParams p, int grou
     }
 }
 
-constexpr int64_t kMaxLds = 64 * 1024;
+// the classic kernel's codes [M][K] (gfx950 has 160 KB of LDS per CU; the static
+// arrays take 4.2 KB)
+constexpr int64_t kGemvMaxLds = 144 * 1024;
 // streaming kernel: 16-byte weight loads in flight per lane, and blocks per CU
 #ifndef BL_STREAM_DEPTH
 #define BL_STREAM_DEPTH 8
@@ -735,12 +737,18 @@ template <int kWaves, int kT>
 hipError_t launch_cfg(const GemvParams &p, int mode, int64_t batch, hipStream_t s) {
     const dim3 grid((unsigned)((p.N + 15) / 16), (unsigned)batch), block(kWaves * 64);
     const size_t lds = lds_bytes(p.M, p.K, mode);
-    if (mode == kInt8) hipLaunchKernelGGL((gemv_kernel<kInt8, 8, kWaves, kT>), grid, block, lds, s, p);
-    else if (mode == kInt4) hipLaunchKernelGGL((gemv_kernel<kInt4, 4, kWaves, kT>), grid, block, lds, s, p);
-    else if (mode == kRawBf16 && p.bits == 8) hipLaunchKernelGGL((gemv_kernel<kRawBf16, 8, kWaves, kT>), grid, block, lds, s, p);
-    else if (mode == kRawBf16) hipLaunchKernelGGL((gemv_kernel<kRawBf16, 4, kWaves, kT>), grid, block, lds, s, p);
-    else if (p.bits == 8) hipLaunchKernelGGL((gemv_kernel<kRawF32, 8, kWaves, kT>), grid, block, lds, s, p);
-    else hipLaunchKernelGGL((gemv_kernel<kRawF32, 4, kWaves, kT>), grid, block, lds, s, p);
+    void (*k)(GemvParams);
+    if (mode == kInt8) k = gemv_kernel<kInt8, 8, kWaves, kT>;
+    else if (mode == kInt4) k = gemv_kernel<kInt4, 4, kWaves, kT>;
+    else if (mode == kRawBf16 && p.bits == 8) k = gemv_kernel<kRawBf16, 8, kWaves, kT>;
+    else if (mode == kRawBf16) k = gemv_kernel<kRawBf16, 4, kWaves, kT>;
+    else if (p.bits == 8) k = gemv_kernel<kRawF32, 8, kWaves, kT>;
+    else k = gemv_kernel<kRawF32, 4, kWaves, kT>;
+    if (lds > 64 * 1024) {  // large M x K: opt in to more than 64 KB of LDS
+        const hipError_t e = allow_lds((const void *)k, lds);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(k, grid, block, lds, s, p);
     return hipGetLastError();
 }
 
@@ -784,7 +792,7 @@ int device_cus() {
 }  // namespace
 
 bool gemv_supports(int64_t M, int64_t K) {
-    return M >= 1 && M <= kMaxM && K % 64 == 0 && M * K <= kMaxLds;
+    return M >= 1 && M <= kMaxM && K % 64 == 0 && M * K <= kGemvMaxLds;
 }
 
 size_t ws_gemv(int) { return 0; }

@@ -23,7 +23,8 @@ def test_exports_every_header_function(L):
     names = bl.header_functions()
     assert set(names) == {
         "bitlinear_quantize_weights", "bitlinear_quantize_acts", "bitlinear_forward",
-        "bitlinear_forward_fused", "bitlinear_forward_fused_batched", "bitlinear_workspace_size", "bitlinear_status_string",
+        "bitlinear_forward_fused", "bitlinear_forward_fused_batched", "bitlinear_rmsnorm",
+        "bitlinear_workspace_size", "bitlinear_status_string",
         "bitlinear_last_error", "bitlinear_version"}
     for n in names:
         assert hasattr(L, n), n
@@ -148,6 +149,21 @@ def test_forward_fused_batched_rejects(L):
     # prefill-sized problems run one by one and need the fused workspace
     assert call(M=2048) == bl.BL_EWORKSPACE
     assert L.bitlinear_last_error().decode().startswith("bitlinear_forward_fused_batched")
+
+
+def test_rmsnorm_rejects(L):
+    f = L.bitlinear_rmsnorm
+    assert f(None, None, P(A + 4096), 16, 2560, 1e-6, None) == bl.BL_EINVAL
+    assert f(P(A), None, None, 16, 2560, 1e-6, None) == bl.BL_EINVAL
+    assert f(P(A), None, P(A + (1 << 20)), 16, 2564, 1e-6, None) == bl.BL_ESHAPE
+    assert f(P(A), None, P(A + (1 << 20)), 0, 2560, 1e-6, None) == bl.BL_ESHAPE
+    assert f(P(A), None, P(A + (1 << 20)), 16, 2560, 0.0, None) == bl.BL_EINVAL
+    assert f(P(A + 8), None, P(A + (1 << 20)), 16, 2560, 1e-6, None) == bl.BL_EALIGN
+    assert f(P(A), P(A + (1 << 21) + 2), P(A + (1 << 20)), 16, 2560, 1e-6, None) == bl.BL_EALIGN
+    # H overlapping X or delta
+    assert f(P(A), None, P(A + 4096), 16, 2560, 1e-6, None) == bl.BL_EINVAL
+    assert f(P(A), P(A + (1 << 21)), P(A + (1 << 21) + 64), 16, 2560, 1e-6, None) == bl.BL_EINVAL
+    assert L.bitlinear_last_error().decode().startswith("bitlinear_rmsnorm")
 
 
 def _gpu_visible() -> bool:

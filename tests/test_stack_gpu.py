@@ -1,0 +1,103 @@
+"""GPU parity of the glue between BitLinear layers (residual add + RMS norm) and of
+the 30-layer 2B-shaped decode stack, layer by layer: every library call of a layer is
+checked against the oracle fed the GPU's own inputs for that call."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+import ternary_weight_quantized_bitlinear_amd as bl
+from gpu_util import assert_same_bytes, say, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def _check_norm(x_in, delta, x_gpu, h_gpu, what):
+    x_ref, h_ref = oracle.rmsnorm(x_in, delta)
+    assert_same_bytes(x_gpu, x_ref, what + " residual")
+    d = np.abs(h_gpu.astype(np.int32) - h_ref.astype(np.int32))
+    # the fp64 sum of squares is reduced in another order than the oracle's: at most
+    # one bf16 ulp, and (in practice) almost never
+    assert d.max(initial=0) <= 1, what + ": h more than one bf16 ulp off"
+    assert np.count_nonzero(d) <= max(1, h_ref.size // 100000), what + ": too many ulp flips"
+
+
+@pytest.mark.parametrize("M,K,with_delta", [(16, 2560, True), (16, 6912, False), (3, 6912, True),
+                                            (1, 8, False), (5, 4104, True), (2, 65536, True)])
+def test_rmsnorm_parity(M, K, with_delta):
+    rng = np.random.default_rng([M, K])
+    x = workloads.to_bf16_bits((3.0 * rng.standard_normal((M, K))).astype(np.float32))
+    dlt = (workloads.to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
+           if with_delta else None)
+    say("rmsnorm", M, K, with_delta)
+    xd = to_dev(x)
+    h = bl.rmsnorm(xd, to_dev(dlt) if with_delta else None)
+    torch.cuda.synchronize()
+    _check_norm(x, dlt, to_host(xd), to_host(h), "rmsnorm %dx%d" % (M, K))
+
+
+def test_rmsnorm_zero_rows():
+    x = np.zeros((4, 64), np.uint16)
+    xd = to_dev(x)
+    h = bl.rmsnorm(xd)
+    torch.cuda.synchronize()
+    assert not to_host(h).any()
+
+
+def _layer_weights(layer):
+    codes = workloads.stack_layer_codes(3, layer)
+    out = {}
+    for name, c in codes.items():
+        W = c.astype(np.float32)
+        packed, gamma = bl.quantize_weights(to_dev(W))
+        p_ref, g_ref, _ = oracle.quantize_weights(W)
+        out[name] = (packed, gamma, p_ref, g_ref)
+    torch.cuda.synchronize()
+    for name, (packed, gamma, p_ref, g_ref) in out.items():
+        assert_same_bytes(to_host(packed), p_ref, "layer %d %s packed" % (layer, name))
+    return out
+
+
+def _fused(h_dev, packed, gamma, p_ref, g_ref, epi, what):
+    """One BitLinear on the GPU, checked against the oracle on the same bf16 input."""
+    y = bl.forward_fused(h_dev, packed, gamma, epilogue=epi, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    h = to_host(h_dev)
+    y_ref, _, _, _ = oracle.bitlinear(h, p_ref, g_ref, epi=oracle.EPI_RELU2 if epi else oracle.EPI_NONE,
+                                      y_dtype=oracle.BF16)
+    assert_same_bytes(to_host(y), y_ref, what)
+    return y
+
+
+def test_stack_first_layers_parity():
+    """The 2B stack at batch 16, layers 0 and 1: RMS norm, QKV (Q and K rows, then the
+    V rows, whose output feeds O), O, residual, RMS norm, up + ReLU^2, down, residual."""
+    H = workloads.HIDDEN
+    x = workloads.stack_input(seed=3, m=16)
+    xd = to_dev(x)
+    delta = None
+    for layer in range(2):
+        say("stack layer", layer)
+        w = _layer_weights(layer)
+        x_in = to_host(xd)
+        d_in = to_host(delta) if delta is not None else None
+        h = bl.rmsnorm(xd, delta)
+        torch.cuda.synchronize()
+        _check_norm(x_in, d_in, to_host(xd), to_host(h), "layer %d norm 1" % layer)
+        pq, gq, pq_ref, gq_ref = w["qkv"]
+        _fused(h, pq[:2 * H], gq, pq_ref[:2 * H], gq_ref, None, "layer %d QK" % layer)
+        v = _fused(h, pq[2 * H:], gq, pq_ref[2 * H:], gq_ref, None, "layer %d V" % layer)
+        po, go, po_ref, go_ref = w["o"]
+        o = _fused(v, po, go, po_ref, go_ref, None, "layer %d O" % layer)
+        x_in = to_host(xd)
+        h2 = bl.rmsnorm(xd, o)
+        torch.cuda.synchronize()
+        _check_norm(x_in, to_host(o), to_host(xd), to_host(h2), "layer %d norm 2" % layer)
+        pu, gu, pu_ref, gu_ref = w["up"]
+        u = _fused(h2, pu, gu, pu_ref, gu_ref, "relu2", "layer %d up" % layer)
+        pd, gd, pd_ref, gd_ref = w["down"]
+        delta = _fused(u, pd, gd, pd_ref, gd_ref, None, "layer %d down" % layer)
+        assert np.isfinite(workloads.bf16_bits_to_f32(to_host(delta))).all()
