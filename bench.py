@@ -260,7 +260,9 @@ def leg_decode_single(torch, bl, copies=64, reps=200):
 
 
 def leg_prefill(torch, bl, reps=20):
-    """C3: M=2048 tokens; bf16 X -> int8 per token -> MFMA GEMM -> bf16 Y (ReLU^2 on up)."""
+    """Prefill: M=2048 tokens at the 2B FFN shapes, bf16 Y (ReLU^2 on up).  "gemm": the
+    forward on int8 per-token activations (bitlinear_forward); "step": the whole layer on
+    bf16 X (bitlinear_forward_fused: quantization straight into the GEMM's operand form)."""
     import workloads
     dev = torch.device("cuda:0")
     res = {}
@@ -274,15 +276,19 @@ def leg_prefill(torch, bl, reps=20):
         M = X.shape[0]
         xq, s = bl.quantize_acts(Xd)
         y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        # workspaces allocated once, as a serving loop would
+        ws = torch.empty(bl.workspace_size(bl.BL_OP_FORWARD, M, N, K), dtype=torch.uint8,
+                         device=dev)
+        wsf = torch.empty(bl.workspace_size(bl.BL_OP_FORWARD_FUSED, M, N, K), dtype=torch.uint8,
+                          device=dev)
 
         def gemm():
             for _ in range(reps):
-                bl.forward(xq, s, packed, gamma, epilogue=epi, out=y)
+                bl.forward(xq, s, packed, gamma, epilogue=epi, out=y, workspace=ws)
 
         def stepf():
             for _ in range(reps):
-                bl.quantize_acts(Xd, out=(xq, s))
-                bl.forward(xq, s, packed, gamma, epilogue=epi, out=y)
+                bl.forward_fused(Xd, packed, gamma, epilogue=epi, out=y, workspace=wsf)
 
         ms_gemm, _ = graph_time_ms(torch, gemm, replays=1)
         ms_step, _ = graph_time_ms(torch, stepf, replays=1)

@@ -151,15 +151,17 @@ aq_rows_prep(const void *__restrict__ x, int64_t K, float eps,
     if (threadIdx.x == 0) rowsum[m] = csum;
 }
 
-// quantized activations (int8 [M][K] or int4 nibbles [M][K/2]) -> prepared form
+// quantized activations (int8 [M][K] or int4 nibbles [M][K/2]) -> prepared form; one
+// row per wave (four per block), the code sum reduced across the wave
 template <int kBits>
 __global__ void __launch_bounds__(kAqThreads)
-aq_prepare(const uint8_t *__restrict__ xq, int64_t K, uint8_t *__restrict__ xp,
+aq_prepare(const uint8_t *__restrict__ xq, int64_t M, int64_t K, uint8_t *__restrict__ xp,
            int32_t *__restrict__ rowsum) {
-    __shared__ int redi[kAqThreads / kWave];
-    const int64_t m = blockIdx.x;
+    const int64_t m = (int64_t)blockIdx.x * (kAqThreads / kWave) + threadIdx.x / kWave;
+    if (m >= M) return;  // whole wave
+    const int lane = threadIdx.x & (kWave - 1);
     int csum = 0;
-    for (int64_t u = threadIdx.x; u < K / 16; u += kAqThreads) {
+    for (int64_t u = lane; u < K / 16; u += kWave) {
         uint32_t nat[4];
         if (kBits == 8) {
             const uint4 q = *reinterpret_cast<const uint4 *>(xq + m * K + 16 * u);
@@ -171,8 +173,8 @@ aq_prepare(const uint8_t *__restrict__ xq, int64_t K, uint8_t *__restrict__ xp,
         }
         store_prepared(xp + m * K + 16 * u, nat, csum);
     }
-    csum = block_sum(csum, redi);
-    if (threadIdx.x == 0) rowsum[m] = csum;
+    csum = wave_sum(csum);
+    if (lane == 0) rowsum[m] = csum;
 }
 
 template <bool kBf16>
@@ -264,12 +266,13 @@ hipError_t launch_quantize_acts_prepared(const void *x, int x_bf16, int64_t M, i
 
 hipError_t launch_prepare_acts(const void *xq, int bits, int64_t M, int64_t K, uint8_t *xp,
                                int32_t *rowsum, hipStream_t s) {
+    const unsigned g = (unsigned)((M + kAqThreads / kWave - 1) / (kAqThreads / kWave));
     if (bits == 8)
-        hipLaunchKernelGGL(aq_prepare<8>, dim3((unsigned)M), dim3(kAqThreads), 0, s,
-                           static_cast<const uint8_t *>(xq), K, xp, rowsum);
+        hipLaunchKernelGGL(aq_prepare<8>, dim3(g), dim3(kAqThreads), 0, s,
+                           static_cast<const uint8_t *>(xq), M, K, xp, rowsum);
     else
-        hipLaunchKernelGGL(aq_prepare<4>, dim3((unsigned)M), dim3(kAqThreads), 0, s,
-                           static_cast<const uint8_t *>(xq), K, xp, rowsum);
+        hipLaunchKernelGGL(aq_prepare<4>, dim3(g), dim3(kAqThreads), 0, s,
+                           static_cast<const uint8_t *>(xq), M, K, xp, rowsum);
     return hipGetLastError();
 }
 

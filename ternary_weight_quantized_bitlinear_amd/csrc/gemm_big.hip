@@ -6,8 +6,10 @@
 // Guide", "3. Native Hardware INT4 Tensor Core Mapping": int32 accumulators;
 // Output = acc * (s_x * beta) for 4-bit activations.
 //
-// Block tile 256 tokens x 256 output rows, k steps of 64; 4 waves, each a 128 x 128
-// tile of 4 x 4 MFMAs (256 accumulator registers per lane: one wave per SIMD).
+// Block tile 256 tokens x BN output rows (BN = 256: 8 waves; BN = 128: 4 waves, two
+// blocks per CU), k steps of 64; each wave a 128 x 64 tile of 4 x 2 MFMAs (128
+// accumulator registers per lane), so every SIMD runs two waves: while one waits on
+// LDS or the barrier, the other keeps the matrix core busy.
 //
 // Memory pipeline.  Both operands stream straight from global memory into a
 // kStages-deep LDS ring with global_load_lds_dwordx4 (16 bytes per lane, landing at
@@ -45,12 +47,26 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int BM = 256, BN = 256, BK = 64;
-constexpr int kThreads = 256;
-constexpr int kStages = 4;
-constexpr int kAStage = BM * BK;       // 16 KB
-constexpr int kBStage = BN * BK / 4;   // 4 KB
-constexpr int kStageBytes = kAStage + kBStage;
+constexpr int BM = 256, BK = 64;
+#ifndef BL_GEMM_STAGES256
+#define BL_GEMM_STAGES256 4
+#endif
+constexpr int kAStage = BM * BK;  // 16 KB
+// Per block tile width BN (256 or 128).  Every wave owns a 128 (tokens) x 64 (rows)
+// output tile, 4 x 2 MFMA tiles of 32 x 32 (128 accumulator registers), so a CU holds
+// two waves per SIMD either way: one block of 8 waves (BN = 256) or two blocks of 4.
+template <int kBN> struct Tile {
+    static constexpr int kWaves = kBN / 32;       // 2 (tokens) x BN/64 (rows) waves
+    static constexpr int kThreads = 64 * kWaves;
+    static constexpr int kBStage = kBN * BK / 4;  // 4 or 2 KB
+    static constexpr int kStageBytes = kAStage + kBStage;
+    static constexpr int NJ = 2;                  // 32-wide row tiles per wave
+    static constexpr int kADma = 16 / kWaves;     // activation DMAs (16 rows x 64 B) per wave
+    static constexpr int kDma = kADma + 1;        // DMAs per wave per stage
+    // LDS ring depth (deeper rings measured no faster)
+    static constexpr int kStages = kBN == 256 ? BL_GEMM_STAGES256 : 4;
+    static constexpr size_t kLds = (size_t)kStages * kStageBytes + BM * (sizeof(float) + sizeof(int));
+};
 
 struct BigParams {
     const uint8_t *xq;        // prepared int8 activations [M][K]
@@ -85,25 +101,32 @@ __device__ __forceinline__ void lds_dma16(const void *src, void *lds_dst) {
                  : "memory", "m0");
 }
 
-template <int kYD, bool kRelu2, bool kBias>
-__global__ void __launch_bounds__(kThreads, 1) gemm_big_kernel(BigParams p) {
+template <int kBN, int kYD, bool kRelu2, bool kBias>
+__global__ void __launch_bounds__(Tile<kBN>::kThreads, kBN == 128 ? 2 : 1) gemm_big_kernel(BigParams p) {
+    constexpr int kStageBytes = Tile<kBN>::kStageBytes;
+    constexpr int NJ = Tile<kBN>::NJ;
+    constexpr int kWaves = Tile<kBN>::kWaves;
+    constexpr int kADma = Tile<kBN>::kADma;
+    constexpr int kDma = Tile<kBN>::kDma;
+    constexpr int kStages = Tile<kBN>::kStages;
+    constexpr int WN = 64;  // n columns per wave
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     float *s_f = reinterpret_cast<float *>(smem + kStages * kStageBytes);
     int *s_sum = reinterpret_cast<int *>(s_f + BM);
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / (kWaves / 2), wn = wave % (kWaves / 2);
     // tile order: blocks that share an activation row block run back to back
     const int tile = blockIdx.x;
     const int tm = tile % p.tiles_m, tn = tile / p.tiles_m;
-    const int m0 = tm * BM, n0 = tn * BN;
+    const int m0 = tm * BM, n0 = tn * kBN;
     const int K = p.K;
     const int nk = K / BK;
 
     // per-row dequant factors and code sums of this block's 256 tokens
-    {
-        const int m = m0 + tid;
+    for (int t = tid; t < BM; t += Tile<kBN>::kThreads) {
+        const int m = m0 + t;
         float f = 0.0f;
         int cs = 0;
         if (m < p.M) {
@@ -112,38 +135,38 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_big_kernel(BigParams p) {
             f = p.bits == 8 ? g / s : s * g;
             cs = p.rowsum[m];
         }
-        s_f[tid] = f;
-        s_sum[tid] = cs;
+        s_f[t] = f;
+        s_sum[t] = cs;
     }
 
     // ---- direct-to-LDS loads of one k step into ring slot `slot`
-    // activations: wave w loads rows 64w .. 64w+63 in 4 instructions of 16 rows x 64 B
+    // activations: wave w loads rows (256/kWaves) w .. in instructions of 16 rows x 64 B
     const uint8_t *xq = p.xq;
     const uint8_t *w = p.w;
     auto issue_stage = [&](int kt, int slot) __attribute__((always_inline)) {
         const int ktc = min(kt, nk - 1);  // past the end: reload the last step (unused)
         uint8_t *sbase = smem + slot * kStageBytes;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int row = 64 * wave + 16 * q + (lane >> 2);
+        for (int q = 0; q < kADma; ++q) {
+            const int row = 16 * kADma * wave + 16 * q + (lane >> 2);
             const int chunk = (lane & 3) ^ a_swz(row);
             const int gm = min(m0 + row, p.M - 1);
             const uint8_t *src = xq + (size_t)gm * K + ktc * BK + 16 * chunk;
-            lds_dma16(src, sbase + (64 * wave + 16 * q) * BK);
+            lds_dma16(src, sbase + (16 * kADma * wave + 16 * q) * BK);
         }
-        {
-            const int row = 64 * wave + lane;
+        {   // weights: wave w loads rows 32w .. 32w+31 (lanes < 32, one row of 16 B each)
+            const int row = 32 * wave + lane;
             const int gn = min(n0 + row, p.N - 1);
             const uint8_t *src = w + (size_t)gn * (K / 4) + ktc * (BK / 4);
-            lds_dma16(src, sbase + kAStage + 64 * wave * 16);
+            if (lane < 32) lds_dma16(src, sbase + kAStage + 32 * wave * 16);
         }
     };
 
-    v16i acc[4][4];
+    v16i acc[4][NJ];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < NJ; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
 
@@ -162,26 +185,26 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_big_kernel(BigParams p) {
             af[i] = v4i{(int)q.x, (int)q.y, (int)q.z, (int)q.w};
         }
     };
-    auto read_b = [&](int kt, int s, uint32_t (&bw)[4]) __attribute__((always_inline)) {
+    auto read_b = [&](int kt, int s, uint32_t (&bw)[NJ]) __attribute__((always_inline)) {
         const uint8_t *sb = smem + (kt % kStages) * kStageBytes + kAStage;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int row = 128 * wn + 32 * j + r32;
+        for (int j = 0; j < NJ; ++j) {
+            const int row = WN * wn + 32 * j + r32;
             bw[j] = *reinterpret_cast<const uint32_t *>(sb + row * 16 + 4 * (2 * s + kg));
         }
     };
-    auto expand_b = [&](const uint32_t (&bw)[4], v4i (&bf)[4]) __attribute__((always_inline)) {
+    auto expand_b = [&](const uint32_t (&bw)[NJ], v4i (&bf)[NJ]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < NJ; ++j)
             bf[j] = v4i{(int)fields(bw[j], 0), (int)fields(bw[j], 1), (int)fields(bw[j], 2),
                         (int)fields(bw[j], 3)};
     };
     // MFMA (i, j) for i in [i0, i0 + ni)
-    auto mfmas = [&](const v4i (&af)[4], const v4i (&bf)[4], int i0, int ni) __attribute__((always_inline)) {
+    auto mfmas = [&](const v4i (&af)[4], const v4i (&bf)[NJ], int i0, int ni) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = i0; i < i0 + ni; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < NJ; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bf[j], af[i], acc[i][j], 0, 0, 0);
     };
 
@@ -191,11 +214,15 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_big_kernel(BigParams p) {
     // stage, the barrier and the next DMA issue sit halfway through the second
     // sub-step, with 8 MFMAs queued.  The barrier there also certifies that every wave
     // finished step kt - 1, whose slot the new DMA refills.
-    __builtin_amdgcn_s_waitcnt((((kStages - 2) * 5) & 0xF) | ((((kStages - 2) * 5) >> 4) << 14) |
+    __builtin_amdgcn_s_waitcnt((((kStages - 2) * kDma) & 0xF) | ((((kStages - 2) * kDma) >> 4) << 14) |
                                (0x7 << 4) | (0xF << 8));
     __syncthreads();
-    v4i a0[4], b0[4], a1[4], b1[4];
-    uint32_t bw[4];
+    v4i a0[4], b0[NJ], a1[4], b1[NJ];
+    uint32_t bw[NJ];
+    // per sub-step: 4 NJ MFMAs, 4 + NJ fragment reads, 7 NJ VALU of field extraction
+    constexpr int kReads = 4 + NJ;
+    constexpr int kMf = 4 * NJ;
+    constexpr int kValuPer = (7 * NJ + (kMf - kReads) - 1) / (kMf - kReads);
     read_a(0, 0, a0);
     read_b(0, 0, bw);
     expand_b(bw, b0);
@@ -207,20 +234,20 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_big_kernel(BigParams p) {
         mfmas(a0, b0, 0, 4);
         expand_b(bw, b1);
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
+        for (int t = 0; t < kReads; ++t) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
         }
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
+        for (int t = 0; t < kMf - kReads; ++t) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);        // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, kValuPer, 0);  // VALU
         }
         __builtin_amdgcn_sched_barrier(0);
         // phase 2: half of sub-step 1, then the next stage's wait, barrier and DMA
         mfmas(a1, b1, 0, 2);
         __builtin_amdgcn_sched_barrier(0);
-        __builtin_amdgcn_s_waitcnt((((kStages - 3) * 5) & 0xF) | ((((kStages - 3) * 5) >> 4) << 14) |
+        __builtin_amdgcn_s_waitcnt((((kStages - 3) * kDma) & 0xF) | ((((kStages - 3) * kDma) >> 4) << 14) |
                                    (0x7 << 4) | (0xF << 8));
         __syncthreads();
         issue_stage(kt + kStages - 1, (kt + kStages - 1) % kStages);
@@ -230,9 +257,9 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_big_kernel(BigParams p) {
         read_b(kt + 1, 0, bw);
         mfmas(a1, b1, 2, 2);
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
+        for (int t = 0; t < 2 * NJ; ++t) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+            __builtin_amdgcn_sched_group_barrier(0x100, (kReads + 2 * NJ - 1) / (2 * NJ), 0);  // LDS read
         }
         __builtin_amdgcn_sched_barrier(0);
         expand_b(bw, b0);
@@ -253,11 +280,11 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_big_kernel(BigParams p) {
         const int cs = s_sum[ml];
         const bool m_ok = m < p.M;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < NJ; ++j) {
             const v16i c = acc[i][j];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int n = n0 + 128 * wn + 32 * j + 8 * q + 4 * kg;
+                const int n = n0 + WN * wn + 32 * j + 8 * q + 4 * kg;
                 const size_t idx = (size_t)m * p.N + n;
                 float y[4];
                 int av[4];
@@ -308,7 +335,6 @@ bool gemm_big_supports(int64_t M, int64_t N, int64_t K, int bits) {
     return (bits == 8 || bits == 4) && K % BK == 0 && M >= 128 && N >= 128;
 }
 
-size_t gemm_big_lds() { return (size_t)kStages * kStageBytes + BM * (sizeof(float) + sizeof(int)); }
 
 // more than 64 KB of dynamic LDS must be allowed once per device and kernel
 hipError_t allow_lds(const void *fn, size_t lds) {
@@ -323,6 +349,37 @@ hipError_t allow_lds(const void *fn, size_t lds) {
     if (e == hipSuccess) done.insert({dev, fn});
     return e;
 }
+
+namespace {
+template <int kBN>
+hipError_t launch_tiles(const BigParams &p0, const FwdArgs &a, hipStream_t s) {
+    BigParams p = p0;
+    p.tiles_m = (int)((a.M + BM - 1) / BM);
+    p.tiles_n = (int)((a.N + kBN - 1) / kBN);
+    const size_t lds = Tile<kBN>::kLds;
+    const dim3 grid((unsigned)(p.tiles_m * p.tiles_n)), block(Tile<kBN>::kThreads);
+    const int key = a.y_dtype * 4 + (a.epi == 1 ? 2 : 0) + (a.bias ? 1 : 0);
+    switch (key) {
+#define BL_CASE(YD, R, B)                                                                        \
+    case YD * 4 + (R ? 2 : 0) + (B ? 1 : 0): {                                                    \
+        hipError_t e = allow_lds((const void *)gemm_big_kernel<kBN, YD, R, B>, lds);              \
+        if (e != hipSuccess) return e;                                                            \
+        hipLaunchKernelGGL((gemm_big_kernel<kBN, YD, R, B>), grid, block, lds, s, p);             \
+        break;                                                                                    \
+    }
+        BL_CASE(0, false, false) BL_CASE(0, false, true) BL_CASE(0, true, false) BL_CASE(0, true, true)
+        BL_CASE(1, false, false) BL_CASE(1, false, true) BL_CASE(1, true, false) BL_CASE(1, true, true)
+        BL_CASE(2, false, false)
+#undef BL_CASE
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+}  // namespace
+
+#ifndef BL_GEMM_BN
+#define BL_GEMM_BN 0  // 0: choose per shape
+#endif
 
 hipError_t launch_gemm_big(const FwdArgs &a, hipStream_t s) {
     BigParams p;
@@ -340,26 +397,11 @@ hipError_t launch_gemm_big(const FwdArgs &a, hipStream_t s) {
     p.epi = a.epi;
     p.y = a.y;
     p.y_dtype = a.y_dtype;
-    p.tiles_m = (int)((a.M + BM - 1) / BM);
-    p.tiles_n = (int)((a.N + BN - 1) / BN);
-    const size_t lds = gemm_big_lds();
-    const dim3 grid((unsigned)(p.tiles_m * p.tiles_n)), block(kThreads);
-    const int key = a.y_dtype * 4 + (a.epi == 1 ? 2 : 0) + (a.bias ? 1 : 0);
-    switch (key) {
-#define BL_CASE(YD, R, B)                                                                        \
-    case YD * 4 + (R ? 2 : 0) + (B ? 1 : 0): {                                                    \
-        hipError_t e = allow_lds((const void *)gemm_big_kernel<YD, R, B>, lds);                   \
-        if (e != hipSuccess) return e;                                                            \
-        hipLaunchKernelGGL((gemm_big_kernel<YD, R, B>), grid, block, lds, s, p);                  \
-        break;                                                                                    \
-    }
-        BL_CASE(0, false, false) BL_CASE(0, false, true) BL_CASE(0, true, false) BL_CASE(0, true, true)
-        BL_CASE(1, false, false) BL_CASE(1, false, true) BL_CASE(1, true, false) BL_CASE(1, true, true)
-        BL_CASE(2, false, false)
-#undef BL_CASE
-    default: return hipErrorInvalidValue;
-    }
-    return hipGetLastError();
+    // 256-wide tiles (one 8-wave block per CU) when they cover at least half the CUs;
+    // otherwise 128-wide tiles, two 4-wave blocks per CU, twice as many tiles
+    const int64_t tiles256 = ((a.M + BM - 1) / BM) * ((a.N + 255) / 256);
+    const bool narrow = BL_GEMM_BN == 128 || (BL_GEMM_BN == 0 && tiles256 < 128);
+    return narrow ? launch_tiles<128>(p, a, s) : launch_tiles<256>(p, a, s);
 }
 
 }  // namespace bl
