@@ -334,3 +334,30 @@ def test_forward_fused_batched(B, M, K, N, bits, gran, epi, ydt, xdt, with_bias)
 def test_forward_wide_stream(bits, fused):
     _check_forward(3, 64, 131072, bits, "token", "relu2", "f32", True, fused, sampled=False)
     _check_forward(1, 128, 131072 + 40, bits, "tensor", None, "i32", False, fused, sampled=False)
+
+
+# the streamed decode step at full size, in the launch configuration the benchmark
+# times: 64 2B-shaped layers per batched launch (streaming kernel); sampled problems
+# are compared in full against the oracle
+@pytest.mark.parametrize("shape,epi", [(workloads.SHAPE_UP, "relu2"), (workloads.SHAPE_DOWN, None)])
+def test_forward_fused_batched_2b_64_layers(shape, epi):
+    K, N = shape
+    B = 64
+    say("forward_fused_batched 64 layers", shape)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(41)
+    codes = torch.randint(-1, 2, (B, N, K), device="cuda", generator=gen, dtype=torch.int8)
+    packed = torch.empty((B, N, K // 4), dtype=torch.uint8, device="cuda")
+    gamma = torch.empty((B,), dtype=torch.float32, device="cuda")
+    for b in range(B):
+        bl.quantize_weights(codes[b].float(), out=(packed[b], gamma[b:b + 1]))
+    X = torch.randn((B, 1, K), device="cuda", generator=gen).to(torch.bfloat16)
+    y = bl.forward_fused_batched(X, packed, gamma, epilogue=epi, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    e = oracle.EPI_RELU2 if epi else oracle.EPI_NONE
+    for b in (0, 1, 31, 63):
+        W = codes[b].cpu().numpy().astype(np.float32)
+        p_ref, g_ref, _ = oracle.quantize_weights(W)
+        assert_same_bytes(to_host(packed[b]), p_ref, "packed layer %d" % b)
+        y_ref, _, _, _ = oracle.bitlinear(to_host(X[b]), p_ref, g_ref, epi=e, y_dtype=oracle.BF16)
+        assert_same_bytes(to_host(y[b]), y_ref, "Y layer %d" % b)
