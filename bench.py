@@ -397,9 +397,10 @@ def leg_70b(torch, bl, reps=5, err_rows=16):
 def leg_stack(torch, bl, steps=10, layers=30, batch=16):
     """The 2B-shaped decode stack: 30 blocks of QKV 2560->7680, O 2560->2560, up
     2560->6912 (+ReLU^2), down 6912->2560, batch 16 tokens, seed-fixed weights.  Per
-    block: RMS norm -> QKV (Q,K rows; V rows, whose output feeds O) -> O -> residual + RMS
-    norm -> up -> down -> residual; every BitLinear quantizes its bf16 input in its own
-    prologue.  One step = all 30 blocks for the 16 tokens, the K steps in one graph."""
+    block: RMS norm fused with the quantization of h -> QKV on those codes (Q,K rows; V
+    rows, whose output feeds O) -> O -> residual + RMS norm + quantization -> up -> down
+    -> residual; O and down quantize their bf16 inputs themselves.  One step = all 30
+    blocks for the 16 tokens, the K steps in one graph."""
     import workloads
     dev = torch.device("cuda:0")
     H = workloads.HIDDEN
@@ -419,6 +420,8 @@ def leg_stack(torch, bl, steps=10, layers=30, batch=16):
         torch.bfloat16)
     x = x0.clone()
     h = torch.empty_like(x)
+    hq = torch.empty((batch, H), dtype=torch.int8, device=dev)
+    hs = torch.empty((batch,), dtype=torch.float32, device=dev)
     qk = torch.empty((batch, 2 * H), dtype=torch.bfloat16, device=dev)
     v = torch.empty((batch, H), dtype=torch.bfloat16, device=dev)
     o = torch.empty((batch, H), dtype=torch.bfloat16, device=dev)
@@ -430,12 +433,12 @@ def leg_stack(torch, bl, steps=10, layers=30, batch=16):
         delta = None
         for lw in W:
             pq, gq = lw["qkv"]
-            bl.rmsnorm(x, delta, out=h)
-            bl.forward_fused(h, pq[:2 * H], gq, out=qk)
-            bl.forward_fused(h, pq[2 * H:], gq, out=v)
+            bl.rmsnorm_quantize(x, delta, out=(h, hq, hs))
+            bl.forward(hq, hs, pq[:2 * H], gq, out=qk)
+            bl.forward(hq, hs, pq[2 * H:], gq, out=v)
             bl.forward_fused(v, *lw["o"], out=o)
-            bl.rmsnorm(x, o, out=h)
-            bl.forward_fused(h, *lw["up"], epilogue="relu2", out=u)
+            bl.rmsnorm_quantize(x, o, out=(h, hq, hs))
+            bl.forward(hq, hs, *lw["up"], epilogue="relu2", out=u)
             bl.forward_fused(u, *lw["down"], out=d)
             delta = d
         bl.rmsnorm(x, delta, out=h)  # the last residual

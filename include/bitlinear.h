@@ -199,6 +199,23 @@ bl_status bitlinear_forward_fused_batched(const void *X, bl_dtype x_dtype, int b
 bl_status bitlinear_rmsnorm(void *X, const void *delta, void *H, int64_t M, int64_t K,
                             float eps, void *stream);
 
+/*
+ * bitlinear_rmsnorm followed by bitlinear_quantize_acts on its output h, in one launch
+ * for per-token scales: the fused normalisation + absmax quantization prologue of the
+ * next BitLinear ("BitNet 2B4T Guide", "3. Sub-Layer Normalization (SubLN)";
+ * quantization as in bitlinear_quantize_acts: "BitNet b1.58: The 1-Bit Ternary LLM
+ * Architecture Guide", eq. 2; "BitNet a4.8 Guide", "1. Hybrid W1.58 / A4").  The codes
+ * and scales are exactly bitlinear_quantize_acts(H, bits, gran, q_eps); feed them to
+ * bitlinear_forward.  X, delta, H, M, K, eps as in bitlinear_rmsnorm (K % 16 == 0);
+ * bits, gran, q_eps, Xq, act_scale as in bitlinear_quantize_acts.  workspace: >=
+ * bitlinear_workspace_size(BL_OP_QUANTIZE_ACTS, M, 0, K, bits, gran) bytes (per-tensor
+ * scales run as two launches and need the absmax word).
+ */
+bl_status bitlinear_rmsnorm_quantize(void *X, const void *delta, void *H, int64_t M, int64_t K,
+                                     float eps, int bits, bl_gran gran, float q_eps, void *Xq,
+                                     float *act_scale, void *workspace, size_t workspace_bytes,
+                                     void *stream);
+
 /* Workspace bytes a call needs for these sizes (0 if none).  bits and gran are
  * ignored where they do not matter.  Never fails; returns 0 for invalid sizes. */
 size_t bitlinear_workspace_size(bl_op op, int64_t M, int64_t N, int64_t K, int bits,

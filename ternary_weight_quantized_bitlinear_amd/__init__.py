@@ -14,6 +14,7 @@ The functions mirror the C entry points:
 * :func:`forward_fused`     -> ``bitlinear_forward_fused``
 * :func:`forward_fused_batched` -> ``bitlinear_forward_fused_batched``
 * :func:`rmsnorm`           -> ``bitlinear_rmsnorm`` (glue between layers)
+* :func:`rmsnorm_quantize`  -> ``bitlinear_rmsnorm_quantize`` (glue + next layer's quantizer)
 """
 from __future__ import annotations
 
@@ -60,6 +61,7 @@ def lib() -> ctypes.CDLL:
         L.bitlinear_forward_fused_batched.argtypes = [P, I, I, I, F, P, P, P, I64, I64, I64, I64,
                                                       I, P, I, P, SZ, P]
         L.bitlinear_rmsnorm.argtypes = [P, P, P, I64, I64, F, P]
+        L.bitlinear_rmsnorm_quantize.argtypes = [P, P, P, I64, I64, F, I, I, F, P, P, P, SZ, P]
         L.bitlinear_workspace_size.argtypes = [I, I64, I64, I64, I, I]
         L.bitlinear_workspace_size.restype = SZ
         L.bitlinear_status_string.argtypes = [I]
@@ -69,7 +71,7 @@ def lib() -> ctypes.CDLL:
         L.bitlinear_version.restype = I
         for n in ("bitlinear_quantize_weights", "bitlinear_quantize_acts", "bitlinear_forward",
                   "bitlinear_forward_fused", "bitlinear_forward_fused_batched",
-                  "bitlinear_rmsnorm"):
+                  "bitlinear_rmsnorm", "bitlinear_rmsnorm_quantize"):
             getattr(L, n).restype = I
         _lib = L
     return _lib
@@ -245,3 +247,24 @@ def rmsnorm(X, delta=None, eps: float = 1e-6, out=None, stream=None):
     _check(lib().bitlinear_rmsnorm(_ptr(X), _ptr(delta), _ptr(out), M, K, eps,
                                    _stream(X.device, stream)))
     return out
+
+
+def rmsnorm_quantize(X, delta=None, eps: float = 1e-6, bits: int = 8, gran="token",
+                     q_eps: float = 1e-5, out=None, workspace=None, stream=None):
+    """rmsnorm followed by quantize_acts of its output: returns (H, Xq, scale)."""
+    torch = _torch()
+    M, K = X.shape
+    g = _gran_code(gran)
+    if out is None:
+        H = torch.empty_like(X)
+        Xq = torch.empty((M, K if bits == 8 else K // 2),
+                         dtype=torch.int8 if bits == 8 else torch.uint8, device=X.device)
+        sc = torch.empty((M if g == BL_PER_TOKEN else 1,), dtype=torch.float32, device=X.device)
+    else:
+        H, Xq, sc = out
+    ws, wsb = _workspace(workspace_size(BL_OP_QUANTIZE_ACTS, M, 1, K, bits, g), X.device,
+                         workspace)
+    _check(lib().bitlinear_rmsnorm_quantize(_ptr(X), _ptr(delta), _ptr(H), M, K, eps, bits, g,
+                                            q_eps, _ptr(Xq), _ptr(sc), _ptr(ws), wsb,
+                                            _stream(X.device, stream)))
+    return H, Xq, sc

@@ -344,9 +344,8 @@ bl_status bitlinear_forward_fused_batched(const void *X, bl_dtype x_dtype, int b
     return ok();
 }
 
-bl_status bitlinear_rmsnorm(void *X, const void *delta, void *H, int64_t M, int64_t K,
-                            float eps, void *stream) {
-    static const char fn[] = "bitlinear_rmsnorm";
+static bl_status check_norm(const char *fn, void *X, const void *delta, void *H, int64_t M,
+                            int64_t K, float eps) {
     if (!X || !H) return fail(BL_EINVAL, "%s: null pointer", fn);
     if (M <= 0 || K <= 0 || K % 8 != 0)
         return fail(BL_ESHAPE, "%s: M, K must be positive and K a multiple of 8 (M=%lld K=%lld)",
@@ -362,8 +361,43 @@ bl_status bitlinear_rmsnorm(void *X, const void *delta, void *H, int64_t M, int6
     };
     if (overlap(H, X) || (delta && overlap(H, delta)))
         return fail(BL_EINVAL, "%s: H must not overlap X or delta", fn);
+    return BL_OK;
+}
+
+bl_status bitlinear_rmsnorm(void *X, const void *delta, void *H, int64_t M, int64_t K,
+                            float eps, void *stream) {
+    static const char fn[] = "bitlinear_rmsnorm";
+    CHECK(check_norm(fn, X, delta, H, M, K, eps));
     (void)hipGetLastError();
     return device(bl::launch_rmsnorm(X, delta, H, M, K, eps, (hipStream_t)stream), fn);
+}
+
+bl_status bitlinear_rmsnorm_quantize(void *X, const void *delta, void *H, int64_t M, int64_t K,
+                                     float eps, int bits, bl_gran gran, float q_eps, void *Xq,
+                                     float *act_scale, void *workspace, size_t workspace_bytes,
+                                     void *stream) {
+    static const char fn[] = "bitlinear_rmsnorm_quantize";
+    CHECK(check_norm(fn, X, delta, H, M, K, eps));
+    if (!Xq || !act_scale) return fail(BL_EINVAL, "%s: null pointer", fn);
+    if (bits != 8 && bits != 4) return fail(BL_EINVAL, "%s: bits must be 8 or 4", fn);
+    if (gran != BL_PER_TOKEN && gran != BL_PER_TENSOR) return fail(BL_EINVAL, "%s: bad gran", fn);
+    if (K % 16 != 0) return fail(BL_ESHAPE, "%s: K=%lld is not a multiple of 16", fn, (long long)K);
+    CHECK(check_eps(q_eps, fn));
+    if (!aligned(Xq, 16) || !aligned(act_scale, 4))
+        return fail(BL_EALIGN, "%s: Xq needs 16-byte, act_scale 4-byte alignment", fn);
+    const size_t need = bl::ws_quantize_acts((int)gran);
+    if (need && (!workspace || workspace_bytes < need || !aligned(workspace, 16)))
+        return fail(BL_EWORKSPACE, "%s: need %zu bytes of 16-byte aligned workspace", fn, need);
+    (void)hipGetLastError();
+    hipStream_t s = (hipStream_t)stream;
+    if (gran == BL_PER_TOKEN)
+        return device(bl::launch_rmsnorm_quantize(X, delta, H, M, K, eps, bits, q_eps, Xq,
+                                                  act_scale, s), fn);
+    // per-tensor scales need the absmax of all of h: norm, then the quantizer on h
+    hipError_t e = bl::launch_rmsnorm(X, delta, H, M, K, eps, s);
+    if (e != hipSuccess) return device(e, fn);
+    return device(bl::launch_quantize_acts(H, 1, M, K, bits, (int)gran, q_eps, Xq, act_scale,
+                                           workspace, s), fn);
 }
 
 }  // extern "C"

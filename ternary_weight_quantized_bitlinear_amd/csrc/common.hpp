@@ -173,6 +173,10 @@ hipError_t launch_quantize_acts_prepared(const void *x, int x_bf16, int64_t M, i
 // residual add and RMS norm of bf16 rows (glue between BitLinear layers)
 hipError_t launch_rmsnorm(void *x, const void *delta, void *h, int64_t M, int64_t K, float eps,
                           hipStream_t s);
+// the same, fused with the per-token absmax quantization of h into codes and scales
+hipError_t launch_rmsnorm_quantize(void *x, const void *delta, void *h, int64_t M, int64_t K,
+                                   float eps, int bits, float q_eps, void *xq, float *scale,
+                                   hipStream_t s);
 // more than 64 KB of dynamic LDS must be allowed once per device and kernel
 hipError_t allow_lds(const void *fn, size_t lds);
 hipError_t launch_prepare_acts(const void *xq, int bits, int64_t M, int64_t K, uint8_t *xp,

@@ -207,8 +207,22 @@ __global__ void __launch_bounds__(kWaves * 64) gemv_kernel(GemvParams p) {
     const int gbytes = row_bytes / ngroups;  // bytes per group: 64, 32, 16 or 8
     const uint8_t *xbase = static_cast<const uint8_t *>(p.x);
     uint4 xg0[kWpg], xg1[kWpg];
-    load_group<kMode>(xbase, row_bytes, gbytes, ngroups, 0, tid, xg0);
-    load_group<kMode>(xbase, row_bytes, gbytes, ngroups, 0, tid + kThreads, xg1);
+    // quantized codes: the (token, group) pairs t = tid + i kThreads of all M rows are
+    // one index space; the first kPre of this thread's groups are loaded here, before
+    // any weight load, the rest in batches after (each batch one wait, not one per group)
+    constexpr int kPre = 8;
+    const int T = M * ngroups;
+    uint4 xpre[kPre][kWpg];
+    if (kRaw) {
+        load_group<kMode>(xbase, row_bytes, gbytes, ngroups, 0, tid, xg0);
+        load_group<kMode>(xbase, row_bytes, gbytes, ngroups, 0, tid + kThreads, xg1);
+    } else {
+#pragma unroll
+        for (int i = 0; i < kPre; ++i) {
+            const int t = min(tid + i * kThreads, T - 1);
+            load_group<kMode>(xbase, row_bytes, gbytes, ngroups, t / ngroups, t % ngroups, xpre[i]);
+        }
+    }
 
     // ---- then every weight load of this wave's tiles.  Addresses are clamped into
     // the row (row 0 for rows past N, the row's last 64 k for a partial last tile):
@@ -282,22 +296,22 @@ __global__ void __launch_bounds__(kWaves * 64) gemv_kernel(GemvParams p) {
             }
         }
     } else {
-        #pragma unroll 1
-
-        for (int m = 0; m < M; ++m) {
-            uint8_t *xrow_m = xl + (size_t)m * K;
-            if (m == 0) {
-                if (ok0) codes_store<kMode>(xg0, xrow_m, tid);
-                if (ok1) codes_store<kMode>(xg1, xrow_m, tid + kThreads);
+#pragma unroll
+        for (int i = 0; i < kPre; ++i) {
+            const int t = tid + i * kThreads;
+            if (t < T) codes_store<kMode>(xpre[i], xl + (size_t)(t / ngroups) * K, t % ngroups);
+        }
+#pragma unroll 1
+        for (int base = kPre * kThreads; base < T; base += kPre * kThreads) {
+#pragma unroll
+            for (int i = 0; i < kPre; ++i) {
+                const int t = min(base + tid + i * kThreads, T - 1);
+                load_group<kMode>(xbase, row_bytes, gbytes, ngroups, t / ngroups, t % ngroups, xpre[i]);
             }
-            #pragma unroll 1
-
-            for (int i = m == 0 ? 2 : 0; i < gpt; ++i) {
-                const int g = tid + i * kThreads;
-                if (g >= ngroups) break;
-                uint4 r[kWpg];
-                load_group<kMode>(xbase, row_bytes, gbytes, ngroups, m, g, r);
-                codes_store<kMode>(r, xrow_m, g);
+#pragma unroll
+            for (int i = 0; i < kPre; ++i) {
+                const int t = base + tid + i * kThreads;
+                if (t < T) codes_store<kMode>(xpre[i], xl + (size_t)(t / ngroups) * K, t % ngroups);
             }
         }
         if (tid < M) {

@@ -24,7 +24,7 @@ def test_exports_every_header_function(L):
     assert set(names) == {
         "bitlinear_quantize_weights", "bitlinear_quantize_acts", "bitlinear_forward",
         "bitlinear_forward_fused", "bitlinear_forward_fused_batched", "bitlinear_rmsnorm",
-        "bitlinear_workspace_size", "bitlinear_status_string",
+        "bitlinear_rmsnorm_quantize", "bitlinear_workspace_size", "bitlinear_status_string",
         "bitlinear_last_error", "bitlinear_version"}
     for n in names:
         assert hasattr(L, n), n
@@ -164,6 +164,28 @@ def test_rmsnorm_rejects(L):
     assert f(P(A), None, P(A + 4096), 16, 2560, 1e-6, None) == bl.BL_EINVAL
     assert f(P(A), P(A + (1 << 21)), P(A + (1 << 21) + 64), 16, 2560, 1e-6, None) == bl.BL_EINVAL
     assert L.bitlinear_last_error().decode().startswith("bitlinear_rmsnorm")
+
+
+def test_rmsnorm_quantize_rejects(L):
+    f = L.bitlinear_rmsnorm_quantize
+    X, H, Q, S = P(A), P(A + (1 << 20)), P(A + (2 << 20)), P(A + (3 << 20))
+
+    def call(**kw):
+        a = dict(X=X, d=None, H=H, M=16, K=2560, eps=1e-6, bits=8, gran=0, qe=1e-5, Q=Q, S=S,
+                 ws=None, wsb=0)
+        a.update(kw)
+        return f(a["X"], a["d"], a["H"], a["M"], a["K"], a["eps"], a["bits"], a["gran"],
+                 a["qe"], a["Q"], a["S"], a["ws"], a["wsb"], None)
+
+    assert call(bits=2) == bl.BL_EINVAL
+    assert call(gran=3) == bl.BL_EINVAL
+    assert call(K=2568) == bl.BL_ESHAPE          # a multiple of 8 but not of 16
+    assert call(qe=0.0) == bl.BL_EINVAL
+    assert call(Q=None) == bl.BL_EINVAL
+    assert call(Q=P(A + (2 << 20) + 4)) == bl.BL_EALIGN
+    assert call(gran=1) == bl.BL_EWORKSPACE      # per tensor needs the absmax word
+    assert call(H=P(A + 64)) == bl.BL_EINVAL     # H overlaps X
+    assert L.bitlinear_last_error().decode().startswith("bitlinear_rmsnorm_quantize")
 
 
 def _gpu_visible() -> bool:

@@ -47,6 +47,27 @@ def test_rmsnorm_zero_rows():
     assert not to_host(h).any()
 
 
+@pytest.mark.parametrize("M,K,bits,gran,with_delta", [
+    (16, 2560, 8, "token", True), (16, 6912, 8, "token", False), (3, 256, 4, "token", True),
+    (5, 4096, 8, "tensor", True), (2, 65536, 8, "token", False), (1, 16, 4, "tensor", False)])
+def test_rmsnorm_quantize_parity(M, K, bits, gran, with_delta):
+    rng = np.random.default_rng([M, K, bits])
+    x = workloads.to_bf16_bits((2.0 * rng.standard_normal((M, K))).astype(np.float32))
+    dlt = (workloads.to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
+           if with_delta else None)
+    say("rmsnorm_quantize", M, K, bits, gran, with_delta)
+    xd = to_dev(x)
+    h, xq, sc = bl.rmsnorm_quantize(xd, to_dev(dlt) if with_delta else None, bits=bits, gran=gran)
+    torch.cuda.synchronize()
+    hh = to_host(h)
+    _check_norm(x, dlt, to_host(xd), hh, "rmsnorm_quantize %dx%d" % (M, K))
+    # the codes and scales are the quantizer's, applied to the GPU's own h
+    g = oracle.PER_TOKEN if gran == "token" else oracle.PER_TENSOR
+    xq_ref, s_ref = oracle.quantize_acts(hh, bits=bits, gran=g)
+    assert_same_bytes(to_host(xq), xq_ref, "codes")
+    assert_same_bytes(to_host(sc).view(np.uint32), s_ref.view(np.uint32), "scales")
+
+
 def _layer_weights(layer):
     codes = workloads.stack_layer_codes(3, layer)
     out = {}
@@ -61,6 +82,17 @@ def _layer_weights(layer):
     return out
 
 
+def _plain(hq, hs, h_host, packed, gamma, p_ref, g_ref, epi, what):
+    """A BitLinear on the fused norm's codes; the oracle quantizes the same h itself."""
+    y = bl.forward(hq, hs, packed, gamma, epilogue=epi, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    y_ref, _, _, _ = oracle.bitlinear(h_host, p_ref, g_ref,
+                                      epi=oracle.EPI_RELU2 if epi else oracle.EPI_NONE,
+                                      y_dtype=oracle.BF16)
+    assert_same_bytes(to_host(y), y_ref, what)
+    return y
+
+
 def _fused(h_dev, packed, gamma, p_ref, g_ref, epi, what):
     """One BitLinear on the GPU, checked against the oracle on the same bf16 input."""
     y = bl.forward_fused(h_dev, packed, gamma, epilogue=epi, out_dtype=torch.bfloat16)
@@ -73,8 +105,10 @@ def _fused(h_dev, packed, gamma, p_ref, g_ref, epi, what):
 
 
 def test_stack_first_layers_parity():
-    """The 2B stack at batch 16, layers 0 and 1: RMS norm, QKV (Q and K rows, then the
-    V rows, whose output feeds O), O, residual, RMS norm, up + ReLU^2, down, residual."""
+    """The 2B stack at batch 16, layers 0 and 1, in the calls the benchmark makes: RMS
+    norm fused with the quantization of h, QKV on those codes (Q and K rows, then the V
+    rows, whose output feeds O), O, residual + RMS norm + quantization, up + ReLU^2 on
+    the codes, down, residual."""
     H = workloads.HIDDEN
     x = workloads.stack_input(seed=3, m=16)
     xd = to_dev(x)
@@ -84,20 +118,22 @@ def test_stack_first_layers_parity():
         w = _layer_weights(layer)
         x_in = to_host(xd)
         d_in = to_host(delta) if delta is not None else None
-        h = bl.rmsnorm(xd, delta)
+        h, hq, hs = bl.rmsnorm_quantize(xd, delta)
         torch.cuda.synchronize()
-        _check_norm(x_in, d_in, to_host(xd), to_host(h), "layer %d norm 1" % layer)
+        hh = to_host(h)
+        _check_norm(x_in, d_in, to_host(xd), hh, "layer %d norm 1" % layer)
         pq, gq, pq_ref, gq_ref = w["qkv"]
-        _fused(h, pq[:2 * H], gq, pq_ref[:2 * H], gq_ref, None, "layer %d QK" % layer)
-        v = _fused(h, pq[2 * H:], gq, pq_ref[2 * H:], gq_ref, None, "layer %d V" % layer)
+        _plain(hq, hs, hh, pq[:2 * H], gq, pq_ref[:2 * H], gq_ref, None, "layer %d QK" % layer)
+        v = _plain(hq, hs, hh, pq[2 * H:], gq, pq_ref[2 * H:], gq_ref, None, "layer %d V" % layer)
         po, go, po_ref, go_ref = w["o"]
         o = _fused(v, po, go, po_ref, go_ref, None, "layer %d O" % layer)
         x_in = to_host(xd)
-        h2 = bl.rmsnorm(xd, o)
+        h2, h2q, h2s = bl.rmsnorm_quantize(xd, o)
         torch.cuda.synchronize()
-        _check_norm(x_in, to_host(o), to_host(xd), to_host(h2), "layer %d norm 2" % layer)
+        h2h = to_host(h2)
+        _check_norm(x_in, to_host(o), to_host(xd), h2h, "layer %d norm 2" % layer)
         pu, gu, pu_ref, gu_ref = w["up"]
-        u = _fused(h2, pu, gu, pu_ref, gu_ref, "relu2", "layer %d up" % layer)
+        u = _plain(h2q, h2s, h2h, pu, gu, pu_ref, gu_ref, "relu2", "layer %d up" % layer)
         pd, gd, pd_ref, gd_ref = w["down"]
         delta = _fused(u, pd, gd, pd_ref, gd_ref, None, "layer %d down" % layer)
         assert np.isfinite(workloads.bf16_bits_to_f32(to_host(delta))).all()
