@@ -758,7 +758,7 @@ hipError_t launch_cfg(const GemvParams &p, int mode, int64_t batch, hipStream_t 
     else if (mode == kRawBf16) k = gemv_kernel<kRawBf16, 4, kWaves, kT>;
     else if (p.bits == 8) k = gemv_kernel<kRawF32, 8, kWaves, kT>;
     else k = gemv_kernel<kRawF32, 4, kWaves, kT>;
-    if (lds > 64 * 1024) {  // large M x K: opt in to more than 64 KB of LDS
+    if (lds > 48 * 1024) {  // large M x K: with the static arrays, past 64 KB of LDS
         const hipError_t e = allow_lds((const void *)k, lds);
         if (e != hipSuccess) return e;
     }

@@ -361,3 +361,44 @@ def test_forward_fused_batched_2b_64_layers(shape, epi):
         assert_same_bytes(to_host(packed[b]), p_ref, "packed layer %d" % b)
         y_ref, _, _, _ = oracle.bitlinear(to_host(X[b]), p_ref, g_ref, epi=e, y_dtype=oracle.BF16)
         assert_same_bytes(to_host(y[b]), y_ref, "Y layer %d" % b)
+
+
+# maximum sizes: one layer at the ABI's limit N*K < 2^32 (65535 x 65536, 8.6 GB of bf16
+# weights on the device); gamma against its exact value nnz/(NK), outputs of sampled
+# rows against the oracle (the codes of uniform-ternary weights are the weights)
+def test_max_size_layer():
+    from fractions import Fraction
+    from exact import round_to_f32
+    N, K = 65535, 65536
+    assert N * K < 1 << 32
+    say("max-size layer", N, K)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(99)
+    codes = torch.randint(-1, 2, (N, K), device="cuda", generator=gen, dtype=torch.int8)
+    nnz = int(torch.count_nonzero(codes))
+    W = codes.to(torch.bfloat16)
+    packed, gamma = bl.quantize_weights(W)
+    del W
+    torch.cuda.synchronize()
+    g_ref = round_to_f32(Fraction(nnz, N * K))
+    assert bits32(to_host(gamma))[0] == bits32(np.array([g_ref]))[0], "gamma differs"
+    rows = np.array([0, 1, 12345, 40000, N - 2, N - 1])
+    c_rows = codes[torch.from_numpy(rows).cuda()].cpu().numpy()
+    # the packed rows are the codes, re-packed by the oracle's own packer
+    p_rows, _, _ = oracle.quantize_weights(c_rows.astype(np.float32))
+    assert_same_bytes(to_host(packed[torch.from_numpy(rows).cuda()]), p_rows, "packed rows")
+    del codes
+    for M in (1, 300):
+        rng = np.random.default_rng(M)
+        X = workloads.to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
+        say("max-size forward", M)
+        y = bl.forward_fused(to_dev(X), packed, gamma, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        xq_ref, s_ref = oracle.quantize_acts(X)
+        ms = np.repeat(np.arange(M)[[0, M // 2, M - 1]], len(rows))
+        ns_local = np.tile(np.arange(len(rows)), 3)
+        y_ref, _ = oracle.forward_at(xq_ref, 8, s_ref, oracle.PER_TOKEN, p_rows, g_ref,
+                                     ms, ns_local, y_dtype=oracle.F32)
+        got = to_host(y)[ms, rows[ns_local]]
+        assert_y_matches(got, y_ref, "f32", "Y max-size M=%d" % M)
+        del y
