@@ -42,6 +42,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, GB/s
 INT8_PEAK_TOPS = 5000.0         # MI355X dense int8 MFMA, TOPS (5.0 POP/s)
+F6F4_PEAK_TOPS = 10100.0        # MI355X dense FP6/FP4 MFMA (10.1 PFLOP/s), the int4 path's units
 MALL_BYTES = 256 << 20          # Infinity Cache
 METRIC = "BitLinear decode GEMV HBM GB/s + prefill GEMM int TOPS, % of MI355X roofline"
 CSRC = os.path.join(ROOT, "ternary_weight_quantized_bitlinear_amd", "csrc")
@@ -262,7 +263,9 @@ def leg_decode_single(torch, bl, copies=64, reps=200):
 def leg_prefill(torch, bl, reps=20):
     """Prefill: M=2048 tokens at the 2B FFN shapes, bf16 Y (ReLU^2 on up).  "gemm": the
     forward on int8 per-token activations (bitlinear_forward); "step": the whole layer on
-    bf16 X (bitlinear_forward_fused: quantization straight into the GEMM's operand form)."""
+    bf16 X (bitlinear_forward_fused: quantization straight into the GEMM's operand form).
+    "int4": the same two calls with 4-bit activations, whose contraction runs exactly on
+    the FP6 x FP4 matrix cores (their operand preparation is inside both timings)."""
     import workloads
     dev = torch.device("cuda:0")
     res = {}
@@ -274,37 +277,50 @@ def leg_prefill(torch, bl, reps=20):
         packed, gamma = bl.quantize_weights(torch.from_numpy(W).to(dev))
         Xd = torch.from_numpy(X.view(np.int16)).to(dev).view(torch.bfloat16)
         M = X.shape[0]
-        xq, s = bl.quantize_acts(Xd)
         y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-        # workspaces allocated once, as a serving loop would
-        ws = torch.empty(bl.workspace_size(bl.BL_OP_FORWARD, M, N, K), dtype=torch.uint8,
-                         device=dev)
-        wsf = torch.empty(bl.workspace_size(bl.BL_OP_FORWARD_FUSED, M, N, K), dtype=torch.uint8,
-                          device=dev)
-
-        def gemm():
-            for _ in range(reps):
-                bl.forward(xq, s, packed, gamma, epilogue=epi, out=y, workspace=ws)
-
-        def stepf():
-            for _ in range(reps):
-                bl.forward_fused(Xd, packed, gamma, epilogue=epi, out=y, workspace=wsf)
-
-        ms_gemm, _ = graph_time_ms(torch, gemm, replays=1)
-        ms_step, _ = graph_time_ms(torch, stepf, replays=1)
-        ms_gemm /= reps
-        ms_step /= reps
         ops = 2.0 * M * N * K
-        res[name] = {"M": M, "K": K, "N": N, "gemm_us": ms_gemm * 1e3,
-                     "gemm_tops": ops / (ms_gemm * 1e-3) / 1e12,
-                     "step_us": ms_step * 1e3, "step_tops": ops / (ms_step * 1e-3) / 1e12}
-        tot_ops += ops
-        tot_gemm_ms += ms_gemm
-        tot_step_ms += ms_step
+        for bits in (8, 4):
+            xq, s = bl.quantize_acts(Xd, bits=bits)
+            # workspaces allocated once, as a serving loop would
+            ws = torch.empty(bl.workspace_size(bl.BL_OP_FORWARD, M, N, K, bits), dtype=torch.uint8,
+                             device=dev)
+            wsf = torch.empty(bl.workspace_size(bl.BL_OP_FORWARD_FUSED, M, N, K, bits),
+                              dtype=torch.uint8, device=dev)
+
+            def gemm():
+                for _ in range(reps):
+                    bl.forward(xq, s, packed, gamma, bits=bits, epilogue=epi, out=y, workspace=ws)
+
+            def stepf():
+                for _ in range(reps):
+                    bl.forward_fused(Xd, packed, gamma, bits=bits, epilogue=epi, out=y,
+                                     workspace=wsf)
+
+            ms_gemm, _ = graph_time_ms(torch, gemm, replays=1)
+            ms_step, _ = graph_time_ms(torch, stepf, replays=1)
+            ms_gemm /= reps
+            ms_step /= reps
+            r = {"gemm_us": ms_gemm * 1e3, "gemm_tops": ops / (ms_gemm * 1e-3) / 1e12,
+                 "step_us": ms_step * 1e3, "step_tops": ops / (ms_step * 1e-3) / 1e12}
+            if bits == 8:
+                res[name] = {"M": M, "K": K, "N": N, **r}
+                tot_ops += ops
+                tot_gemm_ms += ms_gemm
+                tot_step_ms += ms_step
+            else:
+                res.setdefault("int4", {})[name] = r
+                t4 = res["int4"]
+                t4["_ms"] = t4.get("_ms", 0.0) + ms_gemm
+            del xq, ws, wsf
     tops = tot_ops / (tot_gemm_ms * 1e-3) / 1e12
     res["gemm_tops"] = tops
     res["gemm_frac"] = tops / INT8_PEAK_TOPS
     res["step_tops"] = tot_ops / (tot_step_ms * 1e-3) / 1e12
+    t4 = res["int4"]
+    t4["gemm_tops"] = tot_ops / (t4.pop("_ms") * 1e-3) / 1e12
+    t4["mfma"] = "fp6 x fp4 32x32x64 (exact)"
+    t4["peak_tops"] = F6F4_PEAK_TOPS
+    t4["frac"] = t4["gemm_tops"] / F6F4_PEAK_TOPS
     return res
 
 
@@ -384,7 +400,10 @@ def leg_70b(torch, bl, reps=5, err_rows=16):
         ms_f /= reps
         yr = torch.from_numpy(rows).to(dev)
         yh = y.index_select(0, yr).float().cpu().numpy().astype(np.float64)
+        peak = INT8_PEAK_TOPS if bits == 8 else F6F4_PEAK_TOPS
         out["int%d" % bits] = {
+            "mfma": "int8 32x32x32" if bits == 8 else "fp6 x fp4 32x32x64 (exact)",
+            "peak_tops": peak, "frac": ops / (ms_g * 1e-3) / 1e12 / peak,
             "gemm_us": ms_g * 1e3, "gemm_tops": ops / (ms_g * 1e-3) / 1e12,
             "fused_us": ms_f * 1e3, "fused_tops": ops / (ms_f * 1e-3) / 1e12,
             "act_bytes": M * K if bits == 8 else M * K // 2,
@@ -589,7 +608,8 @@ def main():
                           "roofline": {"bound": "mfma", "peak": INT8_PEAK_TOPS, "unit": "TOPS",
                                        "frac": round(pf["gemm_frac"], 4)},
                           "with_act_quant_tops": round(pf["step_tops"], 2),
-                          "shapes": {k: v for k, v in pf.items() if isinstance(v, dict)}}
+                          "shapes": {k: pf[k] for k in ("up", "down")},
+                          "int4_activations": pf["int4"]}
     if "pack" in legs:
         out["pack"] = leg_pack(torch, bl)
     if "stack" in legs:

@@ -134,6 +134,12 @@ bl_status bitlinear_quantize_acts(const void *X, bl_dtype x_dtype, int64_t M, in
  * Y         device [M][N] in y_dtype (BL_F32, BL_BF16, or BL_I32 = raw acc; with
  *           BL_I32 epi must be BL_EPI_NONE and bias NULL)
  * workspace device, >= bitlinear_workspace_size(BL_OP_FORWARD, ...) bytes (may be 0).
+ *
+ * With bits = 4 at prefill sizes (M >= 128, N >= 128, K % 64 == 0, K < 2^20) the
+ * contraction runs on the FP6 x FP4 matrix cores ([a48] "3. Native Hardware INT4 Tensor
+ * Core Mapping": the 4-bit GEMM at twice the int8 rate): q/2 in e2m3 times (c+1)/2 in
+ * e2m1, every partial sum a multiple of 1/4 below 2^22, so the fp32 accumulation is
+ * exact and acc, Y are bit-identical to the int32 contraction.
  */
 bl_status bitlinear_forward(const void *Xq, int bits, const float *act_scale, bl_gran gran,
                             const uint8_t *W_packed, const float *gamma, const float *bias,

@@ -65,9 +65,19 @@ size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 // prepared activations (int8 [M][K]) and their per-token code sums
 size_t ws_prepared(int64_t M, int64_t K) { return up256((size_t)(M * K)) + up256((size_t)M * 4); }
+// FP6 operand blocks of int4 codes and their per-token code sums
+size_t ws_prepared_f6(int64_t M, int64_t K) {
+    return up256(bl::f6_prepared_bytes(M, K)) + up256((size_t)M * 4);
+}
+
+// 4-bit activations at prefill sizes run on the FP6 x FP4 matrix cores
+bool use_f6f4(int64_t M, int64_t N, int64_t K, int bits) {
+    return !bl::gemv_supports(M, K) && bl::gemm_f6f4_supports(M, N, K, bits);
+}
 
 size_t ws_forward(int64_t M, int64_t N, int64_t K, int bits, bl_gran gran) {
     if (bl::gemv_supports(M, K)) return bl::ws_gemv((int)gran);
+    if (use_f6f4(M, N, K, bits)) return ws_prepared_f6(M, K);
     if (bl::gemm_big_supports(M, N, K, bits)) return ws_prepared(M, K);
     return bl::ws_gemm(M, N, K);
 }
@@ -85,6 +95,8 @@ size_t ws_fused(int64_t M, int64_t N, int64_t K, int bits, bl_gran gran) {
     // absmax and the GEMM's own workspace, each 256-byte aligned
     const size_t sc = up256((size_t)M * sizeof(float));
     const size_t aq = up256(bl::ws_quantize_acts((int)gran));
+    // int4 codes, their FP6 operand blocks, scales, the per-tensor absmax
+    if (use_f6f4(M, N, K, bits)) return up256((size_t)(M * K / 2)) + ws_prepared_f6(M, K) + sc + aq;
     if (!bl::gemv_supports(M, K) && bl::gemm_big_supports(M, N, K, bits))
         return ws_prepared(M, K) + sc + aq;
     const size_t xq = (size_t)(bits == 8 ? M * K : M * K / 2);
@@ -217,8 +229,21 @@ static bl::FwdArgs make_args(const void *x, int x_bf16, int bits, const float *a
 
 // forward on quantized activations: decode GEMV, large-tile GEMM (after preparing the
 // activations into the workspace) or general GEMM
+// FP6 operand blocks of the int4 codes a.xq in ws, then the FP6 x FP4 GEMM
+static hipError_t launch_f6f4(const bl::FwdArgs &a, void *ws, hipStream_t s) {
+    uint8_t *xp = static_cast<uint8_t *>(ws);
+    int32_t *rs = reinterpret_cast<int32_t *>(xp + up256(bl::f6_prepared_bytes(a.M, a.K)));
+    const hipError_t e = bl::launch_prepare_acts_f6(a.xq, a.M, a.K, xp, rs, s);
+    if (e != hipSuccess) return e;
+    bl::FwdArgs b = a;
+    b.xq = xp;
+    b.rowsum = rs;
+    return bl::launch_gemm_f6f4(b, s);
+}
+
 static hipError_t launch_forward(const bl::FwdArgs &a, void *ws, hipStream_t s) {
     if (bl::gemv_supports(a.M, a.K)) return bl::launch_gemv(a, false, ws, s);
+    if (use_f6f4(a.M, a.N, a.K, a.bits)) return launch_f6f4(a, ws, s);
     if (bl::gemm_big_supports(a.M, a.N, a.K, a.bits)) {
         uint8_t *xp = static_cast<uint8_t *>(ws);
         int32_t *rs = reinterpret_cast<int32_t *>(xp + up256((size_t)(a.M * a.K)));
@@ -273,6 +298,19 @@ bl_status bitlinear_forward_fused(const void *X, bl_dtype x_dtype, int bits, bl_
         return device(bl::launch_gemv(a, true, workspace, s), fn);
     }
     uint8_t *base = static_cast<uint8_t *>(workspace);
+    if (use_f6f4(M, N, K, bits)) {
+        // int4 codes, then their FP6 operand blocks and the FP6 x FP4 GEMM
+        void *xq = base;
+        uint8_t *f6 = base + up256((size_t)(M * K / 2));
+        float *scale = reinterpret_cast<float *>(f6 + ws_prepared_f6(M, K));
+        void *aq_ws = reinterpret_cast<uint8_t *>(scale) + up256((size_t)M * sizeof(float));
+        hipError_t e = bl::launch_quantize_acts(X, x_dtype == BL_BF16, M, K, bits, (int)gran, eps,
+                                                xq, scale, aq_ws, s);
+        if (e != hipSuccess) return device(e, fn);
+        const bl::FwdArgs a = make_args(xq, 0, bits, scale, gran, eps, W_packed, gamma, bias, M, N,
+                                        K, epi, Y, y_dtype);
+        return device(launch_f6f4(a, f6, s), fn);
+    }
     if (!bl::gemv_supports(M, K) && bl::gemm_big_supports(M, N, K, bits)) {
         // quantize straight into the large-tile GEMM's prepared form, then the GEMM
         uint8_t *xp = base;

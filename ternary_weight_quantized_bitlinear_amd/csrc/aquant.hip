@@ -177,6 +177,69 @@ aq_prepare(const uint8_t *__restrict__ xq, int64_t M, int64_t K, uint8_t *__rest
     if (lane == 0) rowsum[m] = csum;
 }
 
+// FP6 operand blocks for the 4-bit-activation GEMM on the scaled matrix cores (see
+// gemm_f6f4.hip): code q enters as q/2 in e2m3 (sign, 2 exponent bits with bias 1, 3
+// mantissa bits), exact for every int4 code -8..7: |q| <= 4 gives the codes 4|q| (0,
+// 0.5 subnormal, 1, 1.5, 2), |q| in 5..8 gives 2|q| + 8 (2.5, 3, 3.5, 4).
+__device__ __forceinline__ uint32_t fp6_half(int q) {
+    const int a = q < 0 ? -q : q;
+    return (q < 0 ? 32u : 0u) | (uint32_t)(a <= 4 ? 4 * a : 2 * a + 8);
+}
+
+// Block (kb, mb) holds tokens 32 mb .. 32 mb + 31 over k = 64 kb .. 64 kb + 63 as the
+// matrix core's operand registers: lane slot l (token l % 32, k half l / 32) owns 32
+// values, element e of the half being k_local(e) = 16 (e / 16) + 2 (e % 8) + (e / 8) % 2
+// (the order in which the GEMM spreads 2-bit weight fields into FP4 nibbles), value e
+// in bits 6e of the slot's 192 bits.  Slot dwords 0-1 sit in a 512-byte plane, dwords
+// 2-5 in a 1024-byte plane, so that a wave reads each plane with consecutive lanes.
+// Blocks of one kb are contiguous over mb; tokens past M are zero.
+template <int kKbPerWave>
+__global__ void __launch_bounds__(kAqThreads)
+aq_prepare_f6(const uint8_t *__restrict__ xq, int64_t M, int64_t K, int64_t mb_pad,
+              uint8_t *__restrict__ xp, int32_t *__restrict__ rowsum) {
+    __shared__ int red[kAqThreads / kWave][32];
+    const int64_t mb = blockIdx.x;
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+    const int r32 = lane >> 1, g = lane & 1;  // adjacent lanes read adjacent 16 bytes of a row
+    const int slot = r32 + 32 * g;
+    const int64_t m = 32 * mb + r32;
+    const int64_t nkb = K / 64;
+    const int64_t kb0 = (int64_t)blockIdx.y * (kKbPerWave * (kAqThreads / kWave));
+    int csum = 0;
+#pragma unroll
+    for (int it = 0; it < kKbPerWave; ++it) {
+        const int64_t kb = kb0 + (int64_t)it * (kAqThreads / kWave) + wave;
+        if (kb >= nkb) break;
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+        if (m < M) v = *reinterpret_cast<const uint4 *>(xq + m * (K / 2) + 32 * kb + 16 * g);
+        const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+        uint32_t o[6] = {0u, 0u, 0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int e = 0; e < 32; ++e) {
+            const int kl = 16 * (e / 16) + 2 * (e % 8) + (e / 8) % 2;
+            const int q = ((int)(d[kl / 8] << (28 - 4 * (kl % 8)))) >> 28;
+            csum += q;
+            const uint32_t c = fp6_half(q);
+            const int bit = 6 * e;
+            o[bit / 32] |= c << (bit % 32);
+            if (bit % 32 > 26) o[bit / 32 + 1] |= c >> (32 - bit % 32);
+        }
+        uint8_t *blk = xp + ((size_t)kb * (size_t)mb_pad + (size_t)mb) * 1536;
+        *reinterpret_cast<uint2 *>(blk + 8 * slot) = make_uint2(o[0], o[1]);
+        *reinterpret_cast<uint4 *>(blk + 512 + 16 * slot) = make_uint4(o[2], o[3], o[4], o[5]);
+    }
+    // the token's two halves, then the block's waves; one atomic per token and block
+    csum += __shfl_xor(csum, 1);
+    if (g == 0) red[wave][r32] = csum;
+    __syncthreads();
+    if (threadIdx.x < 32 && 32 * mb + threadIdx.x < M) {
+        int t = 0;
+#pragma unroll
+        for (int w = 0; w < kAqThreads / kWave; ++w) t += red[w][threadIdx.x];
+        atomicAdd(rowsum + 32 * mb + threadIdx.x, t);
+    }
+}
+
 template <bool kBf16>
 __global__ void __launch_bounds__(kAqThreads)
 aq_tensor_amax(const void *__restrict__ x, int64_t n8, uint32_t *__restrict__ amax_bits) {
@@ -273,6 +336,19 @@ hipError_t launch_prepare_acts(const void *xq, int bits, int64_t M, int64_t K, u
     else
         hipLaunchKernelGGL(aq_prepare<4>, dim3(g), dim3(kAqThreads), 0, s,
                            static_cast<const uint8_t *>(xq), M, K, xp, rowsum);
+    return hipGetLastError();
+}
+
+hipError_t launch_prepare_acts_f6(const void *xq, int64_t M, int64_t K, uint8_t *xp,
+                                  int32_t *rowsum, hipStream_t s) {
+    constexpr int kKbPerWave = 2;
+    constexpr int kKbPerBlock = kKbPerWave * (kAqThreads / kWave);
+    hipError_t e = launch_zero_u32(reinterpret_cast<uint32_t *>(rowsum), M, s);
+    if (e != hipSuccess) return e;
+    const int64_t mb_pad = f6_mb_pad(M);
+    const dim3 grid((unsigned)mb_pad, (unsigned)((K / 64 + kKbPerBlock - 1) / kKbPerBlock));
+    hipLaunchKernelGGL(aq_prepare_f6<kKbPerWave>, grid, dim3(kAqThreads), 0, s,
+                       static_cast<const uint8_t *>(xq), M, K, mb_pad, xp, rowsum);
     return hipGetLastError();
 }
 

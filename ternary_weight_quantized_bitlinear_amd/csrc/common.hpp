@@ -181,6 +181,14 @@ hipError_t launch_rmsnorm_quantize(void *x, const void *delta, void *h, int64_t 
 hipError_t allow_lds(const void *fn, size_t lds);
 hipError_t launch_prepare_acts(const void *xq, int bits, int64_t M, int64_t K, uint8_t *xp,
                                int32_t *rowsum, hipStream_t s);
+// FP6 operand blocks of int4 codes for the scaled-MFMA GEMM: 1536 bytes per 32 tokens x
+// 64 k, tokens padded to a multiple of 256; plus sum_k q per token
+inline int64_t f6_mb_pad(int64_t M) { return 8 * ((M + 255) / 256); }
+inline size_t f6_prepared_bytes(int64_t M, int64_t K) {
+    return (size_t)(K / 64) * (size_t)f6_mb_pad(M) * 1536;
+}
+hipError_t launch_prepare_acts_f6(const void *xq, int64_t M, int64_t K, uint8_t *xp,
+                                  int32_t *rowsum, hipStream_t s);
 // decode-sized M: one launch, optional fused activation quantization prologue
 bool gemv_supports(int64_t M, int64_t K);
 hipError_t launch_gemv(const FwdArgs &a, bool fused, void *ws, hipStream_t s);
@@ -191,5 +199,8 @@ hipError_t launch_gemm(const FwdArgs &a, void *ws, hipStream_t s);
 bool gemm_big_supports(int64_t M, int64_t N, int64_t K, int bits);
 hipError_t launch_gemm_big(const FwdArgs &a, hipStream_t s);
 size_t ws_gemm(int64_t M, int64_t N, int64_t K);
+// prefill-sized M with 4-bit activations: FP6 x FP4 scaled MFMA (exact for K < 2^20)
+bool gemm_f6f4_supports(int64_t M, int64_t N, int64_t K, int bits);
+hipError_t launch_gemm_f6f4(const FwdArgs &a, hipStream_t s);
 
 }  // namespace bl
