@@ -4,15 +4,23 @@
 // Formulation of BitLinear", eq. 1, and "BitNet 2B4T Guide", "1. The BitLinear
 // Operator": gamma = (1/nm) sum |W_ij|, W~ = Clip(Round(W / gamma), -1, 1).
 //
-// Three kernels:
-//  1. bins    -- the exact sum of |W|: every finite fp32 |w| is m * 2^(max(e,1)-150)
+// Four kernels:
+//  1. zero    -- clears the exponent sums in the workspace.
+//  2. bins    -- the exact sum of |W|: every finite fp32 |w| is m * 2^(max(e,1)-150)
 //               with a 24-bit integer m, so summing m per biased exponent e in 64-bit
-//               integers (LDS atomics per wave, then global atomics) is exact and
-//               independent of the order in which the GPU adds.
-//  2. finalize -- one thread combines the 256 exponent sums into a 320-bit integer,
-//               divides by N*K and rounds once to fp32 (nearest, ties to even):
-//               gamma = max(that, eps).  It also derives the code threshold T below.
-//  3. pack    -- c = sign(w) if |w| >= T else 0, written as 2-bit fields c+1.
+//               integers is exact and independent of the order in which the GPU adds.
+//               Each lane adds most values into one 64-bit fixed-point register whose
+//               unit is 2^(e_lo-150), for e in a 24-exponent window [e_lo, e_lo + 24)
+//               set from its wave's first values (every term < 2^48, so 2^11 of them
+//               fit); every 256 loads the register goes into the bins as three 24-bit
+//               chunks at e_lo, e_lo + 24, e_lo + 48, which is the same number.  Values
+//               outside the window go to the per-wave LDS bins one by one.  The block's
+//               bins then go to the global ones with atomics.
+//  3. finalize -- one wave: the 256 sums become a 320-bit integer (limb by limb, in
+//               registers, reduced across the wave), which is divided by N*K and
+//               rounded once to fp32 (nearest, ties to even): gamma = max(that, eps).
+//               It also derives the code threshold T below.
+//  4. pack    -- c = sign(w) if |w| >= T else 0, written as 2-bit fields c+1.
 //
 // Threshold form of the rounding: the fp32 quotient q = fl(|w| / gamma) rounds (half
 // to even) to a nonzero code exactly when q > 1/2, i.e. when the real quotient
@@ -34,98 +42,151 @@ struct WqWorkspace {
 
 constexpr int kBinThreads = 256;
 constexpr int kBinWaves = kBinThreads / kWave;
+constexpr int kWindow = 24;        // exponents summed in registers
+constexpr int kFlushEvery = 256;   // loads between register flushes (<= 2^11 terms)
 
-__device__ __forceinline__ void bin_one(unsigned long long *wbins, float w) {
-    uint32_t b = __float_as_uint(w) & 0x7FFFFFFFu;
-    uint32_t e = b >> 23;
-    uint32_t m = (b & 0x7FFFFFu) | (e ? 0x800000u : 0u);
-    if (m) atomicAdd(&wbins[e], (unsigned long long)m);
+__device__ __forceinline__ void split_abs(float w, uint32_t &e, uint32_t &m) {
+    const uint32_t b = __float_as_uint(w) & 0x7FFFFFFFu;
+    e = b >> 23;
+    m = (b & 0x7FFFFFu) | (e ? 0x800000u : 0u);
 }
 
-template <bool kBf16>
-__global__ void __launch_bounds__(kBinThreads) wq_bins(const void *__restrict__ w, int64_t nvec,
-                                                       WqWorkspace *__restrict__ ws) {
-    __shared__ unsigned long long sb[kBinWaves][256];
-    for (int i = threadIdx.x; i < kBinWaves * 256; i += kBinThreads) (&sb[0][0])[i] = 0ull;
-    __syncthreads();
-    unsigned long long *wb = sb[threadIdx.x / kWave];
-    const int64_t stride = (int64_t)gridDim.x * kBinThreads;
-    for (int64_t v = (int64_t)blockIdx.x * kBinThreads + threadIdx.x; v < nvec; v += stride) {
-        // one 16-byte vector: 4 fp32 or 8 bf16
-        uint4 q = reinterpret_cast<const uint4 *>(w)[v];
-        if (kBf16) {
-            bin_one(wb, bf16_lo(q.x)); bin_one(wb, bf16_hi(q.x));
-            bin_one(wb, bf16_lo(q.y)); bin_one(wb, bf16_hi(q.y));
-            bin_one(wb, bf16_lo(q.z)); bin_one(wb, bf16_hi(q.z));
-            bin_one(wb, bf16_lo(q.w)); bin_one(wb, bf16_hi(q.w));
-        } else {
-            bin_one(wb, __uint_as_float(q.x)); bin_one(wb, __uint_as_float(q.y));
-            bin_one(wb, __uint_as_float(q.z)); bin_one(wb, __uint_as_float(q.w));
-        }
-    }
-    __syncthreads();
-    for (int e = threadIdx.x; e < 256; e += kBinThreads) {
-        unsigned long long t = 0;
+// into the lane's fixed-point register when inside the window; returns whether the
+// value is nonzero and outside it (then it goes to the wave's LDS bins separately)
+__device__ __forceinline__ bool add_fast(unsigned long long &acc, int e_lo, float w) {
+    uint32_t e, m;
+    split_abs(w, e, m);
+    const uint32_t d = e - (uint32_t)e_lo;
+    const bool in = d < (uint32_t)kWindow;
+    acc += in ? (unsigned long long)m << d : 0ull;
+    return !in && m != 0u;
+}
+
+// element j of a 16-byte vector of 4 fp32 or 8 bf16 weights
+template <bool kBf16> __device__ __forceinline__ float elem(const uint4 &q, int j) {
+    if (!kBf16) return __uint_as_float(j == 0 ? q.x : j == 1 ? q.y : j == 2 ? q.z : q.w);
+    const uint32_t word = j < 2 ? q.x : j < 4 ? q.y : j < 6 ? q.z : q.w;
+    return (j & 1) ? bf16_hi(word) : bf16_lo(word);
+}
+
+__device__ __forceinline__ void add_slow(unsigned long long *wbins, float w) {
+    uint32_t e, m;
+    split_abs(w, e, m);
+    atomicAdd(&wbins[e], (unsigned long long)m);
+}
+
+// the wave's registers into its bins: acc * 2^(e_lo-150) as three 24-bit significands at
+// exponents e_lo, +24, +48, each summed over the wave first (64 x 2^24 < 2^31); the
+// whole wave must call it (e_lo is the same in every lane)
+__device__ __forceinline__ void flush(unsigned long long *wbins, unsigned long long &acc, int e_lo) {
 #pragma unroll
-        for (int j = 0; j < kBinWaves; ++j) t += sb[j][e];
-        if (t) atomicAdd(&ws->bins[e], t);
+    for (int c = 0; c < 3; ++c) {
+        const int part = wave_sum((int)((acc >> (24 * c)) & 0xFFFFFFull));
+        if ((threadIdx.x & (kWave - 1)) == 0 && part) wbins[e_lo + 24 * c] += (unsigned long long)part;
     }
+    acc = 0;
 }
 
-__global__ void wq_zero(WqWorkspace *ws) {
-    for (int i = threadIdx.x; i < 256; i += blockDim.x) ws->bins[i] = 0ull;
+// 64-bit sum over the wave on DPP lane moves (as wave_sum, with a carry between halves)
+template <int kCtrl, int kRowMask = 0xF>
+__device__ __forceinline__ void dpp_add_u64(uint32_t &lo, uint32_t &hi) {
+    const uint32_t l2 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)lo, kCtrl, kRowMask, 0xF, false);
+    const uint32_t h2 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)hi, kCtrl, kRowMask, 0xF, false);
+    const uint32_t nl = lo + l2;
+    hi = hi + h2 + (nl < lo ? 1u : 0u);
+    lo = nl;
+}
+__device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v) {
+    uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+    dpp_add_u64<kDppQuadXor1>(lo, hi);
+    dpp_add_u64<kDppQuadXor2>(lo, hi);
+    dpp_add_u64<kDppHalfMirror>(lo, hi);
+    dpp_add_u64<kDppMirror>(lo, hi);
+    dpp_add_u64<kDppBcast15, 0xA>(lo, hi);
+    dpp_add_u64<kDppBcast31, 0xC>(lo, hi);
+    lo = (uint32_t)__builtin_amdgcn_readlane((int)lo, 63);
+    hi = (uint32_t)__builtin_amdgcn_readlane((int)hi, 63);
+    return ((unsigned long long)hi << 32) | lo;
 }
 
-// 320-bit unsigned integer, little-endian 32-bit limbs.
+// 320-bit unsigned integers as 10 little-endian 32-bit limbs, always indexed by
+// compile-time constants so that they live in registers
 constexpr int kLimbs = 10;
 
-__device__ void big_add(uint32_t *a, uint64_t v, int shift) {
-    // add v * 2^shift; v < 2^64, shift <= 253
-    int li = shift >> 5, off = shift & 31;
-    uint32_t p0 = (uint32_t)(v << off);
-    uint32_t p1 = off ? (uint32_t)(v >> (32 - off)) : (uint32_t)(v >> 32);
-    uint32_t p2 = off ? (uint32_t)(v >> (64 - off)) : 0u;
-    uint64_t c = 0;
-    for (int i = li; i < kLimbs; ++i) {
-        uint32_t add = i == li ? p0 : i == li + 1 ? p1 : i == li + 2 ? p2 : 0u;
-        uint64_t t = (uint64_t)a[i] + add + c;
-        a[i] = (uint32_t)t;
-        c = t >> 32;
-    }
+// bits [32 L, 32 L + 32) of v * 2^sh, v < 2^56
+template <int L> __device__ __forceinline__ uint32_t limb_of(unsigned long long v, int sh) {
+    const int d = 32 * L - sh;
+    if (d >= 56 || d <= -32) return 0u;
+    return d >= 0 ? (uint32_t)(v >> d) : (uint32_t)(v << (-d));
 }
 
-__device__ __forceinline__ int big_bit(const uint32_t *a, int i) { return (a[i >> 5] >> (i & 31)) & 1; }
+template <int L> __device__ __forceinline__ void add_limbs(unsigned long long (&t)[kLimbs],
+                                                           unsigned long long v, int sh) {
+    t[L] += limb_of<L>(v, sh);
+    if constexpr (L + 1 < kLimbs) add_limbs<L + 1>(t, v, sh);
+}
 
-__global__ void wq_finalize(WqWorkspace *__restrict__ ws, uint64_t count, float eps,
-                            float *__restrict__ gamma_out) {
-    if (threadIdx.x != 0) return;
-    // sum_e bins[e] * 2^(max(e,1)-1), in units of 2^-149
-    uint32_t s[kLimbs];
-    for (int i = 0; i < kLimbs; ++i) s[i] = 0;
-    for (int e = 0; e < 255; ++e) {
-        uint64_t v = ws->bins[e];
-        if (v) big_add(s, v, (e ? e : 1) - 1);
+// bit i (runtime) of the limbs
+__device__ __forceinline__ uint32_t bit_at(const uint32_t (&s)[kLimbs], int i) {
+    uint32_t w = 0;
+#pragma unroll
+    for (int L = 0; L < kLimbs; ++L) w = (i >> 5) == L ? s[L] : w;
+    return (i >= 0 && i < 32 * kLimbs) ? (w >> (i & 31)) & 1u : 0u;
+}
+
+// one wave: gamma and the threshold from the finished exponent sums
+__global__ void __launch_bounds__(kWave) wq_finalize(WqWorkspace *__restrict__ ws, uint64_t count,
+                                                     float eps, float *__restrict__ gamma_out) {
+    const int lane = threadIdx.x;
+    // sum_e bins[e] * 2^(max(e,1)-1), in units of 2^-149: lane l adds bins 4l .. 4l+3
+    unsigned long long t[kLimbs];
+#pragma unroll
+    for (int L = 0; L < kLimbs; ++L) t[L] = 0ull;
+    bool nonfinite = false;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int e = 4 * lane + j;
+        const unsigned long long v = ws->bins[e];
+        if (e == 255) nonfinite = v != 0ull;
+        else add_limbs<0>(t, v, (e ? e : 1) - 1);
     }
-    bool nonfinite = ws->bins[255] != 0ull;
+    nonfinite = __any(nonfinite);
+    uint32_t s[kLimbs];
+    unsigned long long carry = 0;
+#pragma unroll
+    for (int L = 0; L < kLimbs; ++L) {
+        const unsigned long long x = wave_sum_u64(t[L]) + carry;  // each < 2^40
+        s[L] = (uint32_t)x;
+        carry = x >> 32;
+    }
     // quotient and remainder of the division by count (< 2^32)
-    uint64_t r = 0;
-    for (int i = kLimbs - 1; i >= 0; --i) {
-        uint64_t cur = (r << 32) | s[i];
-        s[i] = (uint32_t)(cur / count);
-        r = cur - (uint64_t)s[i] * count;
+    unsigned long long r = 0;
+#pragma unroll
+    for (int L = kLimbs - 1; L >= 0; --L) {
+        const unsigned long long cur = (r << 32) | s[L];
+        s[L] = (uint32_t)(cur / count);
+        r = cur - (unsigned long long)s[L] * count;
     }
     int top = -1;
-    for (int i = kLimbs - 1; i >= 0 && top < 0; --i)
-        if (s[i]) top = i * 32 + 31 - __clz(s[i]);
+#pragma unroll
+    for (int L = 0; L < kLimbs; ++L)
+        if (s[L]) top = 32 * L + 31 - __clz(s[L]);
     // keep 24 significant bits (fewer below 2^23 units: subnormal quantum = 1 unit)
-    int sh = top > 23 ? top - 23 : 0;
+    const int sh = top > 23 ? top - 23 : 0;
     uint32_t mant = 0;
-    for (int i = 23; i >= 0; --i) mant = (mant << 1) | (uint32_t)big_bit(s, sh + i);
+#pragma unroll
+    for (int i = 23; i >= 0; --i) mant = (mant << 1) | bit_at(s, sh + i);
     bool up;
     if (sh > 0) {
-        bool half = big_bit(s, sh - 1);
+        const bool half = bit_at(s, sh - 1);
         bool rest = r != 0;
-        for (int i = 0; i < sh - 1 && !rest; ++i) rest = big_bit(s, i);
+        // any bit below sh - 1
+#pragma unroll
+        for (int L = 0; L < kLimbs; ++L) {
+            const int lo = 32 * L, n = sh - 1 - lo;  // bits of limb L below sh - 1
+            const uint32_t mask = n >= 32 ? 0xFFFFFFFFu : n <= 0 ? 0u : ((1u << n) - 1u);
+            rest = rest || (s[L] & mask) != 0u;
+        }
         up = half && (rest || (mant & 1u));
     } else {
         up = 2 * r > count || (2 * r == count && (mant & 1u));
@@ -138,12 +199,98 @@ __global__ void wq_finalize(WqWorkspace *__restrict__ ws, uint64_t count, float 
         g = __uint_as_float(0x7FC00000u);
         thr = g;  // every comparison false: all codes 0
     } else {
-        double t = (double)g * (0.5 + 0x1p-25);  // exact in fp64
-        thr = (float)t;
-        if ((double)thr <= t) thr = __uint_as_float(__float_as_uint(thr) + 1u);
+        const double tt = (double)g * (0.5 + 0x1p-25);  // exact in fp64
+        thr = (float)tt;
+        if ((double)thr <= tt) thr = __uint_as_float(__float_as_uint(thr) + 1u);
     }
-    ws->thr = thr;
-    *gamma_out = g;
+    if (lane == 0) {
+        ws->thr = thr;
+        *gamma_out = g;
+    }
+}
+
+template <bool kBf16>
+__global__ void __launch_bounds__(kBinThreads) wq_bins(const void *__restrict__ w, int64_t nvec,
+                                                       WqWorkspace *__restrict__ ws) {
+    __shared__ unsigned long long sb[kBinWaves][256];
+    for (int i = threadIdx.x; i < kBinWaves * 256; i += kBinThreads) (&sb[0][0])[i] = 0ull;
+    const int wave = threadIdx.x / kWave;
+    unsigned long long *wb = sb[wave];
+    const int64_t stride = (int64_t)gridDim.x * kBinThreads;
+    const int64_t v0 = (int64_t)blockIdx.x * kBinThreads + threadIdx.x;
+    // one 16-byte vector: 4 fp32 or 8 bf16
+    auto load = [&](int64_t v, float (&x)[8]) __attribute__((always_inline)) {
+        const uint4 q = reinterpret_cast<const uint4 *>(w)[v];
+        if (kBf16) {
+            x[0] = bf16_lo(q.x); x[1] = bf16_hi(q.x); x[2] = bf16_lo(q.y); x[3] = bf16_hi(q.y);
+            x[4] = bf16_lo(q.z); x[5] = bf16_hi(q.z); x[6] = bf16_lo(q.w); x[7] = bf16_hi(q.w);
+        } else {
+            x[0] = __uint_as_float(q.x); x[1] = __uint_as_float(q.y);
+            x[2] = __uint_as_float(q.z); x[3] = __uint_as_float(q.w);
+        }
+    };
+    constexpr int kPer = kBf16 ? 8 : 4;
+    // the window: its top 4 exponents above the largest of the wave's first values
+    uint32_t emax = 0;
+    if (v0 < nvec) {
+        float x[8];
+        load(v0, x);
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            uint32_t e, m;
+            split_abs(x[j], e, m);
+            emax = e > emax && e < 255u ? e : emax;
+        }
+    }
+    emax = __float_as_uint(wave_max_abs(__uint_as_float(emax)));  // max over the wave's bits
+    const int e_lo = min(max((int)emax + 4 - kWindow, 1), 190);
+    __syncthreads();
+    unsigned long long acc = 0;
+    int n = 0;
+    // Several loads in flight per lane.  Every lane runs its wave's trip count (loads past
+    // the end read as zeros, which add nothing), so the flushes, which reduce across the
+    // wave, always run with the whole wave.
+    constexpr int kU = kBf16 ? 4 : 8;  // 32 values per group
+    const int64_t wbase = (int64_t)blockIdx.x * kBinThreads + (threadIdx.x & ~(kWave - 1));
+    const int64_t trips = wbase < nvec ? (nvec - wbase + stride - 1) / stride : 0;
+    for (int64_t it = 0; it < trips; it += kU) {
+        uint4 q[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const int64_t v = v0 + (it + u) * stride;
+            q[u] = v < nvec ? reinterpret_cast<const uint4 *>(w)[v] : make_uint4(0u, 0u, 0u, 0u);
+        }
+        uint64_t slow = 0;  // one bit per value outside the window
+#pragma unroll
+        for (int u = 0; u < kU; ++u)
+#pragma unroll
+            for (int j = 0; j < kPer; ++j)
+                slow |= (uint64_t)add_fast(acc, e_lo, elem<kBf16>(q[u], j)) << (u * kPer + j);
+        if (slow) {
+#pragma unroll
+            for (int u = 0; u < kU; ++u)
+#pragma unroll
+                for (int j = 0; j < kPer; ++j)
+                    if ((slow >> (u * kPer + j)) & 1u) add_slow(wb, elem<kBf16>(q[u], j));
+        }
+        n += kU;
+        if (n >= kFlushEvery) {  // the same count in every lane of the wave
+            flush(wb, acc, e_lo);
+            n = 0;
+        }
+    }
+    flush(wb, acc, e_lo);
+    __syncthreads();
+    for (int e = threadIdx.x; e < 256; e += kBinThreads) {
+        unsigned long long t = 0;
+#pragma unroll
+        for (int j = 0; j < kBinWaves; ++j) t += sb[j][e];
+        if (t) atomicAdd(&ws->bins[e], t);
+    }
+}
+
+__global__ void wq_zero(WqWorkspace *ws) {
+    for (int i = threadIdx.x; i < 256; i += blockDim.x) ws->bins[i] = 0ull;
 }
 
 __device__ __forceinline__ uint32_t field_of(float w, float thr) {
@@ -201,13 +348,14 @@ hipError_t launch_quantize_weights(const void *w, int w_bf16, int64_t N, int64_t
     const int64_t count = N * K;
     const int64_t nvec = count / (w_bf16 ? 8 : 4);  // K % 16 == 0: whole 16-byte vectors
     hipLaunchKernelGGL(wq_zero, dim3(1), dim3(256), 0, s, ws);
-    // enough blocks to fill the chip several times; each block flushes <= 256 atomics
-    const int nb = grid_for(nvec, kBinThreads * 8, 2048);
+    // about two blocks per CU: every block adds its nonzero bins to the same few global
+    // ones, so fewer, longer blocks contend less
+    const int nb = grid_for(nvec, kBinThreads * 8, 512);
     if (w_bf16)
         hipLaunchKernelGGL(wq_bins<true>, dim3(nb), dim3(kBinThreads), 0, s, w, nvec, ws);
     else
         hipLaunchKernelGGL(wq_bins<false>, dim3(nb), dim3(kBinThreads), 0, s, w, nvec, ws);
-    hipLaunchKernelGGL(wq_finalize, dim3(1), dim3(64), 0, s, ws, (uint64_t)count, eps, gamma);
+    hipLaunchKernelGGL(wq_finalize, dim3(1), dim3(kWave), 0, s, ws, (uint64_t)count, eps, gamma);
     const int np = grid_for(nvec, 256, 1 << 20);
     if (w_bf16)
         hipLaunchKernelGGL(wq_pack_bf16, dim3(np), dim3(256), 0, s,

@@ -37,6 +37,9 @@ def _weights_case(kind, n, k, seed=0):
         return (1e-9 * rng.standard_normal((n, k))).astype(np.float32)
     if kind == "halfgrid":  # many exact ties at gamma/2 multiples
         return (rng.integers(-4, 5, (n, k)) * 0.25).astype(np.float32)
+    if kind == "wide":  # exponents over the whole finite range, subnormals included
+        mag = np.ldexp(1.0 + rng.random((n, k)), rng.integers(-150, 120, (n, k)))
+        return (np.where(rng.random((n, k)) < 0.5, -1.0, 1.0) * mag).astype(np.float32)
     raise ValueError(kind)
 
 
@@ -51,6 +54,8 @@ def _weights_case(kind, n, k, seed=0):
     ("zeros", 16, 64, "f32"),
     ("tiny", 33, 32, "f32"),
     ("halfgrid", 64, 128, "f32"),
+    ("wide", 300, 512, "f32"),
+    ("wide", 1000, 1024, "bf16"),
     ("ternary", 6912, 2560, "f32"),
     ("ternary", 2560, 6912, "f32"),
     ("gauss", 7680, 2560, "bf16"),
