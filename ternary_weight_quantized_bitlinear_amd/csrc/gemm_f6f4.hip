@@ -153,14 +153,11 @@ gemm_f6f4_kernel(F6Params p) {
         doff[i] = act ? 1024 * u : kAStage + wr * 16;
         dlanes[i] = (act || T::kWRows == 64) ? ~0ull : (1ull << T::kWRows) - 1;
     }
-    // DMA i of the stage for k step kt into ring slot `slot`
-    auto issue_dma = [&](int kt, int slot, int i) __attribute__((always_inline)) {
-        const uint64_t ktc = (uint64_t)min(kt, nk - 1);  // past the end: reload the last step (unused)
-        lds_dma16(dsrc[i] + ktc * dstride[i], lds0 + slot * T::kStageBytes + doff[i], dlanes[i]);
-    };
     auto issue_stage = [&](int kt, int slot) __attribute__((always_inline)) {
+        const uint64_t ktc = (uint64_t)min(kt, nk - 1);  // past the end: reload the last step (unused)
 #pragma unroll
-        for (int i = 0; i < kDma; ++i) issue_dma(kt, slot, i);
+        for (int i = 0; i < kDma; ++i)
+            lds_dma16(dsrc[i] + ktc * dstride[i], lds0 + slot * T::kStageBytes + doff[i], dlanes[i]);
     };
 
     v16f acc[2][4];
@@ -201,51 +198,6 @@ gemm_f6f4_kernel(F6Params p) {
         c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wf, af, c, 4, 2, 0, 127, 0, 127);
     };
 
-#ifndef BL_F6_PIPE
-#define BL_F6_PIPE 1
-#endif
-#if BL_F6_PIPE == 2
-    // Per k step: the wait for the next stage and the barrier (which also certifies that
-    // every wave is done with the slot the new DMAs refill); the next step's fragment
-    // reads; then the eight MFMAs of this step on fragments already in registers, with
-    // this wave's DMAs spread between them (a DMA can wait to be accepted while the CU's
-    // other waves issue theirs: MFMAs queued ahead of it keep the matrix core busy) and
-    // the next step's field spreading last.  Two fragment sets take turns (the loop is
-    // unrolled by two).
-    struct Frag { v8i a[2]; v8i w[4]; };
-    Frag f0, f1;
-    uint2 wp[4];
-    wait_vm<(kStages - 2) * kDma>();
-    __syncthreads();
-    read_w(0, wp);
-    read_a(0, 0, f0.a[0]);
-    read_a(0, 1, f0.a[1]);
-    expand(wp, f0.w);
-    constexpr int kMfPerDma = 8 / kDma;
-    auto step = [&](int kt, Frag &cur, Frag &nxt) __attribute__((always_inline)) {
-        wait_vm<(kStages - 3) * kDma>();
-        __syncthreads();
-        read_w(kt + 1, wp);
-        read_a(kt + 1, 0, nxt.a[0]);
-        read_a(kt + 1, 1, nxt.a[1]);
-#pragma unroll
-        for (int q = 0; q < kDma; ++q) {
-#pragma unroll
-            for (int t = q * kMfPerDma; t < (q + 1) * kMfPerDma; ++t)
-                mfma(cur.w[t & 3], cur.a[t >> 2], acc[t >> 2][t & 3]);
-            __builtin_amdgcn_sched_barrier(0);
-            issue_dma(kt + kStages - 1, (kt + kStages - 1) % kStages, q);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        expand(wp, nxt.w);
-    };
-#pragma unroll 1
-    for (int kt = 0; kt + 1 < nk; kt += 2) {
-        step(kt, f0, f1);
-        step(kt + 1, f1, f0);
-    }
-    if (nk & 1) step(nk - 1, f0, f1);
-#elif BL_F6_PIPE
     // Per k step: the wait for the next stage, the barrier (which also certifies that
     // every wave is done with the slot the new DMA refills) and the DMA; then the eight
     // MFMAs of this step on fragments already in registers, with the next step's reads
@@ -291,45 +243,6 @@ gemm_f6f4_kernel(F6Params p) {
         step(kt + 1, f1, f0);
     }
     if (nk & 1) step(nk - 1, f0, f1);
-#else
-    // Per k step: the four MFMAs of token block 0; the wait for the next stage, the
-    // barrier (which also certifies that every wave is done with the slot the new DMA
-    // refills) and the DMA; then the four MFMAs of token block 1 with the next step's
-    // block-0 and weight reads; last, the next step's block-1 read and field spreading,
-    // which overlap the MFMAs still in flight.
-    wait_vm<(kStages - 2) * kDma>();
-    __syncthreads();
-    v8i a0, a1, wf[4];
-    uint2 wp[4];
-    read_a(0, 0, a0);
-    read_a(0, 1, a1);
-    read_w(0, wp);
-    expand(wp, wf);
-#pragma unroll 1
-    for (int kt = 0; kt < nk; ++kt) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) mfma(wf[j], a0, acc[0][j]);
-        __builtin_amdgcn_sched_barrier(0);
-        wait_vm<(kStages - 3) * kDma>();
-        __syncthreads();
-        issue_stage(kt + kStages - 1, (kt + kStages - 1) % kStages);
-        __builtin_amdgcn_sched_barrier(0);
-        read_a(kt + 1, 0, a0);
-        read_w(kt + 1, wp);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) mfma(wf[j], a1, acc[1][j]);
-#pragma unroll
-        for (int t = 0; t < 3; ++t) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS read
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_barrier(0);
-        read_a(kt + 1, 1, a1);
-        expand(wp, wf);
-    }
-
-#endif
 
     // ---- epilogue: lane l holds acc[i][j][r] = 4 x sum for token 64 wt + 32 i + l % 32
     // and row 128 wn + 32 j + 8 (r / 4) + 4 (l / 32) + r % 4: four consecutive outputs
