@@ -19,6 +19,11 @@ source header):
 * :func:`forward`, :func:`forward_at` -- integer contraction, rescale
   ([b158] eq. 3; [a48] dataflow figure), bias, ReLU^2 ([2b4t] "2. Squared
   ReLU Activation").
+* :func:`hadamard_block`, :func:`hadamard_rows`, :func:`quantize_acts_rotated`,
+  :func:`quantize_weights_rotated` -- the Hadamard rotation folded into both
+  operands before the 4-bit activation quantization ([a48] "Best Practices for
+  Deploying BitNet a4.8 in Production", Outlier Suppression row): block-diagonal
+  Sylvester blocks on the K axis, unnormalized fp32 fast transform, 1/b in gamma.
 
 bf16 arrays are passed as ``numpy.uint16`` holding the bf16 bit patterns.
 """
@@ -74,8 +79,14 @@ def _load():
                                           P]
         lib.oracle_to_bf16.argtypes = [P, P, I64]
         lib.oracle_rmsnorm.argtypes = [P, P, I64, I64, F, P, P]
+        lib.oracle_hadamard_block.argtypes = [I64]
+        lib.oracle_hadamard_block.restype = I64
+        lib.oracle_hadamard_rows.argtypes = [P, I, I64, I64, P]
+        lib.oracle_quantize_acts_rotated.argtypes = [P, I, I64, I64, I, I, F, P, P]
+        lib.oracle_quantize_weights_rotated.argtypes = [P, I, I64, I64, F, P, P, P]
         for name in ("oracle_gamma", "oracle_quantize_weights", "oracle_quantize_acts",
-                     "oracle_forward", "oracle_forward_at"):
+                     "oracle_forward", "oracle_forward_at", "oracle_hadamard_rows",
+                     "oracle_quantize_acts_rotated", "oracle_quantize_weights_rotated"):
             getattr(lib, name).restype = I
         lib.oracle_to_bf16.restype = None
         _lib = lib
@@ -198,3 +209,46 @@ def rmsnorm(X: np.ndarray, delta=None, eps: float = 1e-6):
     _check(_load().oracle_rmsnorm(_ptr(X), None if d is None else _ptr(d), M, K, eps,
                                   _ptr(x_out), _ptr(h_out)), "rmsnorm")
     return x_out, h_out
+
+
+def hadamard_block(K: int) -> int:
+    """Block size b of the rotation on a K-wide axis: the largest power of two dividing
+    K, at most 8192."""
+    return int(_load().oracle_hadamard_block(K))
+
+
+def hadamard_rows(X: np.ndarray) -> np.ndarray:
+    """Rows of X (float32, or uint16 bf16 bits) times the block-diagonal unnormalized
+    Hadamard matrix, in fp32 by the fast transform (stage h = 1, 2, ..., b/2)."""
+    X = np.ascontiguousarray(X)
+    M, K = X.shape
+    Y = np.zeros((M, K), np.float32)
+    _check(_load().oracle_hadamard_rows(_ptr(X), _dtype_code(X), M, K, _ptr(Y)),
+           "oracle_hadamard_rows")
+    return Y
+
+
+def quantize_acts_rotated(X: np.ndarray, bits: int = 4, gran: int = PER_TOKEN, eps: float = 1e-5):
+    """quantize_acts of hadamard_rows(X): returns (Xq, act_scale)."""
+    X = np.ascontiguousarray(X)
+    M, K = X.shape
+    Xq = np.zeros((M, K) if bits == 8 else (M, K // 2), np.int8 if bits == 8 else np.uint8)
+    scale = np.zeros(M if gran == PER_TOKEN else 1, np.float32)
+    _check(_load().oracle_quantize_acts_rotated(_ptr(X), _dtype_code(X), M, K, bits, gran, eps,
+                                                _ptr(Xq), _ptr(scale)),
+           "oracle_quantize_acts_rotated")
+    return Xq, scale
+
+
+def quantize_weights_rotated(W: np.ndarray, eps: float = 1e-5):
+    """quantize_weights of hadamard_rows(W), gamma divided by the block size b: returns
+    (packed uint8 [N, K/4], gamma float32, codes int8 [N, K])."""
+    W = np.ascontiguousarray(W)
+    N, K = W.shape
+    packed = np.zeros((N, K // 4), np.uint8)
+    g = np.zeros(1, np.float32)
+    codes = np.zeros((N, K), np.int8)
+    _check(_load().oracle_quantize_weights_rotated(_ptr(W), _dtype_code(W), N, K, eps,
+                                                   _ptr(packed), _ptr(g), _ptr(codes)),
+           "oracle_quantize_weights_rotated")
+    return packed, g[0], codes

@@ -43,8 +43,14 @@
  *     row in bits 2*(k%4) of byte k/4, rows of K/4 bytes, W is [N=out][K=in].
  *   - int4 layout: two's-complement nibbles, element 2i in the low nibble of
  *     byte i, rows of K/2 bytes.
+ *   - the Hadamard rotation before the activation quantization ([a48] "Best
+ *     Practices for Deploying BitNet a4.8 in Production", Outlier Suppression):
+ *     block-diagonal Sylvester blocks of b = the largest power of two dividing K
+ *     (at most 8192), unnormalized, an fp32 fast transform in a fixed stage
+ *     order, folded into both operands, 1/b into gamma (see the section below).
  */
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 #include <math.h>
 
@@ -408,5 +414,84 @@ int oracle_rmsnorm(const uint16_t *X, const uint16_t *delta, int64_t M, int64_t 
             h_out[m * K + k] = narrow_bf16((float)(v * r));
         }
     }
+    return OR_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Hadamard rotation before the activation quantization                      */
+/* ------------------------------------------------------------------------ */
+/*
+ * "BitNet a4.8 Guide", "Best Practices for Deploying BitNet a4.8 in Production",
+ * Outlier Suppression row: rotate with Hadamard transforms, as QuaRot does, before
+ * the 4-bit activation projection, so that outlier channels are spread over many.
+ * The page gives that one line; the readings taken:
+ *   - the transform acts on the K (input) axis of every row and is block-diagonal,
+ *     with Sylvester blocks H_b of size b = the largest power of two dividing K, at
+ *     most 8192:  x'[j b + i] = sum_t x[j b + t] * (-1)^popcount(t & i);
+ *   - as in QuaRot it is folded into both operands of the product: activations
+ *     x -> x H, weight rows w -> w H before the ternary quantization, so that
+ *     x W^T = (x H)(W H)^T / b;  the factor 1/b (a power of two) goes into gamma;
+ *   - H is unnormalized (entries +-1) and applied in fp32 as the fast transform,
+ *     stage h = 1, 2, 4, ..., b/2 in turn, each pair (i, i + h) with (i & h) == 0
+ *     becoming (u + v, u - v): one fixed operation order, so that every value is
+ *     reproducible to the bit.
+ */
+int64_t oracle_hadamard_block(int64_t K)
+{
+    int64_t b = 1;
+    while (b < 8192 && K % (2 * b) == 0) b *= 2;
+    return b;
+}
+
+/* rows of X (fp32 or bf16, [M][K]) -> rows of X H in fp32 */
+int oracle_hadamard_rows(const void *X, int x_dtype, int64_t M, int64_t K, float *Y)
+{
+    if (!X || !Y || M <= 0 || K <= 0) return OR_EINVAL;
+    const int64_t b = oracle_hadamard_block(K);
+    for (int64_t i = 0; i < M * K; ++i) Y[i] = load_elem(X, x_dtype, i);
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t j0 = 0; j0 < K; j0 += b) {
+            float *blk = Y + m * K + j0;
+            for (int64_t h = 1; h < b; h *= 2) {
+                for (int64_t i = 0; i < b; ++i) {
+                    if ((i & h) != 0) continue;
+                    const float u = blk[i], v = blk[i + h];
+                    blk[i] = u + v;
+                    blk[i + h] = u - v;
+                }
+            }
+        }
+    }
+    return OR_OK;
+}
+
+/* activation quantization of X H (the rotation in fp32, then as oracle_quantize_acts) */
+int oracle_quantize_acts_rotated(const void *X, int x_dtype, int64_t M, int64_t K, int bits,
+                                 int gran, float eps, void *Xq, float *act_scale)
+{
+    if (!X || M <= 0 || K <= 0) return OR_EINVAL;
+    float *R = (float *)malloc((size_t)(M * K) * sizeof(float));
+    if (!R) return OR_EINVAL;
+    int st = oracle_hadamard_rows(X, x_dtype, M, K, R);
+    if (st == OR_OK) st = oracle_quantize_acts(R, OR_F32, M, K, bits, gran, eps, Xq, act_scale);
+    free(R);
+    return st;
+}
+
+/* ternary quantization of W H; gamma_out = gamma(W H) / b, the rotation's factor */
+int oracle_quantize_weights_rotated(const void *W, int w_dtype, int64_t N, int64_t K, float eps,
+                                    uint8_t *packed, float *gamma_out, int8_t *codes_out)
+{
+    if (!W || N <= 0 || K <= 0) return OR_EINVAL;
+    float *R = (float *)malloc((size_t)(N * K) * sizeof(float));
+    if (!R) return OR_EINVAL;
+    int st = oracle_hadamard_rows(W, w_dtype, N, K, R);
+    float g = 0.0f;
+    if (st == OR_OK) st = oracle_quantize_weights(R, OR_F32, N, K, eps, packed, &g, codes_out);
+    free(R);
+    if (st != OR_OK) return st;
+    int t = 0; /* b = 2^t */
+    for (int64_t b = oracle_hadamard_block(K); b > 1; b /= 2) ++t;
+    *gamma_out = ldexpf(g, -t);
     return OR_OK;
 }

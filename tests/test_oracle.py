@@ -618,3 +618,125 @@ def test_rmsnorm_eps_dominates_zero_row():
     x = _bf(np.full((1, 32), 2.0 ** -20, np.float32))
     _, h = oracle.rmsnorm(x, eps=1e-6)
     assert np.all(_f(h) < 2.0 ** -20 * 1000.0 * 1.01)
+
+
+# ---------------------------------------------------------------- Hadamard rotation
+# ("BitNet a4.8 Guide", "Best Practices for Deploying BitNet a4.8 in Production",
+# Outlier Suppression row; readings in tests/golden/hadamard_examples.json)
+
+def _hadamard_golden():
+    import json
+    import os
+    with open(os.path.join(os.path.dirname(__file__), "golden", "hadamard_examples.json")) as f:
+        return json.load(f)
+
+
+@pytest.mark.parametrize("K,b", [(4, 4), (12, 4), (48, 16), (256, 256), (2560, 512),
+                                 (6912, 256), (8192, 8192), (16384, 8192), (24576, 8192)])
+def test_hadamard_block_sizes(K, b):
+    # the largest power of two dividing K, at most 8192
+    assert oracle.hadamard_block(K) == b
+
+
+def test_hadamard_worked_examples():
+    for ex in _hadamard_golden()["rows"]:
+        x = np.array([ex["x"]], np.float32)
+        assert oracle.hadamard_block(ex["K"]) == ex["b"]
+        np.testing.assert_array_equal(oracle.hadamard_rows(x)[0], np.array(ex["y"], np.float32),
+                                      err_msg=ex["name"])
+
+
+def test_hadamard_unit_vectors_are_hadamard_rows():
+    # x = e_j -> row j of the Sylvester matrix: (-1)^popcount(i & j), scipy's construction
+    from scipy.linalg import hadamard
+    b = 64
+    H = hadamard(b)
+    X = np.eye(b, dtype=np.float32)
+    Y = oracle.hadamard_rows(X)
+    np.testing.assert_array_equal(Y, H.astype(np.float32))
+    pop = np.array([[bin(i & j).count("1") for i in range(b)] for j in range(b)])
+    np.testing.assert_array_equal(Y, ((-1.0) ** pop).astype(np.float32))
+
+
+@pytest.mark.parametrize("K,dtype", [(1536, "f32"), (2560, "bf16"), (8192, "f32")])
+def test_hadamard_matches_dense_product(K, dtype):
+    # against X @ blockdiag(H_b) in float64: the fp32 fast transform is within its
+    # rounding bound log2(b) * 2^-24 * sum |x| (over the block) of every output
+    from scipy.linalg import hadamard
+    rng = np.random.default_rng(5)
+    X = rng.standard_normal((3, K)).astype(np.float32)
+    X[:, 7] *= 40.0  # an outlier channel
+    Xin = workloads.to_bf16_bits(X) if dtype == "bf16" else X
+    Xf = workloads.bf16_bits_to_f32(Xin) if dtype == "bf16" else X
+    b = oracle.hadamard_block(K)
+    H = hadamard(b).astype(np.float64)
+    Y = oracle.hadamard_rows(Xin).astype(np.float64)
+    L = int(math.log2(b))
+    for j0 in range(0, K, b):
+        blk = Xf[:, j0:j0 + b].astype(np.float64)
+        ref = blk @ H
+        bound = L * 2.0 ** -24 * np.abs(blk).sum(axis=1, keepdims=True) * 1.0001
+        assert (np.abs(Y[:, j0:j0 + b] - ref) <= bound).all()
+
+
+def test_hadamard_involution_exact():
+    # small integers keep every intermediate exact in fp32: H (H x) = b x
+    rng = np.random.default_rng(6)
+    X = rng.integers(-64, 65, (4, 512)).astype(np.float32)
+    b = oracle.hadamard_block(512)
+    np.testing.assert_array_equal(oracle.hadamard_rows(oracle.hadamard_rows(X)), b * X)
+
+
+def test_rotation_folds_into_both_operands_exactly():
+    # (X H)(W H)^T / b = X W^T, exactly for small integers (no quantization involved)
+    rng = np.random.default_rng(7)
+    K = 48
+    X = rng.integers(-8, 9, (3, K)).astype(np.float32)
+    W = rng.integers(-3, 4, (5, K)).astype(np.float32)
+    b = oracle.hadamard_block(K)
+    lhs = oracle.hadamard_rows(X).astype(np.float64) @ oracle.hadamard_rows(W).astype(np.float64).T / b
+    np.testing.assert_array_equal(lhs, X.astype(np.float64) @ W.astype(np.float64).T)
+
+
+def test_rotated_weights_worked_example():
+    ex = _hadamard_golden()["weights"]
+    W = np.array(ex["W"], np.float32)
+    packed, g, codes = oracle.quantize_weights_rotated(W)
+    np.testing.assert_array_equal(codes, np.array(ex["codes"], np.int8))
+    np.testing.assert_array_equal(packed[:, 0], np.array(ex["packed"], np.uint8))
+    assert g == np.float32(ex["gamma"])
+
+
+def test_rotated_acts_worked_example():
+    ex = _hadamard_golden()["acts_int4"]
+    X = np.array([ex["x"]], np.float32)
+    xq, s = oracle.quantize_acts_rotated(X, bits=4)
+    np.testing.assert_array_equal(xq[0], np.array(ex["bytes"], np.uint8))
+    np.testing.assert_array_equal(_unpack_nibbles(xq, 4)[0], np.array(ex["codes"]))
+    assert f32_bits(s[0]) == _bits(ex["scale_bits"])
+
+
+@pytest.mark.parametrize("K", [256, 2560])
+def test_rotated_gamma_is_rotated_mean_over_b(K):
+    # gamma = (exact mean |W H|, rounded once) / b, and the codes are those of W H
+    rng = np.random.default_rng(8)
+    W = (0.02 * rng.standard_normal((64, K))).astype(np.float32)
+    b = oracle.hadamard_block(K)
+    R = oracle.hadamard_rows(W)
+    packed, g, codes = oracle.quantize_weights_rotated(W)
+    ref = Fraction(sum(frac_of_f32(abs(float(v))) for v in R.ravel()), R.size)
+    assert f32_bits(g * np.float32(b)) == f32_bits(round_to_f32(ref))
+    p2, g2, c2 = oracle.quantize_weights(R)
+    np.testing.assert_array_equal(codes, c2)
+    assert g * np.float32(b) == g2
+
+
+def test_rotation_spreads_an_outlier():
+    # one channel 100x the others: rotated, its energy is spread over the block, so the
+    # absmax falls towards the rms (the point of the rotation before 4-bit codes)
+    rng = np.random.default_rng(9)
+    X = rng.standard_normal((8, 512)).astype(np.float32)
+    X[:, 3] = 100.0
+    R = oracle.hadamard_rows(X)
+    ratio = lambda A: (np.abs(A).max(axis=1) / np.sqrt((A.astype(np.float64) ** 2).mean(axis=1)))
+    assert (ratio(X) > 15).all() and (ratio(R) < 5).all()

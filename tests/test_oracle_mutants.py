@@ -31,6 +31,11 @@ MUTANTS = [
     ("rmsnorm_mean_not_sum", "ss / (double)K + (double)eps", "ss + (double)eps", None),
     ("rmsnorm_no_sqrt", "1.0 / sqrt(ss / (double)K + (double)eps)", "1.0 / (ss / (double)K + (double)eps)", None),
     ("rmsnorm_residual_dropped", "v = widen_bf16(narrow_bf16(v + widen_bf16(delta[m * K + k])));", "(void)delta;", None),
+    ("hadamard_butterfly_swapped", "blk[i] = u + v;\n                    blk[i + h] = u - v;", "blk[i] = u - v;\n                    blk[i + h] = u + v;", None),
+    ("hadamard_stage_skipped", "for (int64_t h = 1; h < b; h *= 2)", "for (int64_t h = 2; h < b; h *= 2)", None),
+    ("hadamard_block_uncapped", "while (b < 8192 && K % (2 * b) == 0) b *= 2;", "while (K % (2 * b) == 0) b *= 2;", None),
+    ("hadamard_gamma_not_over_b", "*gamma_out = ldexpf(g, -t);", "*gamma_out = g;", None),
+    ("hadamard_normalized_by_half", "blk[i + h] = u - v;", "blk[i + h] = 0.5f * (u - v);", None),
     ("per_tensor_uses_row_max", "float amax = tensor_max;", "float amax = 0.0f; if (gran == 1) { for (int64_t k = 0; k < K; ++k) { float t = fabsf(load_elem(X, x_dtype, m * K + k)); if (t > amax) amax = t; } }", None),
 ]
 
