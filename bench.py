@@ -410,7 +410,60 @@ def leg_70b(torch, bl, reps=5, err_rows=16):
             "rel_fro_err": float(np.linalg.norm(yh - y_ref) / ref_norm)}
         del xq, ws, wsf
     out["err_sample"] = "%d token rows x all %d outputs vs float64 X (gamma c)^T" % (err_rows, N)
+
+    # Hadamard rotation before the 4-bit activations (the a4.8 page's outlier
+    # suppression), folded into both operands: the same weights rotated and ternarized
+    # again (offline), the activations rotated and quantized in one pass, then the same
+    # FP6 x FP4 GEMM.  Its error is taken against that path's own exact product
+    # (X H)(gamma' c')^T / b, so that it isolates the activation quantization, as above.
+    Wd = torch.from_numpy(codes).to(dev).float()
+    pr, gr = bl.quantize_weights_rotated(Wd)
+    del Wd
+    b = bl.hadamard_block(K)
+    xq, sc = bl.quantize_acts_rotated(Xd, bits=4)
+    ws = torch.empty(bl.workspace_size(bl.BL_OP_FORWARD, M, N, K, 4), dtype=torch.uint8,
+                     device=dev)
+
+    def rot_gemm():
+        for _ in range(reps):
+            bl.forward(xq, sc, pr, gr, bits=4, out=y, workspace=ws)
+
+    def rot_step():
+        for _ in range(reps):
+            bl.quantize_acts_rotated(Xd, bits=4, out=(xq, sc))
+            bl.forward(xq, sc, pr, gr, bits=4, out=y, workspace=ws)
+
+    ms_g = graph_time_ms(torch, rot_gemm, replays=1)[0] / reps
+    ms_s = graph_time_ms(torch, rot_step, replays=1)[0] / reps
+    yh = y.index_select(0, torch.from_numpy(rows).to(dev)).float().cpu().numpy().astype(np.float64)
+    ph = pr.cpu().numpy()
+    c_rot = (((ph[:, :, None] >> np.array([0, 2, 4, 6], np.uint8)) & 3).reshape(N, K)
+             .astype(np.int8) - 1)
+    y_rref = (_fwht_rows(xr, b) @ c_rot.T.astype(np.float64)) * float(gr.cpu()[0])
+    out["int4_rotated"] = {
+        "mfma": "fp6 x fp4 32x32x64 (exact)", "hadamard_block": b,
+        "peak_tops": F6F4_PEAK_TOPS, "frac": ops / (ms_g * 1e-3) / 1e12 / F6F4_PEAK_TOPS,
+        "gemm_us": ms_g * 1e3, "gemm_tops": ops / (ms_g * 1e-3) / 1e12,
+        "step_us": ms_s * 1e3, "step_tops": ops / (ms_s * 1e-3) / 1e12,
+        "rel_fro_err": float(np.linalg.norm(yh - y_rref) / np.linalg.norm(y_rref)),
+        "err_ref": "float64 (X H)(gamma' c')^T / b, c' and gamma' the rotated weights' codes"}
+    del xq, ws, pr
     return out
+
+
+def _fwht_rows(x, b):
+    """Rows of x (float64) times the block-diagonal unnormalized Hadamard matrix, blocks of
+    b along the last axis (a reference: the order of the additions does not matter here)."""
+    M, K = x.shape
+    y = x.reshape(M, K // b, b).copy()
+    h = 1
+    while h < b:
+        v = y.reshape(M, K // b, b // (2 * h), 2, h)
+        lo, hi = v[:, :, :, 0, :].copy(), v[:, :, :, 1, :].copy()
+        v[:, :, :, 0, :] = lo + hi
+        v[:, :, :, 1, :] = lo - hi
+        h *= 2
+    return y.reshape(M, K)
 
 
 def leg_stack(torch, bl, steps=10, layers=30, batch=16):

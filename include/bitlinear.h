@@ -120,6 +120,33 @@ bl_status bitlinear_quantize_acts(const void *X, bl_dtype x_dtype, int64_t M, in
                                   void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Hadamard rotation before the activation quantization ([a48] "Best Practices for
+ * Deploying BitNet a4.8 in Production", Outlier Suppression row: Hadamard rotational
+ * transforms, as in QuaRot, before the 4-bit projection), folded into both operands:
+ *
+ *   H    = block-diagonal along K, Sylvester blocks H_b (entries +-1, unnormalized),
+ *          b = bitlinear_hadamard_block(K): the largest power of two dividing K, at
+ *          most 8192;  (x H)[j b + i] = sum_t x[j b + t] (-1)^popcount(t & i)
+ *   acts:    Xq, act_scale = bitlinear_quantize_acts(X H)
+ *   weights: W_packed, gamma' = bitlinear_quantize_weights(W H);  gamma = gamma' / b
+ *   then bitlinear_forward as usual: x W^T = (x H)(W H)^T / b, the 1/b being in gamma.
+ *
+ * x H is computed in fp32 as the fast transform in stage order h = 1, 2, 4, ..., b/2
+ * (each pair (i, i + h) with (i & h) == 0 becomes (u + v, u - v)), so every rotated
+ * value, code and scale is reproducible to the bit.  Arguments, layouts, workspace and
+ * errors are those of the unrotated calls; in addition K <= 16384 (a rotated row is
+ * held on chip), else BL_EUNSUPPORTED.  Both operands of a product must be rotated.
+ */
+int64_t bitlinear_hadamard_block(int64_t K);
+bl_status bitlinear_quantize_weights_rotated(const void *W, bl_dtype w_dtype, int64_t N, int64_t K,
+                                             float eps, uint8_t *W_packed, float *gamma,
+                                             void *workspace, size_t workspace_bytes, void *stream);
+bl_status bitlinear_quantize_acts_rotated(const void *X, bl_dtype x_dtype, int64_t M, int64_t K,
+                                          int bits, bl_gran gran, float eps, void *Xq,
+                                          float *act_scale, void *workspace,
+                                          size_t workspace_bytes, void *stream);
+
+/*
  * Forward on quantized activations: integer contraction, rescale, bias, ReLU^2.
  *   acc[m][n] = sum_k q[m][k] * c[n][k]          int32 ([a48] "3. Native Hardware
  *                                                INT4 Tensor Core Mapping")

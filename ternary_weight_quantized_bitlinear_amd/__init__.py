@@ -62,6 +62,10 @@ def lib() -> ctypes.CDLL:
                                                       I, P, I, P, SZ, P]
         L.bitlinear_rmsnorm.argtypes = [P, P, P, I64, I64, F, P]
         L.bitlinear_rmsnorm_quantize.argtypes = [P, P, P, I64, I64, F, I, I, F, P, P, P, SZ, P]
+        L.bitlinear_quantize_weights_rotated.argtypes = [P, I, I64, I64, F, P, P, P, SZ, P]
+        L.bitlinear_quantize_acts_rotated.argtypes = [P, I, I64, I64, I, I, F, P, P, P, SZ, P]
+        L.bitlinear_hadamard_block.argtypes = [I64]
+        L.bitlinear_hadamard_block.restype = I64
         L.bitlinear_workspace_size.argtypes = [I, I64, I64, I64, I, I]
         L.bitlinear_workspace_size.restype = SZ
         L.bitlinear_status_string.argtypes = [I]
@@ -71,7 +75,8 @@ def lib() -> ctypes.CDLL:
         L.bitlinear_version.restype = I
         for n in ("bitlinear_quantize_weights", "bitlinear_quantize_acts", "bitlinear_forward",
                   "bitlinear_forward_fused", "bitlinear_forward_fused_batched",
-                  "bitlinear_rmsnorm", "bitlinear_rmsnorm_quantize"):
+                  "bitlinear_rmsnorm", "bitlinear_rmsnorm_quantize",
+                  "bitlinear_quantize_weights_rotated", "bitlinear_quantize_acts_rotated"):
             getattr(L, n).restype = I
         _lib = L
     return _lib
@@ -179,6 +184,45 @@ def quantize_acts(X, bits: int = 8, gran="token", eps: float = 1e-5, workspace=N
                          workspace)
     _check(lib().bitlinear_quantize_acts(_ptr(X), _dtype_code(X), M, K, bits, g, eps, _ptr(Xq),
                                          _ptr(scale), _ptr(ws), wsb, _stream(X.device, stream)))
+    return Xq, scale
+
+
+def hadamard_block(K: int) -> int:
+    """Block size b of the Hadamard rotation on a K-wide axis."""
+    return int(lib().bitlinear_hadamard_block(K))
+
+
+def quantize_weights_rotated(W, eps: float = 1e-5, workspace=None, stream=None, out=None):
+    """quantize_weights of W H (block Hadamard rotation of the rows), gamma divided by the
+    block size: use with activations from quantize_acts_rotated."""
+    torch = _torch()
+    N, K = W.shape
+    packed = out[0] if out else torch.empty((N, K // 4), dtype=torch.uint8, device=W.device)
+    gamma = out[1] if out else torch.empty(1, dtype=torch.float32, device=W.device)
+    ws, wsb = _workspace(workspace_size(BL_OP_QUANTIZE_WEIGHTS, 1, N, K), W.device, workspace)
+    _check(lib().bitlinear_quantize_weights_rotated(_ptr(W), _dtype_code(W), N, K, eps,
+                                                    _ptr(packed), _ptr(gamma), _ptr(ws), wsb,
+                                                    _stream(W.device, stream)))
+    return packed, gamma
+
+
+def quantize_acts_rotated(X, bits: int = 4, gran="token", eps: float = 1e-5, workspace=None,
+                          stream=None, out=None):
+    """quantize_acts of X H (block Hadamard rotation of the rows)."""
+    torch = _torch()
+    M, K = X.shape
+    g = _gran_code(gran)
+    if out:
+        Xq, scale = out
+    else:
+        Xq = torch.empty((M, K) if bits == 8 else (M, K // 2),
+                         dtype=torch.int8 if bits == 8 else torch.uint8, device=X.device)
+        scale = torch.empty(M if g == BL_PER_TOKEN else 1, dtype=torch.float32, device=X.device)
+    ws, wsb = _workspace(workspace_size(BL_OP_QUANTIZE_ACTS, M, 1, K, bits, g), X.device,
+                         workspace)
+    _check(lib().bitlinear_quantize_acts_rotated(_ptr(X), _dtype_code(X), M, K, bits, g, eps,
+                                                 _ptr(Xq), _ptr(scale), _ptr(ws), wsb,
+                                                 _stream(X.device, stream)))
     return Xq, scale
 
 

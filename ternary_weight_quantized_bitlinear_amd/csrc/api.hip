@@ -184,6 +184,56 @@ bl_status bitlinear_quantize_acts(const void *X, bl_dtype x_dtype, int64_t M, in
                   fn);
 }
 
+int64_t bitlinear_hadamard_block(int64_t K) { return K > 0 ? bl::hadamard_block(K) : 0; }
+
+bl_status bitlinear_quantize_weights_rotated(const void *W, bl_dtype w_dtype, int64_t N, int64_t K,
+                                             float eps, uint8_t *W_packed, float *gamma,
+                                             void *workspace, size_t workspace_bytes, void *stream) {
+    static const char fn[] = "bitlinear_quantize_weights_rotated";
+    if (!W || !W_packed || !gamma) return fail(BL_EINVAL, "%s: null pointer", fn);
+    if (!is_xdtype(w_dtype)) return fail(BL_EINVAL, "%s: w_dtype must be BL_F32 or BL_BF16", fn);
+    CHECK(check_shape(1, N, K, fn));
+    CHECK(check_eps(eps, fn));
+    if (K > bl::kRotMaxK)
+        return fail(BL_EUNSUPPORTED, "%s: K=%lld above %lld (a rotated row is held in LDS)", fn,
+                    (long long)K, (long long)bl::kRotMaxK);
+    if (!aligned(W, 16) || !aligned(W_packed, 16) || !aligned(gamma, 4))
+        return fail(BL_EALIGN, "%s: W and W_packed need 16-byte, gamma 4-byte alignment", fn);
+    const size_t need = bl::ws_quantize_weights();
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 16))
+        return fail(BL_EWORKSPACE, "%s: need %zu bytes of 16-byte aligned workspace", fn, need);
+    (void)hipGetLastError();
+    return device(bl::launch_quantize_weights_rotated(W, w_dtype == BL_BF16, N, K, eps, W_packed,
+                                                      gamma, workspace, (hipStream_t)stream),
+                  fn);
+}
+
+bl_status bitlinear_quantize_acts_rotated(const void *X, bl_dtype x_dtype, int64_t M, int64_t K,
+                                          int bits, bl_gran gran, float eps, void *Xq,
+                                          float *act_scale, void *workspace,
+                                          size_t workspace_bytes, void *stream) {
+    static const char fn[] = "bitlinear_quantize_acts_rotated";
+    if (!X || !Xq || !act_scale) return fail(BL_EINVAL, "%s: null pointer", fn);
+    if (!is_xdtype(x_dtype)) return fail(BL_EINVAL, "%s: x_dtype must be BL_F32 or BL_BF16", fn);
+    if (bits != 8 && bits != 4) return fail(BL_EINVAL, "%s: bits must be 8 or 4", fn);
+    if (gran != BL_PER_TOKEN && gran != BL_PER_TENSOR) return fail(BL_EINVAL, "%s: bad gran", fn);
+    CHECK(check_shape(M, 1, K, fn));
+    CHECK(check_eps(eps, fn));
+    if (K > bl::kRotMaxK)
+        return fail(BL_EUNSUPPORTED, "%s: K=%lld above %lld (a rotated row is held in LDS)", fn,
+                    (long long)K, (long long)bl::kRotMaxK);
+    if (!aligned(X, 16) || !aligned(Xq, 16) || !aligned(act_scale, 4))
+        return fail(BL_EALIGN, "%s: X and Xq need 16-byte, act_scale 4-byte alignment", fn);
+    const size_t need = bl::ws_quantize_acts((int)gran);
+    if (need && (!workspace || workspace_bytes < need || !aligned(workspace, 16)))
+        return fail(BL_EWORKSPACE, "%s: need %zu bytes of 16-byte aligned workspace", fn, need);
+    (void)hipGetLastError();
+    return device(bl::launch_quantize_acts_rotated(X, x_dtype == BL_BF16, M, K, bits, (int)gran,
+                                                   eps, Xq, act_scale, workspace,
+                                                   (hipStream_t)stream),
+                  fn);
+}
+
 static bl_status check_forward_common(const char *fn, int bits, bl_gran gran,
                                       const uint8_t *W_packed, const float *gamma,
                                       const float *bias, int64_t M, int64_t N, int64_t K,

@@ -240,6 +240,58 @@ aq_prepare_f6(const uint8_t *__restrict__ xq, int64_t M, int64_t K, int64_t mb_p
     }
 }
 
+// Rotated activations: each row times the block-diagonal Hadamard matrix (in LDS, in
+// fp32, the fixed stage order of lds_hadamard), then the absmax quantization above.
+// kPass 0: per token; 1: per tensor, first pass (the rotated rows' absmax into
+// *tensor_amax, nothing stored); 2: per tensor, second pass (codes with that absmax).
+template <bool kBf16, int kBits, int kPass>
+__global__ void __launch_bounds__(kAqThreads)
+aq_rows_rot(const void *__restrict__ x, int64_t K, int b, float eps, uint32_t *__restrict__ tensor_amax,
+            void *__restrict__ xq, float *__restrict__ scale) {
+    extern __shared__ __attribute__((aligned(16))) float rowl[];
+    __shared__ float red[kAqThreads / kWave];
+    const int64_t m = blockIdx.x;
+    const void *row = kBf16 ? (const void *)(static_cast<const uint16_t *>(x) + m * K)
+                            : (const void *)(static_cast<const float *>(x) + m * K);
+    const int k8 = (int)(K / 8);
+    for (int u = threadIdx.x; u < k8; u += kAqThreads) {
+        float v[8];
+        load8<kBf16>(row, (int64_t)u * 8, v);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) rowl[8 * u + j] = v[j];
+    }
+    lds_hadamard(rowl, (int)K, b, threadIdx.x, kAqThreads);
+    float amax;
+    if (kPass == 2) {
+        amax = __uint_as_float(*tensor_amax);
+    } else {
+        float mx = 0.0f;
+        for (int k = threadIdx.x; k < K; k += kAqThreads) mx = fmaxf(mx, fabsf(rowl[k]));
+        amax = block_max(mx, red);
+        if (kPass == 1) {
+            if (threadIdx.x == 0) atomicMax(tensor_amax, __float_as_uint(amax));
+            return;
+        }
+    }
+    const float a = fmaxf(amax, eps);
+    const float s = kBits == 8 ? 127.0f / a : a / 7.0f;
+    if (threadIdx.x == 0 && (kPass == 0 || m == 0)) scale[kPass == 0 ? m : 0] = s;
+    for (int u = threadIdx.x; u < k8; u += kAqThreads) {
+        const float *v = rowl + 8 * u;
+        if (kBits == 8) {
+            uint2 o;
+            o.x = q8(v[0], s) | (q8(v[1], s) << 8) | (q8(v[2], s) << 16) | (q8(v[3], s) << 24);
+            o.y = q8(v[4], s) | (q8(v[5], s) << 8) | (q8(v[6], s) << 16) | (q8(v[7], s) << 24);
+            reinterpret_cast<uint2 *>(static_cast<int8_t *>(xq) + m * K)[u] = o;
+        } else {
+            uint32_t o = 0;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) o |= q4(v[j], s) << (4 * j);
+            reinterpret_cast<uint32_t *>(static_cast<uint8_t *>(xq) + m * (K / 2))[u] = o;
+        }
+    }
+}
+
 template <bool kBf16>
 __global__ void __launch_bounds__(kAqThreads)
 aq_tensor_amax(const void *__restrict__ x, int64_t n8, uint32_t *__restrict__ amax_bits) {
@@ -350,6 +402,43 @@ hipError_t launch_prepare_acts_f6(const void *xq, int64_t M, int64_t K, uint8_t 
     hipLaunchKernelGGL(aq_prepare_f6<kKbPerWave>, grid, dim3(kAqThreads), 0, s,
                        static_cast<const uint8_t *>(xq), M, K, mb_pad, xp, rowsum);
     return hipGetLastError();
+}
+
+namespace {
+template <bool kBf16, int kBits>
+hipError_t launch_rot(const void *x, int64_t M, int64_t K, int gran, float eps, void *xq,
+                      float *scale, uint32_t *amax, hipStream_t s) {
+    const int b = hadamard_block(K);
+    const size_t lds = (size_t)K * sizeof(float);
+    if (lds > 48 * 1024) {
+        for (const void *fn : {(const void *)aq_rows_rot<kBf16, kBits, 0>,
+                               (const void *)aq_rows_rot<kBf16, kBits, 1>,
+                               (const void *)aq_rows_rot<kBf16, kBits, 2>}) {
+            const hipError_t e = allow_lds(fn, lds);
+            if (e != hipSuccess) return e;
+        }
+    }
+    const dim3 grid((unsigned)M), block(kAqThreads);
+    if (gran == 0) {
+        hipLaunchKernelGGL((aq_rows_rot<kBf16, kBits, 0>), grid, block, lds, s, x, K, b, eps, amax, xq, scale);
+    } else {
+        hipError_t e = launch_zero_u32(amax, 1, s);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((aq_rows_rot<kBf16, kBits, 1>), grid, block, lds, s, x, K, b, eps, amax, xq, scale);
+        hipLaunchKernelGGL((aq_rows_rot<kBf16, kBits, 2>), grid, block, lds, s, x, K, b, eps, amax, xq, scale);
+    }
+    return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_quantize_acts_rotated(const void *x, int x_bf16, int64_t M, int64_t K, int bits,
+                                        int gran, float eps, void *xq, float *scale, void *ws,
+                                        hipStream_t s) {
+    uint32_t *amax = static_cast<uint32_t *>(ws);
+    if (x_bf16) return bits == 8 ? launch_rot<true, 8>(x, M, K, gran, eps, xq, scale, amax, s)
+                                 : launch_rot<true, 4>(x, M, K, gran, eps, xq, scale, amax, s);
+    return bits == 8 ? launch_rot<false, 8>(x, M, K, gran, eps, xq, scale, amax, s)
+                     : launch_rot<false, 4>(x, M, K, gran, eps, xq, scale, amax, s);
 }
 
 hipError_t launch_quantize_acts(const void *x, int x_bf16, int64_t M, int64_t K, int bits,

@@ -132,6 +132,54 @@ __device__ __forceinline__ uint32_t q4(float x, float s) {
     return (uint32_t)((int)v) & 0xFu;
 }
 
+// ---------------------------------------------------------------- Hadamard rotation
+// "BitNet a4.8 Guide", "Best Practices for Deploying BitNet a4.8 in Production",
+// Outlier Suppression row: a Hadamard rotation (as in QuaRot) before the 4-bit
+// activation quantization.  Block-diagonal Sylvester blocks of size b on the K axis,
+// b = the largest power of two dividing K, at most 8192; unnormalized (+-1 entries).
+constexpr int kHadamardMaxBlock = 8192;
+__host__ __device__ inline int hadamard_block(int64_t K) {
+    int b = 1;
+    while (b < kHadamardMaxBlock && K % (2 * b) == 0) b *= 2;
+    return b;
+}
+
+// In place on a row of K fp32 values in LDS, by the whole block: stages h = 1, 2, 4,
+// ..., b/2, each pair (i, i + h) with (i & h) == 0 becoming (u + v, u - v).  Two
+// stages go per LDS round trip (the four values i, i+h, i+2h, i+3h: stage h on the
+// pairs (0,1) and (2,3), then stage 2h on (0,2) and (1,3)), a last odd stage alone.
+// Every value goes through the same additions in the same order as the stage-by-stage
+// definition, so the result is that definition's to the bit.  Barriers inside: every
+// thread of the block must call it; it ends with a barrier.
+__device__ inline void lds_hadamard(float *row, int K, int b, int tid, int nthreads) {
+    __syncthreads();
+    int h = 1;
+    for (; 4 * h <= b; h *= 4) {
+        const int quads = K / 4;
+#pragma unroll 2
+        for (int q = tid; q < quads; q += nthreads) {
+            // quad q: i = ((q / h) * 4h) + (q % h); members i, i + h, i + 2h, i + 3h
+            const int i = (q / h) * (4 * h) + (q % h);
+            const float x0 = row[i], x1 = row[i + h], x2 = row[i + 2 * h], x3 = row[i + 3 * h];
+            const float y0 = x0 + x1, y1 = x0 - x1, y2 = x2 + x3, y3 = x2 - x3;
+            row[i] = y0 + y2;
+            row[i + 2 * h] = y0 - y2;
+            row[i + h] = y1 + y3;
+            row[i + 3 * h] = y1 - y3;
+        }
+        __syncthreads();
+    }
+    if (h < b) {  // one stage left: h = b / 2
+        for (int q = tid; q < K / 2; q += nthreads) {
+            const int i = (q / h) * (2 * h) + (q % h);
+            const float u = row[i], v = row[i + h];
+            row[i] = u + v;
+            row[i + h] = u - v;
+        }
+        __syncthreads();
+    }
+}
+
 }  // namespace bl
 
 // ---------------------------------------------------------------- launchers
@@ -170,6 +218,14 @@ size_t ws_quantize_acts(int gran);
 hipError_t launch_quantize_acts_prepared(const void *x, int x_bf16, int64_t M, int64_t K,
                                          int bits, int gran, float eps, uint8_t *xp,
                                          float *scale, int32_t *rowsum, void *ws, hipStream_t s);
+// the same with the Hadamard rotation of each row first (K <= kRotMaxK)
+constexpr int64_t kRotMaxK = 16384;
+hipError_t launch_quantize_acts_rotated(const void *x, int x_bf16, int64_t M, int64_t K, int bits,
+                                        int gran, float eps, void *xq, float *scale, void *ws,
+                                        hipStream_t s);
+hipError_t launch_quantize_weights_rotated(const void *w, int w_bf16, int64_t N, int64_t K,
+                                           float eps, uint8_t *packed, float *gamma, void *ws,
+                                           hipStream_t s);
 // residual add and RMS norm of bf16 rows (glue between BitLinear layers)
 hipError_t launch_rmsnorm(void *x, const void *delta, void *h, int64_t M, int64_t K, float eps,
                           hipStream_t s);

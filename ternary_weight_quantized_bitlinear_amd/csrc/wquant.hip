@@ -29,6 +29,8 @@
 // is exact in fp64, and T is the smallest fp32 strictly above it: |w| >= T is then
 // the same test for every fp32 w.  No per-element division is needed; codes above
 // 1.5 clip to 1, which the test gives as well.
+#include <algorithm>
+
 #include "common.hpp"
 
 namespace bl {
@@ -135,8 +137,10 @@ __device__ __forceinline__ uint32_t bit_at(const uint32_t (&s)[kLimbs], int i) {
 }
 
 // one wave: gamma and the threshold from the finished exponent sums
+// gamma_out = gamma * 2^-shift (the rotated quantizer's 1/b); the threshold uses gamma
 __global__ void __launch_bounds__(kWave) wq_finalize(WqWorkspace *__restrict__ ws, uint64_t count,
-                                                     float eps, float *__restrict__ gamma_out) {
+                                                     float eps, float *__restrict__ gamma_out,
+                                                     int shift) {
     const int lane = threadIdx.x;
     // sum_e bins[e] * 2^(max(e,1)-1), in units of 2^-149: lane l adds bins 4l .. 4l+3
     unsigned long long t[kLimbs];
@@ -205,7 +209,7 @@ __global__ void __launch_bounds__(kWave) wq_finalize(WqWorkspace *__restrict__ w
     }
     if (lane == 0) {
         ws->thr = thr;
-        *gamma_out = g;
+        *gamma_out = nonfinite ? g : ldexpf(g, -shift);
     }
 }
 
@@ -331,6 +335,77 @@ __global__ void __launch_bounds__(256) wq_pack_bf16(const uint4 *__restrict__ w,
     }
 }
 
+// ---- rotated weights: each row times the block-diagonal Hadamard matrix (in LDS, the
+// fixed stage order of lds_hadamard) before the exact sum and before the packing; the
+// rotated rows are recomputed in the second pass rather than stored.
+template <bool kBf16>
+__device__ __forceinline__ void load_row_lds(const void *w, int64_t r, int K, float *rowl) {
+    const void *row = kBf16 ? (const void *)(static_cast<const uint16_t *>(w) + r * K)
+                            : (const void *)(static_cast<const float *>(w) + r * K);
+    for (int u = threadIdx.x; u < K / 8; u += kBinThreads) {
+        float v[8];
+        load8<kBf16>(row, (int64_t)u * 8, v);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) rowl[8 * u + j] = v[j];
+    }
+}
+
+template <bool kBf16>
+__global__ void __launch_bounds__(kBinThreads) wq_bins_rot(const void *__restrict__ w, int64_t N,
+                                                           int K, int b, WqWorkspace *__restrict__ ws) {
+    extern __shared__ __attribute__((aligned(16))) float rowl[];
+    __shared__ unsigned long long sb[kBinWaves][256];
+    for (int i = threadIdx.x; i < kBinWaves * 256; i += kBinThreads) (&sb[0][0])[i] = 0ull;
+    unsigned long long *wb = sb[threadIdx.x / kWave];
+    int e_lo = -1;
+    for (int64_t r = blockIdx.x; r < N; r += gridDim.x) {
+        load_row_lds<kBf16>(w, r, K, rowl);
+        lds_hadamard(rowl, K, b, threadIdx.x, kBinThreads);
+        if (e_lo < 0) {  // the window: from the wave's values of its first row
+            uint32_t emax = 0;
+            for (int k = threadIdx.x; k < K; k += kBinThreads) {
+                uint32_t e, m;
+                split_abs(rowl[k], e, m);
+                emax = e > emax && e < 255u ? e : emax;
+            }
+            emax = __float_as_uint(wave_max_abs(__uint_as_float(emax)));
+            e_lo = min(max((int)emax + 4 - kWindow, 1), 190);
+        }
+        // at most K / 256 + 1 <= 65 terms per lane and row below 2^48: no overflow
+        unsigned long long acc = 0;
+        for (int k = threadIdx.x; k < K; k += kBinThreads)
+            if (add_fast(acc, e_lo, rowl[k])) add_slow(wb, rowl[k]);
+        flush(wb, acc, e_lo);
+        __syncthreads();  // the row buffer is reloaded next
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < 256; e += kBinThreads) {
+        unsigned long long t = 0;
+#pragma unroll
+        for (int j = 0; j < kBinWaves; ++j) t += sb[j][e];
+        if (t) atomicAdd(&ws->bins[e], t);
+    }
+}
+
+template <bool kBf16>
+__global__ void __launch_bounds__(kBinThreads) wq_pack_rot(const void *__restrict__ w, int64_t N,
+                                                           int K, int b,
+                                                           const WqWorkspace *__restrict__ ws,
+                                                           uint8_t *__restrict__ out) {
+    extern __shared__ __attribute__((aligned(16))) float rowl[];
+    const float thr = ws->thr;
+    for (int64_t r = blockIdx.x; r < N; r += gridDim.x) {
+        load_row_lds<kBf16>(w, r, K, rowl);
+        lds_hadamard(rowl, K, b, threadIdx.x, kBinThreads);
+        for (int j = threadIdx.x; j < K / 4; j += kBinThreads) {
+            const float *v = rowl + 4 * j;
+            out[r * (K / 4) + j] = (uint8_t)(field_of(v[0], thr) | (field_of(v[1], thr) << 2) |
+                                             (field_of(v[2], thr) << 4) | (field_of(v[3], thr) << 6));
+        }
+        __syncthreads();  // the row buffer is reloaded next
+    }
+}
+
 int grid_for(int64_t items, int threads, int cap) {
     int64_t g = (items + threads - 1) / threads;
     if (g > cap) g = cap;
@@ -355,7 +430,7 @@ hipError_t launch_quantize_weights(const void *w, int w_bf16, int64_t N, int64_t
         hipLaunchKernelGGL(wq_bins<true>, dim3(nb), dim3(kBinThreads), 0, s, w, nvec, ws);
     else
         hipLaunchKernelGGL(wq_bins<false>, dim3(nb), dim3(kBinThreads), 0, s, w, nvec, ws);
-    hipLaunchKernelGGL(wq_finalize, dim3(1), dim3(kWave), 0, s, ws, (uint64_t)count, eps, gamma);
+    hipLaunchKernelGGL(wq_finalize, dim3(1), dim3(kWave), 0, s, ws, (uint64_t)count, eps, gamma, 0);
     const int np = grid_for(nvec, 256, 1 << 20);
     if (w_bf16)
         hipLaunchKernelGGL(wq_pack_bf16, dim3(np), dim3(256), 0, s,
@@ -364,6 +439,34 @@ hipError_t launch_quantize_weights(const void *w, int w_bf16, int64_t N, int64_t
     else
         hipLaunchKernelGGL(wq_pack_f32, dim3(np), dim3(256), 0, s,
                            static_cast<const uint4 *>(w), nvec, ws, packed);
+    return hipGetLastError();
+}
+
+
+hipError_t launch_quantize_weights_rotated(const void *w, int w_bf16, int64_t N, int64_t K,
+                                           float eps, uint8_t *packed, float *gamma, void *ws_,
+                                           hipStream_t s) {
+    WqWorkspace *ws = static_cast<WqWorkspace *>(ws_);
+    const int b = hadamard_block(K);
+    int shift = 0;
+    while ((1 << shift) < b) ++shift;
+    const size_t lds = (size_t)K * sizeof(float);
+    if (lds > 48 * 1024) {
+        for (const void *fn : {(const void *)wq_bins_rot<true>, (const void *)wq_bins_rot<false>,
+                               (const void *)wq_pack_rot<true>, (const void *)wq_pack_rot<false>}) {
+            const hipError_t e = allow_lds(fn, lds);
+            if (e != hipSuccess) return e;
+        }
+    }
+    hipLaunchKernelGGL(wq_zero, dim3(1), dim3(256), 0, s, ws);
+    // rows per block: a few blocks per CU, so that few blocks add to the global bins
+    const unsigned nb = (unsigned)std::min<int64_t>(N, 1024);
+    if (w_bf16) hipLaunchKernelGGL(wq_bins_rot<true>, dim3(nb), dim3(kBinThreads), lds, s, w, N, (int)K, b, ws);
+    else hipLaunchKernelGGL(wq_bins_rot<false>, dim3(nb), dim3(kBinThreads), lds, s, w, N, (int)K, b, ws);
+    hipLaunchKernelGGL(wq_finalize, dim3(1), dim3(kWave), 0, s, ws, (uint64_t)(N * K), eps, gamma, shift);
+    const unsigned np = (unsigned)std::min<int64_t>(N, 4096);
+    if (w_bf16) hipLaunchKernelGGL(wq_pack_rot<true>, dim3(np), dim3(kBinThreads), lds, s, w, N, (int)K, b, ws, packed);
+    else hipLaunchKernelGGL(wq_pack_rot<false>, dim3(np), dim3(kBinThreads), lds, s, w, N, (int)K, b, ws, packed);
     return hipGetLastError();
 }
 

@@ -25,7 +25,8 @@ def test_exports_every_header_function(L):
         "bitlinear_quantize_weights", "bitlinear_quantize_acts", "bitlinear_forward",
         "bitlinear_forward_fused", "bitlinear_forward_fused_batched", "bitlinear_rmsnorm",
         "bitlinear_rmsnorm_quantize", "bitlinear_workspace_size", "bitlinear_status_string",
-        "bitlinear_last_error", "bitlinear_version"}
+        "bitlinear_last_error", "bitlinear_version", "bitlinear_hadamard_block",
+        "bitlinear_quantize_weights_rotated", "bitlinear_quantize_acts_rotated"}
     for n in names:
         assert hasattr(L, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", bl.LIB_PATH], capture_output=True,
@@ -114,6 +115,26 @@ def test_quantize_acts_rejects(L):
     assert f(P(A), 0, 8, 256, 8, 1, 1e-5, P(A), P(A), None, 0, None) == bl.BL_EWORKSPACE
     assert f(P(A), 0, 8, 24, 8, 0, 1e-5, P(A), P(A), None, 0, None) == bl.BL_ESHAPE
     assert f(P(A), 0, 8, 256, 8, 0, -1.0, P(A), P(A), None, 0, None) == bl.BL_EINVAL
+
+
+def test_hadamard_block_host(L):
+    # the largest power of two dividing K, at most 8192 (no device needed)
+    for K, b in ((4, 4), (48, 16), (2560, 512), (6912, 256), (8192, 8192), (16384, 8192)):
+        assert L.bitlinear_hadamard_block(K) == b
+
+
+def test_rotated_quantizers_reject(L):
+    fw = L.bitlinear_quantize_weights_rotated
+    assert fw(P(A), 0, 512, 256, 1e-5, P(A), P(A), None, 0, None) == bl.BL_EWORKSPACE
+    assert fw(P(A), 0, 512, 250, 1e-5, P(A), P(A), P(A), 1 << 20, None) == bl.BL_ESHAPE
+    assert fw(P(A), 0, 4, 32768, 1e-5, P(A), P(A), P(A), 1 << 20, None) == bl.BL_EUNSUPPORTED
+    assert fw(P(A), 2, 512, 256, 1e-5, P(A), P(A), P(A), 1 << 20, None) == bl.BL_EINVAL
+    fa = L.bitlinear_quantize_acts_rotated
+    assert fa(P(A), 0, 8, 256, 3, 0, 1e-5, P(A), P(A), None, 0, None) == bl.BL_EINVAL
+    assert fa(P(A), 0, 8, 256, 8, 1, 1e-5, P(A), P(A), None, 0, None) == bl.BL_EWORKSPACE
+    assert fa(P(A), 0, 8, 32768, 4, 0, 1e-5, P(A), P(A), None, 0, None) == bl.BL_EUNSUPPORTED
+    assert fa(P(A), 0, 8, 24, 8, 0, 1e-5, P(A), P(A), None, 0, None) == bl.BL_ESHAPE
+    assert L.bitlinear_last_error().decode().startswith("bitlinear_quantize_acts_rotated")
 
 
 def test_forward_fused_rejects(L):
