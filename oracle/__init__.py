@@ -19,6 +19,10 @@ source header):
 * :func:`forward`, :func:`forward_at` -- integer contraction, rescale
   ([b158] eq. 3; [a48] dataflow figure), bias, ReLU^2 ([2b4t] "2. Squared
   ReLU Activation").
+* :func:`backward` -- the layer's gradients under the straight-through estimators:
+  int8 per [b158] "Implementation" Step 1-2 listings (identity STE, y = linear(q, c)
+  * gamma/s), int4 per [a48] "Implementation" Step 2-3 listings (masked STE, y =
+  linear(q s, c gamma)); fp64 sums of the fp32 operands the listings materialize.
 * :func:`hadamard_block`, :func:`hadamard_rows`, :func:`quantize_acts_rotated`,
   :func:`quantize_weights_rotated` -- the Hadamard rotation folded into both
   operands before the 4-bit activation quantization ([a48] "Best Practices for
@@ -84,9 +88,11 @@ def _load():
         lib.oracle_hadamard_rows.argtypes = [P, I, I64, I64, P]
         lib.oracle_quantize_acts_rotated.argtypes = [P, I, I64, I64, I, I, F, P, P]
         lib.oracle_quantize_weights_rotated.argtypes = [P, I, I64, I64, F, P, P, P]
+        lib.oracle_backward.argtypes = [P, P, I, P, I, P, P, P, I, P, I, I64, I64, I64, P, P, P]
         for name in ("oracle_gamma", "oracle_quantize_weights", "oracle_quantize_acts",
                      "oracle_forward", "oracle_forward_at", "oracle_hadamard_rows",
-                     "oracle_quantize_acts_rotated", "oracle_quantize_weights_rotated"):
+                     "oracle_quantize_acts_rotated", "oracle_quantize_weights_rotated",
+                     "oracle_backward"):
             getattr(lib, name).restype = I
         lib.oracle_to_bf16.restype = None
         _lib = lib
@@ -252,3 +258,30 @@ def quantize_weights_rotated(W: np.ndarray, eps: float = 1e-5):
                                                    _ptr(packed), _ptr(g), _ptr(codes)),
            "oracle_quantize_weights_rotated")
     return packed, g[0], codes
+
+
+def backward(dY: np.ndarray, Xq: np.ndarray, bits: int, act_scale, gran: int, packed: np.ndarray,
+             gamma_, X=None, W=None, want=("dX", "dW", "dbias")):
+    """dY uint16 bf16 bits [M, N]; Xq, act_scale, packed, gamma as the forward takes them;
+    X, W (float32 or bf16 bits) only for the int4 masks.  Returns a dict of float64 arrays."""
+    dY = np.ascontiguousarray(dY, dtype=np.uint16)
+    Xq = np.ascontiguousarray(Xq)
+    act_scale = np.ascontiguousarray(act_scale, dtype=np.float32)
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    g = np.array([gamma_], np.float32)
+    M, N = dY.shape
+    K = packed.shape[1] * 4
+    out = {}
+    dX = np.zeros((M, K), np.float64) if "dX" in want else None
+    dW = np.zeros((N, K), np.float64) if "dW" in want else None
+    db = np.zeros(N, np.float64) if "dbias" in want else None
+    X = None if X is None else np.ascontiguousarray(X)
+    W = None if W is None else np.ascontiguousarray(W)
+    _check(_load().oracle_backward(_ptr(dY), _ptr(Xq), bits, _ptr(act_scale), gran, _ptr(packed),
+                                   _ptr(g), _ptr(X), 0 if X is None else _dtype_code(X),
+                                   _ptr(W), 0 if W is None else _dtype_code(W), M, N, K,
+                                   _ptr(dX), _ptr(dW), _ptr(db)), "oracle_backward")
+    for name, a in (("dX", dX), ("dW", dW), ("dbias", db)):
+        if a is not None:
+            out[name] = a
+    return out

@@ -48,6 +48,9 @@
  *     block-diagonal Sylvester blocks of b = the largest power of two dividing K
  *     (at most 8192), unnormalized, an fp32 fast transform in a fixed stage
  *     order, folded into both operands, 1/b into gamma (see the section below).
+ *   - the backward (quantization-aware training): each page's straight-through
+ *     estimator for its own activation width, b1.58's identity for int8 and
+ *     a4.8's masked one for int4 (see the last section).
  */
 #include <stdint.h>
 #include <stdlib.h>
@@ -493,5 +496,92 @@ int oracle_quantize_weights_rotated(const void *W, int w_dtype, int64_t N, int64
     int t = 0; /* b = 2^t */
     for (int64_t b = oracle_hadamard_block(K); b > 1; b /= 2) ++t;
     *gamma_out = ldexpf(g, -t);
+    return OR_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* backward under the straight-through estimator (quantization-aware training) */
+/* ------------------------------------------------------------------------ */
+/*
+ * The gradients of the layer's loss with respect to its full-precision input X and
+ * master weights W, given dY = dL/dY ([M][N], bf16), through the quantizers' straight-
+ * through estimators, each page's own formulation for its activation width:
+ *
+ * bits = 8: "BitNet b1.58: The 1-Bit Ternary LLM Architecture Guide", "Implementation",
+ *   Step 1 listing: the quantizers return (codes, scale) and their backward passes the
+ *   codes' gradient through unchanged (and none to the scales); Step 2: y = linear(q, c)
+ *   * (gamma / s) + bias.  With z = linear(q, c) and f[m] = fl32(gamma / s[m]):
+ *     dz[m][n] = fl32(dY[m][n] * f[m])
+ *     dX[m][k] = sum_n dz[m][n] c[n][k]          dW[n][k] = sum_m dz[m][n] q[m][k]
+ * bits = 4: "BitNet a4.8 Guide", "Implementation", Step 2 listing (the quantizers'
+ *   backward: weight gradient zeroed where |w| > 1.5, activation gradient zeroed where
+ *   x / s < -8 or > 7) and Step 3 (y = linear(q * s, c * gamma) + bias, the learnable
+ *   scale factor at its initial value 1):
+ *     dX[m][k] = mask_x * sum_n dY[m][n] (c[n][k] gamma),   mask_x = !(v < -8 || v > 7),
+ *                v = fl32(x[m][k] / s[m])   (no mask when X is NULL)
+ *     dW[n][k] = mask_w * sum_m dY[m][n] fl32(q[m][k] * s[m]),  mask_w = !(|w[n][k]| > 1.5)
+ *                (no mask when W is NULL)
+ * both: dbias[n] = sum_m dY[m][n].
+ * Operands are the fp32 values the listings materialize; products and sums in fp64.
+ * s[m] = act_scale[m], or act_scale[0] for a per-tensor scale.
+ */
+static double bwd_dz(const uint16_t *dY, int bits, const float *act_scale, int gran, float gamma,
+                     int64_t N, int64_t m, int64_t n)
+{
+    const float dy = widen_bf16(dY[m * N + n]);
+    if (bits == 4) return (double)dy;
+    const float f = gamma / act_scale[gran == 0 ? m : 0];
+    return (double)(dy * f);
+}
+
+int oracle_backward(const uint16_t *dY, const void *Xq, int bits, const float *act_scale,
+                    int gran, const uint8_t *packed, const float *gamma, const void *X,
+                    int x_dtype, const void *W, int w_dtype, int64_t M, int64_t N, int64_t K,
+                    double *dX, double *dW, double *dbias)
+{
+    if (!dY || !Xq || !act_scale || !packed || !gamma || M <= 0 || N <= 0 || K <= 0 || K % 4)
+        return OR_EINVAL;
+    if ((bits != 8 && bits != 4) || (gran != 0 && gran != 1)) return OR_EINVAL;
+    const float g = *gamma;
+    if (dX) {
+        for (int64_t m = 0; m < M; ++m) {
+            const float s = act_scale[gran == 0 ? m : 0];
+            for (int64_t k = 0; k < K; ++k) {
+                double acc = 0.0;
+                for (int64_t n = 0; n < N; ++n) {
+                    const double wq = bits == 4 ? (double)((float)weight_code(packed, K, n, k) * g)
+                                                : (double)weight_code(packed, K, n, k);
+                    acc += bwd_dz(dY, bits, act_scale, gran, g, N, m, n) * wq;
+                }
+                if (bits == 4 && X) {
+                    const float v = load_elem(X, x_dtype, m * K + k) / s;
+                    if (v < -8.0f || v > 7.0f) acc = 0.0;
+                }
+                dX[m * K + k] = acc;
+            }
+        }
+    }
+    if (dW) {
+        for (int64_t n = 0; n < N; ++n) {
+            for (int64_t k = 0; k < K; ++k) {
+                double acc = 0.0;
+                for (int64_t m = 0; m < M; ++m) {
+                    const float s = act_scale[gran == 0 ? m : 0];
+                    const int q = act_code(Xq, bits, K, m, k);
+                    const double xq = bits == 4 ? (double)((float)q * s) : (double)q;
+                    acc += bwd_dz(dY, bits, act_scale, gran, g, N, m, n) * xq;
+                }
+                if (bits == 4 && W && fabsf(load_elem(W, w_dtype, n * K + k)) > 1.5f) acc = 0.0;
+                dW[n * K + k] = acc;
+            }
+        }
+    }
+    if (dbias) {
+        for (int64_t n = 0; n < N; ++n) {
+            double acc = 0.0;
+            for (int64_t m = 0; m < M; ++m) acc += (double)widen_bf16(dY[m * N + n]);
+            dbias[n] = acc;
+        }
+    }
     return OR_OK;
 }

@@ -740,3 +740,156 @@ def test_rotation_spreads_an_outlier():
     R = oracle.hadamard_rows(X)
     ratio = lambda A: (np.abs(A).max(axis=1) / np.sqrt((A.astype(np.float64) ** 2).mean(axis=1)))
     assert (ratio(X) > 15).all() and (ratio(R) < 5).all()
+
+
+# ---------------------------------------------------------------- backward (STE)
+# int8: "BitNet b1.58 ...", "Implementation" Step 1-2 listings; int4: "BitNet a4.8
+# Guide", "Implementation" Step 2-3 listings.  The pin: float64 autograd through each
+# listing's own forward, with straight-through functions carrying the listing's masks,
+# so that the chain rule (which operand, which transpose, where the scales go) comes
+# from the library, not from the oracle's formulas.
+
+def _bwd_case(M, N, K, bits, gran=oracle.PER_TOKEN, seed=0, bias=True):
+    rng = np.random.default_rng([seed, M, N, K, bits])
+    W = (0.02 * rng.standard_normal((N, K))).astype(np.float32)
+    W[0, 0] = 2.0   # masked by the int4 weight STE (|w| > 1.5)
+    W[0, 1] = -1.5  # not masked (the test is strict)
+    X = rng.standard_normal((M, K)).astype(np.float32)
+    packed, g, codes = oracle.quantize_weights(W)
+    xq, s = oracle.quantize_acts(X, bits=bits, gran=gran)
+    dY = workloads.to_bf16_bits(rng.standard_normal((M, N)).astype(np.float32))
+    return W, X, packed, g, codes, xq, s, dY
+
+
+def _autograd_ref(W, X, codes, g, xq, s, dY, bits, gran, K):
+    torch64 = torch.float64
+    q = (xq.astype(np.int64) if bits == 8 else _unpack_nibbles(xq, K)).astype(np.float64)
+    c = codes.astype(np.float64)
+    sv = np.asarray(s, np.float32)
+    srow = sv if gran == oracle.PER_TOKEN else np.full(X.shape[0], sv[0], np.float32)
+    x = torch.tensor(X.astype(np.float64), requires_grad=True)
+    w = torch.tensor(W.astype(np.float64), requires_grad=True)
+    bias = torch.zeros(W.shape[0], dtype=torch64, requires_grad=True)
+    dy = torch.tensor(workloads.bf16_bits_to_f32(dY).astype(np.float64))
+
+    class Pass(torch.autograd.Function):  # forward: the given value; backward: identity
+        @staticmethod
+        def forward(ctx, inp, val):
+            return val
+
+        @staticmethod
+        def backward(ctx, grad):
+            return grad, None
+
+    class MaskedAct(torch.autograd.Function):  # [a48] ActivationA4Quantizer
+        @staticmethod
+        def forward(ctx, inp, val, scale32):
+            ctx.save_for_backward(inp, scale32)
+            return val
+
+        @staticmethod
+        def backward(ctx, grad):
+            inp, scale32 = ctx.saved_tensors
+            norm = torch.from_numpy((inp.detach().numpy().astype(np.float32) /
+                                     scale32.numpy()[:, None]).astype(np.float32))
+            grad = grad.clone()
+            grad[(norm < -8.0) | (norm > 7.0)] = 0.0
+            return grad, None, None
+
+    class MaskedW(torch.autograd.Function):  # [a48] WeightTernaryQuantizer
+        @staticmethod
+        def forward(ctx, inp, val):
+            ctx.save_for_backward(inp)
+            return val
+
+        @staticmethod
+        def backward(ctx, grad):
+            (inp,) = ctx.saved_tensors
+            grad = grad.clone()
+            grad[inp.abs() > 1.5] = 0.0
+            return grad, None
+
+    if bits == 8:  # y = linear(q, c) * (gamma / s) + bias, f in fp32 as the listing has it
+        f = (np.float32(g) / srow).astype(np.float32).astype(np.float64)
+        y = torch.nn.functional.linear(Pass.apply(x, torch.tensor(q)), Pass.apply(w, torch.tensor(c)))
+        y = y * torch.tensor(f)[:, None] + bias
+    else:  # y = linear(q s, c gamma) + bias, the dequantized operands in fp32
+        xdq = (q.astype(np.float32) * srow[:, None]).astype(np.float32).astype(np.float64)
+        wdq = (c.astype(np.float32) * np.float32(g)).astype(np.float64)
+        y = torch.nn.functional.linear(MaskedAct.apply(x, torch.tensor(xdq), torch.tensor(srow)),
+                                       MaskedW.apply(w, torch.tensor(wdq))) + bias
+    (y * dy).sum().backward()
+    return x.grad.numpy(), w.grad.numpy(), bias.grad.numpy()
+
+
+@pytest.mark.parametrize("bits,gran", [(8, oracle.PER_TOKEN), (4, oracle.PER_TOKEN),
+                                       (8, oracle.PER_TENSOR), (4, oracle.PER_TENSOR)])
+def test_backward_matches_autograd(bits, gran):
+    M, N, K = 6, 40, 64
+    W, X, packed, g, codes, xq, s, dY = _bwd_case(M, N, K, bits, gran)
+    got = oracle.backward(dY, xq, bits, s, gran, packed, g, X=X, W=W)
+    rx, rw, rb = _autograd_ref(W, X, codes, g, xq, s, dY, bits, gran, K)
+    # the oracle rounds dz = dY * f to fp32 (int8), as the listing's fp32 graph does;
+    # autograd in float64 does not: within 2^-23 of the sum of |terms|
+    dyf = workloads.bf16_bits_to_f32(dY).astype(np.float64)
+    tx = 2.0 ** -23 * (np.abs(dyf) @ np.abs(codes.astype(np.float64))) * (10.0 if bits == 8 else g)
+    np.testing.assert_allclose(got["dX"], rx, rtol=0, atol=float(tx.max()) + 1e-300)
+    q = (xq.astype(np.int64) if bits == 8 else _unpack_nibbles(xq, K)).astype(np.float64)
+    srow = np.broadcast_to(np.asarray(s, np.float64), (M,)) if len(s) == 1 else s.astype(np.float64)
+    fm = (np.float64(g) / srow) if bits == 8 else srow  # per-token factor of the dW terms
+    tw = 2.0 ** -23 * ((np.abs(dyf) * fm[:, None]).T @ np.abs(q)) * 1.01
+    np.testing.assert_allclose(got["dW"], rw, rtol=0, atol=float(tw.max()) + 1e-300)
+    assert (np.abs(got["dW"] - rw) <= tw + 1e-300).all()
+    np.testing.assert_array_equal(got["dbias"], rb)
+    if bits == 4:  # the listing's weight mask: |w| = 2 masked, |w| = 1.5 not
+        assert got["dW"][0, 0] == 0.0 and got["dW"][0, 1] != 0.0
+
+
+def test_backward_one_hot_closed_form():
+    M, N, K = 4, 8, 32
+    for bits in (8, 4):
+        W, X, packed, g, codes, xq, s, _ = _bwd_case(M, N, K, bits, seed=3)
+        m0, n0 = 2, 5
+        dY = np.zeros((M, N), np.uint16)
+        dY[m0, n0] = workloads.to_bf16_bits(np.array([[1.5]], np.float32))[0, 0]
+        got = oracle.backward(dY, xq, bits, s, oracle.PER_TOKEN, packed, g)
+        q = (xq.astype(np.int64) if bits == 8 else _unpack_nibbles(xq, K)).astype(np.float64)
+        if bits == 8:
+            dz = np.float64(np.float32(1.5) * (np.float32(g) / s[m0]))
+            ex_dx, ex_dw = dz * codes[n0], dz * q[m0]
+        else:
+            ex_dx = 1.5 * codes[n0] * np.float64(g)
+            ex_dw = 1.5 * (q[m0].astype(np.float32) * s[m0]).astype(np.float64)
+        assert (got["dX"][np.arange(M) != m0] == 0).all() and (got["dW"][np.arange(N) != n0] == 0).all()
+        np.testing.assert_array_equal(got["dX"][m0], ex_dx)
+        np.testing.assert_array_equal(got["dW"][n0], ex_dw)
+
+
+def test_backward_int4_activation_mask_edge():
+    # x / s rounds to 7.0000005 for the token's own maximum: the listing zeroes it
+    K = 32
+    X = np.zeros((1, K), np.float32)
+    X[0, 3] = np.float32(9.360724449157715)
+    X[0, 4] = np.float32(1.0)
+    xq, s = oracle.quantize_acts(X, bits=4)
+    assert np.float32(X[0, 3]) / s[0] > np.float32(7.0)
+    W = (0.02 * np.random.default_rng(1).standard_normal((4, K))).astype(np.float32)
+    packed, g, _ = oracle.quantize_weights(W)
+    dY = workloads.to_bf16_bits(np.ones((1, 4), np.float32))
+    got = oracle.backward(dY, xq, 4, s, oracle.PER_TOKEN, packed, g, X=X)
+    free = oracle.backward(dY, xq, 4, s, oracle.PER_TOKEN, packed, g)
+    assert got["dX"][0, 3] == 0.0 and free["dX"][0, 3] != 0.0
+    np.testing.assert_array_equal(np.delete(got["dX"][0], 3), np.delete(free["dX"][0], 3))
+
+
+def test_backward_is_linear_in_dy():
+    M, N, K = 5, 12, 48
+    W, X, packed, g, codes, xq, s, dY1 = _bwd_case(M, N, K, 4, seed=4)
+    dY2 = workloads.to_bf16_bits(np.random.default_rng(5).integers(-4, 5, (M, N)).astype(np.float32))
+    dY1 = workloads.to_bf16_bits(np.random.default_rng(6).integers(-4, 5, (M, N)).astype(np.float32))
+    dYs = workloads.to_bf16_bits(workloads.bf16_bits_to_f32(dY1) + workloads.bf16_bits_to_f32(dY2))
+    a = oracle.backward(dY1, xq, 4, s, 0, packed, g, X=X, W=W)
+    b = oracle.backward(dY2, xq, 4, s, 0, packed, g, X=X, W=W)
+    c = oracle.backward(dYs, xq, 4, s, 0, packed, g, X=X, W=W)
+    for k in ("dX", "dW", "dbias"):
+        np.testing.assert_allclose(c[k], a[k] + b[k], rtol=1e-12, atol=1e-12)

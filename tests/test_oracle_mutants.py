@@ -36,6 +36,11 @@ MUTANTS = [
     ("hadamard_block_uncapped", "while (b < 8192 && K % (2 * b) == 0) b *= 2;", "while (K % (2 * b) == 0) b *= 2;", None),
     ("hadamard_gamma_not_over_b", "*gamma_out = ldexpf(g, -t);", "*gamma_out = g;", None),
     ("hadamard_normalized_by_half", "blk[i + h] = u - v;", "blk[i + h] = 0.5f * (u - v);", None),
+    ("bwd_int4_no_gamma", "(double)((float)weight_code(packed, K, n, k) * g)", "(double)weight_code(packed, K, n, k)", None),
+    ("bwd_weight_mask_inclusive", "fabsf(load_elem(W, w_dtype, n * K + k)) > 1.5f", "fabsf(load_elem(W, w_dtype, n * K + k)) >= 1.5f", None),
+    ("bwd_act_mask_dropped", "if (v < -8.0f || v > 7.0f) acc = 0.0;", "(void)v;", None),
+    ("bwd_int8_scale_inverted", "const float f = gamma / act_scale[gran == 0 ? m : 0];", "const float f = act_scale[gran == 0 ? m : 0] / gamma;", None),
+    ("bwd_int4_dw_codes_not_dequantized", "(double)((float)q * s)", "(double)q", None),
     ("per_tensor_uses_row_max", "float amax = tensor_max;", "float amax = 0.0f; if (gran == 1) { for (int64_t k = 0; k < K; ++k) { float t = fabsf(load_elem(X, x_dtype, m * K + k)); if (t > amax) amax = t; } }", None),
 ]
 
