@@ -77,7 +77,8 @@ typedef enum {
     BL_OP_QUANTIZE_WEIGHTS = 0,
     BL_OP_QUANTIZE_ACTS = 1,
     BL_OP_FORWARD = 2,
-    BL_OP_FORWARD_FUSED = 3
+    BL_OP_FORWARD_FUSED = 3,
+    BL_OP_BACKWARD = 4
 } bl_op;
 
 /*
@@ -248,6 +249,51 @@ bl_status bitlinear_rmsnorm_quantize(void *X, const void *delta, void *H, int64_
                                      float eps, int bits, bl_gran gran, float q_eps, void *Xq,
                                      float *act_scale, void *workspace, size_t workspace_bytes,
                                      void *stream);
+
+/*
+ * Backward pass under the quantizers' straight-through estimators (quantization-aware
+ * training): the gradients of the loss with respect to the layer's full-precision input
+ * X, its latent weights W and its bias, given dY = dL/dY.
+ *
+ * bits = 8 ([b158] "Implementation": the Step 1 quantizers pass the codes' gradient
+ * straight through and none to the scales; Step 2: y = linear(q, c) * gamma / s + bias).
+ * With f[m] = fl32(gamma / s[m]):
+ *   dX[m][k] = f[m] * sum_n dY[m][n] c[n][k]
+ *   dW[n][k] = sum_m dY[m][n] q[m][k] f[m]
+ * bits = 4 ([a48] "Implementation": the Step 2 quantizers zero the weight gradient where
+ * |w| > 1.5 and the activation gradient where x / s falls outside [-8, 7]; Step 3: y =
+ * linear(q s, c gamma) + bias):
+ *   dX[m][k] = mask_x[m][k] * gamma * sum_n dY[m][n] c[n][k]
+ *              mask_x = 0 where fl32(X[m][k] / s[m]) < -8 or > 7 (1 if X is NULL)
+ *   dW[n][k] = mask_w[n][k] * sum_m dY[m][n] fl32(q[m][k] s[m])
+ *              mask_w = 0 where |W[n][k]| > 1.5 (1 if W is NULL)
+ * both: dbias[n] = sum_m dY[m][n].
+ * The contractions run on bf16 matrix cores with exact operands (fp32 products carried as
+ * three bf16 parts) and fp32 accumulation; the results are the exact sums up to fp32
+ * accumulation error (bounded by about (n/16 + 4) * 2^-24 * sum |terms| for a sum of n
+ * terms) and, for 8-bit codes, the rounding of each f[m] product taken in another order.
+ * dbias is summed in fp64 and rounded once.  Summation orders are fixed: repeated calls
+ * give identical results.
+ *
+ * dY        device bf16 [M][N]
+ * Xq, bits, act_scale, gran, W_packed, gamma: the forward's operands, as in
+ *           bitlinear_forward (act_scale is the quantizer's scale: q = x * s for 8 bits,
+ *           x = q * s for 4 bits)
+ * X, x_dtype  4 bits: device [M][K] fp32/bf16 input of the quantizer, for mask_x, or
+ *           NULL; ignored for 8 bits
+ * W, w_dtype  4 bits: device [N][K] fp32/bf16 latent weights, for mask_w, or NULL;
+ *           ignored for 8 bits
+ * dX, dW    device fp32 [M][K], [N][K], each written if not NULL
+ * dbias     device fp32 [N], written if not NULL; at least one of dX, dW, dbias given
+ * workspace device, >= bitlinear_workspace_size(BL_OP_BACKWARD, M, N, K, bits, gran)
+ *           bytes, 256-byte aligned.
+ * M, N, K <= 2^21 (and the general shape rules).
+ */
+bl_status bitlinear_backward(const void *dY, const void *Xq, int bits, const float *act_scale,
+                             bl_gran gran, const uint8_t *W_packed, const float *gamma,
+                             const void *X, bl_dtype x_dtype, const void *W, bl_dtype w_dtype,
+                             int64_t M, int64_t N, int64_t K, float *dX, float *dW, float *dbias,
+                             void *workspace, size_t workspace_bytes, void *stream);
 
 /* Workspace bytes a call needs for these sizes (0 if none).  bits and gran are
  * ignored where they do not matter.  Never fails; returns 0 for invalid sizes. */

@@ -15,6 +15,7 @@ The functions mirror the C entry points:
 * :func:`forward_fused_batched` -> ``bitlinear_forward_fused_batched``
 * :func:`rmsnorm`           -> ``bitlinear_rmsnorm`` (glue between layers)
 * :func:`rmsnorm_quantize`  -> ``bitlinear_rmsnorm_quantize`` (glue + next layer's quantizer)
+* :func:`backward`          -> ``bitlinear_backward`` (straight-through-estimator gradients)
 """
 from __future__ import annotations
 
@@ -31,7 +32,8 @@ BL_OK, BL_EINVAL, BL_ESHAPE, BL_EALIGN, BL_EUNSUPPORTED, BL_EDEVICE, BL_EWORKSPA
 BL_F32, BL_BF16, BL_I32 = 0, 1, 2
 BL_PER_TOKEN, BL_PER_TENSOR = 0, 1
 BL_EPI_NONE, BL_EPI_RELU2 = 0, 1
-BL_OP_QUANTIZE_WEIGHTS, BL_OP_QUANTIZE_ACTS, BL_OP_FORWARD, BL_OP_FORWARD_FUSED = range(4)
+(BL_OP_QUANTIZE_WEIGHTS, BL_OP_QUANTIZE_ACTS, BL_OP_FORWARD, BL_OP_FORWARD_FUSED,
+ BL_OP_BACKWARD) = range(5)
 
 
 class BitLinearError(RuntimeError):
@@ -65,6 +67,8 @@ def lib() -> ctypes.CDLL:
         L.bitlinear_quantize_weights_rotated.argtypes = [P, I, I64, I64, F, P, P, P, SZ, P]
         L.bitlinear_quantize_acts_rotated.argtypes = [P, I, I64, I64, I, I, F, P, P, P, SZ, P]
         L.bitlinear_hadamard_block.argtypes = [I64]
+        L.bitlinear_backward.argtypes = [P, P, I, P, I, P, P, P, I, P, I, I64, I64, I64, P, P, P,
+                                         P, SZ, P]
         L.bitlinear_hadamard_block.restype = I64
         L.bitlinear_workspace_size.argtypes = [I, I64, I64, I64, I, I]
         L.bitlinear_workspace_size.restype = SZ
@@ -76,7 +80,8 @@ def lib() -> ctypes.CDLL:
         for n in ("bitlinear_quantize_weights", "bitlinear_quantize_acts", "bitlinear_forward",
                   "bitlinear_forward_fused", "bitlinear_forward_fused_batched",
                   "bitlinear_rmsnorm", "bitlinear_rmsnorm_quantize",
-                  "bitlinear_quantize_weights_rotated", "bitlinear_quantize_acts_rotated"):
+                  "bitlinear_quantize_weights_rotated", "bitlinear_quantize_acts_rotated",
+                  "bitlinear_backward"):
             getattr(L, n).restype = I
         _lib = L
     return _lib
@@ -312,3 +317,32 @@ def rmsnorm_quantize(X, delta=None, eps: float = 1e-6, bits: int = 8, gran="toke
                                             q_eps, _ptr(Xq), _ptr(sc), _ptr(ws), wsb,
                                             _stream(X.device, stream)))
     return H, Xq, sc
+
+
+def backward(dY, Xq, act_scale, packed, gamma, bits: int = 8, gran="token", X=None, W=None,
+             want=("dX", "dW", "dbias"), workspace=None, stream=None, out=None):
+    """Straight-through-estimator gradients of the layer: dY [M, N] bf16 (the loss's
+    gradient with respect to Y) and the forward's Xq, act_scale, packed, gamma -> dict with
+    the fp32 gradients requested in `want`: "dX" [M, K], "dW" [N, K], "dbias" [N].  X and
+    W (fp32/bf16, 4-bit activations only) switch on the clipping masks.  `out` may hold
+    preallocated tensors under the same keys."""
+    torch = _torch()
+    M, N = dY.shape
+    K = packed.shape[1] * 4
+    g = _gran_code(gran)
+    dev = dY.device
+    shapes = {"dX": (M, K), "dW": (N, K), "dbias": (N,)}
+    res = {}
+    for name in want:
+        if name not in shapes:
+            raise ValueError("unknown gradient %r" % name)
+        t = (out or {}).get(name)
+        res[name] = t if t is not None else torch.empty(shapes[name], dtype=torch.float32,
+                                                        device=dev)
+    ws, wsb = _workspace(workspace_size(BL_OP_BACKWARD, M, N, K, bits, g), dev, workspace)
+    _check(lib().bitlinear_backward(
+        _ptr(dY), _ptr(Xq), bits, _ptr(act_scale), g, _ptr(packed), _ptr(gamma), _ptr(X),
+        BL_F32 if X is None else _dtype_code(X), _ptr(W), BL_F32 if W is None else _dtype_code(W),
+        M, N, K, _ptr(res.get("dX")), _ptr(res.get("dW")), _ptr(res.get("dbias")), _ptr(ws), wsb,
+        _stream(dev, stream)))
+    return res

@@ -23,7 +23,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libbitlinear.so")
 SOURCES = ["api.hip", "wquant.hip", "aquant.hip", "gemv.hip", "gemm.hip", "gemm_big.hip",
-           "gemm_f6f4.hip", "norm.hip"]
+           "gemm_f6f4.hip", "norm.hip", "gemm_bf16.hip", "backward.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -140,6 +140,9 @@ size_t bitlinear_workspace_size(bl_op op, int64_t M, int64_t N, int64_t K, int b
         return (bits == 8 || bits == 4) ? ws_forward(M, N, K, bits, gran) : 0;
     case BL_OP_FORWARD_FUSED:
         return (bits == 8 || bits == 4) ? ws_fused(M, N, K, bits, gran) : 0;
+    case BL_OP_BACKWARD:
+        if (M > bl::kBwdMaxDim || N > bl::kBwdMaxDim || K > bl::kBwdMaxDim) return 0;
+        return (bits == 8 || bits == 4) ? bl::ws_backward(M, N, K, (int)gran) : 0;
     }
     return 0;
 }
@@ -430,6 +433,53 @@ bl_status bitlinear_forward_fused_batched(const void *X, bl_dtype x_dtype, int b
         if (st != BL_OK) return st;
     }
     return ok();
+}
+
+bl_status bitlinear_backward(const void *dY, const void *Xq, int bits, const float *act_scale,
+                             bl_gran gran, const uint8_t *W_packed, const float *gamma,
+                             const void *X, bl_dtype x_dtype, const void *W, bl_dtype w_dtype,
+                             int64_t M, int64_t N, int64_t K, float *dX, float *dW, float *dbias,
+                             void *workspace, size_t workspace_bytes, void *stream) {
+    static const char fn[] = "bitlinear_backward";
+    if (!dY || !Xq || !act_scale || !W_packed || !gamma)
+        return fail(BL_EINVAL, "%s: null pointer", fn);
+    if (!dX && !dW && !dbias) return fail(BL_EINVAL, "%s: no output requested", fn);
+    if (bits != 8 && bits != 4) return fail(BL_EINVAL, "%s: bits must be 8 or 4", fn);
+    if (gran != BL_PER_TOKEN && gran != BL_PER_TENSOR) return fail(BL_EINVAL, "%s: bad gran", fn);
+    const bool use_x = bits == 4 && X, use_w = bits == 4 && W;
+    if ((use_x && !is_xdtype(x_dtype)) || (use_w && !is_xdtype(w_dtype)))
+        return fail(BL_EINVAL, "%s: x_dtype and w_dtype must be BL_F32 or BL_BF16", fn);
+    CHECK(check_shape(M, N, K, fn));
+    if (M > bl::kBwdMaxDim || N > bl::kBwdMaxDim || K > bl::kBwdMaxDim)
+        return fail(BL_ESHAPE, "%s: M, N, K must be at most %lld", fn, (long long)bl::kBwdMaxDim);
+    if (!aligned(dY, 16) || !aligned(Xq, 16) || !aligned(W_packed, 16) || (dX && !aligned(dX, 16)) ||
+        (dW && !aligned(dW, 16)) || (use_x && !aligned(X, 16)) || (use_w && !aligned(W, 16)) ||
+        !aligned(act_scale, 4) || !aligned(gamma, 4) || (dbias && !aligned(dbias, 4)))
+        return fail(BL_EALIGN, "%s: dY, Xq, W_packed, X, W, dX, dW need 16-byte, act_scale, gamma "
+                    "and dbias 4-byte alignment", fn);
+    const size_t need = bl::ws_backward(M, N, K, (int)gran);
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
+        return fail(BL_EWORKSPACE, "%s: need %zu bytes of 256-byte aligned workspace", fn, need);
+    bl::BwdArgs a;
+    a.dy = static_cast<const uint16_t *>(dY);
+    a.xq = Xq;
+    a.bits = bits;
+    a.act_scale = act_scale;
+    a.gran = (int)gran;
+    a.w = W_packed;
+    a.gamma = gamma;
+    a.x = use_x ? X : nullptr;
+    a.x_bf16 = x_dtype == BL_BF16;
+    a.wf = use_w ? W : nullptr;
+    a.w_bf16 = w_dtype == BL_BF16;
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    a.dx = dX;
+    a.dw = dW;
+    a.dbias = dbias;
+    (void)hipGetLastError();
+    return device(bl::launch_backward(a, workspace, (hipStream_t)stream), fn);
 }
 
 static bl_status check_norm(const char *fn, void *X, const void *delta, void *H, int64_t M,

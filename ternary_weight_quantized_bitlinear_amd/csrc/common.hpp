@@ -259,4 +259,24 @@ size_t ws_gemm(int64_t M, int64_t N, int64_t K);
 bool gemm_f6f4_supports(int64_t M, int64_t N, int64_t K, int bits);
 hipError_t launch_gemm_f6f4(const FwdArgs &a, hipStream_t s);
 
+// backward under the straight-through estimators: dX, dW, dbias from dY
+struct BwdArgs {
+    const uint16_t *dy;     // bf16 [M][N]
+    const void *xq;         // the forward's activation codes (int8 or int4 nibbles)
+    int bits;               // 8 or 4
+    const float *act_scale;
+    int gran;               // 0 per token, 1 per tensor
+    const uint8_t *w;       // packed ternary codes [N][K/4]
+    const float *gamma;
+    const void *x;          // 4-bit: X for the activation mask, or null
+    int x_bf16;
+    const void *wf;         // 4-bit: latent W for the weight mask, or null
+    int w_bf16;
+    int64_t M, N, K;
+    float *dx, *dw, *dbias; // each may be null
+};
+constexpr int64_t kBwdMaxDim = 1ll << 21;  // M, N, K limit of the backward pass (grid extents)
+size_t ws_backward(int64_t M, int64_t N, int64_t K, int gran);
+hipError_t launch_backward(const BwdArgs &a, void *ws, hipStream_t s);
+
 }  // namespace bl

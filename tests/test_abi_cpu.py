@@ -26,7 +26,8 @@ def test_exports_every_header_function(L):
         "bitlinear_forward_fused", "bitlinear_forward_fused_batched", "bitlinear_rmsnorm",
         "bitlinear_rmsnorm_quantize", "bitlinear_workspace_size", "bitlinear_status_string",
         "bitlinear_last_error", "bitlinear_version", "bitlinear_hadamard_block",
-        "bitlinear_quantize_weights_rotated", "bitlinear_quantize_acts_rotated"}
+        "bitlinear_quantize_weights_rotated", "bitlinear_quantize_acts_rotated",
+        "bitlinear_backward"}
     for n in names:
         assert hasattr(L, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", bl.LIB_PATH], capture_output=True,
@@ -207,6 +208,68 @@ def test_rmsnorm_quantize_rejects(L):
     assert call(gran=1) == bl.BL_EWORKSPACE      # per tensor needs the absmax word
     assert call(H=P(A + 64)) == bl.BL_EINVAL     # H overlaps X
     assert L.bitlinear_last_error().decode().startswith("bitlinear_rmsnorm_quantize")
+
+
+def _bwd(L, **kw):
+    a = dict(dY=P(A), Xq=P(A), bits=8, scale=P(A), gran=0, W=P(A), gamma=P(A), X=None, xdt=0,
+             Wf=None, wdt=0, M=2048, N=6912, K=2560, dX=P(A), dW=P(A), db=P(A), ws=P(A),
+             wsb=1 << 40, stream=None)
+    a.update(kw)
+    return L.bitlinear_backward(a["dY"], a["Xq"], a["bits"], a["scale"], a["gran"], a["W"],
+                                a["gamma"], a["X"], a["xdt"], a["Wf"], a["wdt"], a["M"], a["N"],
+                                a["K"], a["dX"], a["dW"], a["db"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dY=None), bl.BL_EINVAL),
+    (dict(Xq=None), bl.BL_EINVAL),
+    (dict(scale=None), bl.BL_EINVAL),
+    (dict(W=None), bl.BL_EINVAL),
+    (dict(gamma=None), bl.BL_EINVAL),
+    (dict(dX=None, dW=None, db=None), bl.BL_EINVAL),
+    (dict(bits=2), bl.BL_EINVAL),
+    (dict(gran=4), bl.BL_EINVAL),
+    (dict(bits=4, X=P(A), xdt=2), bl.BL_EINVAL),   # int32 is no input dtype
+    (dict(bits=4, Wf=P(A), wdt=7), bl.BL_EINVAL),
+    (dict(K=100), bl.BL_ESHAPE),
+    (dict(M=0), bl.BL_ESHAPE),
+    (dict(M=(1 << 21) + 1), bl.BL_ESHAPE),
+    (dict(N=(1 << 21) + 16, K=16), bl.BL_ESHAPE),
+    (dict(dY=P(A + 2)), bl.BL_EALIGN),
+    (dict(dX=P(A + 4)), bl.BL_EALIGN),
+    (dict(dW=P(A + 8)), bl.BL_EALIGN),
+    (dict(db=P(A + 2)), bl.BL_EALIGN),
+    (dict(bits=4, X=P(A + 4), xdt=0), bl.BL_EALIGN),
+    (dict(ws=None), bl.BL_EWORKSPACE),
+    (dict(wsb=1024), bl.BL_EWORKSPACE),
+    (dict(ws=P(A + 16)), bl.BL_EWORKSPACE),         # workspace must be 256-byte aligned
+])
+def test_backward_rejects(L, kw, status):
+    assert _bwd(L, **kw) == status
+    assert L.bitlinear_last_error().decode().startswith("bitlinear_backward")
+
+
+def test_backward_ignores_masks_for_8_bits(L):
+    # X and W only feed the 4-bit clipping masks: with 8-bit codes a bad dtype or alignment
+    # there is not an error, and the call gets as far as the device
+    if _gpu_visible():
+        pytest.skip("a GPU is visible: this test needs a host with no device")
+    assert _bwd(L, X=P(A + 4), xdt=9, Wf=P(A + 2), wdt=9) == bl.BL_EDEVICE
+
+
+def test_backward_workspace_size(L):
+    f = L.bitlinear_workspace_size
+    M, N, K = 2048, 6912, 2560
+    tok = f(bl.BL_OP_BACKWARD, M, N, K, 8, 0)
+    ten = f(bl.BL_OP_BACKWARD, M, N, K, 8, 1)
+    # transposed codes [K][N] + transposed dY [N][M] + 3 (per token) or 1 planes of [K][M]
+    assert tok >= 2 * (K * N + N * M + 3 * K * M)
+    assert ten >= 2 * (K * N + N * M + K * M) and ten < tok
+    assert f(bl.BL_OP_BACKWARD, M, N, K, 4, 0) == tok
+    assert f(bl.BL_OP_BACKWARD, M, N, K, 3, 0) == 0
+    assert f(bl.BL_OP_BACKWARD, (1 << 21) + 1, N, K, 8, 0) == 0
+    # a ragged N adds the padded copy of dY
+    assert f(bl.BL_OP_BACKWARD, M, N + 8, K, 8, 0) > tok
 
 
 def _gpu_visible() -> bool:
