@@ -23,6 +23,8 @@ roofline     = the batched GEMV kernel against MI355X HBM (8 TB/s); traffic from
                kernel sources
 decode_chain = one layer's FFN step alone (two dependent 4.4 MB launches: latency-bound)
 prefill      = the prefill GEMM leg: M=2048 tokens, int TOPS against int8 MFMA peak
+backward     = the straight-through-estimator backward (dX, dW, dbias), TFLOP/s against
+               the bf16 MFMA peak
 cpu_baseline = the CPU oracle on one layer's decode FFN step, single-threaded
 """
 from __future__ import annotations
@@ -529,6 +531,60 @@ def leg_stack(torch, bl, steps=10, layers=30, batch=16):
             "library_calls_per_step": layers * 7 + 1, "output_finite": finite}
 
 
+BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, TFLOP/s
+
+
+def leg_backward(torch, bl, reps=5):
+    """Backward pass under the straight-through estimators (bitlinear_backward: dX, dW and
+    dbias from a bf16 dY), at the 2B prefill shapes (M=2048, int8 per-token codes, the
+    b1.58 training layer) and at the 70B-class layer with 4-bit codes and both clipping
+    masks (the a4.8 training layer).  Per shape: the whole call, dX alone and dW alone
+    (each with its operand preparation).  Algorithmic flops: 2 M N K per gradient GEMM;
+    per-token dW runs three bf16 passes (the fp32 operand in three exact parts), so the
+    matrix cores execute 3x its algorithmic flops."""
+    import workloads
+    dev = torch.device("cuda:0")
+    out = {}
+    cases = [("up_2b", workloads.SHAPE_UP, 2048, 8, None),
+             ("down_2b", workloads.SHAPE_DOWN, 2048, 8, None),
+             ("layer_70b_int4", workloads.SHAPE_70B, 4096, 4, "masks")]
+    for name, (K, N), M, bits, masks in cases:
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(11)
+        W = (0.02 * torch.randn((N, K), device=dev, generator=gen))
+        packed, gamma = bl.quantize_weights(W)
+        X = torch.randn((M, K), device=dev, generator=gen).to(torch.bfloat16)
+        xq, s = bl.quantize_acts(X, bits=bits)
+        dY = (0.01 * torch.randn((M, N), device=dev, generator=gen)).to(torch.bfloat16)
+        Wb = W.to(torch.bfloat16) if masks else None
+        del W
+        Xm = X if masks else None
+        ws = torch.empty(bl.workspace_size(bl.BL_OP_BACKWARD, M, N, K, bits), dtype=torch.uint8,
+                         device=dev)
+        res = {k: torch.empty(v, dtype=torch.float32, device=dev)
+               for k, v in (("dX", (M, K)), ("dW", (N, K)), ("dbias", (N,)))}
+        flops = 2.0 * M * N * K
+        r = {"M": M, "K": K, "N": N, "bits": bits, "masks": bool(masks)}
+        for tag, want in (("all", ("dX", "dW", "dbias")), ("dX", ("dX",)), ("dW", ("dW",))):
+            def run():
+                for _ in range(reps):
+                    bl.backward(dY, xq, s, packed, gamma, bits=bits, X=Xm, W=Wb, want=want,
+                                workspace=ws, out=res)
+            ms = graph_time_ms(torch, run, replays=1)[0] / reps
+            fl = flops * (2 if tag == "all" else 1)
+            r[tag + "_us"] = ms * 1e3
+            r[tag + "_tflops"] = fl / (ms * 1e-3) / 1e12
+        r["dX_frac"] = r["dX_tflops"] / BF16_PEAK_TFLOPS
+        r["dW_mfma_tflops"] = 3 * r["dW_tflops"]
+        r["dW_mfma_frac"] = r["dW_mfma_tflops"] / BF16_PEAK_TFLOPS
+        out[name] = r
+        del packed, X, xq, dY, Wb, ws, res
+        torch.cuda.synchronize()
+    out["peak_tflops"] = BF16_PEAK_TFLOPS
+    out["mfma"] = "bf16 32x32x16, fp32 accumulation, exact operands"
+    return out
+
+
 def leg_pack(torch, bl, reps=10):
     """a1: weight quantization + packing of the 2B up projection, fp32 W in HBM."""
     import workloads
@@ -583,7 +639,7 @@ def main():
     ap.add_argument("--batch", type=int, default=64, help="layers per streamed launch")
     ap.add_argument("--copies", type=int, default=64, help="weight copies of the chain leg")
     ap.add_argument("--chain-steps", type=int, default=2000)
-    ap.add_argument("--legs", default="decode,chain,single,prefill,stack,c5,pack,cpu")
+    ap.add_argument("--legs", default="decode,chain,single,prefill,stack,c5,pack,backward,cpu")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -609,6 +665,8 @@ def main():
             side["layer_70b"] = leg_70b(torch, bl)
         if "stack" in legs:
             side["stack_2b"] = leg_stack(torch, bl)
+        if "backward" in legs:
+            side["backward"] = leg_backward(torch, bl)
         if side:
             print(json.dumps(side))
         return
@@ -676,6 +734,12 @@ def main():
                                         "0.5% outlier channels x30, bf16 out: int8 vs int4 "
                                         "activations",
                             "unit": "TOPS", "peak_int8": INT8_PEAK_TOPS, **c5}
+    if "backward" in legs:
+        out["backward"] = {"workload": "straight-through-estimator backward (dX, dW, dbias from "
+                                       "bf16 dY): 2B FFN shapes at M=2048 with int8 codes, and "
+                                       "the 70B-class layer at M=4096 with int4 codes and both "
+                                       "clipping masks",
+                           "unit": "TFLOP/s", **leg_backward(torch, bl)}
     if "cpu" in legs:
         out["cpu_baseline"] = cpu_baseline(st["x"], st["W_up"], st["W_dn"])
     out["device"] = torch.cuda.get_device_name(0)

@@ -3,7 +3,8 @@
 //
 //   C[r][c] = epilogue( sum_k A[r][k] * B[c][k] )        r < R, c < S
 //
-// with both operands bf16 and k-contiguous ("NT"), prepared by the operand kernels of
+// with both operands bf16 and k-blocked (32-wide k slices of all rows stored one after
+// another, so a stage's loads are contiguous), prepared by the operand kernels of
 // the backward pass so that every operand value is exact in bf16 (ternary codes,
 // activation codes, bf16 upstream gradients, and fp32 values carried as three bf16
 // parts along the contraction axis).  The epilogue multiplies by one fp32 scale per
@@ -14,12 +15,14 @@
 // Tiling.  Block tile 256 x 256, k steps of 32 elements (64 bytes); 8 waves of 128 x
 // 64 (4 x 2 MFMA tiles of 32 x 32, 128 accumulator registers), two waves per SIMD.
 // Both operands stream straight from global memory into a 4-deep LDS ring with
-// global_load_lds_dwordx4 (16 bytes per lane landing at consecutive LDS slots); rows
-// are stored with their four 16-byte chunks XOR-swizzled by row so that fragment
-// reads of 8 or 16 consecutive rows hit distinct banks.  Operand columns are read
-// modulo a per-operand period (a_kt, b_kt steps), so one operand can be reused
-// against the three parts of the other without being copied.  Rows past R or S read
-// clamped addresses and are never stored.
+// global_load_lds_dwordx4 (16 bytes per lane landing at consecutive LDS slots): with
+// the k-blocked layout each instruction reads 1 KB of whole cache lines (16 rows of 64
+// bytes), which moves operands at about 1.5x the rate of 16 separate row-major rows.
+// Rows are stored in LDS with their four 16-byte chunks XOR-swizzled by row so that
+// fragment reads of 8 or 16 consecutive rows hit distinct banks.  Operand k blocks are
+// read modulo a per-operand period (a_kt, b_kt steps), so one operand can be reused
+// against the three parts of the other without being copied.  Operands are padded
+// with zero rows to whole tiles; rows past R or S are never stored.
 //
 // Work items.  Tiles [0, dp_tiles) run whole; each remaining tile is split into
 // `splits` contiguous k ranges whose raw accumulators go to a scratch area in
@@ -37,10 +40,18 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 
 constexpr int BM = kBfTile, BN = kBfTile;
 constexpr int BKE = 32, BKB = 64;                // k step: elements, bytes per row
+// 8 waves of 128 x 64 (two per SIMD) measured faster than 4 waves of 128 x 128 (one per
+// SIMD, a third less LDS read traffic); the code takes either
 constexpr int kWaves = 8, kThreads = 64 * kWaves;
+constexpr int NJ = kWaves == 8 ? 2 : 4;          // 32-wide column tiles per wave
+constexpr int WN = 32 * NJ;                      // columns per wave (rows per wave: 128)
+constexpr int kWavesN = BN / WN;
 constexpr int kAStage = BM * BKB, kStageBytes = (BM + BN) * BKB;  // 32 KB
-constexpr int kStages = 4;
-constexpr int kDma = 4;                          // DMA instructions per wave per stage
+constexpr int kStages = 4;  // 5 stages and an XCD-grouped tile order measured no faster
+constexpr int kDmaRows = BM / kWaves;            // rows of each operand a wave loads per stage
+constexpr int kDmaOp = kDmaRows / 16;            // DMA instructions (16 rows) per operand
+constexpr int kDma = 2 * kDmaOp;                 // DMA instructions per wave per stage
+constexpr int kQuadsPerWave = 4 * NJ * 4 * 64;   // accumulator float4s per wave
 constexpr size_t kLds = (size_t)kStages * kStageBytes;
 
 __device__ __forceinline__ int swz(int row) { return ((row >> 1) & 3) ^ ((row >> 3) & 1); }
@@ -113,7 +124,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_bf16_nt_kernel(BfParams p) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 2, wn = wave & 3;
+    const int wm = wave / kWavesN, wn = wave % kWavesN;
 
     // ---- work item: a whole tile or one k range of a split tile
     const int item = blockIdx.x;
@@ -135,32 +146,33 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_bf16_nt_kernel(BfParams p) {
     // advances modulo each operand's period; steps past the range reload in-bounds
     // columns that are never read.
     int ka = k0 % p.a_kt, kb = k0 % p.b_kt;
-    const int drow = 32 * wave + (lane >> 2);
-    const uint16_t *arow[2], *brow[2];
+    const int drow = kDmaRows * wave + (lane >> 2);
+    const uint16_t *arow[kDmaOp], *brow[kDmaOp];
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
+    for (int q = 0; q < kDmaOp; ++q) {
         const int row = drow + 16 * q;
         const int chunk = (lane & 3) ^ swz(row);
-        arow[q] = p.a + (int64_t)min(m0 + row, p.R - 1) * p.lda + 8 * chunk;
-        brow[q] = p.b + (int64_t)min(n0 + row, p.S - 1) * p.ldb + 8 * chunk;
+        arow[q] = p.a + (int64_t)(m0 + row) * BKE + 8 * chunk;
+        brow[q] = p.b + (int64_t)(n0 + row) * BKE + 8 * chunk;
     }
+    const int64_t astep = p.a_rows * BKE, bstep = p.b_rows * BKE;  // elements per k block
     auto issue_stage = [&](int slot) __attribute__((always_inline)) {
         uint8_t *sbase = smem + slot * kStageBytes;
 #pragma unroll
-        for (int q = 0; q < 2; ++q)
-            lds_dma16(arow[q] + ka * BKE, sbase + (32 * wave + 16 * q) * BKB);
+        for (int q = 0; q < kDmaOp; ++q)
+            lds_dma16(arow[q] + ka * astep, sbase + (kDmaRows * wave + 16 * q) * BKB);
 #pragma unroll
-        for (int q = 0; q < 2; ++q)
-            lds_dma16(brow[q] + kb * BKE, sbase + kAStage + (32 * wave + 16 * q) * BKB);
+        for (int q = 0; q < kDmaOp; ++q)
+            lds_dma16(brow[q] + kb * bstep, sbase + kAStage + (kDmaRows * wave + 16 * q) * BKB);
         ka = ka + 1 == p.a_kt ? 0 : ka + 1;
         kb = kb + 1 == p.b_kt ? 0 : kb + 1;
     };
 
-    v16f acc[4][2];
+    v16f acc[4][NJ];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < NJ; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
@@ -174,71 +186,78 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_bf16_nt_kernel(BfParams p) {
         const uint4 q = *reinterpret_cast<const uint4 *>(base + row * BKB + 16 * ((2 * s + kg) ^ swz(row)));
         return __builtin_bit_cast(v8bf, q);
     };
-    auto read = [&](int t, int s, v8bf (&af)[4], v8bf (&bf)[2]) __attribute__((always_inline)) {
+    auto read = [&](int t, int s, v8bf (&af)[4], v8bf (&bf)[NJ]) __attribute__((always_inline)) {
         const uint8_t *sa = smem + (t % kStages) * kStageBytes;
 #pragma unroll
         for (int i = 0; i < 4; ++i) af[i] = frag(sa, 128 * wm + 32 * i + r32, s);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) bf[j] = frag(sa + kAStage, 64 * wn + 32 * j + r32, s);
+        for (int j = 0; j < NJ; ++j) bf[j] = frag(sa + kAStage, WN * wn + 32 * j + r32, s);
     };
     // B as the first operand: lane l's accumulators then hold four consecutive output
     // columns of one row per register quad
-    auto mfmas = [&](const v8bf (&af)[4], const v8bf (&bf)[2], int i0, int ni) __attribute__((always_inline)) {
+    auto mfmas = [&](const v8bf (&af)[4], const v8bf (&bf)[NJ], int i0, int ni) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = i0; i < i0 + ni; ++i)
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
+            for (int j = 0; j < NJ; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[j], af[i], acc[i][j], 0, 0, 0);
     };
 
-    // Software pipeline as in the forward's large-tile GEMM: the next sub-step's
-    // fragment reads interleave with the current sub-step's MFMAs; the wait for the
-    // next step's stage, the barrier (which also certifies every wave is done with the
-    // slot being refilled) and the next DMA sit in the middle of the second sub-step.
-    wait_vm<(kStages - 2) * kDma>();
-    __syncthreads();
-    v8bf a0[4], b0[2], a1[4], b1[2];
-    read(0, 0, a0, b0);
-#pragma unroll 1
-    for (int t = 0; t < steps; ++t) {
-        read(t, 1, a1, b1);
-        mfmas(a0, b0, 0, 4);
-#pragma unroll
-        for (int g = 0; g < 6; ++g) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-        __builtin_amdgcn_sched_barrier(0);
-        mfmas(a1, b1, 0, 2);
-        __builtin_amdgcn_sched_barrier(0);
+    // Software pipeline one whole k step deep: at the top of step t one barrier makes
+    // stage t + 1 visible (each wave first waits for its own loads of it) and certifies
+    // that every wave is done with step t - 1's slot, which the next DMA then refills;
+    // the twelve fragment reads of step t + 1 then interleave with step t's sixteen
+    // MFMAs, whose fragments were read during step t - 1 -- each read has a whole step
+    // to land.
+    struct Frags {
+        v8bf a[2][4], b[2][NJ];
+    };
+    auto read_step = [&](int t, Frags &f) __attribute__((always_inline)) {
+        read(t, 0, f.a[0], f.b[0]);
+        read(t, 1, f.a[1], f.b[1]);
+    };
+    auto step = [&](int t, const Frags &cur, Frags &nxt) __attribute__((always_inline)) {
         wait_vm<(kStages - 3) * kDma>();
         __syncthreads();
         issue_stage((t + kStages - 1) % kStages);
         __builtin_amdgcn_sched_barrier(0);
-        read(t + 1, 0, a0, b0);
-        mfmas(a1, b1, 2, 2);
+        read_step(t + 1, nxt);
+        mfmas(cur.a[0], cur.b[0], 0, 4);
+        mfmas(cur.a[1], cur.b[1], 0, 4);
+        constexpr int kReads = 2 * (4 + NJ), kMfmas = 2 * 4 * NJ;
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
+        for (int g = 0; g < kReads; ++g) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS reads
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
         }
+        __builtin_amdgcn_sched_group_barrier(0x008, kMfmas - kReads, 0);
         __builtin_amdgcn_sched_barrier(0);
+    };
+    wait_vm<(kStages - 2) * kDma>();
+    __syncthreads();
+    Frags f0, f1;
+    read_step(0, f0);
+    int t = 0;
+#pragma unroll 1
+    for (; t + 1 < steps; t += 2) {
+        step(t, f0, f1);
+        step(t + 1, f1, f0);
     }
+    if (t < steps) step(t, f0, f1);
     wait_vm<0>();  // the ring's last (unused) loads
 
     // ---- lane l holds acc[i][j][4q + t] = C[row 32i + l%32][col 32j + 8q + 4(l/32) + t]
-    // of the wave's 128 x 64 tile
+    // of the wave's 128 x WN tile
     if (split) {
         float4 *dst = reinterpret_cast<float4 *>(p.partial) +
-                      ((int64_t)(item - p.dp_tiles) * (BM * BN / 4)) + wave * 2048 + lane;
+                      ((int64_t)(item - p.dp_tiles) * (BM * BN / 4)) + wave * kQuadsPerWave + lane;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
+            for (int j = 0; j < NJ; ++j)
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
-                    dst[((i * 2 + j) * 4 + q) * 64] =
+                    dst[((i * NJ + j) * 4 + q) * 64] =
                         make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
                                     acc[i][j][4 * q + 3]);
         return;
@@ -249,10 +268,10 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_bf16_nt_kernel(BfParams p) {
         if (row >= p.R) continue;
         const float sc = row_scale(p.epi, row);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < NJ; ++j) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int col = n0 + 64 * wn + 32 * j + 8 * q + 4 * kg;
+                const int col = n0 + WN * wn + 32 * j + 8 * q + 4 * kg;
                 if (col >= p.S) continue;
                 const float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
                                     acc[i][j][4 * q + 3]};
@@ -268,10 +287,11 @@ __global__ void __launch_bounds__(256) bf16_fixup_kernel(BfParams p) {
     const int per_tile = BM * BN / 4;
     const int u = (int)(g / per_tile), e = (int)(g % per_tile);
     const int tile = p.dp_tiles + u;
-    const int lane = e & 63, q = (e >> 6) & 3, j = (e >> 8) & 1, i = (e >> 9) & 3, wave = e >> 11;
+    const int lane = e & 63, q = (e >> 6) & 3, ij = (e >> 8) % (4 * NJ), wave = e / kQuadsPerWave;
+    const int i = ij / NJ, j = ij % NJ;
     const int tm = tile % p.tiles_m, tn = tile / p.tiles_m;
-    const int row = tm * BM + 128 * (wave >> 2) + 32 * i + (lane & 31);
-    const int col = tn * BN + 64 * (wave & 3) + 32 * j + 8 * q + 4 * (lane >> 5);
+    const int row = tm * BM + 128 * (wave / kWavesN) + 32 * i + (lane & 31);
+    const int col = tn * BN + WN * (wave % kWavesN) + 32 * j + 8 * q + 4 * (lane >> 5);
     if (row >= p.R || col >= p.S) return;
     const float4 *src = reinterpret_cast<const float4 *>(p.partial) + (int64_t)u * p.splits * per_tile + e;
     float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};

@@ -31,12 +31,15 @@ struct BfPlan {
     int splits = 1;    // k ranges per split tile
 };
 
+// Operands are k-blocked: element (row r, k) of an operand with `rows` (padded) rows sits
+// at ((k / 32) * rows + r) * 32 + k % 32, so the 32-wide k slice of 256 consecutive rows
+// that one pipeline stage loads is one contiguous 16 KB block.
 struct BfParams {
-    const uint16_t *a = nullptr;  // A [R][lda] bf16, k step t reads columns 32 (t % a_kt) ..
-    int64_t lda = 0;
+    const uint16_t *a = nullptr;  // A [a_kt][a_rows][32] bf16; k step t reads block t % a_kt
+    int64_t a_rows = 0;           // >= 256 * tiles_m
     int a_kt = 0;
-    const uint16_t *b = nullptr;  // B [S][ldb] bf16, columns 32 (t % b_kt) ..
-    int64_t ldb = 0;
+    const uint16_t *b = nullptr;  // B [b_kt][b_rows][32] bf16; k step t reads block t % b_kt
+    int64_t b_rows = 0;           // >= 256 * tiles_n
     int b_kt = 0;
     int nk = 0;                   // k steps of 32
     int R = 0, S = 0;             // output [R][S] fp32, S % 4 == 0
@@ -48,7 +51,7 @@ struct BfParams {
 
 BfPlan plan_bf16(int64_t R, int64_t S, int nk);
 size_t bf16_partial_bytes(const BfPlan &pl);
-// every pointer 16-byte aligned, lda and ldb multiples of 8, R, S >= 1
+// every pointer 16-byte aligned, R, S >= 1
 hipError_t launch_gemm_bf16(const BfParams &p, hipStream_t s);
 
 }  // namespace bl
