@@ -219,6 +219,7 @@ __global__ void __launch_bounds__(256) bwd_colsum_kernel(const uint16_t *__restr
     double acc[kV];
 #pragma unroll
     for (int j = 0; j < kV; ++j) acc[j] = 0.0;
+#pragma unroll 4
     for (int64_t m = r0; m < r1; ++m) {
         if (kV == 8) {
             const uint4 u = *reinterpret_cast<const uint4 *>(dy + m * N + n);
@@ -236,14 +237,27 @@ __global__ void __launch_bounds__(256) bwd_colsum_kernel(const uint16_t *__restr
     for (int j = 0; j < kV; ++j) part[blockIdx.y * N + n + j] = acc[j];
 }
 
+// 32 columns per block: eight groups of 32 threads each sum every eighth chunk, then the
+// eight group sums are added in group order (a fixed order: repeat calls agree bitwise)
 __global__ void __launch_bounds__(256) bwd_colsum_final_kernel(const double *__restrict__ part,
                                                                int64_t N, int chunks,
                                                                float *__restrict__ dbias) {
-    const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (n >= N) return;
+    __shared__ double red[8][32];
+    const int j = threadIdx.x & 31, g = threadIdx.x >> 5;
+    const int64_t n = (int64_t)blockIdx.x * 32 + j;
     double acc = 0.0;
-    for (int c = 0; c < chunks; ++c) acc += part[c * N + n];
-    dbias[n] = (float)acc;
+    if (n < N) {
+#pragma unroll 4
+        for (int c = g; c < chunks; c += 8) acc += part[(int64_t)c * N + n];
+    }
+    red[g][j] = acc;
+    __syncthreads();
+    if (g == 0 && n < N) {
+        double t = 0.0;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) t += red[k][j];
+        dbias[n] = (float)t;
+    }
 }
 
 int64_t up32(int64_t v) { return (v + 31) / 32 * 32; }
@@ -267,7 +281,8 @@ Layout layout(int64_t M, int64_t N, int64_t K, int gran) {
     L.Npad = up256r(N);
     L.Kpad = up256r(K);
     L.planes = gran == 0 ? 3 : 1;
-    L.colsum_rows = M / 64 > 64 ? M / 64 : 64;
+    // dbias row chunks: at least 8 rows, at most 256 chunks (fp64 partials [chunks][N])
+    L.colsum_rows = (M + 255) / 256 > 8 ? (M + 255) / 256 : 8;
     L.colsum_chunks = (int)((M + L.colsum_rows - 1) / L.colsum_rows);
     L.px = plan_bf16(M, K, (int)(L.Np / 32));
     L.pw = plan_bf16(N, K, (int)(L.planes * L.Mp / 32));
@@ -398,7 +413,7 @@ hipError_t launch_backward(const BwdArgs &a, void *ws, hipStream_t s) {
         else
             hipLaunchKernelGGL((bwd_colsum_kernel<1>), g, dim3(256), 0, s, a.dy, a.M, a.N, L.colsum_rows, part);
         if (!check()) return e;
-        hipLaunchKernelGGL(bwd_colsum_final_kernel, dim3((unsigned)((a.N + 255) / 256)), dim3(256), 0, s,
+        hipLaunchKernelGGL(bwd_colsum_final_kernel, dim3((unsigned)((a.N + 31) / 32)), dim3(256), 0, s,
                            part, a.N, L.colsum_chunks, a.dbias);
         if (!check()) return e;
     }
