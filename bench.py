@@ -621,7 +621,7 @@ def cpu_baseline(x, W_up, W_dn, budget_s=12.0):
         oracle.bitlinear(h, p_dn, g_dn, y_dtype=oracle.BF16)
         n += 1
         el = time.perf_counter() - t0
-        if el > budget_s or n >= 200:
+        if el > budget_s or n >= 5000:
             break
     step_bytes = gemv_bytes(K1, N1) + gemv_bytes(K2, N2)
     return {"value": step_bytes * n / el / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
