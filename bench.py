@@ -25,6 +25,7 @@ decode_chain = one layer's FFN step alone (two dependent 4.4 MB launches: latenc
 prefill      = the prefill GEMM leg: M=2048 tokens, int TOPS against int8 MFMA peak
 backward     = the straight-through-estimator backward (dX, dW, dbias), TFLOP/s against
                the bf16 MFMA peak
+parity_layer = the 8 x 256 -> 512 parity configuration, timed only
 cpu_baseline = the CPU oracle on one layer's decode FFN step, single-threaded
 """
 from __future__ import annotations
@@ -531,6 +532,31 @@ def leg_stack(torch, bl, steps=10, layers=30, batch=16):
             "library_calls_per_step": layers * 7 + 1, "output_finite": finite}
 
 
+def leg_parity_layer(torch, bl, reps=200):
+    """The parity configuration timed (no roofline claim: 32 KB of weights): the single
+    fp32 BitLinear at M=8, K=256, N=512, fused quantize + forward + ReLU^2, fp32 Y, for
+    int8 / int4 codes and per-token / per-tensor scales."""
+    import workloads
+    dev = torch.device("cuda:0")
+    W, X = workloads.parity_layer(seed=0, m=8, k=256, n=512)
+    packed, gamma = bl.quantize_weights(torch.from_numpy(W).to(dev))
+    Xd = torch.from_numpy(X).to(dev)
+    y = torch.empty((8, 512), dtype=torch.float32, device=dev)
+    out = {"M": 8, "K": 256, "N": 512}
+    for bits in (8, 4):
+        for gran in ("token", "tensor"):
+            ws = torch.empty(max(256, bl.workspace_size(bl.BL_OP_FORWARD_FUSED, 8, 512, 256, bits, gran)),
+                             dtype=torch.uint8, device=dev)
+
+            def run():
+                for _ in range(reps):
+                    bl.forward_fused(Xd, packed, gamma, bits=bits, gran=gran, epilogue="relu2", out=y,
+                                     workspace=ws)
+            ms = graph_time_ms(torch, run, replays=1)[0] / reps
+            out["int%d_%s_us" % (bits, gran)] = ms * 1e3
+    return out
+
+
 BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, TFLOP/s
 
 
@@ -639,7 +665,7 @@ def main():
     ap.add_argument("--batch", type=int, default=64, help="layers per streamed launch")
     ap.add_argument("--copies", type=int, default=64, help="weight copies of the chain leg")
     ap.add_argument("--chain-steps", type=int, default=2000)
-    ap.add_argument("--legs", default="decode,chain,single,prefill,stack,c5,pack,backward,cpu")
+    ap.add_argument("--legs", default="decode,chain,single,c1,prefill,stack,c5,pack,backward,cpu")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -667,6 +693,8 @@ def main():
             side["stack_2b"] = leg_stack(torch, bl)
         if "backward" in legs:
             side["backward"] = leg_backward(torch, bl)
+        if "c1" in legs:
+            side["parity_layer"] = leg_parity_layer(torch, bl)
         if side:
             print(json.dumps(side))
         return
@@ -734,6 +762,10 @@ def main():
                                         "0.5% outlier channels x30, bf16 out: int8 vs int4 "
                                         "activations",
                             "unit": "TOPS", "peak_int8": INT8_PEAK_TOPS, **c5}
+    if "c1" in legs:
+        out["parity_layer"] = {"workload": "single fp32 BitLinear, M=8, K=256, N=512, fused "
+                                           "quantize + forward + ReLU^2, fp32 out (timed only)",
+                               **leg_parity_layer(torch, bl)}
     if "backward" in legs:
         out["backward"] = {"workload": "straight-through-estimator backward (dX, dW, dbias from "
                                        "bf16 dY): 2B FFN shapes at M=2048 with int8 codes, and "
