@@ -419,16 +419,25 @@ __global__ void __launch_bounds__(kWaves * 64) gemv_kernel(GemvParams p) {
 //    with a buffer load at a fixed per-lane offset plus a uniform (group, tile)
 //    offset; rows past N (and loads past the wave's last tile, sent 2 GB out) fall
 //    outside the buffer's range and return zeros without touching memory.  A ring of kDepth registers keeps kDepth tiles in flight per lane.
+//  - Whole-line mode (kFull, rows a multiple of 128 bytes, K % 512 == 0): a load reads
+//    8 rows x 128 bytes instead -- lane (r8 = l/8, c8 = l%8) the 16 bytes c8 of line
+//    T of row 8h + r8, h alternating -- as a nontemporal load.  Each load instruction
+//    then fetches whole cache lines, which streams ~16% faster than 16 half lines
+//    (and nontemporal loads of half lines are slower than plain ones).  Two such
+//    loads (h = 0, 1) hold 16 rows x 128 bytes, two k tiles; the wave writes them
+//    to its own 2 KB of LDS ([16 rows][128 B], 16-byte chunks XOR-swizzled by row)
+//    and reads them back as the two tiles in the matrix core's layout.
 //  - Per tile: weight dword d (16 codes, byte q holds k = 16d + 4q + i in bits 2i)
 //    yields field i of all four dwords with one AND (fields scaled by 4^i, i < 3,
 //    still valid int8) or a shift and an AND (i = 3); MFMA i pairs them with the
 //    activations k = 16d + 4q + i, stored in that order in LDS by the prologue, and
 //    accumulates into acc[i].  The row-tile epilogue takes acc0 + acc1/4 + acc2/16 +
 //    acc3 - sum_k q (all exact integers), rescales and stores.
-template <int kMode, int kBits, int kDepth, int kR>
+template <int kMode, int kBits, int kDepth, int kR, bool kFull>
 __global__ void __launch_bounds__(256) gemv_stream_kernel(GemvParams p, int groups_per_block,
                                                           int xcd_order) {
     constexpr int kThreads = 256;
+    static_assert(!kFull || kR == 1, "whole-line mode streams one 16-row tile per wave item");
     // dynamic LDS: [M + 1][Kpad] int8 codes (row M all zero), then the block's bias rows
     extern __shared__ __attribute__((aligned(16))) uint8_t xl[];
     __shared__ float s_f[kMaxM];
@@ -486,7 +495,8 @@ __global__ void __launch_bounds__(256) gemv_stream_kernel(GemvParams p, int grou
     const uint32_t kw = (uint32_t)K >> 2;  // packed bytes per row
     const __amdgpu_buffer_rsrc_t wsrc = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t *>(p.w), (short)0, (int)((uint32_t)N * kw), 0x00020000);
-    const uint32_t voff = (uint32_t)r16 * kw + (uint32_t)chunk * 16u;
+    const uint32_t voff = kFull ? (uint32_t)(lane >> 3) * kw + (uint32_t)(lane & 7) * 16u
+                                : (uint32_t)r16 * kw + (uint32_t)chunk * 16u;
     constexpr uint32_t kPast = 0x80000000u;  // beyond any buffer: loads return zeros
     // next load's first row tile: wave w owns rows [g GS + 16 kR w, +16 kR) of group g
     uint32_t lso = ((uint32_t)g0 * GS + (uint32_t)wave * 16u * kR) * kw;
@@ -495,13 +505,15 @@ __global__ void __launch_bounds__(256) gemv_stream_kernel(GemvParams p, int grou
     auto next_load = [&]() __attribute__((always_inline)) {
         // the whole offset goes in the VGPR operand, whose range check is what makes
         // rows past N and loads past the wave's last tile return zeros
-        const uint32_t so = lso + 64u * (uint32_t)lt;
+        // whole-line mode: load lt is line lt/2 of rows 8 (lt%2) .. 8 (lt%2) + 7
+        const uint32_t so = kFull ? lso + 128u * (uint32_t)(lt >> 1) + 8u * kw * (uint32_t)(lt & 1)
+                                  : lso + 64u * (uint32_t)lt;
         const bool live = lg < items;
         Tile t;
 #pragma unroll
         for (int j = 0; j < kR; ++j)
             t.w[j] = __builtin_amdgcn_raw_buffer_load_b128(
-                wsrc, voff + (live ? so + 16u * kw * j : kPast), 0, 0);
+                wsrc, voff + (live ? so + 16u * kw * j : kPast), 0, kFull ? 2 : 0);
         if (++lt == ntiles) { lt = 0; ++lg; lso += (uint32_t)GS * kw; }
         return t;
     };
@@ -649,6 +661,18 @@ __global__ void __launch_bounds__(256) gemv_stream_kernel(GemvParams p, int grou
     constexpr int kIssue = 4;
     static_assert(kDepth % kIssue == 0, "ring depth must be a multiple of the issue group");
     Tile hold[kIssue];
+    // whole-line mode: this wave's 2 KB LDS window; lane (row, chunk c8) at row 128 +
+    // 16 (c8 ^ ((row >> 1) & 7)), so both the line-wise writes and the tile-wise reads
+    // of 16 lanes cover all 64 banks once
+    __shared__ __attribute__((aligned(16))) uint8_t s_perm[kFull ? 4 : 1][kFull ? 2048 : 16];
+    uint8_t *perm = &s_perm[kFull ? wave : 0][0];
+    const int wrow = lane >> 3, wc8 = lane & 7;  // write: rows wrow (+8), chunk wc8
+    const uint32_t woff0 = (uint32_t)wrow * 128u + 16u * (uint32_t)(wc8 ^ ((wrow >> 1) & 7));
+    const uint32_t woff1 = (uint32_t)(wrow + 8) * 128u + 16u * (uint32_t)(wc8 ^ (((wrow + 8) >> 1) & 7));
+    auto read_off = [&](int u) __attribute__((always_inline)) {  // tile u: row r16, chunk 4u + chunk
+        return (uint32_t)r16 * 128u + 16u * (uint32_t)((4 * u + chunk) ^ ((r16 >> 1) & 7));
+    };
+    Tile pend;  // whole-line mode: the second tile of the last permuted pair
 #pragma unroll 1
     for (int fb = 0; fb < F; fb += kDepth) {
 #pragma unroll
@@ -660,7 +684,19 @@ __global__ void __launch_bounds__(256) gemv_stream_kernel(GemvParams p, int grou
                     ring[d + e] = next_load();
                 }
             }
-            const Tile wt = hold[d % kIssue];
+            Tile wt;
+            if (kFull) {
+                if (d % 2 == 0) {  // a pair of line loads -> two tiles in matrix-core layout
+                    *reinterpret_cast<v4i *>(perm + woff0) = hold[d % kIssue].w[0];
+                    *reinterpret_cast<v4i *>(perm + woff1) = hold[d % kIssue + 1].w[0];
+                    wt.w[0] = *reinterpret_cast<const v4i *>(perm + read_off(0));
+                    pend.w[0] = *reinterpret_cast<const v4i *>(perm + read_off(1));
+                } else {
+                    wt = pend;
+                }
+            } else {
+                wt = hold[d % kIssue];
+            }
             if (fb + d >= F) continue;  // uniform: past this wave's last tile
             const uint8_t *xa = xrow + ut * 256;
             v4i a[4];
@@ -793,12 +829,22 @@ hipError_t launch_stream(const GemvParams &p, int mode, dim3 grid, int gpb, hipS
     const dim3 block(256);
     const int xo = kStreamXcdOrder && (grid.x * grid.y) % 8 == 0;
     const size_t lds = stream_lds_bytes(p.M, p.K, p.bias != nullptr, p.y_dtype == 1 ? 2 : 4, gpb);
-    if (mode == kInt8) hipLaunchKernelGGL((gemv_stream_kernel<kInt8, 8, kDepth, kStreamRows>), grid, block, lds, s, p, gpb, xo);
-    else if (mode == kInt4) hipLaunchKernelGGL((gemv_stream_kernel<kInt4, 4, kDepth, kStreamRows>), grid, block, lds, s, p, gpb, xo);
-    else if (mode == kRawBf16 && p.bits == 8) hipLaunchKernelGGL((gemv_stream_kernel<kRawBf16, 8, kDepth, kStreamRows>), grid, block, lds, s, p, gpb, xo);
-    else if (mode == kRawBf16) hipLaunchKernelGGL((gemv_stream_kernel<kRawBf16, 4, kDepth, kStreamRows>), grid, block, lds, s, p, gpb, xo);
-    else if (p.bits == 8) hipLaunchKernelGGL((gemv_stream_kernel<kRawF32, 8, kDepth, kStreamRows>), grid, block, lds, s, p, gpb, xo);
-    else hipLaunchKernelGGL((gemv_stream_kernel<kRawF32, 4, kDepth, kStreamRows>), grid, block, lds, s, p, gpb, xo);
+    // whole-line loads when every row is a whole number of 128-byte lines
+    const bool full = kStreamRows == 1 && p.K % 512 == 0;
+#define BL_STREAM(MODE, BITS)                                                                      \
+    do {                                                                                           \
+        if (full) hipLaunchKernelGGL((gemv_stream_kernel<MODE, BITS, kDepth, kStreamRows, true>),  \
+                                     grid, block, lds, s, p, gpb, xo);                             \
+        else hipLaunchKernelGGL((gemv_stream_kernel<MODE, BITS, kDepth, kStreamRows, false>),      \
+                                grid, block, lds, s, p, gpb, xo);                                  \
+    } while (0)
+    if (mode == kInt8) BL_STREAM(kInt8, 8);
+    else if (mode == kInt4) BL_STREAM(kInt4, 4);
+    else if (mode == kRawBf16 && p.bits == 8) BL_STREAM(kRawBf16, 8);
+    else if (mode == kRawBf16) BL_STREAM(kRawBf16, 4);
+    else if (p.bits == 8) BL_STREAM(kRawF32, 8);
+    else BL_STREAM(kRawF32, 4);
+#undef BL_STREAM
     return hipGetLastError();
 }
 
