@@ -4,14 +4,15 @@
 
 Headline (one JSON line on stdout): decode-GEMV HBM throughput on the BitNet 2B FFN
 shapes at M=1 token, streamed.  One step = the FFN of 64 independent 2B-shaped layers
-(64 distinct weight sets, 566 MB, more than twice the 256 MB Infinity Cache, so the
-weight stream really comes from HBM), each at decode time:
+(64 distinct weight copies, 566 MB per step), each at decode time:
     x_b (bf16 [1, 2560])  --up 2560->6912, ReLU^2-->  h_b (bf16 [1, 6912])
                           --down 6912->2560-->         y_b (bf16 [1, 2560])
 as two launches of bitlinear_forward_fused_batched (all 64 up projections, then all 64
 down projections).  Each fuses per-token absmax int8 quantization of its input (for
 down: the requantization of up's output), the ternary GEMV with int32 accumulation and
-the rescale epilogue.  Packed weights are pre-quantized (bitlinear_quantize_weights,
+the rescale epilogue.  Consecutive steps cycle through 3 such sets (1.7 GB), so no
+weights are still in the 256 MB Infinity Cache when they are read again and the stream
+really comes from HBM.  Packed weights are pre-quantized (bitlinear_quantize_weights,
 timed separately as the "pack" leg): the pages treat weights as static.
 
 Inputs are resident in HBM before timing.  The K timed steps are captured in one HIP
@@ -200,17 +201,22 @@ def make_weight_batch(torch, bl, W0, batch, seed):
     return packed, gamma
 
 
-def leg_decode_stream(torch, bl, steps, warmup, batch):
+def leg_decode_stream(torch, bl, steps, warmup, batch, sets=3):
     """Headline: the FFN decode step of `batch` independent 2B-shaped layers, M=1 each.
     Per step two launches of bitlinear_forward_fused_batched: up (x_b -> h_b, ReLU^2) over
-    all layers, then down (h_b requantized -> y_b).  The K timed steps are one HIP graph."""
+    all layers, then down (h_b requantized -> y_b).  Consecutive steps cycle through
+    `sets` independent weight sets (3 x 566 MB), so that no weights can still sit in the
+    256 MB Infinity Cache when they are read again: every step streams its weights from
+    HBM.  (With one set, the whole-line kernel's nontemporal up loads leave most of the
+    down weights cached between steps, which would overstate the HBM rate.)  The K timed
+    steps are one HIP graph."""
     import workloads
     dev = torch.device("cuda:0")
     (K1, N1), (K2, N2) = workloads.SHAPE_UP, workloads.SHAPE_DOWN
     W_up, x = workloads.decode_gemv(seed=1, shape=workloads.SHAPE_UP)
     W_dn, _ = workloads.decode_gemv(seed=1, shape=workloads.SHAPE_DOWN)
-    pu, gu = make_weight_batch(torch, bl, W_up, batch, 41)
-    pd, gd = make_weight_batch(torch, bl, W_dn, batch, 42)
+    wsets = [make_weight_batch(torch, bl, W_up, batch, 41 + 10 * i) +
+             make_weight_batch(torch, bl, W_dn, batch, 42 + 10 * i) for i in range(sets)]
     gen = torch.Generator(device=dev)
     gen.manual_seed(43)
     X = torch.randn((batch, 1, K1), device=dev, generator=gen).to(torch.bfloat16)
@@ -218,24 +224,25 @@ def leg_decode_stream(torch, bl, steps, warmup, batch):
     h = torch.empty((batch, 1, N1), dtype=torch.bfloat16, device=dev)
     y = torch.empty((batch, 1, N2), dtype=torch.bfloat16, device=dev)
 
-    def step():
+    def step(i):
+        pu, gu, pd, gd = wsets[i % sets]
         bl.forward_fused_batched(X, pu, gu, epilogue="relu2", out=h)
         bl.forward_fused_batched(h, pd, gd, out=y)
 
     def run_k():
-        for _ in range(steps):
-            step()
+        for i in range(steps):
+            step(i)
 
-    for _ in range(warmup):
-        step()
+    for i in range(warmup):
+        step(i)
     torch.cuda.synchronize()
     ms_total, _ = graph_time_ms(torch, run_k, replays=1, warm=1)
     ms_step = ms_total / steps
     step_bytes = batch * (gemv_bytes(K1, N1) + gemv_bytes(K2, N2))
     return {"ms_per_step": ms_step, "gbs": step_bytes / (ms_step * 1e-3) / 1e9,
             "step_bytes": step_bytes, "per_launch_us": ms_step * 1e3 / 2,
-            "bytes_per_launch": step_bytes / 2, "batch": batch, "x": x, "W_up": W_up,
-            "W_dn": W_dn}
+            "bytes_per_launch": step_bytes / 2, "batch": batch, "sets": sets, "x": x,
+            "W_up": W_up, "W_dn": W_dn}
 
 
 def leg_decode_single(torch, bl, copies=64, reps=200):
@@ -716,8 +723,10 @@ def main():
         "data": "synthetic: seeded uniform-ternary weights, N(0,1) bf16 activations",
         "config": {"workload": "BitNet-2B FFN decode GEMVs, M=1, streamed: %d independent layers "
                                "per launch; step = up 2560->6912 (+ReLU^2) then down 6912->2560 "
-                               "on every layer, fused int8 per-token quantization, bf16 out"
-                               % st["batch"],
+                               "on every layer, fused int8 per-token quantization, bf16 out; "
+                               "steps cycle %d weight sets (%d MB) so weights come from HBM"
+                               % (st["batch"], st["sets"], st["sets"] * st["step_bytes"] // 10**6),
+                   "weight_sets": st["sets"],
                    "tokens_per_layer": 1, "hidden": 2560, "ffn": 6912,
                    "layers_per_launch": st["batch"], "weight_bytes_per_step": st["step_bytes"]},
         "roofline": {"bound": "hbm", "kernel": "gemv_kernel (fused decode GEMV, batched)",
