@@ -411,7 +411,7 @@ __global__ void __launch_bounds__(kWaves * 64) gemv_kernel(GemvParams p) {
 //    It brings that problem's activations into LDS once (quantizing them, for the
 //    fused modes), plus sum_k q[m][k] per token (the offset-binary correction) and
 //    the bias of its rows.  LDS rows are zero-padded to a multiple of 256 k and
-//    absent tokens read a zero row, so the main loop needs no masks or clamps.
+//    absent tokens read a zero row, so the main loop needs no masks.
 //  - Wave w owns row tile 4g + w (16 rows) of each group g over the full K: no
 //    cross-wave reduction and no barrier after the prologue.
 //  - A wave's weight loads form one flat sequence over (group, 256-wide k tile):
@@ -419,7 +419,7 @@ __global__ void __launch_bounds__(kWaves * 64) gemv_kernel(GemvParams p) {
 //    with a buffer load at a fixed per-lane offset plus a uniform (group, tile)
 //    offset; rows past N (and loads past the wave's last tile, sent 2 GB out) fall
 //    outside the buffer's range and return zeros without touching memory.  A ring of kDepth registers keeps kDepth tiles in flight per lane.
-//  - Whole-line mode (kFull, rows a multiple of 128 bytes, K % 512 == 0): a load reads
+//  - Whole-line mode (kLine 1, rows a multiple of 128 bytes, K % 512 == 0): a load reads
 //    8 rows x 128 bytes instead -- lane (r8 = l/8, c8 = l%8) the 16 bytes c8 of line
 //    T of row 8h + r8, h alternating -- as a nontemporal load.  Each load instruction
 //    then fetches whole cache lines, which streams ~16% faster than 16 half lines
@@ -427,16 +427,27 @@ __global__ void __launch_bounds__(kWaves * 64) gemv_kernel(GemvParams p) {
 //    loads (h = 0, 1) hold 16 rows x 128 bytes, two k tiles; the wave writes them
 //    to its own 2 KB of LDS ([16 rows][128 B], 16-byte chunks XOR-swizzled by row)
 //    and reads them back as the two tiles in the matrix core's layout.
+//  - Shifted whole-line mode (kLine 2: K % 512 == 256, at most 8 tokens): rows are
+//    an odd number of 64-byte halves, so every odd row starts half way into a line.
+//    Odd rows then load the lines that start 64 bytes before their k tile pairs:
+//    at virtual tile v an even row holds its k tile v and an odd row its tile v - 1,
+//    for v in [0, ntiles], with the half before an odd row's start and the half
+//    after an even row's end loaded as zeros (sent out of range).  The matrix core
+//    takes token m's activations of tile v in row m of its A operand and those of
+//    tile v - 1 in row 8 + m, so even output rows read their sums in accumulator
+//    rows 0-7 and odd ones in rows 8-15; the other eight rows are discarded.
 //  - Per tile: weight dword d (16 codes, byte q holds k = 16d + 4q + i in bits 2i)
 //    yields field i of all four dwords with one AND (fields scaled by 4^i, i < 3,
 //    still valid int8) or a shift and an AND (i = 3); MFMA i pairs them with the
 //    activations k = 16d + 4q + i, stored in that order in LDS by the prologue, and
 //    accumulates into acc[i].  The row-tile epilogue takes acc0 + acc1/4 + acc2/16 +
 //    acc3 - sum_k q (all exact integers), rescales and stores.
-template <int kMode, int kBits, int kDepth, int kR, bool kFull>
+template <int kMode, int kBits, int kDepth, int kR, int kLine>
 __global__ void __launch_bounds__(256) gemv_stream_kernel(GemvParams p, int groups_per_block,
                                                           int xcd_order) {
     constexpr int kThreads = 256;
+    constexpr bool kFull = kLine != 0;  // whole-line loads, permuted through LDS
+    constexpr bool kShift = kLine == 2;  // odd rows one k tile behind (M <= 8)
     static_assert(!kFull || kR == 1, "whole-line mode streams one 16-row tile per wave item");
     // dynamic LDS: [M + 1][Kpad] int8 codes (row M all zero), then the block's bias rows
     extern __shared__ __attribute__((aligned(16))) uint8_t xl[];
@@ -471,6 +482,7 @@ __global__ void __launch_bounds__(256) gemv_stream_kernel(GemvParams p, int grou
     const int ngroups = K >> 4;                  // 16-element activation groups
     const int ntiles = (K + 255) >> 8;           // 256-wide k tiles per row tile
     const int Kpad = ntiles << 8;
+    const int vtiles = kShift ? ntiles + 1 : ntiles;  // tiles streamed per row tile
     constexpr int GS = 64 * kR;                  // rows per group: 4 waves x kR x 16
     const int G = (N + GS - 1) / GS;
     const int g0 = bx * groups_per_block;
@@ -478,7 +490,7 @@ __global__ void __launch_bounds__(256) gemv_stream_kernel(GemvParams p, int grou
     if (g0 >= G) return;  // whole block, before any barrier
     const int items = g1 - g0;
     const int r16 = lane & 15, chunk = lane >> 4;
-    const int F = items * ntiles;                // this wave's tiles
+    const int F = items * vtiles;                // this wave's tiles
 
     // ---- activation loads first (they retire before the weights)
     constexpr bool kRaw = kMode == kRawBf16 || kMode == kRawF32;
@@ -495,8 +507,15 @@ __global__ void __launch_bounds__(256) gemv_stream_kernel(GemvParams p, int grou
     const uint32_t kw = (uint32_t)K >> 2;  // packed bytes per row
     const __amdgpu_buffer_rsrc_t wsrc = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t *>(p.w), (short)0, (int)((uint32_t)N * kw), 0x00020000);
-    const uint32_t voff = kFull ? (uint32_t)(lane >> 3) * kw + (uint32_t)(lane & 7) * 16u
+    // (shifted mode: odd rows start 64 bytes early; row 1 starts at kw >= 64)
+    const uint32_t voff = kFull ? (uint32_t)(lane >> 3) * kw + (uint32_t)(lane & 7) * 16u -
+                                      (kShift && (lane & 8) ? 64u : 0u)
                                 : (uint32_t)r16 * kw + (uint32_t)chunk * 16u;
+    // shifted mode: an odd row's first line and an even row's last line are half
+    // another row's; those lanes load zeros instead
+    const bool odd_row = (lane & 8) != 0, lo_half = (lane & 7) < 4;
+    const bool skip_first = kShift && odd_row && lo_half;
+    const bool skip_last = kShift && !odd_row && !lo_half;
     constexpr uint32_t kPast = 0x80000000u;  // beyond any buffer: loads return zeros
     // next load's first row tile: wave w owns rows [g GS + 16 kR w, +16 kR) of group g
     uint32_t lso = ((uint32_t)g0 * GS + (uint32_t)wave * 16u * kR) * kw;
@@ -508,13 +527,15 @@ __global__ void __launch_bounds__(256) gemv_stream_kernel(GemvParams p, int grou
         // whole-line mode: load lt is line lt/2 of rows 8 (lt%2) .. 8 (lt%2) + 7
         const uint32_t so = kFull ? lso + 128u * (uint32_t)(lt >> 1) + 8u * kw * (uint32_t)(lt & 1)
                                   : lso + 64u * (uint32_t)lt;
-        const bool live = lg < items;
+        bool live = lg < items;
+        if (kShift) live = live && !((lt >> 1) == 0 && skip_first) &&
+                           !((lt >> 1) == (vtiles >> 1) - 1 && skip_last);
         Tile t;
 #pragma unroll
         for (int j = 0; j < kR; ++j)
             t.w[j] = __builtin_amdgcn_raw_buffer_load_b128(
                 wsrc, voff + (live ? so + 16u * kw * j : kPast), 0, kFull ? 2 : 0);
-        if (++lt == ntiles) { lt = 0; ++lg; lso += (uint32_t)GS * kw; }
+        if (++lt == vtiles) { lt = 0; ++lg; lso += (uint32_t)GS * kw; }
         return t;
     };
     Tile ring[kDepth];
@@ -637,14 +658,22 @@ __global__ void __launch_bounds__(256) gemv_stream_kernel(GemvParams p, int grou
     __syncthreads();
 
     // ---- stream
-    const uint8_t *xrow = xl + (size_t)(r16 < M ? r16 : M) * Kpad + chunk * 64;
+    // A operand row r16: token r16 (shifted mode: token r16 % 8, rows 8-15 one k tile
+    // behind); absent tokens read the zero row M
+    const int xtok = kShift ? (r16 & 7) : r16;
+    const int xsh = kShift && r16 >= 8 ? 1 : 0;
+    const uint8_t *xrow = xl + (size_t)(xtok < M ? xtok : M) * Kpad + chunk * 64;
+    // accumulator rows 4 chunk + r of output row r16 belong to token mb + r (shifted
+    // mode: odd output rows read rows 8-15); rows outside [0, M) are discarded
+    const int mb = 4 * chunk - (kShift && (r16 & 1) ? 8 : 0);
     float f4[4];
     int sum4[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-        const int m = 4 * chunk + r;
-        f4[r] = s_f[m < M ? m : 0];
-        sum4[r] = s_sum[m < M ? m : 0];
+        const int m = mb + r;
+        const bool ok = m >= 0 && m < M;
+        f4[r] = s_f[ok ? m : 0];
+        sum4[r] = s_sum[ok ? m : 0];
     }
     // the accumulators run on across row tiles (int32 wrap-around); a row tile's sums
     // are the differences from their values at the previous row tile's end, exact
@@ -698,7 +727,10 @@ __global__ void __launch_bounds__(256) gemv_stream_kernel(GemvParams p, int grou
                 wt = hold[d % kIssue];
             }
             if (fb + d >= F) continue;  // uniform: past this wave's last tile
-            const uint8_t *xa = xrow + ut * 256;
+            // shifted mode: the tiles that pair only with zero weights (v - 1 < 0 in
+            // rows 8-15, v = ntiles in rows 0-7) read a real tile instead
+            const int xt = kShift ? min(max(ut - xsh, 0), ntiles - 1) : ut;
+            const uint8_t *xa = xrow + xt * 256;
             v4i a[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -717,7 +749,7 @@ __global__ void __launch_bounds__(256) gemv_stream_kernel(GemvParams p, int grou
                 acc[j][2] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[2], b2, acc[j][2], 0, 0, 0);
                 acc[j][3] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[3], b3, acc[j][3], 0, 0, 0);
             }
-            if (++ut == ntiles) {  // row tiles done: epilogue (uniform branch)
+            if (++ut == vtiles) {  // row tiles done: epilogue (uniform branch)
 #pragma unroll
                 for (int j = 0; j < kR; ++j) {
                     const int nrow = (g0 + ug) * GS + (wave * kR + j) * 16 + r16;
@@ -730,8 +762,8 @@ __global__ void __launch_bounds__(256) gemv_stream_kernel(GemvParams p, int grou
                     if (nrow >= N) continue;
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        const int m = 4 * chunk + r;
-                        if (m >= M) continue;
+                        const int m = mb + r;
+                        if (m < 0 || m >= M) continue;
                         const int av = dd[0][r] + dd[3][r] + (dd[1][r] >> 2) + (dd[2][r] >> 4) - sum4[r];
                         const int sidx = m * brow + (nrow - g0 * GS);
                         if (p.y_dtype == 2) {
@@ -829,13 +861,16 @@ hipError_t launch_stream(const GemvParams &p, int mode, dim3 grid, int gpb, hipS
     const dim3 block(256);
     const int xo = kStreamXcdOrder && (grid.x * grid.y) % 8 == 0;
     const size_t lds = stream_lds_bytes(p.M, p.K, p.bias != nullptr, p.y_dtype == 1 ? 2 : 4, gpb);
-    // whole-line loads when every row is a whole number of 128-byte lines
-    const bool full = kStreamRows == 1 && p.K % 512 == 0;
+    // whole-line loads when every row is a whole number of 128-byte lines, or (at most
+    // 8 tokens) an odd number of 64-byte halves
+    const int line = kStreamRows != 1 ? 0 : p.K % 512 == 0 ? 1 : p.K % 512 == 256 && p.M <= 8 ? 2 : 0;
 #define BL_STREAM(MODE, BITS)                                                                      \
     do {                                                                                           \
-        if (full) hipLaunchKernelGGL((gemv_stream_kernel<MODE, BITS, kDepth, kStreamRows, true>),  \
-                                     grid, block, lds, s, p, gpb, xo);                             \
-        else hipLaunchKernelGGL((gemv_stream_kernel<MODE, BITS, kDepth, kStreamRows, false>),      \
+        if (line == 1) hipLaunchKernelGGL((gemv_stream_kernel<MODE, BITS, kDepth, kStreamRows, 1>), \
+                                          grid, block, lds, s, p, gpb, xo);                        \
+        else if (line == 2) hipLaunchKernelGGL((gemv_stream_kernel<MODE, BITS, kDepth, kStreamRows, 2>), \
+                                               grid, block, lds, s, p, gpb, xo);                   \
+        else hipLaunchKernelGGL((gemv_stream_kernel<MODE, BITS, kDepth, kStreamRows, 0>),          \
                                 grid, block, lds, s, p, gpb, xo);                                  \
     } while (0)
     if (mode == kInt8) BL_STREAM(kInt8, 8);

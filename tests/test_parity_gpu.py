@@ -303,6 +303,16 @@ def test_forward_deterministic():
     (36, 5, 256, 4096, 4, "tensor", None, "f32", "f32", True),
     (33, 16, 192, 4100, 8, "token", "relu2", "f32", "bf16", True),
     (64, 2, 64, 2048, 8, "token", None, "i32", "f32", False),
+    # whole-line loads (K % 512 == 0), up to the 16-token limit
+    (34, 3, 1024, 4000, 8, "token", "relu2", "bf16", "bf16", True),
+    (33, 16, 512, 4100, 8, "token", None, "f32", "f32", False),
+    # shifted whole-line loads (K % 512 == 256, at most 8 tokens): ragged last row tile
+    # ending on an odd row and on an even row, both activation widths, int4 codes
+    (36, 8, 768, 4003, 8, "token", "relu2", "f32", "bf16", True),
+    (33, 7, 1280, 4004, 4, "tensor", None, "i32", "f32", False),
+    (32, 1, 256, 4096, 4, "token", None, "bf16", "bf16", True),
+    # 9 tokens at K % 512 == 256: the half-line loads
+    (32, 9, 768, 4096, 8, "token", None, "bf16", "bf16", False),
 ])
 def test_forward_fused_batched(B, M, K, N, bits, gran, epi, ydt, xdt, with_bias):
     say("forward_fused_batched", dict(B=B, M=M, K=K, N=N, bits=bits, gran=gran, epi=epi, y=ydt,
