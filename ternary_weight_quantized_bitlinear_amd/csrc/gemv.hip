@@ -428,14 +428,18 @@ __global__ void __launch_bounds__(kWaves * 64) gemv_kernel(GemvParams p) {
 //    to its own 2 KB of LDS ([16 rows][128 B], 16-byte chunks XOR-swizzled by row)
 //    and reads them back as the two tiles in the matrix core's layout.
 //  - Shifted whole-line mode (kLine 2: K % 512 == 256, at most 8 tokens): rows are
-//    an odd number of 64-byte halves, so every odd row starts half way into a line.
-//    Odd rows then load the lines that start 64 bytes before their k tile pairs:
-//    at virtual tile v an even row holds its k tile v and an odd row its tile v - 1,
-//    for v in [0, ntiles], with the half before an odd row's start and the half
-//    after an even row's end loaded as zeros (sent out of range).  The matrix core
-//    takes token m's activations of tile v in row m of its A operand and those of
-//    tile v - 1 in row 8 + m, so even output rows read their sums in accumulator
-//    rows 0-7 and odd ones in rows 8-15; the other eight rows are discarded.
+//    an odd number (ntiles) of 64-byte halves, so every odd row starts half way into
+//    a line, and each even row's last line ends with its odd partner's first half.
+//    A row tile streams ntiles + 1 virtual tiles v as (ntiles + 1) / 2 line pairs.
+//    Even rows load their lines in order (tile v at v < ntiles; the last half, v =
+//    ntiles, is the partner's tile 0).  Odd rows load the lines that start 64 bytes
+//    before their tile pairs, rotated by one so that the shared line comes last, in
+//    the same instruction as the even row's: odd tile v + 1 at v < ntiles - 1, the
+//    partner's last tile at v = ntiles - 1, odd tile 0 at v = ntiles.  The matrix
+//    core takes token m's activations for the even rows in row m of its A operand
+//    and for the odd rows in row 8 + m, with the LDS zero row where the weights are
+//    the partner's; even output rows read their sums in accumulator rows 0-7, odd
+//    ones in rows 8-15, and the other eight rows are discarded.
 //  - Per tile: weight dword d (16 codes, byte q holds k = 16d + 4q + i in bits 2i)
 //    yields field i of all four dwords with one AND (fields scaled by 4^i, i < 3,
 //    still valid int8) or a shift and an AND (i = 3); MFMA i pairs them with the
@@ -511,11 +515,7 @@ __global__ void __launch_bounds__(256) gemv_stream_kernel(GemvParams p, int grou
     const uint32_t voff = kFull ? (uint32_t)(lane >> 3) * kw + (uint32_t)(lane & 7) * 16u -
                                       (kShift && (lane & 8) ? 64u : 0u)
                                 : (uint32_t)r16 * kw + (uint32_t)chunk * 16u;
-    // shifted mode: an odd row's first line and an even row's last line are half
-    // another row's; those lanes load zeros instead
-    const bool odd_row = (lane & 8) != 0, lo_half = (lane & 7) < 4;
-    const bool skip_first = kShift && odd_row && lo_half;
-    const bool skip_last = kShift && !odd_row && !lo_half;
+    const bool odd_row = kShift && (lane & 8) != 0;
     constexpr uint32_t kPast = 0x80000000u;  // beyond any buffer: loads return zeros
     // next load's first row tile: wave w owns rows [g GS + 16 kR w, +16 kR) of group g
     uint32_t lso = ((uint32_t)g0 * GS + (uint32_t)wave * 16u * kR) * kw;
@@ -525,11 +525,12 @@ __global__ void __launch_bounds__(256) gemv_stream_kernel(GemvParams p, int grou
         // the whole offset goes in the VGPR operand, whose range check is what makes
         // rows past N and loads past the wave's last tile return zeros
         // whole-line mode: load lt is line lt/2 of rows 8 (lt%2) .. 8 (lt%2) + 7
-        const uint32_t so = kFull ? lso + 128u * (uint32_t)(lt >> 1) + 8u * kw * (uint32_t)(lt & 1)
+        // (shifted mode: odd rows take line pair + 1, and the first line last)
+        const uint32_t pair = (uint32_t)(lt >> 1);
+        const uint32_t opair = (int)pair + 1 == (vtiles >> 1) ? 0u : pair + 1u;
+        const uint32_t so = kFull ? lso + 128u * (odd_row ? opair : pair) + 8u * kw * (uint32_t)(lt & 1)
                                   : lso + 64u * (uint32_t)lt;
-        bool live = lg < items;
-        if (kShift) live = live && !((lt >> 1) == 0 && skip_first) &&
-                           !((lt >> 1) == (vtiles >> 1) - 1 && skip_last);
+        const bool live = lg < items;
         Tile t;
 #pragma unroll
         for (int j = 0; j < kR; ++j)
@@ -661,8 +662,9 @@ __global__ void __launch_bounds__(256) gemv_stream_kernel(GemvParams p, int grou
     // A operand row r16: token r16 (shifted mode: token r16 % 8, rows 8-15 one k tile
     // behind); absent tokens read the zero row M
     const int xtok = kShift ? (r16 & 7) : r16;
-    const int xsh = kShift && r16 >= 8 ? 1 : 0;
+    const bool xodd = kShift && r16 >= 8;
     const uint8_t *xrow = xl + (size_t)(xtok < M ? xtok : M) * Kpad + chunk * 64;
+    const uint8_t *xzero = xl + (size_t)M * Kpad + chunk * 64;
     // accumulator rows 4 chunk + r of output row r16 belong to token mb + r (shifted
     // mode: odd output rows read rows 8-15); rows outside [0, M) are discarded
     const int mb = 4 * chunk - (kShift && (r16 & 1) ? 8 : 0);
@@ -727,10 +729,15 @@ __global__ void __launch_bounds__(256) gemv_stream_kernel(GemvParams p, int grou
                 wt = hold[d % kIssue];
             }
             if (fb + d >= F) continue;  // uniform: past this wave's last tile
-            // shifted mode: the tiles that pair only with zero weights (v - 1 < 0 in
-            // rows 8-15, v = ntiles in rows 0-7) read a real tile instead
-            const int xt = kShift ? min(max(ut - xsh, 0), ntiles - 1) : ut;
-            const uint8_t *xa = xrow + xt * 256;
+            // shifted mode: the k tile of virtual tile ut for A rows 0-7 (even output
+            // rows) and 8-15 (odd ones), or the zero row where the weights are the
+            // partner row's
+            const uint8_t *xa = xrow + ut * 256;
+            if (kShift) {
+                const bool zero = xodd ? ut == ntiles - 1 : ut == ntiles;
+                const int xt = xodd ? (ut == ntiles ? 0 : ut + 1) : ut;
+                xa = zero ? xzero : xrow + xt * 256;
+            }
             v4i a[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
