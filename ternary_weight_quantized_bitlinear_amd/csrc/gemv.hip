@@ -403,16 +403,41 @@ __global__ void __launch_bounds__(kWaves * 64) gemv_kernel(GemvParams p) {
 }
 
 // ---------------------------------------------------------------- streaming variant
+// streaming kernel: 16-byte weight loads in flight per lane, waves per block, blocks
+// per CU.  One block of 8 waves per CU streams ~6% faster than two blocks of 4: of two
+// co-resident blocks one was served consistently slower (by up to ~10% over a whole
+// launch), and the CU waited for it at the end; waves of one block kept pace.
+#ifndef BL_STREAM_DEPTH
+#define BL_STREAM_DEPTH 8
+#endif
+#ifndef BL_STREAM_WAVES
+#define BL_STREAM_WAVES 8
+#endif
+#ifndef BL_STREAM_BLOCKS_PER_CU
+#define BL_STREAM_BLOCKS_PER_CU 1
+#endif
+#ifndef BL_STREAM_ROWS
+#define BL_STREAM_ROWS 1
+#endif
+#ifndef BL_STREAM_XCD
+#define BL_STREAM_XCD 1
+#endif
+constexpr int kStreamDepth = BL_STREAM_DEPTH;
+constexpr int kStreamWaves = BL_STREAM_WAVES;
+constexpr int kStreamBlocksPerCu = BL_STREAM_BLOCKS_PER_CU;
+constexpr int kStreamRows = BL_STREAM_ROWS;      // 16-row tiles per wave item
+constexpr int kStreamXcdOrder = BL_STREAM_XCD;  // problem-per-XCD block order
 // For many row tiles per launch (a batch of layers, or a very wide layer): the weight
 // stream has to stay in flight for the whole launch, and the issue cost per weight
 // byte has to stay well below what the stream allows (about 1 KB per SIMD every
 // ~300 cycles at full HBM rate), so the work is reorganised.
-//  - A block owns a contiguous range of 64-row groups of one problem (blockIdx.y).
+//  - A block owns a contiguous range of row groups (16 rows per wave) of one problem
+//    (blockIdx.y).
 //    It brings that problem's activations into LDS once (quantizing them, for the
 //    fused modes), plus sum_k q[m][k] per token (the offset-binary correction) and
 //    the bias of its rows.  LDS rows are zero-padded to a multiple of 256 k and
 //    absent tokens read a zero row, so the main loop needs no masks.
-//  - Wave w owns row tile 4g + w (16 rows) of each group g over the full K: no
+//  - Wave w of W owns row tile W g + w (16 rows) of each group g over the full K: no
 //    cross-wave reduction and no barrier after the prologue.
 //  - A wave's weight loads form one flat sequence over (group, 256-wide k tile):
 //    lane (r16 = l%16, c = l/16) reads bytes [64t + 16c, +16) of row r16 of the tile
@@ -447,9 +472,9 @@ __global__ void __launch_bounds__(kWaves * 64) gemv_kernel(GemvParams p) {
 //    accumulates into acc[i].  The row-tile epilogue takes acc0 + acc1/4 + acc2/16 +
 //    acc3 - sum_k q (all exact integers), rescales and stores.
 template <int kMode, int kBits, int kDepth, int kR, int kLine>
-__global__ void __launch_bounds__(256) gemv_stream_kernel(GemvParams p, int groups_per_block,
+__global__ void __launch_bounds__(64 * kStreamWaves) gemv_stream_kernel(GemvParams p, int groups_per_block,
                                                           int xcd_order) {
-    constexpr int kThreads = 256;
+    constexpr int kThreads = 64 * kStreamWaves;
     constexpr bool kFull = kLine != 0;  // whole-line loads, permuted through LDS
     constexpr bool kShift = kLine == 2;  // odd rows one k tile behind (M <= 8)
     static_assert(!kFull || kR == 1, "whole-line mode streams one 16-row tile per wave item");
@@ -487,7 +512,7 @@ __global__ void __launch_bounds__(256) gemv_stream_kernel(GemvParams p, int grou
     const int ntiles = (K + 255) >> 8;           // 256-wide k tiles per row tile
     const int Kpad = ntiles << 8;
     const int vtiles = kShift ? ntiles + 1 : ntiles;  // tiles streamed per row tile
-    constexpr int GS = 64 * kR;                  // rows per group: 4 waves x kR x 16
+    constexpr int GS = 16 * kStreamWaves * kR;   // rows per group: kR 16-row tiles per wave
     const int G = (N + GS - 1) / GS;
     const int g0 = bx * groups_per_block;
     const int g1 = min(g0 + groups_per_block, G);
@@ -695,7 +720,7 @@ __global__ void __launch_bounds__(256) gemv_stream_kernel(GemvParams p, int grou
     // whole-line mode: this wave's 2 KB LDS window; lane (row, chunk c8) at row 128 +
     // 16 (c8 ^ ((row >> 1) & 7)), so both the line-wise writes and the tile-wise reads
     // of 16 lanes cover all 64 banks once
-    __shared__ __attribute__((aligned(16))) uint8_t s_perm[kFull ? 4 : 1][kFull ? 2048 : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t s_perm[kFull ? kStreamWaves : 1][kFull ? 2048 : 16];
     uint8_t *perm = &s_perm[kFull ? wave : 0][0];
     const int wrow = lane >> 3, wc8 = lane & 7;  // write: rows wrow (+8), chunk wc8
     const uint32_t woff0 = (uint32_t)wrow * 128u + 16u * (uint32_t)(wc8 ^ ((wrow >> 1) & 7));
@@ -815,23 +840,6 @@ __global__ void __launch_bounds__(256) gemv_stream_kernel(GemvParams p, int grou
 // the classic kernel's codes [M][K] (gfx950 has 160 KB of LDS per CU; the static
 // arrays take 4.2 KB)
 constexpr int64_t kGemvMaxLds = 144 * 1024;
-// streaming kernel: 16-byte weight loads in flight per lane, and blocks per CU
-#ifndef BL_STREAM_DEPTH
-#define BL_STREAM_DEPTH 8
-#endif
-#ifndef BL_STREAM_BLOCKS_PER_CU
-#define BL_STREAM_BLOCKS_PER_CU 2
-#endif
-#ifndef BL_STREAM_ROWS
-#define BL_STREAM_ROWS 1
-#endif
-#ifndef BL_STREAM_XCD
-#define BL_STREAM_XCD 1
-#endif
-constexpr int kStreamDepth = BL_STREAM_DEPTH;
-constexpr int kStreamBlocksPerCu = BL_STREAM_BLOCKS_PER_CU;
-constexpr int kStreamRows = BL_STREAM_ROWS;      // 16-row tiles per wave item
-constexpr int kStreamXcdOrder = BL_STREAM_XCD;  // problem-per-XCD block order
 constexpr int64_t kStreamLds = 63 * 1024;         // dynamic LDS (static use is < 1 KB)
 
 // the int8 codes [M][K]
@@ -860,12 +868,12 @@ hipError_t launch_cfg(const GemvParams &p, int mode, int64_t batch, hipStream_t 
 // bias (4 bytes, if any) and M staged outputs of ysz bytes
 size_t stream_lds_bytes(int64_t M, int64_t K, bool bias, int ysz, int64_t gpb) {
     return (size_t)((M + 1) * ((K + 255) / 256 * 256)) +
-           (size_t)gpb * 64 * kStreamRows * ((bias ? 4 : 0) + M * ysz);
+           (size_t)gpb * 16 * kStreamWaves * kStreamRows * ((bias ? 4 : 0) + M * ysz);
 }
 
 template <int kDepth>
 hipError_t launch_stream(const GemvParams &p, int mode, dim3 grid, int gpb, hipStream_t s) {
-    const dim3 block(256);
+    const dim3 block(64 * kStreamWaves);
     const int xo = kStreamXcdOrder && (grid.x * grid.y) % 8 == 0;
     const size_t lds = stream_lds_bytes(p.M, p.K, p.bias != nullptr, p.y_dtype == 1 ? 2 : 4, gpb);
     // whole-line loads when every row is a whole number of 128-byte lines, or (at most
@@ -935,11 +943,12 @@ hipError_t launch_gemv(const FwdArgs &a, bool fused, void *, hipStream_t s) {
     p.w_bstride = a.N * (a.K / 4);
     p.y_bstride = a.M * a.N * (a.y_dtype == 1 ? 2 : 4);
     const int mode = fused ? (a.x_raw_bf16 ? kRawBf16 : kRawF32) : (a.bits == 8 ? kInt8 : kInt4);
-    // many 64-row groups per launch: the streaming kernel, two blocks per CU, each block
-    // a contiguous run of one problem's groups
+    // at least four 16-row tiles per streaming wave: the streaming kernel, each block a
+    // contiguous run of one problem's row groups
     const int64_t target = kStreamBlocksPerCu * (int64_t)device_cus();
-    if (a.batch * ((a.N + 63) / 64) >= 4 * target) {
-        const int64_t G = (a.N + 64 * kStreamRows - 1) / (64 * kStreamRows);
+    if (a.batch * ((a.N + 15) / 16) >= 4 * target * kStreamWaves) {
+        const int64_t GSr = 16 * kStreamWaves * kStreamRows;  // rows per group
+        const int64_t G = (a.N + GSr - 1) / GSr;
         const int64_t bpp = std::max<int64_t>(1, std::min<int64_t>(G, target / a.batch));
         int64_t gpb = (G + bpp - 1) / bpp;
         // the block's bias rows and staged outputs share LDS with the codes (64 KB in all)
