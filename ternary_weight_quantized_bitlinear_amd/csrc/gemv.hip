@@ -519,7 +519,18 @@ __global__ void __launch_bounds__(64 * kStreamWaves) gemv_stream_kernel(GemvPara
     if (g0 >= G) return;  // whole block, before any barrier
     const int items = g1 - g0;
     const int r16 = lane & 15, chunk = lane >> 4;
-    const int F = items * vtiles;                // this wave's tiles
+    // The block's row items (kR 16-row tiles each, item i at rows g0 GS + 16 kR i) are
+    // shared out among its waves: wave w first takes items w, w + W, ... (P of them,
+    // enough that the loads issued before the prologue's barrier never need more),
+    // then claims the next unclaimed item from an LDS counter each time it starts one,
+    // so that waves the memory system serves faster take more items.
+    const int T = items * kStreamWaves;
+    const int P = kDepth / vtiles + 1;
+    __shared__ int s_next;                       // the block's next unclaimed item
+    __shared__ int s_fifo[kStreamWaves][16];     // each wave's items, in load order
+    // (a wave's loads run at most kDepth + 4 tiles, so at most kDepth + 5 items, ahead
+    // of its consumption, and each FIFO entry is read before it is written again)
+    static_assert(kDepth + 6 <= 16, "item FIFO too short for the ring depth");
 
     // ---- activation loads first (they retire before the weights)
     constexpr bool kRaw = kMode == kRawBf16 || kMode == kRawF32;
@@ -542,9 +553,10 @@ __global__ void __launch_bounds__(64 * kStreamWaves) gemv_stream_kernel(GemvPara
                                 : (uint32_t)r16 * kw + (uint32_t)chunk * 16u;
     const bool odd_row = kShift && (lane & 8) != 0;
     constexpr uint32_t kPast = 0x80000000u;  // beyond any buffer: loads return zeros
-    // next load's first row tile: wave w owns rows [g GS + 16 kR w, +16 kR) of group g
+    // next load: tile lt of item pitem (the pk-th item of this wave), at row offset lso
+    int lt = 0, pk = 0, pitem = wave;
     uint32_t lso = ((uint32_t)g0 * GS + (uint32_t)wave * 16u * kR) * kw;
-    int lt = 0, lg = 0;  // next load's (tile, item)
+    if (lane == 0) s_fifo[wave][0] = wave;
     struct Tile { v4i w[kR]; };
     auto next_load = [&]() __attribute__((always_inline)) {
         // the whole offset goes in the VGPR operand, whose range check is what makes
@@ -555,13 +567,29 @@ __global__ void __launch_bounds__(64 * kStreamWaves) gemv_stream_kernel(GemvPara
         const uint32_t opair = (int)pair + 1 == (vtiles >> 1) ? 0u : pair + 1u;
         const uint32_t so = kFull ? lso + 128u * (odd_row ? opair : pair) + 8u * kw * (uint32_t)(lt & 1)
                                   : lso + 64u * (uint32_t)lt;
-        const bool live = lg < items;
+        const bool live = pitem < T;
         Tile t;
 #pragma unroll
         for (int j = 0; j < kR; ++j)
             t.w[j] = __builtin_amdgcn_raw_buffer_load_b128(
                 wsrc, voff + (live ? so + 16u * kw * j : kPast), 0, kFull ? 2 : 0);
-        if (++lt == vtiles) { lt = 0; ++lg; lso += (uint32_t)GS * kw; }
+        if (++lt == vtiles) {  // next item: fixed, claimed, or (once past the end) none
+            lt = 0;
+            ++pk;
+            int nid = pitem;
+            if (pitem < T) {
+                if (pk < P) {
+                    nid = wave + kStreamWaves * pk;
+                } else {
+                    int v = 0;
+                    if (lane == 0) v = atomicAdd(&s_next, 1);
+                    nid = __builtin_amdgcn_readfirstlane(v);
+                }
+            }
+            pitem = nid;
+            if (lane == 0) s_fifo[wave][pk & 15] = nid;
+            lso = ((uint32_t)g0 * GS + (uint32_t)(nid < T ? nid : 0) * 16u * kR) * kw;
+        }
         return t;
     };
     Tile ring[kDepth];
@@ -570,6 +598,7 @@ __global__ void __launch_bounds__(64 * kStreamWaves) gemv_stream_kernel(GemvPara
 
     // ---- prologue: per-token absmax, scale, codes into LDS, code sums, bias rows
     if (tid < kMaxM) { s_amax[tid] = 0u; s_sum[tid] = 0; }
+    if (tid == 0) s_next = P * kStreamWaves;
     float *s_bias = reinterpret_cast<float *>(xl + (size_t)(M + 1) * Kpad);
     // outputs of the block's rows, [M][items * GS] in the output type, written to Y
     // row-contiguously at the end (the row tiles' own stores would be 32-byte pieces)
@@ -710,7 +739,8 @@ __global__ void __launch_bounds__(64 * kStreamWaves) gemv_stream_kernel(GemvPara
     for (int j = 0; j < kR; ++j)
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc[j][i] = pre[j][i] = v4i{0, 0, 0, 0};
-    int ug = 0, ut = 0;  // tile being consumed (uniform)
+    int ci = 0, citem = wave, ut = 0;  // tile ut of item citem (this wave's ci-th) is next
+    bool cdone = false;
     // Ring slots are taken and refilled kIssue at a time: the loads of consecutive k
     // tiles of a row (the two 64-byte halves of its 128-byte lines) then reach the
     // memory system back to back, which measured 2.5-3% faster than one at a time.
@@ -730,7 +760,7 @@ __global__ void __launch_bounds__(64 * kStreamWaves) gemv_stream_kernel(GemvPara
     };
     Tile pend;  // whole-line mode: the second tile of the last permuted pair
 #pragma unroll 1
-    for (int fb = 0; fb < F; fb += kDepth) {
+    while (!cdone) {
 #pragma unroll
         for (int d = 0; d < kDepth; ++d) {
             if (d % kIssue == 0) {
@@ -753,7 +783,7 @@ __global__ void __launch_bounds__(64 * kStreamWaves) gemv_stream_kernel(GemvPara
             } else {
                 wt = hold[d % kIssue];
             }
-            if (fb + d >= F) continue;  // uniform: past this wave's last tile
+            if (cdone) continue;  // uniform: past this wave's last item
             // shifted mode: the k tile of virtual tile ut for A rows 0-7 (even output
             // rows) and 8-15 (odd ones), or the zero row where the weights are the
             // partner row's
@@ -784,7 +814,7 @@ __global__ void __launch_bounds__(64 * kStreamWaves) gemv_stream_kernel(GemvPara
             if (++ut == vtiles) {  // row tiles done: epilogue (uniform branch)
 #pragma unroll
                 for (int j = 0; j < kR; ++j) {
-                    const int nrow = (g0 + ug) * GS + (wave * kR + j) * 16 + r16;
+                    const int nrow = g0 * GS + (citem * kR + j) * 16 + r16;
                     v4i dd[4];
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
@@ -813,7 +843,9 @@ __global__ void __launch_bounds__(64 * kStreamWaves) gemv_stream_kernel(GemvPara
                     }
                 }
                 ut = 0;
-                ++ug;
+                ++ci;
+                citem = __builtin_amdgcn_readfirstlane(s_fifo[wave][ci & 15]);
+                cdone = citem >= T;
             }
         }
     }
