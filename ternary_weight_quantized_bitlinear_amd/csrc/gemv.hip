@@ -30,7 +30,10 @@
 // plain variant reads int8 or int4 codes.  The activation loads are issued first and
 // every weight load of the wave right after, so the weights are in flight while
 // the prologue runs (vector-memory counters retire in order: the prologue's waits
-// then never wait on the weights).
+// then never wait on the weights).  int8 codes go straight from memory into LDS
+// (global_load_lds), all of them before the weights and with one wait for both, in
+// natural order with rows padded by 16 bytes (the 16 tokens' reads of one k then
+// fall on distinct banks); the main loop applies the k-interleave on reading.
 //
 // Epilogue.  The waves' 16x16 partial tiles are summed through LDS; the first wave
 // applies f = gamma/s (int8) or s*gamma (int4), bias, ReLU^2, and stores.
@@ -69,6 +72,20 @@ __device__ __forceinline__ int dot4(uint32_t a, uint32_t b, int c) {
     return __builtin_amdgcn_sdot4((int)a, (int)b, c, false);
 }
 
+
+// 16 bytes per lane from global memory straight into LDS: lane i's bytes land at
+// lds_dst + 16 i (lds_dst the same in every active lane).  Inline asm so that the
+// compiler does not put later LDS reads behind a full vmcnt wait; the kernel waits
+// for these loads itself (vmcnt(0) and a barrier) before reading LDS.  The
+// instruction has no register result, so no load in flight can overwrite a register.
+__device__ __forceinline__ void lds_dma16(const void *src, void *lds_dst) {
+    const uint32_t lds = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)lds_dst);
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(src), "s"(lds)
+                 : "memory", "m0");
+}
 
 template <int kMode> struct RawWords { static constexpr int n = kMode == kRawF32 ? 4 : kMode == kRawBf16 ? 2 : 1; };
 
@@ -206,6 +223,8 @@ __global__ void __launch_bounds__(kWaves * 64) gemv_kernel(GemvParams p) {
                         : kMode == kInt8 ? K : K / 2;
     const int gbytes = row_bytes / ngroups;  // bytes per group: 64, 32, 16 or 8
     const uint8_t *xbase = static_cast<const uint8_t *>(p.x);
+    constexpr bool kDma = kMode == kInt8;  // int8 codes: DMA into LDS, natural order
+    const int S = kDma ? K + 16 : K;       // LDS row stride
     uint4 xg0[kWpg], xg1[kWpg];
     // quantized codes: the (token, group) pairs t = tid + i kThreads of all M rows are
     // one index space; the first kPre of this thread's groups are loaded here, before
@@ -216,6 +235,15 @@ __global__ void __launch_bounds__(kWaves * 64) gemv_kernel(GemvParams p) {
     if (kRaw) {
         load_group<kMode>(xbase, row_bytes, gbytes, ngroups, 0, tid, xg0);
         load_group<kMode>(xbase, row_bytes, gbytes, ngroups, 0, tid + kThreads, xg1);
+    } else if (kDma) {
+        // row m's 1 KB pieces j (lanes past K idle): wave w issues pieces w, w + nw, ...
+        const int R = (K + 1023) >> 10;
+#pragma unroll 1
+        for (int q = wave; q < M * R; q += kWaves) {
+            const int m = q / R, j = q - m * R;
+            const int col = 1024 * j + 16 * lane;
+            if (col < K) lds_dma16(xbase + (size_t)m * K + col, xl + (size_t)m * S + 1024 * j);
+        }
     } else {
 #pragma unroll
         for (int i = 0; i < kPre; ++i) {
@@ -298,6 +326,12 @@ __global__ void __launch_bounds__(kWaves * 64) gemv_kernel(GemvParams p) {
                 quantize_store<kMode, kBits>(r, sc, xrow_m, g);
             }
         }
+    } else if (kDma) {
+        if (tid < M) {
+            const float sc = p.act_scale[p.gran == 1 ? 0 : tid];
+            s_f[tid] = gamma / sc;
+        }
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the codes (and the weights) landed
     } else {
 #pragma unroll
         for (int i = 0; i < kPre; ++i) {
@@ -332,7 +366,7 @@ __global__ void __launch_bounds__(kWaves * 64) gemv_kernel(GemvParams p) {
     v4i acc = v4i{0, 0, 0, 0}, acc1 = v4i{0, 0, 0, 0}, accs = v4i{0, 0, 0, 0};
     const v4i ones = v4i{0x01010101, 0x01010101, 0x01010101, 0x01010101};
     const bool tok_ok = r16 < M;  // this lane's activation row (token) exists
-    const uint8_t *xrow = xl + (size_t)(tok_ok ? r16 : 0) * K;
+    const uint8_t *xrow = xl + (size_t)(tok_ok ? r16 : 0) * S;
     auto run_batch = [&](int t0) __attribute__((always_inline)) {
         v4i af[kMaxTilesPerWave][4];
 #pragma unroll
@@ -343,7 +377,12 @@ __global__ void __launch_bounds__(kWaves * 64) gemv_kernel(GemvParams p) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const uint4 q = *reinterpret_cast<const uint4 *>(xrow + kb + 16 * j);
-                af[i][j] = ok ? v4i{(int)q.x, (int)q.y, (int)q.z, (int)q.w} : v4i{0, 0, 0, 0};
+                uint32_t il[4] = {q.x, q.y, q.z, q.w};
+                if (kDma) {  // natural order -> k-interleaved
+                    const uint32_t nat[4] = {q.x, q.y, q.z, q.w};
+                    interleave16(nat, il);
+                }
+                af[i][j] = ok ? v4i{(int)il[0], (int)il[1], (int)il[2], (int)il[3]} : v4i{0, 0, 0, 0};
             }
         }
 #pragma unroll
@@ -874,8 +913,8 @@ __global__ void __launch_bounds__(64 * kStreamWaves) gemv_stream_kernel(GemvPara
 constexpr int64_t kGemvMaxLds = 144 * 1024;
 constexpr int64_t kStreamLds = 63 * 1024;         // dynamic LDS (static use is < 1 KB)
 
-// the int8 codes [M][K]
-size_t lds_bytes(int64_t M, int64_t K, int) { return (size_t)(M * K); }
+// the int8 codes [M][K] (int8 codes mode: rows padded by 16 bytes)
+size_t lds_bytes(int64_t M, int64_t K, int mode) { return (size_t)(M * (mode == kInt8 ? K + 16 : K)); }
 
 template <int kWaves, int kT>
 hipError_t launch_cfg(const GemvParams &p, int mode, int64_t batch, hipStream_t s) {
