@@ -479,9 +479,9 @@ def _fwht_rows(x, b):
 def leg_stack(torch, bl, steps=10, layers=30, batch=16):
     """The 2B-shaped decode stack: 30 blocks of QKV 2560->7680, O 2560->2560, up
     2560->6912 (+ReLU^2), down 6912->2560, batch 16 tokens, seed-fixed weights.  Per
-    block: RMS norm fused with the quantization of h -> QKV on those codes (Q,K rows; V
-    rows, whose output feeds O) -> O -> residual + RMS norm + quantization -> up -> down
-    -> residual; O and down quantize their bf16 inputs themselves.  One step = all 30
+    block: RMS norm fused with the quantization of h -> Q, K, V on those codes in one
+    call (V feeds O) -> O -> residual + RMS norm + quantization -> up -> down ->
+    residual; O and down quantize their bf16 inputs themselves.  One step = all 30
     blocks for the 16 tokens, the K steps in one graph."""
     import workloads
     dev = torch.device("cuda:0")
@@ -496,6 +496,9 @@ def leg_stack(torch, bl, steps=10, layers=30, batch=16):
             lw[name] = bl.quantize_weights(Wd)
             wbytes += c.size // 4
             del Wd
+        # the QKV tensor (one gamma) as three 2560-row parts of one input
+        pq, gq = lw["qkv"]
+        lw["qkv3"] = (pq.view(3, H, pq.shape[1]), gq.expand(3).contiguous())
         W.append(lw)
     torch.cuda.synchronize()
     x0 = torch.from_numpy(workloads.stack_input(seed=3, m=batch).view(np.int16)).to(dev).view(
@@ -504,8 +507,8 @@ def leg_stack(torch, bl, steps=10, layers=30, batch=16):
     h = torch.empty_like(x)
     hq = torch.empty((batch, H), dtype=torch.int8, device=dev)
     hs = torch.empty((batch,), dtype=torch.float32, device=dev)
-    qk = torch.empty((batch, 2 * H), dtype=torch.bfloat16, device=dev)
-    v = torch.empty((batch, H), dtype=torch.bfloat16, device=dev)
+    qkv = torch.empty((3, batch, H), dtype=torch.bfloat16, device=dev)
+    v = qkv[2]
     o = torch.empty((batch, H), dtype=torch.bfloat16, device=dev)
     u = torch.empty((batch, workloads.FFN), dtype=torch.bfloat16, device=dev)
     d = torch.empty((batch, H), dtype=torch.bfloat16, device=dev)
@@ -514,10 +517,9 @@ def leg_stack(torch, bl, steps=10, layers=30, batch=16):
         x.copy_(x0)
         delta = None
         for lw in W:
-            pq, gq = lw["qkv"]
+            pq3, gq3 = lw["qkv3"]
             bl.rmsnorm_quantize(x, delta, out=(h, hq, hs))
-            bl.forward(hq, hs, pq[:2 * H], gq, out=qk)
-            bl.forward(hq, hs, pq[2 * H:], gq, out=v)
+            bl.forward_multi(hq, hs, pq3, gq3, out=qkv)  # Q, K, V: one call, V = qkv[2]
             bl.forward_fused(v, *lw["o"], out=o)
             bl.rmsnorm_quantize(x, o, out=(h, hq, hs))
             bl.forward(hq, hs, *lw["up"], epilogue="relu2", out=u)
@@ -536,7 +538,7 @@ def leg_stack(torch, bl, steps=10, layers=30, batch=16):
     ms /= steps
     return {"layers": layers, "batch": batch, "ms_per_step": ms, "tokens_per_s": batch / (ms * 1e-3),
             "weight_bytes_per_step": wbytes, "weight_gbs": wbytes / (ms * 1e-3) / 1e9,
-            "library_calls_per_step": layers * 7 + 1, "output_finite": finite}
+            "library_calls_per_step": layers * 6 + 1, "output_finite": finite}
 
 
 def leg_parity_layer(torch, bl, reps=200):

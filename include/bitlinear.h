@@ -214,6 +214,28 @@ bl_status bitlinear_forward_fused_batched(const void *X, bl_dtype x_dtype, int b
                                           size_t workspace_bytes, void *stream);
 
 /*
+ * Several BitLinear projections of one quantized input in one launch where the shape
+ * allows (decode-sized M), e.g. a block's query, key and value projections ("BitNet
+ * 2B4T Guide", "End-to-End PyTorch Implementation": each is a BitLinear of the same
+ * normalized input).  Part p computes exactly what bitlinear_forward computes on
+ *   Xq, act_scale (shared), W_packed + p*N*K/4 bytes, gamma[p], bias + p*N (if bias),
+ *   Y + p*M*N elements,
+ * i.e. W_packed is [parts][N][K/4], gamma [parts], bias [parts][N] or NULL, Y
+ * [parts][M][N], all contiguous: each part's output is a contiguous [M][N] matrix.
+ * Same equations and citations as bitlinear_forward.  A tensor quantized as one
+ * weight (one gamma) and split into equal row blocks passes its gamma once per part.
+ * 1 <= parts <= 65535; per-part W and Y strides must be multiples of 16 bytes.
+ * workspace: >= bitlinear_workspace_size(BL_OP_FORWARD, M, N, K, bits, gran) bytes
+ * (shapes that need more than one launch run the parts one after another on
+ * `stream`, reusing it).
+ */
+bl_status bitlinear_forward_multi(const void *Xq, int bits, const float *act_scale, bl_gran gran,
+                                  const uint8_t *W_packed, const float *gamma, const float *bias,
+                                  int64_t parts, int64_t M, int64_t N, int64_t K, bl_epi epi,
+                                  void *Y, bl_dtype y_dtype, void *workspace,
+                                  size_t workspace_bytes, void *stream);
+
+/*
  * Glue between the BitLinear layers of a transformer block, outside the BitLinear
  * steps themselves: residual add and RMS normalisation of bf16 rows ("BitNet 2B4T
  * Guide", "3. Sub-Layer Normalization (SubLN)", and the block of its "End-to-End

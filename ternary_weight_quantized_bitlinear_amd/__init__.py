@@ -13,6 +13,7 @@ The functions mirror the C entry points:
 * :func:`forward`           -> ``bitlinear_forward``
 * :func:`forward_fused`     -> ``bitlinear_forward_fused``
 * :func:`forward_fused_batched` -> ``bitlinear_forward_fused_batched``
+* :func:`forward_multi`     -> ``bitlinear_forward_multi`` (several projections of one input)
 * :func:`rmsnorm`           -> ``bitlinear_rmsnorm`` (glue between layers)
 * :func:`rmsnorm_quantize`  -> ``bitlinear_rmsnorm_quantize`` (glue + next layer's quantizer)
 * :func:`backward`          -> ``bitlinear_backward`` (straight-through-estimator gradients)
@@ -62,6 +63,8 @@ def lib() -> ctypes.CDLL:
                                               SZ, P]
         L.bitlinear_forward_fused_batched.argtypes = [P, I, I, I, F, P, P, P, I64, I64, I64, I64,
                                                       I, P, I, P, SZ, P]
+        L.bitlinear_forward_multi.argtypes = [P, I, P, I, P, P, P, I64, I64, I64, I64, I, P, I, P,
+                                              SZ, P]
         L.bitlinear_rmsnorm.argtypes = [P, P, P, I64, I64, F, P]
         L.bitlinear_rmsnorm_quantize.argtypes = [P, P, P, I64, I64, F, I, I, F, P, P, P, SZ, P]
         L.bitlinear_quantize_weights_rotated.argtypes = [P, I, I64, I64, F, P, P, P, SZ, P]
@@ -79,7 +82,7 @@ def lib() -> ctypes.CDLL:
         L.bitlinear_version.restype = I
         for n in ("bitlinear_quantize_weights", "bitlinear_quantize_acts", "bitlinear_forward",
                   "bitlinear_forward_fused", "bitlinear_forward_fused_batched",
-                  "bitlinear_rmsnorm", "bitlinear_rmsnorm_quantize",
+                  "bitlinear_forward_multi", "bitlinear_rmsnorm", "bitlinear_rmsnorm_quantize",
                   "bitlinear_quantize_weights_rotated", "bitlinear_quantize_acts_rotated",
                   "bitlinear_backward"):
             getattr(L, n).restype = I
@@ -283,6 +286,25 @@ def forward_fused_batched(X, packed, gamma, bits: int = 8, gran="token", eps: fl
         _ptr(X), _dtype_code(X), bits, g, eps, _ptr(packed), _ptr(gamma), _ptr(bias), B, M, N, K,
         _epi_code(epilogue), _ptr(out), _dtype_code(out), _ptr(ws), wsb,
         _stream(X.device, stream)))
+    return out
+
+
+def forward_multi(Xq, act_scale, packed, gamma, bits: int = 8, gran="token", bias=None,
+                  epilogue=None, out_dtype=None, workspace=None, stream=None, out=None):
+    """`parts` projections of one quantized input: Xq [M, K] codes, packed [P, N, K/4],
+    gamma [P], bias [P, N] or None -> Y [P, M, N]; part p is forward(Xq, act_scale,
+    packed[p], gamma[p:p+1], ...)."""
+    torch = _torch()
+    M = Xq.shape[0]
+    K = Xq.shape[1] * (1 if bits == 8 else 2)
+    Pn, N = packed.shape[0], packed.shape[1]
+    g = _gran_code(gran)
+    if out is None:
+        out = torch.empty((Pn, M, N), dtype=out_dtype or torch.float32, device=Xq.device)
+    ws, wsb = _workspace(workspace_size(BL_OP_FORWARD, M, N, K, bits, g), Xq.device, workspace)
+    _check(lib().bitlinear_forward_multi(
+        _ptr(Xq), bits, _ptr(act_scale), g, _ptr(packed), _ptr(gamma), _ptr(bias), Pn, M, N, K,
+        _epi_code(epilogue), _ptr(out), _dtype_code(out), _ptr(ws), wsb, _stream(Xq.device, stream)))
     return out
 
 

@@ -435,6 +435,47 @@ bl_status bitlinear_forward_fused_batched(const void *X, bl_dtype x_dtype, int b
     return ok();
 }
 
+bl_status bitlinear_forward_multi(const void *Xq, int bits, const float *act_scale, bl_gran gran,
+                                  const uint8_t *W_packed, const float *gamma, const float *bias,
+                                  int64_t parts, int64_t M, int64_t N, int64_t K, bl_epi epi,
+                                  void *Y, bl_dtype y_dtype, void *workspace,
+                                  size_t workspace_bytes, void *stream) {
+    static const char fn[] = "bitlinear_forward_multi";
+    if (!Xq || !act_scale) return fail(BL_EINVAL, "%s: null pointer", fn);
+    if (parts < 1 || parts > 65535)
+        return fail(BL_ESHAPE, "%s: parts=%lld must be in [1, 65535]", fn, (long long)parts);
+    CHECK(check_forward_common(fn, bits, gran, W_packed, gamma, bias, M, N, K, epi, Y, y_dtype));
+    if (!aligned(Xq, 16) || !aligned(act_scale, 4))
+        return fail(BL_EALIGN, "%s: Xq needs 16-byte, act_scale 4-byte alignment", fn);
+    // byte strides between parts; every part's pointers keep the single-call alignment
+    const int64_t ws_ = N * (K / 4);
+    const int64_t ys = M * N * (y_dtype == BL_BF16 ? 2 : 4);
+    if (parts > 1 && (ws_ % 16 != 0 || ys % 16 != 0))
+        return fail(BL_EALIGN, "%s: per-part strides (W %lld, Y %lld bytes) must be multiples of 16",
+                    fn, (long long)ws_, (long long)ys);
+    if (parts * ws_ >= (1ll << 40) || parts * ys >= (1ll << 40))
+        return fail(BL_ESHAPE, "%s: parts too large for these sizes", fn);
+    const size_t need = bitlinear_workspace_size(BL_OP_FORWARD, M, N, K, bits, gran);
+    if (need && (!workspace || workspace_bytes < need || !aligned(workspace, 256)))
+        return fail(BL_EWORKSPACE, "%s: need %zu bytes of 256-byte aligned workspace", fn, need);
+    (void)hipGetLastError();
+    if (bl::gemv_supports(M, K)) {
+        bl::FwdArgs a = make_args(Xq, 0, bits, act_scale, gran, 0.0f, W_packed, gamma, bias, M, N, K,
+                                  epi, Y, y_dtype);
+        a.batch = parts;
+        a.x_shared = 1;
+        return device(bl::launch_gemv(a, false, workspace, (hipStream_t)stream), fn);
+    }
+    for (int64_t b = 0; b < parts; ++b) {
+        const bl_status st = bitlinear_forward(Xq, bits, act_scale, gran, W_packed + b * ws_, gamma + b,
+                                               bias ? bias + b * N : nullptr, M, N, K, epi,
+                                               static_cast<uint8_t *>(Y) + b * ys, y_dtype, workspace,
+                                               workspace_bytes, stream);
+        if (st != BL_OK) return st;
+    }
+    return ok();
+}
+
 bl_status bitlinear_backward(const void *dY, const void *Xq, int bits, const float *act_scale,
                              bl_gran gran, const uint8_t *W_packed, const float *gamma,
                              const void *X, bl_dtype x_dtype, const void *W, bl_dtype w_dtype,

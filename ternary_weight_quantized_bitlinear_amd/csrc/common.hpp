@@ -202,6 +202,7 @@ struct FwdArgs {
     void *y;
     int y_dtype;           // 0 f32, 1 bf16, 2 i32
     int64_t batch = 1;     // independent problems laid out back to back (GEMV path)
+    int x_shared = 0;      // GEMV path: every problem reads the same xq and act_scale
     const int32_t *rowsum = nullptr;  // prepared activations: sum_k q[m][k] per token
 };
 

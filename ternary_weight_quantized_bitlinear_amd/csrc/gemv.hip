@@ -66,6 +66,7 @@ struct GemvParams {
     int y_dtype;
     // problem blockIdx.y starts this many bytes further on (0 for a single problem)
     int64_t x_bstride, w_bstride, y_bstride;
+    int64_t s_bstride;  // act_scale elements between problems (0: one shared input)
 };
 
 __device__ __forceinline__ int dot4(uint32_t a, uint32_t b, int c) {
@@ -190,7 +191,7 @@ __global__ void __launch_bounds__(kWaves * 64) gemv_kernel(GemvParams p) {
         p.w += b * p.w_bstride;
         p.gamma += b;
         if (p.bias) p.bias += b * p.N;
-        if (p.act_scale) p.act_scale += b * (p.gran == 1 ? 1 : p.M);
+        if (p.act_scale) p.act_scale += b * p.s_bstride;
         p.y = static_cast<uint8_t *>(p.y) + b * p.y_bstride;
     }
     extern __shared__ __attribute__((aligned(16))) uint8_t xl[];  // [M][K] int8, k-interleaved
@@ -541,7 +542,7 @@ __global__ void __launch_bounds__(64 * kStreamWaves) gemv_stream_kernel(GemvPara
         p.w += b * p.w_bstride;
         p.gamma += b;
         if (p.bias) p.bias += b * p.N;
-        if (p.act_scale) p.act_scale += b * (p.gran == 1 ? 1 : p.M);
+        if (p.act_scale) p.act_scale += b * p.s_bstride;
         p.y = static_cast<uint8_t *>(p.y) + b * p.y_bstride;
     }
     const int tid = threadIdx.x, lane = tid & 63;
@@ -1010,7 +1011,8 @@ hipError_t launch_gemv(const FwdArgs &a, bool fused, void *, hipStream_t s) {
     p.y = a.y;
     p.y_dtype = a.y_dtype;
     const int64_t xrow = fused ? (a.x_raw_bf16 ? 2 * a.K : 4 * a.K) : (a.bits == 8 ? a.K : a.K / 2);
-    p.x_bstride = a.M * xrow;
+    p.x_bstride = a.x_shared ? 0 : a.M * xrow;
+    p.s_bstride = a.x_shared ? 0 : (a.gran == 1 ? 1 : a.M);
     p.w_bstride = a.N * (a.K / 4);
     p.y_bstride = a.M * a.N * (a.y_dtype == 1 ? 2 : 4);
     const int mode = fused ? (a.x_raw_bf16 ? kRawBf16 : kRawF32) : (a.bits == 8 ? kInt8 : kInt4);

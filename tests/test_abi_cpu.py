@@ -23,7 +23,8 @@ def test_exports_every_header_function(L):
     names = bl.header_functions()
     assert set(names) == {
         "bitlinear_quantize_weights", "bitlinear_quantize_acts", "bitlinear_forward",
-        "bitlinear_forward_fused", "bitlinear_forward_fused_batched", "bitlinear_rmsnorm",
+        "bitlinear_forward_fused", "bitlinear_forward_fused_batched", "bitlinear_forward_multi",
+        "bitlinear_rmsnorm",
         "bitlinear_rmsnorm_quantize", "bitlinear_workspace_size", "bitlinear_status_string",
         "bitlinear_last_error", "bitlinear_version", "bitlinear_hadamard_block",
         "bitlinear_quantize_weights_rotated", "bitlinear_quantize_acts_rotated",
@@ -171,6 +172,30 @@ def test_forward_fused_batched_rejects(L):
     # prefill-sized problems run one by one and need the fused workspace
     assert call(M=2048) == bl.BL_EWORKSPACE
     assert L.bitlinear_last_error().decode().startswith("bitlinear_forward_fused_batched")
+
+
+def test_forward_multi_rejects(L):
+    f = L.bitlinear_forward_multi
+
+    def call(**kw):
+        a = dict(X=P(A), bits=8, s=P(A), gran=0, W=P(A), gamma=P(A), bias=None, parts=3, M=16,
+                 N=2560, K=2560, epi=0, Y=P(A), ydt=1, ws=None, wsb=0)
+        a.update(kw)
+        return f(a["X"], a["bits"], a["s"], a["gran"], a["W"], a["gamma"], a["bias"], a["parts"],
+                 a["M"], a["N"], a["K"], a["epi"], a["Y"], a["ydt"], a["ws"], a["wsb"], None)
+
+    assert call(parts=0) == bl.BL_ESHAPE
+    assert call(parts=65536) == bl.BL_ESHAPE
+    assert call(X=None) == bl.BL_EINVAL
+    assert call(s=None) == bl.BL_EINVAL
+    assert call(bits=5) == bl.BL_EINVAL
+    assert call(K=100) == bl.BL_ESHAPE
+    assert call(X=P(A + 4)) == bl.BL_EALIGN
+    # part 1 would start 4 bytes into a 16-byte line (N*K/4 = 4 bytes of weights)
+    assert call(N=1, K=16) == bl.BL_EALIGN
+    # a bf16 output row of 3 elements puts part 1's Y off 16-byte alignment
+    assert call(M=1, N=3, K=64) == bl.BL_EALIGN
+    assert L.bitlinear_last_error().decode().startswith("bitlinear_forward_multi")
 
 
 def test_rmsnorm_rejects(L):

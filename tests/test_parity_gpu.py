@@ -343,6 +343,53 @@ def test_forward_fused_batched(B, M, K, N, bits, gran, epi, ydt, xdt, with_bias)
         assert_y_matches(yh[b], acc_ref if ydt == "i32" else y_ref, ydt, "Y problem %d" % b)
 
 
+# several projections of one quantized input in one call (a block's Q, K, V): part p
+# against the oracle's forward of the shared codes with part p's weights
+@pytest.mark.parametrize("P,M,K,N,bits,gran,epi,ydt,with_bias", [
+    (3, 16, 2560, 2560, 8, "token", None, "bf16", False),   # the 2B block's Q, K, V
+    (2, 1, 256, 512, 8, "token", "relu2", "f32", True),
+    (4, 5, 640, 304, 4, "tensor", None, "i32", False),
+    (2, 16, 6912, 2560, 8, "tensor", "relu2", "bf16", True),
+    (3, 300, 256, 128, 8, "token", None, "f32", False),     # prefill-sized: one call per part
+    (3, 2, 512, 44000, 8, "token", None, "bf16", False),    # >= 8192 row tiles: streaming
+])
+def test_forward_multi(P, M, K, N, bits, gran, epi, ydt, with_bias):
+    say("forward_multi", dict(P=P, M=M, K=K, N=N, bits=bits, gran=gran, epi=epi, y=ydt,
+                              bias=with_bias))
+    g = oracle.PER_TOKEN if gran == "token" else oracle.PER_TENSOR
+    e = oracle.EPI_RELU2 if epi == "relu2" else oracle.EPI_NONE
+    tdt, odt = YD[ydt]
+    kind = "ternary" if N * K > 1 << 20 else "gauss"
+    X = _acts_case(M, K, seed=77)
+    xq_ref, s_ref = oracle.quantize_acts(X, bits=bits, gran=g)
+    Ws = [_weights_case(kind, N, K, seed=20 + p) for p in range(P)]
+    bias = (np.random.default_rng(P).standard_normal((P, N)).astype(np.float32)
+            if with_bias else None)
+    packed = torch.empty((P, N, K // 4), dtype=torch.uint8, device="cuda")
+    gamma = torch.empty((P,), dtype=torch.float32, device="cuda")
+    for p, W in enumerate(Ws):
+        bl.quantize_weights(to_dev(W), out=(packed[p], gamma[p:p + 1]))
+    y = bl.forward_multi(to_dev(xq_ref), to_dev(s_ref), packed, gamma, bits=bits, gran=gran,
+                         bias=to_dev(bias) if with_bias else None, epilogue=epi, out_dtype=tdt)
+    torch.cuda.synchronize()
+    yh = to_host(y)
+    for p, W in enumerate(Ws):
+        p_ref, g_ref, _ = oracle.quantize_weights(W)
+        assert_same_bytes(to_host(packed[p]), p_ref, "packed part %d" % p)
+        if M * N * K > 3e8:
+            ms, ns = sample_positions(M, N, 4096, p)
+            y_ref, acc_ref = oracle.forward_at(xq_ref, bits, s_ref, g, p_ref, g_ref, ms, ns,
+                                               bias=bias[p] if with_bias else None, epi=e,
+                                               y_dtype=odt if odt is not None else oracle.F32)
+            assert_y_matches(yh[p][ms, ns], acc_ref if ydt == "i32" else y_ref, ydt,
+                             "Y part %d (sampled)" % p)
+        else:
+            y_ref, acc_ref = oracle.forward(xq_ref, bits, s_ref, g, p_ref, g_ref,
+                                            bias=bias[p] if with_bias else None, epi=e,
+                                            y_dtype=odt if odt is not None else oracle.F32)
+            assert_y_matches(yh[p], acc_ref if ydt == "i32" else y_ref, ydt, "Y part %d" % p)
+
+
 # one very wide layer (2048 groups of 64 rows): the streaming kernel on a single problem
 @pytest.mark.parametrize("bits", [8, 4])
 @pytest.mark.parametrize("fused", [False, True])

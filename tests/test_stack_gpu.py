@@ -106,9 +106,8 @@ def _fused(h_dev, packed, gamma, p_ref, g_ref, epi, what):
 
 def test_stack_first_layers_parity():
     """The 2B stack at batch 16, layers 0 and 1, in the calls the benchmark makes: RMS
-    norm fused with the quantization of h, QKV on those codes (Q and K rows, then the V
-    rows, whose output feeds O), O, residual + RMS norm + quantization, up + ReLU^2 on
-    the codes, down, residual."""
+    norm fused with the quantization of h, Q, K and V on those codes in one call (V feeds
+    O), O, residual + RMS norm + quantization, up + ReLU^2 on the codes, down, residual."""
     H = workloads.HIDDEN
     x = workloads.stack_input(seed=3, m=16)
     xd = to_dev(x)
@@ -123,8 +122,15 @@ def test_stack_first_layers_parity():
         hh = to_host(h)
         _check_norm(x_in, d_in, to_host(xd), hh, "layer %d norm 1" % layer)
         pq, gq, pq_ref, gq_ref = w["qkv"]
-        _plain(hq, hs, hh, pq[:2 * H], gq, pq_ref[:2 * H], gq_ref, None, "layer %d QK" % layer)
-        v = _plain(hq, hs, hh, pq[2 * H:], gq, pq_ref[2 * H:], gq_ref, None, "layer %d V" % layer)
+        # Q, K and V in one call: three 2560-row parts of the one QKV tensor (one gamma)
+        qkv = bl.forward_multi(hq, hs, pq.view(3, H, pq.shape[1]), gq.expand(3).contiguous(),
+                               out_dtype=torch.bfloat16)
+        torch.cuda.synchronize()
+        for part, name in enumerate("QKV"):
+            y_ref, _, _, _ = oracle.bitlinear(hh, pq_ref[part * H:(part + 1) * H], gq_ref,
+                                              epi=oracle.EPI_NONE, y_dtype=oracle.BF16)
+            assert_same_bytes(to_host(qkv[part]), y_ref, "layer %d %s" % (layer, name))
+        v = qkv[2]
         po, go, po_ref, go_ref = w["o"]
         o = _fused(v, po, go, po_ref, go_ref, None, "layer %d O" % layer)
         x_in = to_host(xd)
