@@ -11,8 +11,9 @@
 // (v_rndne_f32), so the codes are exactly those of the definition.
 //
 // Per token: one 256-thread block per row; pass 1 reduces the row's absmax (wave
-// shuffles, then LDS across the 4 waves), pass 2 re-reads the row (an L2 hit) and
-// writes the codes.  Per tensor: a grid-wide absmax into the workspace (|x| is
+// shuffles, then LDS across the 4 waves), pass 2 writes the codes from the values
+// pass 1 kept in registers (a thread's first kAqRegGroups groups of 8; K <= 8192) or
+// re-reads the rest (an L2 hit).  Per tensor: a grid-wide absmax into the workspace (|x| is
 // non-negative, so its fp32 bits order like unsigned integers and atomicMax on the
 // bits is the float max), then the same pass 2 with that shared absmax.
 #include "common.hpp"
@@ -21,6 +22,7 @@ namespace bl {
 namespace {
 
 constexpr int kAqThreads = 256;
+constexpr int kAqRegGroups = 4;  // 8-element groups per thread kept from pass 1
 
 __device__ __forceinline__ float block_max(float v, float *red) {
     v = wave_max_abs(v);
@@ -44,11 +46,24 @@ aq_rows(const void *__restrict__ x, int64_t K, float eps, const uint32_t *__rest
                             : (const void *)(static_cast<const float *>(x) + m * K);
     const int64_t n8 = K / 8;
     float amax;
+    float keep[kAqRegGroups][8];  // per token: this thread's first groups, from pass 1
     if (kTensor) {
         amax = __uint_as_float(*tensor_amax);
     } else {
         float mx = 0.0f;
-        for (int64_t u = threadIdx.x; u < n8; u += kAqThreads) {
+#pragma unroll
+        for (int i = 0; i < kAqRegGroups; ++i) {  // all loads first, then the maxima
+            const int64_t u = threadIdx.x + (int64_t)i * kAqThreads;
+            if (u < n8) load8<kBf16>(row, u * 8, keep[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < kAqRegGroups; ++i) {
+            const int64_t u = threadIdx.x + (int64_t)i * kAqThreads;
+            if (u < n8)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) mx = fmaxf(mx, fabsf(keep[i][j]));
+        }
+        for (int64_t u = threadIdx.x + (int64_t)kAqRegGroups * kAqThreads; u < n8; u += kAqThreads) {
             float v[8];
             load8<kBf16>(row, u * 8, v);
 #pragma unroll
@@ -59,9 +74,17 @@ aq_rows(const void *__restrict__ x, int64_t K, float eps, const uint32_t *__rest
     const float a = fmaxf(amax, eps);
     const float s = kBits == 8 ? 127.0f / a : a / 7.0f;
     if (threadIdx.x == 0 && (!kTensor || m == 0)) scale[kTensor ? 0 : m] = s;
-    for (int64_t u = threadIdx.x; u < n8; u += kAqThreads) {
+    for (int64_t u = threadIdx.x, i = 0; u < n8; u += kAqThreads, ++i) {
         float v[8];
-        load8<kBf16>(row, u * 8, v);
+        if (!kTensor && i < kAqRegGroups) {
+#pragma unroll
+            for (int t = 0; t < kAqRegGroups; ++t)
+                if (t == i)
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) v[j] = keep[t][j];
+        } else {
+            load8<kBf16>(row, u * 8, v);
+        }
         if (kBits == 8) {
             uint2 o;
             o.x = q8(v[0], s) | (q8(v[1], s) << 8) | (q8(v[2], s) << 16) | (q8(v[3], s) << 24);
@@ -347,7 +370,8 @@ namespace {
 // grid-wide absmax of X into *amax (as float bits), for per-tensor scales
 hipError_t launch_tensor_amax(const void *x, int x_bf16, int64_t M, int64_t K, uint32_t *amax,
                               hipStream_t s) {
-    launch_zero_u32(amax, 1, s);
+    const hipError_t e = launch_zero_u32(amax, 1, s);
+    if (e != hipSuccess) return e;
     const int64_t n8 = M * K / 8;
     int g = (int)((n8 + kAqThreads * 4 - 1) / (kAqThreads * 4));
     if (g > 2048) g = 2048;
