@@ -731,7 +731,7 @@ def main():
                    "weight_sets": st["sets"],
                    "tokens_per_layer": 1, "hidden": 2560, "ffn": 6912,
                    "layers_per_launch": st["batch"], "weight_bytes_per_step": st["step_bytes"]},
-        "roofline": {"bound": "hbm", "kernel": "gemv_kernel (fused decode GEMV, batched)",
+        "roofline": {"bound": "hbm", "kernel": "gemv_stream_kernel (fused decode GEMV, 64 layers per launch)",
                      "achieved": round(alg, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(alg / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(),
