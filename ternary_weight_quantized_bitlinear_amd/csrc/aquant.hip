@@ -389,7 +389,10 @@ hipError_t launch_quantize_acts_prepared(const void *x, int x_bf16, int64_t M, i
                                          float *scale, int32_t *rowsum, void *ws,
                                          hipStream_t s) {
     uint32_t *amax = static_cast<uint32_t *>(ws);
-    if (gran == 1) launch_tensor_amax(x, x_bf16, M, K, amax, s);
+    if (gran == 1) {
+        const hipError_t e = launch_tensor_amax(x, x_bf16, M, K, amax, s);
+        if (e != hipSuccess) return e;
+    }
     const bool t = gran == 1;
 #define BL_PREP(BF, B, T) launch_rows_prep<BF, B, T>(x, M, K, eps, amax, xp, scale, rowsum, s)
     if (x_bf16) {
@@ -469,7 +472,10 @@ hipError_t launch_quantize_acts(const void *x, int x_bf16, int64_t M, int64_t K,
                                 int gran, float eps, void *xq, float *scale, void *ws,
                                 hipStream_t s) {
     uint32_t *amax = static_cast<uint32_t *>(ws);
-    if (gran == 1) launch_tensor_amax(x, x_bf16, M, K, amax, s);
+    if (gran == 1) {
+        const hipError_t e = launch_tensor_amax(x, x_bf16, M, K, amax, s);
+        if (e != hipSuccess) return e;
+    }
     const bool t = gran == 1;
     if (x_bf16) {
         if (bits == 8) t ? launch_rows<true, 8, true>(x, M, K, eps, amax, xq, scale, s)

@@ -69,10 +69,6 @@ struct GemvParams {
     int64_t s_bstride;  // act_scale elements between problems (0: one shared input)
 };
 
-__device__ __forceinline__ int dot4(uint32_t a, uint32_t b, int c) {
-    return __builtin_amdgcn_sdot4((int)a, (int)b, c, false);
-}
-
 
 // 16 bytes per lane from global memory straight into LDS: lane i's bytes land at
 // lds_dst + 16 i (lds_dst the same in every active lane).  Inline asm so that the
@@ -196,7 +192,6 @@ __global__ void __launch_bounds__(kWaves * 64) gemv_kernel(GemvParams p) {
     }
     extern __shared__ __attribute__((aligned(16))) uint8_t xl[];  // [M][K] int8, k-interleaved
     __shared__ float s_f[kMaxM];        // dequant factor per token
-    __shared__ float s_sc[kMaxM];       // activation scale per token
     __shared__ uint32_t s_amax[kMaxM];  // absmax bits per token (non-negative: uint order)
     __shared__ v4i s_acc[kWaves][64];
 
@@ -216,8 +211,6 @@ __global__ void __launch_bounds__(kWaves * 64) gemv_kernel(GemvParams p) {
     // only after (any earlier use would make the compiler wait for them, and
     // vector-memory loads retire in order, which would hold back the weights).
     constexpr bool kRaw = kMode == kRawBf16 || kMode == kRawF32;
-    constexpr bool kBf = kMode == kRawBf16;
-    constexpr int kXG = 2;  // groups per thread kept in registers
     // 16-byte words per group: fp32 4, bf16 2, int8 1, int4 1 (half used)
     constexpr int kWpg = RawWords<kMode>::n;
     const int row_bytes = kMode == kRawF32 ? 4 * K : kMode == kRawBf16 ? 2 * K

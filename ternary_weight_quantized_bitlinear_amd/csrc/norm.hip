@@ -60,7 +60,7 @@ rmsnorm_rows(uint16_t *__restrict__ x, const uint16_t *__restrict__ delta,
     __syncthreads();
 #pragma unroll
     for (int s = kNormThreads / 2; s > 0; s >>= 1) {
-        if (threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
+        if ((int)threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
         __syncthreads();
     }
     const double r = 1.0 / sqrt(red[0] / (double)K + (double)eps);
@@ -148,7 +148,7 @@ rmsnorm_quant_rows(uint16_t *__restrict__ x, const uint16_t *__restrict__ delta,
     __syncthreads();
 #pragma unroll
     for (int s = kNormThreads / 2; s > 0; s >>= 1) {
-        if (threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
+        if ((int)threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
         __syncthreads();
     }
     const double r = 1.0 / sqrt(red[0] / (double)K + (double)eps);
