@@ -642,6 +642,36 @@ def leg_pack(torch, bl, reps=10):
             "alg_bytes": alg}
 
 
+def leg_acts(torch, bl, reps=20):
+    """a2: per-token absmax activation quantization of bf16 X in HBM, at the prefill
+    shapes (2B: M=2048, K=2560 and 6912; 70B: M=4096, K=8192), int8 and int4 codes.
+    Algorithmic bytes: X read once (2MK), codes (MK or MK/2) and scales (4M) written."""
+    dev = torch.device("cuda:0")
+    out = {}
+    for M, K in ((2048, 2560), (2048, 6912), (4096, 8192)):
+        g = torch.Generator(device=dev)
+        g.manual_seed(5)
+        # two copies alternate, so the 67 MB of the 70B input is not read from the
+        # Infinity Cache on consecutive calls
+        Xs = [torch.randn((M, K), device=dev, generator=g).to(torch.bfloat16) for _ in range(2)]
+        for bits in (8, 4):
+            xq = torch.empty((M, K if bits == 8 else K // 2), dtype=torch.int8, device=dev)
+            sc = torch.empty((M,), dtype=torch.float32, device=dev)
+
+            def run():
+                for i in range(reps):
+                    bl.quantize_acts(Xs[i % 2], bits=bits, out=(xq, sc))
+
+            ms, _ = graph_time_ms(torch, run, replays=1)
+            ms /= reps
+            alg = 2 * M * K + (M * K if bits == 8 else M * K // 2) + 4 * M
+            out["%dx%d_int%d" % (M, K, bits)] = {
+                "us": round(ms * 1e3, 2), "gbs": round(alg / (ms * 1e-3) / 1e9, 1),
+                "frac": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "alg_bytes": alg}
+        del Xs
+    return out
+
+
 def cpu_baseline(x, W_up, W_dn, budget_s=12.0):
     """The oracle (single-threaded C, as it stands) on the same decode FFN step."""
     import oracle
@@ -674,7 +704,7 @@ def main():
     ap.add_argument("--batch", type=int, default=64, help="layers per streamed launch")
     ap.add_argument("--copies", type=int, default=64, help="weight copies of the chain leg")
     ap.add_argument("--chain-steps", type=int, default=2000)
-    ap.add_argument("--legs", default="decode,chain,single,c1,prefill,stack,c5,pack,backward,cpu")
+    ap.add_argument("--legs", default="decode,chain,single,c1,prefill,stack,c5,pack,acts,backward,cpu")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -696,6 +726,8 @@ def main():
             side["prefill"] = leg_prefill(torch, bl)
         if "pack" in legs:
             side["pack"] = leg_pack(torch, bl)
+        if "acts" in legs:
+            side["acts"] = leg_acts(torch, bl)
         if "c5" in legs:
             side["layer_70b"] = leg_70b(torch, bl)
         if "stack" in legs:
@@ -762,6 +794,9 @@ def main():
                           "int4_activations": pf["int4"]}
     if "pack" in legs:
         out["pack"] = leg_pack(torch, bl)
+    if "acts" in legs:
+        out["acts"] = {"workload": "per-token absmax quantization of bf16 X (a2), prefill shapes",
+                       "unit": "GB/s", "peak": HBM_PEAK_GBS, **leg_acts(torch, bl)}
     if "stack" in legs:
         out["stack_2b"] = {"workload": "30-layer BitNet-2B-shaped decode stack, batch 16: QKV, O, "
                                        "up (+ReLU^2), down per layer with RMS norm, residual and "

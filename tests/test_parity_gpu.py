@@ -290,6 +290,87 @@ def test_forward_deterministic():
     assert_same_bytes(to_host(p2), to_host(packed), "repeat pack")
 
 
+def _near_tie_acts(m, k, bits, seed=0):
+    """fp32 rows whose codes sit on rounding decisions: each row's absmax a is pinned at
+    column 0, and the other columns hold t = fl(h * s) for every half-integer h that
+    |x| <= a allows (s = fl(a / 7) for 4 bits, x = h / s8 with s8 = fl(127 / a) for 8
+    bits), and t's neighbours up to 3 ulps either side.  Scales with short mantissas
+    make some of these exact ties (round half to even decides)."""
+    rng = np.random.default_rng([seed, m, k, bits])
+    X = np.zeros((m, k), dtype=np.float32)
+    amaxes = [5.25, 1.0, 3.3, 0.0173, 1.0e4, 7.0, 0.4375, 123.456]
+    for r in range(m):
+        a = np.float32(amaxes[r % len(amaxes)] * (1.0 if r < len(amaxes) else rng.uniform(0.5, 2)))
+        vals = []
+        if bits == 4:
+            sc = np.float32(a) / np.float32(7.0)
+            hs = [h + 0.5 for h in range(-7, 7)]
+            base = [np.float32(np.float32(h) * sc) for h in hs]
+        else:
+            s8 = np.float32(127.0) / np.float32(a)
+            hs = [h + 0.5 for h in range(-127, 127, 7)]
+            base = [np.float32(np.float32(h) / s8) for h in hs]
+        for t in base:
+            v = t
+            for _ in range(3):
+                v = np.nextafter(v, np.float32(np.inf), dtype=np.float32)
+                vals.append(v)
+            v = t
+            for _ in range(3):
+                v = np.nextafter(v, np.float32(-np.inf), dtype=np.float32)
+                vals.append(v)
+            vals.append(t)
+        vals = [v for v in vals if abs(v) <= a]
+        rng.shuffle(vals)
+        n = min(len(vals), k - 1)
+        X[r, 0] = a if r % 2 == 0 else -a
+        X[r, 1:1 + n] = vals[:n]
+    return X
+
+
+# activation codes on rounding decisions: x / s (4 bits) or x * s (8 bits) at, and a
+# few ulps around, every half-integer, against the oracle's exact quotient and product;
+# through the quantizer, the fused GEMV prologue (M <= 4) and the streaming kernel's
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("gran", ["token", "tensor"])
+def test_quantize_acts_near_ties(bits, gran):
+    say("quantize_acts near ties", bits, gran)
+    g = oracle.PER_TOKEN if gran == "token" else oracle.PER_TENSOR
+    X = _near_tie_acts(16, 256, bits)
+    xq, s = bl.quantize_acts(to_dev(X), bits=bits, gran=gran)
+    torch.cuda.synchronize()
+    xq_ref, s_ref = oracle.quantize_acts(X, bits=bits, gran=g)
+    assert_same_bytes(bits32(to_host(s)), bits32(s_ref), "act_scale")
+    assert_same_bytes(to_host(xq), xq_ref, "activation codes")
+    # fused forward, M <= 4: quantization in the GEMV prologue; int32 accumulators
+    W = _weights_case("gauss", 64, 256, seed=3)
+    packed, gamma = bl.quantize_weights(to_dev(W))
+    p_ref, g_ref, _ = oracle.quantize_weights(W)
+    for m0 in (0, 4, 8):
+        Xm = np.ascontiguousarray(X[m0:m0 + 4])
+        y = bl.forward_fused(to_dev(Xm), packed, gamma, bits=bits, gran=gran, out_dtype=torch.int32)
+        torch.cuda.synchronize()
+        xq_m, s_m = oracle.quantize_acts(Xm, bits=bits, gran=g)
+        _, acc_ref = oracle.forward(xq_m, bits, s_m, g, p_ref, g_ref, y_dtype=oracle.F32)
+        assert_same_bytes(to_host(y), acc_ref, "fused accumulators rows %d.." % m0)
+    # streaming kernel (64 problems x 2048 rows): its prologue quantizes too
+    B, N = 64, 2048
+    Xb = np.stack([X[(4 * b) % 16:(4 * b) % 16 + 4] for b in range(B)])
+    Wb = _weights_case("gauss", N, 256, seed=4)
+    pb, gb = bl.quantize_weights(to_dev(Wb))
+    pbr, gbr, _ = oracle.quantize_weights(Wb)
+    packed_b = pb.unsqueeze(0).expand(B, N, 64).contiguous()
+    gamma_b = gb.expand(B).contiguous()
+    y = bl.forward_fused_batched(to_dev(Xb), packed_b, gamma_b, bits=bits, gran=gran,
+                                 out_dtype=torch.int32)
+    torch.cuda.synchronize()
+    yh = to_host(y)
+    for b in (0, 1, 2, 3):
+        xq_b, s_b = oracle.quantize_acts(Xb[b], bits=bits, gran=g)
+        _, acc_ref = oracle.forward(xq_b, bits, s_b, g, pbr, gbr, y_dtype=oracle.F32)
+        assert_same_bytes(yh[b], acc_ref, "streamed accumulators problem %d" % b)
+
+
 # batched fused forward: independent problems of one shape in one call
 @pytest.mark.parametrize("B,M,K,N,bits,gran,epi,ydt,xdt,with_bias", [
     (3, 1, 256, 512, 8, "token", "relu2", "f32", "f32", True),
