@@ -215,6 +215,16 @@ def test_forward_prefill_variants(gran, epi, ydt):
         _check_forward(300, 512, 260, bits, gran, epi, ydt, ydt != "i32", bits == 4)
 
 
+# few large tiles and a long K (the 128-wide tile path with one 4-wave block per tile):
+# both entry points, every output type, ragged last row / column tiles
+@pytest.mark.parametrize("M,K,N", [(300, 4096, 300), (512, 3072, 1000), (128, 3072, 128),
+                                   (1000, 6400, 520)])
+@pytest.mark.parametrize("ydt", ["f32", "bf16", "i32"])
+def test_forward_prefill_long_k(M, K, N, ydt):
+    _check_forward(M, K, N, 8, "token", None if ydt == "i32" else "relu2", ydt, ydt != "i32", False)
+    _check_forward(M, K, N, 8, "tensor", None, ydt, False, True, x_dtype="bf16")
+
+
 # full-size 2B shapes, sampled
 @pytest.mark.parametrize("shape,epi", [(workloads.SHAPE_UP, "relu2"), (workloads.SHAPE_DOWN, None)])
 @pytest.mark.parametrize("bits", [8, 4])
