@@ -196,6 +196,18 @@ def test_forward_decode_variants(gran, epi, ydt, fused):
                        kind="ternary")
 
 
+# fused forward of 5..16 bf16 tokens (the quantizer's own launch, then the GEMV on the
+# codes); bf16 inputs put many quotients exactly on rounding ties (x = a/2), which the
+# codes must break as defined
+@pytest.mark.parametrize("M", [5, 8, 11, 16])
+@pytest.mark.parametrize("K,N", [(256, 512), (2560, 2560), (640, 300), (1024, 4096)])
+@pytest.mark.parametrize("bits", [8, 4])
+def test_forward_fused_mid_m(M, K, N, bits):
+    _check_forward(M, K, N, bits, "token", "relu2", "f32", True, True, x_dtype="bf16")
+    _check_forward(M, K, N, bits, "tensor", None, "i32", False, True, x_dtype="bf16")
+    _check_forward(M, K, N, bits, "token", None, "bf16", False, True, x_dtype="bf16", kind="ternary")
+
+
 # prefill path (MFMA GEMM)
 @pytest.mark.parametrize("M,K,N", [(9, 256, 512), (130, 48, 37), (200, 336, 300),
                                    (128, 128, 128), (257, 2560, 129), (64, 6912, 200)])
