@@ -528,6 +528,47 @@ def test_forward_fused_batched_2b_64_layers(shape, epi):
         assert_same_bytes(to_host(y[b]), y_ref, "Y layer %d" % b)
 
 
+# streamed launches of a few tokens with long rows in all three load modes -- whole
+# lines (K % 512 == 0), shifted whole lines (K % 512 == 256) and half lines with a
+# partial last k tile; device-drawn uniform-ternary codes, sampled problems compared in
+# full against the oracle (their packing first against the oracle's)
+@pytest.mark.parametrize("B,M,K,N,bits,gran,epi,ydt,with_bias", [
+    (32, 2, 4096, 4096, 8, "token", "relu2", "bf16", True),
+    (32, 3, 4864, 4096, 4, "tensor", None, "i32", False),
+    (32, 4, 4416, 4096, 8, "token", None, "f32", False),
+    (64, 4, 6912, 2560, 8, "tensor", "relu2", "bf16", True),
+])
+def test_forward_stream_long_rows(B, M, K, N, bits, gran, epi, ydt, with_bias):
+    say("stream long rows", dict(B=B, M=M, K=K, N=N, bits=bits, gran=gran, epi=epi, y=ydt,
+                                 bias=with_bias))
+    g = oracle.PER_TOKEN if gran == "token" else oracle.PER_TENSOR
+    e = oracle.EPI_RELU2 if epi == "relu2" else oracle.EPI_NONE
+    tdt, odt = YD[ydt]
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(B * 7 + K)
+    packed = torch.empty((B, N, K // 4), dtype=torch.uint8, device="cuda")
+    gamma = torch.empty((B,), dtype=torch.float32, device="cuda")
+    sampled = (0, 1, B // 2, B - 1)
+    host_codes = {}
+    for b in range(B):
+        codes = torch.randint(-1, 2, (N, K), device="cuda", generator=gen, dtype=torch.int8)
+        bl.quantize_weights(codes.float(), out=(packed[b], gamma[b:b + 1]))
+        if b in sampled:
+            host_codes[b] = codes.cpu().numpy().astype(np.float32)
+    X = torch.randn((B, M, K), device="cuda", generator=gen).to(torch.bfloat16)
+    bias = torch.randn((B, N), device="cuda", generator=gen) if with_bias else None
+    y = bl.forward_fused_batched(X, packed, gamma, bits=bits, gran=gran, bias=bias, epilogue=epi,
+                                 out_dtype=tdt)
+    torch.cuda.synchronize()
+    for b in sampled:
+        p_ref, g_ref, _ = oracle.quantize_weights(host_codes[b])
+        assert_same_bytes(to_host(packed[b]), p_ref, "packed problem %d" % b)
+        y_ref, acc_ref, _, _ = oracle.bitlinear(to_host(X[b]), p_ref, g_ref, bits=bits, gran=g,
+                                                bias=to_host(bias[b]) if with_bias else None, epi=e,
+                                                y_dtype=odt if odt is not None else oracle.F32)
+        assert_y_matches(to_host(y[b]), acc_ref if ydt == "i32" else y_ref, ydt, "Y problem %d" % b)
+
+
 # maximum sizes: one layer at the ABI's limit N*K < 2^32 (65535 x 65536, 8.6 GB of bf16
 # weights on the device); gamma against its exact value nnz/(NK), outputs of sampled
 # rows against the oracle (the codes of uniform-ternary weights are the weights)
