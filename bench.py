@@ -753,7 +753,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int8 x ternary -> int32 acc, fp32 rescale, bf16 io",
+        "dtype": "int8",
+        "arithmetic": "int8 x ternary -> int32 accumulation, fp32 rescale, bf16 in and out",
         "data": "synthetic: seeded uniform-ternary weights, N(0,1) bf16 activations",
         "config": {"workload": "BitNet-2B FFN decode GEMVs, M=1, streamed: %d independent layers "
                                "per launch; step = up 2560->6912 (+ReLU^2) then down 6912->2560 "
