@@ -6,7 +6,8 @@
 //     x' = bf16(fl32(x + delta)),   r = 1 / sqrt(sum x'^2 / K + eps) in fp64,
 //     h  = bf16(fl32(x' * r))       (product in fp64).
 // One 256-thread block per row: each thread keeps its 8-element groups in registers
-// between the two passes; the fp64 sum of squares is reduced in a fixed tree order.
+// between the two passes; the fp64 sum of squares is reduced in a fixed tree order
+// (a shuffle butterfly per wave, then the waves in order).
 #include "common.hpp"
 
 namespace bl {
@@ -15,10 +16,23 @@ namespace {
 constexpr int kNormThreads = 256;
 constexpr int kNormRegGroups = 4;  // 8-element groups per thread held in registers
 
+// The block's fp64 sum in a fixed order (deterministic): a butterfly of xor shuffles
+// within each wave, then the waves' sums in wave order.  One barrier.
+__device__ __forceinline__ double block_sum_f64(double v, double *red) {
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = v;
+    __syncthreads();
+    double t = red[0];
+#pragma unroll
+    for (int i = 1; i < kNormThreads / kWave; ++i) t += red[i];
+    return t;
+}
+
 __global__ void __launch_bounds__(kNormThreads)
 rmsnorm_rows(uint16_t *__restrict__ x, const uint16_t *__restrict__ delta,
              uint16_t *__restrict__ h, int64_t K, float eps) {
-    __shared__ double red[kNormThreads];
+    __shared__ double red[kNormThreads / kWave];
     const int64_t m = blockIdx.x;
     const int64_t n8 = K / 8;
     uint16_t *xr = x + m * K;
@@ -56,14 +70,7 @@ rmsnorm_rows(uint16_t *__restrict__ x, const uint16_t *__restrict__ delta,
                 if (t == i) keep[t] = q;
         }
     }
-    red[threadIdx.x] = ss;
-    __syncthreads();
-#pragma unroll
-    for (int s = kNormThreads / 2; s > 0; s >>= 1) {
-        if ((int)threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
-        __syncthreads();
-    }
-    const double r = 1.0 / sqrt(red[0] / (double)K + (double)eps);
+    const double r = 1.0 / sqrt(block_sum_f64(ss, red) / (double)K + (double)eps);
     // pass 2: normalize (groups beyond the register-held ones are re-read)
     for (int64_t u = threadIdx.x, i = 0; u < n8; u += kNormThreads, ++i) {
         uint4 q;
@@ -97,7 +104,7 @@ __global__ void __launch_bounds__(kNormThreads)
 rmsnorm_quant_rows(uint16_t *__restrict__ x, const uint16_t *__restrict__ delta,
                    uint16_t *__restrict__ h, int64_t K, float eps, float q_eps,
                    uint8_t *__restrict__ xq, float *__restrict__ scale) {
-    __shared__ double red[kNormThreads];
+    __shared__ double red[kNormThreads / kWave];
     __shared__ float redf[kNormThreads / kWave];
     const int64_t m = blockIdx.x;
     const int64_t n8 = K / 8;
@@ -144,14 +151,7 @@ rmsnorm_quant_rows(uint16_t *__restrict__ x, const uint16_t *__restrict__ delta,
         }
         if (i < kNormRegGroups) put((int)i, q);
     }
-    red[threadIdx.x] = ss;
-    __syncthreads();
-#pragma unroll
-    for (int s = kNormThreads / 2; s > 0; s >>= 1) {
-        if ((int)threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
-        __syncthreads();
-    }
-    const double r = 1.0 / sqrt(red[0] / (double)K + (double)eps);
+    const double r = 1.0 / sqrt(block_sum_f64(ss, red) / (double)K + (double)eps);
     // pass 2: h (kept in registers for pass 3), max |h|
     float mx = 0.0f;
     for (int64_t u = threadIdx.x, i = 0; u < n8; u += kNormThreads, ++i) {
