@@ -113,7 +113,7 @@ size_t ws_fused(int64_t M, int64_t N, int64_t K, int bits, bl_gran gran) {
 
 extern "C" {
 
-int bitlinear_version(void) { return 10000; }
+int bitlinear_version(void) { return 10100; }  // 1.1.0: bitlinear_forward_multi
 
 const char *bitlinear_status_string(bl_status s) {
     switch (s) {
