@@ -707,7 +707,7 @@ def main():
     ap.add_argument("--legs", default="decode,chain,single,c1,prefill,stack,c5,pack,acts,backward,cpu")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
 

@@ -65,7 +65,7 @@ typedef enum {
     BL_EINVAL = 1,       /* null pointer, bad enum, eps <= 0 or not finite */
     BL_ESHAPE = 2,       /* M, N, K out of range (K % 16 != 0, N*K >= 2^32, ...) */
     BL_EALIGN = 3,       /* pointer not aligned as required */
-    BL_EUNSUPPORTED = 4, /* valid request this build does not implement */
+    BL_EUNSUPPORTED = 4, /* valid request the library does not implement */
     BL_EDEVICE = 5,      /* HIP error; see bitlinear_last_error() */
     BL_EWORKSPACE = 6    /* workspace missing or smaller than bitlinear_workspace_size() */
 } bl_status;
