@@ -455,6 +455,8 @@ def test_forward_fused_batched(B, M, K, N, bits, gran, epi, ydt, xdt, with_bias)
     (2, 16, 6912, 2560, 8, "tensor", "relu2", "bf16", True),
     (3, 300, 256, 128, 8, "token", None, "f32", False),     # prefill-sized: one call per part
     (3, 2, 512, 44000, 8, "token", None, "bf16", False),    # >= 8192 row tiles: streaming
+    (1, 3, 256, 128, 8, "token", None, "f32", False),       # a single part
+    (2, 4, 256, 36, 8, "tensor", "relu2", "f32", True),     # ragged: 36 rows per part
 ])
 def test_forward_multi(P, M, K, N, bits, gran, epi, ydt, with_bias):
     say("forward_multi", dict(P=P, M=M, K=K, N=N, bits=bits, gran=gran, epi=epi, y=ydt,
