@@ -441,7 +441,7 @@ __global__ void __launch_bounds__(kWaves * 64) gemv_kernel(GemvParams p) {
 // co-resident blocks one was served consistently slower (by up to ~10% over a whole
 // launch), and the CU waited for it at the end; waves of one block kept pace.
 #ifndef BL_STREAM_DEPTH
-#define BL_STREAM_DEPTH 8
+#define BL_STREAM_DEPTH 4  // with one 8-wave block per CU, 4 loads per lane beat 8 by ~2%
 #endif
 #ifndef BL_STREAM_WAVES
 #define BL_STREAM_WAVES 8
