@@ -83,6 +83,7 @@ def _load():
                                           P]
         lib.oracle_to_bf16.argtypes = [P, P, I64]
         lib.oracle_rmsnorm.argtypes = [P, P, I64, I64, F, P, P]
+        lib.oracle_sumsq.argtypes = [P, I64, P]
         lib.oracle_hadamard_block.argtypes = [I64]
         lib.oracle_hadamard_block.restype = I64
         lib.oracle_hadamard_rows.argtypes = [P, I, I64, I64, P]
@@ -91,6 +92,7 @@ def _load():
         lib.oracle_backward.argtypes = [P, P, I, P, I, P, P, P, I, P, I, I64, I64, I64, P, P, P]
         for name in ("oracle_gamma", "oracle_quantize_weights", "oracle_quantize_acts",
                      "oracle_forward", "oracle_forward_at", "oracle_hadamard_rows",
+                     "oracle_rmsnorm", "oracle_sumsq",
                      "oracle_quantize_acts_rotated", "oracle_quantize_weights_rotated",
                      "oracle_backward"):
             getattr(lib, name).restype = I
@@ -215,6 +217,15 @@ def rmsnorm(X: np.ndarray, delta=None, eps: float = 1e-6):
     _check(_load().oracle_rmsnorm(_ptr(X), None if d is None else _ptr(d), M, K, eps,
                                   _ptr(x_out), _ptr(h_out)), "rmsnorm")
     return x_out, h_out
+
+
+def sumsq(row: np.ndarray) -> float:
+    """The sum of squares of one row of bf16 values (uint16 bit patterns), exact, rounded
+    once to fp64 (nearest, ties to even): the S of the RMS norm."""
+    row = np.ascontiguousarray(row, dtype=np.uint16).reshape(-1)
+    out = np.zeros(1, np.float64)
+    _check(_load().oracle_sumsq(_ptr(row), row.size, _ptr(out)), "sumsq")
+    return float(out[0])
 
 
 def hadamard_block(K: int) -> int:

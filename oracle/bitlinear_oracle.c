@@ -393,24 +393,95 @@ void oracle_to_bf16(const float *src, uint16_t *dst, int64_t count)
  * mean square before its BitLinear quantizes it.  Reading taken (the pages give no
  * epsilon, no precision and no learned weight at initialisation): weight 1,
  *     x' = bf16(fl32(x + delta))                 (delta absent: x' = x)
- *     r  = 1 / sqrt(sum_k x'^2 / K + eps)         in fp64, sum in k order
+ *     S  = sum_k x'^2, exactly, rounded once to fp64 (nearest, ties to even)
+ *     r  = 1 / sqrt(S / K + eps)                  in fp64
  *     h  = bf16(fl32(x' * r))                     product in fp64
+ * The mean square is a sum, and the pages fix no order for it; its exact value is
+ * the one result that does not depend on an order.
  * Arrays are bf16 bit patterns, row-major [M][K]; delta may be NULL.
  */
+
+/*
+ * The exact sum of squares.  A finite bf16 value is +-m * 2^(e - 134), m its 8-bit
+ * significand with the hidden bit (e is the biased exponent, taken as 1 for
+ * subnormals, whose hidden bit is 0).  Its square is the integer m^2 * 2^(2e - 2) in
+ * units of 2^-266.  Those integers are added into a 576-bit accumulator (each square
+ * is below 2^524 and a row has fewer than 2^31 values), and the total is rounded to
+ * the nearest fp64, ties to even.
+ */
+#define SQ_LIMBS 18
+
+/* acc += v * 2^shift, v < 2^32 */
+static void sq_add(uint32_t *acc, uint64_t v, int shift)
+{
+    const int li = shift / 32, off = shift % 32;
+    const uint64_t w = v << off;
+    uint64_t carry = 0;
+    for (int i = li; i < SQ_LIMBS; ++i) {
+        uint64_t add = 0;
+        if (i == li) add = w & 0xFFFFFFFFu;
+        else if (i == li + 1) add = w >> 32;
+        const uint64_t t = (uint64_t)acc[i] + add + carry;
+        acc[i] = (uint32_t)t;
+        carry = t >> 32;
+    }
+}
+
+static void sq_add_bf16(uint32_t *acc, uint16_t h)
+{
+    const uint32_t e = (h >> 7) & 0xFFu;
+    const uint64_t m = (h & 0x7Fu) | (e ? 0x80u : 0u);
+    const int ee = e ? (int)e : 1;
+    sq_add(acc, m * m, 2 * ee - 2);
+}
+
+static int sq_bit(const uint32_t *acc, int i) { return (int)((acc[i / 32] >> (i % 32)) & 1u); }
+
+/* the accumulator (units of 2^-266) rounded to the nearest fp64, ties to even */
+static double sq_round_f64(const uint32_t *acc)
+{
+    int top = -1;
+    for (int i = SQ_LIMBS * 32 - 1; i >= 0 && top < 0; --i)
+        if (sq_bit(acc, i)) top = i;
+    if (top < 0) return 0.0;
+    const int low = top - 52; /* lowest of the 53 bits kept */
+    uint64_t mant = 0;
+    for (int i = top; i >= (low > 0 ? low : 0); --i)
+        mant = (mant << 1) | (uint64_t)sq_bit(acc, i);
+    if (low <= 0) return ldexp((double)mant, -266); /* 53 bits or fewer: exact */
+    const int half = sq_bit(acc, low - 1);
+    int sticky = 0;
+    for (int i = low - 2; i >= 0; --i) sticky |= sq_bit(acc, i);
+    if (half && (sticky || (mant & 1u))) mant += 1;
+    return ldexp((double)mant, low - 266);
+}
+
+/* S of one row of K bf16 values (exposed for tests of the oracle) */
+int oracle_sumsq(const uint16_t *x, int64_t K, double *out)
+{
+    if (!x || !out || K <= 0 || K >= ((int64_t)1 << 31)) return OR_EINVAL;
+    uint32_t acc[SQ_LIMBS];
+    memset(acc, 0, sizeof acc);
+    for (int64_t k = 0; k < K; ++k) sq_add_bf16(acc, x[k]);
+    *out = sq_round_f64(acc);
+    return OR_OK;
+}
+
 int oracle_rmsnorm(const uint16_t *X, const uint16_t *delta, int64_t M, int64_t K, float eps,
                    uint16_t *x_out, uint16_t *h_out)
 {
-    if (!X || !x_out || !h_out || M <= 0 || K <= 0 || !(eps > 0.0f))
+    if (!X || !x_out || !h_out || M <= 0 || K <= 0 || K >= ((int64_t)1 << 31) ||
+        !(eps > 0.0f))
         return OR_EINVAL;
     for (int64_t m = 0; m < M; ++m) {
-        double ss = 0.0;
         for (int64_t k = 0; k < K; ++k) {
             float v = widen_bf16(X[m * K + k]);
             if (delta)
                 v = widen_bf16(narrow_bf16(v + widen_bf16(delta[m * K + k])));
             x_out[m * K + k] = narrow_bf16(v);
-            ss += (double)v * (double)v;
         }
+        double ss = 0.0;
+        if (oracle_sumsq(x_out + m * K, K, &ss) != OR_OK) return OR_EINVAL;
         const double r = 1.0 / sqrt(ss / (double)K + (double)eps);
         for (int64_t k = 0; k < K; ++k) {
             const double v = (double)widen_bf16(x_out[m * K + k]);

@@ -620,6 +620,65 @@ def test_rmsnorm_eps_dominates_zero_row():
     assert np.all(_f(h) < 2.0 ** -20 * 1000.0 * 1.01)
 
 
+def _exact_sumsq(bits_row) -> float:
+    """sum of squares in exact rational arithmetic, rounded once to fp64 (CPython's
+    int / int division rounds to nearest, ties to even)."""
+    s = sum(Fraction(float(v)) ** 2 for v in _f(np.asarray(bits_row, np.uint16)))
+    return s.numerator / s.denominator
+
+
+def _wide_bf16_rows(rng, m, k):
+    """bf16 bit patterns with exponents over the whole finite range (subnormals and
+    zeros included), random signs and significands."""
+    e = rng.integers(0, 255, size=(m, k))
+    mant = rng.integers(0, 128, size=(m, k))
+    sign = rng.integers(0, 2, size=(m, k))
+    return ((sign << 15) | (e << 7) | mant).astype(np.uint16)
+
+
+@pytest.mark.parametrize("k", [1, 3, 16, 64, 2560])
+def test_rmsnorm_sum_of_squares_exact(k):
+    # S = sum x'^2 exactly, rounded once: rows spanning the whole exponent range, rows
+    # spanning a narrow one (Gaussian), and rows of subnormals
+    rng = np.random.default_rng([11, k])
+    rows = list(_wide_bf16_rows(rng, 4, k))
+    rows.append(_bf(rng.standard_normal(k).astype(np.float32)))
+    rows.append((rng.integers(0, 128, size=k) | (rng.integers(0, 2, size=k) << 15)).astype(np.uint16))
+    for row in rows:
+        assert oracle.sumsq(row) == _exact_sumsq(row)
+
+
+def test_rmsnorm_sum_of_squares_hand_ties():
+    # worked by hand: 2^54 + 2 lies half way between the fp64 neighbours 2^54 and
+    # 2^54 + 4 and rounds to the even one, 2^54; any positive remainder tips it up;
+    # 2^54 + 3 is past the half way point.  (A running fp64 sum gives 2^54 for all
+    # three: each 1 is below half an ulp of 2^54.)
+    assert oracle.sumsq(_bf([2.0 ** 27, 1.0, 1.0])) == 2.0 ** 54
+    assert oracle.sumsq(_bf([1.0, 2.0 ** 27, 1.0, 2.0 ** -60])) == 2.0 ** 54 + 4
+    assert oracle.sumsq(_bf([1.0, 1.0, 1.0, 2.0 ** 27])) == 2.0 ** 54 + 4
+    # the extremes of bf16: the smallest subnormal 2^-133 squares to 2^-266; the largest
+    # finite value (2 - 2^-7) 2^127 squares to 255^2 2^240, both exact in fp64
+    assert oracle.sumsq(np.array([0x0001], np.uint16)) == 2.0 ** -266
+    assert oracle.sumsq(np.array([0x7F7F, 0xFF7F], np.uint16)) == 2 * 255.0 ** 2 * 2.0 ** 240
+    # the subnormal significand has no hidden bit: 0x0040 is 2^-127
+    assert oracle.sumsq(np.array([0x0040, 0x8040], np.uint16)) == 2 * 2.0 ** -254
+    assert oracle.sumsq(np.zeros(7, np.uint16)) == 0.0
+
+
+def test_rmsnorm_h_from_the_exact_sum():
+    # h = bf16(fl32(x' r)), r = 1 / sqrt(S / K + eps), recomputed from the exact S
+    rng = np.random.default_rng(12)
+    X = np.concatenate([_wide_bf16_rows(rng, 3, 96) & np.uint16(0xBFFF),  # |x| < 2^1
+                        _bf((0.3 * rng.standard_normal((3, 96))).astype(np.float32))])
+    eps = np.float32(1e-6)
+    _, h = oracle.rmsnorm(X, eps=float(eps))
+    for i in range(X.shape[0]):
+        S = _exact_sumsq(X[i])
+        r = 1.0 / math.sqrt(S / 96 + float(eps))
+        prod = (_f(X[i]).astype(np.float64) * r).astype(np.float32)
+        assert np.array_equal(h[i], _bf(prod)), i
+
+
 # ---------------------------------------------------------------- Hadamard rotation
 # ("BitNet a4.8 Guide", "Best Practices for Deploying BitNet a4.8 in Production",
 # Outlier Suppression row; readings in tests/golden/hadamard_examples.json)

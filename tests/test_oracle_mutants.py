@@ -30,6 +30,12 @@ MUTANTS = [
     ("bf16_truncate", "u += 0x7FFFu + lsb;", "(void)lsb;", None),
     ("rmsnorm_mean_not_sum", "ss / (double)K + (double)eps", "ss + (double)eps", None),
     ("rmsnorm_no_sqrt", "1.0 / sqrt(ss / (double)K + (double)eps)", "1.0 / (ss / (double)K + (double)eps)", None),
+    ("sumsq_truncated", "if (half && (sticky || (mant & 1u))) mant += 1;", "", None),
+    ("sumsq_ties_away", "if (half && (sticky || (mant & 1u))) mant += 1;", "if (half) mant += 1;", None),
+    ("sumsq_subnormal_hidden_bit", "(h & 0x7Fu) | (e ? 0x80u : 0u)", "(h & 0x7Fu) | 0x80u", None),
+    ("sumsq_exponent_not_doubled", "sq_add(acc, m * m, 2 * ee - 2);", "sq_add(acc, m * m, ee - 1);", None),
+    ("sumsq_carry_dropped", "const uint64_t t = (uint64_t)acc[i] + add + carry;\n        acc[i] = (uint32_t)t;\n        carry = t >> 32;",
+     "const uint64_t t = (uint64_t)acc[i] + add + carry;\n        acc[i] = (uint32_t)t;\n        carry = 0;", None),
     ("rmsnorm_residual_dropped", "v = widen_bf16(narrow_bf16(v + widen_bf16(delta[m * K + k])));", "(void)delta;", None),
     ("hadamard_butterfly_swapped", "blk[i] = u + v;\n                    blk[i + h] = u - v;", "blk[i] = u - v;\n                    blk[i + h] = u + v;", None),
     ("hadamard_stage_skipped", "for (int64_t h = 1; h < b; h *= 2)", "for (int64_t h = 2; h < b; h *= 2)", None),
