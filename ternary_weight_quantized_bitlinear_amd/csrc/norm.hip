@@ -3,46 +3,63 @@
 // (SubLN)", and the block of its "End-to-End PyTorch Implementation" listing: each
 // sub-layer adds its output to the residual stream, the next one normalizes the stream
 // before its BitLinear quantizes it).  Weight 1 (its initial value); per row
-//     x' = bf16(fl32(x + delta)),   r = 1 / sqrt(sum x'^2 / K + eps) in fp64,
-//     h  = bf16(fl32(x' * r))       (product in fp64).
+//     x' = bf16(fl32(x + delta)),   S = sum x'^2 exactly, rounded once to fp64,
+//     r  = 1 / sqrt(S / K + eps) in fp64,   h = bf16(fl32(x' * r))  (product in fp64).
 // One 256-thread block per row: each thread keeps its 8-element groups in registers
-// between the two passes; the fp64 sum of squares is reduced in a fixed tree order
-// (a shuffle butterfly per wave, then the waves in order).
+// between the passes.  The exact S (exact_sumsq.hpp) needs the row's largest exponent
+// first, so pass 1 is two sweeps over the kept values with a barrier between them; the
+// window sums are integers, so the block's reduction order cannot change S.
 #include "common.hpp"
+#include "exact_sumsq.hpp"
 
 namespace bl {
 namespace {
 
 constexpr int kNormThreads = 256;
+constexpr int kNormWaves = kNormThreads / kWave;
 constexpr int kNormRegGroups = 4;  // 8-element groups per thread held in registers
 
-// The block's fp64 sum in a fixed order (deterministic): a butterfly of xor shuffles
-// within each wave, then the waves' sums in wave order.  One barrier.
-__device__ __forceinline__ double block_sum_f64(double v, double *red) {
-#pragma unroll
-    for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o);
-    if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = v;
-    __syncthreads();
-    double t = red[0];
-#pragma unroll
-    for (int i = 1; i < kNormThreads / kWave; ++i) t += red[i];
-    return t;
+struct NormShared {
+    uint64_t bins[256];   // slow path: sum of m^2 per biased exponent
+    uint64_t wsum[kNormWaves][2];
+    int wmax[kNormWaves];
+    uint32_t big[kSqLimbs];  // slow path: the exact total
+    double S;
+};
+
+__device__ __forceinline__ int wave_max_int(int v) {
+    v = max(v, dpp_mov<kDppQuadXor1>(0, v));
+    v = max(v, dpp_mov<kDppQuadXor2>(0, v));
+    v = max(v, dpp_mov<kDppHalfMirror>(0, v));
+    v = max(v, dpp_mov<kDppMirror>(0, v));
+    v = max(v, dpp_mov<kDppBcast15, 0xA>(0, v));
+    v = max(v, dpp_mov<kDppBcast31, 0xC>(0, v));
+    return __builtin_amdgcn_readlane(v, 63);
 }
 
-__global__ void __launch_bounds__(kNormThreads)
-rmsnorm_rows(uint16_t *__restrict__ x, const uint16_t *__restrict__ delta,
-             uint16_t *__restrict__ h, int64_t K, float eps) {
-    __shared__ double red[kNormThreads / kWave];
-    const int64_t m = blockIdx.x;
-    const int64_t n8 = K / 8;
-    uint16_t *xr = x + m * K;
-    const uint16_t *dr = delta ? delta + m * K : nullptr;
-    uint16_t *hr = h + m * K;
-    double ss = 0.0;
-    uint4 keep[kNormRegGroups];
+template <int kN>
+__device__ __forceinline__ void keep_put(uint4 (&keep)[kN], int64_t i, uint4 q) {
 #pragma unroll
-    for (int i = 0; i < kNormRegGroups; ++i) keep[i] = make_uint4(0u, 0u, 0u, 0u);
-    // pass 1: residual add (written back), sum of squares
+    for (int t = 0; t < kN; ++t)
+        if (t == i) keep[t] = q;
+}
+template <int kN>
+__device__ __forceinline__ uint4 keep_get(const uint4 (&keep)[kN], int64_t i) {
+    uint4 q = keep[0];
+#pragma unroll
+    for (int t = 1; t < kN; ++t)
+        if (t == i) q = keep[t];
+    return q;
+}
+
+// Pass 1 of both kernels: x' = bf16(fl32(x + delta)) (written back when delta is given),
+// this thread's first kNormRegGroups groups of x' kept in `keep`, and r of the row.
+// Every thread of the block must call it (barriers inside).
+__device__ __forceinline__ double row_residual_r(uint16_t *xr, const uint16_t *dr, int64_t n8,
+                                                 float eps, uint4 (&keep)[kNormRegGroups],
+                                                 NormShared &sh) {
+    sh.bins[threadIdx.x] = 0;  // kNormThreads == 256 bins
+    int emax = 0;
     for (int64_t u = threadIdx.x, i = 0; u < n8; u += kNormThreads, ++i) {
         uint4 q = reinterpret_cast<const uint4 *>(xr)[u];
         uint32_t w[4] = {q.x, q.y, q.z, q.w};
@@ -59,29 +76,79 @@ rmsnorm_rows(uint16_t *__restrict__ x, const uint16_t *__restrict__ delta,
             reinterpret_cast<uint4 *>(xr)[u] = q;
         }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const double a = (double)bf16_lo(w[j]), b = (double)bf16_hi(w[j]);
-            ss += a * a;
-            ss += b * b;
-        }
-        if (i < kNormRegGroups) {
+        for (int j = 0; j < 4; ++j) emax = max(emax, max(sq_exp(w[j]), sq_exp(w[j] >> 16)));
+        if (i < kNormRegGroups) keep_put(keep, i, q);
+    }
+    emax = wave_max_int(emax);
+    const int wv = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+    if (lane == 0) sh.wmax[wv] = emax;
+    __syncthreads();
+    int E = 1;
 #pragma unroll
-            for (int t = 0; t < kNormRegGroups; ++t)
-                if (t == i) keep[t] = q;
+    for (int i = 0; i < kNormWaves; ++i) E = max(E, sh.wmax[i]);
+    // the window sum of this thread's squares; values below the window go to the bins
+    u128 acc = 0;
+    int spill = 0;
+    for (int64_t u = threadIdx.x, i = 0; u < n8; u += kNormThreads, ++i) {
+        const uint4 q = i < kNormRegGroups ? keep_get(keep, i)
+                                           : reinterpret_cast<const uint4 *>(xr)[u];
+        const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            uint32_t sq;
+            int bin;
+            if (!sq_window_add(w[j / 2] >> (16 * (j % 2)), E, acc, &sq, &bin)) {
+                atomicAdd(reinterpret_cast<unsigned long long *>(&sh.bins[bin]),
+                          (unsigned long long)sq);
+                spill = 1;
+            }
         }
     }
-    const double r = 1.0 / sqrt(block_sum_f64(ss, red) / (double)K + (double)eps);
+    // integer sums: the same total in any order
+    uint64_t lo = (uint64_t)acc, hi = (uint64_t)(acc >> 64);
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) {
+        const uint64_t l2 = __shfl_xor(lo, o), h2 = __shfl_xor(hi, o);
+        const u128 t = (((u128)hi << 64) | lo) + (((u128)h2 << 64) | l2);
+        lo = (uint64_t)t;
+        hi = (uint64_t)(t >> 64);
+    }
+    if (lane == 0) {
+        sh.wsum[wv][0] = lo;
+        sh.wsum[wv][1] = hi;
+    }
+    const int any_spill = __syncthreads_or(spill);
+    u128 total = 0;
+#pragma unroll
+    for (int i = 0; i < kNormWaves; ++i) total += ((u128)sh.wsum[i][1] << 64) | sh.wsum[i][0];
+    double S;
+    if (!any_spill) {
+        S = sq_round(total, 2 * E - 268 - kSqFrac);
+    } else {
+        if (threadIdx.x == 0) sh.S = sq_round_with_bins(total, E, sh.bins, sh.big);
+        __syncthreads();
+        S = sh.S;
+    }
+    return 1.0 / sqrt(S / (double)(n8 * 8) + (double)eps);
+}
+
+__global__ void __launch_bounds__(kNormThreads)
+rmsnorm_rows(uint16_t *__restrict__ x, const uint16_t *__restrict__ delta,
+             uint16_t *__restrict__ h, int64_t K, float eps) {
+    __shared__ NormShared sh;
+    const int64_t m = blockIdx.x;
+    const int64_t n8 = K / 8;
+    uint16_t *xr = x + m * K;
+    const uint16_t *dr = delta ? delta + m * K : nullptr;
+    uint16_t *hr = h + m * K;
+    uint4 keep[kNormRegGroups];
+#pragma unroll
+    for (int i = 0; i < kNormRegGroups; ++i) keep[i] = make_uint4(0u, 0u, 0u, 0u);
+    const double r = row_residual_r(xr, dr, n8, eps, keep, sh);
     // pass 2: normalize (groups beyond the register-held ones are re-read)
     for (int64_t u = threadIdx.x, i = 0; u < n8; u += kNormThreads, ++i) {
-        uint4 q;
-        if (i < kNormRegGroups) {
-            q = keep[0];
-#pragma unroll
-            for (int t = 1; t < kNormRegGroups; ++t)
-                if (t == i) q = keep[t];
-        } else {
-            q = reinterpret_cast<const uint4 *>(xr)[u];
-        }
+        const uint4 q = i < kNormRegGroups ? keep_get(keep, i)
+                                           : reinterpret_cast<const uint4 *>(xr)[u];
         const uint32_t w[4] = {q.x, q.y, q.z, q.w};
         uint32_t o[4];
 #pragma unroll
@@ -104,54 +171,19 @@ __global__ void __launch_bounds__(kNormThreads)
 rmsnorm_quant_rows(uint16_t *__restrict__ x, const uint16_t *__restrict__ delta,
                    uint16_t *__restrict__ h, int64_t K, float eps, float q_eps,
                    uint8_t *__restrict__ xq, float *__restrict__ scale) {
-    __shared__ double red[kNormThreads / kWave];
-    __shared__ float redf[kNormThreads / kWave];
+    __shared__ NormShared sh;
+    __shared__ float redf[kNormWaves];
     const int64_t m = blockIdx.x;
     const int64_t n8 = K / 8;
     uint16_t *xr = x + m * K;
     const uint16_t *dr = delta ? delta + m * K : nullptr;
     uint16_t *hr = h + m * K;
-    double ss = 0.0;
     uint4 keep[kNormRegGroups];
 #pragma unroll
     for (int i = 0; i < kNormRegGroups; ++i) keep[i] = make_uint4(0u, 0u, 0u, 0u);
-    auto put = [&](int i, uint4 q) __attribute__((always_inline)) {
-#pragma unroll
-        for (int t = 0; t < kNormRegGroups; ++t)
-            if (t == i) keep[t] = q;
-    };
-    auto get = [&](int i) __attribute__((always_inline)) {
-        uint4 q = keep[0];
-#pragma unroll
-        for (int t = 1; t < kNormRegGroups; ++t)
-            if (t == i) q = keep[t];
-        return q;
-    };
-    // pass 1: residual add (written back), sum of squares
-    for (int64_t u = threadIdx.x, i = 0; u < n8; u += kNormThreads, ++i) {
-        uint4 q = reinterpret_cast<const uint4 *>(xr)[u];
-        uint32_t w[4] = {q.x, q.y, q.z, q.w};
-        if (dr) {
-            const uint4 dq = reinterpret_cast<const uint4 *>(dr)[u];
-            const uint32_t dw[4] = {dq.x, dq.y, dq.z, dq.w};
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const uint32_t lo = to_bf16_bits(__fadd_rn(bf16_lo(w[j]), bf16_lo(dw[j])));
-                const uint32_t hi = to_bf16_bits(__fadd_rn(bf16_hi(w[j]), bf16_hi(dw[j])));
-                w[j] = (lo & 0xFFFFu) | (hi << 16);
-            }
-            q = make_uint4(w[0], w[1], w[2], w[3]);
-            reinterpret_cast<uint4 *>(xr)[u] = q;
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const double a = (double)bf16_lo(w[j]), b = (double)bf16_hi(w[j]);
-            ss += a * a;
-            ss += b * b;
-        }
-        if (i < kNormRegGroups) put((int)i, q);
-    }
-    const double r = 1.0 / sqrt(block_sum_f64(ss, red) / (double)K + (double)eps);
+    auto put = [&](int64_t i, uint4 q) __attribute__((always_inline)) { keep_put(keep, i, q); };
+    auto get = [&](int64_t i) __attribute__((always_inline)) { return keep_get(keep, i); };
+    const double r = row_residual_r(xr, dr, n8, eps, keep, sh);
     // pass 2: h (kept in registers for pass 3), max |h|
     float mx = 0.0f;
     for (int64_t u = threadIdx.x, i = 0; u < n8; u += kNormThreads, ++i) {
@@ -174,7 +206,7 @@ rmsnorm_quant_rows(uint16_t *__restrict__ x, const uint16_t *__restrict__ delta,
     __syncthreads();
     float amax = redf[0];
 #pragma unroll
-    for (int i = 1; i < kNormThreads / kWave; ++i) amax = fmaxf(amax, redf[i]);
+    for (int i = 1; i < kNormWaves; ++i) amax = fmaxf(amax, redf[i]);
     const float a = fmaxf(amax, q_eps);
     const float sc = kBits == 8 ? 127.0f / a : a / 7.0f;
     if (threadIdx.x == 0) scale[m] = sc;

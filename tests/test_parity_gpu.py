@@ -237,15 +237,35 @@ def test_forward_prefill_long_k(M, K, N, ydt):
     _check_forward(M, K, N, 8, "tensor", None, ydt, False, True, x_dtype="bf16")
 
 
-# full-size 2B shapes, sampled
+def _codes_f64(xq_ref, bits, p_ref, K):
+    """The oracle's activation and weight codes as float64 matrices, unpacked from the
+    documented layouts (int4: element 2i in the low nibble; 2-bit field c + 1 of code k in
+    bits 2 (k % 4) of byte k / 4)."""
+    if bits == 8:
+        q = xq_ref.astype(np.float64)
+    else:
+        lo = (xq_ref & 0xF).astype(np.int16)
+        hi = (xq_ref >> 4).astype(np.int16)
+        v = np.stack([lo, hi], axis=-1).reshape(xq_ref.shape[0], K)
+        q = np.where(v >= 8, v - 16, v).astype(np.float64)
+    f = np.stack([(p_ref >> (2 * j)) & 3 for j in range(4)], axis=-1).reshape(p_ref.shape[0], K)
+    return q, f.astype(np.float64) - 1.0
+
+
+# full-size 2B shapes: outputs sampled; the int32 accumulators in full, against a float64
+# matmul of the oracle's codes (exact: every partial sum is an integer below 2^53)
 @pytest.mark.parametrize("shape,epi", [(workloads.SHAPE_UP, "relu2"), (workloads.SHAPE_DOWN, None)])
 @pytest.mark.parametrize("bits", [8, 4])
 def test_forward_prefill_2b_shapes(shape, epi, bits):
     K, N = shape
     _check_forward(2048, K, N, bits, "token", epi, "bf16", False, True, x_dtype="bf16",
                    kind="ternary", sampled=True)
-    _check_forward(2048, K, N, bits, "token", None, "i32", False, False, x_dtype="bf16",
-                   kind="ternary", sampled=True)
+    W, X = _layer(2048, K, N, 0, "ternary")
+    say("forward 2B prefill, full int32 accumulators", K, N, bits)
+    acc, (p_ref, _, xq_ref, _, _) = _run_forward(W, X, bits, "token", None, "i32", None, False,
+                                                 "bf16")
+    q, c = _codes_f64(xq_ref, bits, p_ref, K)
+    assert np.array_equal(acc.astype(np.float64), q @ c.T), "int32 accumulators differ"
 
 
 @pytest.mark.parametrize("shape,epi", [(workloads.SHAPE_UP, "relu2"), (workloads.SHAPE_DOWN, None)])

@@ -105,9 +105,7 @@ def test_rotated_70b_layer_sampled():
     p_ref, g_ref, _ = oracle.quantize_weights_rotated(W)
     del W
     assert bits32(to_host(gamma))[0] == bits32(np.array([g_ref]))[0], "gamma differs"
-    ph = to_host(packed)
-    rows = rng.choice(N, 64, replace=False)
-    assert_same_bytes(ph[rows], p_ref[rows], "rotated packed weights (64 rows)")
+    assert_same_bytes(to_host(packed), p_ref, "rotated packed weights (all rows)")
     xq_ref, s_ref = oracle.quantize_acts_rotated(X, bits=4)
     assert_same_bytes(bits32(to_host(s)), bits32(s_ref), "act_scale")
     assert_same_bytes(to_host(xq), xq_ref, "rotated int4 codes")
