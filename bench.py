@@ -97,8 +97,14 @@ def cpu_model() -> str:
     return platform.processor() or "unknown"
 
 
-def graph_time_ms(torch, fn, replays: int, warm: int = 2):
-    """Capture fn() in a HIP graph; return (ms per replay, graph) over `replays` replays."""
+def graph_time_ms(torch, fn, replays: int, warm: int = 2, steady_ms: float = 0.0):
+    """Capture fn() in a HIP graph; return (ms per replay, graph) over `replays` replays.
+
+    steady_ms > 0: before timing, untimed replays keep the GPU busy for at least that
+    long, so that clocks and memory have left their idle states whatever the replay's
+    length.  The timed replays are queued behind a short spin kernel, so the first one is
+    already submitted when the start event fires: the host's submission time is not
+    timed."""
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
@@ -112,6 +118,17 @@ def graph_time_ms(torch, fn, replays: int, warm: int = 2):
         g.replay()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
+    if steady_ms > 0:
+        w0 = torch.cuda.Event(enable_timing=True)
+        w1 = torch.cuda.Event(enable_timing=True)
+        w0.record(stream)
+        g.replay()
+        w1.record(stream)
+        torch.cuda.synchronize()
+        one = max(w0.elapsed_time(w1), 1e-3)
+        for _ in range(int(steady_ms / one) + 1):
+            g.replay()
+        torch.cuda._sleep(2_000_000)  # ~1 ms of spinning while the timed replays queue up
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record(stream)
@@ -236,13 +253,25 @@ def leg_decode_stream(torch, bl, steps, warmup, batch, sets=3):
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    ms_total, _ = graph_time_ms(torch, run_k, replays=1, warm=1)
+    # exactly `steps` steps timed, after at least 300 ms of untimed streaming
+    ms_total, g = graph_time_ms(torch, run_k, replays=1, warm=1, steady_ms=300.0)
     ms_step = ms_total / steps
+    # context only: the same graph replayed 5 more times, each timed on its own
+    rep = []
+    for _ in range(5):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(2_000_000)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        rep.append(e0.elapsed_time(e1) / steps)
     step_bytes = batch * (gemv_bytes(K1, N1) + gemv_bytes(K2, N2))
     return {"ms_per_step": ms_step, "gbs": step_bytes / (ms_step * 1e-3) / 1e9,
             "step_bytes": step_bytes, "per_launch_us": ms_step * 1e3 / 2,
             "bytes_per_launch": step_bytes / 2, "batch": batch, "sets": sets, "x": x,
-            "W_up": W_up, "W_dn": W_dn}
+            "W_up": W_up, "W_dn": W_dn, "repeat_ms_per_step": rep}
 
 
 def leg_decode_single(torch, bl, copies=64, reps=200):
@@ -769,7 +798,9 @@ def main():
                      "frac": round(alg / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(),
                      "bytes_per_launch": st["bytes_per_launch"],
-                     "us_per_launch": st["per_launch_us"]},
+                     "us_per_launch": st["per_launch_us"],
+                     "repeat_us_per_launch": [round(v * 1e3 / 2, 2)
+                                              for v in st["repeat_ms_per_step"]]},
     }
     if "chain" in legs:
         dec = leg_decode(torch, bl, args.chain_steps, args.warmup, args.copies)
