@@ -153,6 +153,9 @@ def _workspace(nbytes, device, workspace):
     if nbytes == 0:
         return None, 0
     if workspace is not None:
+        _arg(workspace, "workspace", None, (torch.uint8,))
+        if workspace.device != device:
+            _fail(BL_EINVAL, "workspace is on %s, the operands on %s" % (workspace.device, device))
         return workspace, workspace.numel() * workspace.element_size()
     return torch.empty(nbytes, dtype=torch.uint8, device=device), nbytes
 
@@ -161,37 +164,148 @@ def workspace_size(op: int, M: int, N: int, K: int, bits: int = 8, gran="token")
     return lib().bitlinear_workspace_size(op, M, N, K, bits, _gran_code(gran))
 
 
+# ------------------------------------------------------------------ argument checks
+# Every tensor is checked before the C call: the C ABI sees only pointers and sizes, so a
+# tensor of the wrong shape, dtype or device, or a strided view, would otherwise reach the
+# kernels as an out-of-bounds or host address.  Order: dtype, shape, layout, device.
+
+def _fail(status, msg):
+    raise BitLinearError(status, msg)
+
+
+def _dims(t, name, ndim):
+    if t is None:
+        _fail(BL_EINVAL, "%s is required" % name)
+    if t.dim() != ndim:
+        _fail(BL_ESHAPE, "%s must have %d dimensions, has shape %s" % (name, ndim, tuple(t.shape)))
+    return tuple(t.shape)
+
+
+def _arg(t, name, shape, dtypes, optional=False):
+    if t is None:
+        if optional:
+            return
+        _fail(BL_EINVAL, "%s is required" % name)
+    if dtypes is not None and t.dtype not in dtypes:
+        _fail(BL_EINVAL, "%s has dtype %s, expected %s" % (
+            name, t.dtype, " or ".join(str(d) for d in dtypes)))
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        _fail(BL_ESHAPE, "%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    if not t.is_contiguous():
+        _fail(BL_EINVAL, "%s must be contiguous" % name)
+
+
+def _gpu(**tensors):
+    """All given tensors (None skipped) on one GPU: returns that device."""
+    dev = None
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if t.device.type != "cuda":
+            _fail(BL_EINVAL, "%s must be a GPU tensor (is on %s)" % (name, t.device))
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            _fail(BL_EINVAL, "%s is on %s, the other operands on %s" % (name, t.device, dev))
+    return dev
+
+
+def _bits(bits):
+    if bits not in (8, 4):
+        _fail(BL_EINVAL, "bits must be 8 or 4")
+    return bits
+
+
+def _float_types():
+    torch = _torch()
+    return (torch.float32, torch.bfloat16)
+
+
+def _code_types():
+    torch = _torch()
+    return (torch.int8, torch.uint8)
+
+
+def _out_types():
+    torch = _torch()
+    return (torch.float32, torch.bfloat16, torch.int32)
+
+
+def _code_cols(K, bits):
+    """Bytes per row of the activation codes: K (int8) or K/2 (two int4 per byte)."""
+    return K if bits == 8 else K // 2
+
+
+def _scale_len(M, g):
+    return M if g == BL_PER_TOKEN else 1
+
+
 # ------------------------------------------------------------------ entry points
+# Each entry point: dimensions, then every tensor's dtype, shape and layout, then one
+# device for all of them; only then are outputs allocated and the library called.
 
 def quantize_weights(W, eps: float = 1e-5, workspace=None, stream=None, out=None):
     """W [N, K] fp32/bf16 (device) -> (packed uint8 [N, K/4], gamma fp32 [1])."""
+    return _quantize_weights(lib().bitlinear_quantize_weights, W, eps, workspace, stream, out)
+
+
+def quantize_weights_rotated(W, eps: float = 1e-5, workspace=None, stream=None, out=None):
+    """quantize_weights of W H (block Hadamard rotation of the rows), gamma divided by the
+    block size: use with activations from quantize_acts_rotated."""
+    return _quantize_weights(lib().bitlinear_quantize_weights_rotated, W, eps, workspace, stream,
+                             out)
+
+
+def _quantize_weights(fn, W, eps, workspace, stream, out):
     torch = _torch()
-    N, K = W.shape
-    packed = out[0] if out else torch.empty((N, K // 4), dtype=torch.uint8, device=W.device)
-    gamma = out[1] if out else torch.empty(1, dtype=torch.float32, device=W.device)
-    ws, wsb = _workspace(workspace_size(BL_OP_QUANTIZE_WEIGHTS, 1, N, K), W.device, workspace)
-    _check(lib().bitlinear_quantize_weights(_ptr(W), _dtype_code(W), N, K, eps, _ptr(packed),
-                                            _ptr(gamma), _ptr(ws), wsb,
-                                            _stream(W.device, stream)))
+    N, K = _dims(W, "W", 2)
+    _arg(W, "W", None, _float_types())
+    packed, gamma = out if out else (None, None)
+    if out:
+        _arg(packed, "packed", (N, K // 4), (torch.uint8,))
+        _arg(gamma, "gamma", (1,), (torch.float32,))
+    dev = _gpu(W=W, packed=packed, gamma=gamma)
+    if not out:
+        packed = torch.empty((N, K // 4), dtype=torch.uint8, device=dev)
+        gamma = torch.empty(1, dtype=torch.float32, device=dev)
+    ws, wsb = _workspace(workspace_size(BL_OP_QUANTIZE_WEIGHTS, 1, N, K), dev, workspace)
+    _check(fn(_ptr(W), _dtype_code(W), N, K, eps, _ptr(packed), _ptr(gamma), _ptr(ws), wsb,
+              _stream(dev, stream)))
     return packed, gamma
 
 
 def quantize_acts(X, bits: int = 8, gran="token", eps: float = 1e-5, workspace=None,
                   stream=None, out=None):
     """X [M, K] fp32/bf16 -> (Xq int8 [M, K] or uint8 [M, K/2], act_scale fp32 [M] or [1])."""
+    return _quantize_acts(lib().bitlinear_quantize_acts, X, bits, gran, eps, workspace, stream,
+                          out)
+
+
+def quantize_acts_rotated(X, bits: int = 4, gran="token", eps: float = 1e-5, workspace=None,
+                          stream=None, out=None):
+    """quantize_acts of X H (block Hadamard rotation of the rows)."""
+    return _quantize_acts(lib().bitlinear_quantize_acts_rotated, X, bits, gran, eps, workspace,
+                          stream, out)
+
+
+def _quantize_acts(fn, X, bits, gran, eps, workspace, stream, out):
     torch = _torch()
-    M, K = X.shape
+    M, K = _dims(X, "X", 2)
+    _arg(X, "X", None, _float_types())
+    bits = _bits(bits)
     g = _gran_code(gran)
+    Xq, scale = out if out else (None, None)
     if out:
-        Xq, scale = out
-    else:
-        Xq = torch.empty((M, K) if bits == 8 else (M, K // 2),
-                         dtype=torch.int8 if bits == 8 else torch.uint8, device=X.device)
-        scale = torch.empty(M if g == BL_PER_TOKEN else 1, dtype=torch.float32, device=X.device)
-    ws, wsb = _workspace(workspace_size(BL_OP_QUANTIZE_ACTS, M, 1, K, bits, g), X.device,
-                         workspace)
-    _check(lib().bitlinear_quantize_acts(_ptr(X), _dtype_code(X), M, K, bits, g, eps, _ptr(Xq),
-                                         _ptr(scale), _ptr(ws), wsb, _stream(X.device, stream)))
+        _arg(Xq, "Xq", (M, _code_cols(K, bits)), _code_types())
+        _arg(scale, "act_scale", (_scale_len(M, g),), (torch.float32,))
+    dev = _gpu(X=X, Xq=Xq, act_scale=scale)
+    if not out:
+        Xq = torch.empty((M, _code_cols(K, bits)),
+                         dtype=torch.int8 if bits == 8 else torch.uint8, device=dev)
+        scale = torch.empty(_scale_len(M, g), dtype=torch.float32, device=dev)
+    ws, wsb = _workspace(workspace_size(BL_OP_QUANTIZE_ACTS, M, 1, K, bits, g), dev, workspace)
+    _check(fn(_ptr(X), _dtype_code(X), M, K, bits, g, eps, _ptr(Xq), _ptr(scale), _ptr(ws), wsb,
+              _stream(dev, stream)))
     return Xq, scale
 
 
@@ -200,72 +314,66 @@ def hadamard_block(K: int) -> int:
     return int(lib().bitlinear_hadamard_block(K))
 
 
-def quantize_weights_rotated(W, eps: float = 1e-5, workspace=None, stream=None, out=None):
-    """quantize_weights of W H (block Hadamard rotation of the rows), gamma divided by the
-    block size: use with activations from quantize_acts_rotated."""
-    torch = _torch()
-    N, K = W.shape
-    packed = out[0] if out else torch.empty((N, K // 4), dtype=torch.uint8, device=W.device)
-    gamma = out[1] if out else torch.empty(1, dtype=torch.float32, device=W.device)
-    ws, wsb = _workspace(workspace_size(BL_OP_QUANTIZE_WEIGHTS, 1, N, K), W.device, workspace)
-    _check(lib().bitlinear_quantize_weights_rotated(_ptr(W), _dtype_code(W), N, K, eps,
-                                                    _ptr(packed), _ptr(gamma), _ptr(ws), wsb,
-                                                    _stream(W.device, stream)))
-    return packed, gamma
+def _out_arg(out, shape):
+    if out is not None:
+        _arg(out, "out", shape, _out_types())
 
 
-def quantize_acts_rotated(X, bits: int = 4, gran="token", eps: float = 1e-5, workspace=None,
-                          stream=None, out=None):
-    """quantize_acts of X H (block Hadamard rotation of the rows)."""
+def _new_out(out, shape, out_dtype, dev):
     torch = _torch()
-    M, K = X.shape
-    g = _gran_code(gran)
-    if out:
-        Xq, scale = out
-    else:
-        Xq = torch.empty((M, K) if bits == 8 else (M, K // 2),
-                         dtype=torch.int8 if bits == 8 else torch.uint8, device=X.device)
-        scale = torch.empty(M if g == BL_PER_TOKEN else 1, dtype=torch.float32, device=X.device)
-    ws, wsb = _workspace(workspace_size(BL_OP_QUANTIZE_ACTS, M, 1, K, bits, g), X.device,
-                         workspace)
-    _check(lib().bitlinear_quantize_acts_rotated(_ptr(X), _dtype_code(X), M, K, bits, g, eps,
-                                                 _ptr(Xq), _ptr(scale), _ptr(ws), wsb,
-                                                 _stream(X.device, stream)))
-    return Xq, scale
+    return out if out is not None else torch.empty(shape, dtype=out_dtype or torch.float32,
+                                                   device=dev)
 
 
 def forward(Xq, act_scale, packed, gamma, bits: int = 8, gran="token", bias=None,
             epilogue=None, out_dtype=None, workspace=None, stream=None, out=None):
     """Quantized activations -> Y [M, N] (fp32, bf16 or int32 accumulators)."""
     torch = _torch()
-    M = Xq.shape[0]
-    K = Xq.shape[1] * (1 if bits == 8 else 2)
-    N = packed.shape[0]
+    bits = _bits(bits)
+    M, cols = _dims(Xq, "Xq", 2)
+    N, _ = _dims(packed, "packed", 2)
+    K = cols * (1 if bits == 8 else 2)
     g = _gran_code(gran)
-    if out is None:
-        out = torch.empty((M, N), dtype=out_dtype or torch.float32, device=Xq.device)
-    ws, wsb = _workspace(workspace_size(BL_OP_FORWARD, M, N, K, bits, g), Xq.device, workspace)
+    _arg(Xq, "Xq", None, _code_types())
+    _arg(packed, "packed", (N, K // 4), (torch.uint8,))
+    _arg(act_scale, "act_scale", (_scale_len(M, g),), (torch.float32,))
+    _arg(gamma, "gamma", (1,), (torch.float32,))
+    _arg(bias, "bias", (N,), (torch.float32,), optional=True)
+    _out_arg(out, (M, N))
+    dev = _gpu(Xq=Xq, packed=packed, act_scale=act_scale, gamma=gamma, bias=bias, out=out)
+    out = _new_out(out, (M, N), out_dtype, dev)
+    ws, wsb = _workspace(workspace_size(BL_OP_FORWARD, M, N, K, bits, g), dev, workspace)
     _check(lib().bitlinear_forward(_ptr(Xq), bits, _ptr(act_scale), g, _ptr(packed), _ptr(gamma),
                                    _ptr(bias), M, N, K, _epi_code(epilogue), _ptr(out),
-                                   _dtype_code(out), _ptr(ws), wsb, _stream(Xq.device, stream)))
+                                   _dtype_code(out), _ptr(ws), wsb, _stream(dev, stream)))
     return out
+
+
+def _fused_args(X, packed, gamma, bias, out):
+    torch = _torch()
+    M, K = _dims(X, "X", 2)
+    N, _ = _dims(packed, "packed", 2)
+    _arg(X, "X", None, _float_types())
+    _arg(packed, "packed", (N, K // 4), (torch.uint8,))
+    _arg(gamma, "gamma", (1,), (torch.float32,))
+    _arg(bias, "bias", (N,), (torch.float32,), optional=True)
+    _out_arg(out, (M, N))
+    dev = _gpu(X=X, packed=packed, gamma=gamma, bias=bias, out=out)
+    return M, N, K, dev
 
 
 def forward_fused(X, packed, gamma, bits: int = 8, gran="token", eps: float = 1e-5, bias=None,
                   epilogue=None, out_dtype=None, workspace=None, stream=None, out=None):
     """Unquantized activations X [M, K] fp32/bf16 -> Y [M, N]: quantize_acts + forward."""
-    torch = _torch()
-    M, K = X.shape
-    N = packed.shape[0]
+    bits = _bits(bits)
+    M, N, K, dev = _fused_args(X, packed, gamma, bias, out)
     g = _gran_code(gran)
-    if out is None:
-        out = torch.empty((M, N), dtype=out_dtype or torch.float32, device=X.device)
-    ws, wsb = _workspace(workspace_size(BL_OP_FORWARD_FUSED, M, N, K, bits, g), X.device,
-                         workspace)
+    out = _new_out(out, (M, N), out_dtype, dev)
+    ws, wsb = _workspace(workspace_size(BL_OP_FORWARD_FUSED, M, N, K, bits, g), dev, workspace)
     _check(lib().bitlinear_forward_fused(_ptr(X), _dtype_code(X), bits, g, eps, _ptr(packed),
                                          _ptr(gamma), _ptr(bias), M, N, K, _epi_code(epilogue),
                                          _ptr(out), _dtype_code(out), _ptr(ws), wsb,
-                                         _stream(X.device, stream)))
+                                         _stream(dev, stream)))
     return out
 
 
@@ -275,17 +383,21 @@ def forward_fused_batched(X, packed, gamma, bits: int = 8, gran="token", eps: fl
     """`batch` independent layers of one shape: X [B, M, K], packed [B, N, K/4], gamma [B],
     bias [B, N] or None -> Y [B, M, N]; problem b is forward_fused(X[b], packed[b], ...)."""
     torch = _torch()
-    B, M, K = X.shape
-    N = packed.shape[1]
+    bits = _bits(bits)
+    B, M, K = _dims(X, "X", 3)
+    _, N, _ = _dims(packed, "packed", 3)
+    _arg(X, "X", None, _float_types())
+    _arg(packed, "packed", (B, N, K // 4), (torch.uint8,))
+    _arg(gamma, "gamma", (B,), (torch.float32,))
+    _arg(bias, "bias", (B, N), (torch.float32,), optional=True)
+    _out_arg(out, (B, M, N))
+    dev = _gpu(X=X, packed=packed, gamma=gamma, bias=bias, out=out)
     g = _gran_code(gran)
-    if out is None:
-        out = torch.empty((B, M, N), dtype=out_dtype or torch.float32, device=X.device)
-    ws, wsb = _workspace(workspace_size(BL_OP_FORWARD_FUSED, M, N, K, bits, g), X.device,
-                         workspace)
+    out = _new_out(out, (B, M, N), out_dtype, dev)
+    ws, wsb = _workspace(workspace_size(BL_OP_FORWARD_FUSED, M, N, K, bits, g), dev, workspace)
     _check(lib().bitlinear_forward_fused_batched(
         _ptr(X), _dtype_code(X), bits, g, eps, _ptr(packed), _ptr(gamma), _ptr(bias), B, M, N, K,
-        _epi_code(epilogue), _ptr(out), _dtype_code(out), _ptr(ws), wsb,
-        _stream(X.device, stream)))
+        _epi_code(epilogue), _ptr(out), _dtype_code(out), _ptr(ws), wsb, _stream(dev, stream)))
     return out
 
 
@@ -295,16 +407,23 @@ def forward_multi(Xq, act_scale, packed, gamma, bits: int = 8, gran="token", bia
     gamma [P], bias [P, N] or None -> Y [P, M, N]; part p is forward(Xq, act_scale,
     packed[p], gamma[p:p+1], ...)."""
     torch = _torch()
-    M = Xq.shape[0]
-    K = Xq.shape[1] * (1 if bits == 8 else 2)
-    Pn, N = packed.shape[0], packed.shape[1]
+    bits = _bits(bits)
+    M, cols = _dims(Xq, "Xq", 2)
+    Pn, N, _ = _dims(packed, "packed", 3)
+    K = cols * (1 if bits == 8 else 2)
     g = _gran_code(gran)
-    if out is None:
-        out = torch.empty((Pn, M, N), dtype=out_dtype or torch.float32, device=Xq.device)
-    ws, wsb = _workspace(workspace_size(BL_OP_FORWARD, M, N, K, bits, g), Xq.device, workspace)
+    _arg(Xq, "Xq", None, _code_types())
+    _arg(packed, "packed", (Pn, N, K // 4), (torch.uint8,))
+    _arg(act_scale, "act_scale", (_scale_len(M, g),), (torch.float32,))
+    _arg(gamma, "gamma", (Pn,), (torch.float32,))
+    _arg(bias, "bias", (Pn, N), (torch.float32,), optional=True)
+    _out_arg(out, (Pn, M, N))
+    dev = _gpu(Xq=Xq, packed=packed, act_scale=act_scale, gamma=gamma, bias=bias, out=out)
+    out = _new_out(out, (Pn, M, N), out_dtype, dev)
+    ws, wsb = _workspace(workspace_size(BL_OP_FORWARD, M, N, K, bits, g), dev, workspace)
     _check(lib().bitlinear_forward_multi(
         _ptr(Xq), bits, _ptr(act_scale), g, _ptr(packed), _ptr(gamma), _ptr(bias), Pn, M, N, K,
-        _epi_code(epilogue), _ptr(out), _dtype_code(out), _ptr(ws), wsb, _stream(Xq.device, stream)))
+        _epi_code(epilogue), _ptr(out), _dtype_code(out), _ptr(ws), wsb, _stream(dev, stream)))
     return out
 
 
@@ -312,11 +431,15 @@ def rmsnorm(X, delta=None, eps: float = 1e-6, out=None, stream=None):
     """Residual add and RMS norm of bf16 rows: X [M, K] bf16 (overwritten with X + delta
     when delta is given) -> H [M, K] bf16 = X / rms(X)."""
     torch = _torch()
-    M, K = X.shape
+    M, K = _dims(X, "X", 2)
+    _arg(X, "X", None, (torch.bfloat16,))
+    _arg(delta, "delta", (M, K), (torch.bfloat16,), optional=True)
+    _arg(out, "out", (M, K), (torch.bfloat16,), optional=True)
+    dev = _gpu(X=X, delta=delta, out=out)
     if out is None:
         out = torch.empty_like(X)
     _check(lib().bitlinear_rmsnorm(_ptr(X), _ptr(delta), _ptr(out), M, K, eps,
-                                   _stream(X.device, stream)))
+                                   _stream(dev, stream)))
     return out
 
 
@@ -324,20 +447,26 @@ def rmsnorm_quantize(X, delta=None, eps: float = 1e-6, bits: int = 8, gran="toke
                      q_eps: float = 1e-5, out=None, workspace=None, stream=None):
     """rmsnorm followed by quantize_acts of its output: returns (H, Xq, scale)."""
     torch = _torch()
-    M, K = X.shape
+    bits = _bits(bits)
+    M, K = _dims(X, "X", 2)
     g = _gran_code(gran)
-    if out is None:
+    _arg(X, "X", None, (torch.bfloat16,))
+    _arg(delta, "delta", (M, K), (torch.bfloat16,), optional=True)
+    H, Xq, sc = out if out else (None, None, None)
+    if out:
+        _arg(H, "H", (M, K), (torch.bfloat16,))
+        _arg(Xq, "Xq", (M, _code_cols(K, bits)), _code_types())
+        _arg(sc, "act_scale", (_scale_len(M, g),), (torch.float32,))
+    dev = _gpu(X=X, delta=delta, H=H, Xq=Xq, act_scale=sc)
+    if not out:
         H = torch.empty_like(X)
-        Xq = torch.empty((M, K if bits == 8 else K // 2),
-                         dtype=torch.int8 if bits == 8 else torch.uint8, device=X.device)
-        sc = torch.empty((M if g == BL_PER_TOKEN else 1,), dtype=torch.float32, device=X.device)
-    else:
-        H, Xq, sc = out
-    ws, wsb = _workspace(workspace_size(BL_OP_QUANTIZE_ACTS, M, 1, K, bits, g), X.device,
-                         workspace)
+        Xq = torch.empty((M, _code_cols(K, bits)),
+                         dtype=torch.int8 if bits == 8 else torch.uint8, device=dev)
+        sc = torch.empty((_scale_len(M, g),), dtype=torch.float32, device=dev)
+    ws, wsb = _workspace(workspace_size(BL_OP_QUANTIZE_ACTS, M, 1, K, bits, g), dev, workspace)
     _check(lib().bitlinear_rmsnorm_quantize(_ptr(X), _ptr(delta), _ptr(H), M, K, eps, bits, g,
                                             q_eps, _ptr(Xq), _ptr(sc), _ptr(ws), wsb,
-                                            _stream(X.device, stream)))
+                                            _stream(dev, stream)))
     return H, Xq, sc
 
 
@@ -349,18 +478,30 @@ def backward(dY, Xq, act_scale, packed, gamma, bits: int = 8, gran="token", X=No
     W (fp32/bf16, 4-bit activations only) switch on the clipping masks.  `out` may hold
     preallocated tensors under the same keys."""
     torch = _torch()
-    M, N = dY.shape
-    K = packed.shape[1] * 4
+    bits = _bits(bits)
+    M, N = _dims(dY, "dY", 2)
+    _, kq = _dims(packed, "packed", 2)
+    K = kq * 4
     g = _gran_code(gran)
-    dev = dY.device
+    _arg(dY, "dY", None, (torch.bfloat16,))
+    _arg(packed, "packed", (N, kq), (torch.uint8,))
+    _arg(Xq, "Xq", (M, _code_cols(K, bits)), _code_types())
+    _arg(act_scale, "act_scale", (_scale_len(M, g),), (torch.float32,))
+    _arg(gamma, "gamma", (1,), (torch.float32,))
+    _arg(X, "X", (M, K), _float_types(), optional=True)
+    _arg(W, "W", (N, K), _float_types(), optional=True)
     shapes = {"dX": (M, K), "dW": (N, K), "dbias": (N,)}
-    res = {}
+    given = {}
     for name in want:
         if name not in shapes:
             raise ValueError("unknown gradient %r" % name)
         t = (out or {}).get(name)
-        res[name] = t if t is not None else torch.empty(shapes[name], dtype=torch.float32,
-                                                        device=dev)
+        if t is not None:
+            _arg(t, name, shapes[name], (torch.float32,))
+        given[name] = t
+    dev = _gpu(dY=dY, Xq=Xq, act_scale=act_scale, packed=packed, gamma=gamma, X=X, W=W, **given)
+    res = {name: t if t is not None else torch.empty(shapes[name], dtype=torch.float32, device=dev)
+           for name, t in given.items()}
     ws, wsb = _workspace(workspace_size(BL_OP_BACKWARD, M, N, K, bits, g), dev, workspace)
     _check(lib().bitlinear_backward(
         _ptr(dY), _ptr(Xq), bits, _ptr(act_scale), g, _ptr(packed), _ptr(gamma), _ptr(X),

@@ -329,17 +329,26 @@ bl_status bitlinear_forward(const void *Xq, int bits, const float *act_scale, bl
     return device(launch_forward(a, workspace, (hipStream_t)stream), fn);
 }
 
+static bl_status check_fused(const char *fn, const void *X, bl_dtype x_dtype, int bits,
+                             bl_gran gran, float eps, const uint8_t *W_packed, const float *gamma,
+                             const float *bias, int64_t M, int64_t N, int64_t K, bl_epi epi,
+                             void *Y, bl_dtype y_dtype) {
+    if (!X) return fail(BL_EINVAL, "%s: null pointer", fn);
+    if (!is_xdtype(x_dtype)) return fail(BL_EINVAL, "%s: x_dtype must be BL_F32 or BL_BF16", fn);
+    CHECK(check_forward_common(fn, bits, gran, W_packed, gamma, bias, M, N, K, epi, Y, y_dtype));
+    CHECK(check_eps(eps, fn));
+    if (!aligned(X, 16)) return fail(BL_EALIGN, "%s: X needs 16-byte alignment", fn);
+    return BL_OK;
+}
+
 bl_status bitlinear_forward_fused(const void *X, bl_dtype x_dtype, int bits, bl_gran gran,
                                   float eps, const uint8_t *W_packed, const float *gamma,
                                   const float *bias, int64_t M, int64_t N, int64_t K, bl_epi epi,
                                   void *Y, bl_dtype y_dtype, void *workspace,
                                   size_t workspace_bytes, void *stream) {
     static const char fn[] = "bitlinear_forward_fused";
-    if (!X) return fail(BL_EINVAL, "%s: null pointer", fn);
-    if (!is_xdtype(x_dtype)) return fail(BL_EINVAL, "%s: x_dtype must be BL_F32 or BL_BF16", fn);
-    CHECK(check_forward_common(fn, bits, gran, W_packed, gamma, bias, M, N, K, epi, Y, y_dtype));
-    CHECK(check_eps(eps, fn));
-    if (!aligned(X, 16)) return fail(BL_EALIGN, "%s: X needs 16-byte alignment", fn);
+    CHECK(check_fused(fn, X, x_dtype, bits, gran, eps, W_packed, gamma, bias, M, N, K, epi, Y,
+                      y_dtype));
     const size_t need = ws_fused(M, N, K, bits, gran);
     if (need && (!workspace || workspace_bytes < need || !aligned(workspace, 256)))
         return fail(BL_EWORKSPACE, "%s: need %zu bytes of 256-byte aligned workspace", fn, need);
@@ -529,8 +538,9 @@ static bl_status check_norm(const char *fn, void *X, const void *delta, void *H,
     if (M <= 0 || K <= 0 || K % 8 != 0)
         return fail(BL_ESHAPE, "%s: M, K must be positive and K a multiple of 8 (M=%lld K=%lld)",
                     fn, (long long)M, (long long)K);
-    if (M > (1ll << 31) || M * K >= (1ll << 40))
-        return fail(BL_ESHAPE, "%s: M=%lld too large", fn, (long long)M);
+    if (M > (1ll << 31) || K >= (1ll << 31) || M * K >= (1ll << 40))
+        return fail(BL_ESHAPE, "%s: M=%lld, K=%lld too large (K < 2^31, M*K < 2^40)", fn,
+                    (long long)M, (long long)K);
     CHECK(check_eps(eps, fn));
     if (!aligned(X, 16) || !aligned(H, 16) || (delta && !aligned(delta, 16)))
         return fail(BL_EALIGN, "%s: X, delta and H need 16-byte alignment", fn);
