@@ -192,6 +192,35 @@ bl_status bitlinear_forward_fused(const void *X, bl_dtype x_dtype, int bits, bl_
                                   size_t workspace_bytes, void *stream);
 
 /*
+ * bitlinear_forward_fused without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments, equations, results and errors as bitlinear_forward_fused
+ * (whose kernels it runs), minus the workspace: the scratch memory comes from a fixed
+ * array that the library holds on each GPU it runs on until the process ends,
+ * bitlinear_noalloc_scratch_bytes() bytes (64 MiB) each.  It allocates nothing and
+ * calls no allocating routine.
+ *
+ * Limit: calls whose bitlinear_workspace_size(BL_OP_FORWARD_FUSED, M, N, K, bits, gran)
+ * exceeds the scratch size return BL_EWORKSPACE before any HIP call.  The prefill paths
+ * hold about M*K bytes (8-bit codes) or 0.9*M*K bytes (4-bit) there: the 2B prefill at
+ * M = 2048 and the 70B layer at M = 4096 fit, M = 8192 tokens of K = 8192 do not.
+ * Decode-sized calls (up to 4 tokens) need none of it.
+ *
+ * All calls on one GPU share its scratch: calls that may overlap on one GPU (on different
+ * streams, or from different threads) race and must be ordered by the caller.  Every
+ * call clears what it needs cleared itself.  The first call on each device resolves the
+ * scratch address (hipGetSymbolAddress); make it outside graph capture.
+ */
+bl_status bitlinear_forward_fused_noalloc(const void *X, bl_dtype x_dtype, int bits,
+                                          bl_gran gran, float eps, const uint8_t *W_packed,
+                                          const float *gamma, const float *bias, int64_t M,
+                                          int64_t N, int64_t K, bl_epi epi, void *Y,
+                                          bl_dtype y_dtype, void *stream);
+
+/* Bytes of the per-GPU scratch array of bitlinear_forward_fused_noalloc. */
+size_t bitlinear_noalloc_scratch_bytes(void);
+
+/*
  * bitlinear_forward_fused over `batch` independent layers of one shape, in one
  * launch where the shape allows (decode-sized M): problem b computes exactly what
  * bitlinear_forward_fused computes on

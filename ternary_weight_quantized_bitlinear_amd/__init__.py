@@ -13,6 +13,7 @@ The functions mirror the C entry points:
 * :func:`forward`           -> ``bitlinear_forward``
 * :func:`forward_fused`     -> ``bitlinear_forward_fused``
 * :func:`forward_fused_batched` -> ``bitlinear_forward_fused_batched``
+* :func:`forward_fused_noalloc` -> ``bitlinear_forward_fused_noalloc`` (no workspace)
 * :func:`forward_multi`     -> ``bitlinear_forward_multi`` (several projections of one input)
 * :func:`rmsnorm`           -> ``bitlinear_rmsnorm`` (glue between layers)
 * :func:`rmsnorm_quantize`  -> ``bitlinear_rmsnorm_quantize`` (glue + next layer's quantizer)
@@ -65,6 +66,10 @@ def lib() -> ctypes.CDLL:
                                                       I, P, I, P, SZ, P]
         L.bitlinear_forward_multi.argtypes = [P, I, P, I, P, P, P, I64, I64, I64, I64, I, P, I, P,
                                               SZ, P]
+        L.bitlinear_forward_fused_noalloc.argtypes = [P, I, I, I, F, P, P, P, I64, I64, I64, I,
+                                                      P, I, P]
+        L.bitlinear_noalloc_scratch_bytes.argtypes = []
+        L.bitlinear_noalloc_scratch_bytes.restype = SZ
         L.bitlinear_rmsnorm.argtypes = [P, P, P, I64, I64, F, P]
         L.bitlinear_rmsnorm_quantize.argtypes = [P, P, P, I64, I64, F, I, I, F, P, P, P, SZ, P]
         L.bitlinear_quantize_weights_rotated.argtypes = [P, I, I64, I64, F, P, P, P, SZ, P]
@@ -82,7 +87,8 @@ def lib() -> ctypes.CDLL:
         L.bitlinear_version.restype = I
         for n in ("bitlinear_quantize_weights", "bitlinear_quantize_acts", "bitlinear_forward",
                   "bitlinear_forward_fused", "bitlinear_forward_fused_batched",
-                  "bitlinear_forward_multi", "bitlinear_rmsnorm", "bitlinear_rmsnorm_quantize",
+                  "bitlinear_forward_multi", "bitlinear_forward_fused_noalloc",
+                  "bitlinear_rmsnorm", "bitlinear_rmsnorm_quantize",
                   "bitlinear_quantize_weights_rotated", "bitlinear_quantize_acts_rotated",
                   "bitlinear_backward"):
             getattr(L, n).restype = I
@@ -374,6 +380,21 @@ def forward_fused(X, packed, gamma, bits: int = 8, gran="token", eps: float = 1e
                                          _ptr(gamma), _ptr(bias), M, N, K, _epi_code(epilogue),
                                          _ptr(out), _dtype_code(out), _ptr(ws), wsb,
                                          _stream(dev, stream)))
+    return out
+
+
+def forward_fused_noalloc(X, packed, gamma, out, bits: int = 8, gran="token", eps: float = 1e-5,
+                          bias=None, epilogue=None, stream=None):
+    """forward_fused without a workspace: the library's fixed per-GPU scratch is used and
+    nothing is allocated (`out`, the [M, N] result, must be given)."""
+    bits = _bits(bits)
+    if out is None:
+        _fail(BL_EINVAL, "out is required")
+    M, N, K, dev = _fused_args(X, packed, gamma, bias, out)
+    _check(lib().bitlinear_forward_fused_noalloc(_ptr(X), _dtype_code(X), bits, _gran_code(gran),
+                                                 eps, _ptr(packed), _ptr(gamma), _ptr(bias), M,
+                                                 N, K, _epi_code(epilogue), _ptr(out),
+                                                 _dtype_code(out), _stream(dev, stream)))
     return out
 
 

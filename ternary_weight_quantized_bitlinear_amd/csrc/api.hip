@@ -8,6 +8,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "../../include/bitlinear.h"
@@ -109,11 +110,48 @@ size_t ws_fused(int64_t M, int64_t N, int64_t K, int bits, bl_gran gran) {
         if (st_ != BL_OK) return st_;                                                              \
     } while (0)
 
+// Scratch memory of bitlinear_forward_fused_noalloc: one array on each GPU the library
+// runs on, held until the process ends.  Host code never uses the array's name as an
+// address: the device address comes from hipGetSymbolAddress, per device.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+constexpr int kScratchMaxDevices = 64;
+
+}  // namespace
+
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kScratchMaxDevices];
+
+// The current device's scratch address: resolved once per device (with that device
+// current), then reused.
+bl_status scratch_address(void **out, const char *fn) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(BL_EDEVICE, "%s: hipGetDevice: %s", fn, hipGetErrorString(e));
+    if (dev < 0 || dev >= kScratchMaxDevices)
+        return fail(BL_EUNSUPPORTED, "%s: device %d beyond the %d the library tracks", fn, dev,
+                    kScratchMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(BL_EDEVICE, "%s: hipGetSymbolAddress(scratch) on device %d: %s", fn, dev,
+                        hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return BL_OK;
+}
+
 }  // namespace
 
 extern "C" {
 
-int bitlinear_version(void) { return 10100; }  // 1.1.0: bitlinear_forward_multi
+int bitlinear_version(void) { return 10200; }  // 1.2.0: bitlinear_forward_fused_noalloc
 
 const char *bitlinear_status_string(bl_status s) {
     switch (s) {
@@ -399,6 +437,27 @@ bl_status bitlinear_forward_fused(const void *X, bl_dtype x_dtype, int bits, bl_
     const bl::FwdArgs a = make_args(xq, 0, bits, scale, gran, eps, W_packed, gamma, bias, M, N, K,
                                     epi, Y, y_dtype);
     return device(launch_forward(a, gemm_ws, s), fn);
+}
+
+size_t bitlinear_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+bl_status bitlinear_forward_fused_noalloc(const void *X, bl_dtype x_dtype, int bits, bl_gran gran,
+                                          float eps, const uint8_t *W_packed, const float *gamma,
+                                          const float *bias, int64_t M, int64_t N, int64_t K,
+                                          bl_epi epi, void *Y, bl_dtype y_dtype, void *stream) {
+    static const char fn[] = "bitlinear_forward_fused_noalloc";
+    CHECK(check_fused(fn, X, x_dtype, bits, gran, eps, W_packed, gamma, bias, M, N, K, epi, Y,
+                      y_dtype));
+    const size_t need = ws_fused(M, N, K, bits, gran);
+    if (need > kScratchBytes)
+        return fail(BL_EWORKSPACE, "%s: M=%lld N=%lld K=%lld bits=%d needs %zu bytes of scratch; "
+                    "the library's scratch holds %zu (use bitlinear_forward_fused with a "
+                    "workspace)", fn, (long long)M, (long long)N, (long long)K, bits, need,
+                    kScratchBytes);
+    void *ws = nullptr;
+    CHECK(scratch_address(&ws, fn));
+    return bitlinear_forward_fused(X, x_dtype, bits, gran, eps, W_packed, gamma, bias, M, N, K, epi,
+                                   Y, y_dtype, ws, kScratchBytes, stream);
 }
 
 bl_status bitlinear_forward_fused_batched(const void *X, bl_dtype x_dtype, int bits,

@@ -28,7 +28,8 @@ def test_exports_every_header_function(L):
         "bitlinear_rmsnorm_quantize", "bitlinear_workspace_size", "bitlinear_status_string",
         "bitlinear_last_error", "bitlinear_version", "bitlinear_hadamard_block",
         "bitlinear_quantize_weights_rotated", "bitlinear_quantize_acts_rotated",
-        "bitlinear_backward"}
+        "bitlinear_backward", "bitlinear_forward_fused_noalloc",
+        "bitlinear_noalloc_scratch_bytes"}
     for n in names:
         assert hasattr(L, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", bl.LIB_PATH], capture_output=True,
@@ -46,7 +47,7 @@ def test_library_is_gfx950_code():
 def test_status_strings_and_version(L):
     for s in range(7):
         assert L.bitlinear_status_string(s).decode()
-    assert L.bitlinear_version() >= 10100  # 1.1: bitlinear_forward_multi
+    assert L.bitlinear_version() >= 10200  # 1.2: bitlinear_forward_fused_noalloc
 
 
 def test_workspace_sizes(L):
@@ -146,6 +147,39 @@ def test_forward_fused_rejects(L):
              None) == bl.BL_EWORKSPACE
     assert f(P(A), 2, 8, 0, 1e-5, P(A), P(A), None, 1, 6912, 2560, 0, P(A), 1, None, 0,
              None) == bl.BL_EINVAL
+
+
+def test_forward_fused_noalloc_rejects(L):
+    f = L.bitlinear_forward_fused_noalloc
+    assert L.bitlinear_noalloc_scratch_bytes() == 64 << 20
+    # the same argument checks as bitlinear_forward_fused, before any HIP call
+    assert f(None, 1, 8, 0, 1e-5, P(A), P(A), None, 1, 6912, 2560, 0, P(A), 1, None) == bl.BL_EINVAL
+    assert f(P(A), 1, 6, 0, 1e-5, P(A), P(A), None, 1, 6912, 2560, 0, P(A), 1, None) == bl.BL_EINVAL
+    assert f(P(A), 1, 8, 0, 1e-5, P(A), P(A), None, 1, 6912, 2500, 0, P(A), 1, None) == bl.BL_ESHAPE
+    assert f(P(A + 4), 1, 8, 0, 1e-5, P(A), P(A), None, 1, 6912, 2560, 0, P(A), 1,
+             None) == bl.BL_EALIGN
+    # sizes whose scratch would exceed the fixed array are rejected with the limit named
+    need = L.bitlinear_workspace_size(bl.BL_OP_FORWARD_FUSED, 8192, 6912, 8192, 8, 0)
+    assert need > 64 << 20
+    assert f(P(A), 1, 8, 0, 1e-5, P(A), P(A), None, 8192, 6912, 8192, 0, P(A), 1,
+             None) == bl.BL_EWORKSPACE
+    msg = L.bitlinear_last_error().decode()
+    assert "scratch" in msg and str(need) in msg and str(64 << 20) in msg
+    # the 2B prefill and the 70B layer fit, with either code width; twice the 70B tokens
+    # do not
+    for M, N, K, bits, fits in ((2048, 6912, 2560, 8, True), (2048, 2560, 6912, 4, True),
+                                (4096, 28672, 8192, 8, True), (4096, 28672, 8192, 4, True),
+                                (8192, 28672, 8192, 8, False), (8192, 28672, 8192, 4, False)):
+        ws = L.bitlinear_workspace_size(bl.BL_OP_FORWARD_FUSED, M, N, K, bits, 0)
+        assert (ws <= 64 << 20) == fits, (M, N, K, bits, ws)
+
+
+def test_forward_fused_noalloc_without_device(L):
+    if _gpu_visible():
+        pytest.skip("a GPU is visible: this test needs a host with no device")
+    st = L.bitlinear_forward_fused_noalloc(P(A), 1, 8, 0, 1e-5, P(A), P(A), None, 16, 6912, 2560,
+                                           0, P(A), 1, None)
+    assert st == bl.BL_EDEVICE and L.bitlinear_last_error().decode()
 
 
 def test_forward_fused_batched_rejects(L):

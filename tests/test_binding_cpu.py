@@ -86,6 +86,10 @@ CASES = [
     ("fused: workspace dtype", lambda: bl.forward_fused(
         t((2048, K)), t((N, K // 4), torch.uint8), t((1,)), workspace=t((1 << 20,))),
      bl.BL_EINVAL, "GPU"),
+    ("noalloc: out shape", lambda: bl.forward_fused_noalloc(
+        t((M, K)), t((N, K // 4), torch.uint8), t((1,)), t((M, N + 1))), bl.BL_ESHAPE, "out"),
+    ("noalloc: host tensors", lambda: bl.forward_fused_noalloc(
+        t((M, K)), t((N, K // 4), torch.uint8), t((1,)), t((M, N))), bl.BL_EINVAL, "GPU"),
     # batched and multi-part
     ("batched: gamma per problem", lambda: bl.forward_fused_batched(
         t((4, 1, K)), t((4, N, K // 4), torch.uint8), t((3,))), bl.BL_ESHAPE, "gamma"),
