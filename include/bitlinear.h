@@ -70,15 +70,22 @@ typedef enum {
     BL_EWORKSPACE = 6    /* workspace missing or smaller than bitlinear_workspace_size() */
 } bl_status;
 
-typedef enum { BL_F32 = 0, BL_BF16 = 1, BL_I32 = 2 } bl_dtype;
-typedef enum { BL_PER_TOKEN = 0, BL_PER_TENSOR = 1 } bl_gran;
-typedef enum { BL_EPI_NONE = 0, BL_EPI_RELU2 = 1 } bl_epi;
+/* The argument enums carry two range markers (never valid arguments) that give them
+ * the whole range of int: any int a caller passes is a value of the type, which every
+ * call checks and rejects with BL_EINVAL when it names no enumerator (a C++ enum with
+ * only small enumerators would make out-of-range values undefined to read). */
+#define BL_ENUM_RANGE(prefix) prefix##_RANGE_MIN_ = -2147483647 - 1, prefix##_RANGE_MAX_ = 2147483647
+
+typedef enum { BL_F32 = 0, BL_BF16 = 1, BL_I32 = 2, BL_ENUM_RANGE(BL_DTYPE) } bl_dtype;
+typedef enum { BL_PER_TOKEN = 0, BL_PER_TENSOR = 1, BL_ENUM_RANGE(BL_GRAN) } bl_gran;
+typedef enum { BL_EPI_NONE = 0, BL_EPI_RELU2 = 1, BL_ENUM_RANGE(BL_EPI) } bl_epi;
 typedef enum {
     BL_OP_QUANTIZE_WEIGHTS = 0,
     BL_OP_QUANTIZE_ACTS = 1,
     BL_OP_FORWARD = 2,
     BL_OP_FORWARD_FUSED = 3,
-    BL_OP_BACKWARD = 4
+    BL_OP_BACKWARD = 4,
+    BL_ENUM_RANGE(BL_OP)
 } bl_op;
 
 /*

@@ -26,7 +26,8 @@ import os
 import re
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG_DIR, "libbitlinear.so")
+# BITLINEAR_LIB selects another build of the library (the tests' host-sanitizer build)
+LIB_PATH = os.environ.get("BITLINEAR_LIB") or os.path.join(PKG_DIR, "libbitlinear.so")
 HEADER = os.path.join(os.path.dirname(PKG_DIR), "include", "bitlinear.h")
 
 # enums of include/bitlinear.h
