@@ -265,13 +265,41 @@ __global__ void __launch_bounds__(Tile<kBN>::kThreads, kBN == 128 ? 2 : 1) gemm_
         expand_b(bw, b0);
     }
 
-    // ---- epilogue straight from the accumulators.  The MFMAs compute the transposed
-    // tile (weights as the first operand), so lane l holds acc[i][j][r] =
-    // Y[32i + l%32][32j + 8(r/4) + 4(l/32) + r%4]: four consecutive outputs of one
-    // token row per r/4, stored together (8 bytes of bf16, 16 of fp32/int32) when N
-    // keeps them aligned.  The token's dequant factor and code sum are per lane.
+    // ---- epilogue.  The MFMAs compute the transposed tile (weights as the first
+    // operand), so lane l holds acc[i][j][r] = Y[32i + l%32][32j + 8(r/4) + 4(l/32) + r%4]:
+    // four consecutive outputs of one token row per r/4.  The token's dequant factor and
+    // code sum are per lane.
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the ring's last (dummy) loads
-    const bool vec = (p.N & 3) == 0;
+    __syncthreads();                     // every wave past its last ring read: the ring is free
+    auto outputs = [&](const v16i &c, int q, float f, int cs, int n, float (&y)[4], int (&av)[4])
+        __attribute__((always_inline)) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            av[t] = c[4 * q + t] - cs;
+            float v = __fmul_rn((float)av[t], f);
+            if (kBias) v = __fadd_rn(v, n + t < p.N ? p.bias[n + t] : 0.0f);
+            if (kRelu2) {
+                const float rr = v > 0.0f ? v : 0.0f;
+                v = __fmul_rn(rr, rr);
+            }
+            y[t] = v;
+        }
+    };
+    // Stores go out through LDS when the wave's whole 64-column strip lies inside N and
+    // rows are 16-byte aligned: each 32-row slice is written into the wave's own LDS
+    // region in row order, then read back 16 bytes per lane with consecutive lanes along
+    // a row, so that every store instruction writes whole 128-byte lines (8 rows of bf16,
+    // 4 of fp32 / int32) instead of 16-byte pieces of 32 rows: the L2's request rate, not
+    // the bytes, bounded the direct stores.
+    constexpr int kOutB = kYD == 1 ? 2 : 4;
+    constexpr int kRowB = WN * kOutB;                  // 128 or 256 bytes per wave row
+    constexpr int kPitch = kRowB + (kYD == 1 ? 8 : 16);  // padded: rows start on other banks
+    constexpr int kLanesPerRow = kRowB / 16;
+    constexpr int kRowsPerStore = 64 / kLanesPerRow;
+    static_assert(kWaves * 32 * kPitch <= kStages * kStageBytes, "staging fits the ring");
+    const int nw0 = n0 + WN * wn;
+    const bool staged = nw0 + WN <= p.N && ((int64_t)p.N * kOutB) % 16 == 0;
+    uint8_t *stg = smem + wave * 32 * kPitch;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int ml = 128 * wm + 32 * i + r32;
@@ -279,28 +307,57 @@ __global__ void __launch_bounds__(Tile<kBN>::kThreads, kBN == 128 ? 2 : 1) gemm_
         const float f = s_f[ml];
         const int cs = s_sum[ml];
         const bool m_ok = m < p.M;
+        if (staged) {
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int nl = 32 * j + 8 * q + 4 * kg;  // column within the strip
+                    float y[4];
+                    int av[4];
+                    outputs(acc[i][j], q, f, cs, nw0 + nl, y, av);
+                    uint8_t *dst = stg + r32 * kPitch + nl * kOutB;
+                    if (kYD == 2) {
+                        *reinterpret_cast<int4 *>(dst) = make_int4(av[0], av[1], av[2], av[3]);
+                    } else if (kYD == 1) {
+                        typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+                        const bf2 lo = {(__bf16)y[0], (__bf16)y[1]};
+                        const bf2 hi = {(__bf16)y[2], (__bf16)y[3]};
+                        *reinterpret_cast<uint2 *>(dst) = make_uint2(
+                            __builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+                    } else {
+                        *reinterpret_cast<float4 *>(dst) = make_float4(y[0], y[1], y[2], y[3]);
+                    }
+                }
+            }
+            // the slice's rows, whole: this wave's LDS writes complete before its reads
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+            for (int t = 0; t < 32 / kRowsPerStore; ++t) {
+                const int row = kRowsPerStore * t + lane / kLanesPerRow;
+                const int cb = 16 * (lane % kLanesPerRow);
+                const uint4 v = *reinterpret_cast<const uint4 *>(stg + row * kPitch + cb);
+                const int mr = m0 + 128 * wm + 32 * i + row;
+                if (mr < p.M)
+                    *reinterpret_cast<uint4 *>(static_cast<uint8_t *>(p.y) +
+                                               ((size_t)mr * p.N + nw0) * kOutB + cb) = v;
+            }
+            // reads of this slice done before the next slice's writes reuse the region
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            continue;
+        }
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
             const v16i c = acc[i][j];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int n = n0 + WN * wn + 32 * j + 8 * q + 4 * kg;
+                const int n = nw0 + 32 * j + 8 * q + 4 * kg;
                 const size_t idx = (size_t)m * p.N + n;
                 float y[4];
                 int av[4];
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    av[t] = c[4 * q + t] - cs;
-                    float v = __fmul_rn((float)av[t], f);
-                    if (kBias) v = __fadd_rn(v, n + t < p.N ? p.bias[n + t] : 0.0f);
-                    if (kRelu2) {
-                        const float rr = v > 0.0f ? v : 0.0f;
-                        v = __fmul_rn(rr, rr);
-                    }
-                    y[t] = v;
-                }
+                outputs(c, q, f, cs, n, y, av);
                 if (!m_ok) continue;
-                if (vec && n + 3 < p.N) {
+                if ((p.N & 3) == 0 && n + 3 < p.N) {
                     if (kYD == 2) {
                         *reinterpret_cast<int4 *>(static_cast<int32_t *>(p.y) + idx) =
                             make_int4(av[0], av[1], av[2], av[3]);

@@ -246,8 +246,36 @@ gemm_f6f4_kernel(F6Params p) {
 
     // ---- epilogue: lane l holds acc[i][j][r] = 4 x sum for token 64 wt + 32 i + l % 32
     // and row 128 wn + 32 j + 8 (r / 4) + 4 (l / 32) + r % 4: four consecutive outputs
-    // of one token per r / 4, stored together when N keeps them aligned
-    wait_vm<0>();  // the ring's last (dummy) loads
+    // of one token per r / 4
+    wait_vm<0>();     // the ring's last (dummy) loads
+    __syncthreads();  // every wave past its last ring read: the ring is free
+    auto outputs = [&](const v16f &c, int q, float f, int cs, int n, float (&y)[4], int (&av)[4])
+        __attribute__((always_inline)) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            av[t] = (int)(4.0f * c[4 * q + t]) - cs;  // exact: an integer below 2^24
+            float v = __fmul_rn((float)av[t], f);
+            if (kBias) v = __fadd_rn(v, n + t < p.N ? p.bias[n + t] : 0.0f);
+            if (kRelu2) {
+                const float rr = v > 0.0f ? v : 0.0f;
+                v = __fmul_rn(rr, rr);
+            }
+            y[t] = v;
+        }
+    };
+    // Stores go out through LDS, as in the int8 GEMM, in half strips of 64 columns: each
+    // 32-row slice is written into the wave's own LDS region in row order and read back 16
+    // bytes per lane along rows, so every store instruction writes whole 128-byte lines.
+    // Used when the half strip lies inside N, rows are 16-byte aligned and the waves'
+    // regions fit the ring (else the direct stores below).
+    constexpr int kOutB = kYD == 1 ? 2 : 4;
+    constexpr int kRowB = 64 * kOutB;
+    constexpr int kPitch = kRowB + (kYD == 1 ? 8 : 16);
+    constexpr int kLanesPerRow = kRowB / 16;
+    constexpr int kRowsPerStore = 64 / kLanesPerRow;
+    constexpr bool kCanStage = F6Tile<kBN>::kWaves * 32 * kPitch <= kStages * T::kStageBytes;
+    uint8_t *stg = smem + wave * 32 * kPitch;
+    const bool rows16 = ((int64_t)p.N * kOutB) % 16 == 0;
     const bool vec = (p.N & 3) == 0;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -257,51 +285,82 @@ gemm_f6f4_kernel(F6Params p) {
         const int cs = s_sum[ml];
         const bool m_ok = m < p.M;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const v16f c = acc[i][j];
+        for (int h = 0; h < 2; ++h) {
+            const int nh0 = n0 + 128 * wn + 64 * h;  // first column of the half strip
+            if (kCanStage && rows16 && nh0 + 64 <= p.N) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int n = n0 + 128 * wn + 32 * j + 8 * q + 4 * g;
-                const size_t idx = (size_t)m * p.N + n;
-                float y[4];
-                int av[4];
+                for (int jj = 0; jj < 2; ++jj) {
 #pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    av[t] = (int)(4.0f * c[4 * q + t]) - cs;  // exact: an integer below 2^24
-                    float v = __fmul_rn((float)av[t], f);
-                    if (kBias) v = __fadd_rn(v, n + t < p.N ? p.bias[n + t] : 0.0f);
-                    if (kRelu2) {
-                        const float rr = v > 0.0f ? v : 0.0f;
-                        v = __fmul_rn(rr, rr);
-                    }
-                    y[t] = v;
-                }
-                if (!m_ok) continue;
-                if (vec && n + 3 < p.N) {
-                    if (kYD == 2) {
-                        *reinterpret_cast<int4 *>(static_cast<int32_t *>(p.y) + idx) =
-                            make_int4(av[0], av[1], av[2], av[3]);
-                    } else if (kYD == 1) {
-                        typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
-                        const bf2 lo = {(__bf16)y[0], (__bf16)y[1]};
-                        const bf2 hi = {(__bf16)y[2], (__bf16)y[3]};
-                        *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(p.y) + idx) =
-                            make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
-                    } else {
-                        *reinterpret_cast<float4 *>(static_cast<float *>(p.y) + idx) =
-                            make_float4(y[0], y[1], y[2], y[3]);
-                    }
-                } else {
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) {
-                        if (n + t >= p.N) continue;
-                        if (kYD == 2) static_cast<int32_t *>(p.y)[idx + t] = av[t];
-                        else if (kYD == 1) static_cast<uint16_t *>(p.y)[idx + t] = (uint16_t)to_bf16_bits(y[t]);
-                        else static_cast<float *>(p.y)[idx + t] = y[t];
+                    for (int q = 0; q < 4; ++q) {
+                        const int nl = 32 * jj + 8 * q + 4 * g;
+                        float y[4];
+                        int av[4];
+                        outputs(acc[i][2 * h + jj], q, f, cs, nh0 + nl, y, av);
+                        uint8_t *dst = stg + r32 * kPitch + nl * kOutB;
+                        if (kYD == 2) {
+                            *reinterpret_cast<int4 *>(dst) = make_int4(av[0], av[1], av[2], av[3]);
+                        } else if (kYD == 1) {
+                            typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+                            const bf2 lo = {(__bf16)y[0], (__bf16)y[1]};
+                            const bf2 hi = {(__bf16)y[2], (__bf16)y[3]};
+                            *reinterpret_cast<uint2 *>(dst) = make_uint2(
+                                __builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+                        } else {
+                            *reinterpret_cast<float4 *>(dst) = make_float4(y[0], y[1], y[2], y[3]);
+                        }
                     }
                 }
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+                for (int t = 0; t < 32 / kRowsPerStore; ++t) {
+                    const int row = kRowsPerStore * t + lane / kLanesPerRow;
+                    const int cb = 16 * (lane % kLanesPerRow);
+                    const uint4 v = *reinterpret_cast<const uint4 *>(stg + row * kPitch + cb);
+                    const int mr = m0 + 64 * wt + 32 * i + row;
+                    if (mr < p.M)
+                        *reinterpret_cast<uint4 *>(static_cast<uint8_t *>(p.y) +
+                                                   ((size_t)mr * p.N + nh0) * kOutB + cb) = v;
+                }
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                continue;
             }
-            __builtin_amdgcn_sched_barrier(0);  // one tile at a time: bounded registers
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) {
+                const v16f c = acc[i][2 * h + jj];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int n = nh0 + 32 * jj + 8 * q + 4 * g;
+                    const size_t idx = (size_t)m * p.N + n;
+                    float y[4];
+                    int av[4];
+                    outputs(c, q, f, cs, n, y, av);
+                    if (!m_ok) continue;
+                    if (vec && n + 3 < p.N) {
+                        if (kYD == 2) {
+                            *reinterpret_cast<int4 *>(static_cast<int32_t *>(p.y) + idx) =
+                                make_int4(av[0], av[1], av[2], av[3]);
+                        } else if (kYD == 1) {
+                            typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+                            const bf2 lo = {(__bf16)y[0], (__bf16)y[1]};
+                            const bf2 hi = {(__bf16)y[2], (__bf16)y[3]};
+                            *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(p.y) + idx) =
+                                make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+                        } else {
+                            *reinterpret_cast<float4 *>(static_cast<float *>(p.y) + idx) =
+                                make_float4(y[0], y[1], y[2], y[3]);
+                        }
+                    } else {
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) {
+                            if (n + t >= p.N) continue;
+                            if (kYD == 2) static_cast<int32_t *>(p.y)[idx + t] = av[t];
+                            else if (kYD == 1) static_cast<uint16_t *>(p.y)[idx + t] = (uint16_t)to_bf16_bits(y[t]);
+                            else static_cast<float *>(p.y)[idx + t] = y[t];
+                        }
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);  // one tile at a time: bounded registers
+            }
         }
     }
 }
