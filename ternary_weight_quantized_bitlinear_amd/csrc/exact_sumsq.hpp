@@ -35,6 +35,35 @@ constexpr int kSqLimbs = 18;   // 576-bit slow-path accumulator, units of 2^-266
 // biased exponent of a bf16 value (bits in the low 16 bits of b)
 __host__ __device__ inline int sq_exp(uint32_t b) { return (int)((b >> 7) & 0xFFu); }
 
+// The window step without branches, for the kernels' per-lane loops: two 64-bit partial
+// sums, A for squares with d <= 40 (as m^2 2^(40 - d)) and B for 40 < d <= kSqFrac (as
+// m^2 2^(kSqFrac - d)); each term is below 2^56, so up to 128 steps cannot overflow
+// either, and the window sum is A 2^40 + B (sq_acc_flush).  Returns whether the value
+// was a nonzero one below the window (left out).
+struct SqAcc {
+    uint64_t a = 0, b = 0;
+};
+constexpr int kSqAccSteps = 128;  // steps between flushes
+
+__host__ __device__ inline bool sq_acc_step(uint32_t b, int E, SqAcc &acc) {
+    const int e = sq_exp(b);
+    const uint32_t m = (b & 0x7Fu) | (e ? 0x80u : 0u);
+    const int d = 2 * (E - (e ? e : 1));
+    const bool high = d <= 40;
+    const bool in = d <= kSqFrac;
+    const uint64_t v = (uint64_t)(m * m) << ((high ? 40 - d : kSqFrac - d) & 63);
+    acc.a += high ? v : 0;
+    acc.b += !high && in ? v : 0;
+    return !in && m != 0;
+}
+
+// adds the partial sums to the 128-bit window sum and clears them
+__host__ __device__ inline void sq_acc_flush(SqAcc &acc, u128 &sum) {
+    sum += ((u128)acc.a << 40) + acc.b;
+    acc.a = 0;
+    acc.b = 0;
+}
+
 // Adds the square of bf16 b to the window sum acc of a row whose largest biased exponent
 // is E (E >= 1).  Returns false if the value lies below the window; then *sq = m^2 and
 // *bin = e' are what the caller adds to its bins instead.
@@ -64,6 +93,49 @@ __host__ __device__ inline double sq_round(u128 acc, int scale) {
     const u128 half = (u128)1 << (sh - 1);
     if (rem > half || (rem == half && (mant & 1u))) mant += 1;
     return ldexp((double)mant, scale + sh);
+}
+
+// The exact sum of a few window sums taken at different anchors: sums[i] in units of
+// 2^(2 (E[i] - 134) - kSqFrac), rounded once to fp64.  Returns false (and leaves *out)
+// when the anchors of the nonzero sums lie more than 16 exponents apart: the caller
+// then takes the general path.
+__host__ __device__ inline bool sq_round_anchored(const u128 *sums, const int *E, int n,
+                                                  double *out) {
+    int emin = 1 << 20, emax = -1;
+    for (int i = 0; i < n; ++i)
+        if (sums[i] != 0) {
+            emin = E[i] < emin ? E[i] : emin;
+            emax = E[i] > emax ? E[i] : emax;
+        }
+    if (emax < 0) {
+        *out = 0.0;
+        return true;
+    }
+    if (emax - emin > 16) return false;
+    // 192-bit total (top:low) in units of the smallest anchor's window
+    u128 low = 0;
+    uint64_t top = 0;
+    for (int i = 0; i < n; ++i) {
+        if (sums[i] == 0) continue;
+        const int sh = 2 * (E[i] - emin);  // 0..32
+        const u128 part = sums[i] << sh;
+        const uint64_t ptop = sh ? (uint64_t)(sums[i] >> (128 - sh)) : 0;
+        low += part;
+        top += ptop + (low < part ? 1u : 0u);
+    }
+    const int scale = 2 * emin - 268 - kSqFrac;
+    if (top == 0) {
+        *out = sq_round(low, scale);
+        return true;
+    }
+    // drop the lowest r bits so that the total fits 128 bits; they lie far below the
+    // rounding position (the top bit stays at 127, the guard bit near 74), so they only
+    // matter as a sticky bit, jammed into bit 0
+    const int r = 64 - __builtin_clzll(top);
+    u128 w = (low >> r) | ((u128)top << (128 - r));
+    if (low & (((u128)1 << r) - 1)) w |= 1;
+    *out = sq_round(w, scale + r);
+    return true;
 }
 
 // big += v * 2^shift (big in 32-bit limbs, least significant first)

@@ -17,12 +17,14 @@ namespace {
 
 constexpr int kNormThreads = 256;
 constexpr int kNormWaves = kNormThreads / kWave;
+static_assert(kNormWaves == 4, "the wave sums are combined four at a time");
 constexpr int kNormRegGroups = 4;  // 8-element groups per thread held in registers
 
 struct NormShared {
     uint64_t bins[256];   // slow path: sum of m^2 per biased exponent
     uint64_t wsum[kNormWaves][2];
-    int wmax[kNormWaves];
+    int wspill[kNormWaves];
+    int wmax[kNormWaves];  // each wave's largest biased exponent
     uint32_t big[kSqLimbs];  // slow path: the exact total
     double S;
 };
@@ -35,6 +37,18 @@ __device__ __forceinline__ int wave_max_int(int v) {
     v = max(v, dpp_mov<kDppBcast15, 0xA>(0, v));
     v = max(v, dpp_mov<kDppBcast31, 0xC>(0, v));
     return __builtin_amdgcn_readlane(v, 63);
+}
+
+// The sum over the wave of each lane's 128-bit integer, exact: six 24-bit digits, each
+// summed with DPP lane moves (64 digits stay below 2^30), then recombined with carries.
+__device__ __forceinline__ u128 wave_sum_u128(u128 v) {
+    u128 total = 0;
+#pragma unroll
+    for (int d = 0; d < 6; ++d) {
+        const int digit = (int)((uint32_t)(v >> (24 * d)) & 0xFFFFFFu);
+        total += (u128)(uint32_t)wave_sum(digit) << (24 * d);
+    }
+    return total;
 }
 
 template <int kN>
@@ -58,7 +72,6 @@ __device__ __forceinline__ uint4 keep_get(const uint4 (&keep)[kN], int64_t i) {
 __device__ __forceinline__ double row_residual_r(uint16_t *xr, const uint16_t *dr, int64_t n8,
                                                  float eps, uint4 (&keep)[kNormRegGroups],
                                                  NormShared &sh) {
-    sh.bins[threadIdx.x] = 0;  // kNormThreads == 256 bins
     int emax = 0;
     for (int64_t u = threadIdx.x, i = 0; u < n8; u += kNormThreads, ++i) {
         uint4 q = reinterpret_cast<const uint4 *>(xr)[u];
@@ -79,53 +92,78 @@ __device__ __forceinline__ double row_residual_r(uint16_t *xr, const uint16_t *d
         for (int j = 0; j < 4; ++j) emax = max(emax, max(sq_exp(w[j]), sq_exp(w[j] >> 16)));
         if (i < kNormRegGroups) keep_put(keep, i, q);
     }
-    emax = wave_max_int(emax);
+    // Each wave anchors its window at its own largest exponent (no barrier needed for
+    // it); the four wave sums are combined exactly after the block's one barrier.  Per
+    // lane, the squares go into two 64-bit partial sums, flushed into a 128-bit sum.
     const int wv = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
-    if (lane == 0) sh.wmax[wv] = emax;
-    __syncthreads();
-    int E = 1;
-#pragma unroll
-    for (int i = 0; i < kNormWaves; ++i) E = max(E, sh.wmax[i]);
-    // the window sum of this thread's squares; values below the window go to the bins
+    const int Ew = max(wave_max_int(emax), 1);
+    SqAcc part;
     u128 acc = 0;
-    int spill = 0;
+    bool spill = false;
     for (int64_t u = threadIdx.x, i = 0; u < n8; u += kNormThreads, ++i) {
         const uint4 q = i < kNormRegGroups ? keep_get(keep, i)
                                            : reinterpret_cast<const uint4 *>(xr)[u];
         const uint32_t w[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            uint32_t sq;
-            int bin;
-            if (!sq_window_add(w[j / 2] >> (16 * (j % 2)), E, acc, &sq, &bin)) {
-                atomicAdd(reinterpret_cast<unsigned long long *>(&sh.bins[bin]),
-                          (unsigned long long)sq);
-                spill = 1;
+        for (int j = 0; j < 8; ++j) spill |= sq_acc_step(w[j / 2] >> (16 * (j % 2)), Ew, part);
+        if ((i + 1) % (kSqAccSteps / 8) == 0) sq_acc_flush(part, acc);
+    }
+    sq_acc_flush(part, acc);
+    // integer sums: the same total in any order
+    const u128 wsum = wave_sum_u128(acc);
+    const bool wspill = __ballot(spill) != 0;
+    if (lane == 0) {
+        sh.wsum[wv][0] = (uint64_t)wsum;
+        sh.wsum[wv][1] = (uint64_t)(wsum >> 64);
+        sh.wspill[wv] = wspill ? 1 : 0;
+        sh.wmax[wv] = Ew;
+    }
+    __syncthreads();
+    u128 sums[kNormWaves];
+    int E[kNormWaves];
+    int any_spill = 0, Erow = 1;
+#pragma unroll
+    for (int i = 0; i < kNormWaves; ++i) {
+        sums[i] = ((u128)sh.wsum[i][1] << 64) | sh.wsum[i][0];
+        E[i] = sh.wmax[i];
+        any_spill |= sh.wspill[i];
+        Erow = max(Erow, E[i]);
+    }
+    double S = 0.0;
+    const bool same = E[0] == E[1] && E[1] == E[2] && E[2] == E[3];
+    if (!any_spill && same) {  // the usual case: every wave's largest in one binade
+        S = sq_round(sums[0] + sums[1] + sums[2] + sums[3], 2 * E[0] - 268 - kSqFrac);
+    } else if (any_spill || !sq_round_anchored(sums, E, kNormWaves, &S)) {
+        // rare: values more than 2^40 below their wave's largest, or waves whose largest
+        // values lie far apart.  Everything again, anchored at the row's largest: the
+        // window sums, and the squares below the window in exponent bins (integer sums),
+        // added exactly
+        sh.bins[threadIdx.x] = 0;  // kNormThreads == 256 bins
+        __syncthreads();           // bins cleared; every wave has read sh.wsum above
+        u128 acc2 = 0;
+        for (int64_t u = threadIdx.x, i = 0; u < n8; u += kNormThreads, ++i) {
+            const uint4 q = i < kNormRegGroups ? keep_get(keep, i)
+                                               : reinterpret_cast<const uint4 *>(xr)[u];
+            const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+            for (int j = 0; j < 8; ++j) {
+                uint32_t sq;
+                int bin;
+                if (!sq_window_add(w[j / 2] >> (16 * (j % 2)), Erow, acc2, &sq, &bin))
+                    atomicAdd(reinterpret_cast<unsigned long long *>(&sh.bins[bin]),
+                              (unsigned long long)sq);
             }
         }
-    }
-    // integer sums: the same total in any order
-    uint64_t lo = (uint64_t)acc, hi = (uint64_t)(acc >> 64);
-#pragma unroll
-    for (int o = kWave / 2; o > 0; o >>= 1) {
-        const uint64_t l2 = __shfl_xor(lo, o), h2 = __shfl_xor(hi, o);
-        const u128 t = (((u128)hi << 64) | lo) + (((u128)h2 << 64) | l2);
-        lo = (uint64_t)t;
-        hi = (uint64_t)(t >> 64);
-    }
-    if (lane == 0) {
-        sh.wsum[wv][0] = lo;
-        sh.wsum[wv][1] = hi;
-    }
-    const int any_spill = __syncthreads_or(spill);
-    u128 total = 0;
-#pragma unroll
-    for (int i = 0; i < kNormWaves; ++i) total += ((u128)sh.wsum[i][1] << 64) | sh.wsum[i][0];
-    double S;
-    if (!any_spill) {
-        S = sq_round(total, 2 * E - 268 - kSqFrac);
-    } else {
-        if (threadIdx.x == 0) sh.S = sq_round_with_bins(total, E, sh.bins, sh.big);
+        const u128 wsum2 = wave_sum_u128(acc2);
+        if (lane == 0) {
+            sh.wsum[wv][0] = (uint64_t)wsum2;
+            sh.wsum[wv][1] = (uint64_t)(wsum2 >> 64);
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            u128 total = 0;
+            for (int i = 0; i < kNormWaves; ++i) total += ((u128)sh.wsum[i][1] << 64) | sh.wsum[i][0];
+            sh.S = sq_round_with_bins(total, Erow, sh.bins, sh.big);
+        }
         __syncthreads();
         S = sh.S;
     }

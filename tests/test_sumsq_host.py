@@ -1,8 +1,9 @@
 """The RMS norm's exact sum of squares as the kernels compute it, run on the CPU.
 
 tests/host/sumsq_host.hip builds the kernels' own helpers (csrc/exact_sumsq.hpp) for the
-host and runs the kernels' algorithm on one row: the row's largest exponent, a 128-bit
-window sum, exponent bins for values far below the largest, and one rounding to fp64.
+host and runs the kernels' algorithm on one row: per-wave anchors (each wave's largest
+exponent), 128-bit window sums combined exactly, and, when needed, the general path with
+exponent bins for values far below the row's largest; one rounding to fp64.
 Each result must equal the exact rational sum rounded to nearest, ties to even ("BitNet
 2B4T Guide", "3. Sub-Layer Normalization (SubLN)": the mean square of the row, read as
 the exact sum rounded once).  Both the fast path (everything in the window) and the slow
@@ -56,7 +57,7 @@ def _bf(vals):
     return workloads.to_bf16_bits(np.asarray(vals, dtype=np.float32))
 
 
-@pytest.mark.parametrize("k", [1, 2, 7, 64, 1000])
+@pytest.mark.parametrize("k", [1, 2, 7, 64, 1000, 2560, 6912])
 def test_random_rows_match_exact_sum(host_sumsq, k):
     rng = np.random.default_rng([21, k])
     paths = set()
@@ -86,6 +87,25 @@ def test_ties(host_sumsq):
     # and rounds to the even one; 2^54 + 3 rounds up
     assert host_sumsq(_bf([2.0 ** 27, 1.0, 1.0])) == (2.0 ** 54, False)
     assert host_sumsq(_bf([1.0, 1.0, 1.0, 2.0 ** 27])) == (2.0 ** 54 + 4, False)
+    # the same sums with the terms in different waves (groups of 8 go to threads in turn,
+    # threads 64 apart to the next wave): anchors 2^27 and 2^0 apart by 27 exponents
+    # (> 16) take the general path; closer anchors are combined directly
+    row = np.zeros(8 * 256, np.float32)
+    row[0], row[8 * 64], row[8 * 128] = 2.0 ** 27, 1.0, 1.0
+    assert host_sumsq(_bf(row)) == (2.0 ** 54, True)
+    row[8 * 192] = 2.0 ** -60
+    assert host_sumsq(_bf(row)) == (2.0 ** 54 + 4, True)
+    row = np.zeros(8 * 256, np.float32)
+    row[0], row[8 * 64], row[8 * 128] = 2.0 ** 8, 2.0 ** -19, 2.0 ** -19
+    # 2^16 + 2^-37 is half way between 2^16 and 2^16 + 2^-36: ties to even (the anchors
+    # lie 27 exponents apart: the general path)
+    assert host_sumsq(_bf(row)) == (2.0 ** 16, True)
+    row[8 * 192 + 3] = 2.0 ** -30
+    assert host_sumsq(_bf(row)) == (2.0 ** 16 + 2.0 ** -36, True)
+    # anchors 14 apart are combined directly, exactly: 2^16 + 2 * 2^-12 + 3 * 2^-2
+    row = np.zeros(8 * 256, np.float32)
+    row[1], row[8 * 64 + 5], row[8 * 65], row[8 * 128 + 7] = 2.0 ** 8, 2.0 ** -6, 2.0 ** -6, 1.5
+    assert host_sumsq(_bf(row)) == (2.0 ** 16 + 2.0 ** -11 + 2.25, False)
     # 2^200 + 2^147 is a tie (ulp 2^148): alone it rounds down to 2^200; a value far below
     # the window (2^50 squares to 2^100, 2^100 below) tips it up through the slow path
     assert host_sumsq(_bf([2.0 ** 100, 2.0 ** 73, 2.0 ** 73])) == (2.0 ** 200, False)
