@@ -132,6 +132,45 @@ __device__ __forceinline__ uint32_t q4(float x, float s) {
     return (uint32_t)((int)v) & 0xFu;
 }
 
+// ---------------------------------------------------------------- global -> LDS DMA
+// 16 bytes per lane from global memory straight into LDS: lane i's bytes land at
+// lds_dst + 16 i (lds_dst the same in every lane).  Inline asm, so that the compiler
+// does not put a full vmcnt wait in front of later LDS reads: the kernels wait for these
+// loads themselves (s_waitcnt vmcnt, and a barrier where other waves read the data).
+// The instruction writes no register, so nothing can be overwritten while it is in
+// flight; its address registers are read at issue.
+__device__ __forceinline__ void lds_dma16(const void *src, void *lds_dst) {
+    const uint32_t lds = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)lds_dst);
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(src), "s"(lds)
+                 : "memory", "m0");
+}
+
+// The same for the lanes in `lane_mask` only (wave-uniform), at the LDS byte address
+// lds_addr: exec is narrowed and restored inside the asm, so the mask costs no branch
+// and every wave issues the instruction (its loads-in-flight count stays uniform).
+__device__ __forceinline__ void lds_dma16_lanes(const void *src, uint32_t lds_addr,
+                                                uint64_t lane_mask) {
+    // wave-uniform values into scalar registers (the builtin returns int: widen through
+    // uint32_t, not by sign extension)
+    const uint32_t lds = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_addr);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)lane_mask);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(lane_mask >> 32));
+    const uint64_t lanes = ((uint64_t)hi << 32) | lo;
+    uint64_t saved;
+    asm volatile("s_mov_b64 %0, exec\n\t"
+                 "s_and_b64 exec, exec, %3\n\t"
+                 "s_mov_b32 m0, %2\n\t"
+                 "s_nop 0\n\t"
+                 "global_load_lds_dwordx4 %1, off\n\t"
+                 "s_mov_b64 exec, %0"
+                 : "=&s"(saved)
+                 : "v"(src), "s"(lds), "s"(lanes)
+                 : "memory", "m0");
+}
+
 // ---------------------------------------------------------------- Hadamard rotation
 // "BitNet a4.8 Guide", "Best Practices for Deploying BitNet a4.8 in Production",
 // Outlier Suppression row: a Hadamard rotation (as in QuaRot) before the 4-bit

@@ -56,20 +56,6 @@ constexpr size_t kLds = (size_t)kStages * kStageBytes;
 
 __device__ __forceinline__ int swz(int row) { return ((row >> 1) & 3) ^ ((row >> 3) & 1); }
 
-// 16 bytes per lane from global memory straight into LDS: lane i's bytes land at
-// lds_dst + 16 i (lds_dst the same in every lane).  Inline asm keeps the compiler from
-// ordering later LDS reads behind it with a full vmcnt wait; the kernel waits for these
-// loads itself (s_waitcnt vmcnt + barrier) before reading the slot.  No register
-// result: nothing can be overwritten while the load is in flight.
-__device__ __forceinline__ void lds_dma16(const void *src, void *lds_dst) {
-    const uint32_t lds = __builtin_amdgcn_readfirstlane(
-        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)lds_dst);
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                 :
-                 : "v"(src), "s"(lds)
-                 : "memory", "m0");
-}
-
 template <int kN>
 __device__ __forceinline__ void wait_vm() {
     static_assert(kN >= 0 && kN < 64, "vmcnt is 6 bits");

@@ -86,21 +86,6 @@ struct BigParams {
 
 __device__ __forceinline__ int a_swz(int row) { return ((row >> 1) & 3) ^ ((row >> 3) & 1); }
 
-// 16 bytes per lane from global memory straight into LDS: lane i's bytes land at
-// lds_dst + 16 i (lds_dst must be the same in every lane).  Issued as inline asm so
-// the compiler does not order later LDS reads behind it with a full vmcnt wait; the
-// kernel waits for these loads itself (s_waitcnt vmcnt + barrier) before reading the
-// slot.  The instruction has no register result, so nothing can be overwritten by a
-// load in flight; its address registers are read at issue.
-__device__ __forceinline__ void lds_dma16(const void *src, void *lds_dst) {
-    const uint32_t lds = __builtin_amdgcn_readfirstlane(
-        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)lds_dst);
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                 :
-                 : "v"(src), "s"(lds)
-                 : "memory", "m0");
-}
-
 template <int kBN, int kYD, bool kRelu2, bool kBias>
 __global__ void __launch_bounds__(Tile<kBN>::kThreads, kBN == 128 ? 2 : 1) gemm_big_kernel(BigParams p) {
     constexpr int kStageBytes = Tile<kBN>::kStageBytes;

@@ -74,30 +74,6 @@ struct F6Params {
     int tiles_m;
 };
 
-// 16 bytes per lane from global memory straight into LDS (lane i at lds + 16 i, lds the
-// same in every lane), for the lanes in `lanes` only.  Inline asm so that the compiler
-// does not put a full vmcnt wait in front of later LDS reads (the kernel waits itself:
-// vmcnt + barrier), and so that the lane mask costs no branch: exec is narrowed and
-// restored inside the block.  The instruction writes no register.
-__device__ __forceinline__ void lds_dma16(const void *src, uint32_t lds_addr, uint64_t lane_mask) {
-    // both are wave-uniform; readfirstlane puts them in scalar registers for the asm
-    // (the builtin returns int: widen through uint32_t, not by sign extension)
-    const uint32_t lds = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_addr);
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)lane_mask);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(lane_mask >> 32));
-    const uint64_t lanes = ((uint64_t)hi << 32) | lo;
-    uint64_t saved;
-    asm volatile("s_mov_b64 %0, exec\n\t"
-                 "s_and_b64 exec, exec, %3\n\t"
-                 "s_mov_b32 m0, %2\n\t"
-                 "s_nop 0\n\t"
-                 "global_load_lds_dwordx4 %1, off\n\t"
-                 "s_mov_b64 exec, %0"
-                 : "=&s"(saved)
-                 : "v"(src), "s"(lds), "s"(lanes)
-                 : "memory", "m0");
-}
-
 // s_waitcnt vmcnt(kN) (kN < 64), lgkmcnt and expcnt left open
 template <int kN> __device__ __forceinline__ void wait_vm() {
     __builtin_amdgcn_s_waitcnt((kN & 0xF) | ((kN >> 4) << 14) | (0x7 << 4) | (0xF << 8));
@@ -157,7 +133,7 @@ gemm_f6f4_kernel(F6Params p) {
         const uint64_t ktc = (uint64_t)min(kt, nk - 1);  // past the end: reload the last step (unused)
 #pragma unroll
         for (int i = 0; i < kDma; ++i)
-            lds_dma16(dsrc[i] + ktc * dstride[i], lds0 + slot * T::kStageBytes + doff[i], dlanes[i]);
+            lds_dma16_lanes(dsrc[i] + ktc * dstride[i], lds0 + slot * T::kStageBytes + doff[i], dlanes[i]);
     };
 
     v16f acc[2][4];

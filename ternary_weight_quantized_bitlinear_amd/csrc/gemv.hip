@@ -70,20 +70,6 @@ struct GemvParams {
 };
 
 
-// 16 bytes per lane from global memory straight into LDS: lane i's bytes land at
-// lds_dst + 16 i (lds_dst the same in every active lane).  Inline asm so that the
-// compiler does not put later LDS reads behind a full vmcnt wait; the kernel waits
-// for these loads itself (vmcnt(0) and a barrier) before reading LDS.  The
-// instruction has no register result, so no load in flight can overwrite a register.
-__device__ __forceinline__ void lds_dma16(const void *src, void *lds_dst) {
-    const uint32_t lds = __builtin_amdgcn_readfirstlane(
-        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)lds_dst);
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                 :
-                 : "v"(src), "s"(lds)
-                 : "memory", "m0");
-}
-
 template <int kMode> struct RawWords { static constexpr int n = kMode == kRawF32 ? 4 : kMode == kRawBf16 ? 2 : 1; };
 
 // one 16-element group's raw 16-byte words (address clamped into the row; a group
