@@ -27,7 +27,12 @@ prefill      = the prefill GEMM leg: M=2048 tokens, int TOPS against int8 MFMA p
 backward     = the straight-through-estimator backward (dX, dW, dbias), TFLOP/s against
                the bf16 MFMA peak
 parity_layer = the 8 x 256 -> 512 parity configuration, timed only
-cpu_baseline = the CPU oracle on one layer's decode FFN step, single-threaded
+mfma_ceiling = MFMA-only loops on register operands with each GEMM's operand statistics
+               (int8, FP4 x FP6, bf16): the matrix cores' rate on this chip, reported
+               beside each GEMM's fraction of the published peak
+cpu_baseline = the CPU oracle pinned to one core: one layer's decode FFN step (the
+               headline's unit), plus the parity layer in full and samples of the
+               prefill GEMM, the 30-layer stack and the 70B layer, extrapolated
 """
 from __future__ import annotations
 
@@ -47,6 +52,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, GB/s
 INT8_PEAK_TOPS = 5000.0         # MI355X dense int8 MFMA, TOPS (5.0 POP/s)
 F6F4_PEAK_TOPS = 10100.0        # MI355X dense FP6/FP4 MFMA (10.1 PFLOP/s), the int4 path's units
+BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, TFLOP/s
 MALL_BYTES = 256 << 20          # Infinity Cache
 METRIC = "BitLinear decode GEMV HBM GB/s + prefill GEMM int TOPS, % of MI355X roofline"
 CSRC = os.path.join(ROOT, "ternary_weight_quantized_bitlinear_amd", "csrc")
@@ -595,9 +601,6 @@ def leg_parity_layer(torch, bl, reps=200):
     return out
 
 
-BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, TFLOP/s
-
-
 def leg_backward(torch, bl, reps=5):
     """Backward pass under the straight-through estimators (bitlinear_backward: dX, dW and
     dbias from a bf16 dY), at the 2B prefill shapes (M=2048, int8 per-token codes, the
@@ -639,7 +642,10 @@ def leg_backward(torch, bl, reps=5):
             r[tag + "_us"] = ms * 1e3
             r[tag + "_tflops"] = fl / (ms * 1e-3) / 1e12
         r["dX_frac"] = r["dX_tflops"] / BF16_PEAK_TFLOPS
-        r["dW_mfma_tflops"] = 3 * r["dW_tflops"]
+        # dW against its algorithmic flops (2 M N K), and against the work the matrix
+        # cores execute (per-token scales: three bf16 passes, 3x)
+        r["dW_frac"] = r["dW_tflops"] / BF16_PEAK_TFLOPS
+        r["dW_mfma_tflops"] = 3 * r["dW_tflops"]  # every case here has per-token scales
         r["dW_mfma_frac"] = r["dW_mfma_tflops"] / BF16_PEAK_TFLOPS
         out[name] = r
         del packed, X, xq, dY, Wb, ws, res
@@ -701,28 +707,153 @@ def leg_acts(torch, bl, reps=20):
     return out
 
 
-def cpu_baseline(x, W_up, W_dn, budget_s=12.0):
-    """The oracle (single-threaded C, as it stands) on the same decode FFN step."""
-    import oracle
-    import workloads
-    p_up, g_up, _ = oracle.quantize_weights(W_up)
-    p_dn, g_dn, _ = oracle.quantize_weights(W_dn)
-    (K1, N1), (K2, N2) = workloads.SHAPE_UP, workloads.SHAPE_DOWN
+CALIB_LIB = os.path.join(ROOT, "ternary_weight_quantized_bitlinear_amd", "libbitlinear_calib.so")
+
+
+def leg_mfma_ceiling(torch, reps=3):
+    """Matrix-core ceilings on this chip: MFMA-only loops (no memory, barrier or VALU work)
+    on register operands with the value statistics of the int8 GEMM, the FP4 x FP6 GEMM
+    and the backward's bf16 GEMMs (libbitlinear_calib.so), one 8-wave block per CU.
+    Median of `reps` launches of a few ms each."""
+    import ctypes
+    lib = ctypes.CDLL(CALIB_LIB)
+    lib.bl_calib_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                  ctypes.c_void_p]
+    lib.bl_calib_mfma.restype = ctypes.c_int
+    lib.bl_calib_ops.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    lib.bl_calib_ops.restype = ctypes.c_double
+    blocks = torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.empty(blocks, dtype=torch.float32, device="cuda:0")
+    stream = torch.cuda.current_stream()
+    out = {"blocks": blocks, "waves_per_block": 8}
+    for kind, name, iters, peak in ((0, "int8_32x32x32", 20000, INT8_PEAK_TOPS),
+                                    (1, "fp4_x_fp6_32x32x64", 10000, F6F4_PEAK_TOPS),
+                                    (2, "bf16_32x32x16", 20000, BF16_PEAK_TFLOPS)):
+        def launch():
+            st = lib.bl_calib_mfma(kind, blocks, iters, ctypes.c_void_p(sink.data_ptr()),
+                                   ctypes.c_void_p(stream.cuda_stream))
+            if st != 0:
+                raise RuntimeError("calibration launch failed: HIP status %d" % st)
+        launch()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            launch()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        ms = sorted(ts)[len(ts) // 2]
+        tops = lib.bl_calib_ops(kind, blocks, iters) / (ms * 1e-3) / 1e12
+        out[name] = {"tops": round(tops, 1), "of_peak": round(tops / peak, 4), "ms": round(ms, 3)}
+    return out
+
+
+def _timed(fn, budget_s, max_n=1000):
+    """Calls fn() until budget_s of wall time has passed: (calls, seconds)."""
     n = 0
     t0 = time.perf_counter()
     while True:
-        h, _, _, _ = oracle.bitlinear(x, p_up, g_up, epi=oracle.EPI_RELU2, y_dtype=oracle.BF16)
-        oracle.bitlinear(h, p_dn, g_dn, y_dtype=oracle.BF16)
+        fn()
         n += 1
         el = time.perf_counter() - t0
-        if el > budget_s or n >= 5000:
-            break
-    step_bytes = gemv_bytes(K1, N1) + gemv_bytes(K2, N2)
-    return {"value": step_bytes * n / el / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": "%d decode FFN steps (up 2560->6912 + ReLU^2, down 6912->2560, M=1, "
-                      "int8 per token, bf16 out) in %.1f s on one core of %s" % (
-                          n, el, cpu_model()),
-            "ms_per_step": el * 1e3 / n}
+        if el > budget_s or n >= max_n:
+            return n, el
+
+
+def cpu_baseline(x, W_up, W_dn, decode_budget_s=6.0):
+    """The oracle (single-threaded C, as it stands: never tuned) timed on this host, pinned
+    to one core for the duration, beside each configuration.  The headline entry is the
+    same decode FFN step as the GPU's headline (GB/s of weights); the others time the
+    oracle on the parity layer in full, and on bounded samples of the prefill GEMM, the
+    30-layer stack and the 70B layer, extrapolated to the whole configuration and
+    labelled as such.  A baseline for context, not a target."""
+    import oracle
+    import workloads
+    before = os.sched_getaffinity(0)
+    core = min(before)
+    os.sched_setaffinity(0, {core})
+    try:
+        host = {"cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
+                "cpus_allowed_before_pinning": len(before), "pinned_to_cpu": core}
+        # C2: the decode FFN step (the headline's unit)
+        p_up, g_up, _ = oracle.quantize_weights(W_up)
+        p_dn, g_dn, _ = oracle.quantize_weights(W_dn)
+        (K1, N1), (K2, N2) = workloads.SHAPE_UP, workloads.SHAPE_DOWN
+
+        def step():
+            h, _, _, _ = oracle.bitlinear(x, p_up, g_up, epi=oracle.EPI_RELU2, y_dtype=oracle.BF16)
+            oracle.bitlinear(h, p_dn, g_dn, y_dtype=oracle.BF16)
+        n, el = _timed(step, decode_budget_s, 5000)
+        step_bytes = gemv_bytes(K1, N1) + gemv_bytes(K2, N2)
+        out = {"value": step_bytes * n / el / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "sample": "%d decode FFN steps (up 2560->6912 + ReLU^2, down 6912->2560, M=1, "
+                         "int8 per token, bf16 out) in %.1f s on one core of %s" % (
+                             n, el, host["cpu_model"]),
+               "ms_per_step": el * 1e3 / n, **host}
+        per = {}
+        # C1: the parity layer, whole (weights, activations, forward with ReLU^2)
+        W, X = workloads.parity_layer(seed=0, m=8, k=256, n=512)
+
+        def c1():
+            pk, g, _ = oracle.quantize_weights(W)
+            oracle.bitlinear(X, pk, g, epi=oracle.EPI_RELU2)
+        n, el = _timed(c1, 1.5)
+        per["c1_parity_layer"] = {"us_per_call": el * 1e6 / n, "calls": n,
+                                  "sample": "whole call: quantize W 512x256, quantize X 8x256, "
+                                            "forward + ReLU^2, fp32 out"}
+        # C3: the prefill up projection, 16 of its 2048 token rows, all outputs
+        W3, X3 = workloads.prefill_gemm(seed=2, shape=workloads.SHAPE_UP)
+        p3, g3, _ = oracle.quantize_weights(W3)
+        rows = X3[:16]
+        t0 = time.perf_counter()
+        oracle.bitlinear(rows, p3, g3, epi=oracle.EPI_RELU2, y_dtype=oracle.BF16)
+        el = time.perf_counter() - t0
+        K, N = workloads.SHAPE_UP
+        full_s = el * 2048 / 16
+        per["c3_prefill_up"] = {"s_extrapolated": full_s,
+                                "tops_extrapolated": 2.0 * 2048 * N * K / full_s / 1e12,
+                                "sample": "16 of 2048 token rows x all 6912 outputs in %.2f s, "
+                                          "extrapolated linearly to M=2048" % el}
+        # C4: one block of the batch-16 stack (norm, QKV, O, norm, up + ReLU^2, down)
+        codes = workloads.stack_layer_codes(3, 0)
+        lw = {k: oracle.quantize_weights(c.astype(np.float32))[:2] for k, c in codes.items()}
+        x0 = workloads.stack_input(seed=3, m=16)
+        H = workloads.HIDDEN
+        t0 = time.perf_counter()
+        x1, h1 = oracle.rmsnorm(x0)
+        q1, s1 = oracle.quantize_acts(h1)
+        pq, gq = lw["qkv"]
+        for part in range(3):
+            y, _ = oracle.forward(q1, 8, s1, oracle.PER_TOKEN, pq[part * H:(part + 1) * H], gq,
+                                  y_dtype=oracle.BF16)
+        o, _, _, _ = oracle.bitlinear(y, *lw["o"], y_dtype=oracle.BF16)
+        x2, h2 = oracle.rmsnorm(x1, o)
+        u, _, _, _ = oracle.bitlinear(h2, *lw["up"], epi=oracle.EPI_RELU2, y_dtype=oracle.BF16)
+        oracle.bitlinear(u, *lw["down"], y_dtype=oracle.BF16)
+        el = time.perf_counter() - t0
+        per["c4_stack_2b"] = {"ms_per_step_extrapolated": el * 1e3 * workloads.LAYERS_2B,
+                              "tokens_per_s_extrapolated": 16 / (el * workloads.LAYERS_2B),
+                              "sample": "layer 0 of 30 at batch 16 in %.2f s, times 30" % el}
+        # C5: the 70B layer with int4 activations, 4 of its 4096 token rows
+        c5codes, X5 = workloads.layer_70b(m=4)
+        p5, g5, _ = oracle.quantize_weights(c5codes.astype(np.float32))
+        del c5codes
+        t0 = time.perf_counter()
+        oracle.bitlinear(X5, p5, g5, bits=4, y_dtype=oracle.BF16)
+        el = time.perf_counter() - t0
+        K5, N5 = workloads.SHAPE_70B
+        full_s = el * 4096 / 4
+        per["c5_70b_int4"] = {"s_extrapolated": full_s,
+                              "tops_extrapolated": 2.0 * 4096 * N5 * K5 / full_s / 1e12,
+                              "sample": "4 of 4096 token rows x all 28672 outputs in %.2f s, "
+                                        "extrapolated linearly to M=4096" % el}
+        out["per_config"] = per
+        return out
+    finally:
+        os.sched_setaffinity(0, before)
 
 
 def main():
@@ -733,7 +864,8 @@ def main():
     ap.add_argument("--batch", type=int, default=64, help="layers per streamed launch")
     ap.add_argument("--copies", type=int, default=64, help="weight copies of the chain leg")
     ap.add_argument("--chain-steps", type=int, default=2000)
-    ap.add_argument("--legs", default="decode,chain,single,c1,prefill,stack,c5,pack,acts,backward,cpu")
+    ap.add_argument("--legs", default="decode,chain,single,c1,prefill,stack,c5,pack,acts,backward,"
+                                      "ceiling,cpu")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
@@ -765,6 +897,8 @@ def main():
             side["backward"] = leg_backward(torch, bl)
         if "c1" in legs:
             side["parity_layer"] = leg_parity_layer(torch, bl)
+        if "ceiling" in legs:
+            side["mfma_ceiling"] = leg_mfma_ceiling(torch)
         if side:
             print(json.dumps(side))
         return
@@ -850,6 +984,28 @@ def main():
                                        "the 70B-class layer at M=4096 with int4 codes and both "
                                        "clipping masks",
                            "unit": "TFLOP/s", **leg_backward(torch, bl)}
+    if "ceiling" in legs:
+        # each matrix-core rate beside the MFMA-only ceiling measured for its operands
+        ceil = leg_mfma_ceiling(torch)
+        out["mfma_ceiling"] = ceil
+        c8 = ceil["int8_32x32x32"]["tops"]
+        c4 = ceil["fp4_x_fp6_32x32x64"]["tops"]
+        cb = ceil["bf16_32x32x16"]["tops"]
+        if "prefill" in out:
+            pf = out["prefill"]
+            pf["roofline"]["mfma_ceiling_tops"] = c8
+            pf["roofline"]["frac_of_ceiling"] = round(pf["value"] / c8, 4)
+            pf["int4_activations"]["frac_of_ceiling"] = round(
+                pf["int4_activations"]["gemm_tops"] / c4, 4)
+        if "layer_70b" in out:
+            l7 = out["layer_70b"]
+            l7["int8"]["frac_of_ceiling"] = round(l7["int8"]["gemm_tops"] / c8, 4)
+            l7["int4"]["frac_of_ceiling"] = round(l7["int4"]["gemm_tops"] / c4, 4)
+        if "backward" in out:
+            for k, r in out["backward"].items():
+                if isinstance(r, dict) and "dX_tflops" in r:
+                    r["dX_frac_of_ceiling"] = round(r["dX_tflops"] / cb, 4)
+                    r["dW_mfma_frac_of_ceiling"] = round(r["dW_mfma_tflops"] / cb, 4)
     if "cpu" in legs:
         out["cpu_baseline"] = cpu_baseline(st["x"], st["W_up"], st["W_dn"])
     out["device"] = torch.cuda.get_device_name(0)

@@ -22,6 +22,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libbitlinear.so")
+# matrix-core calibration loops for the benchmark (not part of the BitLinear C ABI)
+CALIB_LIB = os.path.join(PKG, "libbitlinear_calib.so")
+CALIB_SOURCES = ["calib.hip"]
 SOURCES = ["api.hip", "wquant.hip", "aquant.hip", "gemv.hip", "gemm.hip", "gemm_big.hip",
            "gemm_f6f4.hip", "norm.hip", "gemm_bf16.hip", "backward.hip"]
 
@@ -59,7 +62,20 @@ def build(verbose: bool = False, out: str = LIB, build_dir: str = BUILD_DIR, ext
     os.replace(tmp, out)
     if verbose:
         print("built", out)
+    if out == LIB:
+        _link(CALIB_LIB, [_compile(src, build_dir, extra) for src in CALIB_SOURCES])
+        if verbose:
+            print("built", CALIB_LIB)
     return out
+
+
+def _link(out: str, objs) -> None:
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("link failed:\n%s\n%s" % (" ".join(cmd), r.stderr))
+    os.replace(tmp, out)
 
 
 if __name__ == "__main__":
