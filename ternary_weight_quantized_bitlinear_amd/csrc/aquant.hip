@@ -185,18 +185,36 @@ aq_prepare(const uint8_t *__restrict__ xq, int64_t M, int64_t K, uint8_t *__rest
     const int64_t m = (int64_t)blockIdx.x * (kAqThreads / kWave) + threadIdx.x / kWave;
     if (m >= M) return;  // whole wave
     const int lane = threadIdx.x & (kWave - 1);
+    const int64_t n16 = K / 16;
     int csum = 0;
-    for (int64_t u = lane; u < K / 16; u += kWave) {
-        uint32_t nat[4];
-        if (kBits == 8) {
-            const uint4 q = *reinterpret_cast<const uint4 *>(xq + m * K + 16 * u);
-            nat[0] = q.x; nat[1] = q.y; nat[2] = q.z; nat[3] = q.w;
-        } else {
-            const uint2 q = *reinterpret_cast<const uint2 *>(xq + m * (K / 2) + 8 * u);
-            nibbles_to_i8(q.x, nat);
-            nibbles_to_i8(q.y, nat + 2);
+    // kLoads groups per lane in flight at once: the loads are issued together, then the
+    // groups are reordered and stored (a loop of one load at a time waited for each)
+    constexpr int kLoads = 4;
+    for (int64_t u0 = lane; u0 < n16; u0 += kLoads * kWave) {
+        uint4 q[kLoads];
+#pragma unroll
+        for (int j = 0; j < kLoads; ++j) {
+            const int64_t u = min(u0 + j * kWave, n16 - 1);  // past the end: a repeat, unused
+            if (kBits == 8) {
+                q[j] = *reinterpret_cast<const uint4 *>(xq + m * K + 16 * u);
+            } else {
+                const uint2 h = *reinterpret_cast<const uint2 *>(xq + m * (K / 2) + 8 * u);
+                q[j] = make_uint4(h.x, h.y, 0u, 0u);
+            }
         }
-        store_prepared(xp + m * K + 16 * u, nat, csum);
+#pragma unroll
+        for (int j = 0; j < kLoads; ++j) {
+            const int64_t u = u0 + j * kWave;
+            if (u >= n16) break;
+            uint32_t nat[4];
+            if (kBits == 8) {
+                nat[0] = q[j].x; nat[1] = q[j].y; nat[2] = q[j].z; nat[3] = q[j].w;
+            } else {
+                nibbles_to_i8(q[j].x, nat);
+                nibbles_to_i8(q[j].y, nat + 2);
+            }
+            store_prepared(xp + m * K + 16 * u, nat, csum);
+        }
     }
     csum = wave_sum(csum);
     if (lane == 0) rowsum[m] = csum;
