@@ -84,6 +84,8 @@ def _load():
         lib.oracle_to_bf16.argtypes = [P, P, I64]
         lib.oracle_rmsnorm.argtypes = [P, P, I64, I64, F, P, P]
         lib.oracle_sumsq.argtypes = [P, I64, P]
+        lib.oracle_layernorm.argtypes = [P, P, I64, I64, F, P, P]
+        lib.oracle_layernorm_sums.argtypes = [P, I64, P, P]
         lib.oracle_hadamard_block.argtypes = [I64]
         lib.oracle_hadamard_block.restype = I64
         lib.oracle_hadamard_rows.argtypes = [P, I, I64, I64, P]
@@ -92,7 +94,8 @@ def _load():
         lib.oracle_backward.argtypes = [P, P, I, P, I, P, P, P, I, P, I, I64, I64, I64, P, P, P]
         for name in ("oracle_gamma", "oracle_quantize_weights", "oracle_quantize_acts",
                      "oracle_forward", "oracle_forward_at", "oracle_hadamard_rows",
-                     "oracle_rmsnorm", "oracle_sumsq",
+                     "oracle_rmsnorm", "oracle_sumsq", "oracle_layernorm",
+                     "oracle_layernorm_sums",
                      "oracle_quantize_acts_rotated", "oracle_quantize_weights_rotated",
                      "oracle_backward"):
             getattr(lib, name).restype = I
@@ -217,6 +220,31 @@ def rmsnorm(X: np.ndarray, delta=None, eps: float = 1e-6):
     _check(_load().oracle_rmsnorm(_ptr(X), None if d is None else _ptr(d), M, K, eps,
                                   _ptr(x_out), _ptr(h_out)), "rmsnorm")
     return x_out, h_out
+
+
+def layernorm(X: np.ndarray, delta=None, eps: float = 1e-5):
+    """Residual add and non-affine layer norm of bf16 rows (uint16 bit patterns [M, K]):
+    returns (x', h) with x' = bf16(x + delta) (or x) and h = bf16((x' - mean) / sqrt(var
+    + eps)), var the biased variance."""
+    X = np.ascontiguousarray(X, dtype=np.uint16)
+    M, K = X.shape
+    d = None if delta is None else np.ascontiguousarray(delta, dtype=np.uint16)
+    x_out = np.empty_like(X)
+    h_out = np.empty_like(X)
+    _check(_load().oracle_layernorm(_ptr(X), None if d is None else _ptr(d), M, K, eps,
+                                    _ptr(x_out), _ptr(h_out)), "layernorm")
+    return x_out, h_out
+
+
+def layernorm_sums(row: np.ndarray):
+    """(fp64(S1), fp64(D)) of one row of bf16 values: S1 the exact sum, D = K S2 - S1^2
+    with S2 the exact sum of squares, each rounded once to fp64 (nearest, ties to even).
+    The row's mean is S1 / K and its variance D / K^2."""
+    row = np.ascontiguousarray(row, dtype=np.uint16).reshape(-1)
+    out = np.zeros(2, np.float64)
+    _check(_load().oracle_layernorm_sums(_ptr(row), row.size, _ptr(out[0:]), _ptr(out[1:])),
+           "layernorm_sums")
+    return float(out[0]), float(out[1])
 
 
 def sumsq(row: np.ndarray) -> float:

@@ -51,6 +51,9 @@
  *   - the backward (quantization-aware training): each page's straight-through
  *     estimator for its own activation width, b1.58's identity for int8 and
  *     a4.8's masked one for int4 (see the last section).
+ *   - the normalization before the quantizer, in both forms the pages show (RMS:
+ *     [2b4t] SubLN; layer norm: the [b158] Step 2 listing): every row sum is
+ *     exact and rounded once to fp64, weight 1, no bias (see those sections).
  */
 #include <stdint.h>
 #include <stdlib.h>
@@ -486,6 +489,162 @@ int oracle_rmsnorm(const uint16_t *X, const uint16_t *delta, int64_t M, int64_t 
         for (int64_t k = 0; k < K; ++k) {
             const double v = (double)widen_bf16(x_out[m * K + k]);
             h_out[m * K + k] = narrow_bf16((float)(v * r));
+        }
+    }
+    return OR_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* the layer-norm form of the normalization before the quantizer             */
+/* ------------------------------------------------------------------------ */
+/*
+ * "BitNet b1.58: The 1-Bit Ternary LLM Architecture Guide", "Implementation", the
+ * Step 2 BitLinear listing: the layer's input is layer-normalized over its last axis
+ * (no learned weight or bias, the library default epsilon 1e-5) before the activation
+ * quantizer; the "BitNet 2B4T Guide" listing's BitLinear keeps the same non-affine
+ * layer norm as its SubLN.  Per row, with the residual add of the RMS form:
+ *     x'  = bf16(fl32(x + delta))                   (delta absent: x' = x)
+ *     mu  = sum_k x' / K,   var = sum_k (x' - mu)^2 / K
+ * Reading taken (the pages fix no precision or order): with the exact sums
+ * S1 = sum x' and S2 = sum x'^2, var = (K S2 - S1^2) / K^2 exactly, so
+ *     D   = K S2 - S1^2, exactly, rounded once to fp64
+ *     mu  = fp64(S1) / K,   var = fp64(D) / (K * K)         (fp64 operations)
+ *     r   = 1 / sqrt(var + eps)                            in fp64
+ *     h   = bf16(fl32((x' - mu) * r))                      difference, product in fp64
+ * Like S of the RMS form, S1 and D are the values no summation order can change.
+ */
+
+/*
+ * Unsigned integers of LN_LIMBS 32-bit limbs, least significant first.  In units of
+ * 2^-133 (the smallest bf16 subnormal) a value is m * 2^(e' - 1); a row's |S1| stays
+ * below 2^31 * 2^8 * 2^253 < 2^292.  In units of 2^-266, S1^2 < 2^584 and K S2 < 2^31 *
+ * 2^553, so 704 bits hold every quantity.
+ */
+#define LN_LIMBS 22
+
+/* a += v * 2^shift, v < 2^32 */
+static void ln_add(uint32_t *a, uint64_t v, int shift)
+{
+    uint64_t carry = 0;
+    for (int i = shift / 32; i < LN_LIMBS; ++i) {
+        uint64_t part = 0;
+        if (i == shift / 32) part = (v << (shift % 32)) & 0xFFFFFFFFu;
+        else if (i == shift / 32 + 1) part = (v << (shift % 32)) >> 32;
+        const uint64_t t = (uint64_t)a[i] + part + carry;
+        a[i] = (uint32_t)t;
+        carry = t >> 32;
+    }
+}
+
+/* compares a and b: -1, 0 or 1 */
+static int ln_cmp(const uint32_t *a, const uint32_t *b)
+{
+    for (int i = LN_LIMBS - 1; i >= 0; --i)
+        if (a[i] != b[i]) return a[i] < b[i] ? -1 : 1;
+    return 0;
+}
+
+/* out = a - b for a >= b */
+static void ln_sub(const uint32_t *a, const uint32_t *b, uint32_t *out)
+{
+    int64_t borrow = 0;
+    for (int i = 0; i < LN_LIMBS; ++i) {
+        const int64_t t = (int64_t)a[i] - (int64_t)b[i] - borrow;
+        out[i] = (uint32_t)t;
+        borrow = t < 0 ? 1 : 0;
+    }
+}
+
+/* out = a * b (the product must fit LN_LIMBS limbs) */
+static void ln_mul(const uint32_t *a, const uint32_t *b, uint32_t *out)
+{
+    uint32_t r[LN_LIMBS];
+    memset(r, 0, sizeof r);
+    for (int i = 0; i < LN_LIMBS; ++i) {
+        uint64_t carry = 0;
+        for (int j = 0; i + j < LN_LIMBS; ++j) {
+            const uint64_t t = (uint64_t)a[i] * b[j] + r[i + j] + carry;
+            r[i + j] = (uint32_t)t;
+            carry = t >> 32;
+        }
+    }
+    memcpy(out, r, sizeof r);
+}
+
+/* a * 2^unit rounded to the nearest fp64, ties to even */
+static double ln_round_f64(const uint32_t *a, int unit)
+{
+    int top = -1;
+    for (int i = LN_LIMBS * 32 - 1; i >= 0 && top < 0; --i)
+        if ((a[i / 32] >> (i % 32)) & 1u) top = i;
+    if (top < 0) return 0.0;
+    const int low = top - 52;
+    uint64_t mant = 0;
+    for (int i = top; i >= (low > 0 ? low : 0); --i)
+        mant = (mant << 1) | (uint64_t)((a[i / 32] >> (i % 32)) & 1u);
+    if (low <= 0) return ldexp((double)mant, unit);
+    const int half = (int)((a[(low - 1) / 32] >> ((low - 1) % 32)) & 1u);
+    int sticky = 0;
+    for (int i = low - 2; i >= 0; --i) sticky |= (int)((a[i / 32] >> (i % 32)) & 1u);
+    if (half && (sticky || (mant & 1u))) mant += 1;
+    return ldexp((double)mant, low + unit);
+}
+
+/* fp64(S1) and fp64(D) of one row of K bf16 values (exposed for tests of the oracle) */
+int oracle_layernorm_sums(const uint16_t *x, int64_t K, double *s1_out, double *d_out)
+{
+    if (!x || !s1_out || !d_out || K <= 0 || K >= ((int64_t)1 << 31)) return OR_EINVAL;
+    uint32_t pos[LN_LIMBS], neg[LN_LIMBS], s1[LN_LIMBS], s2[LN_LIMBS], kk[LN_LIMBS];
+    memset(pos, 0, sizeof pos);
+    memset(neg, 0, sizeof neg);
+    memset(s2, 0, sizeof s2);
+    memset(kk, 0, sizeof kk);
+    for (int64_t k = 0; k < K; ++k) {
+        const uint16_t h = x[k];
+        const uint32_t e = (h >> 7) & 0xFFu;
+        const uint64_t m = (h & 0x7Fu) | (e ? 0x80u : 0u);
+        const int ee = e ? (int)e : 1;
+        ln_add((h & 0x8000u) ? neg : pos, m, ee - 1);  /* x' in units of 2^-133 */
+        ln_add(s2, m * m, 2 * ee - 2);                 /* x'^2 in units of 2^-266 */
+    }
+    /* S1 = pos - neg, as a sign and a magnitude */
+    const int negative = ln_cmp(pos, neg) < 0;
+    if (negative) ln_sub(neg, pos, s1);
+    else ln_sub(pos, neg, s1);
+    /* D = K S2 - S1^2 >= 0 (Cauchy-Schwarz) */
+    uint32_t ks2[LN_LIMBS], s1sq[LN_LIMBS], d[LN_LIMBS];
+    kk[0] = (uint32_t)K;
+    ln_mul(s2, kk, ks2);
+    ln_mul(s1, s1, s1sq);
+    if (ln_cmp(ks2, s1sq) < 0) return OR_EINVAL;  /* cannot happen */
+    ln_sub(ks2, s1sq, d);
+    const double a1 = ln_round_f64(s1, -133);
+    *s1_out = negative ? -a1 : a1;
+    *d_out = ln_round_f64(d, -266);
+    return OR_OK;
+}
+
+int oracle_layernorm(const uint16_t *X, const uint16_t *delta, int64_t M, int64_t K, float eps,
+                     uint16_t *x_out, uint16_t *h_out)
+{
+    if (!X || !x_out || !h_out || M <= 0 || K <= 0 || K >= ((int64_t)1 << 31) ||
+        !(eps > 0.0f))
+        return OR_EINVAL;
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t k = 0; k < K; ++k) {
+            float v = widen_bf16(X[m * K + k]);
+            if (delta)
+                v = widen_bf16(narrow_bf16(v + widen_bf16(delta[m * K + k])));
+            x_out[m * K + k] = narrow_bf16(v);
+        }
+        double s1 = 0.0, d = 0.0;
+        if (oracle_layernorm_sums(x_out + m * K, K, &s1, &d) != OR_OK) return OR_EINVAL;
+        const double mu = s1 / (double)K;
+        const double var = d / ((double)K * (double)K);
+        const double r = 1.0 / sqrt(var + (double)eps);
+        for (int64_t k = 0; k < K; ++k) {
+            const double v = (double)widen_bf16(x_out[m * K + k]);
+            h_out[m * K + k] = narrow_bf16((float)((v - mu) * r));
         }
     }
     return OR_OK;

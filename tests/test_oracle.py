@@ -679,6 +679,168 @@ def test_rmsnorm_h_from_the_exact_sum():
         assert np.array_equal(h[i], _bf(prod)), i
 
 
+# ---------------------------------------------------------------- layer norm
+# Pins of the non-affine layer norm before the quantizer ("BitNet b1.58: The 1-Bit
+# Ternary LLM Architecture Guide", "Implementation", Step 2 listing): exact rational
+# sums, the two-pass definition of the variance, closed forms, invariants, and the
+# library layer norm.
+
+def _exact_moments(bits_row):
+    """(S1 exact, K * sum (x - S1/K)^2 exact) as Fractions: the sum, and K^2 times the
+    variance taken by its two-pass definition."""
+    xs = [Fraction(float(v)) for v in _f(np.asarray(bits_row, np.uint16))]
+    K = len(xs)
+    s1 = sum(xs)
+    mean = s1 / K
+    return s1, K * sum((x - mean) ** 2 for x in xs)
+
+
+def _to_f64(fr: Fraction) -> float:
+    return fr.numerator / fr.denominator  # int / int: nearest fp64, ties to even
+
+
+def test_layernorm_constant_row_is_zero():
+    # x = c everywhere: the mean is c, every deviation exactly 0, h = +0
+    X = _bf(np.full((5, 48), [[2.0], [-0.5], [3.0e38], [2.0 ** -130], [-7.0]], dtype=np.float32))
+    _, h = oracle.layernorm(X)
+    assert not h.any()
+
+
+def test_layernorm_two_level_rows_are_plus_minus_one():
+    # a row of a (K/2 times) and b (K/2 times): mean (a+b)/2, deviations +-(b-a)/2,
+    # variance ((b-a)/2)^2, so h = sign(x - mean) once eps is negligible
+    rows = []
+    for a, b in [(1.0, 3.0), (-5.0, 2.5), (1000.0, 1008.0), (2.0 ** -10, 2.0 ** -9)]:
+        r = np.full(32, a, np.float32)
+        r[np.random.default_rng(int(abs(a) + 7)).permutation(32)[:16]] = b
+        rows.append(r)
+    X = _bf(np.stack(rows))
+    _, h = oracle.layernorm(X, eps=1e-30)
+    x = _f(X).astype(np.float64)
+    assert np.array_equal(_f(h), np.sign(x - x.mean(axis=1, keepdims=True)))
+
+
+def test_layernorm_worked_example():
+    # x = (1, 2, 3, 4): mean 5/2, variance 5/4, h = (x - 5/2) / sqrt(5/4 + eps)
+    _, h = oracle.layernorm(_bf([[1.0, 2.0, 3.0, 4.0]]), eps=1e-5)
+    want = (np.array([-1.5, -0.5, 0.5, 1.5]) / math.sqrt(1.25 + float(np.float32(1e-5))))
+    assert np.array_equal(h[0], _bf(want.astype(np.float32)))
+    assert list(_f(h[0])) == [-1.34375, -229 / 512, 229 / 512, 1.34375]
+
+
+def test_layernorm_shift_invariant():
+    # integer rows and integer shifts stay exact in bf16; with K = 64 the mean is a short
+    # dyadic number, so every deviation, the variance and h are unchanged by the shift
+    rng = np.random.default_rng(21)
+    X = rng.integers(-60, 60, size=(4, 64)).astype(np.float32)
+    _, h0 = oracle.layernorm(_bf(X))
+    for c in (-100.0, 37.0, 150.0):
+        _, hc = oracle.layernorm(_bf(X + np.float32(c)))
+        assert np.array_equal(hc, h0), c
+
+
+def test_layernorm_power_of_two_scaling_invariant():
+    rng = np.random.default_rng(22)
+    X = _bf((1.0 + rng.standard_normal((4, 256))).astype(np.float32))
+    _, h0 = oracle.layernorm(X, eps=1e-30)
+    for j in (-3, 2, 5):
+        _, hj = oracle.layernorm(_bf(_f(X) * np.float32(2.0 ** j)), eps=1e-30)
+        assert np.array_equal(hj, h0), j
+
+
+def test_layernorm_sign_symmetry():
+    rng = np.random.default_rng(23)
+    X = _bf((0.5 + rng.standard_normal((3, 128))).astype(np.float32))
+    _, h = oracle.layernorm(X)
+    _, hn = oracle.layernorm(_bf(-_f(X)))
+    assert np.array_equal(_f(hn), -_f(h))
+
+
+@pytest.mark.parametrize("k", [1, 2, 3, 16, 64, 2560])
+def test_layernorm_sums_exact(k):
+    # fp64(S1) and fp64(D) against exact rational arithmetic, D by the two-pass
+    # definition K * sum (x - mean)^2: whole-range rows, Gaussian rows around an offset,
+    # subnormal rows, and rows whose terms cancel
+    rng = np.random.default_rng([24, k])
+    rows = list(_wide_bf16_rows(rng, 4, k))
+    rows.append(_bf((5.0 + rng.standard_normal(k)).astype(np.float32)))
+    rows.append((rng.integers(0, 128, size=k) | (rng.integers(0, 2, size=k) << 15)).astype(np.uint16))
+    half = _wide_bf16_rows(rng, 1, (k + 1) // 2)[0]
+    rows.append(np.concatenate([half, half ^ np.uint16(0x8000)])[:k])
+    for row in rows:
+        s1, d = _exact_moments(row)
+        assert oracle.layernorm_sums(row) == (_to_f64(s1), _to_f64(d))
+
+
+def test_layernorm_sums_large_mean_small_spread():
+    # 2^20 everywhere but one 2^20 + 2^13: a one-pass fp32 E[x^2] - E[x]^2 loses this
+    # variance entirely; here S1 = K 2^20 + 2^13 and D = (K - 1) 2^26 exactly
+    for K in (8, 100, 4096):
+        row = np.full(K, 2.0 ** 20, np.float32)
+        row[K // 3] += 2.0 ** 13
+        s1, d = oracle.layernorm_sums(_bf(row))
+        assert s1 == K * 2.0 ** 20 + 2.0 ** 13
+        assert d == (K - 1) * 2.0 ** 26
+    # the bf16 extremes: the smallest subnormal and the largest finite value
+    s1, d = oracle.layernorm_sums(np.array([0x0001, 0x0000], np.uint16))
+    assert s1 == 2.0 ** -133 and d == 2.0 ** -266
+    s1, d = oracle.layernorm_sums(np.array([0x7F7F, 0xFF7F], np.uint16))
+    assert s1 == 0.0 and d == 2 * 2 * (255.0 * 2.0 ** 120) ** 2
+
+
+def test_layernorm_h_from_the_exact_sums():
+    # mean = fp64(S1) / K, var = fp64(D) / K^2, r = 1 / sqrt(var + eps),
+    # h = bf16(fl32((x' - mean) r)), recomputed from the exact rational sums
+    rng = np.random.default_rng(25)
+    X = np.concatenate([_wide_bf16_rows(rng, 3, 96) & np.uint16(0xBFFF),
+                        _bf((2.0 + 0.3 * rng.standard_normal((3, 96))).astype(np.float32))])
+    eps = np.float32(1e-5)
+    _, h = oracle.layernorm(X, eps=float(eps))
+    for i in range(X.shape[0]):
+        s1, d = _exact_moments(X[i])
+        mean = _to_f64(s1) / 96
+        r = 1.0 / math.sqrt(_to_f64(d) / (96.0 * 96.0) + float(eps))
+        dev = (_f(X[i]).astype(np.float64) - mean) * r
+        assert np.array_equal(h[i], _bf(dev.astype(np.float32))), i
+
+
+def test_layernorm_matches_the_library_layer_norm():
+    # torch's non-affine layer_norm (the listing's F.layer_norm) in fp64 on x', rounded
+    # the same way: at most one bf16 ulp apart (a different rounding of mean and
+    # variance), and nearly always identical
+    rng = np.random.default_rng(26)
+    X = _bf((0.7 + 2.0 * rng.standard_normal((16, 2560))).astype(np.float32))
+    _, h = oracle.layernorm(X)
+    ref = torch.nn.functional.layer_norm(torch.from_numpy(_f(X).astype(np.float64)), [2560],
+                                         eps=float(np.float32(1e-5)))
+    ref_bits = _bf(ref.numpy().astype(np.float32)).astype(np.int32)
+    diff = np.abs(h.astype(np.int32) - ref_bits)
+    assert diff.max() <= 1
+    assert np.mean(diff == 0) > 0.99
+
+
+def test_layernorm_output_moments():
+    rng = np.random.default_rng(27)
+    X = _bf((-4.0 + 3.0 * rng.standard_normal((8, 2560))).astype(np.float32))
+    _, h = oracle.layernorm(X)
+    hf = _f(h).astype(np.float64)
+    # each h within half a bf16 ulp (2^-9 relative) of the exact standardized value
+    assert np.all(np.abs(hf.mean(axis=1)) < 2.0 ** -8)
+    assert np.all(np.abs((hf ** 2).mean(axis=1) - 1.0) < 2 * 2.0 ** -8)
+
+
+def test_layernorm_residual_add_as_rmsnorm():
+    rng = np.random.default_rng(28)
+    X = _bf(rng.standard_normal((3, 64)).astype(np.float32))
+    D = _bf(rng.standard_normal((3, 64)).astype(np.float32))
+    x1, _ = oracle.layernorm(X, D)
+    x2, _ = oracle.rmsnorm(X, D)
+    assert np.array_equal(x1, x2)
+    a = oracle.layernorm(X)
+    b = oracle.layernorm(X, np.zeros_like(X))
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
 # ---------------------------------------------------------------- Hadamard rotation
 # ("BitNet a4.8 Guide", "Best Practices for Deploying BitNet a4.8 in Production",
 # Outlier Suppression row; readings in tests/golden/hadamard_examples.json)

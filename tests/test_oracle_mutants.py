@@ -36,6 +36,15 @@ MUTANTS = [
     ("sumsq_exponent_not_doubled", "sq_add(acc, m * m, 2 * ee - 2);", "sq_add(acc, m * m, ee - 1);", None),
     ("sumsq_carry_dropped", "const uint64_t t = (uint64_t)acc[i] + add + carry;\n        acc[i] = (uint32_t)t;\n        carry = t >> 32;",
      "const uint64_t t = (uint64_t)acc[i] + add + carry;\n        acc[i] = (uint32_t)t;\n        carry = 0;", None),
+    ("layernorm_mean_not_subtracted", "narrow_bf16((float)((v - mu) * r))", "narrow_bf16((float)(v * r))", None),
+    ("layernorm_var_over_k", "d / ((double)K * (double)K)", "d / (double)K", None),
+    ("layernorm_negatives_added", "ln_add((h & 0x8000u) ? neg : pos, m, ee - 1);", "ln_add(pos, m, ee - 1);", None),
+    ("layernorm_mean_square_not_variance", "ln_sub(ks2, s1sq, d);", "memcpy(d, ks2, sizeof d);", None),
+    ("layernorm_mean_sign_lost", "*s1_out = negative ? -a1 : a1;", "*s1_out = a1;", None),
+    ("layernorm_mul_carry_dropped", "r[i + j] = (uint32_t)t;\n            carry = t >> 32;", "r[i + j] = (uint32_t)t;\n            carry = 0;", None),
+    ("layernorm_sums_truncated", "if (half && (sticky || (mant & 1u))) mant += 1;\n    return ldexp((double)mant, low + unit);", "return ldexp((double)mant, low + unit);", None),
+    ("layernorm_eps_outside_sqrt", "1.0 / sqrt(var + (double)eps)", "1.0 / (sqrt(var) + (double)eps)", None),
+    ("layernorm_subnormal_hidden_bit", "const uint64_t m = (h & 0x7Fu) | (e ? 0x80u : 0u);\n        const int ee", "const uint64_t m = (h & 0x7Fu) | 0x80u;\n        const int ee", None),
     ("rmsnorm_residual_dropped", "v = widen_bf16(narrow_bf16(v + widen_bf16(delta[m * K + k])));", "(void)delta;", None),
     ("hadamard_butterfly_swapped", "blk[i] = u + v;\n                    blk[i + h] = u - v;", "blk[i] = u - v;\n                    blk[i + h] = u + v;", None),
     ("hadamard_stage_skipped", "for (int64_t h = 1; h < b; h *= 2)", "for (int64_t h = 2; h < b; h *= 2)", None),
