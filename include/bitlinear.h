@@ -284,9 +284,11 @@ bl_status bitlinear_forward_multi(const void *Xq, int bits, const float *act_sca
  * X      device bf16 [M][K], read and (if delta) overwritten with x'
  * delta  device bf16 [M][K], or NULL
  * H      device bf16 [M][K] output (must not overlap X or delta)
- * K % 8 == 0, 16-byte aligned pointers, eps > 0.  The fp64 sum of squares is
- * reduced in a fixed tree order: results are deterministic; against a sequential
- * sum they can differ in the last bit of r, so h can (rarely) differ by one bf16 ulp.
+ * K % 8 == 0 (0 < K < 2^31), 0 < M < 2^24, M * K < 2^40, 16-byte aligned pointers,
+ * eps > 0.  The sum of squares is exact and rounded once to fp64 (nearest, ties to
+ * even), so r, and h, do not depend on any reduction order.  Errors: BL_EINVAL (null X
+ * or H, eps <= 0, H overlapping X or delta), BL_ESHAPE, BL_EALIGN, BL_EDEVICE (launch
+ * failure).
  */
 bl_status bitlinear_rmsnorm(void *X, const void *delta, void *H, int64_t M, int64_t K,
                             float eps, void *stream);
@@ -307,6 +309,34 @@ bl_status bitlinear_rmsnorm_quantize(void *X, const void *delta, void *H, int64_
                                      float eps, int bits, bl_gran gran, float q_eps, void *Xq,
                                      float *act_scale, void *workspace, size_t workspace_bytes,
                                      void *stream);
+
+/*
+ * The same glue with the non-affine layer norm in place of the RMS norm: the form of
+ * the Step 2 BitLinear listing of "BitNet b1.58: The 1-Bit Ternary LLM Architecture
+ * Guide" ("Implementation": the input is layer-normalized over its last axis, no weight
+ * or bias, before the activation quantizer).  Per row m, with x' as in
+ * bitlinear_rmsnorm:
+ *   S1 = sum_k x'[m][k],  D = K sum_k x'[m][k]^2 - S1^2   (each exact, rounded once
+ *                                                          to fp64)
+ *   mu = S1 / K,  r = 1 / sqrt(D / (K K) + eps)             in fp64
+ *   h[m][k] = bf16(fl32((x'[m][k] - mu) * r))               difference, product in fp64
+ * (D / K^2 is the row's biased variance.)  X, delta, H, M, K, eps, alignment and errors
+ * as in bitlinear_rmsnorm; eps = 1e-5 is the listing's library default.
+ */
+bl_status bitlinear_layernorm(void *X, const void *delta, void *H, int64_t M, int64_t K,
+                              float eps, void *stream);
+
+/*
+ * bitlinear_layernorm followed by bitlinear_quantize_acts on its output h: arguments,
+ * launches and workspace as in bitlinear_rmsnorm_quantize.  This is the whole input side
+ * of the Step 2 BitLinear listing ("BitNet b1.58: The 1-Bit Ternary LLM Architecture
+ * Guide", "Implementation": layer norm, then the absmax quantizer of eq. 2) in one launch
+ * for per-token scales.
+ */
+bl_status bitlinear_layernorm_quantize(void *X, const void *delta, void *H, int64_t M,
+                                       int64_t K, float eps, int bits, bl_gran gran,
+                                       float q_eps, void *Xq, float *act_scale, void *workspace,
+                                       size_t workspace_bytes, void *stream);
 
 /*
  * Backward pass under the quantizers' straight-through estimators (quantization-aware

@@ -17,6 +17,8 @@ The functions mirror the C entry points:
 * :func:`forward_multi`     -> ``bitlinear_forward_multi`` (several projections of one input)
 * :func:`rmsnorm`           -> ``bitlinear_rmsnorm`` (glue between layers)
 * :func:`rmsnorm_quantize`  -> ``bitlinear_rmsnorm_quantize`` (glue + next layer's quantizer)
+* :func:`layernorm`         -> ``bitlinear_layernorm`` (the same glue, non-affine layer norm)
+* :func:`layernorm_quantize` -> ``bitlinear_layernorm_quantize``
 * :func:`backward`          -> ``bitlinear_backward`` (straight-through-estimator gradients)
 """
 from __future__ import annotations
@@ -73,6 +75,8 @@ def lib() -> ctypes.CDLL:
         L.bitlinear_noalloc_scratch_bytes.restype = SZ
         L.bitlinear_rmsnorm.argtypes = [P, P, P, I64, I64, F, P]
         L.bitlinear_rmsnorm_quantize.argtypes = [P, P, P, I64, I64, F, I, I, F, P, P, P, SZ, P]
+        L.bitlinear_layernorm.argtypes = [P, P, P, I64, I64, F, P]
+        L.bitlinear_layernorm_quantize.argtypes = [P, P, P, I64, I64, F, I, I, F, P, P, P, SZ, P]
         L.bitlinear_quantize_weights_rotated.argtypes = [P, I, I64, I64, F, P, P, P, SZ, P]
         L.bitlinear_quantize_acts_rotated.argtypes = [P, I, I64, I64, I, I, F, P, P, P, SZ, P]
         L.bitlinear_hadamard_block.argtypes = [I64]
@@ -89,8 +93,8 @@ def lib() -> ctypes.CDLL:
         for n in ("bitlinear_quantize_weights", "bitlinear_quantize_acts", "bitlinear_forward",
                   "bitlinear_forward_fused", "bitlinear_forward_fused_batched",
                   "bitlinear_forward_multi", "bitlinear_forward_fused_noalloc",
-                  "bitlinear_rmsnorm", "bitlinear_rmsnorm_quantize",
-                  "bitlinear_quantize_weights_rotated", "bitlinear_quantize_acts_rotated",
+                  "bitlinear_rmsnorm", "bitlinear_rmsnorm_quantize", "bitlinear_layernorm",
+                  "bitlinear_layernorm_quantize", "bitlinear_quantize_weights_rotated", "bitlinear_quantize_acts_rotated",
                   "bitlinear_backward"):
             getattr(L, n).restype = I
         _lib = L
@@ -449,9 +453,7 @@ def forward_multi(Xq, act_scale, packed, gamma, bits: int = 8, gran="token", bia
     return out
 
 
-def rmsnorm(X, delta=None, eps: float = 1e-6, out=None, stream=None):
-    """Residual add and RMS norm of bf16 rows: X [M, K] bf16 (overwritten with X + delta
-    when delta is given) -> H [M, K] bf16 = X / rms(X)."""
+def _norm(entry, X, delta, eps, out, stream):
     torch = _torch()
     M, K = _dims(X, "X", 2)
     _arg(X, "X", None, (torch.bfloat16,))
@@ -460,14 +462,11 @@ def rmsnorm(X, delta=None, eps: float = 1e-6, out=None, stream=None):
     dev = _gpu(X=X, delta=delta, out=out)
     if out is None:
         out = torch.empty_like(X)
-    _check(lib().bitlinear_rmsnorm(_ptr(X), _ptr(delta), _ptr(out), M, K, eps,
-                                   _stream(dev, stream)))
+    _check(entry(_ptr(X), _ptr(delta), _ptr(out), M, K, eps, _stream(dev, stream)))
     return out
 
 
-def rmsnorm_quantize(X, delta=None, eps: float = 1e-6, bits: int = 8, gran="token",
-                     q_eps: float = 1e-5, out=None, workspace=None, stream=None):
-    """rmsnorm followed by quantize_acts of its output: returns (H, Xq, scale)."""
+def _norm_quantize(entry, X, delta, eps, bits, gran, q_eps, out, workspace, stream):
     torch = _torch()
     bits = _bits(bits)
     M, K = _dims(X, "X", 2)
@@ -486,10 +485,35 @@ def rmsnorm_quantize(X, delta=None, eps: float = 1e-6, bits: int = 8, gran="toke
                          dtype=torch.int8 if bits == 8 else torch.uint8, device=dev)
         sc = torch.empty((_scale_len(M, g),), dtype=torch.float32, device=dev)
     ws, wsb = _workspace(workspace_size(BL_OP_QUANTIZE_ACTS, M, 1, K, bits, g), dev, workspace)
-    _check(lib().bitlinear_rmsnorm_quantize(_ptr(X), _ptr(delta), _ptr(H), M, K, eps, bits, g,
-                                            q_eps, _ptr(Xq), _ptr(sc), _ptr(ws), wsb,
-                                            _stream(dev, stream)))
+    _check(entry(_ptr(X), _ptr(delta), _ptr(H), M, K, eps, bits, g, q_eps, _ptr(Xq), _ptr(sc),
+                 _ptr(ws), wsb, _stream(dev, stream)))
     return H, Xq, sc
+
+
+def rmsnorm(X, delta=None, eps: float = 1e-6, out=None, stream=None):
+    """Residual add and RMS norm of bf16 rows: X [M, K] bf16 (overwritten with X + delta
+    when delta is given) -> H [M, K] bf16 = X / rms(X)."""
+    return _norm(lib().bitlinear_rmsnorm, X, delta, eps, out, stream)
+
+
+def rmsnorm_quantize(X, delta=None, eps: float = 1e-6, bits: int = 8, gran="token",
+                     q_eps: float = 1e-5, out=None, workspace=None, stream=None):
+    """rmsnorm followed by quantize_acts of its output: returns (H, Xq, scale)."""
+    return _norm_quantize(lib().bitlinear_rmsnorm_quantize, X, delta, eps, bits, gran, q_eps,
+                          out, workspace, stream)
+
+
+def layernorm(X, delta=None, eps: float = 1e-5, out=None, stream=None):
+    """Residual add and non-affine layer norm of bf16 rows: X [M, K] bf16 (overwritten with
+    X + delta when delta is given) -> H [M, K] bf16 = (X - mean) / sqrt(var + eps)."""
+    return _norm(lib().bitlinear_layernorm, X, delta, eps, out, stream)
+
+
+def layernorm_quantize(X, delta=None, eps: float = 1e-5, bits: int = 8, gran="token",
+                       q_eps: float = 1e-5, out=None, workspace=None, stream=None):
+    """layernorm followed by quantize_acts of its output: returns (H, Xq, scale)."""
+    return _norm_quantize(lib().bitlinear_layernorm_quantize, X, delta, eps, bits, gran, q_eps,
+                          out, workspace, stream)
 
 
 def backward(dY, Xq, act_scale, packed, gamma, bits: int = 8, gran="token", X=None, W=None,

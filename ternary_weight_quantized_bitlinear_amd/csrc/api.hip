@@ -151,7 +151,7 @@ bl_status scratch_address(void **out, const char *fn) {
 
 extern "C" {
 
-int bitlinear_version(void) { return 10200; }  // 1.2.0: bitlinear_forward_fused_noalloc
+int bitlinear_version(void) { return 10300; }  // 1.3.0: bitlinear_layernorm(_quantize)
 
 const char *bitlinear_status_string(bl_status s) {
     switch (s) {
@@ -597,9 +597,10 @@ static bl_status check_norm(const char *fn, void *X, const void *delta, void *H,
     if (M <= 0 || K <= 0 || K % 8 != 0)
         return fail(BL_ESHAPE, "%s: M, K must be positive and K a multiple of 8 (M=%lld K=%lld)",
                     fn, (long long)M, (long long)K);
-    if (M > (1ll << 31) || K >= (1ll << 31) || M * K >= (1ll << 40))
-        return fail(BL_ESHAPE, "%s: M=%lld, K=%lld too large (K < 2^31, M*K < 2^40)", fn,
-                    (long long)M, (long long)K);
+    // one 256-thread block per row, and a grid holds fewer than 2^32 work-items
+    if (M >= (1ll << 24) || K >= (1ll << 31) || M * K >= (1ll << 40))
+        return fail(BL_ESHAPE, "%s: M=%lld, K=%lld too large (M < 2^24, K < 2^31, M*K < 2^40)",
+                    fn, (long long)M, (long long)K);
     CHECK(check_eps(eps, fn));
     if (!aligned(X, 16) || !aligned(H, 16) || (delta && !aligned(delta, 16)))
         return fail(BL_EALIGN, "%s: X, delta and H need 16-byte alignment", fn);
@@ -612,19 +613,21 @@ static bl_status check_norm(const char *fn, void *X, const void *delta, void *H,
     return BL_OK;
 }
 
-bl_status bitlinear_rmsnorm(void *X, const void *delta, void *H, int64_t M, int64_t K,
-                            float eps, void *stream) {
-    static const char fn[] = "bitlinear_rmsnorm";
+}  // extern "C"
+
+namespace {
+
+bl_status norm_entry(const char *fn, bool centre, void *X, const void *delta, void *H, int64_t M,
+                     int64_t K, float eps, void *stream) {
     CHECK(check_norm(fn, X, delta, H, M, K, eps));
     (void)hipGetLastError();
-    return device(bl::launch_rmsnorm(X, delta, H, M, K, eps, (hipStream_t)stream), fn);
+    return device(bl::launch_norm(X, delta, H, M, K, eps, centre, (hipStream_t)stream), fn);
 }
 
-bl_status bitlinear_rmsnorm_quantize(void *X, const void *delta, void *H, int64_t M, int64_t K,
-                                     float eps, int bits, bl_gran gran, float q_eps, void *Xq,
-                                     float *act_scale, void *workspace, size_t workspace_bytes,
-                                     void *stream) {
-    static const char fn[] = "bitlinear_rmsnorm_quantize";
+bl_status norm_quantize_entry(const char *fn, bool centre, void *X, const void *delta, void *H,
+                              int64_t M, int64_t K, float eps, int bits, bl_gran gran,
+                              float q_eps, void *Xq, float *act_scale, void *workspace,
+                              size_t workspace_bytes, void *stream) {
     CHECK(check_norm(fn, X, delta, H, M, K, eps));
     if (!Xq || !act_scale) return fail(BL_EINVAL, "%s: null pointer", fn);
     if (bits != 8 && bits != 4) return fail(BL_EINVAL, "%s: bits must be 8 or 4", fn);
@@ -639,13 +642,43 @@ bl_status bitlinear_rmsnorm_quantize(void *X, const void *delta, void *H, int64_
     (void)hipGetLastError();
     hipStream_t s = (hipStream_t)stream;
     if (gran == BL_PER_TOKEN)
-        return device(bl::launch_rmsnorm_quantize(X, delta, H, M, K, eps, bits, q_eps, Xq,
-                                                  act_scale, s), fn);
+        return device(bl::launch_norm_quantize(X, delta, H, M, K, eps, centre, bits, q_eps, Xq,
+                                               act_scale, s), fn);
     // per-tensor scales need the absmax of all of h: norm, then the quantizer on h
-    hipError_t e = bl::launch_rmsnorm(X, delta, H, M, K, eps, s);
+    hipError_t e = bl::launch_norm(X, delta, H, M, K, eps, centre, s);
     if (e != hipSuccess) return device(e, fn);
     return device(bl::launch_quantize_acts(H, 1, M, K, bits, (int)gran, q_eps, Xq, act_scale,
                                            workspace, s), fn);
+}
+
+}  // namespace
+
+extern "C" {
+
+bl_status bitlinear_rmsnorm(void *X, const void *delta, void *H, int64_t M, int64_t K,
+                            float eps, void *stream) {
+    return norm_entry("bitlinear_rmsnorm", false, X, delta, H, M, K, eps, stream);
+}
+
+bl_status bitlinear_rmsnorm_quantize(void *X, const void *delta, void *H, int64_t M, int64_t K,
+                                     float eps, int bits, bl_gran gran, float q_eps, void *Xq,
+                                     float *act_scale, void *workspace, size_t workspace_bytes,
+                                     void *stream) {
+    return norm_quantize_entry("bitlinear_rmsnorm_quantize", false, X, delta, H, M, K, eps, bits,
+                               gran, q_eps, Xq, act_scale, workspace, workspace_bytes, stream);
+}
+
+bl_status bitlinear_layernorm(void *X, const void *delta, void *H, int64_t M, int64_t K,
+                              float eps, void *stream) {
+    return norm_entry("bitlinear_layernorm", true, X, delta, H, M, K, eps, stream);
+}
+
+bl_status bitlinear_layernorm_quantize(void *X, const void *delta, void *H, int64_t M, int64_t K,
+                                       float eps, int bits, bl_gran gran, float q_eps, void *Xq,
+                                       float *act_scale, void *workspace, size_t workspace_bytes,
+                                       void *stream) {
+    return norm_quantize_entry("bitlinear_layernorm_quantize", true, X, delta, H, M, K, eps, bits,
+                               gran, q_eps, Xq, act_scale, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

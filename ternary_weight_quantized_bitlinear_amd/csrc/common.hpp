@@ -266,13 +266,14 @@ hipError_t launch_quantize_acts_rotated(const void *x, int x_bf16, int64_t M, in
 hipError_t launch_quantize_weights_rotated(const void *w, int w_bf16, int64_t N, int64_t K,
                                            float eps, uint8_t *packed, float *gamma, void *ws,
                                            hipStream_t s);
-// residual add and RMS norm of bf16 rows (glue between BitLinear layers)
-hipError_t launch_rmsnorm(void *x, const void *delta, void *h, int64_t M, int64_t K, float eps,
-                          hipStream_t s);
+// residual add and normalization of bf16 rows (glue between BitLinear layers): the RMS
+// form, or (centre) the non-affine layer norm
+hipError_t launch_norm(void *x, const void *delta, void *h, int64_t M, int64_t K, float eps,
+                       bool centre, hipStream_t s);
 // the same, fused with the per-token absmax quantization of h into codes and scales
-hipError_t launch_rmsnorm_quantize(void *x, const void *delta, void *h, int64_t M, int64_t K,
-                                   float eps, int bits, float q_eps, void *xq, float *scale,
-                                   hipStream_t s);
+hipError_t launch_norm_quantize(void *x, const void *delta, void *h, int64_t M, int64_t K,
+                                float eps, bool centre, int bits, float q_eps, void *xq,
+                                float *scale, hipStream_t s);
 // more than 64 KB of dynamic LDS must be allowed once per device and kernel
 hipError_t allow_lds(const void *fn, size_t lds);
 hipError_t launch_prepare_acts(const void *xq, int bits, int64_t M, int64_t K, uint8_t *xp,

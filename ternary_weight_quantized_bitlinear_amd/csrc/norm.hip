@@ -1,16 +1,24 @@
-// Glue between the BitLinear layers of a transformer block: residual add and RMS
-// normalisation of bf16 rows ("BitNet 2B4T Guide", "3. Sub-Layer Normalization
-// (SubLN)", and the block of its "End-to-End PyTorch Implementation" listing: each
-// sub-layer adds its output to the residual stream, the next one normalizes the stream
-// before its BitLinear quantizes it).  Weight 1 (its initial value); per row
-//     x' = bf16(fl32(x + delta)),   S = sum x'^2 exactly, rounded once to fp64,
-//     r  = 1 / sqrt(S / K + eps) in fp64,   h = bf16(fl32(x' * r))  (product in fp64).
+// Glue between the BitLinear layers of a transformer block: residual add and the
+// normalization of bf16 rows before the next quantizer, weight 1 and no bias, per row
+//     x' = bf16(fl32(x + delta))
+// in one of the two forms the pages show:
+//   RMS ("BitNet 2B4T Guide", "3. Sub-Layer Normalization (SubLN)", and the block of its
+//   "End-to-End PyTorch Implementation" listing: each sub-layer adds its output to the
+//   residual stream, the next one normalizes the stream before its BitLinear):
+//     S = sum x'^2 exactly, rounded once to fp64,  r = 1 / sqrt(S / K + eps),
+//     h = bf16(fl32(x' * r))  (product in fp64);
+//   layer norm ("BitNet b1.58: The 1-Bit Ternary LLM Architecture Guide",
+//   "Implementation", the Step 2 BitLinear listing: a non-affine layer norm over the
+//   last axis before the activation quantizer):
+//     S1 = sum x', D = K sum x'^2 - S1^2, each exact and rounded once to fp64,
+//     mu = S1 / K,  r = 1 / sqrt(D / (K K) + eps),  h = bf16(fl32((x' - mu) * r)).
 // One 256-thread block per row: each thread keeps its 8-element groups in registers
-// between the passes.  The exact S (exact_sumsq.hpp) needs the row's largest exponent
-// first, so pass 1 is two sweeps over the kept values with a barrier between them; the
-// window sums are integers, so the block's reduction order cannot change S.
+// between the passes.  The exact sums (exact_sumsq.hpp, exact_moments.hpp) need the
+// row's (or the wave's) largest exponent first, so pass 1 is two sweeps over the kept
+// values; the window sums are integers, so the block's reduction order cannot change
+// them.
 #include "common.hpp"
-#include "exact_sumsq.hpp"
+#include "exact_moments.hpp"
 
 namespace bl {
 namespace {
@@ -27,6 +35,32 @@ struct NormShared {
     int wmax[kNormWaves];  // each wave's largest biased exponent
     uint32_t big[kSqLimbs];  // slow path: the exact total
     double S;
+};
+
+// the layer norm's: exponent bins of the values below the window, wave sums, slow-path
+// working memory
+struct LayerShared {
+    int64_t bins1[256];   // sum of +-m per biased exponent
+    uint64_t bins2[256];  // sum of m^2 per biased exponent
+    uint64_t s1[kNormWaves][2], s2[kNormWaves][2];
+    int wspill[kNormWaves];
+    int wmax[kNormWaves];
+    uint32_t work[3 * kMomLimbs];
+    double s1d, dd;
+};
+
+template <bool kCentre>
+struct NormStorage {
+    typedef NormShared type;
+};
+template <>
+struct NormStorage<true> {
+    typedef LayerShared type;
+};
+
+// what pass 2 applies to each x': h = (x' - mu) * r (mu = 0 for the RMS form)
+struct RowNorm {
+    double mu, r;
 };
 
 __device__ __forceinline__ int wave_max_int(int v) {
@@ -66,12 +100,11 @@ __device__ __forceinline__ uint4 keep_get(const uint4 (&keep)[kN], int64_t i) {
     return q;
 }
 
-// Pass 1 of both kernels: x' = bf16(fl32(x + delta)) (written back when delta is given),
-// this thread's first kNormRegGroups groups of x' kept in `keep`, and r of the row.
-// Every thread of the block must call it (barriers inside).
-__device__ __forceinline__ double row_residual_r(uint16_t *xr, const uint16_t *dr, int64_t n8,
-                                                 float eps, uint4 (&keep)[kNormRegGroups],
-                                                 NormShared &sh) {
+// The first sweep of pass 1: x' = bf16(fl32(x + delta)) (written back when delta is
+// given), this thread's first kNormRegGroups groups of x' kept in `keep`.  Returns the
+// largest biased exponent among this thread's values.
+__device__ __forceinline__ int row_residual(uint16_t *xr, const uint16_t *dr, int64_t n8,
+                                            uint4 (&keep)[kNormRegGroups]) {
     int emax = 0;
     for (int64_t u = threadIdx.x, i = 0; u < n8; u += kNormThreads, ++i) {
         uint4 q = reinterpret_cast<const uint4 *>(xr)[u];
@@ -92,6 +125,14 @@ __device__ __forceinline__ double row_residual_r(uint16_t *xr, const uint16_t *d
         for (int j = 0; j < 4; ++j) emax = max(emax, max(sq_exp(w[j]), sq_exp(w[j] >> 16)));
         if (i < kNormRegGroups) keep_put(keep, i, q);
     }
+    return emax;
+}
+
+// The rest of pass 1 for the RMS form: r of the row from the exact sum of squares.
+// Every thread of the block must call it (barriers inside).
+__device__ __forceinline__ RowNorm row_stats(const uint16_t *xr, int64_t n8, int emax, float eps,
+                                             const uint4 (&keep)[kNormRegGroups],
+                                             NormShared &sh) {
     // Each wave anchors its window at its own largest exponent (no barrier needed for
     // it); the four wave sums are combined exactly after the block's one barrier.  Per
     // lane, the squares go into two 64-bit partial sums, flushed into a 128-bit sum.
@@ -167,13 +208,103 @@ __device__ __forceinline__ double row_residual_r(uint16_t *xr, const uint16_t *d
         __syncthreads();
         S = sh.S;
     }
-    return 1.0 / sqrt(S / (double)(n8 * 8) + (double)eps);
+    return RowNorm{0.0, 1.0 / sqrt(S / (double)(n8 * 8) + (double)eps)};
 }
 
+// The rest of pass 1 for the layer norm: mu and r of the row from the exact S1 and D.
+// The window is anchored at the row's largest exponent (one barrier to find it); values
+// more than 2^40 below it go into exponent bins as they are met, and only then does
+// thread 0 add everything exactly (mom_bins_stats).  Every thread of the block must call
+// it (barriers inside).
+__device__ __forceinline__ RowNorm row_stats(const uint16_t *xr, int64_t n8, int emax, float eps,
+                                             const uint4 (&keep)[kNormRegGroups],
+                                             LayerShared &sh) {
+    const int wv = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+    const int Ew = wave_max_int(emax);
+    if (lane == 0) sh.wmax[wv] = Ew;
+    sh.bins1[threadIdx.x] = 0;  // kNormThreads == 256 bins
+    sh.bins2[threadIdx.x] = 0;
+    __syncthreads();
+    const int E = max(max(max(sh.wmax[0], sh.wmax[1]), max(sh.wmax[2], sh.wmax[3])), 1);
+    SqAcc part;
+    u128 acc2 = 0;
+    i128 acc1 = 0;
+    int64_t p1 = 0;
+    bool spill = false;
+    for (int64_t u = threadIdx.x, i = 0; u < n8; u += kNormThreads, ++i) {
+        const uint4 q = i < kNormRegGroups ? keep_get(keep, i)
+                                           : reinterpret_cast<const uint4 *>(xr)[u];
+        const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const uint32_t b = (w[j / 2] >> (16 * (j % 2))) & 0xFFFFu;
+            p1 += mom_s1_term(b, E);
+            if (sq_acc_step(b, E, part)) {  // below the window: into the bins
+                spill = true;
+                const int e = sq_exp(b);
+                const int64_t m = (int64_t)((b & 0x7Fu) | (e ? 0x80u : 0u));
+                atomicAdd(reinterpret_cast<unsigned long long *>(&sh.bins1[e ? e : 1]),
+                          (unsigned long long)((b & 0x8000u) ? -m : m));
+                atomicAdd(reinterpret_cast<unsigned long long *>(&sh.bins2[e ? e : 1]),
+                          (unsigned long long)(m * m));
+            }
+        }
+        if ((i + 1) % (kSqAccSteps / 8) == 0) {
+            sq_acc_flush(part, acc2);
+            acc1 += p1;
+            p1 = 0;
+        }
+    }
+    sq_acc_flush(part, acc2);
+    acc1 += p1;
+    // integer sums (S1 in two's complement, modulo 2^128): the same total in any order
+    const u128 w2 = wave_sum_u128(acc2);
+    const u128 w1 = wave_sum_u128((u128)acc1);
+    const bool wspill = __ballot(spill) != 0;
+    if (lane == 0) {
+        sh.s2[wv][0] = (uint64_t)w2;
+        sh.s2[wv][1] = (uint64_t)(w2 >> 64);
+        sh.s1[wv][0] = (uint64_t)w1;
+        sh.s1[wv][1] = (uint64_t)(w1 >> 64);
+        sh.wspill[wv] = wspill ? 1 : 0;
+    }
+    __syncthreads();  // also: every bin complete
+    u128 s2 = 0, s1 = 0;
+    int any_spill = 0;
+#pragma unroll
+    for (int i = 0; i < kNormWaves; ++i) {
+        s2 += ((u128)sh.s2[i][1] << 64) | sh.s2[i][0];
+        s1 += ((u128)sh.s1[i][1] << 64) | sh.s1[i][0];
+        any_spill |= sh.wspill[i];
+    }
+    double s1d, dd;
+    if (!any_spill) {
+        mom_window_stats(s2, (i128)s1, E, n8 * 8, &s1d, &dd);
+    } else {
+        if (threadIdx.x == 0)
+            mom_bins_stats(s2, (i128)s1, E, sh.bins1, sh.bins2, n8 * 8, sh.work, &sh.s1d, &sh.dd);
+        __syncthreads();
+        s1d = sh.s1d;
+        dd = sh.dd;
+    }
+    const double K = (double)(n8 * 8);
+    return RowNorm{s1d / K, 1.0 / sqrt(dd / (K * K) + (double)eps)};
+}
+
+// x' of one element normalized and rounded to fp32 (pass 2)
+template <bool kCentre>
+__device__ __forceinline__ float norm_value(float v, const RowNorm &s) {
+    if constexpr (kCentre)
+        return (float)(((double)v - s.mu) * s.r);
+    else
+        return (float)((double)v * s.r);
+}
+
+template <bool kCentre>
 __global__ void __launch_bounds__(kNormThreads)
-rmsnorm_rows(uint16_t *__restrict__ x, const uint16_t *__restrict__ delta,
-             uint16_t *__restrict__ h, int64_t K, float eps) {
-    __shared__ NormShared sh;
+norm_rows(uint16_t *__restrict__ x, const uint16_t *__restrict__ delta,
+          uint16_t *__restrict__ h, int64_t K, float eps) {
+    __shared__ typename NormStorage<kCentre>::type sh;
     const int64_t m = blockIdx.x;
     const int64_t n8 = K / 8;
     uint16_t *xr = x + m * K;
@@ -182,7 +313,8 @@ rmsnorm_rows(uint16_t *__restrict__ x, const uint16_t *__restrict__ delta,
     uint4 keep[kNormRegGroups];
 #pragma unroll
     for (int i = 0; i < kNormRegGroups; ++i) keep[i] = make_uint4(0u, 0u, 0u, 0u);
-    const double r = row_residual_r(xr, dr, n8, eps, keep, sh);
+    const int emax = row_residual(xr, dr, n8, keep);
+    const RowNorm s = row_stats(xr, n8, emax, eps, keep, sh);
     // pass 2: normalize (groups beyond the register-held ones are re-read)
     for (int64_t u = threadIdx.x, i = 0; u < n8; u += kNormThreads, ++i) {
         const uint4 q = i < kNormRegGroups ? keep_get(keep, i)
@@ -191,8 +323,8 @@ rmsnorm_rows(uint16_t *__restrict__ x, const uint16_t *__restrict__ delta,
         uint32_t o[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const uint32_t lo = to_bf16_bits((float)((double)bf16_lo(w[j]) * r));
-            const uint32_t hi = to_bf16_bits((float)((double)bf16_hi(w[j]) * r));
+            const uint32_t lo = to_bf16_bits(norm_value<kCentre>(bf16_lo(w[j]), s));
+            const uint32_t hi = to_bf16_bits(norm_value<kCentre>(bf16_hi(w[j]), s));
             o[j] = (lo & 0xFFFFu) | (hi << 16);
         }
         reinterpret_cast<uint4 *>(hr)[u] = make_uint4(o[0], o[1], o[2], o[3]);
@@ -204,12 +336,12 @@ rmsnorm_rows(uint16_t *__restrict__ x, const uint16_t *__restrict__ delta,
 // "BitNet a4.8 Guide", "1. Hybrid W1.58 / A4 Quantization Function"): after h is
 // formed, the block reduces max |h| and writes the codes and the scale exactly as the
 // activation quantizer would from h.
-template <int kBits>
+template <bool kCentre, int kBits>
 __global__ void __launch_bounds__(kNormThreads)
-rmsnorm_quant_rows(uint16_t *__restrict__ x, const uint16_t *__restrict__ delta,
-                   uint16_t *__restrict__ h, int64_t K, float eps, float q_eps,
-                   uint8_t *__restrict__ xq, float *__restrict__ scale) {
-    __shared__ NormShared sh;
+norm_quant_rows(uint16_t *__restrict__ x, const uint16_t *__restrict__ delta,
+                uint16_t *__restrict__ h, int64_t K, float eps, float q_eps,
+                uint8_t *__restrict__ xq, float *__restrict__ scale) {
+    __shared__ typename NormStorage<kCentre>::type sh;
     __shared__ float redf[kNormWaves];
     const int64_t m = blockIdx.x;
     const int64_t n8 = K / 8;
@@ -221,7 +353,8 @@ rmsnorm_quant_rows(uint16_t *__restrict__ x, const uint16_t *__restrict__ delta,
     for (int i = 0; i < kNormRegGroups; ++i) keep[i] = make_uint4(0u, 0u, 0u, 0u);
     auto put = [&](int64_t i, uint4 q) __attribute__((always_inline)) { keep_put(keep, i, q); };
     auto get = [&](int64_t i) __attribute__((always_inline)) { return keep_get(keep, i); };
-    const double r = row_residual_r(xr, dr, n8, eps, keep, sh);
+    const int emax = row_residual(xr, dr, n8, keep);
+    const RowNorm s = row_stats(xr, n8, emax, eps, keep, sh);
     // pass 2: h (kept in registers for pass 3), max |h|
     float mx = 0.0f;
     for (int64_t u = threadIdx.x, i = 0; u < n8; u += kNormThreads, ++i) {
@@ -230,8 +363,8 @@ rmsnorm_quant_rows(uint16_t *__restrict__ x, const uint16_t *__restrict__ delta,
         uint32_t o[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const uint32_t lo = to_bf16_bits((float)((double)bf16_lo(w[j]) * r));
-            const uint32_t hi = to_bf16_bits((float)((double)bf16_hi(w[j]) * r));
+            const uint32_t lo = to_bf16_bits(norm_value<kCentre>(bf16_lo(w[j]), s));
+            const uint32_t hi = to_bf16_bits(norm_value<kCentre>(bf16_hi(w[j]), s));
             o[j] = (lo & 0xFFFFu) | (hi << 16);
             mx = fmaxf(mx, fmaxf(fabsf(bf16_lo(o[j])), fabsf(bf16_hi(o[j]))));
         }
@@ -274,25 +407,33 @@ rmsnorm_quant_rows(uint16_t *__restrict__ x, const uint16_t *__restrict__ delta,
 
 }  // namespace
 
-hipError_t launch_rmsnorm_quantize(void *x, const void *delta, void *h, int64_t M, int64_t K,
-                                   float eps, int bits, float q_eps, void *xq, float *scale,
-                                   hipStream_t s) {
-    if (bits == 8)
-        hipLaunchKernelGGL(rmsnorm_quant_rows<8>, dim3((unsigned)M), dim3(kNormThreads), 0, s,
-                           static_cast<uint16_t *>(x), static_cast<const uint16_t *>(delta),
-                           static_cast<uint16_t *>(h), K, eps, q_eps, static_cast<uint8_t *>(xq), scale);
+hipError_t launch_norm_quantize(void *x, const void *delta, void *h, int64_t M, int64_t K,
+                                float eps, bool centre, int bits, float q_eps, void *xq,
+                                float *scale, hipStream_t s) {
+    uint16_t *xp = static_cast<uint16_t *>(x), *hp = static_cast<uint16_t *>(h);
+    const uint16_t *dp = static_cast<const uint16_t *>(delta);
+    uint8_t *qp = static_cast<uint8_t *>(xq);
+    const dim3 grid((unsigned)M), block(kNormThreads);
+    if (centre && bits == 8)
+        hipLaunchKernelGGL((norm_quant_rows<true, 8>), grid, block, 0, s, xp, dp, hp, K, eps, q_eps, qp, scale);
+    else if (centre)
+        hipLaunchKernelGGL((norm_quant_rows<true, 4>), grid, block, 0, s, xp, dp, hp, K, eps, q_eps, qp, scale);
+    else if (bits == 8)
+        hipLaunchKernelGGL((norm_quant_rows<false, 8>), grid, block, 0, s, xp, dp, hp, K, eps, q_eps, qp, scale);
     else
-        hipLaunchKernelGGL(rmsnorm_quant_rows<4>, dim3((unsigned)M), dim3(kNormThreads), 0, s,
-                           static_cast<uint16_t *>(x), static_cast<const uint16_t *>(delta),
-                           static_cast<uint16_t *>(h), K, eps, q_eps, static_cast<uint8_t *>(xq), scale);
+        hipLaunchKernelGGL((norm_quant_rows<false, 4>), grid, block, 0, s, xp, dp, hp, K, eps, q_eps, qp, scale);
     return hipGetLastError();
 }
 
-hipError_t launch_rmsnorm(void *x, const void *delta, void *h, int64_t M, int64_t K, float eps,
-                          hipStream_t s) {
-    hipLaunchKernelGGL(rmsnorm_rows, dim3((unsigned)M), dim3(kNormThreads), 0, s,
-                       static_cast<uint16_t *>(x), static_cast<const uint16_t *>(delta),
-                       static_cast<uint16_t *>(h), K, eps);
+hipError_t launch_norm(void *x, const void *delta, void *h, int64_t M, int64_t K, float eps,
+                       bool centre, hipStream_t s) {
+    uint16_t *xp = static_cast<uint16_t *>(x), *hp = static_cast<uint16_t *>(h);
+    const uint16_t *dp = static_cast<const uint16_t *>(delta);
+    const dim3 grid((unsigned)M), block(kNormThreads);
+    if (centre)
+        hipLaunchKernelGGL(norm_rows<true>, grid, block, 0, s, xp, dp, hp, K, eps);
+    else
+        hipLaunchKernelGGL(norm_rows<false>, grid, block, 0, s, xp, dp, hp, K, eps);
     return hipGetLastError();
 }
 

@@ -24,8 +24,8 @@ def test_exports_every_header_function(L):
     assert set(names) == {
         "bitlinear_quantize_weights", "bitlinear_quantize_acts", "bitlinear_forward",
         "bitlinear_forward_fused", "bitlinear_forward_fused_batched", "bitlinear_forward_multi",
-        "bitlinear_rmsnorm",
-        "bitlinear_rmsnorm_quantize", "bitlinear_workspace_size", "bitlinear_status_string",
+        "bitlinear_rmsnorm", "bitlinear_rmsnorm_quantize", "bitlinear_layernorm",
+        "bitlinear_layernorm_quantize", "bitlinear_workspace_size", "bitlinear_status_string",
         "bitlinear_last_error", "bitlinear_version", "bitlinear_hadamard_block",
         "bitlinear_quantize_weights_rotated", "bitlinear_quantize_acts_rotated",
         "bitlinear_backward", "bitlinear_forward_fused_noalloc",
@@ -47,7 +47,7 @@ def test_library_is_gfx950_code():
 def test_status_strings_and_version(L):
     for s in range(7):
         assert L.bitlinear_status_string(s).decode()
-    assert L.bitlinear_version() >= 10200  # 1.2: bitlinear_forward_fused_noalloc
+    assert L.bitlinear_version() >= 10300  # 1.3: bitlinear_layernorm(_quantize)
 
 
 def test_workspace_sizes(L):
@@ -232,8 +232,9 @@ def test_forward_multi_rejects(L):
     assert L.bitlinear_last_error().decode().startswith("bitlinear_forward_multi")
 
 
-def test_rmsnorm_rejects(L):
-    f = L.bitlinear_rmsnorm
+@pytest.mark.parametrize("name", ["bitlinear_rmsnorm", "bitlinear_layernorm"])
+def test_norm_rejects(L, name):
+    f = getattr(L, name)
     assert f(None, None, P(A + 4096), 16, 2560, 1e-6, None) == bl.BL_EINVAL
     assert f(P(A), None, None, 16, 2560, 1e-6, None) == bl.BL_EINVAL
     assert f(P(A), None, P(A + (1 << 20)), 16, 2564, 1e-6, None) == bl.BL_ESHAPE
@@ -244,11 +245,14 @@ def test_rmsnorm_rejects(L):
     # H overlapping X or delta
     assert f(P(A), None, P(A + 4096), 16, 2560, 1e-6, None) == bl.BL_EINVAL
     assert f(P(A), P(A + (1 << 21)), P(A + (1 << 21) + 64), 16, 2560, 1e-6, None) == bl.BL_EINVAL
-    assert L.bitlinear_last_error().decode().startswith("bitlinear_rmsnorm")
+    # one block per row: at most 2^24 - 1 rows (the grid's work-item limit)
+    assert f(P(A), None, P(A + (1 << 40)), 1 << 24, 8, 1e-6, None) == bl.BL_ESHAPE
+    assert L.bitlinear_last_error().decode().startswith(name)
 
 
-def test_rmsnorm_quantize_rejects(L):
-    f = L.bitlinear_rmsnorm_quantize
+@pytest.mark.parametrize("name", ["bitlinear_rmsnorm_quantize", "bitlinear_layernorm_quantize"])
+def test_norm_quantize_rejects(L, name):
+    f = getattr(L, name)
     X, H, Q, S = P(A), P(A + (1 << 20)), P(A + (2 << 20)), P(A + (3 << 20))
 
     def call(**kw):
@@ -266,7 +270,7 @@ def test_rmsnorm_quantize_rejects(L):
     assert call(Q=P(A + (2 << 20) + 4)) == bl.BL_EALIGN
     assert call(gran=1) == bl.BL_EWORKSPACE      # per tensor needs the absmax word
     assert call(H=P(A + 64)) == bl.BL_EINVAL     # H overlaps X
-    assert L.bitlinear_last_error().decode().startswith("bitlinear_rmsnorm_quantize")
+    assert L.bitlinear_last_error().decode().startswith(name)
 
 
 def _bwd(L, **kw):

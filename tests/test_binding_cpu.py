@@ -126,6 +126,16 @@ CASES = [
     ("rmsnorm_quantize: out codes", lambda: bl.rmsnorm_quantize(
         t((M, K), torch.bfloat16), out=(t((M, K), torch.bfloat16), t((M, K // 2), torch.int8),
                                         t((M,)))), bl.BL_ESHAPE, "Xq"),
+    ("layernorm: fp32 X", lambda: bl.layernorm(t((M, K))), bl.BL_EINVAL, "X"),
+    ("layernorm: delta dtype", lambda: bl.layernorm(t((M, K), torch.bfloat16), t((M, K))),
+     bl.BL_EINVAL, "delta"),
+    ("layernorm: host tensors", lambda: bl.layernorm(t((M, K), torch.bfloat16)),
+     bl.BL_EINVAL, "GPU"),
+    ("layernorm_quantize: out scale", lambda: bl.layernorm_quantize(
+        t((M, K), torch.bfloat16), out=(t((M, K), torch.bfloat16), t((M, K), torch.int8),
+                                        t((M + 1,)))), bl.BL_ESHAPE, "act_scale"),
+    ("layernorm_quantize: bits", lambda: bl.layernorm_quantize(t((M, K), torch.bfloat16), bits=2),
+     bl.BL_EINVAL, "bits"),
     # backward
     ("backward: fp32 dY", lambda: bl.backward(t((M, N)), t((M, K), torch.int8), t((M,)),
                                               t((N, K // 4), torch.uint8), t((1,))),
