@@ -75,6 +75,7 @@ aq_rows(const void *__restrict__ x, int64_t K, float eps, const uint32_t *__rest
     }
     const float a = fmaxf(amax, eps);
     const float s = kBits == 8 ? 127.0f / a : a / 7.0f;
+    const float r4 = q4_recip(s);
     if (threadIdx.x == 0 && (!kTensor || m == 0)) scale[kTensor ? 0 : m] = s;
     for (int64_t u = threadIdx.x, i = 0; u < n8; u += kT, ++i) {
         float v[8];
@@ -95,7 +96,7 @@ aq_rows(const void *__restrict__ x, int64_t K, float eps, const uint32_t *__rest
         } else {
             uint32_t o = 0;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) o |= q4(v[j], s) << (4 * j);
+            for (int j = 0; j < 8; ++j) o |= q4(v[j], s, r4) << (4 * j);
             reinterpret_cast<uint32_t *>(static_cast<uint8_t *>(xq) + m * (K / 2))[u] = o;
         }
     }
@@ -152,6 +153,7 @@ aq_rows_prep(const void *__restrict__ x, int64_t K, float eps,
     }
     const float a = fmaxf(amax, eps);
     const float s = kBits == 8 ? 127.0f / a : a / 7.0f;
+    const float r4 = q4_recip(s);
     if (threadIdx.x == 0 && (!kTensor || m == 0)) scale[kTensor ? 0 : m] = s;
     int csum = 0;
     for (int64_t u = threadIdx.x; u < n16; u += kAqThreads) {
@@ -165,7 +167,7 @@ aq_rows_prep(const void *__restrict__ x, int64_t K, float eps,
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const uint32_t c = kBits == 8 ? q8(v[4 * d + j], s)
-                                              : ((uint32_t)(((int)(q4(v[4 * d + j], s) << 28)) >> 28) & 0xFFu);
+                                              : ((uint32_t)(((int)(q4(v[4 * d + j], s, r4) << 28)) >> 28) & 0xFFu);
                 o |= c << (8 * j);
             }
             nat[d] = o;
@@ -318,6 +320,7 @@ aq_rows_rot(const void *__restrict__ x, int64_t K, int b, float eps, uint32_t *_
     }
     const float a = fmaxf(amax, eps);
     const float s = kBits == 8 ? 127.0f / a : a / 7.0f;
+    const float r4 = q4_recip(s);
     if (threadIdx.x == 0 && (kPass == 0 || m == 0)) scale[kPass == 0 ? m : 0] = s;
     for (int u = threadIdx.x; u < k8; u += kAqThreads) {
         const float *v = rowl + 8 * u;
@@ -329,7 +332,7 @@ aq_rows_rot(const void *__restrict__ x, int64_t K, int b, float eps, uint32_t *_
         } else {
             uint32_t o = 0;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) o |= q4(v[j], s) << (4 * j);
+            for (int j = 0; j < 8; ++j) o |= q4(v[j], s, r4) << (4 * j);
             reinterpret_cast<uint32_t *>(static_cast<uint8_t *>(xq) + m * (K / 2))[u] = o;
         }
     }

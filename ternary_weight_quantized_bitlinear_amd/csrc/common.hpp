@@ -126,8 +126,20 @@ __device__ __forceinline__ uint32_t q8(float x, float s) {
     v = fminf(fmaxf(v, -128.0f), 127.0f);
     return (uint32_t)((int)v) & 0xFFu;
 }
-__device__ __forceinline__ uint32_t q4(float x, float s) {
-    float v = __builtin_rintf(x / s);
+// The int4 code of x, rint(fl32(x / s)) clipped to [-8, 7] ("BitNet a4.8 Guide", "1. Hybrid
+// W1.58 / A4 Quantization Function"), without a division per code: with r = q4_recip(s),
+// t = fl32(x r).  When |x / s| <= 8 (|x| at most the absmax that set s), t lies within
+// 2^-19 of fl32(x / s): the roundings of r and of t move it by at most 2^-23 |x / s|, and
+// fl32(x / s) is within half an ulp (2^-22) of x / s.  Both therefore round to the same
+// integer unless t lies within 2^-18 of a half-integer (which covers every tie of
+// fl32(x / s)); there, and whenever r is NaN, the quotient is divided exactly.
+__host__ __device__ inline float q4_recip(float s) {
+    return s >= 0x1p-125f ? 1.0f / s : __builtin_nanf("");
+}
+__host__ __device__ inline uint32_t q4(float x, float s, float r) {
+    const float t = x * r;
+    float v = __builtin_rintf(t);
+    if (!(fabsf(fabsf(t - v) - 0.5f) >= 0x1p-18f)) v = __builtin_rintf(x / s);
     v = fminf(fmaxf(v, -8.0f), 7.0f);
     return (uint32_t)((int)v) & 0xFu;
 }

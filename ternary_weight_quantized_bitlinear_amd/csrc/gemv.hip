@@ -132,6 +132,7 @@ __device__ __forceinline__ void quantize_store(const uint4 (&r)[RawWords<kMode>:
                                                uint8_t *xrow, int g) {
     float v[16];
     widen16<kMode>(r, v);
+    const float r4 = kBits == 8 ? 0.0f : q4_recip(sc);
     uint32_t nat[4];
     if (kBits == 8) {
 #pragma unroll
@@ -144,7 +145,7 @@ __device__ __forceinline__ void quantize_store(const uint4 (&r)[RawWords<kMode>:
             uint32_t wd = 0;
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                wd |= ((uint32_t)(((int)(q4(v[4 * d + j], sc) << 28)) >> 28) & 0xFFu) << (8 * j);
+                wd |= ((uint32_t)(((int)(q4(v[4 * d + j], sc, r4) << 28)) >> 28) & 0xFFu) << (8 * j);
             nat[d] = wd;
         }
     }
@@ -678,6 +679,7 @@ __global__ void __launch_bounds__(64 * kStreamWaves) gemv_stream_kernel(GemvPara
             sc = p.act_scale[p.gran == 1 ? 0 : m];
         }
         if (tid == 0) s_f[m] = kBits == 8 ? gamma / sc : sc * gamma;
+        const float r4 = kBits == 8 ? 0.0f : q4_recip(sc);
         uint8_t *xrow_m = xl + (size_t)m * Kpad;
         int csum = 0;
 #pragma unroll 1
@@ -706,7 +708,7 @@ __global__ void __launch_bounds__(64 * kStreamWaves) gemv_stream_kernel(GemvPara
                         uint32_t wd = 0;
 #pragma unroll
                         for (int j = 0; j < 4; ++j)
-                            wd |= ((uint32_t)(((int)(q4(v[4 * d + j], sc) << 28)) >> 28) & 0xFFu) << (8 * j);
+                            wd |= ((uint32_t)(((int)(q4(v[4 * d + j], sc, r4) << 28)) >> 28) & 0xFFu) << (8 * j);
                         nat[d] = wd;
                     }
                 }

@@ -380,6 +380,7 @@ norm_quant_rows(uint16_t *__restrict__ x, const uint16_t *__restrict__ delta,
     for (int i = 1; i < kNormWaves; ++i) amax = fmaxf(amax, redf[i]);
     const float a = fmaxf(amax, q_eps);
     const float sc = kBits == 8 ? 127.0f / a : a / 7.0f;
+    const float r4 = q4_recip(sc);
     if (threadIdx.x == 0) scale[m] = sc;
     // pass 3: codes of h (this thread's own h words: kept, or re-read from its own stores)
     for (int64_t u = threadIdx.x, i = 0; u < n8; u += kNormThreads, ++i) {
@@ -399,7 +400,7 @@ norm_quant_rows(uint16_t *__restrict__ x, const uint16_t *__restrict__ delta,
         } else {
             uint32_t o = 0;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) o |= q4(v[j], sc) << (4 * j);
+            for (int j = 0; j < 8; ++j) o |= q4(v[j], sc, r4) << (4 * j);
             reinterpret_cast<uint32_t *>(xq + m * (K / 2))[u] = o;
         }
     }
