@@ -30,6 +30,8 @@ parity_layer = the 8 x 256 -> 512 parity configuration, timed only
 mfma_ceiling = MFMA-only loops on register operands with each GEMM's operand statistics
                (int8, FP4 x FP6, bf16): the matrix cores' rate on this chip, reported
                beside each GEMM's fraction of the published peak
+hbm_read_ceiling = a read-only sweep of 16-byte loads over 1 GiB: the rate streaming
+               reads reach on this chip, beside the decode kernel's fraction of 8 TB/s
 cpu_baseline = the CPU oracle pinned to one core: one layer's decode FFN step (the
                headline's unit), plus the parity layer in full and samples of the
                prefill GEMM, the 30-layer stack and the 70B layer, extrapolated
@@ -514,10 +516,12 @@ def _fwht_rows(x, b):
 def leg_stack(torch, bl, steps=10, layers=30, batch=16):
     """The 2B-shaped decode stack: 30 blocks of QKV 2560->7680, O 2560->2560, up
     2560->6912 (+ReLU^2), down 6912->2560, batch 16 tokens, seed-fixed weights.  Per
-    block: RMS norm fused with the quantization of h -> Q, K, V on those codes in one
-    call (V feeds O) -> O -> residual + RMS norm + quantization -> up -> down ->
-    residual; O and down quantize their bf16 inputs themselves.  One step = all 30
-    blocks for the 16 tokens, the K steps in one graph."""
+    block: residual add + RMS norm + quantization + Q, K, V in one call (V feeds O)
+    -> O -> residual add + RMS norm + quantization + up in one call -> down; O and down
+    quantize their bf16 inputs themselves.  One step = all 30 blocks for the 16 tokens,
+    the K steps in one graph.  The same block as separate calls (norm + quantization,
+    then the projections) is timed beside it, and both must end on the same residual
+    stream, bit for bit."""
     import workloads
     dev = torch.device("cuda:0")
     H = workloads.HIDDEN
@@ -548,7 +552,35 @@ def leg_stack(torch, bl, steps=10, layers=30, batch=16):
     u = torch.empty((batch, workloads.FFN), dtype=torch.bfloat16, device=dev)
     d = torch.empty((batch, H), dtype=torch.bfloat16, device=dev)
 
+    bufs = (torch.empty_like(x0), torch.empty_like(x0))
+    nf_ws = torch.empty(max(bl.workspace_size(bl.BL_OP_NORM_FORWARD, batch, n, H)
+                            for n in (H, workloads.FFN)), dtype=torch.uint8, device=dev)
+    ff_ws = torch.empty(max(bl.workspace_size(bl.BL_OP_FORWARD_FUSED, batch, n, k)
+                            for n, k in ((H, H), (H, workloads.FFN))), dtype=torch.uint8, device=dev)
+    final = {}
+
     def step():
+        # each sub-layer's input side in one call: residual add (into the other stream
+        # buffer), RMS norm, quantization and the projections (Q, K, V in one call)
+        cur, delta = x0, None
+        for lw in W:
+            pq3, gq3 = lw["qkv3"]
+            nxt = bufs[0] if cur is not bufs[0] else bufs[1]
+            bl.norm_forward(cur, pq3, gq3, delta=delta, x_out=nxt if delta is not None else None,
+                            out=qkv, workspace=nf_ws)
+            cur = nxt if delta is not None else cur
+            bl.forward_fused(v, *lw["o"], out=o, workspace=ff_ws)
+            nxt = bufs[0] if cur is not bufs[0] else bufs[1]
+            bl.norm_forward(cur, *lw["up"], delta=o, x_out=nxt, epilogue="relu2", out=u,
+                            workspace=nf_ws)
+            cur = nxt
+            bl.forward_fused(u, *lw["down"], out=d, workspace=ff_ws)
+            delta = d
+        bl.rmsnorm(cur, delta, out=h)  # the last residual
+        final["x"] = cur
+
+    def step_unfused():
+        # the same block as separate calls: norm + quantization, then the projections
         x.copy_(x0)
         delta = None
         for lw in W:
@@ -566,14 +598,24 @@ def leg_stack(torch, bl, steps=10, layers=30, batch=16):
         for _ in range(steps):
             step()
 
+    def run_unfused():
+        for _ in range(steps):
+            step_unfused()
+
     step()
+    step_unfused()
     torch.cuda.synchronize()
-    finite = bool(torch.isfinite(x.float()).all())
+    finite = bool(torch.isfinite(final["x"].float()).all())
+    same = bool(torch.equal(final["x"].view(torch.int16), x.view(torch.int16)))
     ms, _ = graph_time_ms(torch, run, replays=1)
     ms /= steps
+    ms_u, _ = graph_time_ms(torch, run_unfused, replays=1)
+    ms_u /= steps
     return {"layers": layers, "batch": batch, "ms_per_step": ms, "tokens_per_s": batch / (ms * 1e-3),
             "weight_bytes_per_step": wbytes, "weight_gbs": wbytes / (ms * 1e-3) / 1e9,
-            "library_calls_per_step": layers * 6 + 1, "output_finite": finite}
+            "library_calls_per_step": layers * 4 + 1, "output_finite": finite,
+            "unfused_ms_per_step": ms_u, "unfused_library_calls_per_step": layers * 6 + 1,
+            "fused_equals_unfused": same}
 
 
 def leg_parity_layer(torch, bl, reps=200):
@@ -751,6 +793,51 @@ def leg_mfma_ceiling(torch, reps=3):
     return out
 
 
+def leg_hbm_ceiling(torch, reps=5, mib=1024):
+    """HBM read ceiling on this chip: a read-only sweep of 16-byte non-temporal loads over
+    a buffer four times the last-level cache (libbitlinear_calib.so), at several grid
+    sizes; the best median.  The weight-streaming decode kernels read and barely write,
+    so this is the rate their fraction can be read against, beside the published peak."""
+    import ctypes
+    lib = ctypes.CDLL(CALIB_LIB)
+    lib.bl_calib_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                  ctypes.c_void_p, ctypes.c_void_p]
+    lib.bl_calib_read.restype = ctypes.c_int
+    nbytes = mib << 20
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda:0")
+    stream = torch.cuda.current_stream()
+    best = None
+    sweep = {}
+    modes = {0: "nt4", 1: "nt8", 2: "plain8"}
+    for mode, blocks in [(m, b) for m in modes for b in (2048, 4096, 8192, 16384, 32768)]:
+        sink = torch.empty(blocks, dtype=torch.int32, device="cuda:0")
+
+        def launch():
+            st = lib.bl_calib_read(ctypes.c_void_p(buf.data_ptr()), nbytes, blocks, mode,
+                                   ctypes.c_void_p(sink.data_ptr()),
+                                   ctypes.c_void_p(stream.cuda_stream))
+            if st != 0:
+                raise RuntimeError("calibration launch failed: HIP status %d" % st)
+        launch()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            launch()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        gbs = nbytes / (sorted(ts)[len(ts) // 2] * 1e-3) / 1e9
+        sweep["%s_%d" % (modes[mode], blocks)] = round(gbs, 1)
+        if best is None or gbs > best[0]:
+            best = (gbs, modes[mode], blocks)
+    del buf
+    return {"gbs": round(best[0], 1), "of_peak": round(best[0] / HBM_PEAK_GBS, 4),
+            "loads": best[1], "blocks": best[2], "bytes": nbytes, "gbs_by_config": sweep}
+
+
 def _timed(fn, budget_s, max_n=1000):
     """Calls fn() until budget_s of wall time has passed: (calls, seconds)."""
     n = 0
@@ -899,6 +986,7 @@ def main():
             side["parity_layer"] = leg_parity_layer(torch, bl)
         if "ceiling" in legs:
             side["mfma_ceiling"] = leg_mfma_ceiling(torch)
+            side["hbm_read_ceiling"] = leg_hbm_ceiling(torch)
         if side:
             print(json.dumps(side))
         return
@@ -988,6 +1076,10 @@ def main():
         # each matrix-core rate beside the MFMA-only ceiling measured for its operands
         ceil = leg_mfma_ceiling(torch)
         out["mfma_ceiling"] = ceil
+        hbm = leg_hbm_ceiling(torch)
+        out["hbm_read_ceiling"] = hbm
+        out["roofline"]["read_ceiling_gbs"] = hbm["gbs"]
+        out["roofline"]["frac_of_read_ceiling"] = round(out["roofline"]["achieved"] / hbm["gbs"], 4)
         c8 = ceil["int8_32x32x32"]["tops"]
         c4 = ceil["fp4_x_fp6_32x32x64"]["tops"]
         cb = ceil["bf16_32x32x16"]["tops"]

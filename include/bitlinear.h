@@ -79,12 +79,14 @@ typedef enum {
 typedef enum { BL_F32 = 0, BL_BF16 = 1, BL_I32 = 2, BL_ENUM_RANGE(BL_DTYPE) } bl_dtype;
 typedef enum { BL_PER_TOKEN = 0, BL_PER_TENSOR = 1, BL_ENUM_RANGE(BL_GRAN) } bl_gran;
 typedef enum { BL_EPI_NONE = 0, BL_EPI_RELU2 = 1, BL_ENUM_RANGE(BL_EPI) } bl_epi;
+typedef enum { BL_NORM_NONE = 0, BL_NORM_RMS = 1, BL_NORM_LAYER = 2, BL_ENUM_RANGE(BL_NORM) } bl_norm;
 typedef enum {
     BL_OP_QUANTIZE_WEIGHTS = 0,
     BL_OP_QUANTIZE_ACTS = 1,
     BL_OP_FORWARD = 2,
     BL_OP_FORWARD_FUSED = 3,
     BL_OP_BACKWARD = 4,
+    BL_OP_NORM_FORWARD = 5,
     BL_ENUM_RANGE(BL_OP)
 } bl_op;
 
@@ -337,6 +339,47 @@ bl_status bitlinear_layernorm_quantize(void *X, const void *delta, void *H, int6
                                        int64_t K, float eps, int bits, bl_gran gran,
                                        float q_eps, void *Xq, float *act_scale, void *workspace,
                                        size_t workspace_bytes, void *stream);
+
+/*
+ * The input side of a BitLinear (or of several that share one input, e.g. Q, K, V) and
+ * the projections, in one call: the residual add, the normalization of the next
+ * sub-layer, the absmax quantization of its output h and each part's forward on those
+ * codes ("BitNet 2B4T Guide", "3. Sub-Layer Normalization (SubLN)" and the block of its
+ * "End-to-End PyTorch Implementation" listing: residual add, norm, then each BitLinear
+ * quantizes its input; "BitNet b1.58: The 1-Bit Ternary LLM Architecture Guide",
+ * "Implementation", Step 2: layer norm, quantizer, ternary product, rescale).  Per token:
+ *   x'  = bf16(fl32(X + delta))    stored to X_out (delta NULL: x' = X, nothing stored)
+ *   h   = x' (BL_NORM_NONE), or bitlinear_rmsnorm / bitlinear_layernorm's h of x' (eps)
+ *   codes, scales = bitlinear_quantize_acts(h, bits, gran, q_eps)
+ *   Y[p] = bitlinear_forward(codes, scales, W_packed[p], gamma[p], bias[p], epi)
+ * Every result is bit-identical to those calls made one after another.
+ *
+ * X        device bf16 [M][K], read only
+ * delta    device bf16 [M][K], or NULL; a residual needs a norm (not BL_NORM_NONE)
+ * X_out    device bf16 [M][K], must not overlap X or delta; required with delta
+ * norm     BL_NORM_NONE, BL_NORM_RMS or BL_NORM_LAYER; eps > 0 (ignored for NONE)
+ * bits, gran, q_eps        as in bitlinear_quantize_acts
+ * W_packed, gamma, bias, parts, M, N, K, epi, Y, y_dtype
+ *          as in bitlinear_forward_multi (parts >= 1; one input, `parts` projections)
+ * workspace: >= bitlinear_workspace_size(BL_OP_NORM_FORWARD, M, N, K, bits, gran) bytes,
+ *          256-byte aligned.
+ * Launches: with a norm, the norm and the quantization run as in
+ * bitlinear_rmsnorm_quantize / _layernorm_quantize (into the workspace), then the
+ * forward of every part (one launch on the decode GEMV).  Without one, bf16 rows of at
+ * most 16 tokens with K <= 4096 and per-token scales take a single launch (the decode
+ * GEMV quantizes them in its prologue and needs none of the workspace).  The norm is not
+ * taken into the GEMV's prologue: every block of the GEMV would recompute the exact sum
+ * of squares of every row, which costs more than the norm's own launch.
+ * Errors: BL_EINVAL (null X, W_packed, gamma or Y; bad enum; eps or q_eps <= 0; delta
+ * without X_out or without a norm; X_out overlapping X or delta), BL_ESHAPE, BL_EALIGN,
+ * BL_EWORKSPACE, BL_EDEVICE.
+ */
+bl_status bitlinear_norm_forward(const void *X, const void *delta, void *X_out, bl_norm norm,
+                                 float eps, int bits, bl_gran gran, float q_eps,
+                                 const uint8_t *W_packed, const float *gamma, const float *bias,
+                                 int64_t parts, int64_t M, int64_t N, int64_t K, bl_epi epi,
+                                 void *Y, bl_dtype y_dtype, void *workspace,
+                                 size_t workspace_bytes, void *stream);
 
 /*
  * Backward pass under the quantizers' straight-through estimators (quantization-aware

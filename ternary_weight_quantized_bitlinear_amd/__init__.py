@@ -19,6 +19,7 @@ The functions mirror the C entry points:
 * :func:`rmsnorm_quantize`  -> ``bitlinear_rmsnorm_quantize`` (glue + next layer's quantizer)
 * :func:`layernorm`         -> ``bitlinear_layernorm`` (the same glue, non-affine layer norm)
 * :func:`layernorm_quantize` -> ``bitlinear_layernorm_quantize``
+* :func:`norm_forward`      -> ``bitlinear_norm_forward`` (residual + norm + quantize + projections)
 * :func:`backward`          -> ``bitlinear_backward`` (straight-through-estimator gradients)
 """
 from __future__ import annotations
@@ -38,7 +39,8 @@ BL_F32, BL_BF16, BL_I32 = 0, 1, 2
 BL_PER_TOKEN, BL_PER_TENSOR = 0, 1
 BL_EPI_NONE, BL_EPI_RELU2 = 0, 1
 (BL_OP_QUANTIZE_WEIGHTS, BL_OP_QUANTIZE_ACTS, BL_OP_FORWARD, BL_OP_FORWARD_FUSED,
- BL_OP_BACKWARD) = range(5)
+ BL_OP_BACKWARD, BL_OP_NORM_FORWARD) = range(6)
+BL_NORM_NONE, BL_NORM_RMS, BL_NORM_LAYER = range(3)
 
 
 class BitLinearError(RuntimeError):
@@ -77,6 +79,8 @@ def lib() -> ctypes.CDLL:
         L.bitlinear_rmsnorm_quantize.argtypes = [P, P, P, I64, I64, F, I, I, F, P, P, P, SZ, P]
         L.bitlinear_layernorm.argtypes = [P, P, P, I64, I64, F, P]
         L.bitlinear_layernorm_quantize.argtypes = [P, P, P, I64, I64, F, I, I, F, P, P, P, SZ, P]
+        L.bitlinear_norm_forward.argtypes = [P, P, P, I, F, I, I, F, P, P, P, I64, I64, I64, I64, I,
+                                             P, I, P, SZ, P]
         L.bitlinear_quantize_weights_rotated.argtypes = [P, I, I64, I64, F, P, P, P, SZ, P]
         L.bitlinear_quantize_acts_rotated.argtypes = [P, I, I64, I64, I, I, F, P, P, P, SZ, P]
         L.bitlinear_hadamard_block.argtypes = [I64]
@@ -94,7 +98,8 @@ def lib() -> ctypes.CDLL:
                   "bitlinear_forward_fused", "bitlinear_forward_fused_batched",
                   "bitlinear_forward_multi", "bitlinear_forward_fused_noalloc",
                   "bitlinear_rmsnorm", "bitlinear_rmsnorm_quantize", "bitlinear_layernorm",
-                  "bitlinear_layernorm_quantize", "bitlinear_quantize_weights_rotated", "bitlinear_quantize_acts_rotated",
+                  "bitlinear_layernorm_quantize", "bitlinear_norm_forward",
+                  "bitlinear_quantize_weights_rotated", "bitlinear_quantize_acts_rotated",
                   "bitlinear_backward"):
             getattr(L, n).restype = I
         _lib = L
@@ -514,6 +519,46 @@ def layernorm_quantize(X, delta=None, eps: float = 1e-5, bits: int = 8, gran="to
     """layernorm followed by quantize_acts of its output: returns (H, Xq, scale)."""
     return _norm_quantize(lib().bitlinear_layernorm_quantize, X, delta, eps, bits, gran, q_eps,
                           out, workspace, stream)
+
+
+_NORMS = {None: BL_NORM_NONE, "none": BL_NORM_NONE, "rms": BL_NORM_RMS, "layer": BL_NORM_LAYER}
+
+
+def norm_forward(X, packed, gamma, delta=None, x_out=None, norm="rms", eps: float = 1e-6,
+                 bits: int = 8, gran="token", q_eps: float = 1e-5, bias=None, epilogue=None,
+                 out_dtype=None, workspace=None, stream=None, out=None):
+    """Residual add, norm, absmax quantization and the projections in one call: X [M, K]
+    bf16 (read only), delta [M, K] bf16 or None, x_out [M, K] bf16 (receives X + delta;
+    required with delta), packed [N, K/4] or [P, N, K/4], gamma [1] or [P] -> Y [M, N] or
+    [P, M, N].  norm: "rms", "layer" or None."""
+    torch = _torch()
+    bits = _bits(bits)
+    if norm not in _NORMS:
+        _fail(BL_EINVAL, "norm must be 'rms', 'layer' or None, not %r" % (norm,))
+    M, K = _dims(X, "X", 2)
+    single = packed is not None and packed.dim() == 2
+    if single:
+        N, _ = _dims(packed, "packed", 2)
+        Pn = 1
+    else:
+        Pn, N, _ = _dims(packed, "packed", 3)
+    g = _gran_code(gran)
+    _arg(X, "X", None, (torch.bfloat16,))
+    _arg(delta, "delta", (M, K), (torch.bfloat16,), optional=True)
+    _arg(x_out, "x_out", (M, K), (torch.bfloat16,), optional=delta is None)
+    _arg(packed, "packed", (N, K // 4) if single else (Pn, N, K // 4), (torch.uint8,))
+    _arg(gamma, "gamma", (Pn,), (torch.float32,))
+    _arg(bias, "bias", (N,) if single else (Pn, N), (torch.float32,), optional=True)
+    yshape = (M, N) if single else (Pn, M, N)
+    _out_arg(out, yshape)
+    dev = _gpu(X=X, delta=delta, x_out=x_out, packed=packed, gamma=gamma, bias=bias, out=out)
+    out = _new_out(out, yshape, out_dtype, dev)
+    ws, wsb = _workspace(workspace_size(BL_OP_NORM_FORWARD, M, N, K, bits, g), dev, workspace)
+    _check(lib().bitlinear_norm_forward(
+        _ptr(X), _ptr(delta), _ptr(x_out), _NORMS[norm], eps, bits, g, q_eps, _ptr(packed),
+        _ptr(gamma), _ptr(bias), Pn, M, N, K, _epi_code(epilogue), _ptr(out), _dtype_code(out),
+        _ptr(ws), wsb, _stream(dev, stream)))
+    return out
 
 
 def backward(dY, Xq, act_scale, packed, gamma, bits: int = 8, gran="token", X=None, W=None,

@@ -90,6 +90,14 @@ constexpr int64_t kFusedPrologueMaxM = 4;
 
 bool fused_in_prologue(int64_t M, int64_t K) { return bl::gemv_supports(M, K) && M <= kFusedPrologueMaxM; }
 
+// bitlinear_norm_forward's unfused path: h (bf16), the codes, the scales and the
+// per-tensor absmax word, then the forward's own workspace, each 256-byte aligned
+size_t ws_norm_forward(int64_t M, int64_t N, int64_t K, int bits, bl_gran gran) {
+    return up256((size_t)(M * K * 2)) + up256((size_t)(bits == 8 ? M * K : M * K / 2)) +
+           up256((size_t)M * sizeof(float)) + up256(bl::ws_quantize_acts((int)gran)) +
+           up256(ws_forward(M, N, K, bits, gran));
+}
+
 size_t ws_fused(int64_t M, int64_t N, int64_t K, int bits, bl_gran gran) {
     if (fused_in_prologue(M, K)) return bl::ws_gemv((int)gran);
     // quantized activations (prepared for the large-tile GEMM), scales, the per-tensor
@@ -151,7 +159,7 @@ bl_status scratch_address(void **out, const char *fn) {
 
 extern "C" {
 
-int bitlinear_version(void) { return 10300; }  // 1.3.0: bitlinear_layernorm(_quantize)
+int bitlinear_version(void) { return 10400; }  // 1.4.0: bitlinear_norm_forward
 
 const char *bitlinear_status_string(bl_status s) {
     switch (s) {
@@ -181,6 +189,10 @@ size_t bitlinear_workspace_size(bl_op op, int64_t M, int64_t N, int64_t K, int b
     case BL_OP_BACKWARD:
         if (M > bl::kBwdMaxDim || N > bl::kBwdMaxDim || K > bl::kBwdMaxDim) return 0;
         return (bits == 8 || bits == 4) ? bl::ws_backward(M, N, K, (int)gran) : 0;
+    case BL_OP_NORM_FORWARD:
+        return (bits == 8 || bits == 4) ? ws_norm_forward(M, N, K, bits, gran) : 0;
+    default:
+        break;
     }
     return 0;
 }
@@ -396,6 +408,13 @@ bl_status bitlinear_forward_fused(const void *X, bl_dtype x_dtype, int bits, bl_
         const bl::FwdArgs a = make_args(X, x_dtype == BL_BF16, bits, nullptr, gran, eps, W_packed,
                                         gamma, bias, M, N, K, epi, Y, y_dtype);
         return device(bl::launch_gemv(a, true, workspace, s), fn);
+    }
+    if (x_dtype == BL_BF16 && gran == BL_PER_TOKEN && bl::gemv_rows_supports(M, K)) {
+        // up to 16 bf16 tokens: the GEMV quantizes them in its prologue, a wave per token
+        bl::FwdArgs a = make_args(X, 1, bits, nullptr, gran, eps, W_packed, gamma, bias, M, N, K,
+                                  epi, Y, y_dtype);
+        a.rows = 1;
+        return device(bl::launch_gemv(a, true, nullptr, s), fn);
     }
     uint8_t *base = static_cast<uint8_t *>(workspace);
     if (use_f6f4(M, N, K, bits)) {
@@ -621,7 +640,7 @@ bl_status norm_entry(const char *fn, bool centre, void *X, const void *delta, vo
                      int64_t K, float eps, void *stream) {
     CHECK(check_norm(fn, X, delta, H, M, K, eps));
     (void)hipGetLastError();
-    return device(bl::launch_norm(X, delta, H, M, K, eps, centre, (hipStream_t)stream), fn);
+    return device(bl::launch_norm(X, delta, X, H, M, K, eps, centre, (hipStream_t)stream), fn);
 }
 
 bl_status norm_quantize_entry(const char *fn, bool centre, void *X, const void *delta, void *H,
@@ -642,10 +661,10 @@ bl_status norm_quantize_entry(const char *fn, bool centre, void *X, const void *
     (void)hipGetLastError();
     hipStream_t s = (hipStream_t)stream;
     if (gran == BL_PER_TOKEN)
-        return device(bl::launch_norm_quantize(X, delta, H, M, K, eps, centre, bits, q_eps, Xq,
+        return device(bl::launch_norm_quantize(X, delta, X, H, M, K, eps, centre, bits, q_eps, Xq,
                                                act_scale, s), fn);
     // per-tensor scales need the absmax of all of h: norm, then the quantizer on h
-    hipError_t e = bl::launch_norm(X, delta, H, M, K, eps, centre, s);
+    hipError_t e = bl::launch_norm(X, delta, X, H, M, K, eps, centre, s);
     if (e != hipSuccess) return device(e, fn);
     return device(bl::launch_quantize_acts(H, 1, M, K, bits, (int)gran, q_eps, Xq, act_scale,
                                            workspace, s), fn);
@@ -679,6 +698,94 @@ bl_status bitlinear_layernorm_quantize(void *X, const void *delta, void *H, int6
                                        void *stream) {
     return norm_quantize_entry("bitlinear_layernorm_quantize", true, X, delta, H, M, K, eps, bits,
                                gran, q_eps, Xq, act_scale, workspace, workspace_bytes, stream);
+}
+
+bl_status bitlinear_norm_forward(const void *X, const void *delta, void *X_out, bl_norm norm,
+                                 float eps, int bits, bl_gran gran, float q_eps,
+                                 const uint8_t *W_packed, const float *gamma, const float *bias,
+                                 int64_t parts, int64_t M, int64_t N, int64_t K, bl_epi epi,
+                                 void *Y, bl_dtype y_dtype, void *workspace,
+                                 size_t workspace_bytes, void *stream) {
+    static const char fn[] = "bitlinear_norm_forward";
+    if (!X) return fail(BL_EINVAL, "%s: null pointer", fn);
+    if (norm != BL_NORM_NONE && norm != BL_NORM_RMS && norm != BL_NORM_LAYER)
+        return fail(BL_EINVAL, "%s: bad norm", fn);
+    if (delta && norm == BL_NORM_NONE)
+        return fail(BL_EINVAL, "%s: a residual add needs a norm", fn);
+    if (delta && !X_out) return fail(BL_EINVAL, "%s: delta needs X_out", fn);
+    if (parts < 1 || parts > 65535)
+        return fail(BL_ESHAPE, "%s: parts=%lld must be in [1, 65535]", fn, (long long)parts);
+    CHECK(check_forward_common(fn, bits, gran, W_packed, gamma, bias, M, N, K, epi, Y, y_dtype));
+    if (norm != BL_NORM_NONE) {
+        CHECK(check_eps(eps, fn));
+        if (M >= (1ll << 24))  // the norm kernels: one block per row
+            return fail(BL_ESHAPE, "%s: M=%lld too large for a norm (M < 2^24)", fn, (long long)M);
+    }
+    CHECK(check_eps(q_eps, fn));
+    if (!aligned(X, 16) || (delta && !aligned(delta, 16)) || (X_out && !aligned(X_out, 16)))
+        return fail(BL_EALIGN, "%s: X, delta and X_out need 16-byte alignment", fn);
+    if (X_out) {
+        const uintptr_t bytes = (uintptr_t)(M * K * 2);
+        auto overlap = [&](const void *a, const void *b) {
+            return (uintptr_t)a < (uintptr_t)b + bytes && (uintptr_t)b < (uintptr_t)a + bytes;
+        };
+        if (overlap(X_out, X) || (delta && overlap(X_out, delta)))
+            return fail(BL_EINVAL, "%s: X_out must not overlap X or delta", fn);
+    }
+    const int64_t wst = N * (K / 4);
+    const int64_t yst = M * N * (y_dtype == BL_I32 || y_dtype == BL_F32 ? 4 : 2);
+    if (parts > 1 && (wst % 16 != 0 || yst % 16 != 0))
+        return fail(BL_EALIGN, "%s: per-part strides (W %lld, Y %lld bytes) must be multiples of 16",
+                    fn, (long long)wst, (long long)yst);
+    if (parts * wst >= (1ll << 40) || parts * yst >= (1ll << 40))
+        return fail(BL_ESHAPE, "%s: parts too large for these sizes", fn);
+    hipStream_t s = (hipStream_t)stream;
+    (void)hipGetLastError();
+    if (norm == BL_NORM_NONE && gran == BL_PER_TOKEN && bl::gemv_rows_supports(M, K)) {
+        // one launch: the decode GEMV quantizes the rows in its prologue
+        bl::FwdArgs a = make_args(X, 1, bits, nullptr, gran, q_eps, W_packed, gamma, bias, M, N, K,
+                                  epi, Y, y_dtype);
+        a.rows = 1;
+        a.batch = parts;
+        a.x_shared = 1;
+        return device(bl::launch_gemv(a, true, nullptr, s), fn);
+    }
+    const size_t need = ws_norm_forward(M, N, K, bits, gran);
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
+        return fail(BL_EWORKSPACE, "%s: need %zu bytes of 256-byte aligned workspace", fn, need);
+    uint8_t *h = static_cast<uint8_t *>(workspace);
+    uint8_t *codes = h + up256((size_t)(M * K * 2));
+    float *scale = reinterpret_cast<float *>(codes + up256((size_t)(bits == 8 ? M * K : M * K / 2)));
+    uint8_t *aq_ws = reinterpret_cast<uint8_t *>(scale) + up256((size_t)M * sizeof(float));
+    uint8_t *fwd_ws = aq_ws + up256(bl::ws_quantize_acts((int)gran));
+    void *xo = delta ? X_out : nullptr;
+    hipError_t e = hipSuccess;
+    if (norm == BL_NORM_NONE)
+        e = bl::launch_quantize_acts(X, 1, M, K, bits, (int)gran, q_eps, codes, scale, aq_ws, s);
+    else if (gran == BL_PER_TOKEN)
+        e = bl::launch_norm_quantize(X, delta, xo, h, M, K, eps, norm == BL_NORM_LAYER, bits, q_eps,
+                                     codes, scale, s);
+    else {
+        e = bl::launch_norm(X, delta, xo, h, M, K, eps, norm == BL_NORM_LAYER, s);
+        if (e == hipSuccess)
+            e = bl::launch_quantize_acts(h, 1, M, K, bits, (int)gran, q_eps, codes, scale, aq_ws, s);
+    }
+    if (e != hipSuccess) return device(e, fn);
+    if (bl::gemv_supports(M, K)) {
+        bl::FwdArgs a = make_args(codes, 0, bits, scale, gran, 0.0f, W_packed, gamma, bias, M, N, K,
+                                  epi, Y, y_dtype);
+        a.batch = parts;
+        a.x_shared = 1;
+        return device(bl::launch_gemv(a, false, fwd_ws, s), fn);
+    }
+    for (int64_t b = 0; b < parts; ++b) {
+        const bl::FwdArgs a = make_args(codes, 0, bits, scale, gran, 0.0f, W_packed + b * wst,
+                                        gamma + b, bias ? bias + b * N : nullptr, M, N, K, epi,
+                                        static_cast<uint8_t *>(Y) + b * yst, y_dtype);
+        e = launch_forward(a, fwd_ws, s);
+        if (e != hipSuccess) return device(e, fn);
+    }
+    return ok();
 }
 
 }  // extern "C"

@@ -15,6 +15,11 @@
 //   kind 2  bf16 32x32x16: bf16 gradients of spread 0.01 times ternary codes (the
 //           backward GEMMs).
 // 8 waves per block (two per SIMD), one block per CU; each wave runs 8 accumulators.
+//
+// An HBM read-only loop: a grid-stride sweep of 16-byte non-temporal loads over a buffer
+// larger than the last-level cache, folded into one word per block.  Its rate is what
+// streaming reads reach on this chip -- the ceiling beside the published 8 TB/s for the
+// weight-streaming decode kernels, which read and barely write.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -154,9 +159,64 @@ __global__ void __launch_bounds__(kThreads) mfma_loop(int iters, uint32_t seed, 
     }
 }
 
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+
+template <bool kNT>
+__device__ __forceinline__ v4u load16(const v4u *p) {
+    if constexpr (kNT)
+        return __builtin_nontemporal_load(p);
+    else
+        return *p;
+}
+
+// 256 threads; each thread keeps kU loads in flight per step (non-temporal or plain)
+template <int kU, bool kNT>
+__global__ void __launch_bounds__(256) hbm_read(const v4u *__restrict__ src, int64_t n16,
+                                                uint32_t *sink) {
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    uint32_t acc = 0;
+    int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    for (; i + (kU - 1) * stride < n16; i += kU * stride) {
+        v4u v[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) v[u] = load16<kNT>(src + i + u * stride);
+#pragma unroll
+        for (int u = 0; u < kU; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    }
+    for (; i < n16; i += stride) {
+        const v4u v = load16<kNT>(src + i);
+        acc ^= v.x ^ v.y ^ v.z ^ v.w;
+    }
+    __shared__ uint32_t red[4];
+    for (int o = 32; o > 0; o >>= 1) acc ^= __shfl_xor(acc, o);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) sink[blockIdx.x] = red[0] ^ red[1] ^ red[2] ^ red[3];
+}
+
 }  // namespace
 
 extern "C" {
+
+// Enqueues one read-only sweep of `bytes` bytes (a multiple of 16, src 16-byte aligned)
+// with `blocks` 256-thread blocks on `stream`; sink holds `blocks` words.  mode: 0 = four
+// non-temporal loads in flight per thread, 1 = eight non-temporal, 2 = eight plain loads.
+// Returns the HIP status of the launch (hipErrorInvalidValue for bad arguments).
+int bl_calib_read(const void *src, int64_t bytes, int blocks, int mode, uint32_t *sink,
+                  void *stream) {
+    if (!src || !sink || bytes <= 0 || bytes % 16 != 0 || (uintptr_t)src % 16 != 0 ||
+        blocks <= 0 || mode < 0 || mode > 2)
+        return (int)hipErrorInvalidValue;
+    const v4u *p = static_cast<const v4u *>(src);
+    const dim3 grid((unsigned)blocks), block(256);
+    hipStream_t s = (hipStream_t)stream;
+    switch (mode) {
+    case 0: hipLaunchKernelGGL((hbm_read<4, true>), grid, block, 0, s, p, bytes / 16, sink); break;
+    case 1: hipLaunchKernelGGL((hbm_read<8, true>), grid, block, 0, s, p, bytes / 16, sink); break;
+    default: hipLaunchKernelGGL((hbm_read<8, false>), grid, block, 0, s, p, bytes / 16, sink); break;
+    }
+    return (int)hipGetLastError();
+}
 
 // Operations one launch performs: blocks x 8 waves x iters x 8 MFMAs x ops per MFMA.
 double bl_calib_ops(int kind, int blocks, int iters) {

@@ -255,7 +255,12 @@ struct FwdArgs {
     int64_t batch = 1;     // independent problems laid out back to back (GEMV path)
     int x_shared = 0;      // GEMV path: every problem reads the same xq and act_scale
     const int32_t *rowsum = nullptr;  // prepared activations: sum_k q[m][k] per token
+    // the GEMV's row prologue (raw bf16 X, per-token scales, M <= 16) when rows = 1
+    int rows = 0;
 };
+
+// whether the GEMV's row prologue takes M tokens of K (M <= 16, K <= 4096)
+bool gemv_rows_supports(int64_t M, int64_t K);
 
 hipError_t launch_zero_u32(uint32_t *p, int64_t n, hipStream_t s);
 hipError_t launch_quantize_weights(const void *w, int w_bf16, int64_t N, int64_t K, float eps,
@@ -279,12 +284,13 @@ hipError_t launch_quantize_weights_rotated(const void *w, int w_bf16, int64_t N,
                                            float eps, uint8_t *packed, float *gamma, void *ws,
                                            hipStream_t s);
 // residual add and normalization of bf16 rows (glue between BitLinear layers): the RMS
-// form, or (centre) the non-affine layer norm
-hipError_t launch_norm(void *x, const void *delta, void *h, int64_t M, int64_t K, float eps,
-                       bool centre, hipStream_t s);
+// form, or (centre) the non-affine layer norm.  x' = x (+ delta) goes to x_out when delta
+// is given or x_out is another buffer (x_out may be x; null only without delta).
+hipError_t launch_norm(const void *x, const void *delta, void *x_out, void *h, int64_t M,
+                       int64_t K, float eps, bool centre, hipStream_t s);
 // the same, fused with the per-token absmax quantization of h into codes and scales
-hipError_t launch_norm_quantize(void *x, const void *delta, void *h, int64_t M, int64_t K,
-                                float eps, bool centre, int bits, float q_eps, void *xq,
+hipError_t launch_norm_quantize(const void *x, const void *delta, void *x_out, void *h, int64_t M,
+                                int64_t K, float eps, bool centre, int bits, float q_eps, void *xq,
                                 float *scale, hipStream_t s);
 // more than 64 KB of dynamic LDS must be allowed once per device and kernel
 hipError_t allow_lds(const void *fn, size_t lds);

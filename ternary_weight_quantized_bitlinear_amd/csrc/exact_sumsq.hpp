@@ -157,17 +157,8 @@ __host__ __device__ inline void sq_big_add(uint32_t *big, u128 v, int shift) {
     }
 }
 
-// The slow path's total: the window sum acc of a row with largest biased exponent E, plus
-// bins[e'] * 2^(2e' - 268) for e' = 1..254, rounded once to fp64.  Needs E >= 42 (a
-// value lies below the window only then), so the window's unit 2^(2E' - 348) is a
-// non-negative power of two times 2^-266.  big: kSqLimbs words of working memory (LDS in
-// a kernel, so that no lane needs private scratch memory).
-__host__ __device__ inline double sq_round_with_bins(u128 acc, int E, const uint64_t *bins,
-                                                     uint32_t *big) {
-    for (int i = 0; i < kSqLimbs; ++i) big[i] = 0;
-    sq_big_add(big, acc, 2 * E - 82);
-    for (int e = 1; e < 255; ++e)
-        if (bins[e]) sq_big_add(big, (u128)bins[e], 2 * e - 2);
+// A kSqLimbs-word total in units of 2^-266 rounded once to fp64.
+__host__ __device__ inline double sq_big_round(const uint32_t *big) {
     int t = kSqLimbs - 1;
     while (t >= 0 && big[t] == 0) --t;
     if (t < 0) return 0.0;
@@ -181,6 +172,20 @@ __host__ __device__ inline double sq_round_with_bins(u128 acc, int E, const uint
     for (int i = 0; i < b0; ++i) sticky |= big[i] != 0;
     if (sticky) w |= 1;
     return sq_round(w, 32 * b0 - 266);
+}
+
+// The slow path's total: the window sum acc of a row with largest biased exponent E, plus
+// bins[e'] * 2^(2e' - 268) for e' = 1..254, rounded once to fp64.  Needs E >= 42 (a
+// value lies below the window only then), so the window's unit 2^(2E' - 348) is a
+// non-negative power of two times 2^-266.  big: kSqLimbs words of working memory (LDS in
+// a kernel, so that no lane needs private scratch memory).
+__host__ __device__ inline double sq_round_with_bins(u128 acc, int E, const uint64_t *bins,
+                                                     uint32_t *big) {
+    for (int i = 0; i < kSqLimbs; ++i) big[i] = 0;
+    sq_big_add(big, acc, 2 * E - 82);
+    for (int e = 1; e < 255; ++e)
+        if (bins[e]) sq_big_add(big, (u128)bins[e], 2 * e - 2);
+    return sq_big_round(big);
 }
 
 }  // namespace bl

@@ -49,7 +49,8 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 
 constexpr int kMaxM = 16;
 
-enum Mode { kInt8 = 0, kInt4 = 1, kRawBf16 = 2, kRawF32 = 3 };
+// kRowsBf16: raw bf16 rows quantized a wave per token row (M <= 16, per-token scales)
+enum Mode { kInt8 = 0, kInt4 = 1, kRawBf16 = 2, kRawF32 = 3, kRowsBf16 = 4 };
 
 struct GemvParams {
     const void *x;           // int8/int4 codes, or raw bf16/fp32 rows (fused)
@@ -198,14 +199,16 @@ __global__ void __launch_bounds__(kWaves * 64) gemv_kernel(GemvParams p) {
     // only after (any earlier use would make the compiler wait for them, and
     // vector-memory loads retire in order, which would hold back the weights).
     constexpr bool kRaw = kMode == kRawBf16 || kMode == kRawF32;
+    constexpr bool kRows = kMode == kRowsBf16;
     // 16-byte words per group: fp32 4, bf16 2, int8 1, int4 1 (half used)
     constexpr int kWpg = RawWords<kMode>::n;
-    const int row_bytes = kMode == kRawF32 ? 4 * K : kMode == kRawBf16 ? 2 * K
+    const int row_bytes = kMode == kRawF32 ? 4 * K : kMode == kRawBf16 || kRows ? 2 * K
                         : kMode == kInt8 ? K : K / 2;
     const int gbytes = row_bytes / ngroups;  // bytes per group: 64, 32, 16 or 8
     const uint8_t *xbase = static_cast<const uint8_t *>(p.x);
     constexpr bool kDma = kMode == kInt8;  // int8 codes: DMA into LDS, natural order
-    const int S = kDma ? K + 16 : K;       // LDS row stride
+    constexpr bool kNat = kDma || kRows;   // codes in LDS in natural order (else interleaved)
+    const int S = kNat ? K + 16 : K;       // LDS row stride
     uint4 xg0[kWpg], xg1[kWpg];
     // quantized codes: the (token, group) pairs t = tid + i kThreads of all M rows are
     // one index space; the first kPre of this thread's groups are loaded here, before
@@ -213,7 +216,26 @@ __global__ void __launch_bounds__(kWaves * 64) gemv_kernel(GemvParams p) {
     constexpr int kPre = 8;
     const int T = M * ngroups;
     uint4 xpre[kPre][kWpg];
-    if (kRaw) {
+    // row mode: wave w owns token rows w, w + kWaves, ...; lane l holds the 16-element
+    // groups l, l + 64, ... of each (kG of them: K <= 256 kWaves kMaxTilesPerWave, so
+    // 64 kG groups cover the row), raw bf16 words loaded here, before the weights
+    constexpr int kRW = kRows ? (kMaxM + kWaves - 1) / kWaves : 1;
+    constexpr int kG = kRows ? kWaves * kMaxTilesPerWave / 4 : 1;
+    uint4 rx[kRW][kG][2];
+    if (kRows) {
+#pragma unroll
+        for (int r = 0; r < kRW; ++r) {
+            const int m = min(wave + r * kWaves, M - 1);  // rows past M: loaded, never used
+#pragma unroll
+            for (int j = 0; j < kG; ++j) {
+                const size_t off = (size_t)m * 2 * K + (size_t)min(lane + 64 * j, ngroups - 1) * 32;
+                const uint4 *src = reinterpret_cast<const uint4 *>(xbase + off);
+                rx[r][j][0] = src[0];
+                rx[r][j][1] = src[1];
+            }
+        }
+    } else if (kRaw) {
+
         load_group<kMode>(xbase, row_bytes, gbytes, ngroups, 0, tid, xg0);
         load_group<kMode>(xbase, row_bytes, gbytes, ngroups, 0, tid + kThreads, xg1);
     } else if (kDma) {
@@ -307,6 +329,57 @@ __global__ void __launch_bounds__(kWaves * 64) gemv_kernel(GemvParams p) {
                 quantize_store<kMode, kBits>(r, sc, xrow_m, g);
             }
         }
+    } else if (kRows) {
+        // the per-token absmax quantization of each row, exactly as the activation
+        // quantizer does it (one wave per row: the absmax is one wave reduction); codes
+        // into LDS in natural order
+#pragma unroll
+        for (int r = 0; r < kRW; ++r) {
+            const int m = wave + r * kWaves;
+            if (m < M) {  // uniform per wave
+                uint32_t v[kG][8];
+#pragma unroll
+                for (int j = 0; j < kG; ++j) {
+                    const int g = lane + 64 * j;
+                    const uint32_t w[8] = {rx[r][j][0].x, rx[r][j][0].y, rx[r][j][0].z, rx[r][j][0].w,
+                                           rx[r][j][1].x, rx[r][j][1].y, rx[r][j][1].z, rx[r][j][1].w};
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) v[j][i] = g < ngroups ? w[i] : 0u;
+                }
+                float mx = 0.0f;
+#pragma unroll
+                for (int j = 0; j < kG; ++j)
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        mx = fmaxf(mx, fmaxf(fabsf(bf16_lo(v[j][i])), fabsf(bf16_hi(v[j][i]))));
+                const float a = fmaxf(wave_max_abs(mx), p.eps);
+                const float sc = kBits == 8 ? 127.0f / a : a / 7.0f;
+                const float r4 = kBits == 8 ? 0.0f : q4_recip(sc);
+                if (lane == 0) s_f[m] = kBits == 8 ? gamma / sc : sc * gamma;
+#pragma unroll
+                for (int j = 0; j < kG; ++j) {
+                    const int g = lane + 64 * j;
+                    if (g < ngroups) {
+                        uint32_t nat[4];
+#pragma unroll
+                        for (int d = 0; d < 4; ++d) {
+                            uint32_t o = 0;
+#pragma unroll
+                            for (int b = 0; b < 4; ++b) {
+                                const uint32_t word = v[j][2 * d + b / 2];
+                                const float h = (b & 1) ? bf16_hi(word) : bf16_lo(word);
+                                const uint32_t c = kBits == 8 ? q8(h, sc)
+                                                   : ((uint32_t)(((int)(q4(h, sc, r4) << 28)) >> 28) & 0xFFu);
+                                o |= c << (8 * b);
+                            }
+                            nat[d] = o;
+                        }
+                        *reinterpret_cast<uint4 *>(xl + (size_t)m * S + 16 * g) =
+                            make_uint4(nat[0], nat[1], nat[2], nat[3]);
+                    }
+                }
+            }
+        }
     } else if (kDma) {
         if (tid < M) {
             const float sc = p.act_scale[p.gran == 1 ? 0 : tid];
@@ -359,7 +432,7 @@ __global__ void __launch_bounds__(kWaves * 64) gemv_kernel(GemvParams p) {
             for (int j = 0; j < 4; ++j) {
                 const uint4 q = *reinterpret_cast<const uint4 *>(xrow + kb + 16 * j);
                 uint32_t il[4] = {q.x, q.y, q.z, q.w};
-                if (kDma) {  // natural order -> k-interleaved
+                if (kNat) {  // natural order -> k-interleaved
                     const uint32_t nat[4] = {q.x, q.y, q.z, q.w};
                     interleave16(nat, il);
                 }
@@ -895,8 +968,26 @@ __global__ void __launch_bounds__(64 * kStreamWaves) gemv_stream_kernel(GemvPara
 constexpr int64_t kGemvMaxLds = 144 * 1024;
 constexpr int64_t kStreamLds = 63 * 1024;         // dynamic LDS (static use is < 1 KB)
 
-// the int8 codes [M][K] (int8 codes mode: rows padded by 16 bytes)
-size_t lds_bytes(int64_t M, int64_t K, int mode) { return (size_t)(M * (mode == kInt8 ? K + 16 : K)); }
+// the int8 codes [M][K] (codes in natural order: rows padded by 16 bytes)
+size_t lds_bytes(int64_t M, int64_t K, int mode) {
+    const bool nat = mode == kInt8 || mode == kRowsBf16;
+    return (size_t)(M * (nat ? K + 16 : K));
+}
+
+// the row prologue: 16 waves, one token row each (kMaxM), one k tile per wave (K <= 4096)
+constexpr int kRowWaves = 16;
+hipError_t launch_rows(const GemvParams &p, int64_t batch, hipStream_t s) {
+    const dim3 grid((unsigned)((p.N + 15) / 16), (unsigned)batch), block(kRowWaves * 64);
+    const size_t lds = lds_bytes(p.M, p.K, kRowsBf16);
+    void (*k)(GemvParams) =
+        p.bits == 8 ? gemv_kernel<kRowsBf16, 8, kRowWaves, 1> : gemv_kernel<kRowsBf16, 4, kRowWaves, 1>;
+    if (lds > 48 * 1024) {
+        const hipError_t e = allow_lds((const void *)k, lds);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(k, grid, block, lds, s, p);
+    return hipGetLastError();
+}
 
 template <int kWaves, int kT>
 hipError_t launch_cfg(const GemvParams &p, int mode, int64_t batch, hipStream_t s) {
@@ -973,6 +1064,12 @@ bool gemv_supports(int64_t M, int64_t K) {
     return M >= 1 && M <= kMaxM && K % 64 == 0 && M * K <= kGemvMaxLds;
 }
 
+// (K <= 4096: one k tile per wave; a lane's 4 groups of the row fit the 128 registers of
+// a 16-wave block without spilling, a whole 8192-wide row does not)
+bool gemv_rows_supports(int64_t M, int64_t K) {
+    return M >= 1 && M <= kMaxM && K % 64 == 0 && K <= 4096;
+}
+
 size_t ws_gemv(int) { return 0; }
 
 hipError_t launch_gemv(const FwdArgs &a, bool fused, void *, hipStream_t s) {
@@ -996,6 +1093,10 @@ hipError_t launch_gemv(const FwdArgs &a, bool fused, void *, hipStream_t s) {
     p.s_bstride = a.x_shared ? 0 : (a.gran == 1 ? 1 : a.M);
     p.w_bstride = a.N * (a.K / 4);
     p.y_bstride = a.M * a.N * (a.y_dtype == 1 ? 2 : 4);
+    if (a.rows) {  // raw bf16 rows, a wave per token row (the caller checked the shape)
+        p.x_bstride = a.x_shared ? 0 : a.M * 2 * a.K;
+        return launch_rows(p, a.batch, s);
+    }
     const int mode = fused ? (a.x_raw_bf16 ? kRawBf16 : kRawF32) : (a.bits == 8 ? kInt8 : kInt4);
     // at least four 16-row tiles per streaming wave: the streaming kernel, each block a
     // contiguous run of one problem's row groups

@@ -19,6 +19,7 @@
 // them.
 #include "common.hpp"
 #include "exact_moments.hpp"
+#include "wave_exact.hpp"
 
 namespace bl {
 namespace {
@@ -63,28 +64,6 @@ struct RowNorm {
     double mu, r;
 };
 
-__device__ __forceinline__ int wave_max_int(int v) {
-    v = max(v, dpp_mov<kDppQuadXor1>(0, v));
-    v = max(v, dpp_mov<kDppQuadXor2>(0, v));
-    v = max(v, dpp_mov<kDppHalfMirror>(0, v));
-    v = max(v, dpp_mov<kDppMirror>(0, v));
-    v = max(v, dpp_mov<kDppBcast15, 0xA>(0, v));
-    v = max(v, dpp_mov<kDppBcast31, 0xC>(0, v));
-    return __builtin_amdgcn_readlane(v, 63);
-}
-
-// The sum over the wave of each lane's 128-bit integer, exact: six 24-bit digits, each
-// summed with DPP lane moves (64 digits stay below 2^30), then recombined with carries.
-__device__ __forceinline__ u128 wave_sum_u128(u128 v) {
-    u128 total = 0;
-#pragma unroll
-    for (int d = 0; d < 6; ++d) {
-        const int digit = (int)((uint32_t)(v >> (24 * d)) & 0xFFFFFFu);
-        total += (u128)(uint32_t)wave_sum(digit) << (24 * d);
-    }
-    return total;
-}
-
 template <int kN>
 __device__ __forceinline__ void keep_put(uint4 (&keep)[kN], int64_t i, uint4 q) {
 #pragma unroll
@@ -100,14 +79,16 @@ __device__ __forceinline__ uint4 keep_get(const uint4 (&keep)[kN], int64_t i) {
     return q;
 }
 
-// The first sweep of pass 1: x' = bf16(fl32(x + delta)) (written back when delta is
+// The first sweep of pass 1: x' = bf16(fl32(x + delta)) from row xi, written to row xo
+// when delta is given or xo is another buffer (xo may be xi, or null when delta is not
 // given), this thread's first kNormRegGroups groups of x' kept in `keep`.  Returns the
 // largest biased exponent among this thread's values.
-__device__ __forceinline__ int row_residual(uint16_t *xr, const uint16_t *dr, int64_t n8,
-                                            uint4 (&keep)[kNormRegGroups]) {
+__device__ __forceinline__ int row_residual(const uint16_t *xi, uint16_t *xo, const uint16_t *dr,
+                                            int64_t n8, uint4 (&keep)[kNormRegGroups]) {
+    const bool write = xo && (dr || xo != xi);
     int emax = 0;
     for (int64_t u = threadIdx.x, i = 0; u < n8; u += kNormThreads, ++i) {
-        uint4 q = reinterpret_cast<const uint4 *>(xr)[u];
+        uint4 q = reinterpret_cast<const uint4 *>(xi)[u];
         uint32_t w[4] = {q.x, q.y, q.z, q.w};
         if (dr) {
             const uint4 dq = reinterpret_cast<const uint4 *>(dr)[u];
@@ -119,8 +100,8 @@ __device__ __forceinline__ int row_residual(uint16_t *xr, const uint16_t *dr, in
                 w[j] = (lo & 0xFFFFu) | (hi << 16);
             }
             q = make_uint4(w[0], w[1], w[2], w[3]);
-            reinterpret_cast<uint4 *>(xr)[u] = q;
         }
+        if (write) reinterpret_cast<uint4 *>(xo)[u] = q;
 #pragma unroll
         for (int j = 0; j < 4; ++j) emax = max(emax, max(sq_exp(w[j]), sq_exp(w[j] >> 16)));
         if (i < kNormRegGroups) keep_put(keep, i, q);
@@ -302,18 +283,20 @@ __device__ __forceinline__ float norm_value(float v, const RowNorm &s) {
 
 template <bool kCentre>
 __global__ void __launch_bounds__(kNormThreads)
-norm_rows(uint16_t *__restrict__ x, const uint16_t *__restrict__ delta,
+norm_rows(const uint16_t *xin, const uint16_t *__restrict__ delta, uint16_t *xout,
           uint16_t *__restrict__ h, int64_t K, float eps) {
     __shared__ typename NormStorage<kCentre>::type sh;
     const int64_t m = blockIdx.x;
     const int64_t n8 = K / 8;
-    uint16_t *xr = x + m * K;
+    const uint16_t *xi = xin + m * K;
+    uint16_t *xo = xout ? xout + m * K : nullptr;
+    const uint16_t *xr = xo ? xo : xi;  // x' (re-read for the groups past the registers)
     const uint16_t *dr = delta ? delta + m * K : nullptr;
     uint16_t *hr = h + m * K;
     uint4 keep[kNormRegGroups];
 #pragma unroll
     for (int i = 0; i < kNormRegGroups; ++i) keep[i] = make_uint4(0u, 0u, 0u, 0u);
-    const int emax = row_residual(xr, dr, n8, keep);
+    const int emax = row_residual(xi, xo, dr, n8, keep);
     const RowNorm s = row_stats(xr, n8, emax, eps, keep, sh);
     // pass 2: normalize (groups beyond the register-held ones are re-read)
     for (int64_t u = threadIdx.x, i = 0; u < n8; u += kNormThreads, ++i) {
@@ -338,14 +321,16 @@ norm_rows(uint16_t *__restrict__ x, const uint16_t *__restrict__ delta,
 // activation quantizer would from h.
 template <bool kCentre, int kBits>
 __global__ void __launch_bounds__(kNormThreads)
-norm_quant_rows(uint16_t *__restrict__ x, const uint16_t *__restrict__ delta,
+norm_quant_rows(const uint16_t *xin, const uint16_t *__restrict__ delta, uint16_t *xout,
                 uint16_t *__restrict__ h, int64_t K, float eps, float q_eps,
                 uint8_t *__restrict__ xq, float *__restrict__ scale) {
     __shared__ typename NormStorage<kCentre>::type sh;
     __shared__ float redf[kNormWaves];
     const int64_t m = blockIdx.x;
     const int64_t n8 = K / 8;
-    uint16_t *xr = x + m * K;
+    const uint16_t *xi = xin + m * K;
+    uint16_t *xo = xout ? xout + m * K : nullptr;
+    const uint16_t *xr = xo ? xo : xi;  // x' (re-read for the groups past the registers)
     const uint16_t *dr = delta ? delta + m * K : nullptr;
     uint16_t *hr = h + m * K;
     uint4 keep[kNormRegGroups];
@@ -353,7 +338,7 @@ norm_quant_rows(uint16_t *__restrict__ x, const uint16_t *__restrict__ delta,
     for (int i = 0; i < kNormRegGroups; ++i) keep[i] = make_uint4(0u, 0u, 0u, 0u);
     auto put = [&](int64_t i, uint4 q) __attribute__((always_inline)) { keep_put(keep, i, q); };
     auto get = [&](int64_t i) __attribute__((always_inline)) { return keep_get(keep, i); };
-    const int emax = row_residual(xr, dr, n8, keep);
+    const int emax = row_residual(xi, xo, dr, n8, keep);
     const RowNorm s = row_stats(xr, n8, emax, eps, keep, sh);
     // pass 2: h (kept in registers for pass 3), max |h|
     float mx = 0.0f;
@@ -408,33 +393,33 @@ norm_quant_rows(uint16_t *__restrict__ x, const uint16_t *__restrict__ delta,
 
 }  // namespace
 
-hipError_t launch_norm_quantize(void *x, const void *delta, void *h, int64_t M, int64_t K,
-                                float eps, bool centre, int bits, float q_eps, void *xq,
+hipError_t launch_norm_quantize(const void *x, const void *delta, void *x_out, void *h, int64_t M,
+                                int64_t K, float eps, bool centre, int bits, float q_eps, void *xq,
                                 float *scale, hipStream_t s) {
-    uint16_t *xp = static_cast<uint16_t *>(x), *hp = static_cast<uint16_t *>(h);
-    const uint16_t *dp = static_cast<const uint16_t *>(delta);
+    const uint16_t *xp = static_cast<const uint16_t *>(x), *dp = static_cast<const uint16_t *>(delta);
+    uint16_t *op = static_cast<uint16_t *>(x_out), *hp = static_cast<uint16_t *>(h);
     uint8_t *qp = static_cast<uint8_t *>(xq);
     const dim3 grid((unsigned)M), block(kNormThreads);
     if (centre && bits == 8)
-        hipLaunchKernelGGL((norm_quant_rows<true, 8>), grid, block, 0, s, xp, dp, hp, K, eps, q_eps, qp, scale);
+        hipLaunchKernelGGL((norm_quant_rows<true, 8>), grid, block, 0, s, xp, dp, op, hp, K, eps, q_eps, qp, scale);
     else if (centre)
-        hipLaunchKernelGGL((norm_quant_rows<true, 4>), grid, block, 0, s, xp, dp, hp, K, eps, q_eps, qp, scale);
+        hipLaunchKernelGGL((norm_quant_rows<true, 4>), grid, block, 0, s, xp, dp, op, hp, K, eps, q_eps, qp, scale);
     else if (bits == 8)
-        hipLaunchKernelGGL((norm_quant_rows<false, 8>), grid, block, 0, s, xp, dp, hp, K, eps, q_eps, qp, scale);
+        hipLaunchKernelGGL((norm_quant_rows<false, 8>), grid, block, 0, s, xp, dp, op, hp, K, eps, q_eps, qp, scale);
     else
-        hipLaunchKernelGGL((norm_quant_rows<false, 4>), grid, block, 0, s, xp, dp, hp, K, eps, q_eps, qp, scale);
+        hipLaunchKernelGGL((norm_quant_rows<false, 4>), grid, block, 0, s, xp, dp, op, hp, K, eps, q_eps, qp, scale);
     return hipGetLastError();
 }
 
-hipError_t launch_norm(void *x, const void *delta, void *h, int64_t M, int64_t K, float eps,
-                       bool centre, hipStream_t s) {
-    uint16_t *xp = static_cast<uint16_t *>(x), *hp = static_cast<uint16_t *>(h);
-    const uint16_t *dp = static_cast<const uint16_t *>(delta);
+hipError_t launch_norm(const void *x, const void *delta, void *x_out, void *h, int64_t M, int64_t K,
+                       float eps, bool centre, hipStream_t s) {
+    const uint16_t *xp = static_cast<const uint16_t *>(x), *dp = static_cast<const uint16_t *>(delta);
+    uint16_t *op = static_cast<uint16_t *>(x_out), *hp = static_cast<uint16_t *>(h);
     const dim3 grid((unsigned)M), block(kNormThreads);
     if (centre)
-        hipLaunchKernelGGL(norm_rows<true>, grid, block, 0, s, xp, dp, hp, K, eps);
+        hipLaunchKernelGGL(norm_rows<true>, grid, block, 0, s, xp, dp, op, hp, K, eps);
     else
-        hipLaunchKernelGGL(norm_rows<false>, grid, block, 0, s, xp, dp, hp, K, eps);
+        hipLaunchKernelGGL(norm_rows<false>, grid, block, 0, s, xp, dp, op, hp, K, eps);
     return hipGetLastError();
 }
 

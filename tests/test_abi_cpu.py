@@ -25,7 +25,7 @@ def test_exports_every_header_function(L):
         "bitlinear_quantize_weights", "bitlinear_quantize_acts", "bitlinear_forward",
         "bitlinear_forward_fused", "bitlinear_forward_fused_batched", "bitlinear_forward_multi",
         "bitlinear_rmsnorm", "bitlinear_rmsnorm_quantize", "bitlinear_layernorm",
-        "bitlinear_layernorm_quantize", "bitlinear_workspace_size", "bitlinear_status_string",
+        "bitlinear_layernorm_quantize", "bitlinear_norm_forward", "bitlinear_workspace_size", "bitlinear_status_string",
         "bitlinear_last_error", "bitlinear_version", "bitlinear_hadamard_block",
         "bitlinear_quantize_weights_rotated", "bitlinear_quantize_acts_rotated",
         "bitlinear_backward", "bitlinear_forward_fused_noalloc",
@@ -47,7 +47,7 @@ def test_library_is_gfx950_code():
 def test_status_strings_and_version(L):
     for s in range(7):
         assert L.bitlinear_status_string(s).decode()
-    assert L.bitlinear_version() >= 10300  # 1.3: bitlinear_layernorm(_quantize)
+    assert L.bitlinear_version() >= 10400  # 1.4: bitlinear_norm_forward
 
 
 def test_workspace_sizes(L):
@@ -356,3 +356,51 @@ def test_binding_raises_loudly_without_library(monkeypatch):
     monkeypatch.setattr(bl, "LIB_PATH", "/nonexistent/libbitlinear.so")
     with pytest.raises(bl.BitLinearError):
         bl.lib()
+
+
+def test_calibration_library_exports(L):
+    # the benchmark's ceiling legs load these from their own library
+    path = os.path.join(os.path.dirname(bl.LIB_PATH), "libbitlinear_calib.so")
+    if not os.path.exists(path):
+        pytest.skip("calibration library not built")
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    assert {"bl_calib_mfma", "bl_calib_ops", "bl_calib_read"} <= exported
+
+
+def test_norm_forward_rejects(L):
+    f = L.bitlinear_norm_forward
+    X, D, XO, W, G, Y = (P(A), P(A + (1 << 20)), P(A + (2 << 20)), P(A + (3 << 20)),
+                         P(A + (4 << 20)), P(A + (5 << 20)))
+
+    def call(**kw):
+        a = dict(X=X, d=D, xo=XO, norm=1, eps=1e-6, bits=8, gran=0, qe=1e-5, W=W, g=G, b=None,
+                 parts=1, M=16, N=2560, K=2560, epi=0, Y=Y, ydt=1, ws=None, wsb=0)
+        a.update(kw)
+        return f(a["X"], a["d"], a["xo"], a["norm"], a["eps"], a["bits"], a["gran"], a["qe"],
+                 a["W"], a["g"], a["b"], a["parts"], a["M"], a["N"], a["K"], a["epi"], a["Y"],
+                 a["ydt"], a["ws"], a["wsb"], None)
+
+    assert call(X=None) == bl.BL_EINVAL
+    assert call(norm=3) == bl.BL_EINVAL
+    assert call(norm=0) == bl.BL_EINVAL            # a residual add needs a norm
+    assert call(xo=None) == bl.BL_EINVAL           # delta needs X_out
+    assert call(eps=0.0) == bl.BL_EINVAL
+    assert call(qe=-1.0) == bl.BL_EINVAL
+    assert call(parts=0) == bl.BL_ESHAPE
+    assert call(K=2568) == bl.BL_ESHAPE            # not a multiple of 16
+    assert call(bits=2) == bl.BL_EINVAL
+    assert call(xo=P(A + 64)) == bl.BL_EINVAL      # X_out overlaps X
+    assert call(xo=P(A + (1 << 20) + 64)) == bl.BL_EINVAL  # X_out overlaps delta
+    assert call(X=P(A + 8)) == bl.BL_EALIGN
+    assert call(d=P(A + (1 << 20) + 4)) == bl.BL_EALIGN
+    assert call(M=1 << 24, N=16, K=16) == bl.BL_ESHAPE    # the norm's row limit
+    # the unfused path (the layer norm, or K > 4096) needs its workspace
+    assert call(norm=2) == bl.BL_EWORKSPACE
+    assert call(K=6912) == bl.BL_EWORKSPACE
+    assert call(gran=1) == bl.BL_EWORKSPACE
+    assert L.bitlinear_last_error().decode().startswith("bitlinear_norm_forward")
+    # the workspace covers h, the codes, the scales and the forward's own
+    need = L.bitlinear_workspace_size(5, 16, 2560, 2560, 8, 0)
+    assert need >= 16 * 2560 * 3 + 16 * 4

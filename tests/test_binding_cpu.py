@@ -136,6 +136,19 @@ CASES = [
                                         t((M + 1,)))), bl.BL_ESHAPE, "act_scale"),
     ("layernorm_quantize: bits", lambda: bl.layernorm_quantize(t((M, K), torch.bfloat16), bits=2),
      bl.BL_EINVAL, "bits"),
+    ("norm_forward: delta without x_out", lambda: bl.norm_forward(
+        t((M, K), torch.bfloat16), t((N, K // 4), torch.uint8), t((1,)),
+        delta=t((M, K), torch.bfloat16)), bl.BL_EINVAL, "x_out"),
+    ("norm_forward: bad norm", lambda: bl.norm_forward(
+        t((M, K), torch.bfloat16), t((N, K // 4), torch.uint8), t((1,)), norm="l2"),
+     bl.BL_EINVAL, "norm"),
+    ("norm_forward: parts gamma", lambda: bl.norm_forward(
+        t((M, K), torch.bfloat16), t((3, N, K // 4), torch.uint8), t((1,))), bl.BL_ESHAPE, "gamma"),
+    ("norm_forward: x_out shape", lambda: bl.norm_forward(
+        t((M, K), torch.bfloat16), t((N, K // 4), torch.uint8), t((1,)),
+        delta=t((M, K), torch.bfloat16), x_out=t((M, K + 16), torch.bfloat16)), bl.BL_ESHAPE, "x_out"),
+    ("norm_forward: host tensors", lambda: bl.norm_forward(
+        t((M, K), torch.bfloat16), t((N, K // 4), torch.uint8), t((1,))), bl.BL_EINVAL, "GPU"),
     # backward
     ("backward: fp32 dY", lambda: bl.backward(t((M, N)), t((M, K), torch.int8), t((M,)),
                                               t((N, K // 4), torch.uint8), t((1,))),

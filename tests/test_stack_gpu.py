@@ -110,6 +110,23 @@ def _oracle_layer(x, delta, w):
     return r
 
 
+def _layer_weights(layer):
+    """One block's packed weights on the GPU and in the oracle (checked equal)."""
+    codes = workloads.stack_layer_codes(3, layer)
+    w = {}
+    for name, c in codes.items():
+        W = c.astype(np.float32)
+        packed, gamma = bl.quantize_weights(to_dev(W))
+        p_ref, g_ref, _ = oracle.quantize_weights(W)
+        w[name] = ((packed, gamma), p_ref, g_ref)
+    torch.cuda.synchronize()
+    for name, ((packed, gamma), p_ref, g_ref) in w.items():
+        assert_same_bytes(to_host(packed), p_ref, "layer %d %s packed" % (layer, name))
+        assert_same_bytes(bits32(to_host(gamma)), bits32(np.float32(g_ref).reshape(1)),
+                          "layer %d %s gamma" % (layer, name))
+    return w
+
+
 @pytest.mark.timeout(1200)
 def test_stack_30_layers_parity():
     """The 2B stack at batch 16, all 30 layers, in the calls the benchmark makes: RMS norm
@@ -128,18 +145,7 @@ def test_stack_30_layers_parity():
     compared = 0
     for layer in range(workloads.LAYERS_2B):
         say("stack layer", layer)
-        codes = workloads.stack_layer_codes(3, layer)
-        w = {}
-        for name, c in codes.items():
-            W = c.astype(np.float32)
-            packed, gamma = bl.quantize_weights(to_dev(W))
-            p_ref, g_ref, _ = oracle.quantize_weights(W)
-            w[name] = ((packed, gamma), p_ref, g_ref)
-        torch.cuda.synchronize()
-        for name, ((packed, gamma), p_ref, g_ref) in w.items():
-            assert_same_bytes(to_host(packed), p_ref, "layer %d %s packed" % (layer, name))
-            assert_same_bytes(bits32(to_host(gamma)), bits32(np.float32(g_ref).reshape(1)),
-                              "layer %d %s gamma" % (layer, name))
+        w = _layer_weights(layer)
         ref = _oracle_layer(x_ref, d_ref, w)
         (pq, gq), _, _ = w["qkv"]
         h, hq, hs = bl.rmsnorm_quantize(xd, delta)
@@ -172,3 +178,53 @@ def test_stack_30_layers_parity():
     assert_same_bytes(to_host(xf_gpu), xf, "final residual stream")
     assert np.isfinite(workloads.bf16_bits_to_f32(xf)).all()
     say("stack: %d values compared over %d layers, 0 differ" % (compared, workloads.LAYERS_2B))
+
+
+@pytest.mark.timeout(1200)
+def test_stack_30_layers_fused_parity():
+    """The same 30-layer stack in the benchmark's fused calls: residual add + RMS norm +
+    quantization + Q, K, V in one call (bitlinear_norm_forward, three parts), O quantizing
+    its own input, residual add + RMS norm + quantization + up (+ReLU^2) in one call,
+    down quantizing its own input; the residual stream alternates between two buffers.
+    Every value these calls write -- the stream after each add, Q, K, V, O, up, down --
+    is compared with the oracle's chain from the same x0 and weights, bit for bit, and
+    the final stream after the last residual add."""
+    H = workloads.HIDDEN
+    x = workloads.stack_input(seed=3, m=16)
+    x0 = to_dev(x)
+    bufs = (torch.empty_like(x0), torch.empty_like(x0))
+    cur, delta = x0, None
+    x_ref, d_ref = x.copy(), None
+    compared = 0
+    for layer in range(workloads.LAYERS_2B):
+        say("fused stack layer", layer)
+        w = _layer_weights(layer)
+        ref = _oracle_layer(x_ref, d_ref, w)
+        (pq, gq), _, _ = w["qkv"]
+        nxt = bufs[0] if cur is not bufs[0] else bufs[1]
+        qkv = bl.norm_forward(cur, pq.view(3, H, pq.shape[1]), gq.expand(3).contiguous(),
+                              delta=delta, x_out=nxt if delta is not None else None,
+                              out_dtype=torch.bfloat16)
+        cur = nxt if delta is not None else cur
+        x1 = to_host(cur)
+        (po, go), _, _ = w["o"]
+        o = bl.forward_fused(qkv[2], po, go, out_dtype=torch.bfloat16)
+        (pu, gu), _, _ = w["up"]
+        nxt = bufs[0] if cur is not bufs[0] else bufs[1]
+        u = bl.norm_forward(cur, pu, gu, delta=o, x_out=nxt, epilogue="relu2",
+                            out_dtype=torch.bfloat16)
+        cur = nxt
+        (pd, gd), _, _ = w["down"]
+        delta = bl.forward_fused(u, pd, gd, out_dtype=torch.bfloat16)
+        torch.cuda.synchronize()
+        got = {"x1": x1, "Q": to_host(qkv[0]), "K": to_host(qkv[1]), "V": to_host(qkv[2]),
+               "O": to_host(o), "x2": to_host(cur), "up": to_host(u), "down": to_host(delta)}
+        for key, val in got.items():
+            assert_same_bytes(val, ref[key], "layer %d %s" % (layer, key))
+            compared += val.size
+        x_ref, d_ref = ref["x2"], ref["down"]
+    xf, _ = oracle.rmsnorm(x_ref, d_ref)
+    bl.rmsnorm(cur, delta)
+    torch.cuda.synchronize()
+    assert_same_bytes(to_host(cur), xf, "final residual stream")
+    say("fused stack: %d values compared over %d layers, 0 differ" % (compared, workloads.LAYERS_2B))

@@ -132,3 +132,4 @@ def test_many_equal_terms_carry(host_sumsq):
     row = np.full(1 << 20, 0x3FFF, np.uint16)  # 1.9921875
     v, slow = host_sumsq(row)
     assert not slow and v == float(2 ** 20 * Fraction(255, 128) ** 2)
+
