@@ -352,6 +352,12 @@ __global__ void __launch_bounds__(kWaves * 64) gemv_kernel(GemvParams p) {
 #pragma unroll
                     for (int i = 0; i < 8; ++i)
                         mx = fmaxf(mx, fmaxf(fabsf(bf16_lo(v[j][i])), fabsf(bf16_hi(v[j][i]))));
+                // the words as the codes loop sees them: the widened values of the max
+                // loop are not kept for it (a whole row of them would not fit)
+#pragma unroll
+                for (int j = 0; j < kG; ++j)
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) asm volatile("" : "+v"(v[j][i]));
                 const float a = fmaxf(wave_max_abs(mx), p.eps);
                 const float sc = kBits == 8 ? 127.0f / a : a / 7.0f;
                 const float r4 = kBits == 8 ? 0.0f : q4_recip(sc);
@@ -1064,8 +1070,10 @@ bool gemv_supports(int64_t M, int64_t K) {
     return M >= 1 && M <= kMaxM && K % 64 == 0 && M * K <= kGemvMaxLds;
 }
 
-// (K <= 4096: one k tile per wave; a lane's 4 groups of the row fit the 128 registers of
-// a 16-wave block without spilling, a whole 8192-wide row does not)
+// (K <= 4096, one k tile per wave.  Wider rows fit too -- two tiles per wave, 8 groups of
+// a row per lane -- but every block then quantizes 16 rows of up to 8192 values: at the
+// 6912-wide down projection of the 2B stack that measured slower than the separate
+// quantizer launch it saves)
 bool gemv_rows_supports(int64_t M, int64_t K) {
     return M >= 1 && M <= kMaxM && K % 64 == 0 && K <= 4096;
 }

@@ -67,6 +67,7 @@ CASES = [
     # without: one launch, the GEMV's row prologue quantizes
     (16, 2560, 2560, 1, None, False, 8, "token", False, "bf16", "gauss"),
     (12, 2048, 384, 2, None, False, 4, "token", True, "f32", "gauss"),
+    (16, 6912, 2560, 1, None, False, 8, "token", False, "bf16", "gauss"),
     # the layer norm, per-tensor scales, K > 4096 (the codes GEMV), M > 16 (the GEMM)
     (16, 2560, 2560, 3, "layer", True, 8, "token", False, "bf16", "gauss"),
     (16, 2560, 512, 1, "rms", True, 8, "tensor", False, "f32", "gauss"),
@@ -112,10 +113,12 @@ def test_norm_forward_parity(M, K, N, parts, norm, res, bits, gran, epi, ydt, ki
 
 @pytest.mark.parametrize("M,K,N,bits,epi", [(5, 2560, 6912, 8, True), (16, 2560, 2560, 8, False),
                                             (16, 4096, 1000, 4, False), (8, 64, 16, 8, True),
-                                            (13, 1024, 4096, 4, True)])
+                                            (13, 1024, 4096, 4, True), (16, 6912, 2560, 8, False),
+                                            (7, 8192, 272, 4, True), (16, 4160, 48, 8, False)])
 def test_forward_fused_row_prologue(M, K, N, bits, epi):
     """5..16 bf16 tokens, per-token scales: bitlinear_forward_fused quantizes in the GEMV's
-    prologue, a wave per token row; the codes must be the activation quantizer's."""
+    prologue, a wave per token row, up to K = 4096 (wider rows, also checked here, take
+    the quantizer's own launch); the codes must be the activation quantizer's."""
     rng = np.random.default_rng([62, M, K, N, bits])
     x = workloads.to_bf16_bits((3.0 * rng.standard_normal((M, K))).astype(np.float32))
     W = workloads.ternary_weights(rng, N, K)
