@@ -516,13 +516,12 @@ def _fwht_rows(x, b):
 def leg_stack(torch, bl, steps=10, layers=30, batch=16):
     """The 2B-shaped decode stack: 30 blocks of QKV 2560->7680, O 2560->2560, up
     2560->6912 (+ReLU^2), down 6912->2560, batch 16 tokens, seed-fixed weights.  Per
-    block: RMS norm + quantization + Q, K, V in one call (V feeds O) -> O, adding its
-    output to the residual stream and gathering the rows' exact statistics -> RMS norm
-    from those statistics + quantization + up -> down, adding to the stream likewise.
-    O and down quantize their bf16 inputs themselves.  One step = all 30 blocks for the
-    16 tokens, the K steps in one graph.  The same block as six separate calls per
-    layer (norm + quantization, then the projections) is timed beside it, and both must
-    end on the same residual stream, bit for bit."""
+    block: residual add + RMS norm + quantization + Q, K, V in one call (V feeds O)
+    -> O -> residual add + RMS norm + quantization + up in one call -> down; O and down
+    quantize their bf16 inputs themselves.  One step = all 30 blocks for the 16 tokens,
+    the K steps in one graph.  The same block as separate calls (norm + quantization,
+    then the projections) is timed beside it, and both must end on the same residual
+    stream, bit for bit."""
     import workloads
     dev = torch.device("cuda:0")
     H = workloads.HIDDEN
@@ -553,32 +552,32 @@ def leg_stack(torch, bl, steps=10, layers=30, batch=16):
     u = torch.empty((batch, workloads.FFN), dtype=torch.bfloat16, device=dev)
     d = torch.empty((batch, H), dtype=torch.bfloat16, device=dev)
 
-    R = torch.empty_like(x0)  # the residual stream
-    stats = (bl.new_norm_stats(batch, dev), bl.new_norm_stats(batch, dev))
+    bufs = (torch.empty_like(x0), torch.empty_like(x0))
     nf_ws = torch.empty(max(bl.workspace_size(bl.BL_OP_NORM_FORWARD, batch, n, H)
                             for n in (H, workloads.FFN)), dtype=torch.uint8, device=dev)
-    res_ws = torch.empty(max(bl.workspace_size(bl.BL_OP_FORWARD_RESIDUAL, batch, H, k)
-                             for k in (H, workloads.FFN)), dtype=torch.uint8, device=dev)
+    ff_ws = torch.empty(max(bl.workspace_size(bl.BL_OP_FORWARD_FUSED, batch, n, k)
+                            for n, k in ((H, H), (H, workloads.FFN))), dtype=torch.uint8, device=dev)
     final = {}
 
     def step():
-        # O and down add their outputs to the stream in their epilogues and gather the new
-        # rows' exact statistics; the next norm (fused into the QKV and up GEMVs) reads them
-        R.copy_(x0)
-        for i, lw in enumerate(W):
+        # each sub-layer's input side in one call: residual add (into the other stream
+        # buffer), RMS norm, quantization and the projections (Q, K, V in one call)
+        cur, delta = x0, None
+        for lw in W:
             pq3, gq3 = lw["qkv3"]
-            if i == 0:  # x0: no producer, the norm computes its own sums
-                bl.norm_forward(R, pq3, gq3, out=qkv, workspace=nf_ws)
-            else:
-                bl.rmsnorm_forward_stats(R, stats[0], pq3, gq3, out=qkv, workspace=nf_ws)
-            bl.forward_fused_residual(v, *lw["o"], R, stats=stats[1], clear=stats[0],
-                                      workspace=res_ws)
-            bl.rmsnorm_forward_stats(R, stats[1], *lw["up"], epilogue="relu2", out=u,
-                                     workspace=nf_ws)
-            last = i + 1 == len(W)
-            bl.forward_fused_residual(u, *lw["down"], R, stats=None if last else stats[0],
-                                      clear=stats[1], workspace=res_ws)
-        final["x"] = R
+            nxt = bufs[0] if cur is not bufs[0] else bufs[1]
+            bl.norm_forward(cur, pq3, gq3, delta=delta, x_out=nxt if delta is not None else None,
+                            out=qkv, workspace=nf_ws)
+            cur = nxt if delta is not None else cur
+            bl.forward_fused(v, *lw["o"], out=o, workspace=ff_ws)
+            nxt = bufs[0] if cur is not bufs[0] else bufs[1]
+            bl.norm_forward(cur, *lw["up"], delta=o, x_out=nxt, epilogue="relu2", out=u,
+                            workspace=nf_ws)
+            cur = nxt
+            bl.forward_fused(u, *lw["down"], out=d, workspace=ff_ws)
+            delta = d
+        bl.rmsnorm(cur, delta, out=h)  # the last residual
+        final["x"] = cur
 
     def step_unfused():
         # the same block as separate calls: norm + quantization, then the projections

@@ -87,7 +87,6 @@ typedef enum {
     BL_OP_FORWARD_FUSED = 3,
     BL_OP_BACKWARD = 4,
     BL_OP_NORM_FORWARD = 5,
-    BL_OP_FORWARD_RESIDUAL = 6,
     BL_ENUM_RANGE(BL_OP)
 } bl_op;
 
@@ -381,52 +380,6 @@ bl_status bitlinear_norm_forward(const void *X, const void *delta, void *X_out, 
                                  int64_t parts, int64_t M, int64_t N, int64_t K, bl_epi epi,
                                  void *Y, bl_dtype y_dtype, void *workspace,
                                  size_t workspace_bytes, void *stream);
-
-/*
- * The residual stream's exact row statistics, carried from the sub-layer that adds to
- * the stream to the norm of the next one, so that the norm needs no launch of its own
- * ("BitNet 2B4T Guide", "3. Sub-Layer Normalization (SubLN)" and its block listing:
- * out-projection, residual add, RMS norm, next BitLinear).  A statistics buffer holds, per
- * token, S = sum_k x'^2 exactly (carry-free 32-bit digits in 64-bit words, added with
- * integer atomics: the total does not depend on the order) and max_k |x'|.  It must be
- * zero when a producer starts filling it; its reader leaves it as it is.  In a stack of
- * blocks two buffers alternate, and the producer that fills one clears the other (its
- * reader has just run, its next producer runs later); allocate both zeroed.
- *
- * bitlinear_norm_stats_bytes(M): a buffer's size in bytes for M tokens.
- *
- * bitlinear_forward_fused_residual: Y = bf16(bitlinear_forward_fused(X, ...)) and
- *   R[m][n] = bf16(fl32(R[m][n] + Y[m][n]))   in place
- * adding the new R rows' statistics to `stats` (NULL: none) after zeroing `clear` (NULL:
- * none; not `stats`).  X, x_dtype, bits, gran, eps, W_packed, gamma, bias, M, N, K, epi as
- * in bitlinear_forward_fused; R device bf16 [M][N] (the residual stream, N its width, not
- * overlapping X or Y); Y device bf16 [M][N] or NULL (then not stored); stats, clear
- * 8-byte aligned.  M < 65536.  workspace: >= bitlinear_workspace_size(
- * BL_OP_FORWARD_RESIDUAL, M, N, K, bits, gran).  Up to 16 tokens the decode GEMV adds the
- * residual and the statistics in its epilogue (one launch, or two with the quantizer).
- *
- * bitlinear_rmsnorm_forward_stats: bitlinear_norm_forward(X, NULL, NULL, BL_NORM_RMS,
- *   eps, bits, BL_PER_TOKEN, q_eps, ...) with each row's sum of squares and max |x'|
- *   taken from `stats`, which must hold the statistics of exactly X's rows, as the last
- *   bitlinear_forward_fused_residual into X left them.  Results are bit-identical to
- *   bitlinear_norm_forward.  Up to 16 bf16 tokens of K <= 4096 this is one launch (the
- *   decode GEMV normalizes and quantizes in its prologue); otherwise the norm kernel
- *   (which computes the sums from X) and the forward.  workspace: >=
- *   bitlinear_workspace_size(BL_OP_NORM_FORWARD, M, N, K, bits, BL_PER_TOKEN).
- * Errors: BL_EINVAL (null pointers, bad enums, eps <= 0, overlaps, clear == stats),
- * BL_ESHAPE, BL_EALIGN, BL_EWORKSPACE, BL_EDEVICE.
- */
-size_t bitlinear_norm_stats_bytes(int64_t M);
-bl_status bitlinear_forward_fused_residual(const void *X, bl_dtype x_dtype, int bits, bl_gran gran,
-                                           float eps, const uint8_t *W_packed, const float *gamma,
-                                           const float *bias, int64_t M, int64_t N, int64_t K,
-                                           bl_epi epi, void *R, void *Y, void *stats, void *clear,
-                                           void *workspace, size_t workspace_bytes, void *stream);
-bl_status bitlinear_rmsnorm_forward_stats(const void *X, const void *stats, float eps, int bits,
-                                          float q_eps, const uint8_t *W_packed, const float *gamma,
-                                          const float *bias, int64_t parts, int64_t M, int64_t N,
-                                          int64_t K, bl_epi epi, void *Y, bl_dtype y_dtype,
-                                          void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Backward pass under the quantizers' straight-through estimators (quantization-aware

@@ -20,9 +20,6 @@ The functions mirror the C entry points:
 * :func:`layernorm`         -> ``bitlinear_layernorm`` (the same glue, non-affine layer norm)
 * :func:`layernorm_quantize` -> ``bitlinear_layernorm_quantize``
 * :func:`norm_forward`      -> ``bitlinear_norm_forward`` (residual + norm + quantize + projections)
-* :func:`forward_fused_residual` -> ``bitlinear_forward_fused_residual`` (R += Y, row statistics)
-* :func:`rmsnorm_forward_stats`  -> ``bitlinear_rmsnorm_forward_stats`` (norm from the statistics)
-* :func:`new_norm_stats`    -> a zeroed ``bitlinear_norm_stats_bytes`` buffer
 * :func:`backward`          -> ``bitlinear_backward`` (straight-through-estimator gradients)
 """
 from __future__ import annotations
@@ -42,7 +39,7 @@ BL_F32, BL_BF16, BL_I32 = 0, 1, 2
 BL_PER_TOKEN, BL_PER_TENSOR = 0, 1
 BL_EPI_NONE, BL_EPI_RELU2 = 0, 1
 (BL_OP_QUANTIZE_WEIGHTS, BL_OP_QUANTIZE_ACTS, BL_OP_FORWARD, BL_OP_FORWARD_FUSED,
- BL_OP_BACKWARD, BL_OP_NORM_FORWARD, BL_OP_FORWARD_RESIDUAL) = range(7)
+ BL_OP_BACKWARD, BL_OP_NORM_FORWARD) = range(6)
 BL_NORM_NONE, BL_NORM_RMS, BL_NORM_LAYER = range(3)
 
 
@@ -84,12 +81,6 @@ def lib() -> ctypes.CDLL:
         L.bitlinear_layernorm_quantize.argtypes = [P, P, P, I64, I64, F, I, I, F, P, P, P, SZ, P]
         L.bitlinear_norm_forward.argtypes = [P, P, P, I, F, I, I, F, P, P, P, I64, I64, I64, I64, I,
                                              P, I, P, SZ, P]
-        L.bitlinear_norm_stats_bytes.argtypes = [I64]
-        L.bitlinear_norm_stats_bytes.restype = SZ
-        L.bitlinear_forward_fused_residual.argtypes = [P, I, I, I, F, P, P, P, I64, I64, I64, I, P,
-                                                       P, P, P, P, SZ, P]
-        L.bitlinear_rmsnorm_forward_stats.argtypes = [P, P, F, I, F, P, P, P, I64, I64, I64, I64, I,
-                                                      P, I, P, SZ, P]
         L.bitlinear_quantize_weights_rotated.argtypes = [P, I, I64, I64, F, P, P, P, SZ, P]
         L.bitlinear_quantize_acts_rotated.argtypes = [P, I, I64, I64, I, I, F, P, P, P, SZ, P]
         L.bitlinear_hadamard_block.argtypes = [I64]
@@ -108,7 +99,6 @@ def lib() -> ctypes.CDLL:
                   "bitlinear_forward_multi", "bitlinear_forward_fused_noalloc",
                   "bitlinear_rmsnorm", "bitlinear_rmsnorm_quantize", "bitlinear_layernorm",
                   "bitlinear_layernorm_quantize", "bitlinear_norm_forward",
-                  "bitlinear_forward_fused_residual", "bitlinear_rmsnorm_forward_stats",
                   "bitlinear_quantize_weights_rotated", "bitlinear_quantize_acts_rotated",
                   "bitlinear_backward"):
             getattr(L, n).restype = I
@@ -568,78 +558,6 @@ def norm_forward(X, packed, gamma, delta=None, x_out=None, norm="rms", eps: floa
         _ptr(X), _ptr(delta), _ptr(x_out), _NORMS[norm], eps, bits, g, q_eps, _ptr(packed),
         _ptr(gamma), _ptr(bias), Pn, M, N, K, _epi_code(epilogue), _ptr(out), _dtype_code(out),
         _ptr(ws), wsb, _stream(dev, stream)))
-    return out
-
-
-def norm_stats_bytes(M: int) -> int:
-    """Bytes of a residual-statistics buffer for M tokens."""
-    return lib().bitlinear_norm_stats_bytes(M)
-
-
-def new_norm_stats(M: int, device=None):
-    """A zeroed residual-statistics buffer for M tokens (uint8 on the GPU)."""
-    torch = _torch()
-    return torch.zeros(norm_stats_bytes(M), dtype=torch.uint8,
-                       device=device if device is not None else "cuda")
-
-
-def forward_fused_residual(X, packed, gamma, R, stats=None, clear=None, y=None, bits: int = 8,
-                           gran="token", eps: float = 1e-5, bias=None, epilogue=None,
-                           workspace=None, stream=None):
-    """R += bf16(forward_fused(X, packed, gamma, ...)) in place (R [M, N] bf16, the residual
-    stream), adding the new rows' exact statistics to `stats` (a new_norm_stats buffer, zero
-    on entry; None: none) after zeroing the statistics buffer `clear` (None: none); y [M, N]
-    bf16 also receives the forward's output when given.  Returns R."""
-    torch = _torch()
-    bits = _bits(bits)
-    M, K = _dims(X, "X", 2)
-    N, _ = _dims(packed, "packed", 2)
-    g = _gran_code(gran)
-    _arg(X, "X", None, (torch.float32, torch.bfloat16))
-    _arg(packed, "packed", (N, K // 4), (torch.uint8,))
-    _arg(gamma, "gamma", (1,), (torch.float32,))
-    _arg(bias, "bias", (N,), (torch.float32,), optional=True)
-    _arg(R, "R", (M, N), (torch.bfloat16,))
-    _arg(y, "y", (M, N), (torch.bfloat16,), optional=True)
-    _arg(stats, "stats", (norm_stats_bytes(M),), (torch.uint8,), optional=True)
-    _arg(clear, "clear", (norm_stats_bytes(M),), (torch.uint8,), optional=True)
-    dev = _gpu(X=X, packed=packed, gamma=gamma, bias=bias, R=R, y=y, stats=stats, clear=clear)
-    ws, wsb = _workspace(workspace_size(BL_OP_FORWARD_RESIDUAL, M, N, K, bits, g), dev, workspace)
-    _check(lib().bitlinear_forward_fused_residual(
-        _ptr(X), _dtype_code(X), bits, g, eps, _ptr(packed), _ptr(gamma), _ptr(bias), M, N, K,
-        _epi_code(epilogue), _ptr(R), _ptr(y), _ptr(stats), _ptr(clear), _ptr(ws), wsb,
-        _stream(dev, stream)))
-    return R
-
-
-def rmsnorm_forward_stats(X, stats, packed, gamma, eps: float = 1e-6, bits: int = 8,
-                          q_eps: float = 1e-5, bias=None, epilogue=None, out_dtype=None,
-                          workspace=None, stream=None, out=None):
-    """norm_forward(X, packed, gamma, norm="rms") with X's row statistics taken from
-    `stats` (as forward_fused_residual left them for exactly X's rows).
-    packed [N, K/4] or [P, N, K/4], gamma [1] or [P] -> Y [M, N] or [P, M, N]."""
-    torch = _torch()
-    bits = _bits(bits)
-    M, K = _dims(X, "X", 2)
-    single = packed is not None and packed.dim() == 2
-    if single:
-        N, _ = _dims(packed, "packed", 2)
-        Pn = 1
-    else:
-        Pn, N, _ = _dims(packed, "packed", 3)
-    _arg(X, "X", None, (torch.bfloat16,))
-    _arg(stats, "stats", (norm_stats_bytes(M),), (torch.uint8,))
-    _arg(packed, "packed", (N, K // 4) if single else (Pn, N, K // 4), (torch.uint8,))
-    _arg(gamma, "gamma", (Pn,), (torch.float32,))
-    _arg(bias, "bias", (N,) if single else (Pn, N), (torch.float32,), optional=True)
-    yshape = (M, N) if single else (Pn, M, N)
-    _out_arg(out, yshape)
-    dev = _gpu(X=X, stats=stats, packed=packed, gamma=gamma, bias=bias, out=out)
-    out = _new_out(out, yshape, out_dtype, dev)
-    ws, wsb = _workspace(workspace_size(BL_OP_NORM_FORWARD, M, N, K, bits, "token"), dev, workspace)
-    _check(lib().bitlinear_rmsnorm_forward_stats(
-        _ptr(X), _ptr(stats), eps, bits, q_eps, _ptr(packed), _ptr(gamma), _ptr(bias), Pn, M, N,
-        K, _epi_code(epilogue), _ptr(out), _dtype_code(out), _ptr(ws), wsb, _stream(dev, stream)))
     return out
 
 

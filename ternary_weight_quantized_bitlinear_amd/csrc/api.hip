@@ -112,12 +112,6 @@ size_t ws_fused(int64_t M, int64_t N, int64_t K, int bits, bl_gran gran) {
     return up256(xq) + sc + aq + up256(bl::gemv_supports(M, K) ? 0 : bl::ws_gemm(M, N, K));
 }
 
-// bitlinear_forward_fused_residual: the fused forward's workspace, then (past the GEMV's
-// sizes) a bf16 [M][N] buffer for Y
-size_t ws_residual(int64_t M, int64_t N, int64_t K, int bits, bl_gran gran) {
-    return up256(ws_fused(M, N, K, bits, gran)) + up256((size_t)(M * N * 2));
-}
-
 #define CHECK(x)                                                                                   \
     do {                                                                                           \
         bl_status st_ = (x);                                                                       \
@@ -165,7 +159,7 @@ bl_status scratch_address(void **out, const char *fn) {
 
 extern "C" {
 
-int bitlinear_version(void) { return 10500; }  // 1.5.0: residual statistics
+int bitlinear_version(void) { return 10400; }  // 1.4.0: bitlinear_norm_forward
 
 const char *bitlinear_status_string(bl_status s) {
     switch (s) {
@@ -197,8 +191,6 @@ size_t bitlinear_workspace_size(bl_op op, int64_t M, int64_t N, int64_t K, int b
         return (bits == 8 || bits == 4) ? bl::ws_backward(M, N, K, (int)gran) : 0;
     case BL_OP_NORM_FORWARD:
         return (bits == 8 || bits == 4) ? ws_norm_forward(M, N, K, bits, gran) : 0;
-    case BL_OP_FORWARD_RESIDUAL:
-        return (bits == 8 || bits == 4) ? ws_residual(M, N, K, bits, gran) : 0;
     default:
         break;
     }
@@ -794,122 +786,6 @@ bl_status bitlinear_norm_forward(const void *X, const void *delta, void *X_out, 
         if (e != hipSuccess) return device(e, fn);
     }
     return ok();
-}
-
-
-size_t bitlinear_norm_stats_bytes(int64_t M) {
-    return M > 0 ? (bl::stats_words(M) * 8 + 15) & ~(size_t)15 : 0;
-}
-
-bl_status bitlinear_forward_fused_residual(const void *X, bl_dtype x_dtype, int bits, bl_gran gran,
-                                           float eps, const uint8_t *W_packed, const float *gamma,
-                                           const float *bias, int64_t M, int64_t N, int64_t K,
-                                           bl_epi epi, void *R, void *Y, void *stats, void *clear,
-                                           void *workspace, size_t workspace_bytes, void *stream) {
-    static const char fn[] = "bitlinear_forward_fused_residual";
-    if (!R) return fail(BL_EINVAL, "%s: null pointer", fn);
-    CHECK(check_fused(fn, X, x_dtype, bits, gran, eps, W_packed, gamma, bias, M, N, K, epi, R,
-                      BL_BF16));
-    if (M >= 65536) return fail(BL_ESHAPE, "%s: M=%lld too large (M < 65536)", fn, (long long)M);
-    if ((Y && !aligned(Y, 16)) || (stats && !aligned(stats, 8)) || (clear && !aligned(clear, 8)))
-        return fail(BL_EALIGN, "%s: Y needs 16-byte, stats and clear 8-byte alignment", fn);
-    if (clear && clear == stats) return fail(BL_EINVAL, "%s: clear must be another buffer", fn);
-    {
-        const uintptr_t rb = (uintptr_t)(M * N * 2);
-        const uintptr_t xb = (uintptr_t)(M * K * (x_dtype == BL_BF16 ? 2 : 4));
-        auto overlap = [](const void *a, uintptr_t na, const void *b, uintptr_t nb) {
-            return (uintptr_t)a < (uintptr_t)b + nb && (uintptr_t)b < (uintptr_t)a + na;
-        };
-        if (overlap(R, rb, X, xb) || (Y && overlap(R, rb, Y, rb)))
-            return fail(BL_EINVAL, "%s: R must not overlap X or Y", fn);
-    }
-    const size_t need = ws_residual(M, N, K, bits, gran);
-    if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
-        return fail(BL_EWORKSPACE, "%s: need %zu bytes of 256-byte aligned workspace", fn, need);
-    hipStream_t s = (hipStream_t)stream;
-    uint64_t *st = static_cast<uint64_t *>(stats);
-    uint64_t *cl = static_cast<uint64_t *>(clear);
-    (void)hipGetLastError();
-    if (bl::gemv_supports(M, K)) {
-        // the decode GEMV adds the residual and the statistics in its epilogue
-        const int xbf = x_dtype == BL_BF16;
-        if (fused_in_prologue(M, K) || (xbf && gran == BL_PER_TOKEN && bl::gemv_rows_supports(M, K))) {
-            bl::FwdArgs a = make_args(X, xbf, bits, nullptr, gran, eps, W_packed, gamma, bias, M, N,
-                                      K, epi, Y, BL_BF16);
-            a.rows = fused_in_prologue(M, K) ? 0 : 1;
-            a.res = R;
-            a.stats = st;
-            a.clear = cl;
-            return device(bl::launch_gemv(a, true, workspace, s), fn);
-        }
-        uint8_t *base = static_cast<uint8_t *>(workspace);
-        void *xq = base;
-        float *scale = reinterpret_cast<float *>(base + up256((size_t)(bits == 8 ? M * K : M * K / 2)));
-        void *aq_ws = reinterpret_cast<uint8_t *>(scale) + up256((size_t)M * sizeof(float));
-        hipError_t e = bl::launch_quantize_acts(X, xbf, M, K, bits, (int)gran, eps, xq, scale,
-                                                aq_ws, s);
-        if (e != hipSuccess) return device(e, fn);
-        bl::FwdArgs a = make_args(xq, 0, bits, scale, gran, eps, W_packed, gamma, bias, M, N, K,
-                                  epi, Y, BL_BF16);
-        a.res = R;
-        a.stats = st;
-        a.clear = cl;
-        return device(bl::launch_gemv(a, false, nullptr, s), fn);
-    }
-    // the fused forward into Y (or the workspace), then the residual add with the statistics
-    uint8_t *yb = Y ? static_cast<uint8_t *>(Y)
-                    : static_cast<uint8_t *>(workspace) + up256(ws_fused(M, N, K, bits, gran));
-    const bl_status r = bitlinear_forward_fused(X, x_dtype, bits, gran, eps, W_packed, gamma, bias,
-                                                M, N, K, epi, yb, BL_BF16, workspace,
-                                                up256(ws_fused(M, N, K, bits, gran)), stream);
-    if (r != BL_OK) return r;
-    return device(bl::launch_residual_stats(R, yb, M, N, st, cl, s), fn);
-}
-
-bl_status bitlinear_rmsnorm_forward_stats(const void *X, const void *stats, float eps, int bits,
-                                          float q_eps, const uint8_t *W_packed, const float *gamma,
-                                          const float *bias, int64_t parts, int64_t M, int64_t N,
-                                          int64_t K, bl_epi epi, void *Y, bl_dtype y_dtype,
-                                          void *workspace, size_t workspace_bytes, void *stream) {
-    static const char fn[] = "bitlinear_rmsnorm_forward_stats";
-    if (!X || !stats) return fail(BL_EINVAL, "%s: null pointer", fn);
-    if (parts < 1 || parts > 65535)
-        return fail(BL_ESHAPE, "%s: parts=%lld must be in [1, 65535]", fn, (long long)parts);
-    CHECK(check_forward_common(fn, bits, BL_PER_TOKEN, W_packed, gamma, bias, M, N, K, epi, Y,
-                               y_dtype));
-    CHECK(check_eps(eps, fn));
-    CHECK(check_eps(q_eps, fn));
-    if (M >= (1ll << 24))
-        return fail(BL_ESHAPE, "%s: M=%lld too large for a norm (M < 2^24)", fn, (long long)M);
-    if (!aligned(X, 16) || !aligned(stats, 8))
-        return fail(BL_EALIGN, "%s: X needs 16-byte, stats 8-byte alignment", fn);
-    const int64_t wst = N * (K / 4);
-    const int64_t yst = M * N * (y_dtype == BL_I32 || y_dtype == BL_F32 ? 4 : 2);
-    if (parts > 1 && (wst % 16 != 0 || yst % 16 != 0))
-        return fail(BL_EALIGN, "%s: per-part strides (W %lld, Y %lld bytes) must be multiples of 16",
-                    fn, (long long)wst, (long long)yst);
-    if (parts * wst >= (1ll << 40) || parts * yst >= (1ll << 40))
-        return fail(BL_ESHAPE, "%s: parts too large for these sizes", fn);
-    hipStream_t s = (hipStream_t)stream;
-    (void)hipGetLastError();
-    if (bl::gemv_rows_supports(M, K)) {
-        // one launch: the decode GEMV normalizes from the statistics and quantizes
-        bl::FwdArgs a = make_args(X, 1, bits, nullptr, BL_PER_TOKEN, q_eps, W_packed, gamma, bias, M,
-                                  N, K, epi, Y, y_dtype);
-        a.rows = 1;
-        a.nstats = const_cast<uint64_t *>(static_cast<const uint64_t *>(stats));
-        a.norm_eps = eps;
-        a.batch = parts;
-        a.x_shared = 1;
-        return device(bl::launch_gemv(a, true, nullptr, s), fn);
-    }
-    // otherwise the norm kernel computes the same statistics from X itself
-    const size_t need = ws_norm_forward(M, N, K, bits, BL_PER_TOKEN);
-    if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
-        return fail(BL_EWORKSPACE, "%s: need %zu bytes of 256-byte aligned workspace", fn, need);
-    return bitlinear_norm_forward(X, nullptr, nullptr, BL_NORM_RMS, eps, bits, BL_PER_TOKEN, q_eps,
-                                  W_packed, gamma, bias, parts, M, N, K, epi, Y, y_dtype, workspace,
-                                  workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -257,25 +257,12 @@ struct FwdArgs {
     const int32_t *rowsum = nullptr;  // prepared activations: sum_k q[m][k] per token
     // the GEMV's row prologue (raw bf16 X, per-token scales, M <= 16) when rows = 1
     int rows = 0;
-    // GEMV path only: the residual epilogue (res, stats) and the row prologue's RMS norm
-    // from statistics (nstats, norm_eps); see GemvParams
-    void *res = nullptr;
-    uint64_t *stats = nullptr;
-    uint64_t *clear = nullptr;
-    uint64_t *nstats = nullptr;
-    float norm_eps = 0.0f;
 };
 
 // whether the GEMV's row prologue takes M tokens of K (M <= 16, K <= 4096)
 bool gemv_rows_supports(int64_t M, int64_t K);
 
 hipError_t launch_zero_u32(uint32_t *p, int64_t n, hipStream_t s);
-// 64-bit words of exact per-token statistics of M tokens (row_stats.hpp)
-size_t stats_words(int64_t M);
-// R = bf16(fl32(R + Y)) for bf16 [M][N] R and Y, adding the new rows' statistics to
-// stats (may be null), after zeroing the statistics `clear` (may be null)
-hipError_t launch_residual_stats(void *R, const void *Y, int64_t M, int64_t N, uint64_t *stats,
-                                 uint64_t *clear, hipStream_t s);
 hipError_t launch_quantize_weights(const void *w, int w_bf16, int64_t N, int64_t K, float eps,
                                    uint8_t *packed, float *gamma, void *ws, hipStream_t s);
 size_t ws_quantize_weights();

@@ -41,7 +41,6 @@
 #include <atomic>
 
 #include "common.hpp"
-#include "row_stats.hpp"
 
 namespace bl {
 namespace {
@@ -69,15 +68,6 @@ struct GemvParams {
     // problem blockIdx.y starts this many bytes further on (0 for a single problem)
     int64_t x_bstride, w_bstride, y_bstride;
     int64_t s_bstride;  // act_scale elements between problems (0: one shared input)
-    // residual epilogue (one problem, bf16 y): R += bf16(y) in place, and the exact
-    // statistics of R's new rows added to `stats` (row_stats.hpp; may be null); block
-    // (0, 0) first zeroes the statistics `clear` (another buffer; may be null)
-    void *res = nullptr;
-    uint64_t *stats = nullptr;
-    uint64_t *clear = nullptr;
-    // row prologue: the RMS norm of the rows from their statistics `nstats`, eps norm_eps
-    uint64_t *nstats = nullptr;
-    float norm_eps = 0.0f;
 };
 
 
@@ -192,14 +182,11 @@ __global__ void __launch_bounds__(kWaves * 64) gemv_kernel(GemvParams p) {
     __shared__ float s_f[kMaxM];        // dequant factor per token
     __shared__ uint32_t s_amax[kMaxM];  // absmax bits per token (non-negative: uint order)
     __shared__ v4i s_acc[kWaves][64];
-    __shared__ uint32_t s_big[kMode == kRowsBf16 ? kWaves : 1][kSqLimbs];
-    __shared__ uint64_t s_tot[kMode == kRowsBf16 ? kWaves : 1][kStatWords];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
     const int M = p.M, K = p.K;
     const int ngroups = K >> 4;
-    if (p.clear && blockIdx.x == 0 && blockIdx.y == 0) stats_clear(p.clear, M);
     const int n0 = blockIdx.x * 16;
     const int r16 = lane & 15, chunk = lane >> 4;
     const int nrow = n0 + r16;
@@ -359,40 +346,19 @@ __global__ void __launch_bounds__(kWaves * 64) gemv_kernel(GemvParams p) {
 #pragma unroll
                     for (int i = 0; i < 8; ++i) v[j][i] = g < ngroups ? w[i] : 0u;
                 }
-                float amax;
-                if (p.nstats) {
-                    // the RMS norm from the row's statistics: r = 1 / sqrt(S / K + eps)
-                    // with S exact, and max |h| = bf16(fl32(max |x'| r)) (the rounding
-                    // steps are monotone), then h = bf16(fl32(x' r)) per value
-                    float mxr;
-                    const double S = stats_read(p.nstats + (size_t)m * kStatWords * kStatCopies,
-                                                s_tot[kRows ? wave : 0], s_big[kRows ? wave : 0], &mxr);
-                    const double rr = 1.0 / sqrt(S / (double)K + (double)p.norm_eps);
-                    amax = bf16_lo(to_bf16_bits((float)((double)mxr * rr)));
+                float mx = 0.0f;
 #pragma unroll
-                    for (int j = 0; j < kG; ++j)
+                for (int j = 0; j < kG; ++j)
 #pragma unroll
-                        for (int i = 0; i < 8; ++i) {
-                            const uint32_t lo = to_bf16_bits((float)((double)bf16_lo(v[j][i]) * rr));
-                            const uint32_t hi = to_bf16_bits((float)((double)bf16_hi(v[j][i]) * rr));
-                            v[j][i] = (lo & 0xFFFFu) | (hi << 16);
-                        }
-                } else {
-                    float mx = 0.0f;
-#pragma unroll
-                    for (int j = 0; j < kG; ++j)
-#pragma unroll
-                        for (int i = 0; i < 8; ++i)
-                            mx = fmaxf(mx, fmaxf(fabsf(bf16_lo(v[j][i])), fabsf(bf16_hi(v[j][i]))));
-                    amax = wave_max_abs(mx);
-                }
+                    for (int i = 0; i < 8; ++i)
+                        mx = fmaxf(mx, fmaxf(fabsf(bf16_lo(v[j][i])), fabsf(bf16_hi(v[j][i]))));
                 // the words as the codes loop sees them: the widened values of the max
                 // loop are not kept for it (a whole row of them would not fit)
 #pragma unroll
                 for (int j = 0; j < kG; ++j)
 #pragma unroll
                     for (int i = 0; i < 8; ++i) asm volatile("" : "+v"(v[j][i]));
-                const float a = fmaxf(amax, p.eps);
+                const float a = fmaxf(wave_max_abs(mx), p.eps);
                 const float sc = kBits == 8 ? 127.0f / a : a / 7.0f;
                 const float r4 = kBits == 8 ? 0.0f : q4_recip(sc);
                 if (lane == 0) s_f[m] = kBits == 8 ? gamma / sc : sc * gamma;
@@ -513,35 +479,6 @@ __global__ void __launch_bounds__(kWaves * 64) gemv_kernel(GemvParams p) {
         for (int w = 1; w < kWaves; ++w) acc += s_acc[w][lane];
     }
     // lane holds C[m = 4*chunk + r][n = n0 + r16]
-    if (p.res) {
-        // residual epilogue: d = bf16(y), R = bf16(fl32(R + d)) in place (d also to Y
-        // when given), and the exact statistics of the new R rows; every lane of a token's
-        // 16-lane group takes part (lanes past N with the value 0)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int m = 4 * chunk + r;
-            if (m >= M) continue;  // uniform in the 16-lane group
-            uint32_t xb = 0;
-            if (row_ok) {
-                float y = __fmul_rn((float)acc[r], s_f[m]);
-                if (p.bias) y = __fadd_rn(y, p.bias[nrow]);
-                if (p.epi == 1) {
-                    const float rr = y > 0.0f ? y : 0.0f;
-                    y = __fmul_rn(rr, rr);
-                }
-                const uint32_t d = to_bf16_bits(y) & 0xFFFFu;
-                const size_t idx = (size_t)m * p.N + nrow;
-                if (p.y) static_cast<uint16_t *>(p.y)[idx] = (uint16_t)d;
-                uint16_t *R = static_cast<uint16_t *>(p.res);
-                xb = to_bf16_bits(__fadd_rn(bf16_lo(R[idx]), bf16_lo(d))) & 0xFFFFu;
-                R[idx] = (uint16_t)xb;
-            }
-            if (p.stats)
-                stats_add_group16(xb, p.stats + (size_t)m * kStatWords * kStatCopies +
-                                          blockIdx.x % kStatCopies);
-        }
-        return;
-    }
     if (!row_ok) return;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -1164,11 +1101,6 @@ hipError_t launch_gemv(const FwdArgs &a, bool fused, void *, hipStream_t s) {
     p.s_bstride = a.x_shared ? 0 : (a.gran == 1 ? 1 : a.M);
     p.w_bstride = a.N * (a.K / 4);
     p.y_bstride = a.M * a.N * (a.y_dtype == 1 ? 2 : 4);
-    p.res = a.res;
-    p.stats = a.stats;
-    p.clear = a.clear;
-    p.nstats = a.nstats;
-    p.norm_eps = a.norm_eps;
     if (a.rows) {  // raw bf16 rows, a wave per token row (the caller checked the shape)
         p.x_bstride = a.x_shared ? 0 : a.M * 2 * a.K;
         return launch_rows(p, a.batch, s);
@@ -1177,8 +1109,7 @@ hipError_t launch_gemv(const FwdArgs &a, bool fused, void *, hipStream_t s) {
     // at least four 16-row tiles per streaming wave: the streaming kernel, each block a
     // contiguous run of one problem's row groups
     const int64_t target = kStreamBlocksPerCu * (int64_t)device_cus();
-    // (the residual epilogue and the statistics prologue live in the latency kernel)
-    if (!a.res && !a.nstats && !a.clear && a.batch * ((a.N + 15) / 16) >= 4 * target * kStreamWaves) {
+    if (a.batch * ((a.N + 15) / 16) >= 4 * target * kStreamWaves) {
         const int64_t GSr = 16 * kStreamWaves * kStreamRows;  // rows per group
         const int64_t G = (a.N + GSr - 1) / GSr;
         const int64_t bpp = std::max<int64_t>(1, std::min<int64_t>(G, target / a.batch));

@@ -20,7 +20,6 @@
 #include "common.hpp"
 #include "exact_moments.hpp"
 #include "wave_exact.hpp"
-#include "row_stats.hpp"
 
 namespace bl {
 namespace {
@@ -392,35 +391,7 @@ norm_quant_rows(const uint16_t *xin, const uint16_t *__restrict__ delta, uint16_
     }
 }
 
-// R = bf16(fl32(R + Y)) over bf16 rows, 256 columns per block (blockIdx.y the token);
-// each 16 consecutive columns add their exact statistics to the token's words
-__global__ void __launch_bounds__(256)
-residual_stats_rows(uint16_t *__restrict__ R, const uint16_t *__restrict__ Y, int64_t N,
-                    uint64_t *__restrict__ stats, uint64_t *__restrict__ clear) {
-    if (clear && blockIdx.x == 0 && blockIdx.y == 0) stats_clear(clear, gridDim.y);
-    const int64_t m = blockIdx.y;
-    const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    uint32_t xb = 0;
-    if (n < N) {
-        const size_t idx = (size_t)m * N + n;
-        xb = to_bf16_bits(__fadd_rn(bf16_lo(R[idx]), bf16_lo(Y[idx]))) & 0xFFFFu;
-        R[idx] = (uint16_t)xb;
-    }
-    if (stats)
-        stats_add_group16(xb, stats + (size_t)m * kStatWords * kStatCopies + blockIdx.x % kStatCopies);
-}
-
 }  // namespace
-
-size_t stats_words(int64_t M) { return (size_t)M * kStatWords * kStatCopies; }
-
-hipError_t launch_residual_stats(void *R, const void *Y, int64_t M, int64_t N, uint64_t *stats,
-                                 uint64_t *clear, hipStream_t s) {
-    const dim3 grid((unsigned)((N + 255) / 256), (unsigned)M);
-    hipLaunchKernelGGL(residual_stats_rows, grid, dim3(256), 0, s, static_cast<uint16_t *>(R),
-                       static_cast<const uint16_t *>(Y), N, stats, clear);
-    return hipGetLastError();
-}
 
 hipError_t launch_norm_quantize(const void *x, const void *delta, void *x_out, void *h, int64_t M,
                                 int64_t K, float eps, bool centre, int bits, float q_eps, void *xq,

@@ -25,9 +25,7 @@ def test_exports_every_header_function(L):
         "bitlinear_quantize_weights", "bitlinear_quantize_acts", "bitlinear_forward",
         "bitlinear_forward_fused", "bitlinear_forward_fused_batched", "bitlinear_forward_multi",
         "bitlinear_rmsnorm", "bitlinear_rmsnorm_quantize", "bitlinear_layernorm",
-        "bitlinear_layernorm_quantize", "bitlinear_norm_forward", "bitlinear_norm_stats_bytes",
-        "bitlinear_forward_fused_residual", "bitlinear_rmsnorm_forward_stats",
-        "bitlinear_workspace_size", "bitlinear_status_string",
+        "bitlinear_layernorm_quantize", "bitlinear_norm_forward", "bitlinear_workspace_size", "bitlinear_status_string",
         "bitlinear_last_error", "bitlinear_version", "bitlinear_hadamard_block",
         "bitlinear_quantize_weights_rotated", "bitlinear_quantize_acts_rotated",
         "bitlinear_backward", "bitlinear_forward_fused_noalloc",
@@ -49,7 +47,7 @@ def test_library_is_gfx950_code():
 def test_status_strings_and_version(L):
     for s in range(7):
         assert L.bitlinear_status_string(s).decode()
-    assert L.bitlinear_version() >= 10500  # 1.5: residual statistics
+    assert L.bitlinear_version() >= 10400  # 1.4: bitlinear_norm_forward
 
 
 def test_workspace_sizes(L):
@@ -406,44 +404,3 @@ def test_norm_forward_rejects(L):
     # the workspace covers h, the codes, the scales and the forward's own
     need = L.bitlinear_workspace_size(5, 16, 2560, 2560, 8, 0)
     assert need >= 16 * 2560 * 3 + 16 * 4
-
-
-def test_residual_stats_rejects(L):
-    f = L.bitlinear_forward_fused_residual
-    X, W, G, R, Y, S = (P(A), P(A + (1 << 20)), P(A + (2 << 20)), P(A + (3 << 20)),
-                        P(A + (4 << 20)), P(A + (5 << 20)))
-
-    def call(**kw):
-        a = dict(X=X, xdt=1, bits=8, gran=0, eps=1e-5, W=W, g=G, b=None, M=16, N=2560, K=2560,
-                 epi=0, R=R, Y=Y, S=S, C=None, ws=None, wsb=0)
-        a.update(kw)
-        return f(a["X"], a["xdt"], a["bits"], a["gran"], a["eps"], a["W"], a["g"], a["b"], a["M"],
-                 a["N"], a["K"], a["epi"], a["R"], a["Y"], a["S"], a["C"], a["ws"], a["wsb"], None)
-
-    assert call(R=None) == bl.BL_EINVAL
-    assert call(X=None) == bl.BL_EINVAL
-    assert call(xdt=2) == bl.BL_EINVAL
-    assert call(M=65536, N=16, K=16) == bl.BL_ESHAPE
-    assert call(S=P(A + (5 << 20) + 4)) == bl.BL_EALIGN
-    assert call(R=P(A + 64)) == bl.BL_EINVAL       # R overlaps X
-    assert call(C=S) == bl.BL_EINVAL               # clear must be another buffer
-    assert call(C=P(A + (6 << 20) + 4)) == bl.BL_EALIGN
-    assert call() == bl.BL_EWORKSPACE              # the workspace is required
-    assert L.bitlinear_last_error().decode().startswith("bitlinear_forward_fused_residual")
-    g = L.bitlinear_rmsnorm_forward_stats
-
-    def call2(**kw):
-        a = dict(X=X, S=S, eps=1e-6, bits=8, qe=1e-5, W=W, g=G, b=None, parts=1, M=16, N=2560,
-                 K=2560, epi=0, Y=Y, ydt=1, ws=None, wsb=0)
-        a.update(kw)
-        return g(a["X"], a["S"], a["eps"], a["bits"], a["qe"], a["W"], a["g"], a["b"], a["parts"],
-                 a["M"], a["N"], a["K"], a["epi"], a["Y"], a["ydt"], a["ws"], a["wsb"], None)
-
-    assert call2(S=None) == bl.BL_EINVAL
-    assert call2(eps=0.0) == bl.BL_EINVAL
-    assert call2(parts=0) == bl.BL_ESHAPE
-    assert call2(S=P(A + (5 << 20) + 2)) == bl.BL_EALIGN
-    assert call2(K=6912) == bl.BL_EWORKSPACE       # past the one-launch path
-    assert L.bitlinear_last_error().decode().startswith("bitlinear_rmsnorm_forward_stats")
-    assert L.bitlinear_norm_stats_bytes(16) >= 16 * 20 * 8 + 8
-    assert L.bitlinear_norm_stats_bytes(0) == 0

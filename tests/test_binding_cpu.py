@@ -147,15 +147,6 @@ CASES = [
     ("norm_forward: x_out shape", lambda: bl.norm_forward(
         t((M, K), torch.bfloat16), t((N, K // 4), torch.uint8), t((1,)),
         delta=t((M, K), torch.bfloat16), x_out=t((M, K + 16), torch.bfloat16)), bl.BL_ESHAPE, "x_out"),
-    ("forward_fused_residual: R shape", lambda: bl.forward_fused_residual(
-        t((M, K), torch.bfloat16), t((N, K // 4), torch.uint8), t((1,)),
-        t((M, N + 16), torch.bfloat16)), bl.BL_ESHAPE, "R"),
-    ("forward_fused_residual: stats dtype", lambda: bl.forward_fused_residual(
-        t((M, K), torch.bfloat16), t((N, K // 4), torch.uint8), t((1,)), t((M, N), torch.bfloat16),
-        stats=t((bl.norm_stats_bytes(M) // 4,))), bl.BL_EINVAL, "stats"),
-    ("rmsnorm_forward_stats: stats size", lambda: bl.rmsnorm_forward_stats(
-        t((M, K), torch.bfloat16), t((8,), torch.uint8), t((N, K // 4), torch.uint8), t((1,))),
-     bl.BL_ESHAPE, "stats"),
     ("norm_forward: host tensors", lambda: bl.norm_forward(
         t((M, K), torch.bfloat16), t((N, K // 4), torch.uint8), t((1,))), bl.BL_EINVAL, "GPU"),
     # backward

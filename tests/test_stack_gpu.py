@@ -182,20 +182,18 @@ def test_stack_30_layers_parity():
 
 @pytest.mark.timeout(1200)
 def test_stack_30_layers_fused_parity():
-    """The same 30-layer stack in the benchmark's fused calls: RMS norm + quantization +
-    Q, K, V in one call (from the norm kernel at layer 0, from the residual statistics
-    after), O adding its output to the residual stream with the rows' exact statistics,
-    RMS norm from those statistics + quantization + up (+ReLU^2) in one call, down adding
-    to the stream likewise.  Every value these calls write -- the stream after each add,
-    Q, K, V, O, up, down -- is compared with the oracle's chain from the same x0 and
-    weights, bit for bit; the two statistics buffers alternate, each producer clearing
-    the other."""
+    """The same 30-layer stack in the benchmark's fused calls: residual add + RMS norm +
+    quantization + Q, K, V in one call (bitlinear_norm_forward, three parts), O quantizing
+    its own input, residual add + RMS norm + quantization + up (+ReLU^2) in one call,
+    down quantizing its own input; the residual stream alternates between two buffers.
+    Every value these calls write -- the stream after each add, Q, K, V, O, up, down --
+    is compared with the oracle's chain from the same x0 and weights, bit for bit, and
+    the final stream after the last residual add."""
     H = workloads.HIDDEN
     x = workloads.stack_input(seed=3, m=16)
-    R = to_dev(x)
-    stats = (bl.new_norm_stats(16), bl.new_norm_stats(16))
-    o = torch.empty((16, H), dtype=torch.bfloat16, device=R.device)
-    d = torch.empty((16, H), dtype=torch.bfloat16, device=R.device)
+    x0 = to_dev(x)
+    bufs = (torch.empty_like(x0), torch.empty_like(x0))
+    cur, delta = x0, None
     x_ref, d_ref = x.copy(), None
     compared = 0
     for layer in range(workloads.LAYERS_2B):
@@ -203,28 +201,30 @@ def test_stack_30_layers_fused_parity():
         w = _layer_weights(layer)
         ref = _oracle_layer(x_ref, d_ref, w)
         (pq, gq), _, _ = w["qkv"]
-        pq3, gq3 = pq.view(3, H, pq.shape[1]), gq.expand(3).contiguous()
-        x1 = to_host(R)
-        if layer == 0:
-            qkv = bl.norm_forward(R, pq3, gq3, out_dtype=torch.bfloat16)
-        else:
-            qkv = bl.rmsnorm_forward_stats(R, stats[0], pq3, gq3, out_dtype=torch.bfloat16)
+        nxt = bufs[0] if cur is not bufs[0] else bufs[1]
+        qkv = bl.norm_forward(cur, pq.view(3, H, pq.shape[1]), gq.expand(3).contiguous(),
+                              delta=delta, x_out=nxt if delta is not None else None,
+                              out_dtype=torch.bfloat16)
+        cur = nxt if delta is not None else cur
+        x1 = to_host(cur)
         (po, go), _, _ = w["o"]
-        bl.forward_fused_residual(qkv[2], po, go, R, stats=stats[1], clear=stats[0], y=o)
-        x2 = to_host(R)
+        o = bl.forward_fused(qkv[2], po, go, out_dtype=torch.bfloat16)
         (pu, gu), _, _ = w["up"]
-        u = bl.rmsnorm_forward_stats(R, stats[1], pu, gu, epilogue="relu2",
-                                     out_dtype=torch.bfloat16)
+        nxt = bufs[0] if cur is not bufs[0] else bufs[1]
+        u = bl.norm_forward(cur, pu, gu, delta=o, x_out=nxt, epilogue="relu2",
+                            out_dtype=torch.bfloat16)
+        cur = nxt
         (pd, gd), _, _ = w["down"]
-        bl.forward_fused_residual(u, pd, gd, R, stats=stats[0], clear=stats[1], y=d)
+        delta = bl.forward_fused(u, pd, gd, out_dtype=torch.bfloat16)
         torch.cuda.synchronize()
-        assert not to_host(stats[1]).any(), "layer %d: statistics not cleared" % layer
         got = {"x1": x1, "Q": to_host(qkv[0]), "K": to_host(qkv[1]), "V": to_host(qkv[2]),
-               "O": to_host(o), "x2": x2, "up": to_host(u), "down": to_host(d)}
+               "O": to_host(o), "x2": to_host(cur), "up": to_host(u), "down": to_host(delta)}
         for key, val in got.items():
             assert_same_bytes(val, ref[key], "layer %d %s" % (layer, key))
             compared += val.size
         x_ref, d_ref = ref["x2"], ref["down"]
     xf, _ = oracle.rmsnorm(x_ref, d_ref)
-    assert_same_bytes(to_host(R), xf, "final residual stream")
+    bl.rmsnorm(cur, delta)
+    torch.cuda.synchronize()
+    assert_same_bytes(to_host(cur), xf, "final residual stream")
     say("fused stack: %d values compared over %d layers, 0 differ" % (compared, workloads.LAYERS_2B))
