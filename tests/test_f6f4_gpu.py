@@ -26,9 +26,11 @@ pytestmark = pytest.mark.gpu
 K_MAX_F6 = (1 << 20) - 64
 
 # (M, K, N): one tile, ragged M and N, several k steps, 128-wide tiles (few tiles) and
-# 256-wide tiles (M=2048, N=4096: 128 tiles of 256 x 256)
+# 256-wide tiles (at least 128 tiles of 256 x 256: the ping-pong k loop of two wave
+# groups), there with one k step, an even and two odd numbers of them, ragged M and N
 F6_SHAPES = [(128, 64, 128), (129, 128, 130), (300, 192, 257), (256, 2560, 384),
-             (513, 640, 1000), (2048, 128, 4096)]
+             (513, 640, 1000), (2048, 128, 4096), (2048, 64, 4096), (2100, 320, 4000),
+             (2304, 448, 3900)]
 
 
 @pytest.mark.parametrize("M,K,N", F6_SHAPES)
