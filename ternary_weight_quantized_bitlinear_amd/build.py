@@ -25,7 +25,7 @@ LIB = os.path.join(PKG, "libbitlinear.so")
 # matrix-core calibration loops for the benchmark (not part of the BitLinear C ABI)
 CALIB_LIB = os.path.join(PKG, "libbitlinear_calib.so")
 CALIB_SOURCES = ["calib.hip"]
-SOURCES = ["api.hip", "wquant.hip", "aquant.hip", "gemv.hip", "gemm.hip", "gemm_big.hip",
+SOURCES = ["api.hip", "wquant.hip", "aquant.hip", "gemv.hip", "gemm.hip", "gemm_big.hip", "gemm_mid.hip",
            "gemm_f6f4.hip", "norm.hip", "gemm_bf16.hip", "backward.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -144,6 +144,15 @@ __host__ __device__ inline uint32_t q4(float x, float s, float r) {
     return (uint32_t)((int)v) & 0xFu;
 }
 
+// ---------------------------------------------------------------- vmcnt waits
+// s_waitcnt vmcnt(kN): at most kN of this wave's vector memory operations (loads, stores,
+// global -> LDS copies) still in flight; lgkmcnt and expcnt left open.
+template <int kN>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(kN >= 0 && kN < 64, "vmcnt is 6 bits");
+    __builtin_amdgcn_s_waitcnt((kN & 0xF) | ((kN >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
 // ---------------------------------------------------------------- global -> LDS DMA
 // 16 bytes per lane from global memory straight into LDS: lane i's bytes land at
 // lds_dst + 16 i (lds_dst the same in every lane).  Inline asm, so that the compiler
@@ -172,6 +181,8 @@ __device__ __forceinline__ void lds_dma16_lanes(const void *src, uint32_t lds_ad
     const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(lane_mask >> 32));
     const uint64_t lanes = ((uint64_t)hi << 32) | lo;
     uint64_t saved;
+    // s_and_b64 also writes SCC: without the clobber the compiler may keep a live
+    // condition in SCC across the statement
     asm volatile("s_mov_b64 %0, exec\n\t"
                  "s_and_b64 exec, exec, %3\n\t"
                  "s_mov_b32 m0, %2\n\t"
@@ -180,7 +191,7 @@ __device__ __forceinline__ void lds_dma16_lanes(const void *src, uint32_t lds_ad
                  "s_mov_b64 exec, %0"
                  : "=&s"(saved)
                  : "v"(src), "s"(lds), "s"(lanes)
-                 : "memory", "m0");
+                 : "memory", "m0", "scc");
 }
 
 // ---------------------------------------------------------------- Hadamard rotation
@@ -313,6 +324,10 @@ hipError_t launch_gemm(const FwdArgs &a, void *ws, hipStream_t s);
 // prefill-sized M with whole 64-wide k steps: 256x256 tiles, LDS ring, 32x32x32 MFMA
 bool gemm_big_supports(int64_t M, int64_t N, int64_t K, int bits);
 hipError_t launch_gemm_big(const FwdArgs &a, hipStream_t s);
+// the balanced-tile variant (128 x 160 tiles, 16 x 16 x 64 MFMAs) on the same prepared
+// operands; launch_gemm_big takes it where it leaves fewer CUs idle
+bool gemm_mid_preferred(int64_t M, int64_t N, int64_t K, int bits);
+hipError_t launch_gemm_mid(const FwdArgs &a, hipStream_t s);
 size_t ws_gemm(int64_t M, int64_t N, int64_t K);
 // prefill-sized M with 4-bit activations: FP6 x FP4 scaled MFMA (exact for K < 2^20)
 bool gemm_f6f4_supports(int64_t M, int64_t N, int64_t K, int bits);

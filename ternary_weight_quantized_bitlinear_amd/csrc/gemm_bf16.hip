@@ -56,12 +56,6 @@ constexpr size_t kLds = (size_t)kStages * kStageBytes;
 
 __device__ __forceinline__ int swz(int row) { return ((row >> 1) & 3) ^ ((row >> 3) & 1); }
 
-template <int kN>
-__device__ __forceinline__ void wait_vm() {
-    static_assert(kN >= 0 && kN < 64, "vmcnt is 6 bits");
-    __builtin_amdgcn_s_waitcnt((kN & 0xF) | ((kN >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
 __device__ __forceinline__ float row_scale(const BfEpilogue &e, int row) {
     switch (e.scale_mode) {
     case kScaleGammaOverS: return *e.gamma / e.act_scale[row];

@@ -199,8 +199,7 @@ __global__ void __launch_bounds__(Tile<kBN>::kThreads, kBN == 128 ? 2 : 1) gemm_
     // stage, the barrier and the next DMA issue sit halfway through the second
     // sub-step, with 8 MFMAs queued.  The barrier there also certifies that every wave
     // finished step kt - 1, whose slot the new DMA refills.
-    __builtin_amdgcn_s_waitcnt((((kStages - 2) * kDma) & 0xF) | ((((kStages - 2) * kDma) >> 4) << 14) |
-                               (0x7 << 4) | (0xF << 8));
+    wait_vm<(kStages - 2) * kDma>();
     __syncthreads();
     v4i a0[4], b0[NJ], a1[4], b1[NJ];
     uint32_t bw[NJ];
@@ -232,8 +231,7 @@ __global__ void __launch_bounds__(Tile<kBN>::kThreads, kBN == 128 ? 2 : 1) gemm_
         // phase 2: half of sub-step 1, then the next stage's wait, barrier and DMA
         mfmas(a1, b1, 0, 2);
         __builtin_amdgcn_sched_barrier(0);
-        __builtin_amdgcn_s_waitcnt((((kStages - 3) * kDma) & 0xF) | ((((kStages - 3) * kDma) >> 4) << 14) |
-                                   (0x7 << 4) | (0xF << 8));
+        wait_vm<(kStages - 3) * kDma>();
         __syncthreads();
         issue_stage(kt + kStages - 1, (kt + kStages - 1) % kStages);
         __builtin_amdgcn_sched_barrier(0);
@@ -254,7 +252,7 @@ __global__ void __launch_bounds__(Tile<kBN>::kThreads, kBN == 128 ? 2 : 1) gemm_
     // operand), so lane l holds acc[i][j][r] = Y[32i + l%32][32j + 8(r/4) + 4(l/32) + r%4]:
     // four consecutive outputs of one token row per r/4.  The token's dequant factor and
     // code sum are per lane.
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the ring's last (dummy) loads
+    wait_vm<0>();  // the ring's last (dummy) loads
     __syncthreads();                     // every wave past its last ring read: the ring is free
     auto outputs = [&](const v16i &c, int q, float f, int cs, int n, float (&y)[4], int (&av)[4])
         __attribute__((always_inline)) {
@@ -422,8 +420,12 @@ hipError_t launch_tiles(const BigParams &p0, const FwdArgs &a, hipStream_t s) {
 #ifndef BL_GEMM_BN
 #define BL_GEMM_BN 0  // 0: choose per shape
 #endif
+#ifndef BL_GEMM_MID
+#define BL_GEMM_MID 1  // 0: never the balanced tiles
+#endif
 
 hipError_t launch_gemm_big(const FwdArgs &a, hipStream_t s) {
+    if (BL_GEMM_MID && BL_GEMM_BN == 0 && gemm_mid_preferred(a.M, a.N, a.K, a.bits)) return launch_gemm_mid(a, s);
     BigParams p;
     p.xq = static_cast<const uint8_t *>(a.xq);
     p.rowsum = a.rowsum;

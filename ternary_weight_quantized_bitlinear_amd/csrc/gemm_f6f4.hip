@@ -74,11 +74,6 @@ struct F6Params {
     int tiles_m;
 };
 
-// s_waitcnt vmcnt(kN) (kN < 64), lgkmcnt and expcnt left open
-template <int kN> __device__ __forceinline__ void wait_vm() {
-    __builtin_amdgcn_s_waitcnt((kN & 0xF) | ((kN >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
 template <int kBN, int kYD, bool kRelu2, bool kBias>
 __global__ void __launch_bounds__(F6Tile<kBN>::kThreads, kBN == 128 ? 2 : 1)
 gemm_f6f4_kernel(F6Params p) {

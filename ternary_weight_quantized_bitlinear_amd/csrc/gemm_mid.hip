@@ -1,0 +1,321 @@
+// Prefill BitLinear forward, balanced tiles: the ternary x int8 contraction of the
+// large-tile kernel (gemm_big.hip) on the gfx950 16 x 16 x 64 int8 matrix cores
+// (v_mfma_i32_16x16x64_i8), int32 accumulation, for shapes where 256-row tiles leave
+// many CUs idle.
+//
+// "BitNet b1.58: The 1-Bit Ternary LLM Architecture Guide", "3. Multiplier-Free
+// Forward Pass & Dequantization": Y = (X~ W~^T) * (gamma / scale_X); "BitNet a4.8
+// Guide", "3. Native Hardware INT4 Tensor Core Mapping": int32 accumulators, Output =
+// acc * (s_x * beta) for 4-bit activations.
+//
+// Block tile 128 tokens x 160 output rows.  A 2048 x 2560 output (the 2B model's down
+// projection at 2048 tokens) is exactly 256 such tiles, one per CU, each 128 x 160 x K:
+// the large-tile kernel's 256 x 128 tiles number 160 there, so 96 CUs would idle and
+// the busy ones would carry 1.6 times the work.  Four waves (2 token halves x 2 row
+// halves), each 64 tokens x 80 rows: 4 x 5 MFMAs of 16 x 16 x 64 per k step, 80
+// accumulator registers.
+//
+// Operands as in the large-tile kernel: the activations arrive prepared (int8 codes,
+// int4 codes widened, in 16-element groups stored 4x4-transposed, plus sum_k q per
+// token); a weight dword (16 codes) splits with a shift and a mask per output dword into
+// the raw fields c+1 in {0,1,2}, in the order of a prepared group; each MFMA accumulates
+// sum x (c+1) and the epilogue subtracts sum_k x per token.  A lane's 16 bytes of either
+// operand are one 16-element group (token or row lane % 16, k group lane / 16), so both
+// operands pair the same k.
+//
+// Memory pipeline: a kStages-deep LDS ring filled by global_load_lds_dwordx4 (activation
+// rows 64 bytes, their four 16-byte chunks XOR-swizzled by row so that the fragment reads
+// of 8 consecutive rows hit distinct banks; weight rows 16 bytes), issued kStages-1 steps
+// ahead; one barrier per k step publishes the landed stage and frees the slot the next
+// DMA refills; the fragments of step k+1 are read while step k's MFMAs run.
+//
+// Requires K % 64 == 0.  Rows past M or N read clamped addresses and are never stored.
+#include "common.hpp"
+
+namespace bl {
+namespace {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+constexpr int TM = 128, TN = 160, BK = 64;
+constexpr int kWaves = 4, kThreads = 64 * kWaves;
+constexpr int WM = 64, WN = 80;            // wave tile (tokens x rows)
+constexpr int FI = WM / 16, FJ = WN / 16;  // 4 x 5 MFMA tiles per wave
+constexpr int kAStage = TM * BK;           // 8 KB
+constexpr int kBStage = TN * 16;           // 2.5 KB
+constexpr int kStageBytes = kAStage + kBStage;
+#ifndef BL_MID_STAGES
+#define BL_MID_STAGES 6
+#endif
+constexpr int kStages = BL_MID_STAGES;
+constexpr int kADma = TM / 16 / kWaves;    // activation DMAs (16 rows x 64 B) per wave
+constexpr int kBRows = TN / kWaves;        // weight rows per wave (one DMA, lanes < 40)
+constexpr int kDma = kADma + 1;            // DMAs per wave per stage
+constexpr size_t kLds = (size_t)kStages * kStageBytes + TM * (sizeof(float) + sizeof(int));
+static_assert(kBRows <= 64, "one weight DMA per wave");
+static_assert((kStages - 2) * kDma < 64, "vmcnt is 6 bits");
+
+struct MidParams {
+    const uint8_t *xq;      // prepared int8 activations [M][K]
+    const int32_t *rowsum;  // sum_k q[m][k]
+    const float *act_scale;
+    int gran;
+    int bits;               // of the codes: selects gamma/s (8) or s*gamma (4)
+    const uint8_t *w;
+    const float *gamma;
+    const float *bias;
+    int M, N, K;
+    void *y;
+    int tiles_m;
+};
+
+__device__ __forceinline__ int a_swz(int row) { return ((row >> 1) & 3) ^ ((row >> 3) & 1); }
+
+template <int kYD, bool kRelu2, bool kBias>
+__global__ void __launch_bounds__(kThreads, 2) gemm_mid_kernel(MidParams p) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    float *s_f = reinterpret_cast<float *>(smem + kStages * kStageBytes);
+    int *s_sum = reinterpret_cast<int *>(s_f + TM);
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    // token blocks of one row block back to back: consecutive blocks (spread over the
+    // XCDs) share the weights, each XCD keeps its few token blocks in its L2
+    const int tile = blockIdx.x;
+    const int tm = tile % p.tiles_m, tn = tile / p.tiles_m;
+    const int m0 = tm * TM, n0 = tn * TN;
+    const int K = p.K, nk = K / BK;
+
+    for (int t = tid; t < TM; t += kThreads) {
+        const int m = m0 + t;
+        float f = 0.0f;
+        int cs = 0;
+        if (m < p.M) {
+            const float s = p.act_scale[p.gran == 1 ? 0 : m];
+            const float g = *p.gamma;
+            f = p.bits == 8 ? g / s : s * g;
+            cs = p.rowsum[m];
+        }
+        s_f[t] = f;
+        s_sum[t] = cs;
+    }
+
+    // ---- one k step into ring slot `slot`: wave w copies activation rows 32w .. 32w+31
+    // (16 rows x 64 B per instruction, lane -> row lane/4, the global chunk that lands at
+    // the lane's swizzled position) and weight rows 40w .. 40w+39 (lanes < 40, 16 B each)
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)smem;
+    const uint8_t *asrc[kADma];
+#pragma unroll
+    for (int q = 0; q < kADma; ++q) {
+        const int row = 16 * (kADma * wave + q) + (lane >> 2);
+        const int chunk = (lane & 3) ^ a_swz(row);
+        asrc[q] = p.xq + (size_t)min(m0 + row, p.M - 1) * K + 16 * chunk;
+    }
+    const uint8_t *bsrc = p.w + (size_t)min(n0 + kBRows * wave + lane, p.N - 1) * (K / 4);
+    auto issue_stage = [&](int kt, int slot) __attribute__((always_inline)) {
+        const int ktc = min(kt, nk - 1);  // past the end: reload the last step (unused)
+        const uint32_t base = lds0 + slot * kStageBytes;
+#pragma unroll
+        for (int q = 0; q < kADma; ++q)
+            lds_dma16_lanes(asrc[q] + (size_t)ktc * BK, base + 16 * (kADma * wave + q) * BK, ~0ull);
+        lds_dma16_lanes(bsrc + (size_t)ktc * (BK / 4), base + kAStage + kBRows * wave * 16,
+                        (1ull << kBRows) - 1);
+    };
+
+    v4i acc[FI][FJ];
+#pragma unroll
+    for (int i = 0; i < FI; ++i)
+#pragma unroll
+        for (int j = 0; j < FJ; ++j) acc[i][j] = v4i{0, 0, 0, 0};
+
+#pragma unroll
+    for (int st = 0; st < kStages - 1; ++st) issue_stage(st, st);
+
+    // ---- fragments of step kt: lane l takes token / row l % 16 of its 16-wide tile and
+    // k group l / 16 (16 bytes of activations, one weight dword)
+    const int r16 = lane & 15, kg = lane >> 4;
+    auto read_a = [&](int kt, v4i (&af)[FI]) __attribute__((always_inline)) {
+        const uint8_t *sa = smem + (kt % kStages) * kStageBytes;
+#pragma unroll
+        for (int i = 0; i < FI; ++i) {
+            const int row = WM * wm + 16 * i + r16;
+            const uint4 q = *reinterpret_cast<const uint4 *>(sa + row * BK + 16 * (kg ^ a_swz(row)));
+            af[i] = v4i{(int)q.x, (int)q.y, (int)q.z, (int)q.w};
+        }
+    };
+    auto read_b = [&](int kt, uint32_t (&bw)[FJ]) __attribute__((always_inline)) {
+        const uint8_t *sb = smem + (kt % kStages) * kStageBytes + kAStage;
+#pragma unroll
+        for (int j = 0; j < FJ; ++j)
+            bw[j] = *reinterpret_cast<const uint32_t *>(sb + (WN * wn + 16 * j + r16) * 16 + 4 * kg);
+    };
+    auto expand = [&](const uint32_t (&bw)[FJ], v4i (&bf)[FJ]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < FJ; ++j)
+            bf[j] = v4i{(int)fields(bw[j], 0), (int)fields(bw[j], 1), (int)fields(bw[j], 2),
+                        (int)fields(bw[j], 3)};
+    };
+
+    // Per k step: the wait for the next stage, the barrier (it also certifies that every
+    // wave is done with the slot the new DMA refills: that stage's fragments were read a
+    // step earlier and used by the MFMAs before the barrier) and the DMA; then the
+    // twenty MFMAs of this step on fragments already in registers, with the next step's
+    // reads and field spreading in their shadow.  Two fragment sets take turns.
+    struct Frag { v4i a[FI]; v4i b[FJ]; };
+    Frag f0, f1;
+    uint32_t bw[FJ];
+    wait_vm<(kStages - 2) * kDma>();
+    __syncthreads();
+    read_b(0, bw);
+    read_a(0, f0.a);
+    expand(bw, f0.b);
+    constexpr int kReads = FI + FJ;
+    constexpr int kMf = FI * FJ;
+    constexpr int kValu = 7 * FJ;
+    constexpr int kValuPer = (kValu + (kMf - kReads) - 1) / (kMf - kReads);
+    auto step = [&](int kt, Frag &cur, Frag &nxt) __attribute__((always_inline)) {
+        wait_vm<(kStages - 3) * kDma>();
+        __syncthreads();
+        issue_stage(kt + kStages - 1, (kt + kStages - 1) % kStages);
+        __builtin_amdgcn_sched_barrier(0);
+        read_b(kt + 1, bw);
+        read_a(kt + 1, nxt.a);
+#pragma unroll
+        for (int i = 0; i < FI; ++i)
+#pragma unroll
+            for (int j = 0; j < FJ; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(cur.b[j], cur.a[i], acc[i][j], 0, 0, 0);
+        expand(bw, nxt.b);
+#pragma unroll
+        for (int t = 0; t < kReads; ++t) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+        }
+#pragma unroll
+        for (int t = 0; t < kMf - kReads; ++t) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);         // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, kValuPer, 0);  // VALU
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+#pragma unroll 1
+    for (int kt = 0; kt + 1 < nk; kt += 2) {
+        step(kt, f0, f1);
+        step(kt + 1, f1, f0);
+    }
+    if (nk & 1) step(nk - 1, f0, f1);
+    wait_vm<0>();  // the ring's last (dummy) loads land before the block's LDS is released
+
+    // ---- epilogue.  The MFMAs compute the transposed tile (weights as the first
+    // operand): lane l holds acc[i][j][r] = Y[16 i + l % 16][16 j + 4 (l / 16) + r], four
+    // consecutive outputs of one token row; its dequant factor and code sum are per lane.
+    const int ml = WM * wm + r16;
+#pragma unroll
+    for (int i = 0; i < FI; ++i) {
+        const int m = m0 + ml + 16 * i;
+        const float f = s_f[ml + 16 * i];
+        const int cs = s_sum[ml + 16 * i];
+        if (m >= p.M) continue;
+#pragma unroll
+        for (int j = 0; j < FJ; ++j) {
+            const int n = n0 + WN * wn + 16 * j + 4 * kg;
+            const size_t idx = (size_t)m * p.N + n;
+            float y[4];
+            int av[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                av[t] = acc[i][j][t] - cs;
+                float v = __fmul_rn((float)av[t], f);
+                if (kBias) v = __fadd_rn(v, n + t < p.N ? p.bias[n + t] : 0.0f);
+                if (kRelu2) {
+                    const float rr = v > 0.0f ? v : 0.0f;
+                    v = __fmul_rn(rr, rr);
+                }
+                y[t] = v;
+            }
+            if ((p.N & 3) == 0 && n + 3 < p.N) {
+                if (kYD == 2) {
+                    *reinterpret_cast<int4 *>(static_cast<int32_t *>(p.y) + idx) =
+                        make_int4(av[0], av[1], av[2], av[3]);
+                } else if (kYD == 1) {
+                    typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+                    const bf2 lo = {(__bf16)y[0], (__bf16)y[1]};
+                    const bf2 hi = {(__bf16)y[2], (__bf16)y[3]};
+                    *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(p.y) + idx) =
+                        make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+                } else {
+                    *reinterpret_cast<float4 *>(static_cast<float *>(p.y) + idx) =
+                        make_float4(y[0], y[1], y[2], y[3]);
+                }
+            } else {
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    if (n + t >= p.N) continue;
+                    if (kYD == 2) static_cast<int32_t *>(p.y)[idx + t] = av[t];
+                    else if (kYD == 1) static_cast<uint16_t *>(p.y)[idx + t] = (uint16_t)to_bf16_bits(y[t]);
+                    else static_cast<float *>(p.y)[idx + t] = y[t];
+                }
+            }
+        }
+    }
+}
+
+}  // namespace
+
+// The balanced tiles pay off where they take at most about three quarters of the work
+// per CU that the large-tile kernel's launch would: per CU, the tiles of one round times
+// their area (256 x 256 with one 8-wave block per CU; 256 x 128 with two 4-wave blocks,
+// when fewer than 128 of the wide tiles exist).
+bool gemm_mid_preferred(int64_t M, int64_t N, int64_t K, int bits) {
+    if ((bits != 8 && bits != 4) || K % BK != 0 || M < 1 || N < 1) return false;
+    constexpr int64_t kCUs = 256;
+    const int64_t mid = ((M + TM - 1) / TM) * ((N + TN - 1) / TN);
+    const int64_t mid_work = ((mid + kCUs - 1) / kCUs) * TM * TN;
+    const int64_t wide = ((M + 255) / 256) * ((N + 255) / 256);
+    int64_t big_work;
+    if (wide >= 128) {
+        big_work = ((wide + kCUs - 1) / kCUs) * 256 * 256;
+    } else {
+        const int64_t narrow = ((M + 255) / 256) * ((N + 127) / 128);
+        big_work = ((narrow + kCUs - 1) / kCUs) * 256 * 128;
+    }
+    return 4 * mid_work <= 3 * big_work;
+}
+
+hipError_t launch_gemm_mid(const FwdArgs &a, hipStream_t s) {
+    MidParams p;
+    p.xq = static_cast<const uint8_t *>(a.xq);
+    p.rowsum = a.rowsum;
+    p.act_scale = a.act_scale;
+    p.gran = a.gran;
+    p.bits = a.bits;
+    p.w = a.w;
+    p.gamma = a.gamma;
+    p.bias = a.bias;
+    p.M = (int)a.M;
+    p.N = (int)a.N;
+    p.K = (int)a.K;
+    p.y = a.y;
+    p.tiles_m = (int)((a.M + TM - 1) / TM);
+    const int tiles_n = (int)((a.N + TN - 1) / TN);
+    const dim3 grid((unsigned)(p.tiles_m * tiles_n)), block(kThreads);
+    const int key = a.y_dtype * 4 + (a.epi == 1 ? 2 : 0) + (a.bias ? 1 : 0);
+    switch (key) {
+#define BL_CASE(YD, R, B)                                                                        \
+    case YD * 4 + (R ? 2 : 0) + (B ? 1 : 0): {                                                    \
+        hipError_t e = allow_lds((const void *)gemm_mid_kernel<YD, R, B>, kLds);                  \
+        if (e != hipSuccess) return e;                                                            \
+        hipLaunchKernelGGL((gemm_mid_kernel<YD, R, B>), grid, block, kLds, s, p);                 \
+        break;                                                                                    \
+    }
+        BL_CASE(0, false, false) BL_CASE(0, false, true) BL_CASE(0, true, false) BL_CASE(0, true, true)
+        BL_CASE(1, false, false) BL_CASE(1, false, true) BL_CASE(1, true, false) BL_CASE(1, true, true)
+        BL_CASE(2, false, false)
+#undef BL_CASE
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace bl
