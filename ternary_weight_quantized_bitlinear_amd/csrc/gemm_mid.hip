@@ -24,10 +24,17 @@
 // operands pair the same k.
 //
 // Memory pipeline: a kStages-deep LDS ring filled by global_load_lds_dwordx4 (activation
-// rows 64 bytes, their four 16-byte chunks XOR-swizzled by row so that the fragment reads
-// of 8 consecutive rows hit distinct banks; weight rows 16 bytes), issued kStages-1 steps
-// ahead; one barrier per k step publishes the landed stage and frees the slot the next
-// DMA refills; the fragments of step k+1 are read while step k's MFMAs run.
+// rows of 64 bytes, their 16-byte chunks XOR-swizzled by row so that the fragment reads
+// of 8 consecutive rows hit distinct banks; weight rows 16 bytes), issued kStages-1
+// stages ahead; one barrier per stage publishes the landed stage and frees the slot the
+// next DMA refills; the fragments of the next k step are read while this one's MFMAs run.
+//
+// Where K % 128 == 0 the block has two such groups of four waves (two waves per SIMD,
+// so one wave's MFMAs cover the other's waits), each with its own ring, on alternate
+// 64-wide k steps of the same tile; the second group's int32 sums are added to the
+// first's through LDS before the epilogue.  On the 2B down projection this measured
+// 48-50 us, against 51-52 us for one group with two k steps per stage and 54-55 us for
+// one group with one.
 //
 // Requires K % 64 == 0.  Rows past M or N read clamped addresses and are never stored.
 #include "common.hpp"
@@ -37,23 +44,36 @@ namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 
-constexpr int TM = 128, TN = 160, BK = 64;
+constexpr int TM = 128, TN = 160;
 constexpr int kWaves = 4, kThreads = 64 * kWaves;
 constexpr int WM = 64, WN = 80;            // wave tile (tokens x rows)
 constexpr int FI = WM / 16, FJ = WN / 16;  // 4 x 5 MFMA tiles per wave
-constexpr int kAStage = TM * BK;           // 8 KB
-constexpr int kBStage = TN * 16;           // 2.5 KB
-constexpr int kStageBytes = kAStage + kBStage;
-#ifndef BL_MID_STAGES
-#define BL_MID_STAGES 6
+#ifndef BL_MID_STAGES1
+#define BL_MID_STAGES1 6  // ring depth with one k step per stage
 #endif
-constexpr int kStages = BL_MID_STAGES;
-constexpr int kADma = TM / 16 / kWaves;    // activation DMAs (16 rows x 64 B) per wave
-constexpr int kBRows = TN / kWaves;        // weight rows per wave (one DMA, lanes < 40)
-constexpr int kDma = kADma + 1;            // DMAs per wave per stage
-constexpr size_t kLds = (size_t)kStages * kStageBytes + TM * (sizeof(float) + sizeof(int));
-static_assert(kBRows <= 64, "one weight DMA per wave");
-static_assert((kStages - 2) * kDma < 64, "vmcnt is 6 bits");
+#ifndef BL_MID_STAGES2
+#define BL_MID_STAGES2 4  // with two
+#endif
+#ifndef BL_MID_MODE
+#define BL_MID_MODE 2  // where K % 128 == 0: 1 two k steps per stage, 2 the k split
+#endif
+constexpr int kBRows = TN / kWaves;        // weight rows per wave and DMA (lanes < 40)
+static_assert(kBRows <= 64, "one weight DMA per wave and k half");
+
+// kSub 64-wide k steps per LDS stage (one barrier per stage): 1 where K % 128 != 0
+template <int kSub> struct MidTile {
+    static constexpr int BK = 64 * kSub;
+    static constexpr int kAStage = TM * BK;        // 8 or 16 KB
+    static constexpr int kBStage = TN * 16 * kSub;  // 2.5 or 5 KB: kSub planes of 16 B rows
+    static constexpr int kStageBytes = kAStage + kBStage;
+    static constexpr int kStages = kSub == 1 ? BL_MID_STAGES1 : BL_MID_STAGES2;
+    static constexpr int kARows = 1024 / BK;       // activation rows per 1 KB DMA
+    static constexpr int kADma = kAStage / 1024 / kWaves;
+    static constexpr int kDma = kADma + kSub;      // DMAs per wave per stage
+    static constexpr size_t kLds = (size_t)kStages * kStageBytes + TM * (sizeof(float) + sizeof(int));
+    static_assert((kStages - 2) * kDma < 64, "vmcnt is 6 bits");
+    static_assert(kLds <= 160 * 1024, "LDS");
+};
 
 struct MidParams {
     const uint8_t *xq;      // prepared int8 activations [M][K]
@@ -69,25 +89,38 @@ struct MidParams {
     int tiles_m;
 };
 
-__device__ __forceinline__ int a_swz(int row) { return ((row >> 1) & 3) ^ ((row >> 3) & 1); }
+// position of 16-byte chunk c within activation row `row` of the stage: rows of 64 bytes
+// (kSub = 1) or 128 bytes (kSub = 2); 8 consecutive rows read at one chunk hit 8 distinct
+// 16-byte bank groups
+template <int kSub> __device__ __forceinline__ int a_pos(int row, int c) {
+    return kSub == 1 ? c ^ ((row >> 1) & 3) ^ ((row >> 3) & 1) : c ^ (row & 7);
+}
 
-template <int kYD, bool kRelu2, bool kBias>
-__global__ void __launch_bounds__(kThreads, 2) gemm_mid_kernel(MidParams p) {
+// kSplit = 2: two groups of four waves (two waves per SIMD), each with a ring of its
+// own, take alternate stages of the same tile (group g the stages g, g + 2, ...); the
+// second group's accumulators are added to the first's through LDS at the end.
+template <int kSub, int kSplit, int kYD, bool kRelu2, bool kBias>
+__global__ void __launch_bounds__(kThreads * kSplit, kSplit == 1 ? 2 : 1) gemm_mid_kernel(MidParams p) {
+    using T = MidTile<kSub>;
+    constexpr int BK = T::BK, kAStage = T::kAStage, kStageBytes = T::kStageBytes;
+    constexpr int kStages = T::kStages, kADma = T::kADma, kDma = T::kDma, kARows = T::kARows;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    float *s_f = reinterpret_cast<float *>(smem + kStages * kStageBytes);
+    float *s_f = reinterpret_cast<float *>(smem + kSplit * kStages * kStageBytes);
     int *s_sum = reinterpret_cast<int *>(s_f + TM);
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 1, wn = wave & 1;
+    const int grp = wave >> 2, lw = wave & 3;  // group, and the wave within it
+    const int wm = lw >> 1, wn = lw & 1;
+    uint8_t *ring = smem + grp * kStages * kStageBytes;
     // token blocks of one row block back to back: consecutive blocks (spread over the
     // XCDs) share the weights, each XCD keeps its few token blocks in its L2
     const int tile = blockIdx.x;
     const int tm = tile % p.tiles_m, tn = tile / p.tiles_m;
     const int m0 = tm * TM, n0 = tn * TN;
-    const int K = p.K, nk = K / BK;
+    const int K = p.K, nk = K / BK / kSplit;  // stages of this group (K % (kSplit BK) == 0)
 
-    for (int t = tid; t < TM; t += kThreads) {
+    for (int t = tid; t < TM; t += kThreads * kSplit) {
         const int m = m0 + t;
         float f = 0.0f;
         int cs = 0;
@@ -101,26 +134,31 @@ __global__ void __launch_bounds__(kThreads, 2) gemm_mid_kernel(MidParams p) {
         s_sum[t] = cs;
     }
 
-    // ---- one k step into ring slot `slot`: wave w copies activation rows 32w .. 32w+31
-    // (16 rows x 64 B per instruction, lane -> row lane/4, the global chunk that lands at
-    // the lane's swizzled position) and weight rows 40w .. 40w+39 (lanes < 40, 16 B each)
-    const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)smem;
+    // ---- one stage into ring slot `slot`: wave w copies activation rows 32w .. 32w+31
+    // (kARows rows per 1 KB instruction; lane -> row lane / (4 kSub), and the global chunk
+    // that belongs at the lane's position) and weight rows 40w .. 40w+39 of each k plane
+    // (lanes < 40, 16 B each)
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)ring;
     const uint8_t *asrc[kADma];
 #pragma unroll
     for (int q = 0; q < kADma; ++q) {
-        const int row = 16 * (kADma * wave + q) + (lane >> 2);
-        const int chunk = (lane & 3) ^ a_swz(row);
+        const int row = kARows * (kADma * lw + q) + lane / (4 * kSub);
+        const int pos = lane % (4 * kSub);
+        const int chunk = a_pos<kSub>(row, pos);  // the positions form an involution
         asrc[q] = p.xq + (size_t)min(m0 + row, p.M - 1) * K + 16 * chunk;
     }
-    const uint8_t *bsrc = p.w + (size_t)min(n0 + kBRows * wave + lane, p.N - 1) * (K / 4);
+    const uint8_t *bsrc = p.w + (size_t)min(n0 + kBRows * lw + lane, p.N - 1) * (K / 4);
+    // stage kt of this group: k columns [BK (kSplit kt + grp), + BK)
     auto issue_stage = [&](int kt, int slot) __attribute__((always_inline)) {
-        const int ktc = min(kt, nk - 1);  // past the end: reload the last step (unused)
+        const int ktc = kSplit * min(kt, nk - 1) + grp;  // past the end: the last one again (unused)
         const uint32_t base = lds0 + slot * kStageBytes;
 #pragma unroll
         for (int q = 0; q < kADma; ++q)
-            lds_dma16_lanes(asrc[q] + (size_t)ktc * BK, base + 16 * (kADma * wave + q) * BK, ~0ull);
-        lds_dma16_lanes(bsrc + (size_t)ktc * (BK / 4), base + kAStage + kBRows * wave * 16,
-                        (1ull << kBRows) - 1);
+            lds_dma16_lanes(asrc[q] + (size_t)ktc * BK, base + 1024 * (kADma * lw + q), ~0ull);
+#pragma unroll
+        for (int h = 0; h < kSub; ++h)
+            lds_dma16_lanes(bsrc + (size_t)ktc * (BK / 4) + 16 * h,
+                            base + kAStage + (h * TN + kBRows * lw) * 16, (1ull << kBRows) - 1);
     };
 
     v4i acc[FI][FJ];
@@ -132,20 +170,21 @@ __global__ void __launch_bounds__(kThreads, 2) gemm_mid_kernel(MidParams p) {
 #pragma unroll
     for (int st = 0; st < kStages - 1; ++st) issue_stage(st, st);
 
-    // ---- fragments of step kt: lane l takes token / row l % 16 of its 16-wide tile and
-    // k group l / 16 (16 bytes of activations, one weight dword)
+    // ---- fragments of 64-wide k step `sub` of stage kt: lane l takes token / row l % 16
+    // of its 16-wide tile and k group l / 16 (16 bytes of activations, one weight dword)
     const int r16 = lane & 15, kg = lane >> 4;
-    auto read_a = [&](int kt, v4i (&af)[FI]) __attribute__((always_inline)) {
-        const uint8_t *sa = smem + (kt % kStages) * kStageBytes;
+    auto read_a = [&](int kt, int sub, v4i (&af)[FI]) __attribute__((always_inline)) {
+        const uint8_t *sa = ring + (kt % kStages) * kStageBytes;
 #pragma unroll
         for (int i = 0; i < FI; ++i) {
             const int row = WM * wm + 16 * i + r16;
-            const uint4 q = *reinterpret_cast<const uint4 *>(sa + row * BK + 16 * (kg ^ a_swz(row)));
+            const uint4 q = *reinterpret_cast<const uint4 *>(sa + row * BK +
+                                                              16 * a_pos<kSub>(row, 4 * sub + kg));
             af[i] = v4i{(int)q.x, (int)q.y, (int)q.z, (int)q.w};
         }
     };
-    auto read_b = [&](int kt, uint32_t (&bw)[FJ]) __attribute__((always_inline)) {
-        const uint8_t *sb = smem + (kt % kStages) * kStageBytes + kAStage;
+    auto read_b = [&](int kt, int sub, uint32_t (&bw)[FJ]) __attribute__((always_inline)) {
+        const uint8_t *sb = ring + (kt % kStages) * kStageBytes + kAStage + sub * TN * 16;
 #pragma unroll
         for (int j = 0; j < FJ; ++j)
             bw[j] = *reinterpret_cast<const uint32_t *>(sb + (WN * wn + 16 * j + r16) * 16 + 4 * kg);
@@ -157,30 +196,34 @@ __global__ void __launch_bounds__(kThreads, 2) gemm_mid_kernel(MidParams p) {
                         (int)fields(bw[j], 3)};
     };
 
-    // Per k step: the wait for the next stage, the barrier (it also certifies that every
-    // wave is done with the slot the new DMA refills: that stage's fragments were read a
-    // step earlier and used by the MFMAs before the barrier) and the DMA; then the
-    // twenty MFMAs of this step on fragments already in registers, with the next step's
-    // reads and field spreading in their shadow.  Two fragment sets take turns.
+    // Per stage: the wait for the next stage, the barrier (it also certifies that every
+    // wave is done with the slot the new DMA refills: that stage's fragments were read
+    // and used by the MFMAs before the barrier) and the DMA; then, per 64-wide k step,
+    // twenty MFMAs on fragments already in registers, with the following step's reads
+    // (the next stage's first, after the last step of a stage) and field spreading in
+    // their shadow.  Two fragment sets take turns.
     struct Frag { v4i a[FI]; v4i b[FJ]; };
     Frag f0, f1;
     uint32_t bw[FJ];
     wait_vm<(kStages - 2) * kDma>();
     __syncthreads();
-    read_b(0, bw);
-    read_a(0, f0.a);
+    read_b(0, 0, bw);
+    read_a(0, 0, f0.a);
     expand(bw, f0.b);
     constexpr int kReads = FI + FJ;
     constexpr int kMf = FI * FJ;
     constexpr int kValu = 7 * FJ;
     constexpr int kValuPer = (kValu + (kMf - kReads) - 1) / (kMf - kReads);
-    auto step = [&](int kt, Frag &cur, Frag &nxt) __attribute__((always_inline)) {
-        wait_vm<(kStages - 3) * kDma>();
+    auto sync = [&](int kt) __attribute__((always_inline)) {
+        wait_vm<(kStages - 3) * kDma>();  // this wave's copies of stage kt + 1 landed
         __syncthreads();
         issue_stage(kt + kStages - 1, (kt + kStages - 1) % kStages);
         __builtin_amdgcn_sched_barrier(0);
-        read_b(kt + 1, bw);
-        read_a(kt + 1, nxt.a);
+    };
+    // the MFMAs of `cur`; meanwhile step `rsub` of stage `rkt` into `nxt`
+    auto sub = [&](int rkt, int rsub, Frag &cur, Frag &nxt) __attribute__((always_inline)) {
+        read_b(rkt, rsub, bw);
+        read_a(rkt, rsub, nxt.a);
 #pragma unroll
         for (int i = 0; i < FI; ++i)
 #pragma unroll
@@ -199,13 +242,48 @@ __global__ void __launch_bounds__(kThreads, 2) gemm_mid_kernel(MidParams p) {
         }
         __builtin_amdgcn_sched_barrier(0);
     };
+    if constexpr (kSub == 2) {
 #pragma unroll 1
-    for (int kt = 0; kt + 1 < nk; kt += 2) {
-        step(kt, f0, f1);
-        step(kt + 1, f1, f0);
+        for (int kt = 0; kt < nk; ++kt) {
+            sync(kt);
+            sub(kt, 1, f0, f1);
+            sub(kt + 1, 0, f1, f0);
+        }
+    } else {
+#pragma unroll 1
+        for (int kt = 0; kt + 1 < nk; kt += 2) {
+            sync(kt);
+            sub(kt + 1, 0, f0, f1);
+            sync(kt + 1);
+            sub(kt + 2, 0, f1, f0);
+        }
+        if (nk & 1) {
+            sync(nk - 1);
+            sub(nk, 0, f0, f1);
+        }
     }
-    if (nk & 1) step(nk - 1, f0, f1);
     wait_vm<0>();  // the ring's last (dummy) loads land before the block's LDS is released
+    if constexpr (kSplit == 2) {
+        // the second group's sums into the first's: lane-wise, through the (now free) rings
+        __syncthreads();
+        int *red = reinterpret_cast<int *>(smem) + (lw * FI * FJ * 4) * 64 + lane;
+        if (grp == 1) {
+#pragma unroll
+            for (int i = 0; i < FI; ++i)
+#pragma unroll
+                for (int j = 0; j < FJ; ++j)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) red[((i * FJ + j) * 4 + r) * 64] = acc[i][j][r];
+        }
+        __syncthreads();
+        if (grp == 1) return;
+#pragma unroll
+        for (int i = 0; i < FI; ++i)
+#pragma unroll
+            for (int j = 0; j < FJ; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[i][j][r] += red[((i * FJ + j) * 4 + r) * 64];
+    }
 
     // ---- epilogue.  The MFMAs compute the transposed tile (weights as the first
     // operand): lane l holds acc[i][j][r] = Y[16 i + l % 16][16 j + 4 (l / 16) + r], four
@@ -268,7 +346,7 @@ __global__ void __launch_bounds__(kThreads, 2) gemm_mid_kernel(MidParams p) {
 // their area (256 x 256 with one 8-wave block per CU; 256 x 128 with two 4-wave blocks,
 // when fewer than 128 of the wide tiles exist).
 bool gemm_mid_preferred(int64_t M, int64_t N, int64_t K, int bits) {
-    if ((bits != 8 && bits != 4) || K % BK != 0 || M < 1 || N < 1) return false;
+    if ((bits != 8 && bits != 4) || K % 64 != 0 || M < 1 || N < 1) return false;
     constexpr int64_t kCUs = 256;
     const int64_t mid = ((M + TM - 1) / TM) * ((N + TN - 1) / TN);
     const int64_t mid_work = ((mid + kCUs - 1) / kCUs) * TM * TN;
@@ -299,20 +377,30 @@ hipError_t launch_gemm_mid(const FwdArgs &a, hipStream_t s) {
     p.y = a.y;
     p.tiles_m = (int)((a.M + TM - 1) / TM);
     const int tiles_n = (int)((a.N + TN - 1) / TN);
-    const dim3 grid((unsigned)(p.tiles_m * tiles_n)), block(kThreads);
+    const dim3 grid((unsigned)(p.tiles_m * tiles_n));
     const int key = a.y_dtype * 4 + (a.epi == 1 ? 2 : 0) + (a.bias ? 1 : 0);
+    // K % 128 == 0: two 64-wide k steps per stage (4 waves) or the k split (8 waves)
+    const int mode = a.K % 128 == 0 ? BL_MID_MODE : 0;
     switch (key) {
-#define BL_CASE(YD, R, B)                                                                        \
-    case YD * 4 + (R ? 2 : 0) + (B ? 1 : 0): {                                                    \
-        hipError_t e = allow_lds((const void *)gemm_mid_kernel<YD, R, B>, kLds);                  \
+#define BL_LAUNCH(SUB, SPLIT, YD, R, B)                                                          \
+    {                                                                                             \
+        constexpr size_t lds = SPLIT * MidTile<SUB>::kStages * MidTile<SUB>::kStageBytes + TM * 8; \
+        hipError_t e = allow_lds((const void *)gemm_mid_kernel<SUB, SPLIT, YD, R, B>, lds);       \
         if (e != hipSuccess) return e;                                                            \
-        hipLaunchKernelGGL((gemm_mid_kernel<YD, R, B>), grid, block, kLds, s, p);                 \
-        break;                                                                                    \
+        hipLaunchKernelGGL((gemm_mid_kernel<SUB, SPLIT, YD, R, B>), grid, dim3(kThreads * SPLIT), \
+                           lds, s, p);                                                            \
     }
+#define BL_CASE(YD, R, B)                                                                        \
+    case YD * 4 + (R ? 2 : 0) + (B ? 1 : 0):                                                      \
+        if (mode == 1) BL_LAUNCH(2, 1, YD, R, B)                                                  \
+        else if (mode == 2) BL_LAUNCH(1, 2, YD, R, B)                                             \
+        else BL_LAUNCH(1, 1, YD, R, B)                                                            \
+        break;
         BL_CASE(0, false, false) BL_CASE(0, false, true) BL_CASE(0, true, false) BL_CASE(0, true, true)
         BL_CASE(1, false, false) BL_CASE(1, false, true) BL_CASE(1, true, false) BL_CASE(1, true, true)
         BL_CASE(2, false, false)
 #undef BL_CASE
+#undef BL_LAUNCH
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -7,8 +7,9 @@ whose full int32 accumulators test_parity_gpu.py checks).
 "BitNet b1.58: The 1-Bit Ternary LLM Architecture Guide", "3. Multiplier-Free Forward
 Pass & Dequantization": int32 accumulators and every output bit-exact against the
 oracle, element by element: ragged M and N (partial tiles in both directions), one k
-step, odd and even numbers of them, more tiles than CUs; every epilogue and output
-type; per-token and per-tensor scales."""
+step, odd and even numbers of them, K a multiple of 128 (two k steps per LDS stage) or
+not, more tiles than CUs; every epilogue and output type; per-token and per-tensor
+scales."""
 from __future__ import annotations
 
 import numpy as np
@@ -36,15 +37,17 @@ def test_mid_shapes(M, K, N, fused):
 @pytest.mark.parametrize("epi", [None, "relu2"])
 @pytest.mark.parametrize("ydt", ["f32", "bf16"])
 @pytest.mark.parametrize("with_bias", [False, True])
-def test_mid_variants(gran, epi, ydt, with_bias):
-    _check_forward(300, 320, 260, 8, gran, epi, ydt, with_bias, False, sampled=False)
+@pytest.mark.parametrize("K", [320, 256])
+def test_mid_variants(gran, epi, ydt, with_bias, K):
+    _check_forward(300, K, 260, 8, gran, epi, ydt, with_bias, False, sampled=False)
 
 
-def test_mid_more_tiles_than_cus():
+@pytest.mark.parametrize("K", [320, 384])
+def test_mid_more_tiles_than_cus(K):
     # 17 x 25 = 425 tiles: two blocks on some CUs; outputs sampled, then the full int32
     # accumulators against a float64 product of the oracle's codes (exact: integers
     # below 2^53)
-    M, K, N = 2100, 320, 4000
+    M, N = 2100, 4000
     _check_forward(M, K, N, 8, "token", "relu2", "bf16", True, True, x_dtype="bf16",
                    kind="ternary", sampled=True)
     W, X = _layer(M, K, N, 0, "ternary")
