@@ -170,13 +170,22 @@ __global__ void __launch_bounds__(Tile<kBN>::kThreads, kBN == 128 ? 2 : 1) gemm_
             af[i] = v4i{(int)q.x, (int)q.y, (int)q.z, (int)q.w};
         }
     };
-    auto read_b = [&](int kt, int s, uint32_t (&bw)[NJ]) __attribute__((always_inline)) {
+    // Weight rows are read whole, once per k step (16 bytes: the dwords of both
+    // sub-steps and both k groups): 16 lanes at 16-byte steps cover the LDS banks once,
+    // where 32 lanes reading one dword each at that step would hit every bank four times.
+    // Sub-step s of lane (row, kg) then takes dword 2s + kg.
+    auto read_b = [&](int kt, uint4 (&qb)[NJ]) __attribute__((always_inline)) {
         const uint8_t *sb = smem + (kt % kStages) * kStageBytes + kAStage;
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
             const int row = WN * wn + 32 * j + r32;
-            bw[j] = *reinterpret_cast<const uint32_t *>(sb + row * 16 + 4 * (2 * s + kg));
+            qb[j] = *reinterpret_cast<const uint4 *>(sb + row * 16);
         }
+    };
+    auto pick_b = [&](const uint4 (&qb)[NJ], int s, uint32_t (&bw)[NJ]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+            bw[j] = s == 0 ? (kg ? qb[j].y : qb[j].x) : (kg ? qb[j].w : qb[j].z);
     };
     auto expand_b = [&](const uint32_t (&bw)[NJ], v4i (&bf)[NJ]) __attribute__((always_inline)) {
 #pragma unroll
@@ -203,27 +212,31 @@ __global__ void __launch_bounds__(Tile<kBN>::kThreads, kBN == 128 ? 2 : 1) gemm_
     __syncthreads();
     v4i a0[4], b0[NJ], a1[4], b1[NJ];
     uint32_t bw[NJ];
-    // per sub-step: 4 NJ MFMAs, 4 + NJ fragment reads, 7 NJ VALU of field extraction
+    uint4 qb[NJ];
+    // per k step: 8 NJ MFMAs, 8 + NJ fragment reads (4 for sub-step 1 in phase 1, 4 + NJ
+    // for the next step's sub-step 0 in phase 3), 8 NJ VALU per sub-step of dword choice
+    // and field extraction
     constexpr int kReads = 4 + NJ;
     constexpr int kMf = 4 * NJ;
-    constexpr int kValuPer = (7 * NJ + (kMf - kReads) - 1) / (kMf - kReads);
+    constexpr int kValuPer = (8 * NJ + (kMf - 4) - 1) / (kMf - 4);
     read_a(0, 0, a0);
-    read_b(0, 0, bw);
+    read_b(0, qb);
+    pick_b(qb, 0, bw);
     expand_b(bw, b0);
 #pragma unroll 1
     for (int kt = 0; kt < nk; ++kt) {
         // phase 1: sub-step 0 MFMAs; reads and field extraction of sub-step 1
         read_a(kt, 1, a1);
-        read_b(kt, 1, bw);
+        pick_b(qb, 1, bw);
         mfmas(a0, b0, 0, 4);
         expand_b(bw, b1);
 #pragma unroll
-        for (int t = 0; t < kReads; ++t) {
+        for (int t = 0; t < 4; ++t) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
         }
 #pragma unroll
-        for (int t = 0; t < kMf - kReads; ++t) {
+        for (int t = 0; t < kMf - 4; ++t) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);        // MFMA
             __builtin_amdgcn_sched_group_barrier(0x002, kValuPer, 0);  // VALU
         }
@@ -237,7 +250,7 @@ __global__ void __launch_bounds__(Tile<kBN>::kThreads, kBN == 128 ? 2 : 1) gemm_
         __builtin_amdgcn_sched_barrier(0);
         // phase 3: rest of sub-step 1; reads of the next step's sub-step 0
         read_a(kt + 1, 0, a0);
-        read_b(kt + 1, 0, bw);
+        read_b(kt + 1, qb);
         mfmas(a1, b1, 2, 2);
 #pragma unroll
         for (int t = 0; t < 2 * NJ; ++t) {
@@ -245,6 +258,7 @@ __global__ void __launch_bounds__(Tile<kBN>::kThreads, kBN == 128 ? 2 : 1) gemm_
             __builtin_amdgcn_sched_group_barrier(0x100, (kReads + 2 * NJ - 1) / (2 * NJ), 0);  // LDS read
         }
         __builtin_amdgcn_sched_barrier(0);
+        pick_b(qb, 0, bw);
         expand_b(bw, b0);
     }
 
