@@ -47,6 +47,12 @@ constexpr int kADma = kAStage / 1024;                // 12 DMAs of 64 lanes x 16
 #ifndef BL_F6_STAGES
 #define BL_F6_STAGES 4
 #endif
+#ifndef BL_F6_MID
+#define BL_F6_MID 1        // 0: never the balanced tiles
+#endif
+#ifndef BL_F6_MID_SPLIT
+#define BL_F6_MID_SPLIT 1  // where K % 256 == 0: two wave groups on alternate stages
+#endif
 
 template <int kBN> struct F6Tile {
     static constexpr int kWaves = kBN / 32;          // 4 token waves x BN/128 row waves
@@ -361,6 +367,295 @@ hipError_t launch_f6_tiles(const F6Params &p0, const FwdArgs &a, hipStream_t s) 
     return hipGetLastError();
 }
 
+
+// ---------------------------------------------------------------- balanced tiles
+// The FP6 x FP4 contraction in 128 x 160 tiles on the 16 x 16 x 128 scaled MFMA, for
+// shapes whose 256-row tiles leave CUs idle (the 2B down projection at 2048 tokens:
+// 256 tiles, one per CU, against 160 of 256 x 128).  The int8 kernel of gemm_mid.hip in
+// FP6 form: four waves of 64 tokens x 80 rows (4 x 5 MFMAs per 128-wide k stage),
+// and where K % 256 == 0 two such groups (two waves per SIMD), each with its own LDS
+// ring, on alternate stages, summed through LDS before the epilogue.
+//
+// Operands.  A stage is 128 k: the tile's four 32-token FP6 blocks of two 64-k steps
+// (12 KB, two contiguous 6 KB runs in global memory) and the 160 weight rows' codes
+// as two 16-byte planes (one per 64-k half).  Lane l of a 16 x 16 x 128 operand holds
+// row l % 16 and 32-k chunk l / 16: for activations that is slot (row within the
+// 32-token block) + 32 (chunk % 2) of block (chunk / 2), 8 + 16 bytes as the prepare
+// pass laid them out; for weights 8 bytes of plane chunk / 2 at byte 8 (chunk % 2)
+// of the row, spread into FP4 nibbles as in the 256-row kernel.
+constexpr int kMTM = 128, kMTN = 160;
+constexpr int kMWaves = 4;
+constexpr int kMAStage = 2 * 4 * kBlockBytes;     // 12 KB
+constexpr int kMBPlane = kMTN * 16;                // 2.5 KB
+constexpr int kMStageBytes = kMAStage + 2 * kMBPlane;
+#ifndef BL_F6_MID_STAGES
+#define BL_F6_MID_STAGES 4
+#endif
+constexpr int kMStages = BL_F6_MID_STAGES;
+constexpr int kMBRows = kMTN / kMWaves;            // 40 weight rows per wave and plane
+constexpr int kMDma = 3 + 2;                       // per wave and stage: 3 x 1 KB of blocks, 2 planes
+static_assert((kMStages - 2) * kMDma < 64, "vmcnt is 6 bits");
+
+template <int kSplit, int kYD, bool kRelu2, bool kBias>
+__global__ void __launch_bounds__(64 * kMWaves * kSplit, kSplit == 1 ? 2 : 1)
+gemm_f6f4_mid_kernel(F6Params p) {
+    typedef float v4f __attribute__((ext_vector_type(4)));
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    float *s_f = reinterpret_cast<float *>(smem + kSplit * kMStages * kMStageBytes);
+    int *s_sum = reinterpret_cast<int *>(s_f + kMTM);
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = wave >> 2, lw = wave & 3;
+    const int wm = lw >> 1, wn = lw & 1;
+    uint8_t *ring = smem + grp * kMStages * kMStageBytes;
+    const int tile = blockIdx.x;
+    const int tm = tile % p.tiles_m, tn = tile / p.tiles_m;
+    const int m0 = tm * kMTM, n0 = tn * kMTN;
+    const int K = p.K, nk = K / 128 / kSplit;  // stages of this group
+
+    for (int t = tid; t < kMTM; t += 64 * kMWaves * kSplit) {
+        const int m = m0 + t;
+        float f = 0.0f;
+        int cs = 0;
+        if (m < p.M) {
+            f = p.act_scale[p.gran == 1 ? 0 : m] * *p.gamma;
+            cs = p.rowsum[m];
+        }
+        s_f[t] = f;
+        s_sum[t] = cs;
+    }
+
+    // stage kt of this group = 128-wide k step kSplit kt + grp.  Wave w copies 1 KB
+    // pieces 3w .. 3w+2 of the two 6 KB activation runs and weight rows 40w .. 40w+39
+    // of both planes (lanes < 40)
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)ring;
+    const uint8_t *asrc[3];
+    uint32_t adst[3];
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+        const int u = 3 * lw + i, kb2 = u / 6, part = u % 6;
+        asrc[i] = p.xp + ((size_t)kb2 * p.mb_pad + 4 * (size_t)tm) * kBlockBytes + 1024 * part + 16 * lane;
+        adst[i] = kb2 * 4 * kBlockBytes + 1024 * part;
+    }
+    const uint8_t *bsrc = p.w + (size_t)min(n0 + kMBRows * lw + lane, p.N - 1) * (K / 4);
+    const size_t astep = (size_t)2 * p.mb_pad * kBlockBytes;  // one 128-wide k step of blocks
+    auto issue_stage = [&](int kt, int slot) __attribute__((always_inline)) {
+        const int ktc = kSplit * min(kt, nk - 1) + grp;  // past the end: the last one again (unused)
+        const uint32_t base = lds0 + slot * kMStageBytes;
+#pragma unroll
+        for (int i = 0; i < 3; ++i) lds_dma16_lanes(asrc[i] + ktc * astep, base + adst[i], ~0ull);
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            lds_dma16_lanes(bsrc + (size_t)ktc * 32 + 16 * h,
+                            base + kMAStage + h * kMBPlane + kMBRows * lw * 16, (1ull << kMBRows) - 1);
+    };
+
+    v4f acc[4][5];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 5; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+#pragma unroll
+    for (int st = 0; st < kMStages - 1; ++st) issue_stage(st, st);
+
+    const int r16 = lane & 15, q = lane >> 4;  // row and 32-k chunk of the lane
+    auto read_a = [&](int kt, v8i (&af)[4]) __attribute__((always_inline)) {
+        const uint8_t *sa = ring + (kt % kMStages) * kMStageBytes + (q >> 1) * 4 * kBlockBytes;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int tok = 64 * wm + 16 * i;  // first token of the subtile
+            const uint8_t *blk = sa + (tok >> 5) * kBlockBytes;
+            const int slot = (tok & 31) + r16 + 32 * (q & 1);
+            const uint2 p0 = *reinterpret_cast<const uint2 *>(blk + 8 * slot);
+            const uint4 p1 = *reinterpret_cast<const uint4 *>(blk + 512 + 16 * slot);
+            af[i] = v8i{(int)p0.x, (int)p0.y, (int)p1.x, (int)p1.y, (int)p1.z, (int)p1.w, 0, 0};
+        }
+    };
+    auto read_w = [&](int kt, uint2 (&wp)[5]) __attribute__((always_inline)) {
+        const uint8_t *sb = ring + (kt % kMStages) * kMStageBytes + kMAStage + (q >> 1) * kMBPlane;
+#pragma unroll
+        for (int j = 0; j < 5; ++j)
+            wp[j] = *reinterpret_cast<const uint2 *>(sb + (80 * wn + 16 * j + r16) * 16 + 8 * (q & 1));
+    };
+    auto expand = [&](const uint2 (&wp)[5], v8i (&wf)[5]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < 5; ++j)
+            wf[j] = v8i{(int)(wp[j].x & 0x33333333u), (int)((wp[j].x >> 2) & 0x33333333u),
+                        (int)(wp[j].y & 0x33333333u), (int)((wp[j].y >> 2) & 0x33333333u), 0, 0, 0, 0};
+    };
+
+    // per stage: the wait for the next stage, the barrier (the slot refilled next was read
+    // and used a stage earlier) and the DMA; then the twenty MFMAs of this stage on
+    // fragments already in registers, the next stage's reads and spreading in their shadow
+    struct Frag { v8i a[4]; v8i w[5]; };
+    Frag f0, f1;
+    uint2 wp[5];
+    wait_vm<(kMStages - 2) * kMDma>();
+    __syncthreads();
+    read_w(0, wp);
+    read_a(0, f0.a);
+    expand(wp, f0.w);
+    auto step = [&](int kt, Frag &cur, Frag &nxt) __attribute__((always_inline)) {
+        wait_vm<(kMStages - 3) * kMDma>();
+        __syncthreads();
+        issue_stage(kt + kMStages - 1, (kt + kMStages - 1) % kMStages);
+        __builtin_amdgcn_sched_barrier(0);
+        read_w(kt + 1, wp);
+        read_a(kt + 1, nxt.a);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 5; ++j)
+                // A = weights (format 4, e2m1), B = activations (format 2, e2m3), unit scales
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(cur.w[j], cur.a[i], acc[i][j],
+                                                                             4, 2, 0, 127, 0, 127);
+        expand(wp, nxt.w);
+#pragma unroll
+        for (int t = 0; t < 7; ++t) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS read
+        }
+#pragma unroll
+        for (int t = 0; t < 13; ++t) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // VALU
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+#pragma unroll 1
+    for (int kt = 0; kt + 1 < nk; kt += 2) {
+        step(kt, f0, f1);
+        step(kt + 1, f1, f0);
+    }
+    if (nk & 1) step(nk - 1, f0, f1);
+    wait_vm<0>();  // the ring's last (dummy) loads land before the block's LDS is released
+    if constexpr (kSplit == 2) {
+        // the second group's sums into the first's: lane-wise, through the (now free) rings
+        __syncthreads();
+        float *red = reinterpret_cast<float *>(smem) + (lw * 4 * 5 * 4) * 64 + lane;
+        if (grp == 1) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 5; ++j)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) red[((i * 5 + j) * 4 + r) * 64] = acc[i][j][r];
+        }
+        __syncthreads();
+        if (grp == 1) return;
+        // each partial is an fp32 integer multiple of 1/4 below 2^22: the sum is exact
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 5; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[i][j][r] += red[((i * 5 + j) * 4 + r) * 64];
+    }
+
+    // ---- epilogue: lane l holds acc[i][j][r] = 4 x sum for token 16 i + l % 16 and row
+    // 16 j + 4 (l / 16) + r of the wave's tile: four consecutive outputs of one token
+    const int ml = 64 * wm + r16;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int m = m0 + ml + 16 * i;
+        const float f = s_f[ml + 16 * i];
+        const int cs = s_sum[ml + 16 * i];
+        if (m >= p.M) continue;
+#pragma unroll
+        for (int j = 0; j < 5; ++j) {
+            const int n = n0 + 80 * wn + 16 * j + 4 * q;
+            const size_t idx = (size_t)m * p.N + n;
+            float y[4];
+            int av[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                av[t] = (int)(4.0f * acc[i][j][t]) - cs;  // exact: an integer below 2^24
+                float v = __fmul_rn((float)av[t], f);
+                if (kBias) v = __fadd_rn(v, n + t < p.N ? p.bias[n + t] : 0.0f);
+                if (kRelu2) {
+                    const float rr = v > 0.0f ? v : 0.0f;
+                    v = __fmul_rn(rr, rr);
+                }
+                y[t] = v;
+            }
+            if ((p.N & 3) == 0 && n + 3 < p.N) {
+                if (kYD == 2) {
+                    *reinterpret_cast<int4 *>(static_cast<int32_t *>(p.y) + idx) =
+                        make_int4(av[0], av[1], av[2], av[3]);
+                } else if (kYD == 1) {
+                    typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+                    const bf2 lo = {(__bf16)y[0], (__bf16)y[1]};
+                    const bf2 hi = {(__bf16)y[2], (__bf16)y[3]};
+                    *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(p.y) + idx) =
+                        make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+                } else {
+                    *reinterpret_cast<float4 *>(static_cast<float *>(p.y) + idx) =
+                        make_float4(y[0], y[1], y[2], y[3]);
+                }
+            } else {
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    if (n + t >= p.N) continue;
+                    if (kYD == 2) static_cast<int32_t *>(p.y)[idx + t] = av[t];
+                    else if (kYD == 1) static_cast<uint16_t *>(p.y)[idx + t] = (uint16_t)to_bf16_bits(y[t]);
+                    else static_cast<float *>(p.y)[idx + t] = y[t];
+                }
+            }
+        }
+    }
+}
+
+hipError_t launch_f6_mid(const F6Params &p0, const FwdArgs &a, hipStream_t s) {
+    F6Params p = p0;
+    p.tiles_m = (int)((a.M + kMTM - 1) / kMTM);
+    const int tiles_n = (int)((a.N + kMTN - 1) / kMTN);
+    const dim3 grid((unsigned)(p.tiles_m * tiles_n));
+    const int key = a.y_dtype * 4 + (a.epi == 1 ? 2 : 0) + (a.bias ? 1 : 0);
+    const bool split = BL_F6_MID_SPLIT && a.K % 256 == 0;
+    switch (key) {
+#define BL_LAUNCH(SPLIT, YD, R, B)                                                               \
+    {                                                                                             \
+        constexpr size_t lds = SPLIT * kMStages * kMStageBytes + kMTM * 8;                        \
+        hipError_t e = allow_lds((const void *)gemm_f6f4_mid_kernel<SPLIT, YD, R, B>, lds);       \
+        if (e != hipSuccess) return e;                                                            \
+        hipLaunchKernelGGL((gemm_f6f4_mid_kernel<SPLIT, YD, R, B>), grid, dim3(64 * kMWaves * SPLIT), \
+                           lds, s, p);                                                            \
+    }
+#define BL_CASE(YD, R, B)                                                                        \
+    case YD * 4 + (R ? 2 : 0) + (B ? 1 : 0):                                                      \
+        if (split) BL_LAUNCH(2, YD, R, B)                                                         \
+        else BL_LAUNCH(1, YD, R, B)                                                               \
+        break;
+        BL_CASE(0, false, false) BL_CASE(0, false, true) BL_CASE(0, true, false) BL_CASE(0, true, true)
+        BL_CASE(1, false, false) BL_CASE(1, false, true) BL_CASE(1, true, false) BL_CASE(1, true, true)
+        BL_CASE(2, false, false)
+#undef BL_CASE
+#undef BL_LAUNCH
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+// the balanced tiles where they take at most three quarters of the 256-row tiles' work
+// per CU (tiles of one round times their area, as for the int8 kernels)
+bool f6_mid_preferred(int64_t M, int64_t N, int64_t K) {
+    if (!BL_F6_MID || K % 128 != 0) return false;
+    constexpr int64_t kCUs = 256;
+    const int64_t mid = ((M + kMTM - 1) / kMTM) * ((N + kMTN - 1) / kMTN);
+    const int64_t mid_work = ((mid + kCUs - 1) / kCUs) * kMTM * kMTN;
+    const int64_t wide = ((M + 255) / 256) * ((N + 255) / 256);
+    int64_t big_work;
+    if (wide >= 128) {
+        big_work = ((wide + kCUs - 1) / kCUs) * 256 * 256;
+    } else {
+        const int64_t narrow = ((M + 255) / 256) * ((N + 127) / 128);
+        big_work = ((narrow + kCUs - 1) / kCUs) * 256 * 128;
+    }
+    return 4 * mid_work <= 3 * big_work;
+}
+
 }  // namespace
 
 bool gemm_f6f4_supports(int64_t M, int64_t N, int64_t K, int bits) {
@@ -381,6 +676,7 @@ hipError_t launch_gemm_f6f4(const FwdArgs &a, hipStream_t s) {
     p.K = (int)a.K;
     p.mb_pad = (int)f6_mb_pad(a.M);
     p.y = a.y;
+    if (f6_mid_preferred(a.M, a.N, a.K)) return launch_f6_mid(p, a, s);
     // 256-wide tiles when they cover at least half the CUs, else 128-wide, two per CU
     const int64_t tiles256 = ((a.M + BM - 1) / BM) * ((a.N + 255) / 256);
     return tiles256 < 128 ? launch_f6_tiles<128>(p, a, s) : launch_f6_tiles<256>(p, a, s);

@@ -4,7 +4,7 @@ matrix cores (bits=4, M >= 128, N >= 128, K % 64 == 0, K < 2^20).
 The int4 codes enter the MFMA as q/2 in e2m3 and the ternary fields as (c+1)/2 in
 e2m1; the claim is that the fp32 accumulation is then exact, so the path must match
 the oracle's integer contraction to the bit:
-- element by element at ragged shapes on both tile widths, every epilogue and output;
+- element by element at ragged shapes on every tile shape, every epilogue and output;
 - closed forms at the largest K the path takes (2^20 - 64), where the accumulator sits
   at 4K, the edge of exact fp32: all codes -8 against c = +1 must give exactly -8K;
 - sampled oracle outputs for random codes at that K, and the same closed forms at
@@ -25,9 +25,11 @@ pytestmark = pytest.mark.gpu
 
 K_MAX_F6 = (1 << 20) - 64
 
-# (M, K, N): one tile, ragged M and N, several k steps, 128-wide tiles (few tiles) and
-# 256-wide tiles (at least 128 tiles of 256 x 256: the ping-pong k loop of two wave
-# groups), there with one k step, an even and two odd numbers of them, ragged M and N
+# (M, K, N): one tile, ragged M and N, several k steps; 128-wide tiles (few tiles),
+# 256-wide tiles (at least 128 tiles of 256 x 256) with one k step, an even and two odd
+# numbers of them; and, where K % 128 == 0 and they leave fewer CUs idle, the balanced
+# 128 x 160 tiles on the 16 x 16 x 128 MFMA (one wave group: 129 x 128 x 130,
+# 513 x 640 x 1000, 2048 x 128 x 4096; two on alternate stages: 256 x 2560 x 384)
 F6_SHAPES = [(128, 64, 128), (129, 128, 130), (300, 192, 257), (256, 2560, 384),
              (513, 640, 1000), (2048, 128, 4096), (2048, 64, 4096), (2100, 320, 4000),
              (2304, 448, 3900)]
@@ -47,7 +49,10 @@ def test_f6f4_shapes(M, K, N, fused):
 def test_f6f4_variants(gran, epi, ydt, with_bias):
     if ydt == "i32" and (epi or with_bias):
         pytest.skip("raw accumulators take no epilogue")
+    # 256-row tiles (K = 320); balanced 128 x 160 tiles with one wave group (K = 384) and
+    # with two on alternate k stages (K = 256)
     _check_forward(300, 320, 260, 4, gran, epi, ydt, with_bias, False, sampled=False)
+    _check_forward(300, 384, 260, 4, gran, epi, ydt, with_bias, False, sampled=False, seed=3)
     _check_forward(257, 256, 388, 4, gran, epi, ydt, with_bias, True, x_dtype="bf16",
                    sampled=False, seed=2)
 
