@@ -365,7 +365,7 @@ def leg_prefill(torch, bl, reps=20):
     res["step_tops"] = tot_ops / (tot_step_ms * 1e-3) / 1e12
     t4 = res["int4"]
     t4["gemm_tops"] = tot_ops / (t4.pop("_ms") * 1e-3) / 1e12
-    t4["mfma"] = "fp6 x fp4 32x32x64 (exact)"
+    t4["mfma"] = "fp6 x fp4 scaled MFMA (exact): 32x32x64 on up, 16x16x128 in balanced tiles on down"
     t4["peak_tops"] = F6F4_PEAK_TOPS
     t4["frac"] = t4["gemm_tops"] / F6F4_PEAK_TOPS
     return res
@@ -1041,6 +1041,8 @@ def main():
                           "workload": "M=2048 tokens, 2560->6912 (+ReLU^2) and 6912->2560, "
                                       "int8 per token, bf16 out",
                           "value": round(pf["gemm_tops"], 2), "unit": "TOPS",
+                          "mfma": "int8 32x32x32 in 256 x 256 tiles (up); 16x16x64 in balanced "
+                                  "128 x 160 tiles (down)",
                           "roofline": {"bound": "mfma", "peak": INT8_PEAK_TOPS, "unit": "TOPS",
                                        "frac": round(pf["gemm_frac"], 4)},
                           "with_act_quant_tops": round(pf["step_tops"], 2),
