@@ -50,20 +50,27 @@ constexpr int kADma = kAStage / 1024;                // 12 DMAs of 64 lanes x 16
 #ifndef BL_F6_MID
 #define BL_F6_MID 1        // 0: never the balanced tiles
 #endif
+#ifndef BL_F6_KSUB2
+#define BL_F6_KSUB2 1      // 256-row tiles, K % 128 == 0: two 64-wide k steps per stage
+#endif
 #ifndef BL_F6_MID_SPLIT
 #define BL_F6_MID_SPLIT 1  // where K % 256 == 0: two wave groups on alternate stages
 #endif
 
-template <int kBN> struct F6Tile {
+// kSub 64-wide k steps per LDS stage (one barrier per stage); a stage is kSub
+// sub-stages of (activation blocks, weight rows) laid out as one step's stage
+template <int kBN, int kSub = 1> struct F6Tile {
     static constexpr int kWaves = kBN / 32;          // 4 token waves x BN/128 row waves
     static constexpr int kThreads = 64 * kWaves;
     static constexpr int kBStage = kBN * 16;
-    static constexpr int kStageBytes = kAStage + kBStage;
-    static constexpr int kDma = 16 / kWaves;         // 12 activation + 4 weight DMAs per stage
+    static constexpr int kSubBytes = kAStage + kBStage;
+    static constexpr int kStageBytes = kSub * kSubBytes;
+    static constexpr int kDma = 16 * kSub / kWaves;  // per sub-stage 12 activation + 4 weight DMAs
     static constexpr int kWRows = kBN / 4;           // rows per weight DMA (lanes < kWRows)
     // LDS ring depth; two 128-wide blocks share a CU's 160 KB
     static constexpr int kStages = kBN == 256 ? BL_F6_STAGES : (BL_F6_STAGES < 5 ? BL_F6_STAGES : 5);
     static constexpr size_t kLds = (size_t)kStages * kStageBytes + BM * (sizeof(float) + sizeof(int));
+    static_assert(kLds <= 160 * 1024, "LDS");
 };
 
 struct F6Params {
@@ -80,10 +87,10 @@ struct F6Params {
     int tiles_m;
 };
 
-template <int kBN, int kYD, bool kRelu2, bool kBias>
+template <int kBN, int kSub, int kYD, bool kRelu2, bool kBias>
 __global__ void __launch_bounds__(F6Tile<kBN>::kThreads, kBN == 128 ? 2 : 1)
 gemm_f6f4_kernel(F6Params p) {
-    using T = F6Tile<kBN>;
+    using T = F6Tile<kBN, kSub>;
     constexpr int kDma = T::kDma;
     constexpr int kStages = T::kStages;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -96,7 +103,7 @@ gemm_f6f4_kernel(F6Params p) {
     const int tile = blockIdx.x;
     const int tm = tile % p.tiles_m, tn = tile / p.tiles_m;  // row blocks of a column back to back
     const int m0 = tm * BM, n0 = tn * kBN;
-    const int K = p.K, nk = K / BK;
+    const int K = p.K, nk = K / (BK * kSub);  // stages
 
     for (int t = tid; t < BM; t += T::kThreads) {
         const int m = m0 + t;
@@ -110,24 +117,24 @@ gemm_f6f4_kernel(F6Params p) {
         s_sum[t] = cs;
     }
 
-    // DMA u of a stage is issued by wave u / kDma: u < 12 copies 1 KB of the tile's
-    // activation blocks, u >= 12 kWRows weight rows of 16 bytes.  The choice is made once
-    // here (source of step 0, bytes per k step, LDS offset, lanes), so that the loop
-    // issues its DMAs without branches.
+    // DMA u of a stage is issued by wave u / kDma: in sub-stage u / 16, u % 16 < 12
+    // copies 1 KB of the tile's activation blocks, u % 16 >= 12 kWRows weight rows of 16
+    // bytes.  The choice is made once here (source of stage 0, bytes per stage, LDS
+    // offset, lanes), so that the loop issues its DMAs without branches.
     const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)smem;
     const uint8_t *dsrc[kDma];
     uint64_t dstride[kDma], dlanes[kDma];
     uint32_t doff[kDma];
 #pragma unroll
     for (int i = 0; i < kDma; ++i) {
-        const int u = wave * kDma + i;
+        const int sub = (wave * kDma + i) / 16, u = (wave * kDma + i) % 16;
         const bool act = u < kADma;
         const int wr = (act ? 0 : u - kADma) * T::kWRows;
         const int gn = min(n0 + wr + lane, p.N - 1);
-        dsrc[i] = act ? p.xp + (size_t)8 * tm * kBlockBytes + 1024 * u + 16 * lane
-                      : p.w + (size_t)gn * (K / 4);
-        dstride[i] = act ? (uint64_t)p.mb_pad * kBlockBytes : (uint64_t)(BK / 4);
-        doff[i] = act ? 1024 * u : kAStage + wr * 16;
+        dsrc[i] = act ? p.xp + ((size_t)sub * p.mb_pad + 8 * (size_t)tm) * kBlockBytes + 1024 * u + 16 * lane
+                      : p.w + (size_t)gn * (K / 4) + sub * (BK / 4);
+        dstride[i] = act ? (uint64_t)kSub * p.mb_pad * kBlockBytes : (uint64_t)(kSub * BK / 4);
+        doff[i] = sub * T::kSubBytes + (act ? 1024 * u : kAStage + wr * 16);
         dlanes[i] = (act || T::kWRows == 64) ? ~0ull : (1ull << T::kWRows) - 1;
     }
     auto issue_stage = [&](int kt, int slot) __attribute__((always_inline)) {
@@ -149,16 +156,17 @@ gemm_f6f4_kernel(F6Params p) {
     for (int st = 0; st < kStages - 1; ++st) issue_stage(st, st);
 
     const int r32 = lane & 31, g = lane >> 5;
-    // activation fragment of token block i (of the wave's two) in step kt
-    auto read_a = [&](int kt, int i, v8i &af) __attribute__((always_inline)) {
-        const uint8_t *blk = smem + (kt % kStages) * T::kStageBytes + (2 * wt + i) * kBlockBytes;
+    // activation fragment of token block i (of the wave's two) in sub-step sub of stage kt
+    auto read_a = [&](int kt, int sub, int i, v8i &af) __attribute__((always_inline)) {
+        const uint8_t *blk = smem + (kt % kStages) * T::kStageBytes + sub * T::kSubBytes +
+                             (2 * wt + i) * kBlockBytes;
         const uint2 p0 = *reinterpret_cast<const uint2 *>(blk + 8 * lane);
         const uint4 p1 = *reinterpret_cast<const uint4 *>(blk + 512 + 16 * lane);
         af = v8i{(int)p0.x, (int)p0.y, (int)p1.x, (int)p1.y, (int)p1.z, (int)p1.w, 0, 0};
     };
     // packed weights of the wave's four 32-row fragments: 8 bytes (32 codes, k half g)
-    auto read_w = [&](int kt, uint2 (&wp)[4]) __attribute__((always_inline)) {
-        const uint8_t *sb = smem + (kt % kStages) * T::kStageBytes + kAStage;
+    auto read_w = [&](int kt, int sub, uint2 (&wp)[4]) __attribute__((always_inline)) {
+        const uint8_t *sb = smem + (kt % kStages) * T::kStageBytes + sub * T::kSubBytes + kAStage;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
             wp[j] = *reinterpret_cast<const uint2 *>(sb + (128 * wn + 32 * j + r32) * 16 + 8 * g);
@@ -185,18 +193,21 @@ gemm_f6f4_kernel(F6Params p) {
     uint2 wp[4];
     wait_vm<(kStages - 2) * kDma>();
     __syncthreads();
-    read_w(0, wp);
-    read_a(0, 0, f0.a[0]);
-    read_a(0, 1, f0.a[1]);
+    read_w(0, 0, wp);
+    read_a(0, 0, 0, f0.a[0]);
+    read_a(0, 0, 1, f0.a[1]);
     expand(wp, f0.w);
-    auto step = [&](int kt, Frag &cur, Frag &nxt) __attribute__((always_inline)) {
-        wait_vm<(kStages - 3) * kDma>();
+    auto sync = [&](int kt) __attribute__((always_inline)) {
+        wait_vm<(kStages - 3) * kDma>();  // this wave's copies of stage kt + 1 landed
         __syncthreads();
         issue_stage(kt + kStages - 1, (kt + kStages - 1) % kStages);
         __builtin_amdgcn_sched_barrier(0);
-        read_w(kt + 1, wp);
-        read_a(kt + 1, 0, nxt.a[0]);
-        read_a(kt + 1, 1, nxt.a[1]);
+    };
+    // the eight MFMAs of `cur`; meanwhile sub-step rsub of stage rkt into `nxt`
+    auto sub_step = [&](int rkt, int rsub, Frag &cur, Frag &nxt) __attribute__((always_inline)) {
+        read_w(rkt, rsub, wp);
+        read_a(rkt, rsub, 0, nxt.a[0]);
+        read_a(rkt, rsub, 1, nxt.a[1]);
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -214,12 +225,26 @@ gemm_f6f4_kernel(F6Params p) {
         }
         __builtin_amdgcn_sched_barrier(0);
     };
+    if constexpr (kSub == 2) {
 #pragma unroll 1
-    for (int kt = 0; kt + 1 < nk; kt += 2) {
-        step(kt, f0, f1);
-        step(kt + 1, f1, f0);
+        for (int kt = 0; kt < nk; ++kt) {
+            sync(kt);
+            sub_step(kt, 1, f0, f1);
+            sub_step(kt + 1, 0, f1, f0);
+        }
+    } else {
+#pragma unroll 1
+        for (int kt = 0; kt + 1 < nk; kt += 2) {
+            sync(kt);
+            sub_step(kt + 1, 0, f0, f1);
+            sync(kt + 1);
+            sub_step(kt + 2, 0, f1, f0);
+        }
+        if (nk & 1) {
+            sync(nk - 1);
+            sub_step(nk, 0, f0, f1);
+        }
     }
-    if (nk & 1) step(nk - 1, f0, f1);
 
     // ---- epilogue: lane l holds acc[i][j][r] = 4 x sum for token 64 wt + 32 i + l % 32
     // and row 128 wn + 32 j + 8 (r / 4) + 4 (l / 32) + r % 4: four consecutive outputs
@@ -250,7 +275,7 @@ gemm_f6f4_kernel(F6Params p) {
     constexpr int kPitch = kRowB + (kYD == 1 ? 8 : 16);
     constexpr int kLanesPerRow = kRowB / 16;
     constexpr int kRowsPerStore = 64 / kLanesPerRow;
-    constexpr bool kCanStage = F6Tile<kBN>::kWaves * 32 * kPitch <= kStages * T::kStageBytes;
+    constexpr bool kCanStage = T::kWaves * 32 * kPitch <= kStages * T::kStageBytes;
     uint8_t *stg = smem + wave * 32 * kPitch;
     const bool rows16 = ((int64_t)p.N * kOutB) % 16 == 0;
     const bool vec = (p.N & 3) == 0;
@@ -342,20 +367,20 @@ gemm_f6f4_kernel(F6Params p) {
     }
 }
 
-template <int kBN>
+template <int kBN, int kSub>
 hipError_t launch_f6_tiles(const F6Params &p0, const FwdArgs &a, hipStream_t s) {
     F6Params p = p0;
     p.tiles_m = (int)((a.M + BM - 1) / BM);
     const int tiles_n = (int)((a.N + kBN - 1) / kBN);
-    const size_t lds = F6Tile<kBN>::kLds;
-    const dim3 grid((unsigned)(p.tiles_m * tiles_n)), block(F6Tile<kBN>::kThreads);
+    const size_t lds = F6Tile<kBN, kSub>::kLds;
+    const dim3 grid((unsigned)(p.tiles_m * tiles_n)), block(F6Tile<kBN, kSub>::kThreads);
     const int key = a.y_dtype * 4 + (a.epi == 1 ? 2 : 0) + (a.bias ? 1 : 0);
     switch (key) {
 #define BL_CASE(YD, R, B)                                                                        \
     case YD * 4 + (R ? 2 : 0) + (B ? 1 : 0): {                                                    \
-        hipError_t e = allow_lds((const void *)gemm_f6f4_kernel<kBN, YD, R, B>, lds);             \
+        hipError_t e = allow_lds((const void *)gemm_f6f4_kernel<kBN, kSub, YD, R, B>, lds);       \
         if (e != hipSuccess) return e;                                                            \
-        hipLaunchKernelGGL((gemm_f6f4_kernel<kBN, YD, R, B>), grid, block, lds, s, p);            \
+        hipLaunchKernelGGL((gemm_f6f4_kernel<kBN, kSub, YD, R, B>), grid, block, lds, s, p);      \
         break;                                                                                    \
     }
         BL_CASE(0, false, false) BL_CASE(0, false, true) BL_CASE(0, true, false) BL_CASE(0, true, true)
@@ -679,7 +704,8 @@ hipError_t launch_gemm_f6f4(const FwdArgs &a, hipStream_t s) {
     if (f6_mid_preferred(a.M, a.N, a.K)) return launch_f6_mid(p, a, s);
     // 256-wide tiles when they cover at least half the CUs, else 128-wide, two per CU
     const int64_t tiles256 = ((a.M + BM - 1) / BM) * ((a.N + 255) / 256);
-    return tiles256 < 128 ? launch_f6_tiles<128>(p, a, s) : launch_f6_tiles<256>(p, a, s);
+    if (tiles256 < 128) return launch_f6_tiles<128, 1>(p, a, s);
+    return BL_F6_KSUB2 && a.K % 128 == 0 ? launch_f6_tiles<256, 2>(p, a, s) : launch_f6_tiles<256, 1>(p, a, s);
 }
 
 }  // namespace bl

@@ -27,12 +27,13 @@ K_MAX_F6 = (1 << 20) - 64
 
 # (M, K, N): one tile, ragged M and N, several k steps; 128-wide tiles (few tiles),
 # 256-wide tiles (at least 128 tiles of 256 x 256) with one k step, an even and two odd
-# numbers of them; and, where K % 128 == 0 and they leave fewer CUs idle, the balanced
-# 128 x 160 tiles on the 16 x 16 x 128 MFMA (one wave group: 129 x 128 x 130,
+# numbers of them, and with two k steps per LDS stage where K % 128 == 0 (3000 x 384 x
+# 4000: three stages, ragged); and, where K % 128 == 0 and they leave fewer CUs idle, the
+# balanced 128 x 160 tiles on the 16 x 16 x 128 MFMA (one wave group: 129 x 128 x 130,
 # 513 x 640 x 1000, 2048 x 128 x 4096; two on alternate stages: 256 x 2560 x 384)
 F6_SHAPES = [(128, 64, 128), (129, 128, 130), (300, 192, 257), (256, 2560, 384),
              (513, 640, 1000), (2048, 128, 4096), (2048, 64, 4096), (2100, 320, 4000),
-             (2304, 448, 3900)]
+             (2304, 448, 3900), (3000, 384, 4000)]
 
 
 @pytest.mark.parametrize("M,K,N", F6_SHAPES)
