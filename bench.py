@@ -754,8 +754,9 @@ CALIB_LIB = os.path.join(ROOT, "ternary_weight_quantized_bitlinear_amd", "libbit
 
 def leg_mfma_ceiling(torch, reps=3):
     """Matrix-core ceilings on this chip: MFMA-only loops (no memory, barrier or VALU work)
-    on register operands with the value statistics of the int8 GEMM, the FP4 x FP6 GEMM
-    and the backward's bf16 GEMMs (libbitlinear_calib.so), one 8-wave block per CU.
+    on register operands with the value statistics of the int8 GEMMs (on both int8
+    instruction shapes), the FP4 x FP6 GEMM and the backward's bf16 GEMMs
+    (libbitlinear_calib.so), one 8-wave block per CU.
     Median of `reps` launches of a few ms each."""
     import ctypes
     lib = ctypes.CDLL(CALIB_LIB)
@@ -769,6 +770,7 @@ def leg_mfma_ceiling(torch, reps=3):
     stream = torch.cuda.current_stream()
     out = {"blocks": blocks, "waves_per_block": 8}
     for kind, name, iters, peak in ((0, "int8_32x32x32", 20000, INT8_PEAK_TOPS),
+                                    (3, "int8_16x16x64", 40000, INT8_PEAK_TOPS),
                                     (1, "fp4_x_fp6_32x32x64", 10000, F6F4_PEAK_TOPS),
                                     (2, "bf16_32x32x16", 20000, BF16_PEAK_TFLOPS)):
         def launch():
@@ -1041,8 +1043,8 @@ def main():
                           "workload": "M=2048 tokens, 2560->6912 (+ReLU^2) and 6912->2560, "
                                       "int8 per token, bf16 out",
                           "value": round(pf["gemm_tops"], 2), "unit": "TOPS",
-                          "mfma": "int8 32x32x32 in 256 x 256 tiles (up); 16x16x64 in balanced "
-                                  "128 x 160 tiles (down)",
+                          "mfma": "int8 16x16x64 in balanced tiles: 128 x 448 (up), 128 x 160 "
+                                  "(down)",
                           "roofline": {"bound": "mfma", "peak": INT8_PEAK_TOPS, "unit": "TOPS",
                                        "frac": round(pf["gemm_frac"], 4)},
                           "with_act_quant_tops": round(pf["step_tops"], 2),
@@ -1083,12 +1085,14 @@ def main():
         out["roofline"]["read_ceiling_gbs"] = hbm["gbs"]
         out["roofline"]["frac_of_read_ceiling"] = round(out["roofline"]["achieved"] / hbm["gbs"], 4)
         c8 = ceil["int8_32x32x32"]["tops"]
+        c8m = ceil["int8_16x16x64"]["tops"]
         c4 = ceil["fp4_x_fp6_32x32x64"]["tops"]
         cb = ceil["bf16_32x32x16"]["tops"]
         if "prefill" in out:
+            # both 2B prefill shapes run on the 16x16x64 int8 matrix cores
             pf = out["prefill"]
-            pf["roofline"]["mfma_ceiling_tops"] = c8
-            pf["roofline"]["frac_of_ceiling"] = round(pf["value"] / c8, 4)
+            pf["roofline"]["mfma_ceiling_tops"] = c8m
+            pf["roofline"]["frac_of_ceiling"] = round(pf["value"] / c8m, 4)
             pf["int4_activations"]["frac_of_ceiling"] = round(
                 pf["int4_activations"]["gemm_tops"] / c4, 4)
         if "layer_70b" in out:

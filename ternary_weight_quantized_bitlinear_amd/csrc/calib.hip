@@ -13,7 +13,9 @@
 //   kind 1  FP4 x FP6 32x32x64, scaled MFMA with unit scales: e2m1 weight fields
 //           {0, 0.5, 1} times e2m3 halves of int4 codes (the 4-bit GEMM);
 //   kind 2  bf16 32x32x16: bf16 gradients of spread 0.01 times ternary codes (the
-//           backward GEMMs).
+//           backward GEMMs);
+//   kind 3  int8 16x16x64: the operands of kind 0 on v_mfma_i32_16x16x64_i8 (the
+//           balanced-tile prefill GEMM).
 // 8 waves per block (two per SIMD), one block per CU; each wave runs 8 accumulators.
 //
 // An HBM read-only loop: a grid-stride sweep of 16-byte non-temporal loads over a buffer
@@ -59,6 +61,23 @@ __device__ __forceinline__ uint32_t e2m3_half_code(uint32_t h) {
     return (q < 0 ? 0x20u : 0u) | mag;
 }
 
+// two operand sets of 16 bytes per lane: activation codes a, weight fields b
+__device__ __forceinline__ void int8_operands(uint32_t base, v4i (&a)[2], v4i (&b)[2]) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            const uint32_t h = mix(base * 16 + s * 8 + d);
+            a[s][d] = (int)(gauss_i8(h) | (gauss_i8(mix(h + 1)) << 8) |
+                            (gauss_i8(mix(h + 2)) << 16) | (gauss_i8(mix(h + 3)) << 24));
+            const uint32_t f = mix(h + 4);
+            uint32_t w = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) w |= ((f >> (8 * j)) % 3u) << (8 * j);
+            b[s][d] = (int)w;
+        }
+}
+
 template <int kKind>
 __global__ void __launch_bounds__(kThreads) mfma_loop(int iters, uint32_t seed, float *sink) {
     const uint32_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -66,19 +85,7 @@ __global__ void __launch_bounds__(kThreads) mfma_loop(int iters, uint32_t seed, 
     float total = 0.0f;
     if constexpr (kKind == 0) {
         v4i a[2], b[2];
-#pragma unroll
-        for (int s = 0; s < 2; ++s)
-#pragma unroll
-            for (int d = 0; d < 4; ++d) {
-                const uint32_t h = mix(base * 16 + s * 8 + d);
-                a[s][d] = (int)(gauss_i8(h) | (gauss_i8(mix(h + 1)) << 8) |
-                                (gauss_i8(mix(h + 2)) << 16) | (gauss_i8(mix(h + 3)) << 24));
-                const uint32_t f = mix(h + 4);
-                uint32_t w = 0;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) w |= ((f >> (8 * j)) % 3u) << (8 * j);
-                b[s][d] = (int)w;
-            }
+        int8_operands(base, a, b);
         v16i acc[kAcc];
 #pragma unroll
         for (int j = 0; j < kAcc; ++j) acc[j] = v16i{};
@@ -89,6 +96,19 @@ __global__ void __launch_bounds__(kThreads) mfma_loop(int iters, uint32_t seed, 
         }
 #pragma unroll
         for (int j = 0; j < kAcc; ++j) total += (float)acc[j][lane & 15];
+    } else if constexpr (kKind == 3) {
+        v4i a[2], b[2];
+        int8_operands(base, a, b);
+        v4i acc[kAcc];
+#pragma unroll
+        for (int j = 0; j < kAcc; ++j) acc[j] = v4i{};
+        for (int it = 0; it < iters; ++it) {
+#pragma unroll
+            for (int j = 0; j < kAcc; ++j)
+                acc[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(b[j & 1], a[j & 1], acc[j], 0, 0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < kAcc; ++j) total += (float)acc[j][lane & 3];
     } else if constexpr (kKind == 1) {
         v8i a[2], b[2];
 #pragma unroll
@@ -220,8 +240,10 @@ int bl_calib_read(const void *src, int64_t bytes, int blocks, int mode, uint32_t
 
 // Operations one launch performs: blocks x 8 waves x iters x 8 MFMAs x ops per MFMA.
 double bl_calib_ops(int kind, int blocks, int iters) {
-    const double per = kind == 0 ? 2.0 * 32 * 32 * 32 : kind == 1 ? 2.0 * 32 * 32 * 64
-                                                                  : 2.0 * 32 * 32 * 16;
+    const double per = kind == 0   ? 2.0 * 32 * 32 * 32
+                       : kind == 1 ? 2.0 * 32 * 32 * 64
+                       : kind == 2 ? 2.0 * 32 * 32 * 16
+                                   : 2.0 * 16 * 16 * 64;
     return (double)blocks * (kThreads / 64) * iters * kAcc * per;
 }
 
@@ -235,6 +257,7 @@ int bl_calib_mfma(int kind, int blocks, int iters, float *sink, void *stream) {
     case 0: hipLaunchKernelGGL(mfma_loop<0>, grid, block, 0, s, iters, 1u, sink); break;
     case 1: hipLaunchKernelGGL(mfma_loop<1>, grid, block, 0, s, iters, 1u, sink); break;
     case 2: hipLaunchKernelGGL(mfma_loop<2>, grid, block, 0, s, iters, 1u, sink); break;
+    case 3: hipLaunchKernelGGL(mfma_loop<3>, grid, block, 0, s, iters, 1u, sink); break;
     default: return (int)hipErrorInvalidValue;
     }
     return (int)hipGetLastError();

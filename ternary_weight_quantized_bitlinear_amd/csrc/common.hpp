@@ -324,10 +324,11 @@ hipError_t launch_gemm(const FwdArgs &a, void *ws, hipStream_t s);
 // prefill-sized M with whole 64-wide k steps: 256x256 tiles, LDS ring, 32x32x32 MFMA
 bool gemm_big_supports(int64_t M, int64_t N, int64_t K, int bits);
 hipError_t launch_gemm_big(const FwdArgs &a, hipStream_t s);
-// the balanced-tile variant (128 x 160 tiles, 16 x 16 x 64 MFMAs) on the same prepared
-// operands; launch_gemm_big takes it where it leaves fewer CUs idle
-bool gemm_mid_preferred(int64_t M, int64_t N, int64_t K, int bits);
-hipError_t launch_gemm_mid(const FwdArgs &a, hipStream_t s);
+// the balanced-tile variants (128 x 160 or 128 x 448 tiles, 16 x 16 x 64 MFMAs) on the
+// same prepared operands; launch_gemm_big takes the width gemm_mid_tiles returns (0: the
+// large tiles), where it leaves fewer CUs idle
+int gemm_mid_tiles(int64_t M, int64_t N, int64_t K, int bits);
+hipError_t launch_gemm_mid(const FwdArgs &a, int tn, hipStream_t s);
 size_t ws_gemm(int64_t M, int64_t N, int64_t K);
 // prefill-sized M with 4-bit activations: FP6 x FP4 scaled MFMA (exact for K < 2^20)
 bool gemm_f6f4_supports(int64_t M, int64_t N, int64_t K, int bits);

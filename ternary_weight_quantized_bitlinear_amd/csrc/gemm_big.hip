@@ -439,7 +439,10 @@ hipError_t launch_tiles(const BigParams &p0, const FwdArgs &a, hipStream_t s) {
 #endif
 
 hipError_t launch_gemm_big(const FwdArgs &a, hipStream_t s) {
-    if (BL_GEMM_MID && BL_GEMM_BN == 0 && gemm_mid_preferred(a.M, a.N, a.K, a.bits)) return launch_gemm_mid(a, s);
+    if (BL_GEMM_MID && BL_GEMM_BN == 0) {
+        const int tn = gemm_mid_tiles(a.M, a.N, a.K, a.bits);
+        if (tn != 0) return launch_gemm_mid(a, tn, s);
+    }
     BigParams p;
     p.xq = static_cast<const uint8_t *>(a.xq);
     p.rowsum = a.rowsum;

@@ -8,12 +8,19 @@
 // Guide", "3. Native Hardware INT4 Tensor Core Mapping": int32 accumulators, Output =
 // acc * (s_x * beta) for 4-bit activations.
 //
-// Block tile 128 tokens x 160 output rows.  A 2048 x 2560 output (the 2B model's down
-// projection at 2048 tokens) is exactly 256 such tiles, one per CU, each 128 x 160 x K:
-// the large-tile kernel's 256 x 128 tiles number 160 there, so 96 CUs would idle and
-// the busy ones would carry 1.6 times the work.  Four waves (2 token halves x 2 row
-// halves), each 64 tokens x 80 rows: 4 x 5 MFMAs of 16 x 16 x 64 per k step, 80
-// accumulator registers.
+// Two block tiles, 128 tokens by 160 or 448 output rows:
+// - 128 x 160.  A 2048 x 2560 output (the 2B model's down projection at 2048 tokens) is
+//   exactly 256 such tiles, one per CU, each 128 x 160 x K: the large-tile kernel's
+//   256 x 128 tiles number 160 there, so 96 CUs would idle and the busy ones would carry
+//   1.6 times the work.  Four waves (2 token halves x 2 row halves), each 64 tokens x 80
+//   rows: 4 x 5 MFMAs of 16 x 16 x 64 per k step, 80 accumulator registers.
+// - 128 x 448.  A 2048 x 6912 output (the up projection) is 16 x 16 such tiles (the last
+//   row block 192 wide), one per CU; the large-tile kernel's 216 tiles of 256 x 256 give
+//   the busy CUs 8/7 of that work.  Eight waves (2 token halves x 4 row quarters), each
+//   64 tokens x 112 rows: 4 x 7 MFMAs per k step, 112 accumulator registers.  On the up
+//   projection the kernel takes 42.6 us against 44.8 us for the large tiles, and a call
+//   including the operand preparation 48-50 us against 53-54 us (same box, alternating
+//   runs): each CU does 12.5% less work at a 6% lower MFMA rate.
 //
 // Operands as in the large-tile kernel: the activations arrive prepared (int8 codes,
 // int4 codes widened, in 16-element groups stored 4x4-transposed, plus sum_k q per
@@ -32,12 +39,15 @@
 // chunk-major layout avoids them but spreads each DMA instruction over 16 rows, and
 // measured slower (46.0 against 40.2 us on the down projection).
 //
-// Where K % 128 == 0 the block has two such groups of four waves (two waves per SIMD,
-// so one wave's MFMAs cover the other's waits), each with its own ring, on alternate
-// 64-wide k steps of the same tile; the second group's int32 sums are added to the
-// first's through LDS before the epilogue.  On the 2B down projection this measured
-// 48-50 us, against 51-52 us for one group with two k steps per stage and 54-55 us for
-// one group with one.
+// Where K % 128 == 0 the 128 x 160 block has two such groups of four waves (two waves
+// per SIMD, so one wave's MFMAs cover the other's waits), each with its own ring, on
+// alternate 64-wide k steps of the same tile; the second group's int32 sums are added
+// to the first's through LDS before the epilogue.  On the 2B down projection this
+// measured 48-50 us, against 51-52 us for one group with two k steps per stage and 54-55
+// us for one group with one.  The eight-wave 128 x 448 block already has two waves per
+// SIMD (a second group would leave 128 registers per wave for 112 accumulators); it
+// takes two k steps per stage where K % 128 == 0, one barrier per 56 MFMAs per wave
+// (ring depths 3, 4 and 5 measured alike).
 //
 // Requires K % 64 == 0.  Rows past M or N read clamped addresses and are never stored.
 #include "common.hpp"
@@ -47,10 +57,7 @@ namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 
-constexpr int TM = 128, TN = 160;
-constexpr int kWaves = 4, kThreads = 64 * kWaves;
-constexpr int WM = 64, WN = 80;            // wave tile (tokens x rows)
-constexpr int FI = WM / 16, FJ = WN / 16;  // 4 x 5 MFMA tiles per wave
+constexpr int TM = 128;
 #ifndef BL_MID_STAGES1
 #define BL_MID_STAGES1 6  // ring depth with one k step per stage
 #endif
@@ -58,22 +65,43 @@ constexpr int FI = WM / 16, FJ = WN / 16;  // 4 x 5 MFMA tiles per wave
 #define BL_MID_STAGES2 4  // with two
 #endif
 #ifndef BL_MID_MODE
-#define BL_MID_MODE 2  // where K % 128 == 0: 1 two k steps per stage, 2 the k split
+#define BL_MID_MODE 2  // 128 x 160 tiles where K % 128 == 0: 1 two k steps per stage, 2 the k split
 #endif
-constexpr int kBRows = TN / kWaves;        // weight rows per wave and DMA (lanes < 40)
-static_assert(kBRows <= 64, "one weight DMA per wave and k half");
+#ifndef BL_WIDE_TILES
+#define BL_WIDE_TILES 1  // 0: never the 128 x 448 tiles
+#endif
+#ifndef BL_WIDE_MODE
+#define BL_WIDE_MODE 1  // 128 x 448 tiles where K % 128 == 0: 1 two k steps per stage, 0 one
+#endif
+
+// Tile shapes: 128 x 160 with four waves per group (2 x 2, wave tiles 64 x 80) or
+// 128 x 448 with eight (2 x 4, wave tiles 64 x 112); every wave DMAs the same share of
+// the weight rows (lanes below kBRows)
+template <int kTN> struct MidShape {
+    static constexpr int TN = kTN;
+    static constexpr int kWaves = kTN == 160 ? 4 : 8;
+    static constexpr int kThreads = 64 * kWaves;
+    static constexpr int kWavesN = kWaves / 2;
+    static constexpr int WM = TM / 2, WN = kTN / kWavesN;  // wave tile (tokens x rows)
+    static constexpr int FI = WM / 16, FJ = WN / 16;       // 16 x 16 MFMA tiles per wave
+    static constexpr int kBRows = kTN / kWaves;
+    static_assert(kTN == 160 || kTN == 448, "tile shapes");
+    static_assert(WN % 16 == 0 && kBRows <= 64, "one weight DMA per wave and k plane");
+};
 
 // kSub 64-wide k steps per LDS stage (one barrier per stage): 1 where K % 128 != 0
-template <int kSub> struct MidTile {
+template <int kTN, int kSub> struct MidTile {
+    using S = MidShape<kTN>;
     static constexpr int BK = 64 * kSub;
-    static constexpr int kAStage = TM * BK;        // 8 or 16 KB
-    static constexpr int kBStage = TN * 16 * kSub;  // 2.5 or 5 KB: kSub planes of 16 B rows
+    static constexpr int kAStage = TM * BK;         // 8 or 16 KB
+    static constexpr int kBStage = kTN * 16 * kSub;  // kSub planes of 16 B rows
     static constexpr int kStageBytes = kAStage + kBStage;
     static constexpr int kStages = kSub == 1 ? BL_MID_STAGES1 : BL_MID_STAGES2;
-    static constexpr int kARows = 1024 / BK;       // activation rows per 1 KB DMA
-    static constexpr int kADma = kAStage / 1024 / kWaves;
-    static constexpr int kDma = kADma + kSub;      // DMAs per wave per stage
+    static constexpr int kARows = 1024 / BK;        // activation rows per 1 KB DMA
+    static constexpr int kADma = kAStage / 1024 / S::kWaves;
+    static constexpr int kDma = kADma + kSub;       // DMAs per wave per stage
     static constexpr size_t kLds = (size_t)kStages * kStageBytes + TM * (sizeof(float) + sizeof(int));
+    static_assert(kADma >= 1 && kAStage == 1024 * kADma * S::kWaves, "activation DMAs");
     static_assert((kStages - 2) * kDma < 64, "vmcnt is 6 bits");
     static_assert(kLds <= 160 * 1024, "LDS");
 };
@@ -102,9 +130,16 @@ template <int kSub> __device__ __forceinline__ int a_pos(int row, int c) {
 // kSplit = 2: two groups of four waves (two waves per SIMD), each with a ring of its
 // own, take alternate stages of the same tile (group g the stages g, g + 2, ...); the
 // second group's accumulators are added to the first's through LDS at the end.
-template <int kSub, int kSplit, int kYD, bool kRelu2, bool kBias>
-__global__ void __launch_bounds__(kThreads * kSplit, kSplit == 1 ? 2 : 1) gemm_mid_kernel(MidParams p) {
-    using T = MidTile<kSub>;
+// Two waves per SIMD in every form (four-wave blocks two per CU), so at most 256
+// registers per wave: the accumulators stay in the register file without spilling.
+template <int kTN, int kSub, int kSplit, int kYD, bool kRelu2, bool kBias>
+__global__ void __launch_bounds__(MidShape<kTN>::kThreads * kSplit,
+                                  MidShape<kTN>::kWaves * kSplit == 4 ? 2 : 1)
+gemm_mid_kernel(MidParams p) {
+    using S = MidShape<kTN>;
+    using T = MidTile<kTN, kSub>;
+    constexpr int TN = S::TN, kThreads = S::kThreads, kWaves = S::kWaves, kWavesN = S::kWavesN;
+    constexpr int WM = S::WM, WN = S::WN, FI = S::FI, FJ = S::FJ, kBRows = S::kBRows;
     constexpr int BK = T::BK, kAStage = T::kAStage, kStageBytes = T::kStageBytes;
     constexpr int kStages = T::kStages, kADma = T::kADma, kDma = T::kDma, kARows = T::kARows;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -113,8 +148,8 @@ __global__ void __launch_bounds__(kThreads * kSplit, kSplit == 1 ? 2 : 1) gemm_m
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int grp = wave >> 2, lw = wave & 3;  // group, and the wave within it
-    const int wm = lw >> 1, wn = lw & 1;
+    const int grp = wave / kWaves, lw = wave % kWaves;  // group, and the wave within it
+    const int wm = lw / kWavesN, wn = lw % kWavesN;
     uint8_t *ring = smem + grp * kStages * kStageBytes;
     // token blocks of one row block back to back: consecutive blocks (spread over the
     // XCDs) share the weights, each XCD keeps its few token blocks in its L2
@@ -137,10 +172,10 @@ __global__ void __launch_bounds__(kThreads * kSplit, kSplit == 1 ? 2 : 1) gemm_m
         s_sum[t] = cs;
     }
 
-    // ---- one stage into ring slot `slot`: wave w copies activation rows 32w .. 32w+31
-    // (kARows rows per 1 KB instruction; lane -> row lane / (4 kSub), and the global chunk
-    // that belongs at the lane's position) and weight rows 40w .. 40w+39 of each k plane
-    // (lanes < 40, 16 B each)
+    // ---- one stage into ring slot `slot`: wave w copies activation rows from
+    // (TM / kWaves) w on (kARows rows per 1 KB instruction; lane -> row lane / (4 kSub),
+    // and the global chunk that belongs at the lane's position) and weight rows kBRows w
+    // .. kBRows (w + 1) - 1 of each k plane (lanes < kBRows, 16 B each)
     const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)ring;
     const uint8_t *asrc[kADma];
 #pragma unroll
@@ -344,27 +379,67 @@ __global__ void __launch_bounds__(kThreads * kSplit, kSplit == 1 ? 2 : 1) gemm_m
 
 }  // namespace
 
-// The balanced tiles pay off where they take at most about three quarters of the work
-// per CU that the large-tile kernel's launch would: per CU, the tiles of one round times
-// their area (256 x 256 with one 8-wave block per CU; 256 x 128 with two 4-wave blocks,
-// when fewer than 128 of the wide tiles exist).
-bool gemm_mid_preferred(int64_t M, int64_t N, int64_t K, int bits) {
-    if ((bits != 8 && bits != 4) || K % 64 != 0 || M < 1 || N < 1) return false;
+// Work per CU of one launch: the tiles of a round times their area, rounds = tiles / 256
+// rounded up.  The large-tile kernel runs 256 x 256 tiles with one 8-wave block per CU,
+// or 256 x 128 tiles with two 4-wave blocks when fewer than 128 of the wide tiles exist.
+// 128 x 160 tiles are taken where they carry at most three quarters of that work per CU
+// (the 2B down projection at 2048 tokens: 0.625), 128 x 448 tiles where they carry at
+// most nine tenths (the 2B up projection at 2048 tokens: 0.875).  Returns the tile
+// width, or 0 for the large tiles.
+int gemm_mid_tiles(int64_t M, int64_t N, int64_t K, int bits) {
+    if ((bits != 8 && bits != 4) || K % 64 != 0 || M < 1 || N < 1) return 0;
     constexpr int64_t kCUs = 256;
-    const int64_t mid = ((M + TM - 1) / TM) * ((N + TN - 1) / TN);
-    const int64_t mid_work = ((mid + kCUs - 1) / kCUs) * TM * TN;
+    auto work = [&](int64_t tm, int64_t tn) {
+        const int64_t tiles = ((M + tm - 1) / tm) * ((N + tn - 1) / tn);
+        return ((tiles + kCUs - 1) / kCUs) * tm * tn;
+    };
     const int64_t wide = ((M + 255) / 256) * ((N + 255) / 256);
-    int64_t big_work;
-    if (wide >= 128) {
-        big_work = ((wide + kCUs - 1) / kCUs) * 256 * 256;
-    } else {
-        const int64_t narrow = ((M + 255) / 256) * ((N + 127) / 128);
-        big_work = ((narrow + kCUs - 1) / kCUs) * 256 * 128;
-    }
-    return 4 * mid_work <= 3 * big_work;
+    const int64_t big_work = wide >= 128 ? work(256, 256) : work(256, 128);
+    if (4 * work(TM, 160) <= 3 * big_work) return 160;
+    if (BL_WIDE_TILES && 10 * work(TM, 448) <= 9 * big_work) return 448;
+    return 0;
 }
 
-hipError_t launch_gemm_mid(const FwdArgs &a, hipStream_t s) {
+namespace {
+template <int kTN>
+hipError_t launch_shape(const MidParams &p, const FwdArgs &a, hipStream_t s) {
+    const int tiles_n = (int)((a.N + kTN - 1) / kTN);
+    const dim3 grid((unsigned)(p.tiles_m * tiles_n));
+    const int key = a.y_dtype * 4 + (a.epi == 1 ? 2 : 0) + (a.bias ? 1 : 0);
+    // K % 128 == 0: two 64-wide k steps per stage (mode 1) or, for the four-wave tiles,
+    // the k split over two wave groups (mode 2)
+    const int mode = a.K % 128 != 0 ? 0 : kTN == 160 ? BL_MID_MODE : BL_WIDE_MODE;
+    constexpr int kThreads = MidShape<kTN>::kThreads;
+    constexpr int kSplit2 = kTN == 160 ? 2 : 1;  // eight-wave tiles have no k split
+    switch (key) {
+#define BL_LAUNCH(SUB, SPLIT, YD, R, B)                                                          \
+    {                                                                                             \
+        using T = MidTile<kTN, SUB>;                                                              \
+        constexpr size_t lds = SPLIT * T::kStages * T::kStageBytes + TM * 8;                      \
+        const void *fn = (const void *)gemm_mid_kernel<kTN, SUB, SPLIT, YD, R, B>;                \
+        hipError_t e = allow_lds(fn, lds);                                                        \
+        if (e != hipSuccess) return e;                                                            \
+        hipLaunchKernelGGL((gemm_mid_kernel<kTN, SUB, SPLIT, YD, R, B>), grid,                    \
+                           dim3(kThreads * SPLIT), lds, s, p);                                    \
+    }
+#define BL_CASE(YD, R, B)                                                                        \
+    case YD * 4 + (R ? 2 : 0) + (B ? 1 : 0):                                                      \
+        if (mode == 1) BL_LAUNCH(2, 1, YD, R, B)                                                  \
+        else if (mode == 2) BL_LAUNCH(1, kSplit2, YD, R, B)                                       \
+        else BL_LAUNCH(1, 1, YD, R, B)                                                            \
+        break;
+        BL_CASE(0, false, false) BL_CASE(0, false, true) BL_CASE(0, true, false) BL_CASE(0, true, true)
+        BL_CASE(1, false, false) BL_CASE(1, false, true) BL_CASE(1, true, false) BL_CASE(1, true, true)
+        BL_CASE(2, false, false)
+#undef BL_CASE
+#undef BL_LAUNCH
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_gemm_mid(const FwdArgs &a, int tn, hipStream_t s) {
     MidParams p;
     p.xq = static_cast<const uint8_t *>(a.xq);
     p.rowsum = a.rowsum;
@@ -379,34 +454,9 @@ hipError_t launch_gemm_mid(const FwdArgs &a, hipStream_t s) {
     p.K = (int)a.K;
     p.y = a.y;
     p.tiles_m = (int)((a.M + TM - 1) / TM);
-    const int tiles_n = (int)((a.N + TN - 1) / TN);
-    const dim3 grid((unsigned)(p.tiles_m * tiles_n));
-    const int key = a.y_dtype * 4 + (a.epi == 1 ? 2 : 0) + (a.bias ? 1 : 0);
-    // K % 128 == 0: two 64-wide k steps per stage (4 waves) or the k split (8 waves)
-    const int mode = a.K % 128 == 0 ? BL_MID_MODE : 0;
-    switch (key) {
-#define BL_LAUNCH(SUB, SPLIT, YD, R, B)                                                          \
-    {                                                                                             \
-        constexpr size_t lds = SPLIT * MidTile<SUB>::kStages * MidTile<SUB>::kStageBytes + TM * 8; \
-        hipError_t e = allow_lds((const void *)gemm_mid_kernel<SUB, SPLIT, YD, R, B>, lds);       \
-        if (e != hipSuccess) return e;                                                            \
-        hipLaunchKernelGGL((gemm_mid_kernel<SUB, SPLIT, YD, R, B>), grid, dim3(kThreads * SPLIT), \
-                           lds, s, p);                                                            \
-    }
-#define BL_CASE(YD, R, B)                                                                        \
-    case YD * 4 + (R ? 2 : 0) + (B ? 1 : 0):                                                      \
-        if (mode == 1) BL_LAUNCH(2, 1, YD, R, B)                                                  \
-        else if (mode == 2) BL_LAUNCH(1, 2, YD, R, B)                                             \
-        else BL_LAUNCH(1, 1, YD, R, B)                                                            \
-        break;
-        BL_CASE(0, false, false) BL_CASE(0, false, true) BL_CASE(0, true, false) BL_CASE(0, true, true)
-        BL_CASE(1, false, false) BL_CASE(1, false, true) BL_CASE(1, true, false) BL_CASE(1, true, true)
-        BL_CASE(2, false, false)
-#undef BL_CASE
-#undef BL_LAUNCH
-    default: return hipErrorInvalidValue;
-    }
-    return hipGetLastError();
+    if (tn == 160) return launch_shape<160>(p, a, s);
+    if (tn == 448) return launch_shape<448>(p, a, s);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace bl
