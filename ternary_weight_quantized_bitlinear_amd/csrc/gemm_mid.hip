@@ -70,6 +70,9 @@ constexpr int TM = 128;
 #ifndef BL_WIDE_TILES
 #define BL_WIDE_TILES 1  // 0: never the 128 x 448 tiles
 #endif
+#ifndef BL_WIDE_TENTHS
+#define BL_WIDE_TENTHS 10  // 128 x 448 tiles at most this many tenths of the large tiles' work
+#endif
 #ifndef BL_WIDE_MODE
 #define BL_WIDE_MODE 1  // 128 x 448 tiles where K % 128 == 0: 1 two k steps per stage, 0 one
 #endif
@@ -383,9 +386,11 @@ gemm_mid_kernel(MidParams p) {
 // rounded up.  The large-tile kernel runs 256 x 256 tiles with one 8-wave block per CU,
 // or 256 x 128 tiles with two 4-wave blocks when fewer than 128 of the wide tiles exist.
 // 128 x 160 tiles are taken where they carry at most three quarters of that work per CU
-// (the 2B down projection at 2048 tokens: 0.625), 128 x 448 tiles where they carry at
-// most nine tenths (the 2B up projection at 2048 tokens: 0.875).  Returns the tile
-// width, or 0 for the large tiles.
+// (the 2B down projection at 2048 tokens: 0.625), 128 x 448 tiles where they carry no
+// more (the 2B up projection at 2048 tokens: 0.875; a 70B-class layer, 4096 x 28672
+// outputs: 1.0, where the 16 x 16 x 64 MFMAs still ran 5% faster than the large tiles'
+// 32 x 32 x 32 ones, 802-805 against 843-856 us).  Returns the tile width, or 0 for
+// the large tiles.
 int gemm_mid_tiles(int64_t M, int64_t N, int64_t K, int bits) {
     if ((bits != 8 && bits != 4) || K % 64 != 0 || M < 1 || N < 1) return 0;
     constexpr int64_t kCUs = 256;
@@ -396,7 +401,7 @@ int gemm_mid_tiles(int64_t M, int64_t N, int64_t K, int bits) {
     const int64_t wide = ((M + 255) / 256) * ((N + 255) / 256);
     const int64_t big_work = wide >= 128 ? work(256, 256) : work(256, 128);
     if (4 * work(TM, 160) <= 3 * big_work) return 160;
-    if (BL_WIDE_TILES && 10 * work(TM, 448) <= 9 * big_work) return 448;
+    if (BL_WIDE_TILES && 10 * work(TM, 448) <= BL_WIDE_TENTHS * big_work) return 448;
     return 0;
 }
 
