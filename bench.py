@@ -773,6 +773,7 @@ def leg_mfma_ceiling(torch, reps=3):
     for kind, name, iters, peak in ((0, "int8_32x32x32", 20000, INT8_PEAK_TOPS),
                                     (3, "int8_16x16x64", 40000, INT8_PEAK_TOPS),
                                     (1, "fp4_x_fp6_32x32x64", 10000, F6F4_PEAK_TOPS),
+                                    (4, "fp4_x_fp6_16x16x128", 20000, F6F4_PEAK_TOPS),
                                     (2, "bf16_32x32x16", 20000, BF16_PEAK_TFLOPS)):
         def launch():
             st = lib.bl_calib_mfma(kind, blocks, iters, ctypes.c_void_p(sink.data_ptr()),

@@ -15,7 +15,9 @@
 //   kind 2  bf16 32x32x16: bf16 gradients of spread 0.01 times ternary codes (the
 //           backward GEMMs);
 //   kind 3  int8 16x16x64: the operands of kind 0 on v_mfma_i32_16x16x64_i8 (the
-//           balanced-tile prefill GEMM).
+//           balanced-tile prefill GEMM);
+//   kind 4  FP4 x FP6 16x16x128: the operands of kind 1 on the 16x16x128 scaled MFMA
+//           (the balanced-tile 4-bit GEMM).
 // 8 waves per block (two per SIMD), one block per CU; each wave runs 8 accumulators.
 //
 // An HBM read-only loop: a grid-stride sweep of 16-byte non-temporal loads over a buffer
@@ -31,6 +33,7 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
 constexpr int kThreads = 512;
@@ -109,7 +112,7 @@ __global__ void __launch_bounds__(kThreads) mfma_loop(int iters, uint32_t seed, 
         }
 #pragma unroll
         for (int j = 0; j < kAcc; ++j) total += (float)acc[j][lane & 3];
-    } else if constexpr (kKind == 1) {
+    } else if constexpr (kKind == 1 || kKind == 4) {
         v8i a[2], b[2];
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
@@ -133,17 +136,31 @@ __global__ void __launch_bounds__(kThreads) mfma_loop(int iters, uint32_t seed, 
 #pragma unroll
             for (int d = 0; d < 8; ++d) b[s][d] = d < 6 ? (int)bits[d] : 0;
         }
-        v16f acc[kAcc];
+        if constexpr (kKind == 1) {
+            v16f acc[kAcc];
 #pragma unroll
-        for (int j = 0; j < kAcc; ++j) acc[j] = v16f{};
-        for (int it = 0; it < iters; ++it) {
+            for (int j = 0; j < kAcc; ++j) acc[j] = v16f{};
+            for (int it = 0; it < iters; ++it) {
 #pragma unroll
-            for (int j = 0; j < kAcc; ++j)
-                acc[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[j & 1], b[j & 1], acc[j],
-                                                                          4, 2, 0, 127, 0, 127);
+                for (int j = 0; j < kAcc; ++j)
+                    acc[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[j & 1], b[j & 1], acc[j],
+                                                                              4, 2, 0, 127, 0, 127);
+            }
+#pragma unroll
+            for (int j = 0; j < kAcc; ++j) total += acc[j][lane & 15];
+        } else {
+            v4f acc[kAcc];
+#pragma unroll
+            for (int j = 0; j < kAcc; ++j) acc[j] = v4f{};
+            for (int it = 0; it < iters; ++it) {
+#pragma unroll
+                for (int j = 0; j < kAcc; ++j)
+                    acc[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[j & 1], b[j & 1], acc[j],
+                                                                              4, 2, 0, 127, 0, 127);
+            }
+#pragma unroll
+            for (int j = 0; j < kAcc; ++j) total += acc[j][lane & 3];
         }
-#pragma unroll
-        for (int j = 0; j < kAcc; ++j) total += acc[j][lane & 15];
     } else {
         v8bf a[2], b[2];
 #pragma unroll
@@ -243,7 +260,8 @@ double bl_calib_ops(int kind, int blocks, int iters) {
     const double per = kind == 0   ? 2.0 * 32 * 32 * 32
                        : kind == 1 ? 2.0 * 32 * 32 * 64
                        : kind == 2 ? 2.0 * 32 * 32 * 16
-                                   : 2.0 * 16 * 16 * 64;
+                       : kind == 3 ? 2.0 * 16 * 16 * 64
+                                   : 2.0 * 16 * 16 * 128;
     return (double)blocks * (kThreads / 64) * iters * kAcc * per;
 }
 
@@ -258,6 +276,7 @@ int bl_calib_mfma(int kind, int blocks, int iters, float *sink, void *stream) {
     case 1: hipLaunchKernelGGL(mfma_loop<1>, grid, block, 0, s, iters, 1u, sink); break;
     case 2: hipLaunchKernelGGL(mfma_loop<2>, grid, block, 0, s, iters, 1u, sink); break;
     case 3: hipLaunchKernelGGL(mfma_loop<3>, grid, block, 0, s, iters, 1u, sink); break;
+    case 4: hipLaunchKernelGGL(mfma_loop<4>, grid, block, 0, s, iters, 1u, sink); break;
     default: return (int)hipErrorInvalidValue;
     }
     return (int)hipGetLastError();

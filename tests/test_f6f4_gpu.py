@@ -19,7 +19,7 @@ import torch
 import oracle
 import ternary_weight_quantized_bitlinear_amd as bl
 from gpu_util import DEV, assert_same_bytes, say, to_dev, to_host
-from test_parity_gpu import _check_forward
+from test_parity_gpu import _check_forward, _codes_f64, _layer, _run_forward
 
 pytestmark = pytest.mark.gpu
 
@@ -56,6 +56,25 @@ def test_f6f4_variants(gran, epi, ydt, with_bias):
     _check_forward(300, 384, 260, 4, gran, epi, ydt, with_bias, False, sampled=False, seed=3)
     _check_forward(257, 256, 388, 4, gran, epi, ydt, with_bias, True, x_dtype="bf16",
                    sampled=False, seed=2)
+    # 256-row tiles with two k steps per LDS stage, 256 tiles (outputs sampled)
+    _check_forward(1024, 128, 14336, 4, gran, epi, ydt, with_bias, False, sampled=True, seed=4)
+
+
+# Larger shapes on the 256-row tiles with two k steps per LDS stage: outputs sampled,
+# then the full int32 accumulators against a float64 product of the oracle's codes
+# (exact: integers below 2^53).  The 2B up projection at 2048 tokens (216 tiles), two
+# rounds of tiles (432), and ragged shapes with 256 tiles and with an odd number of
+# stages.
+@pytest.mark.parametrize("M,K,N", [(2048, 2560, 6912), (2048, 256, 13824), (2000, 256, 6900),
+                                   (2000, 384, 8100)])
+def test_f6f4_accumulators(M, K, N):
+    _check_forward(M, K, N, 4, "token", "relu2", "bf16", True, True, x_dtype="bf16",
+                   kind="ternary", sampled=True)
+    W, X = _layer(M, K, N, 0, "ternary")
+    say("FP6 x FP4 GEMM, full int32 accumulators", M, K, N)
+    acc, (p_ref, _, xq_ref, _, _) = _run_forward(W, X, 4, "token", None, "i32", None, False, "bf16")
+    q, c = _codes_f64(xq_ref, 4, p_ref, K)
+    assert np.array_equal(acc.astype(np.float64), q @ c.T), "int32 accumulators differ"
 
 
 def _const_case(M, N, K, qbyte, wbyte):
