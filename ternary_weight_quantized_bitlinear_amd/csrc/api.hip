@@ -66,9 +66,9 @@ size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 // prepared activations (int8 [M][K]) and their per-token code sums
 size_t ws_prepared(int64_t M, int64_t K) { return up256((size_t)(M * K)) + up256((size_t)M * 4); }
-// FP6 operand blocks of int4 codes and their per-token code sums
+// FP6 operand blocks of int4 codes and their per-token code sums (as partials)
 size_t ws_prepared_f6(int64_t M, int64_t K) {
-    return up256(bl::f6_prepared_bytes(M, K)) + up256((size_t)M * 4);
+    return up256(bl::f6_prepared_bytes(M, K)) + up256(bl::f6_sum_bytes(M, K));
 }
 
 // 4-bit activations at prefill sizes run on the FP6 x FP4 matrix cores

@@ -238,50 +238,65 @@ __device__ __forceinline__ uint32_t fp6_half(int q) {
 // in bits 6e of the slot's 192 bits.  Slot dwords 0-1 sit in a 512-byte plane, dwords
 // 2-5 in a 1024-byte plane, so that a wave reads each plane with consecutive lanes.
 // Blocks of one kb are contiguous over mb; tokens past M are zero.
-template <int kKbPerWave>
+//
+// Block (mb, y) converts k blocks y kb_per_block .. (y + 1) kb_per_block - 1 of token
+// block mb (wave w the k blocks w, w + 4, ..., two in flight) and stores the partial
+// code sum of each of its 32 tokens at sums[y][32 mb + t]: every partial is written once
+// (0 for an empty range or a token past M), so nothing is cleared beforehand and no
+// atomics are needed.
 __global__ void __launch_bounds__(kAqThreads)
 aq_prepare_f6(const uint8_t *__restrict__ xq, int64_t M, int64_t K, int64_t mb_pad,
-              uint8_t *__restrict__ xp, int32_t *__restrict__ rowsum) {
-    __shared__ int red[kAqThreads / kWave][32];
+              int kb_per_block, uint8_t *__restrict__ xp, int32_t *__restrict__ sums) {
+    constexpr int kW = kAqThreads / kWave;
+    __shared__ int red[kW][32];
     const int64_t mb = blockIdx.x;
     const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
     const int r32 = lane >> 1, g = lane & 1;  // adjacent lanes read adjacent 16 bytes of a row
     const int slot = r32 + 32 * g;
     const int64_t m = 32 * mb + r32;
     const int64_t nkb = K / 64;
-    const int64_t kb0 = (int64_t)blockIdx.y * (kKbPerWave * (kAqThreads / kWave));
+    const int64_t kb_begin = (int64_t)blockIdx.y * kb_per_block;
+    const int64_t kb_end = min(nkb, kb_begin + kb_per_block);
     int csum = 0;
+    for (int64_t kb0 = kb_begin + wave; kb0 < kb_end; kb0 += 2 * kW) {
+        uint4 v[2];
 #pragma unroll
-    for (int it = 0; it < kKbPerWave; ++it) {
-        const int64_t kb = kb0 + (int64_t)it * (kAqThreads / kWave) + wave;
-        if (kb >= nkb) break;
-        uint4 v = make_uint4(0u, 0u, 0u, 0u);
-        if (m < M) v = *reinterpret_cast<const uint4 *>(xq + m * (K / 2) + 32 * kb + 16 * g);
-        const uint32_t d[4] = {v.x, v.y, v.z, v.w};
-        uint32_t o[6] = {0u, 0u, 0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int e = 0; e < 32; ++e) {
-            const int kl = 16 * (e / 16) + 2 * (e % 8) + (e / 8) % 2;
-            const int q = ((int)(d[kl / 8] << (28 - 4 * (kl % 8)))) >> 28;
-            csum += q;
-            const uint32_t c = fp6_half(q);
-            const int bit = 6 * e;
-            o[bit / 32] |= c << (bit % 32);
-            if (bit % 32 > 26) o[bit / 32 + 1] |= c >> (32 - bit % 32);
+        for (int h = 0; h < 2; ++h) {
+            const int64_t kb = kb0 + h * kW;
+            v[h] = make_uint4(0u, 0u, 0u, 0u);
+            if (m < M && kb < kb_end)
+                v[h] = *reinterpret_cast<const uint4 *>(xq + m * (K / 2) + 32 * kb + 16 * g);
         }
-        uint8_t *blk = xp + ((size_t)kb * (size_t)mb_pad + (size_t)mb) * 1536;
-        *reinterpret_cast<uint2 *>(blk + 8 * slot) = make_uint2(o[0], o[1]);
-        *reinterpret_cast<uint4 *>(blk + 512 + 16 * slot) = make_uint4(o[2], o[3], o[4], o[5]);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int64_t kb = kb0 + h * kW;
+            if (kb >= kb_end) break;
+            const uint32_t d[4] = {v[h].x, v[h].y, v[h].z, v[h].w};
+            uint32_t o[6] = {0u, 0u, 0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int e = 0; e < 32; ++e) {
+                const int kl = 16 * (e / 16) + 2 * (e % 8) + (e / 8) % 2;
+                const int q = ((int)(d[kl / 8] << (28 - 4 * (kl % 8)))) >> 28;
+                csum += q;
+                const uint32_t c = fp6_half(q);
+                const int bit = 6 * e;
+                o[bit / 32] |= c << (bit % 32);
+                if (bit % 32 > 26) o[bit / 32 + 1] |= c >> (32 - bit % 32);
+            }
+            uint8_t *blk = xp + ((size_t)kb * (size_t)mb_pad + (size_t)mb) * 1536;
+            *reinterpret_cast<uint2 *>(blk + 8 * slot) = make_uint2(o[0], o[1]);
+            *reinterpret_cast<uint4 *>(blk + 512 + 16 * slot) = make_uint4(o[2], o[3], o[4], o[5]);
+        }
     }
-    // the token's two halves, then the block's waves; one atomic per token and block
+    // the token's two halves, then the block's waves
     csum += __shfl_xor(csum, 1);
     if (g == 0) red[wave][r32] = csum;
     __syncthreads();
-    if (threadIdx.x < 32 && 32 * mb + threadIdx.x < M) {
+    if (threadIdx.x < 32) {
         int t = 0;
 #pragma unroll
-        for (int w = 0; w < kAqThreads / kWave; ++w) t += red[w][threadIdx.x];
-        atomicAdd(rowsum + 32 * mb + threadIdx.x, t);
+        for (int w = 0; w < kW; ++w) t += red[w][threadIdx.x];
+        sums[(size_t)blockIdx.y * (size_t)(32 * mb_pad) + (size_t)(32 * mb) + threadIdx.x] = t;
     }
 }
 
@@ -446,15 +461,13 @@ hipError_t launch_prepare_acts(const void *xq, int bits, int64_t M, int64_t K, u
 }
 
 hipError_t launch_prepare_acts_f6(const void *xq, int64_t M, int64_t K, uint8_t *xp,
-                                  int32_t *rowsum, hipStream_t s) {
-    constexpr int kKbPerWave = 2;
-    constexpr int kKbPerBlock = kKbPerWave * (kAqThreads / kWave);
-    hipError_t e = launch_zero_u32(reinterpret_cast<uint32_t *>(rowsum), M, s);
-    if (e != hipSuccess) return e;
+                                  int32_t *sums, hipStream_t s) {
     const int64_t mb_pad = f6_mb_pad(M);
-    const dim3 grid((unsigned)mb_pad, (unsigned)((K / 64 + kKbPerBlock - 1) / kKbPerBlock));
-    hipLaunchKernelGGL(aq_prepare_f6<kKbPerWave>, grid, dim3(kAqThreads), 0, s,
-                       static_cast<const uint8_t *>(xq), M, K, mb_pad, xp, rowsum);
+    const int parts = f6_sum_parts(K);
+    const int kb_per_block = (int)((K / 64 + parts - 1) / parts);
+    const dim3 grid((unsigned)mb_pad, (unsigned)parts);
+    hipLaunchKernelGGL(aq_prepare_f6, grid, dim3(kAqThreads), 0, s,
+                       static_cast<const uint8_t *>(xq), M, K, mb_pad, kb_per_block, xp, sums);
     return hipGetLastError();
 }
 

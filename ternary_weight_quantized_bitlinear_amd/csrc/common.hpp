@@ -265,7 +265,8 @@ struct FwdArgs {
     int y_dtype;           // 0 f32, 1 bf16, 2 i32
     int64_t batch = 1;     // independent problems laid out back to back (GEMV path)
     int x_shared = 0;      // GEMV path: every problem reads the same xq and act_scale
-    const int32_t *rowsum = nullptr;  // prepared activations: sum_k q[m][k] per token
+    const int32_t *rowsum = nullptr;  // prepared activations: sum_k q[m][k] per token (the
+                                      // FP6 path: its partial sums, see f6_sum_parts)
     // the GEMV's row prologue (raw bf16 X, per-token scales, M <= 16) when rows = 1
     int rows = 0;
 };
@@ -308,13 +309,23 @@ hipError_t allow_lds(const void *fn, size_t lds);
 hipError_t launch_prepare_acts(const void *xq, int bits, int64_t M, int64_t K, uint8_t *xp,
                                int32_t *rowsum, hipStream_t s);
 // FP6 operand blocks of int4 codes for the scaled-MFMA GEMM: 1536 bytes per 32 tokens x
-// 64 k, tokens padded to a multiple of 256; plus sum_k q per token
+// 64 k, tokens padded to a multiple of 256; plus sum_k q per token, as partial sums over
+// f6_sum_parts(K) ranges of k (eight 64-wide k blocks a range, at most 16 ranges), laid
+// out [range][32 f6_mb_pad(M)] int32: written once each, nothing to clear first; the
+// GEMM adds a token's partials
 inline int64_t f6_mb_pad(int64_t M) { return 8 * ((M + 255) / 256); }
 inline size_t f6_prepared_bytes(int64_t M, int64_t K) {
     return (size_t)(K / 64) * (size_t)f6_mb_pad(M) * 1536;
 }
+inline int f6_sum_parts(int64_t K) {
+    const int64_t p = (K / 64 + 7) / 8;
+    return (int)(p < 1 ? 1 : p > 16 ? 16 : p);
+}
+inline size_t f6_sum_bytes(int64_t M, int64_t K) {
+    return (size_t)f6_sum_parts(K) * 32 * (size_t)f6_mb_pad(M) * sizeof(int32_t);
+}
 hipError_t launch_prepare_acts_f6(const void *xq, int64_t M, int64_t K, uint8_t *xp,
-                                  int32_t *rowsum, hipStream_t s);
+                                  int32_t *sums, hipStream_t s);
 // decode-sized M: one launch, optional fused activation quantization prologue
 bool gemv_supports(int64_t M, int64_t K);
 hipError_t launch_gemv(const FwdArgs &a, bool fused, void *ws, hipStream_t s);

@@ -75,7 +75,7 @@ template <int kBN, int kSub = 1> struct F6Tile {
 
 struct F6Params {
     const uint8_t *xp;        // FP6 operand blocks [K/64][mb_pad][1536]
-    const int32_t *rowsum;    // sum_k q[m][k]
+    const int32_t *rowsum;    // sum_k q[m][k] in sum_parts partials [part][sum_ld]
     const float *act_scale;
     int gran;
     const uint8_t *w;
@@ -83,9 +83,23 @@ struct F6Params {
     const float *bias;
     int M, N, K;
     int mb_pad;
+    int sum_parts;
+    int sum_ld;
     void *y;
     int tiles_m;
 };
+
+// a token's code sum: its partials from the prepare pass (at most 16), all loaded at
+// once (past the last one the last again, not added) so that their latencies overlap
+__device__ __forceinline__ int f6_code_sum(const F6Params &p, int m) {
+    int v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) v[u] = p.rowsum[(size_t)min(u, p.sum_parts - 1) * p.sum_ld + m];
+    int cs = 0;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) cs += u < p.sum_parts ? v[u] : 0;
+    return cs;
+}
 
 template <int kBN, int kSub, int kYD, bool kRelu2, bool kBias>
 __global__ void __launch_bounds__(F6Tile<kBN>::kThreads, kBN == 128 ? 2 : 1)
@@ -111,7 +125,7 @@ gemm_f6f4_kernel(F6Params p) {
         int cs = 0;
         if (m < p.M) {
             f = p.act_scale[p.gran == 1 ? 0 : m] * *p.gamma;
-            cs = p.rowsum[m];
+            cs = f6_code_sum(p, m);
         }
         s_f[t] = f;
         s_sum[t] = cs;
@@ -445,7 +459,7 @@ gemm_f6f4_mid_kernel(F6Params p) {
         int cs = 0;
         if (m < p.M) {
             f = p.act_scale[p.gran == 1 ? 0 : m] * *p.gamma;
-            cs = p.rowsum[m];
+            cs = f6_code_sum(p, m);
         }
         s_f[t] = f;
         s_sum[t] = cs;
@@ -700,6 +714,9 @@ hipError_t launch_gemm_f6f4(const FwdArgs &a, hipStream_t s) {
     p.N = (int)a.N;
     p.K = (int)a.K;
     p.mb_pad = (int)f6_mb_pad(a.M);
+    p.sum_parts = f6_sum_parts(a.K);
+    p.sum_ld = 32 * p.mb_pad;
+    if (p.sum_parts < 1 || p.sum_parts > 16) return hipErrorInvalidValue;  // f6_code_sum's bound
     p.y = a.y;
     if (f6_mid_preferred(a.M, a.N, a.K)) return launch_f6_mid(p, a, s);
     // 256-wide tiles when they cover at least half the CUs, else 128-wide, two per CU

@@ -59,6 +59,10 @@ def test_workspace_sizes(L):
     assert L.bitlinear_workspace_size(bl.BL_OP_FORWARD_FUSED, 2048, 6912, 2560, 8, 0) >= 2048 * 2560
     assert L.bitlinear_workspace_size(bl.BL_OP_FORWARD_FUSED, 2048, 6912, 2560, 4, 0) >= 2048 * 1280
     assert L.bitlinear_workspace_size(bl.BL_OP_FORWARD, -1, 6912, 2560, 8, 0) == 0
+    # int4 at prefill sizes: FP6 operand blocks (1536 bytes per 32 tokens x 64 k) and the
+    # per-token code sums as partials, one per range of eight 64-wide k blocks (five here)
+    assert L.bitlinear_workspace_size(bl.BL_OP_FORWARD, 2048, 6912, 2560, 4, 0) >= \
+        (2560 // 64) * (2048 // 32) * 1536 + 5 * 2048 * 4
 
 
 # Fake device addresses: validation must reject the call before touching them.
