@@ -47,6 +47,9 @@ constexpr int kADma = kAStage / 1024;                // 12 DMAs of 64 lanes x 16
 #ifndef BL_F6_STAGES
 #define BL_F6_STAGES 4
 #endif
+#ifndef BL_F6_NT_STORE
+#define BL_F6_NT_STORE 1   // whole-line output stores of the 256-row tiles: 1 nontemporal, 0 plain
+#endif
 #ifndef BL_F6_MID
 #define BL_F6_MID 1        // 0: never the balanced tiles
 #endif
@@ -333,9 +336,16 @@ gemm_f6f4_kernel(F6Params p) {
                     const int cb = 16 * (lane % kLanesPerRow);
                     const uint4 v = *reinterpret_cast<const uint4 *>(stg + row * kPitch + cb);
                     const int mr = m0 + 64 * wt + 32 * i + row;
-                    if (mr < p.M)
-                        *reinterpret_cast<uint4 *>(static_cast<uint8_t *>(p.y) +
-                                                   ((size_t)mr * p.N + nh0) * kOutB + cb) = v;
+                    if (mr < p.M) {
+                        uint4 *dst = reinterpret_cast<uint4 *>(static_cast<uint8_t *>(p.y) +
+                                                               ((size_t)mr * p.N + nh0) * kOutB + cb);
+                        if (BL_F6_NT_STORE) {
+                            typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+                            __builtin_nontemporal_store(u4{v.x, v.y, v.z, v.w}, reinterpret_cast<u4 *>(dst));
+                        } else {
+                            *dst = v;
+                        }
+                    }
                 }
                 asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
                 continue;

@@ -41,7 +41,10 @@ def test_mid_shapes(M, K, N, fused):
 @pytest.mark.parametrize("with_bias", [False, True])
 @pytest.mark.parametrize("K", [320, 256])
 def test_mid_variants(gran, epi, ydt, with_bias, K):
+    # N % 8 != 0 (bf16 stored from registers) and N % 8 == 0 (bf16 staged through LDS and
+    # stored in whole 16-byte chunks), each with a partial last row block
     _check_forward(300, K, 260, 8, gran, epi, ydt, with_bias, False, sampled=False)
+    _check_forward(300, K, 264, 8, gran, epi, ydt, with_bias, False, sampled=False, seed=5)
 
 
 @pytest.mark.parametrize("K", [320, 384])
