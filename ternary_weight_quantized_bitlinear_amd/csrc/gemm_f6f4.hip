@@ -48,7 +48,8 @@ constexpr int kADma = kAStage / 1024;                // 12 DMAs of 64 lanes x 16
 #define BL_F6_STAGES 4
 #endif
 #ifndef BL_F6_NT_STORE
-#define BL_F6_NT_STORE 1   // whole-line output stores of the 256-row tiles: 1 nontemporal, 0 plain
+#define BL_F6_NT_STORE 1   // 1: whole-line nontemporal output stores (the 256-row tiles' staged
+                           // lines; bf16 tiles of the balanced kernel staged through LDS); 0 not
 #endif
 #ifndef BL_F6_MID
 #define BL_F6_MID 1        // 0: never the balanced tiles
@@ -593,15 +594,68 @@ gemm_f6f4_mid_kernel(F6Params p) {
                     for (int r = 0; r < 4; ++r) red[((i * 5 + j) * 4 + r) * 64] = acc[i][j][r];
         }
         __syncthreads();
-        if (grp == 1) return;
         // each partial is an fp32 integer multiple of 1/4 below 2^22: the sum is exact
+        if (grp == 0)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < 5; ++j)
+                for (int j = 0; j < 5; ++j)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) acc[i][j][r] += red[((i * 5 + j) * 4 + r) * 64];
+                    for (int r = 0; r < 4; ++r) acc[i][j][r] += red[((i * 5 + j) * 4 + r) * 64];
     }
+
+    // ---- bf16 output with N % 8 == 0: staged through LDS (inside the free rings) and
+    // stored as whole 16-byte chunks along rows with the nontemporal hint, as in the int8
+    // balanced kernel
+    if constexpr (kYD == 1 && BL_F6_NT_STORE) {
+        if (p.N % 8 == 0) {
+            constexpr int kRowB = 2 * kMTN + 16, kChunks = kMTN / 8;
+            static_assert(kMTM * kRowB <= kMStages * kMStageBytes, "staging fits the ring");
+            __syncthreads();  // every wave is done with the rings and the reduction buffer
+            if (grp == 0) {
+                const int ml = 64 * wm + r16;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int row = ml + 16 * i;
+                    const float f = s_f[row];
+                    const int cs = s_sum[row];
+#pragma unroll
+                    for (int j = 0; j < 5; ++j) {
+                        const int col = 80 * wn + 16 * j + 4 * q, n = n0 + col;
+                        float y[4];
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) {
+                            float v = __fmul_rn((float)((int)(4.0f * acc[i][j][t]) - cs), f);
+                            if (kBias) v = __fadd_rn(v, n + t < p.N ? p.bias[n + t] : 0.0f);
+                            if (kRelu2) {
+                                const float rr = v > 0.0f ? v : 0.0f;
+                                v = __fmul_rn(rr, rr);
+                            }
+                            y[t] = v;
+                        }
+                        typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+                        const bf2 lo = {(__bf16)y[0], (__bf16)y[1]};
+                        const bf2 hi = {(__bf16)y[2], (__bf16)y[3]};
+                        *reinterpret_cast<uint2 *>(smem + row * kRowB + 2 * col) =
+                            make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+                    }
+                }
+            }
+            __syncthreads();
+            typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+            for (int c = tid; c < kMTM * kChunks; c += 64 * kMWaves * kSplit) {
+                const int row = c / kChunks, cc = c - row * kChunks;
+                const int m = m0 + row, n = n0 + 8 * cc;
+                if (m < p.M && n < p.N) {  // N % 8 == 0: a chunk is whole or past the end
+                    const u4 v = *reinterpret_cast<const u4 *>(smem + row * kRowB + 16 * cc);
+                    __builtin_nontemporal_store(
+                        v, reinterpret_cast<u4 *>(static_cast<uint16_t *>(p.y) + (size_t)m * p.N + n));
+                }
+            }
+            return;
+        }
+    }
+    if (grp != 0) return;
 
     // ---- epilogue: lane l holds acc[i][j][r] = 4 x sum for token 16 i + l % 16 and row
     // 16 j + 4 (l / 16) + r of the wave's tile: four consecutive outputs of one token

@@ -56,6 +56,10 @@ def test_f6f4_variants(gran, epi, ydt, with_bias):
     _check_forward(300, 384, 260, 4, gran, epi, ydt, with_bias, False, sampled=False, seed=3)
     _check_forward(257, 256, 388, 4, gran, epi, ydt, with_bias, True, x_dtype="bf16",
                    sampled=False, seed=2)
+    # the same two balanced forms with N % 8 == 0 (bf16 staged through LDS, whole chunks)
+    _check_forward(300, 384, 264, 4, gran, epi, ydt, with_bias, False, sampled=False, seed=6)
+    _check_forward(257, 256, 392, 4, gran, epi, ydt, with_bias, True, x_dtype="bf16",
+                   sampled=False, seed=7)
     # 256-row tiles with two k steps per LDS stage, 256 tiles (outputs sampled)
     _check_forward(1024, 128, 14336, 4, gran, epi, ydt, with_bias, False, sampled=True, seed=4)
 
