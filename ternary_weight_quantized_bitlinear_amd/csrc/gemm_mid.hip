@@ -34,10 +34,13 @@
 // rows of 64 bytes with their 16-byte chunks XOR-swizzled by row, four consecutive DMA
 // lanes covering one row; weight rows 16 bytes), issued kStages-1 stages ahead; one
 // barrier per stage publishes the landed stage and frees the slot the next DMA refills;
-// the fragments of the next k step are read while this one's MFMAs run.  The fragment
-// reads (16 rows x 4 chunks per instruction) still meet 2-way bank conflicts: a
-// chunk-major layout avoids them but spreads each DMA instruction over 16 rows, and
-// measured slower (46.0 against 40.2 us on the down projection).
+// the fragments of the next k step are read while this one's MFMAs run.  The activation
+// fragment reads (16 rows x 4 chunks per instruction) are free of bank conflicts with
+// the 128-byte rows of two k steps per stage, and 2-way with the 64-byte rows of one
+// (every XOR swizzle tried): a chunk-major layout avoids them but spreads each DMA
+// instruction over 16 rows, and measured slower (46.0 against 40.2 us on the down
+// projection), and so did a k split with two k steps per stage.  The one-dword weight
+// reads (16 rows at a 16-byte stride) are 2-way in both.
 //
 // Where K % 128 == 0 the 128 x 160 block has two such groups of four waves (two waves
 // per SIMD, so one wave's MFMAs cover the other's waits), each with its own ring, on
