@@ -237,6 +237,17 @@ def test_forward_prefill_long_k(M, K, N, ydt):
     _check_forward(M, K, N, 8, "tensor", None, ydt, False, True, x_dtype="bf16")
 
 
+# rows longer than the activation preparation keeps in registers (8192 elements per
+# 256-thread row): the groups past them are read a second time, and the reorder of
+# quantized codes takes two rounds of eight loads per lane
+@pytest.mark.parametrize("xdt", ["f32", "bf16"])
+@pytest.mark.parametrize("gran", ["token", "tensor"])
+def test_forward_prefill_rows_past_registers(xdt, gran):
+    for fused in (False, True):
+        _check_forward(260, 12288, 136, 8, gran, "relu2", "f32", True, fused, x_dtype=xdt,
+                       sampled=False)
+
+
 def _codes_f64(xq_ref, bits, p_ref, K):
     """The oracle's activation and weight codes as float64 matrices, unpacked from the
     documented layouts (int4: element 2i in the low nibble; 2-bit field c + 1 of code k in
