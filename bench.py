@@ -35,6 +35,8 @@ hbm_read_ceiling = a read-only sweep of 16-byte loads over 1 GiB: the rate strea
 cpu_baseline = the CPU oracle pinned to one core: one layer's decode FFN step (the
                headline's unit), plus the parity layer in full and samples of the
                prefill GEMM, the 30-layer stack and the 70B layer, extrapolated
+stack_launches_us = (leg "launches", only when named) each call of the 2B stack's block
+               at 16 tokens and at 1, repeated with rotated weights: per-launch costs
 """
 from __future__ import annotations
 
@@ -619,6 +621,79 @@ def leg_stack(torch, bl, steps=10, layers=30, batch=16):
             "fused_equals_unfused": same}
 
 
+def leg_stack_launches(torch, bl, copies=24, reps=48):
+    """Per-launch cost of each call of the 2B stack's block at batch 16 and at one token,
+    each call repeated with `copies` weight sets rotated, graph-timed after 100 ms of
+    untimed replays: the latency floor each of the stack's launches sits on.  Not in the
+    default legs (name it in --legs)."""
+    import workloads
+    dev = torch.device("cuda:0")
+    H, F = workloads.HIDDEN, workloads.FFN
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(5)
+
+    def wset(n, k):
+        out = []
+        for _ in range(copies):
+            W = torch.randint(-1, 2, (n, k), device=dev, generator=gen).float()
+            out.append(bl.quantize_weights(W))
+            del W
+        return out
+
+    w_hh, w_fh, w_hf = wset(H, H), wset(F, H), wset(H, F)
+    w_q3 = [(p.repeat(3, 1).view(3, H, p.shape[1]), g.expand(3).contiguous()) for p, g in w_hh]
+    ws = torch.empty(max(bl.workspace_size(bl.BL_OP_FORWARD_FUSED, 16, H, F),
+                         bl.workspace_size(bl.BL_OP_FORWARD, 16, F, H)) + 256,
+                     dtype=torch.uint8, device=dev)
+    res = {"copies": copies, "calls_per_graph": reps}
+    for M in (16, 1):
+        x = torch.randn((M, H), device=dev, generator=gen).to(torch.bfloat16)
+        dl = torch.randn((M, H), device=dev, generator=gen).to(torch.bfloat16)
+        u = torch.randn((M, F), device=dev, generator=gen).to(torch.bfloat16)
+        xq, xs = bl.quantize_acts(x)
+        uq, us = bl.quantize_acts(u)
+        yH = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
+        yF = torch.empty((M, F), dtype=torch.bfloat16, device=dev)
+        y3 = torch.empty((3, M, H), dtype=torch.bfloat16, device=dev)
+        h = torch.empty_like(x)
+        hq = torch.empty((M, H), dtype=torch.int8, device=dev)
+        hs = torch.empty((M,), dtype=torch.float32, device=dev)
+        cases = (
+            ("rmsnorm_quantize 2560", lambda i: bl.rmsnorm_quantize(x, dl, out=(h, hq, hs))),
+            ("qkv codes 2560->3x2560", lambda i: bl.forward_multi(xq, xs, *w_q3[i % copies], out=y3)),
+            ("o bf16 2560->2560", lambda i: bl.forward_fused(x, *w_hh[i % copies], out=yH, workspace=ws)),
+            ("up codes 2560->6912 relu2", lambda i: bl.forward(xq, xs, *w_fh[i % copies], epilogue="relu2",
+                                                              out=yF, workspace=ws)),
+            ("quantize_acts 6912", lambda i: bl.quantize_acts(u, out=(uq, us))),
+            ("down codes 6912->2560", lambda i: bl.forward(uq, us, *w_hf[i % copies], out=yH, workspace=ws)),
+            ("down bf16 6912->2560", lambda i: bl.forward_fused(u, *w_hf[i % copies], out=yH, workspace=ws)),
+        )
+        row = {}
+        for name, f in cases:
+            def run():
+                for i in range(reps):
+                    f(i)
+            ms, _ = graph_time_ms(torch, run, replays=3, steady_ms=100.0)
+            row[name] = round(ms * 1e3 / reps, 2)
+        res["M=%d" % M] = row
+    # the codes GEMVs over the token count: the part of a launch that grows with M
+    sweep = {}
+    for M in (1, 2, 4, 8, 12, 16):
+        xq, xs = bl.quantize_acts(torch.randn((M, H), device=dev, generator=gen).to(torch.bfloat16))
+        uq, us = bl.quantize_acts(torch.randn((M, F), device=dev, generator=gen).to(torch.bfloat16))
+        yF = torch.empty((M, F), dtype=torch.bfloat16, device=dev)
+        yH = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
+        for name, f in (("up", lambda i: bl.forward(xq, xs, *w_fh[i % copies], out=yF, workspace=ws)),
+                        ("down", lambda i: bl.forward(uq, us, *w_hf[i % copies], out=yH, workspace=ws))):
+            def run():
+                for i in range(reps):
+                    f(i)
+            ms, _ = graph_time_ms(torch, run, replays=3, steady_ms=100.0)
+            sweep.setdefault(name, {})["M=%d" % M] = round(ms * 1e3 / reps, 2)
+    res["codes_gemv_by_tokens"] = sweep
+    return res
+
+
 def leg_parity_layer(torch, bl, reps=200):
     """The parity configuration timed (no roofline claim: 32 KB of weights): the single
     fp32 BitLinear at M=8, K=256, N=512, fused quantize + forward + ReLU^2, fp32 Y, for
@@ -991,6 +1066,8 @@ def main():
         if "ceiling" in legs:
             side["mfma_ceiling"] = leg_mfma_ceiling(torch)
             side["hbm_read_ceiling"] = leg_hbm_ceiling(torch)
+        if "launches" in legs:
+            side["stack_launches_us"] = leg_stack_launches(torch, bl)
         if side:
             print(json.dumps(side))
         return

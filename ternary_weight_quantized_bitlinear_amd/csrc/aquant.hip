@@ -226,9 +226,64 @@ aq_prepare(const uint8_t *__restrict__ xq, int64_t M, int64_t K, uint8_t *__rest
 // gemm_f6f4.hip): code q enters as q/2 in e2m3 (sign, 2 exponent bits with bias 1, 3
 // mantissa bits), exact for every int4 code -8..7: |q| <= 4 gives the codes 4|q| (0,
 // 0.5 subnormal, 1, 1.5, 2), |q| in 5..8 gives 2|q| + 8 (2.5, 3, 3.5, 4).
-__device__ __forceinline__ uint32_t fp6_half(int q) {
-    const int a = q < 0 ? -q : q;
-    return (q < 0 ? 32u : 0u) | (uint32_t)(a <= 4 ? 4 * a : 2 * a + 8);
+__host__ __device__ constexpr uint32_t fp6_half(int q) {
+    return (q < 0 ? 32u : 0u) | (uint32_t)((q < 0 ? -q : q) <= 4 ? 4 * (q < 0 ? -q : q)
+                                                                  : 2 * (q < 0 ? -q : q) + 8);
+}
+
+// fp6_half of the code held by each raw nibble value n = 0..15 (n >= 8 is n - 16), as
+// four dwords of byte lanes: table word t holds the codes of n = 4t .. 4t + 3
+constexpr uint32_t fp6_table_word(int t) {
+    uint32_t w = 0;
+    for (int b = 0; b < 4; ++b) {
+        const int n = 4 * t + b;
+        w |= fp6_half(n < 8 ? n : n - 16) << (8 * b);
+    }
+    return w;
+}
+
+// Four codes at once: nb holds raw nibble values 0..15 in its four bytes.  The FP6 codes
+// come from byte permutes of the table (one per half of it, the nibble's bit 3 picking
+// the half); the signed codes' sum is added to csum.  Returns the four 6-bit codes
+// packed as a 24-bit chunk, byte 0's code lowest.
+__device__ __forceinline__ uint32_t fp6_chunk(uint32_t nb, int &csum) {
+    constexpr uint32_t t0 = fp6_table_word(0), t1 = fp6_table_word(1);
+    constexpr uint32_t t2 = fp6_table_word(2), t3 = fp6_table_word(3);
+    const uint32_t sel = nb & 0x07070707u;
+    const uint32_t lo = __builtin_amdgcn_perm(t1, t0, sel);  // codes of n = 0..7
+    const uint32_t hi = __builtin_amdgcn_perm(t3, t2, sel);  // codes of n = 8..15
+    const uint32_t b3 = (nb >> 3) & 0x01010101u;
+    const uint32_t neg = (b3 << 8) - b3;  // 0xFF in the bytes with n >= 8
+    const uint32_t r = (hi & neg) | (lo & ~neg);
+    // the codes as signed bytes (n - 16 where n >= 8), summed
+    csum = __builtin_amdgcn_sdot4((int)(nb | (neg & 0xF0F0F0F0u)), 0x01010101, csum, false);
+    // bytes (6 bits each) -> 12-bit pairs at bits 0 and 16 -> one 24-bit chunk
+    const uint32_t pr = (r & 0x003F003Fu) | ((r >> 2) & 0x0FC00FC0u);
+    return (pr & 0xFFFu) | ((pr >> 4) & 0xFFF000u);
+}
+
+// The 32 codes of a lane slot (dwords d: nibble j of d[i] is k_local 8i + j) -> the
+// slot's 192 bits o, element e at bits 6e.  Element groups of four are byte vectors of
+// the nibbles: e 0-3 the even nibbles of d[0], 4-7 those of d[1], 8-11 and 12-15 the odd
+// nibbles of d[0] and d[1], and 16-31 the same of d[2] and d[3] (k_local(e) of the
+// block layout below).
+__device__ __forceinline__ void fp6_slot(const uint32_t (&d)[4], uint32_t (&o)[6], int &csum) {
+    uint32_t c[8];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const uint32_t a = d[2 * h], b = d[2 * h + 1];
+        c[4 * h + 0] = fp6_chunk(a & 0x0F0F0F0Fu, csum);
+        c[4 * h + 1] = fp6_chunk(b & 0x0F0F0F0Fu, csum);
+        c[4 * h + 2] = fp6_chunk((a >> 4) & 0x0F0F0F0Fu, csum);
+        c[4 * h + 3] = fp6_chunk((b >> 4) & 0x0F0F0F0Fu, csum);
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const uint32_t *q = c + 4 * h;
+        o[3 * h + 0] = q[0] | (q[1] << 24);
+        o[3 * h + 1] = (q[1] >> 8) | (q[2] << 16);
+        o[3 * h + 2] = (q[2] >> 16) | (q[3] << 8);
+    }
 }
 
 // Block (kb, mb) holds tokens 32 mb .. 32 mb + 31 over k = 64 kb .. 64 kb + 63 as the
@@ -272,17 +327,8 @@ aq_prepare_f6(const uint8_t *__restrict__ xq, int64_t M, int64_t K, int64_t mb_p
             const int64_t kb = kb0 + h * kW;
             if (kb >= kb_end) break;
             const uint32_t d[4] = {v[h].x, v[h].y, v[h].z, v[h].w};
-            uint32_t o[6] = {0u, 0u, 0u, 0u, 0u, 0u};
-#pragma unroll
-            for (int e = 0; e < 32; ++e) {
-                const int kl = 16 * (e / 16) + 2 * (e % 8) + (e / 8) % 2;
-                const int q = ((int)(d[kl / 8] << (28 - 4 * (kl % 8)))) >> 28;
-                csum += q;
-                const uint32_t c = fp6_half(q);
-                const int bit = 6 * e;
-                o[bit / 32] |= c << (bit % 32);
-                if (bit % 32 > 26) o[bit / 32 + 1] |= c >> (32 - bit % 32);
-            }
+            uint32_t o[6];
+            fp6_slot(d, o, csum);
             uint8_t *blk = xp + ((size_t)kb * (size_t)mb_pad + (size_t)mb) * 1536;
             *reinterpret_cast<uint2 *>(blk + 8 * slot) = make_uint2(o[0], o[1]);
             *reinterpret_cast<uint4 *>(blk + 512 + 16 * slot) = make_uint4(o[2], o[3], o[4], o[5]);
