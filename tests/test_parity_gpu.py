@@ -248,6 +248,21 @@ def test_forward_prefill_rows_past_registers(xdt, gran):
                        sampled=False)
 
 
+# 4-bit activations from raw rows at prefill sizes (int4 codes, their FP6 operand blocks,
+# the FP6 x FP4 GEMM).  Ragged token counts (padding inside the last 32-token group and
+# up to the 256-token multiple), both input types, per-tensor scales, and K = 8256 (129 k
+# blocks: the last of the 16 code-sum ranges is empty); raw int32 accumulators and
+# rescaled outputs in full
+@pytest.mark.parametrize("M,K,N,xdt,gran", [(130, 512, 136, "bf16", "token"),
+                                            (257, 2560, 129, "f32", "token"),
+                                            (300, 8256, 200, "f32", "tensor"),
+                                            (137, 8256, 160, "bf16", "token"),
+                                            (512, 1024, 384, "bf16", "tensor")])
+def test_forward_fused_int4_fp6_blocks(M, K, N, xdt, gran):
+    _check_forward(M, K, N, 4, gran, None, "i32", False, True, x_dtype=xdt, sampled=False)
+    _check_forward(M, K, N, 4, gran, "relu2", "f32", True, True, x_dtype=xdt, sampled=False)
+
+
 def _codes_f64(xq_ref, bits, p_ref, K):
     """The oracle's activation and weight codes as float64 matrices, unpacked from the
     documented layouts (int4: element 2i in the low nibble; 2-bit field c + 1 of code k in
